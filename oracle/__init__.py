@@ -1,0 +1,22 @@
+"""fp64 CPU oracle for the TTT-with-KV-binding forward pass.
+
+Test infrastructure only: imported by the tests, the smoke check and the
+benchmark's CPU-baseline leg, never by the library or its binding.
+"""
+from .ttt_oracle import (  # noqa: F401
+    NORM_EPS,
+    forward,
+    large_chunk_linear,
+    large_chunk_swiglu,
+    linear_binding_grad,
+    linear_binding_loss,
+    normalize_columns,
+    per_token_linear,
+    silu,
+    silu_prime,
+    swiglu_binding_grad,
+    swiglu_binding_loss,
+    swiglu_forward,
+    swiglu_pack,
+    swiglu_unpack,
+)

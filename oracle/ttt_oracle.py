@@ -1,0 +1,256 @@
+"""Plain fp64 CPU oracle for the TTT-with-KV-binding forward pass.
+
+TEST INFRASTRUCTURE ONLY. Nothing on the product path imports, calls or
+links this module: only the tests, the smoke check and the CPU-baseline leg
+of the benchmark do. It shares no code with the HIP library.
+
+What it computes (sources are the pages on "Test-Time Training with KV
+Binding Is Secretly Linear Attention" and on LaCT, "Test-Time Training Done
+Right"; no page prints an equation, so each step below restates in symbols
+what the cited passage says in words):
+
+* A fast weight ``W`` is a small model ``f_W``.  Each token ``i`` carries a
+  key ``k_i``, a value ``v_i``, a query ``q_i`` and a learning rate
+  ``eta_i``.  The inner-loop (binding) loss for a token is the negative inner
+  product ``L_i(W) = -<f_W(k_i), v_i>`` (LaCT review, section on non-linear
+  memory and local attention).  An update is one explicit gradient-descent
+  step ``W <- W - eta * dL/dW``; a negative ``eta`` is gradient ascent (paper
+  summary, technical section 2A item 4 and section 3 item 2).
+* Per-token mode (paper summary, technical section 2B; podcast at 7:50 to
+  9:01): a linear ``f_W(k) = k W`` gets one step per token and the query reads
+  the memory.  The read is taken after the token's own update, so the closed
+  form is ``o_t = q_t (W0 + sum_{i<=t} eta_i k_i^T v_i)``; ``inclusive=False``
+  gives the read-before-update variant ``sum_{i<t}``.
+* Large-chunk modes (LaCT review, sections on fast weights, on non-linear
+  memory, and on read order): tokens are grouped in chunks; every token of a
+  chunk reads the memory left by the previous chunks, then one summed,
+  eta-weighted gradient step is applied for the whole chunk and the weights
+  are L2-normalised after the update.  Memory is either a linear map or a
+  SwiGLU MLP with three matrices.
+
+Readings taken where the pages are silent (each also listed in the design doc):
+row-vector convention ``o = q W`` with ``W`` stored ``[d_in, d_out]``; the
+post-update normalisation gives every output unit's fan-in vector (a column
+of the ``[d_in, d_out]`` store) unit L2 norm, dividing by
+``max(norm, 1e-12)``; the initial weights are not normalised before the
+first read; the SwiGLU branch with SiLU is ``x W1``; all SwiGLU gradients of
+a chunk are taken at the weights that read that chunk; a shorter final chunk
+follows the same read-then-update order.
+
+Arrays are float64 numpy arrays.  Shapes: Q, K ``[B,H,T,d_k]``; V
+``[B,H,T,d_v]``; eta ``[B,H,T]``; linear W ``[B,H,d_k,d_v]``; SwiGLU
+W1, W3 ``[B,H,d,d_h]`` and W2 ``[B,H,d_h,d]``.  All (b, h) pairs are
+independent, so every function is vectorised over them only; the token and
+chunk loops are explicit and sequential.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+NORM_EPS = 1e-12
+
+
+def _f64(x):
+    return np.asarray(x, dtype=np.float64)
+
+
+# ---------------------------------------------------------------------------
+# Inner-loop losses and their hand-derived gradients
+# ---------------------------------------------------------------------------
+
+def linear_binding_loss(K, V, eta, W):
+    """``sum_i eta_i * (-<k_i W, v_i>)`` per (b, h): the eta-weighted
+    negative inner-product binding loss of a linear fast weight (LaCT review,
+    non-linear memory section).  Returns ``[B,H]``."""
+    K, V, eta, W = map(_f64, (K, V, eta, W))
+    pred = np.matmul(K, W)                      # f_W(k_i) = k_i W
+    return -np.sum(eta * np.sum(pred * V, axis=-1), axis=-1)
+
+
+def linear_binding_grad(K, V, eta, W=None):
+    """Gradient of :func:`linear_binding_loss` with respect to W.
+
+    d/dW_{ab} of ``-sum_i eta_i sum_j (sum_a k_ia W_aj) v_ij`` is
+    ``-sum_i eta_i k_ia v_ib``: it does not depend on W.  Returned as
+    ``[B,H,d_k,d_v]``."""
+    K, V, eta = map(_f64, (K, V, eta))
+    return -np.matmul(np.swapaxes(K * eta[..., None], -1, -2), V)
+
+
+def silu(a):
+    """SiLU ``a * sigmoid(a)``."""
+    return a / (1.0 + np.exp(-a))
+
+
+def silu_prime(a):
+    """Derivative of SiLU: ``s (1 + a (1 - s))`` with ``s = sigmoid(a)``."""
+    s = 1.0 / (1.0 + np.exp(-a))
+    return s * (1.0 + a * (1.0 - s))
+
+
+def swiglu_forward(X, W1, W3, W2):
+    """SwiGLU fast-weight MLP ``f_W(x) = (silu(x W1) * (x W3)) W2`` (LaCT
+    review: the usual memory is a SwiGLU MLP with three matrices)."""
+    X, W1, W3, W2 = map(_f64, (X, W1, W3, W2))
+    return np.matmul(silu(np.matmul(X, W1)) * np.matmul(X, W3), W2)
+
+
+def swiglu_binding_loss(K, V, eta, W1, W3, W2):
+    """``sum_i eta_i * (-<f_W(k_i), v_i>)`` per (b, h), returns ``[B,H]``."""
+    pred = swiglu_forward(K, W1, W3, W2)
+    return -np.sum(_f64(eta) * np.sum(pred * _f64(V), axis=-1), axis=-1)
+
+
+def swiglu_binding_grad(K, V, eta, W1, W3, W2):
+    """Hand-derived gradient of :func:`swiglu_binding_loss`.
+
+    With ``a = k W1``, ``b = k W3``, ``h = silu(a) * b`` and ``y = h W2``,
+    the loss is ``-sum_i eta_i <y_i, v_i>``.  Back-propagation by hand:
+    ``dL/dy_i = -eta_i v_i``; ``dL/dW2 = sum_i h_i^T dL/dy_i``;
+    ``dL/dh_i = dL/dy_i W2^T``; ``dL/da_i = dL/dh_i * b_i * silu'(a_i)``;
+    ``dL/db_i = dL/dh_i * silu(a_i)``; ``dL/dW1 = sum_i k_i^T dL/da_i``;
+    ``dL/dW3 = sum_i k_i^T dL/db_i``.  Returns (dW1, dW3, dW2)."""
+    K, V, eta, W1, W3, W2 = map(_f64, (K, V, eta, W1, W3, W2))
+    a = np.matmul(K, W1)
+    b = np.matmul(K, W3)
+    h = silu(a) * b
+    dy = -eta[..., None] * V
+    dW2 = np.matmul(np.swapaxes(h, -1, -2), dy)
+    dh = np.matmul(dy, np.swapaxes(W2, -1, -2))
+    da = dh * b * silu_prime(a)
+    db = dh * silu(a)
+    Kt = np.swapaxes(K, -1, -2)
+    return np.matmul(Kt, da), np.matmul(Kt, db), dW2
+
+
+def normalize_columns(W):
+    """Give every column (one output unit's fan-in vector over the
+    second-to-last axis) unit L2 norm, dividing by ``max(norm, 1e-12)``
+    (LaCT review: L2 normalisation after the weight update)."""
+    n = np.sqrt(np.sum(W * W, axis=-2, keepdims=True))
+    return W / np.maximum(n, NORM_EPS)
+
+
+# ---------------------------------------------------------------------------
+# The three forward modes
+# ---------------------------------------------------------------------------
+
+def per_token_linear(Q, K, V, eta, W0, inclusive=True):
+    """Per-token TTT with a linear fast weight: for t = 0..T-1 take one
+    gradient step on token t's binding loss, and let q_t read the memory
+    (after the step when ``inclusive``, else before it).
+
+    Paper summary, technical section 2B (TTT rewritten exactly as learned
+    linear attention); podcast at 7:50 (output is the query times a running
+    sum of key-value products).  Returns (O ``[B,H,T,d_v]``, W_T)."""
+    Q, K, V, eta, W = map(_f64, (Q, K, V, eta, W0))
+    W = W.copy()
+    B, H, T, _ = Q.shape
+    O = np.zeros(Q.shape[:-1] + (V.shape[-1],))
+    for t in range(T):
+        k = K[:, :, t:t + 1, :]
+        v = V[:, :, t:t + 1, :]
+        e = eta[:, :, t:t + 1]
+        if not inclusive:
+            O[:, :, t, :] = np.matmul(Q[:, :, t:t + 1, :], W)[:, :, 0, :]
+        g = linear_binding_grad(k, v, np.ones_like(e))   # -k_t^T v_t
+        W = W - e[..., None] * g                          # GD step, rate eta_t
+        if inclusive:
+            O[:, :, t, :] = np.matmul(Q[:, :, t:t + 1, :], W)[:, :, 0, :]
+    return O, W
+
+
+def large_chunk_linear(Q, K, V, eta, W0, chunk, normalize=True):
+    """LaCT with a linear fast weight.  For each chunk (the last may be
+    shorter): every query of the chunk reads W (the state left by earlier
+    chunks); then W takes one step on the chunk's summed, eta-weighted
+    binding loss; then each output unit's fan-in is L2-normalised.
+
+    LaCT review: fast-weights section (one update per large chunk),
+    non-linear-memory section (summed per-token-rate gradients, L2
+    normalisation after the update), read-order section (a chunk reads
+    the memory of earlier chunks and only then updates it).
+    ``normalize=False`` is an oracle-only switch used by the pins."""
+    Q, K, V, eta, W = map(_f64, (Q, K, V, eta, W0))
+    W = W.copy()
+    T = Q.shape[2]
+    O = np.zeros(Q.shape[:-1] + (V.shape[-1],))
+    for s in range(0, T, chunk):
+        e = min(s + chunk, T)
+        O[:, :, s:e, :] = np.matmul(Q[:, :, s:e, :], W)
+        g = linear_binding_grad(K[:, :, s:e, :], V[:, :, s:e, :], eta[:, :, s:e])
+        W = W - g
+        if normalize:
+            W = normalize_columns(W)
+    return O, W
+
+
+def large_chunk_swiglu(Q, K, V, eta, W1, W3, W2, chunk, normalize=True,
+                       update_w1w3=True):
+    """LaCT with a SwiGLU fast-weight MLP.  For each chunk: the chunk's
+    queries read ``f_W``; the eta-weighted binding-loss gradient of the
+    chunk is taken at those same weights; one descent step is applied to
+    W1, W3, W2; then each output unit is L2-normalised (W1, W3 columns over
+    d, W2 columns over d_h).
+
+    LaCT review, non-linear memory and read-order sections.
+    ``normalize=False`` and ``update_w1w3=False`` are oracle-only switches
+    used by the pins.  Returns (O, (W1, W3, W2))."""
+    Q, K, V, eta, W1, W3, W2 = map(_f64, (Q, K, V, eta, W1, W3, W2))
+    W1, W3, W2 = W1.copy(), W3.copy(), W2.copy()
+    T = Q.shape[2]
+    O = np.zeros(Q.shape[:-1] + (W2.shape[-1],))
+    for s in range(0, T, chunk):
+        e = min(s + chunk, T)
+        O[:, :, s:e, :] = swiglu_forward(Q[:, :, s:e, :], W1, W3, W2)
+        g1, g3, g2 = swiglu_binding_grad(K[:, :, s:e, :], V[:, :, s:e, :],
+                                         eta[:, :, s:e], W1, W3, W2)
+        if update_w1w3:
+            W1 = W1 - g1
+            W3 = W3 - g3
+        W2 = W2 - g2
+        if normalize:
+            if update_w1w3:
+                W1 = normalize_columns(W1)
+                W3 = normalize_columns(W3)
+            W2 = normalize_columns(W2)
+    return O, (W1, W3, W2)
+
+
+# ---------------------------------------------------------------------------
+# Packing helpers for the SwiGLU state buffer [B,H] x (W1 | W3 | W2)
+# ---------------------------------------------------------------------------
+
+def swiglu_pack(W1, W3, W2):
+    """Concatenate per-head (W1 [d,d_h], W3 [d,d_h], W2 [d_h,d]) row-major
+    into one ``[B,H,3*d*d_h]`` array (the state buffer layout)."""
+    B, H = W1.shape[:2]
+    return np.concatenate([W1.reshape(B, H, -1), W3.reshape(B, H, -1),
+                           W2.reshape(B, H, -1)], axis=-1)
+
+
+def swiglu_unpack(Wp, d, d_h):
+    """Inverse of :func:`swiglu_pack`."""
+    B, H = Wp.shape[:2]
+    n = d * d_h
+    return (Wp[..., :n].reshape(B, H, d, d_h), Wp[..., n:2 * n].reshape(B, H, d, d_h),
+            Wp[..., 2 * n:].reshape(B, H, d_h, d))
+
+
+def forward(Q, K, V, eta, W0, chunk, mode, d_h=None):
+    """Dispatch by mode name, with the library's argument order.
+
+    ``mode``: "per_token_linear", "large_chunk_linear" or
+    "large_chunk_swiglu".  For per-token mode ``chunk`` does not change the
+    result and is ignored.  For SwiGLU, W0 is the packed state and ``d_h``
+    is required.  Returns (O, W_final) with W_final in W0's layout."""
+    if mode == "per_token_linear":
+        return per_token_linear(Q, K, V, eta, W0)
+    if mode == "large_chunk_linear":
+        return large_chunk_linear(Q, K, V, eta, W0, chunk)
+    if mode == "large_chunk_swiglu":
+        d = Q.shape[-1]
+        W1, W3, W2 = swiglu_unpack(_f64(W0), d, d_h)
+        O, (W1, W3, W2) = large_chunk_swiglu(Q, K, V, eta, W1, W3, W2, chunk)
+        return O, swiglu_pack(W1, W3, W2)
+    raise ValueError(f"unknown mode {mode!r}")
