@@ -1,0 +1,146 @@
+/*
+ * libttt_la - forward pass of a test-time-training (TTT) layer with
+ * key-value binding, for AMD Instinct MI355X (gfx950).
+ *
+ * The method (pages on "Test-Time Training with KV Binding Is Secretly
+ * Linear Attention", paper summary technical sections 2B and 3, and the
+ * LaCT review "Test-Time Training Done Right", sections on fast weights,
+ * non-linear memory and read order):
+ *
+ *   A fast weight W (a linear map, or a SwiGLU MLP) is trained at inference
+ *   time by gradient descent on the binding loss -<f_W(k_i), v_i> with a
+ *   per-token learning rate eta_i, and read by queries q_i.
+ *
+ *   TTT_LA_PER_TOKEN_LINEAR: one step per token, read after the step:
+ *       o_t = q_t (W0 + sum_{i<=t} eta_i k_i^T v_i),
+ *       W_out = W0 + sum_i eta_i k_i^T v_i.
+ *     This is causal linear attention without softmax or scaling; it is
+ *     computed in chunked parallel form.  `chunk` only selects the tile
+ *     length of that form: results do not depend on it beyond rounding.
+ *
+ *   TTT_LA_LARGE_CHUNK_LINEAR: for each chunk of `chunk` tokens (the last
+ *     may be shorter): O_c = Q_c W; W <- W + K_c^T diag(eta_c) V_c; then
+ *     every column of W (one output unit's fan-in) is divided by
+ *     max(||column||_2, 1e-12).  W0 itself is not normalised.
+ *
+ *   TTT_LA_LARGE_CHUNK_SWIGLU: f_W(x) = (silu(x W1) * (x W3)) W2.  For each
+ *     chunk: O_c = f_W(Q_c); the gradient G of sum_{i in c} eta_i
+ *     (-<f_W(k_i), v_i>) is taken at those same weights; W <- W - G for
+ *     W1, W3, W2; then columns of W1 and W3 (over d) and of W2 (over d_h)
+ *     are divided by max(norm, 1e-12).
+ *
+ * Conventions: row vectors, W stored [d_in, d_out] row-major; every tensor
+ * contiguous with the last dimension fastest.
+ *
+ * Threading and ownership: every pointer is caller-owned device memory
+ * (except `desc`, host memory, read during the call only).  The library
+ * allocates nothing, frees nothing and never synchronises: work is enqueued
+ * on `stream` and the call returns.  It keeps no global state and may be
+ * called from several host threads.
+ */
+#ifndef TTT_LA_H
+#define TTT_LA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes returned by every entry point. */
+enum {
+    TTT_LA_OK = 0,
+    TTT_LA_ERR_NULL = 1,        /* a required pointer is NULL                        */
+    TTT_LA_ERR_SHAPE = 2,       /* negative or zero size where one is required,       */
+                                /* or d_k != d_v where the mode needs them equal      */
+    TTT_LA_ERR_CHUNK = 3,       /* chunk < 1                                          */
+    TTT_LA_ERR_DTYPE = 4,       /* io_dtype is not one of ttt_la_dtype                */
+    TTT_LA_ERR_MODE = 5,        /* mode is not one of ttt_la_mode                     */
+    TTT_LA_ERR_UNSUPPORTED = 6, /* valid arguments that no compiled kernel covers     */
+    TTT_LA_ERR_ALIAS = 7,       /* an output overlaps an input or another output      */
+    TTT_LA_ERR_WORKSPACE = 8,   /* workspace smaller than ttt_la_workspace_bytes()    */
+    TTT_LA_ERR_HIP = 9          /* a kernel launch failed (hipGetLastError)           */
+};
+
+/* Modes. */
+enum {
+    TTT_LA_PER_TOKEN_LINEAR = 0,
+    TTT_LA_LARGE_CHUNK_LINEAR = 1,
+    TTT_LA_LARGE_CHUNK_SWIGLU = 2
+};
+
+/* Element type of Q, K, V and O.  eta and the fast-weight state are always
+ * float32. */
+enum {
+    TTT_LA_FP32 = 0,
+    TTT_LA_BF16 = 1
+};
+
+/* Problem description.  d_h is the SwiGLU hidden width (ignored by the
+ * linear modes).  io_dtype is TTT_LA_FP32 or TTT_LA_BF16. */
+typedef struct ttt_la_desc {
+    int64_t B, H, T, d_k, d_v, d_h;
+    int32_t io_dtype;
+    int32_t reserved; /* must be 0 */
+} ttt_la_desc;
+
+/*
+ * ttt_la_forward(Q, K, V, eta, W0, chunk, mode) -> (O, W_out)
+ *
+ *   Q, K   [B,H,T,d_k]  io_dtype, device
+ *   V      [B,H,T,d_v]  io_dtype, device
+ *   eta    [B,H,T]      float32,  device; any sign (negative = ascent)
+ *   W0     initial fast weights, float32, device:
+ *            linear modes  [B,H,d_k,d_v]
+ *            SwiGLU        [B,H, d*d_h + d*d_h + d_h*d] = W1 [d,d_h] | W3 [d,d_h] | W2 [d_h,d]
+ *                          per (b,h), with d = d_k = d_v
+ *   chunk  tokens per chunk (>= 1)
+ *   mode   TTT_LA_PER_TOKEN_LINEAR | TTT_LA_LARGE_CHUNK_LINEAR | TTT_LA_LARGE_CHUNK_SWIGLU
+ *   desc   sizes and io_dtype (host pointer)
+ *   O      [B,H,T,d_v]  io_dtype, device (written)
+ *   W_out  same layout as W0, float32, device (written); W_out == W0 (in
+ *          place) is allowed, any other overlap between an output and an
+ *          input, or between O, W_out and the workspace, is ERR_ALIAS
+ *   workspace, workspace_bytes
+ *          device scratch of at least ttt_la_workspace_bytes(desc, chunk,
+ *          mode) bytes (may be NULL when that is 0); its contents on entry
+ *          do not matter and are undefined on return
+ *   stream hipStream_t to enqueue on (NULL = the default stream)
+ *
+ * Supported set (ERR_UNSUPPORTED otherwise):
+ *   per-token:    d_k = d_v in {64, 128}; bf16 or fp32; chunk in
+ *                 {16, 32, 64, 128} (the bf16 kernel always works in
+ *                 64-token tiles, the fp32 kernel in tiles of `chunk`
+ *                 tokens and needs chunk <= 64);
+ *   large-chunk linear: d_k = d_v in {64, 128}; bf16 or fp32; any chunk;
+ *   large-chunk SwiGLU: d = 128, d_h = 256; bf16; any chunk.
+ *   T = 0 is accepted: O is empty and W_out = W0.
+ *
+ * Every argument is checked before anything is enqueued: on any error
+ * nothing is written and no HIP call is made, except that ERR_HIP reports
+ * a failed launch after earlier kernels of the same call were enqueued.
+ */
+int ttt_la_forward(const void* Q, const void* K, const void* V, const float* eta,
+                   const float* W0, int64_t chunk, int32_t mode, const ttt_la_desc* desc,
+                   void* O, float* W_out, void* workspace, size_t workspace_bytes,
+                   void* stream);
+
+/* Bytes of device workspace ttt_la_forward needs for this problem (0 if
+ * none).  Returns 0 as well for invalid arguments (ttt_la_forward reports
+ * those). */
+size_t ttt_la_workspace_bytes(const ttt_la_desc* desc, int64_t chunk, int32_t mode);
+
+/* Static, NUL-terminated description of a status code. */
+const char* ttt_la_status_string(int status);
+
+/* ABI version of this header (incremented on incompatible change). */
+int ttt_la_abi_version(void);
+
+#define TTT_LA_ABI_VERSION 1
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TTT_LA_H */

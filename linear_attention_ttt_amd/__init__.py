@@ -1,0 +1,143 @@
+"""Python binding of libttt_la (TTT-with-KV-binding forward pass on MI355X).
+
+Argument marshalling only: PyTorch supplies device memory and the current
+stream; every step of the computation runs in the library's HIP kernels.
+There is no CPU fallback: if ``libttt_la.so`` is missing the calls raise.
+
+    O, W_out = forward(Q, K, V, eta, W0, chunk, mode)
+
+``mode`` is "per_token_linear", "large_chunk_linear" or
+"large_chunk_swiglu" (or the integer constant).  Shapes, layouts and the
+supported set are those of ``include/ttt_la.h``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = ["forward", "workspace_bytes", "TTTLAError", "MODES", "Desc", "lib", "library_path",
+           "PER_TOKEN_LINEAR", "LARGE_CHUNK_LINEAR", "LARGE_CHUNK_SWIGLU"]
+
+PER_TOKEN_LINEAR = 0
+LARGE_CHUNK_LINEAR = 1
+LARGE_CHUNK_SWIGLU = 2
+MODES = {"per_token_linear": PER_TOKEN_LINEAR, "large_chunk_linear": LARGE_CHUNK_LINEAR,
+         "large_chunk_swiglu": LARGE_CHUNK_SWIGLU}
+FP32, BF16 = 0, 1
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+library_path = os.path.join(_HERE, "libttt_la.so")
+
+
+class TTTLAError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"ttt_la error {status}: {msg}")
+        self.status = status
+
+
+class Desc(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int64), ("H", ctypes.c_int64), ("T", ctypes.c_int64),
+                ("d_k", ctypes.c_int64), ("d_v", ctypes.c_int64), ("d_h", ctypes.c_int64),
+                ("io_dtype", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
+_LIB = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libttt_la.so (built in-tree); raises if it has not been built."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(library_path):
+            raise RuntimeError(f"{library_path} is missing: build it with "
+                               "`python -m linear_attention_ttt_amd.build` (needs ROCm hipcc)")
+        L = ctypes.CDLL(library_path)
+        vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+        L.ttt_la_forward.argtypes = [vp, vp, vp, vp, vp, i64, i32, ctypes.POINTER(Desc), vp, vp, vp,
+                                     ctypes.c_size_t, vp]
+        L.ttt_la_forward.restype = ctypes.c_int
+        L.ttt_la_workspace_bytes.argtypes = [ctypes.POINTER(Desc), i64, i32]
+        L.ttt_la_workspace_bytes.restype = ctypes.c_size_t
+        L.ttt_la_status_string.argtypes = [ctypes.c_int]
+        L.ttt_la_status_string.restype = ctypes.c_char_p
+        L.ttt_la_abi_version.argtypes = []
+        L.ttt_la_abi_version.restype = ctypes.c_int
+        _LIB = L
+    return _LIB
+
+
+def _mode(mode) -> int:
+    return MODES[mode] if isinstance(mode, str) else int(mode)
+
+
+def make_desc(B, H, T, d_k, d_v, d_h=0, io_dtype=BF16) -> Desc:
+    return Desc(B, H, T, d_k, d_v, d_h, io_dtype, 0)
+
+
+def workspace_bytes(desc: Desc, chunk: int, mode) -> int:
+    return int(lib().ttt_la_workspace_bytes(ctypes.byref(desc), int(chunk), _mode(mode)))
+
+
+def status_string(status: int) -> str:
+    return lib().ttt_la_status_string(int(status)).decode()
+
+
+def forward_raw(Q, K, V, eta, W0, chunk, mode, desc: Desc, O, W_out, workspace, workspace_bytes_,
+                stream) -> int:
+    """Call ttt_la_forward with raw integer device addresses; returns the status."""
+    return int(lib().ttt_la_forward(Q, K, V, eta, W0, int(chunk), _mode(mode), ctypes.byref(desc), O, W_out,
+                                    workspace, int(workspace_bytes_), stream))
+
+
+def forward(Q, K, V, eta, W0, chunk: int, mode, *, out=None, W_out=None, workspace=None, stream=None):
+    """Run the TTT forward pass.
+
+    Q, K ``[B,H,T,d_k]`` and V ``[B,H,T,d_v]`` (bfloat16 or float32, same
+    dtype), eta ``[B,H,T]`` float32, W0 float32 (``[B,H,d_k,d_v]`` for the
+    linear modes, ``[B,H,3*d*d_h]`` packed W1|W3|W2 for SwiGLU), all
+    contiguous CUDA tensors on one device.  Returns ``(O, W_out)``.
+    Passing ``W_out=W0`` updates the state in place."""
+    import torch
+
+    m = _mode(mode)
+    tensors = dict(Q=Q, K=K, V=V, eta=eta, W0=W0)
+    dev = Q.device
+    for name, t in tensors.items():
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name} must be a torch.Tensor")
+        if t.device != dev or dev.type != "cuda":
+            raise ValueError(f"{name} must be on the same CUDA device as Q")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if Q.dtype not in (torch.bfloat16, torch.float32) or K.dtype != Q.dtype or V.dtype != Q.dtype:
+        raise ValueError("Q, K, V must share dtype bfloat16 or float32")
+    if eta.dtype != torch.float32 or W0.dtype != torch.float32:
+        raise ValueError("eta and W0 must be float32")
+    if Q.dim() != 4 or K.shape != Q.shape or V.dim() != 4 or V.shape[:3] != Q.shape[:3]:
+        raise ValueError("Q, K must be [B,H,T,d_k] and V [B,H,T,d_v]")
+    B, H, T, dk = Q.shape
+    dv = V.shape[3]
+    if tuple(eta.shape) != (B, H, T):
+        raise ValueError("eta must be [B,H,T]")
+    dh = 0
+    if m == LARGE_CHUNK_SWIGLU:
+        if W0.dim() != 3 or tuple(W0.shape[:2]) != (B, H) or W0.shape[2] % (3 * dk) != 0:
+            raise ValueError("SwiGLU W0 must be [B,H,3*d*d_h]")
+        dh = W0.shape[2] // (3 * dk)
+    elif tuple(W0.shape) != (B, H, dk, dv):
+        raise ValueError("W0 must be [B,H,d_k,d_v]")
+    desc = make_desc(B, H, T, dk, dv, dh, BF16 if Q.dtype == torch.bfloat16 else FP32)
+    O = out if out is not None else torch.empty((B, H, T, dv), dtype=Q.dtype, device=dev)
+    Wo = W_out if W_out is not None else torch.empty_like(W0)
+    nbytes = workspace_bytes(desc, chunk, m)
+    ws = workspace
+    if nbytes > 0 and (ws is None or ws.numel() * ws.element_size() < nbytes):
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    ws_ptr = ws.data_ptr() if (ws is not None and nbytes > 0) else None
+    ws_len = ws.numel() * ws.element_size() if ws_ptr else 0
+    st = stream if stream is not None else torch.cuda.current_stream(dev).cuda_stream
+    status = forward_raw(Q.data_ptr(), K.data_ptr(), V.data_ptr(), eta.data_ptr(), W0.data_ptr(), chunk, m,
+                         desc, O.data_ptr(), Wo.data_ptr(), ws_ptr, ws_len, st)
+    if status != 0:
+        raise TTTLAError(status, status_string(status))
+    return O, Wo

@@ -1,0 +1,96 @@
+// Device helpers shared by the gfx950 kernels: vector types, bf16
+// conversion, MFMA wrappers, LDS transpose reads, direct-to-LDS loads and
+// explicit wait counters.
+//
+// MFMA lane layouts (verified on gfx950):
+//   v_mfma_f32_16x16x32_bf16: A[16][32]: lane l holds A[l%16][8*(l/16)+j], j<8
+//                             B[32][16]: lane l holds B[8*(l/16)+j][l%16]
+//                             D[16][16]: lane l holds D[4*(l/16)+r][l%16], r<4
+//   v_mfma_f32_32x32x16_bf16: A: A[l%32][8*(l/32)+j]; B: B[8*(l/32)+j][l%32]
+//                             D: reg i of lane l = D[8*(i/4)+4*(l/32)+i%4][l%32]
+//   v_mfma_f32_16x16x4_f32:   A: A[l%16][l/16]; B: B[l/16][l%16]; D as 16x16.
+// ds_read_b64_tr_b16 (per 16-lane group, each lane addressing 8 bytes):
+//   lane i receives element (i%4) of the 8 bytes read by lanes 4*e + i/4,
+//   for e = 0..3.  So if lane L of the group addresses row (r0 + L/4),
+//   columns (c0 + 4*(L%4)) .. +3 of a row-major 16-bit matrix, lane i gets
+//   column c0 + i of rows r0..r0+3: a transposed 4x16 block.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ttt {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short short4v __attribute__((ext_vector_type(4)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) short4v lds_short4;
+
+constexpr int WAVE = 64;
+
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+__device__ __forceinline__ floatx4 mfma16(const bf16x8& a, const bf16x8& b, const floatx4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ floatx16 mfma32(const bf16x8& a, const bf16x8& b, const floatx16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ floatx4 mfma16_f32(float a, float b, const floatx4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// Transposed 4x16 read of 16-bit elements from LDS (see header comment).
+__device__ __forceinline__ bf16x4 lds_read_tr16(const void* p) {
+  short4v v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)(uintptr_t)(p));
+  return __builtin_bit_cast(bf16x4, v);
+}
+
+__device__ __forceinline__ bf16x8 join(const bf16x4& lo, const bf16x4& hi) {
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// Asynchronous 16-byte global -> LDS copy.  `lds_wave_base` must be uniform
+// across the wave; lane l's 16 bytes land at lds_wave_base + 16*l.
+__device__ __forceinline__ void g2lds16(const void* gsrc, void* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds(gsrc, (lds_void*)(uintptr_t)lds_wave_base, 16, 0, 0);
+}
+// 4-byte variant: lane l's 4 bytes land at lds_wave_base + 4*l.
+__device__ __forceinline__ void g2lds4(const void* gsrc, void* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds(gsrc, (lds_void*)(uintptr_t)lds_wave_base, 4, 0, 0);
+}
+
+// s_waitcnt vmcnt(N) (other counters untouched) followed by a workgroup
+// barrier.  The "memory" clobber keeps the compiler from moving LDS or
+// global accesses across it.
+template <int N>
+__device__ __forceinline__ void wait_vm_barrier() {
+  static_assert(N >= 0 && N < 64, "vmcnt out of range");
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt out of range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+__device__ __forceinline__ void barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+__device__ __forceinline__ bf16x4 to_bf16x4(float a, float b, float c, float d) {
+  bf16x4 r;
+  r[0] = (bf16)a; r[1] = (bf16)b; r[2] = (bf16)c; r[3] = (bf16)d;
+  return r;
+}
+
+// Map a flat block index to a logical index such that consecutive logical
+// indices share an XCD (blocks are dispatched round-robin over 8 XCDs).
+// Requires nblocks % 8 == 0.
+__device__ __forceinline__ int xcd_logical_block(int b, int nblocks) {
+  const int per = nblocks >> 3;
+  return (b & 7) * per + (b >> 3);
+}
+
+}  // namespace ttt

@@ -1,0 +1,151 @@
+// C-ABI entry points of libttt_la: argument validation, workspace sizing
+// and dispatch to the gfx950 kernels.  Every check runs before the first
+// HIP call, so an invalid call enqueues nothing and writes nothing.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/ttt_la.h"
+#include "kernels.h"
+
+namespace {
+
+struct Range {
+  uintptr_t lo, hi;  // [lo, hi)
+};
+
+Range range(const void* p, size_t bytes) {
+  uintptr_t a = (uintptr_t)p;
+  return Range{a, a + (p ? bytes : 0)};
+}
+
+bool overlap(Range a, Range b) {
+  if (a.lo == a.hi || b.lo == b.hi) return false;
+  return a.lo < b.hi && b.lo < a.hi;
+}
+
+bool mul_ok(int64_t a, int64_t b, int64_t* out) {
+  if (a < 0 || b < 0) return false;
+  if (a != 0 && b > INT64_MAX / a) return false;
+  *out = a * b;
+  return true;
+}
+
+int64_t state_elems(const ttt_la_desc& d, int mode) {
+  if (mode == TTT_LA_LARGE_CHUNK_SWIGLU) return d.B * d.H * 3 * d.d_k * d.d_h;
+  return d.B * d.H * d.d_k * d.d_v;
+}
+
+// Shape, mode, dtype and chunk checks shared by forward and workspace sizing.
+int check_problem(const ttt_la_desc* d, int64_t chunk, int32_t mode) {
+  if (!d) return TTT_LA_ERR_NULL;
+  if (mode != TTT_LA_PER_TOKEN_LINEAR && mode != TTT_LA_LARGE_CHUNK_LINEAR && mode != TTT_LA_LARGE_CHUNK_SWIGLU)
+    return TTT_LA_ERR_MODE;
+  if (d->io_dtype != TTT_LA_FP32 && d->io_dtype != TTT_LA_BF16) return TTT_LA_ERR_DTYPE;
+  if (d->reserved != 0) return TTT_LA_ERR_SHAPE;
+  if (d->B < 1 || d->H < 1 || d->T < 0 || d->d_k < 1 || d->d_v < 1) return TTT_LA_ERR_SHAPE;
+  if (mode == TTT_LA_LARGE_CHUNK_SWIGLU && (d->d_h < 1 || d->d_k != d->d_v)) return TTT_LA_ERR_SHAPE;
+  int64_t x;
+  const int64_t dmax = d->d_k > d->d_v ? d->d_k : d->d_v;
+  if (!mul_ok(d->B, d->H, &x) || !mul_ok(x, d->T, &x) || !mul_ok(x, dmax, &x) || !mul_ok(x, 4, &x))
+    return TTT_LA_ERR_SHAPE;
+  if (mode == TTT_LA_LARGE_CHUNK_SWIGLU &&
+      (!mul_ok(d->B * d->H, 3 * d->d_k, &x) || !mul_ok(x, d->d_h, &x) || !mul_ok(x, 4, &x)))
+    return TTT_LA_ERR_SHAPE;
+  if (chunk < 1) return TTT_LA_ERR_CHUNK;
+  return TTT_LA_OK;
+}
+
+bool supported(const ttt_la_desc& d, int64_t chunk, int32_t mode) {
+  if (d.T > INT32_MAX || d.B * d.H > (int64_t)1 << 24) return false;
+  switch (mode) {
+    case TTT_LA_PER_TOKEN_LINEAR:
+      return ttt::per_token_supported(d.d_k, d.d_v, chunk, d.io_dtype);
+    case TTT_LA_LARGE_CHUNK_LINEAR:
+      return ttt::large_chunk_linear_supported(d.d_k, d.d_v, chunk, d.io_dtype);
+    case TTT_LA_LARGE_CHUNK_SWIGLU:
+      return ttt::large_chunk_swiglu_supported(d.d_k, d.d_h, chunk, d.io_dtype);
+  }
+  return false;
+}
+
+size_t workspace_for(const ttt_la_desc& d, int64_t chunk, int32_t mode) {
+  switch (mode) {
+    case TTT_LA_LARGE_CHUNK_LINEAR:
+      return ttt::large_chunk_linear_workspace(d.B, d.H, d.T, d.d_k, d.d_v, chunk);
+    case TTT_LA_LARGE_CHUNK_SWIGLU:
+      return ttt::large_chunk_swiglu_workspace(d.B, d.H, d.T, d.d_k, d.d_h, chunk);
+  }
+  return 0;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ttt_la_abi_version(void) { return TTT_LA_ABI_VERSION; }
+
+const char* ttt_la_status_string(int s) {
+  switch (s) {
+    case TTT_LA_OK: return "ok";
+    case TTT_LA_ERR_NULL: return "a required pointer is NULL";
+    case TTT_LA_ERR_SHAPE: return "invalid shape";
+    case TTT_LA_ERR_CHUNK: return "chunk must be >= 1";
+    case TTT_LA_ERR_DTYPE: return "io_dtype is not TTT_LA_FP32 or TTT_LA_BF16";
+    case TTT_LA_ERR_MODE: return "unknown mode";
+    case TTT_LA_ERR_UNSUPPORTED: return "no compiled kernel supports this shape, dtype or chunk";
+    case TTT_LA_ERR_ALIAS: return "an output overlaps an input or another output";
+    case TTT_LA_ERR_WORKSPACE: return "workspace too small";
+    case TTT_LA_ERR_HIP: return "HIP kernel launch failed";
+  }
+  return "unknown status";
+}
+
+size_t ttt_la_workspace_bytes(const ttt_la_desc* desc, int64_t chunk, int32_t mode) {
+  if (check_problem(desc, chunk, mode) != TTT_LA_OK) return 0;
+  if (!supported(*desc, chunk, mode)) return 0;
+  return workspace_for(*desc, chunk, mode);
+}
+
+int ttt_la_forward(const void* Q, const void* K, const void* V, const float* eta, const float* W0,
+                   int64_t chunk, int32_t mode, const ttt_la_desc* desc, void* O, float* W_out,
+                   void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_problem(desc, chunk, mode);
+  if (st != TTT_LA_OK) return st;
+  const ttt_la_desc d = *desc;
+  const bool have_tokens = d.T > 0;
+  if (!W0 || !W_out) return TTT_LA_ERR_NULL;
+  if (have_tokens && (!Q || !K || !V || !eta || !O)) return TTT_LA_ERR_NULL;
+  if (!supported(d, chunk, mode)) return TTT_LA_ERR_UNSUPPORTED;
+  const size_t need = workspace_for(d, chunk, mode);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return TTT_LA_ERR_WORKSPACE;
+
+  const size_t es = d.io_dtype == TTT_LA_BF16 ? 2 : 4;
+  const size_t ntok = (size_t)(d.B * d.H * d.T);
+  const Range rQ = range(Q, ntok * d.d_k * es), rK = range(K, ntok * d.d_k * es);
+  const Range rV = range(V, ntok * d.d_v * es), rE = range(eta, ntok * 4);
+  const Range rW0 = range(W0, (size_t)state_elems(d, mode) * 4);
+  const Range rO = range(O, ntok * d.d_v * es);
+  const Range rWo = range(W_out, (size_t)state_elems(d, mode) * 4);
+  const Range rWs = range(workspace, need);
+  const Range ins[5] = {rQ, rK, rV, rE, rW0};
+  for (const Range& in : ins) {
+    if (overlap(rO, in) || overlap(rWs, in)) return TTT_LA_ERR_ALIAS;
+  }
+  for (int i = 0; i < 4; ++i)
+    if (overlap(rWo, ins[i])) return TTT_LA_ERR_ALIAS;
+  if (overlap(rWo, rW0) && W_out != W0) return TTT_LA_ERR_ALIAS;
+  if (overlap(rO, rWo) || overlap(rO, rWs) || overlap(rWo, rWs)) return TTT_LA_ERR_ALIAS;
+
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = hipSuccess;
+  if (mode == TTT_LA_PER_TOKEN_LINEAR) {
+    ttt::PerTokenArgs a{Q, K, V, eta, W0, O, W_out, d.B, d.H, d.T, d.d_k, d.d_v, chunk, d.io_dtype};
+    e = ttt::launch_per_token(a, s);
+  } else {
+    ttt::LargeChunkArgs a{Q, K, V, eta, W0, O, W_out, workspace, d.B, d.H, d.T, d.d_k, d.d_v, d.d_h, chunk, d.io_dtype};
+    e = mode == TTT_LA_LARGE_CHUNK_LINEAR ? ttt::launch_large_chunk_linear(a, s) : ttt::launch_large_chunk_swiglu(a, s);
+  }
+  return e == hipSuccess ? TTT_LA_OK : TTT_LA_ERR_HIP;
+}
+
+}  // extern "C"

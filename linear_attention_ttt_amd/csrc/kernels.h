@@ -1,0 +1,46 @@
+// Internal interface between the C-ABI host layer and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace ttt {
+
+struct PerTokenArgs {
+  const void* Q;
+  const void* K;
+  const void* V;
+  const float* eta;
+  const float* W0;
+  void* O;
+  float* W_out;
+  int64_t B, H, T, DK, DV, chunk;
+  int dtype;  // 0 = fp32, 1 = bf16
+};
+
+bool per_token_supported(int64_t dk, int64_t dv, int64_t chunk, int dtype);
+hipError_t launch_per_token(const PerTokenArgs& a, hipStream_t stream);
+
+struct LargeChunkArgs {
+  const void* Q;
+  const void* K;
+  const void* V;
+  const float* eta;
+  const float* W0;
+  void* O;
+  float* W_out;
+  void* ws;
+  int64_t B, H, T, DK, DV, DH, chunk;
+  int dtype;
+};
+
+bool large_chunk_linear_supported(int64_t dk, int64_t dv, int64_t chunk, int dtype);
+size_t large_chunk_linear_workspace(int64_t B, int64_t H, int64_t T, int64_t dk, int64_t dv, int64_t chunk);
+hipError_t launch_large_chunk_linear(const LargeChunkArgs& a, hipStream_t stream);
+
+bool large_chunk_swiglu_supported(int64_t d, int64_t dh, int64_t chunk, int dtype);
+size_t large_chunk_swiglu_workspace(int64_t B, int64_t H, int64_t T, int64_t d, int64_t dh, int64_t chunk);
+hipError_t launch_large_chunk_swiglu(const LargeChunkArgs& a, hipStream_t stream);
+
+}  // namespace ttt

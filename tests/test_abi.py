@@ -1,0 +1,132 @@
+"""C-ABI tests that need no GPU: the library loads, exports every declared
+symbol, and rejects invalid arguments before touching the device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import linear_attention_ttt_amd as la
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "ttt_la.h")
+
+needs_lib = pytest.mark.skipif(not os.path.exists(la.library_path), reason="libttt_la.so not built")
+
+# Fake, non-overlapping device addresses: validation never dereferences them.
+BASE = 1 << 40
+GAP = 1 << 34
+
+
+def ptr(i):
+    return BASE + i * GAP
+
+
+def call(Q=ptr(0), K=ptr(1), V=ptr(2), eta=ptr(3), W0=ptr(4), chunk=64, mode=0, desc=None, O=ptr(5),
+         W_out=ptr(6), ws=ptr(7), ws_bytes=1 << 33):
+    if desc is None:
+        desc = la.make_desc(1, 2, 128, 64, 64, 0, la.BF16)
+    return la.forward_raw(Q, K, V, eta, W0, chunk, mode, desc, O, W_out, ws, ws_bytes, None)
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(ttt_la_[a-z_]+)\s*\(", src)))
+
+
+@needs_lib
+def test_exports_every_declared_symbol():
+    L = la.lib()
+    names = declared_functions()
+    assert {"ttt_la_forward", "ttt_la_workspace_bytes", "ttt_la_status_string", "ttt_la_abi_version"} <= set(names)
+    for n in names:
+        assert hasattr(L, n), f"{n} not exported"
+
+
+@needs_lib
+def test_version_and_status_strings():
+    assert la.lib().ttt_la_abi_version() == 1
+    for s in range(10):
+        assert la.status_string(s) and la.status_string(s) != "unknown status"
+    assert la.status_string(99) == "unknown status"
+
+
+@needs_lib
+@pytest.mark.parametrize("kw,code", [
+    (dict(Q=None), 1), (dict(K=None), 1), (dict(V=None), 1), (dict(eta=None), 1), (dict(O=None), 1),
+    (dict(W0=None), 1), (dict(W_out=None), 1),
+    (dict(chunk=0), 3), (dict(chunk=-5), 3),
+    (dict(mode=3), 5), (dict(mode=-1), 5),
+])
+def test_invalid_arguments(kw, code):
+    assert call(**kw) == code
+
+
+@needs_lib
+def test_null_desc():
+    L = la.lib()
+    r = L.ttt_la_forward(ptr(0), ptr(1), ptr(2), ptr(3), ptr(4), 64, 0, None, ptr(5), ptr(6), None, 0, None)
+    assert r == 1
+    assert L.ttt_la_workspace_bytes(None, 64, 0) == 0
+
+
+@needs_lib
+@pytest.mark.parametrize("desc,mode,code", [
+    (la.make_desc(0, 1, 8, 64, 64), 0, 2),
+    (la.make_desc(1, 0, 8, 64, 64), 0, 2),
+    (la.make_desc(1, 1, -1, 64, 64), 0, 2),
+    (la.make_desc(1, 1, 8, 0, 64), 0, 2),
+    (la.make_desc(1, 1, 8, 64, 0), 0, 2),
+    (la.make_desc(1, 1, 8, 128, 64, 256), 2, 2),       # SwiGLU needs d_k == d_v
+    (la.make_desc(1, 1, 8, 128, 128, 0), 2, 2),        # SwiGLU needs d_h
+    (la.make_desc(1, 1, 8, 64, 64, 0, 7), 0, 4),       # bad dtype
+    (la.make_desc(1, 1, 8, 96, 96), 0, 6),             # d not compiled
+    (la.make_desc(1, 1, 8, 64, 128), 0, 6),            # d_k != d_v not compiled
+])
+def test_invalid_shapes(desc, mode, code):
+    assert call(desc=desc, mode=mode) == code
+
+
+@needs_lib
+def test_reserved_field_must_be_zero():
+    d = la.make_desc(1, 1, 8, 64, 64)
+    d.reserved = 1
+    assert call(desc=d) == 2
+
+
+@needs_lib
+@pytest.mark.parametrize("chunk,dtype,code", [(48, la.BF16, 6), (256, la.BF16, 6), (128, la.FP32, 6)])
+def test_unsupported_per_token_chunk(chunk, dtype, code):
+    assert call(chunk=chunk, desc=la.make_desc(1, 1, 64, 64, 64, 0, dtype)) == code
+
+
+@needs_lib
+def test_overflowing_sizes_rejected():
+    assert call(desc=la.make_desc(1 << 40, 1 << 40, 8, 64, 64)) == 2
+
+
+@needs_lib
+def test_aliasing_rejected():
+    desc = la.make_desc(1, 2, 128, 64, 64)
+    qbytes = 1 * 2 * 128 * 64 * 2
+    assert call(O=ptr(0), desc=desc) == 7                      # O == Q
+    assert call(O=ptr(1) + qbytes - 2, desc=desc) == 7         # O overlaps the tail of K
+    assert call(W_out=ptr(2) + 16, desc=desc) == 7             # W_out inside V
+    assert call(W_out=ptr(4) + 4, desc=desc) == 7              # partial overlap with W0
+    assert call(W_out=ptr(5), desc=desc) == 7                  # W_out overlaps O
+    # (an adjacent, non-overlapping layout is valid and would launch: not tested here)
+
+
+@needs_lib
+def test_workspace_query_and_check():
+    d = la.make_desc(1, 12, 196608, 64, 64, 0, la.BF16)
+    n = la.workspace_bytes(d, 4096, "large_chunk_linear")
+    if n == 0:
+        pytest.skip("large-chunk linear needs no workspace in this build")
+    assert call(desc=d, mode=1, chunk=4096, ws=None, ws_bytes=0) == 8
+    assert call(desc=d, mode=1, chunk=4096, ws_bytes=n - 1) == 8
+
+
+@needs_lib
+def test_per_token_needs_no_workspace():
+    d = la.make_desc(4, 16, 4096, 128, 128, 0, la.BF16)
+    assert la.workspace_bytes(d, 64, "per_token_linear") == 0
