@@ -113,7 +113,7 @@ typedef struct ttt_la_desc {
  *                 {16, 32, 64, 128} (the bf16 kernel always works in
  *                 64-token tiles, the fp32 kernel in tiles of `chunk`
  *                 tokens and needs chunk <= 64);
- *   large-chunk linear: d_k = d_v in {64, 128}; bf16 or fp32; any chunk;
+ *   large-chunk linear: d_k = d_v in {64, 128}; bf16; any chunk;
  *   large-chunk SwiGLU: d = 128, d_h = 256; bf16; any chunk.
  *   T = 0 is accepted: O is empty and W_out = W0.
  *

@@ -40,6 +40,12 @@ __device__ __forceinline__ floatx4 mfma16(const bf16x8& a, const bf16x8& b, cons
 __device__ __forceinline__ floatx16 mfma32(const bf16x8& a, const bf16x8& b, const floatx16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
+// v_mfma_f32_16x16x16_bf16: A[16][16]: lane l holds A[l%16][4*(l/16)+j], j<4;
+// B[16][16]: B[4*(l/16)+j][l%16]; D as for the 16x16x32 form.
+__device__ __forceinline__ floatx4 mfma16k16(const bf16x4& a, const bf16x4& b, const floatx4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(short4v, a), __builtin_bit_cast(short4v, b), c,
+                                                  0, 0, 0);
+}
 __device__ __forceinline__ floatx4 mfma16_f32(float a, float b, const floatx4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }

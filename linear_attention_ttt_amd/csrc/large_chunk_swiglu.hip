@@ -1,0 +1,559 @@
+// LaCT large-chunk TTT with a SwiGLU fast-weight MLP (LaCT review "Test-Time
+// Training Done Right": the usual memory is a SwiGLU MLP with three
+// matrices; the chunk's gradients of the negative inner-product loss are
+// summed with per-token rates; the weights are L2-normalised after the
+// update; a chunk reads the memory of earlier chunks, then updates it):
+//     f_W(x) = (silu(x W1) * (x W3)) W2
+//     O_c    = f_{W_{c-1}}(Q_c)
+//     W_c    = normalise(W_{c-1} - grad_W sum_{i in c} eta_i (-<f_W(k_i), v_i>))
+// With G = diag(eta) V, A = K W1, B = K W3, H = silu(A) * B, the descent
+// step is  dW2 = H^T G,  dH = G W2^T,  dW1 = K^T (dH * B * silu'(A)),
+// dW3 = K^T (dH * silu(A)); columns of W1, W3 (over d) and of W2 (over
+// d_h) are then divided by max(norm, 1e-12).
+//
+// Two kernels:
+//  * swiglu_recur_kernel (cooperative, sequential over chunks): a head's
+//    hidden units are split into NSL slices of NS units, one workgroup per
+//    slice.  With that split dW1[:, s], dW3[:, s], dW2[s, :] and the W1/W3
+//    normalisation are local to the slice; only the W2 column norms need a
+//    128-float sum across the head's workgroups, exchanged through global
+//    memory with an acquire/release counter.  Each workgroup stores the
+//    weights every chunk reads (bf16 hi + lo planes, transposed for the
+//    read kernel's operands).
+//  * swiglu_read_kernel (fully parallel): O_c = f_{W_{c-1}}(Q_c) for every
+//    (head, chunk, 128-token tile), hidden units in 32-unit slices staged
+//    through LDS; products use the bf16 hi + lo split of the weights and of
+//    H so the only visible rounding is that of the bf16 output.
+#include <algorithm>
+
+#include "device_common.h"
+#include "kernels.h"
+
+namespace ttt {
+
+namespace {
+
+constexpr int SW_D = 128;
+constexpr int SW_DH = 256;
+constexpr int SW_NS = 16;                 // hidden units per recurrence workgroup
+constexpr int SW_NSL = SW_DH / SW_NS;     // workgroups per head
+constexpr int SW_SB = 64;                 // tokens per LDS sub-block
+constexpr int SW_ROW = SW_D * 2 + 32;     // padded bf16 row of K / V in LDS
+constexpr int SW_TT = 128;                // tokens per read workgroup
+constexpr int SW_US = 32;                 // hidden units per read slice
+constexpr int SW_SPIN_LIMIT = 1 << 24;
+constexpr size_t SW_STATE = (size_t)6 * SW_D * SW_DH;  // bf16 elements per stored state
+
+struct RecurLds {
+  unsigned char k[2][SW_SB * SW_ROW];
+  unsigned char v[2][SW_SB * SW_ROW];
+  float eta[2][SW_SB];
+  float w1[SW_D * SW_NS];   // [d][u]
+  float w3[SW_D * SW_NS];   // [d][u]
+  float w2[SW_NS * SW_D];   // [u][d]
+  float red[4][SW_D * SW_NS];
+};
+
+__device__ __forceinline__ void split_store8(bf16* hi, bf16* lo, const float* f) {
+  bf16x8 h, l;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    h[j] = (bf16)f[j];
+    l[j] = (bf16)(f[j] - (float)h[j]);
+  }
+  *(bf16x8*)hi = h;
+  *(bf16x8*)lo = l;
+}
+
+__global__ void zero_u32_kernel(unsigned* p, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
+__global__ __launch_bounds__(256, 1) void swiglu_recur_kernel(
+    const bf16* __restrict__ K, const bf16* __restrict__ V, const float* __restrict__ eta,
+    const float* __restrict__ W0, float* __restrict__ Wout, bf16* __restrict__ states, float* __restrict__ ss2,
+    unsigned* __restrict__ counters, unsigned* __restrict__ errflag, int T, int chunk, int nchunks, int head0) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
+  RecurLds& S = *reinterpret_cast<RecurLds*>(smem_raw);
+  const int nblocks = gridDim.x;
+  const int logical = (nblocks % 8 == 0) ? xcd_logical_block(blockIdx.x, nblocks) : blockIdx.x;
+  const int bh = head0 + logical / SW_NSL;
+  const int sl = logical % SW_NSL;
+  const int u0 = sl * SW_NS;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g = l >> 4, li = l & 15;
+  constexpr int D = SW_D, DH = SW_DH, NS = SW_NS;
+
+  const bf16* Kh = K + (size_t)bh * T * D;
+  const bf16* Vh = V + (size_t)bh * T * D;
+  const float* Eh = eta + (size_t)bh * T;
+  const float* W0h = W0 + (size_t)bh * 3 * D * DH;
+  bf16* St = states + (size_t)bh * nchunks * SW_STATE;
+
+  // ---- load this slice of the initial weights ----
+  for (int i = tid; i < D * NS; i += 256) {
+    const int d = i / NS, u = i % NS;
+    S.w1[i] = W0h[(size_t)d * DH + u0 + u];
+    S.w3[i] = W0h[(size_t)D * DH + (size_t)d * DH + u0 + u];
+  }
+  for (int i = tid; i < NS * D; i += 256) {
+    const int u = i / D, d = i % D;
+    S.w2[i] = W0h[(size_t)2 * D * DH + (size_t)(u0 + u) * D + d];
+  }
+  __syncthreads();
+
+  // the weights chunk `slot` reads: W1^T, W3^T [DH][D] and W2^T [D][DH], bf16 hi + lo
+  auto store_state = [&](int slot) {
+    bf16* base = St + (size_t)slot * SW_STATE;
+    const size_t P = (size_t)D * DH;
+    {
+      const int idx = tid * 8;               // 8 consecutive d of one unit
+      const int u = idx / D, d = idx % D;
+      float f1[8], f3[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        f1[j] = S.w1[(d + j) * NS + u];
+        f3[j] = S.w3[(d + j) * NS + u];
+      }
+      const size_t o = (size_t)(u0 + u) * D + d;
+      split_store8(base + o, base + P + o, f1);
+      split_store8(base + 2 * P + o, base + 3 * P + o, f3);
+    }
+    {
+      const int idx = tid * 8;               // 8 consecutive units of one output dim
+      const int n = idx / NS, u = idx % NS;
+      float f2[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) f2[j] = S.w2[(u + j) * D + n];
+      const size_t o = (size_t)n * DH + u0 + u;
+      split_store8(base + 4 * P + o, base + 5 * P + o, f2);
+    }
+  };
+  if (nchunks > 0) store_state(0);
+
+  // ---- token sub-blocks, prefetched one ahead through registers ----
+  const int nsb = (chunk + SW_SB - 1) / SW_SB;
+  const int last_len = T - (nchunks - 1) * chunk;
+  const int total = nchunks > 0 ? (nchunks - 1) * nsb + (last_len + SW_SB - 1) / SW_SB : 0;
+  uint4 kr[4], vr[4];
+  float er = 0.f;
+  auto load_regs = [&](int gsb) {
+    const int c = gsb / nsb, i = gsb % nsb;
+    const int t0 = c * chunk + i * SW_SB;
+    const int tend = min(c * chunk + chunk, T);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int p = k * 256 + tid;
+      const int row = p >> 4, col = (p & 15) * 8;
+      const int tc = min(t0 + row, tend - 1);
+      kr[k] = *(const uint4*)(Kh + (size_t)tc * D + col);
+      vr[k] = *(const uint4*)(Vh + (size_t)tc * D + col);
+    }
+    if (tid < SW_SB) er = (t0 + tid < tend) ? Eh[min(t0 + tid, tend - 1)] : 0.f;
+  };
+  auto store_regs = [&](int buf) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int p = k * 256 + tid;
+      const int row = p >> 4, col = (p & 15) * 8;
+      *(uint4*)(S.k[buf] + row * SW_ROW + col * 2) = kr[k];
+      *(uint4*)(S.v[buf] + row * SW_ROW + col * 2) = vr[k];
+    }
+    if (tid < SW_SB) S.eta[buf][tid] = er;
+  };
+
+  bf16x8 w1op[4], w3op[4], w2op[4];
+  floatx4 dW1[8], dW3[8], dW2[8];
+  if (total > 0) load_regs(0);
+
+  for (int gsb = 0; gsb < total; ++gsb) {
+    const int c = gsb / nsb, i = gsb % nsb;
+    if (i == 0) {
+      // operands of this chunk's weights (B operands: col = unit li, k = 8 consecutive d)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int d = 32 * ks + 8 * g + j;
+          w1op[ks][j] = (bf16)S.w1[d * NS + li];
+          w3op[ks][j] = (bf16)S.w3[d * NS + li];
+          w2op[ks][j] = (bf16)S.w2[li * D + d];
+        }
+#pragma unroll
+      for (int m = 0; m < 8; ++m) dW1[m] = dW3[m] = dW2[m] = floatx4{0.f, 0.f, 0.f, 0.f};
+    }
+    const int buf = gsb & 1;
+    store_regs(buf);
+    __syncthreads();
+    if (gsb + 1 < total) load_regs(gsb + 1);
+
+    // ---- forward of the 16 tokens of this wave, and the chunk gradient ----
+    const unsigned char* kb = S.k[buf];
+    const unsigned char* vb = S.v[buf];
+    floatx4 A = {0.f, 0.f, 0.f, 0.f}, Bv = A, Dh = A;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int off = (16 * w + li) * SW_ROW + (32 * ks + 8 * g) * 2;
+      const bf16x8 kop = *(const bf16x8*)(kb + off);
+      const bf16x8 vop = *(const bf16x8*)(vb + off);
+      A = mfma16(kop, w1op[ks], A);
+      Bv = mfma16(kop, w3op[ks], Bv);
+      Dh = mfma16(vop, w2op[ks], Dh);
+    }
+    const floatx4 e4 = *(const floatx4*)(&S.eta[buf][16 * w + 4 * g]);
+    bf16x4 daop, dbop, ehop;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float a = A[r], b = Bv[r];
+      const float sg = 1.0f / (1.0f + __expf(-a));
+      const float sa = a * sg;
+      const float dh = e4[r] * Dh[r];
+      daop[r] = (bf16)(dh * b * sg * (1.0f + a * (1.0f - sg)));
+      dbop[r] = (bf16)(dh * sa);
+      ehop[r] = (bf16)(e4[r] * sa * b);
+    }
+    const int trow = (16 * w + 4 * g + (li >> 2)) * SW_ROW;
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      const bf16x4 kt = lds_read_tr16(kb + trow + (16 * m + 4 * (li & 3)) * 2);
+      dW1[m] = mfma16k16(kt, daop, dW1[m]);
+      dW3[m] = mfma16k16(kt, dbop, dW3[m]);
+      const bf16x4 vt = lds_read_tr16(vb + trow + (16 * m + 4 * (li & 3)) * 2);
+      dW2[m] = mfma16k16(ehop, vt, dW2[m]);
+    }
+
+    const bool chunk_end = (i == nsb - 1) || (gsb == total - 1);
+    if (!chunk_end) continue;
+
+    // ---- end of chunk: sum the waves' partial gradients and update ----
+    // dW1 lane layout: [d = 16m + 4g + r][u = li]; dW2: [u = 4g + r][d = 16m + li]
+#pragma unroll
+    for (int m = 0; m < 8; ++m)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) S.red[w][(16 * m + 4 * g + r) * NS + li] = dW1[m][r];
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int idx = tid * 8 + e;
+      S.w1[idx] += S.red[0][idx] + S.red[1][idx] + S.red[2][idx] + S.red[3][idx];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int m = 0; m < 8; ++m)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) S.red[w][(16 * m + 4 * g + r) * NS + li] = dW3[m][r];
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int idx = tid * 8 + e;
+      S.w3[idx] += S.red[0][idx] + S.red[1][idx] + S.red[2][idx] + S.red[3][idx];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int m = 0; m < 8; ++m)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) S.red[w][(4 * g + r) * D + 16 * m + li] = dW2[m][r];
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int idx = tid * 8 + e;
+      S.w2[idx] += S.red[0][idx] + S.red[1][idx] + S.red[2][idx] + S.red[3][idx];
+    }
+    __syncthreads();
+    // W1, W3: unit columns over d, local (waves 0 and 1)
+    if (w < 2) {
+      float* Wm = w == 0 ? S.w1 : S.w3;
+      const int u = l & 15, r0 = (l >> 4) * 32;
+      float ss = 0.f;
+#pragma unroll 8
+      for (int r = 0; r < 32; ++r) ss = fmaf(Wm[(r0 + r) * NS + u], Wm[(r0 + r) * NS + u], ss);
+      ss += __shfl_xor(ss, 16);
+      ss += __shfl_xor(ss, 32);
+      const float inv = 1.0f / fmaxf(sqrtf(ss), 1e-12f);
+#pragma unroll 8
+      for (int r = 0; r < 32; ++r) Wm[(r0 + r) * NS + u] *= inv;
+    } else {
+      // W2 column d: partial sum of squares over this slice's units
+      const int d = (w - 2) * 64 + l;
+      float ss = 0.f;
+#pragma unroll
+      for (int u = 0; u < NS; ++u) ss = fmaf(S.w2[u * D + d], S.w2[u * D + d], ss);
+      __hip_atomic_store(&ss2[(((size_t)bh * 2 + (c & 1)) * SW_NSL + sl) * D + d], ss, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+    if (tid == 0) {
+      __hip_atomic_fetch_add(&counters[bh], 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+      const unsigned target = (unsigned)SW_NSL * (unsigned)(c + 1);
+      int spins = 0;
+      while (__hip_atomic_load(&counters[bh], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) < target) {
+        __builtin_amdgcn_s_sleep(2);
+        if (++spins > SW_SPIN_LIMIT) {
+          __hip_atomic_store(errflag, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          break;
+        }
+      }
+    }
+    __syncthreads();
+    if (w >= 2) {
+      const int d = (w - 2) * 64 + l;
+      float ss = 0.f;
+      for (int s = 0; s < SW_NSL; ++s)
+        ss += __hip_atomic_load(&ss2[(((size_t)bh * 2 + (c & 1)) * SW_NSL + s) * D + d], __ATOMIC_RELAXED,
+                                __HIP_MEMORY_SCOPE_AGENT);
+      const float inv = 1.0f / fmaxf(sqrtf(ss), 1e-12f);
+#pragma unroll
+      for (int u = 0; u < NS; ++u) S.w2[u * D + d] *= inv;
+    }
+    __syncthreads();
+    if (c + 1 < nchunks) store_state(c + 1);
+  }
+
+  // ---- final weights, packed W1 | W3 | W2 ----
+  float* Wo = Wout + (size_t)bh * 3 * D * DH;
+  for (int i = tid; i < D * NS; i += 256) {
+    const int d = i / NS, u = i % NS;
+    Wo[(size_t)d * DH + u0 + u] = S.w1[i];
+    Wo[(size_t)D * DH + (size_t)d * DH + u0 + u] = S.w3[i];
+  }
+  for (int i = tid; i < NS * D; i += 256) {
+    const int u = i / D, d = i % D;
+    Wo[(size_t)2 * D * DH + (size_t)(u0 + u) * D + d] = S.w2[i];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// read: O = f_{W_{c-1}}(Q_c), computed transposed (tokens on the lanes'
+// column index) so that H^T from one product is directly the B operand of
+// the next.
+// ---------------------------------------------------------------------------
+struct ReadLds {
+  unsigned char w13[2][4][SW_US * (SW_D * 2 + 16)];   // W1T hi, W1T lo, W3T hi, W3T lo; padded rows
+  unsigned char w2[2][2][SW_D * (SW_US * 2 + 8)];     // W2T hi, lo: [n][32 units], padded rows
+};
+constexpr int RW13_ROW = SW_D * 2 + 16;
+constexpr int RW2_ROW = SW_US * 2 + 8;
+
+__global__ __launch_bounds__(256, 1) void swiglu_read_kernel(const bf16* __restrict__ Q,
+                                                             const bf16* __restrict__ states, bf16* __restrict__ O,
+                                                             int T, int chunk, int nchunks, int tiles) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
+  ReadLds& L = *reinterpret_cast<ReadLds*>(smem_raw);
+  constexpr int D = SW_D, DH = SW_DH;
+  const int tile = blockIdx.x % tiles;
+  const int c = (blockIdx.x / tiles) % nchunks;
+  const int bh = blockIdx.x / (tiles * nchunks);
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g = l >> 4, li = l & 15;
+  const int cend = min((c + 1) * chunk, T);
+  const int t0 = c * chunk + tile * SW_TT;
+  if (t0 >= cend) return;
+  const bf16* st = states + ((size_t)bh * nchunks + c) * SW_STATE;
+  const size_t P = (size_t)D * DH;
+
+  // this wave's queries as B operands (col = token, k = 8 consecutive d)
+  const bf16* Qh = Q + (size_t)bh * T * D;
+  bf16x8 qop[2][4];
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt) {
+    const int t = min(t0 + 32 * w + 16 * tt + li, cend - 1);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) qop[tt][ks] = *(const bf16x8*)(Qh + (size_t)t * D + 32 * ks + 8 * g);
+  }
+
+  // weight slice staging: 12 x 16 bytes per thread
+  uint4 wr[12];
+  auto load_slice = [&](int s) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {          // W1T/W3T hi/lo planes: 4 x 32 rows x 16 pieces
+      const int p = k * 256 + tid;
+      const int plane = p >> 9, row = (p >> 4) & 31, pc = p & 15;
+      wr[k] = *(const uint4*)(st + (size_t)plane * P + (size_t)(SW_US * s + row) * D + pc * 8);
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {          // W2T hi/lo: 2 x 128 rows x 4 pieces
+      const int p = k * 256 + tid;
+      const int plane = p >> 9, n = (p >> 2) & 127, pc = p & 3;
+      wr[8 + k] = *(const uint4*)(st + (size_t)(4 + plane) * P + (size_t)n * DH + SW_US * s + pc * 8);
+    }
+  };
+  auto store_slice = [&](int buf) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int p = k * 256 + tid;
+      const int plane = p >> 9, row = (p >> 4) & 31, pc = p & 15;
+      *(uint4*)(L.w13[buf][plane] + row * RW13_ROW + pc * 16) = wr[k];
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int p = k * 256 + tid;
+      const int plane = p >> 9, n = (p >> 2) & 127, pc = p & 3;
+      unsigned char* dst = L.w2[buf][plane] + n * RW2_ROW + pc * 16;
+      *(uint2*)dst = uint2{wr[8 + k].x, wr[8 + k].y};
+      *(uint2*)(dst + 8) = uint2{wr[8 + k].z, wr[8 + k].w};
+    }
+  };
+
+  floatx4 oacc[8][2];
+#pragma unroll
+  for (int nt = 0; nt < 8; ++nt) oacc[nt][0] = oacc[nt][1] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  constexpr int NSLICE = DH / SW_US;
+  load_slice(0);
+  for (int s = 0; s < NSLICE; ++s) {
+    const int buf = s & 1;
+    store_slice(buf);
+    __syncthreads();
+    if (s + 1 < NSLICE) load_slice(s + 1);
+    // A^T, B^T [unit][token] for 2 unit tiles x 2 token tiles
+    floatx4 at[2][2], bt[2][2];
+#pragma unroll
+    for (int ut = 0; ut < 2; ++ut)
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) at[ut][tt] = bt[ut][tt] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ut = 0; ut < 2; ++ut)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const int off = (16 * ut + li) * RW13_ROW + (32 * ks + 8 * g) * 2;
+        const bf16x8 w1h = *(const bf16x8*)(L.w13[buf][0] + off);
+        const bf16x8 w1l = *(const bf16x8*)(L.w13[buf][1] + off);
+        const bf16x8 w3h = *(const bf16x8*)(L.w13[buf][2] + off);
+        const bf16x8 w3l = *(const bf16x8*)(L.w13[buf][3] + off);
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+          at[ut][tt] = mfma16(w1h, qop[tt][ks], at[ut][tt]);
+          at[ut][tt] = mfma16(w1l, qop[tt][ks], at[ut][tt]);
+          bt[ut][tt] = mfma16(w3h, qop[tt][ks], bt[ut][tt]);
+          bt[ut][tt] = mfma16(w3l, qop[tt][ks], bt[ut][tt]);
+        }
+      }
+    // H^T = silu(A^T) * B^T, split into bf16 hi + lo; k-slot order of the
+    // 32 units: 4g..4g+3 of unit tile 0, then of unit tile 1
+    bf16x8 hh[2], hl[2];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int ut = 0; ut < 2; ++ut)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float a = at[ut][tt][r];
+          const float h = a / (1.0f + __expf(-a)) * bt[ut][tt][r];
+          const bf16 hb = (bf16)h;
+          hh[tt][4 * ut + r] = hb;
+          hl[tt][4 * ut + r] = (bf16)(h - (float)hb);
+        }
+    // O^T[n][t] += W2^T[n][units] H^T[units][t]
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt) {
+      const unsigned char* rowh = L.w2[buf][0] + (16 * nt + li) * RW2_ROW;
+      const unsigned char* rowl = L.w2[buf][1] + (16 * nt + li) * RW2_ROW;
+      const bf16x8 w2h = join(*(const bf16x4*)(rowh + 8 * g), *(const bf16x4*)(rowh + 32 + 8 * g));
+      const bf16x8 w2l = join(*(const bf16x4*)(rowl + 8 * g), *(const bf16x4*)(rowl + 32 + 8 * g));
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        oacc[nt][tt] = mfma16(w2h, hh[tt], oacc[nt][tt]);
+        oacc[nt][tt] = mfma16(w2h, hl[tt], oacc[nt][tt]);
+        oacc[nt][tt] = mfma16(w2l, hh[tt], oacc[nt][tt]);
+      }
+    }
+    __syncthreads();
+  }
+  bf16* Oh = O + (size_t)bh * T * D;
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt) {
+    const int t = t0 + 32 * w + 16 * tt + li;
+    if (t < cend) {
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt)
+        *(bf16x4*)(Oh + (size_t)t * D + 16 * nt + 4 * g) =
+            to_bf16x4(oacc[nt][tt][0], oacc[nt][tt][1], oacc[nt][tt][2], oacc[nt][tt][3]);
+    }
+  }
+}
+
+struct SwLayout {
+  size_t states, ss2, counters, err, total;
+};
+
+SwLayout sw_layout(int64_t BH, int64_t nchunks) {
+  SwLayout L;
+  L.states = 0;
+  size_t off = (size_t)BH * nchunks * SW_STATE * 2;
+  off = (off + 255) & ~(size_t)255;
+  L.ss2 = off;
+  off += (size_t)BH * 2 * SW_NSL * SW_D * 4;
+  off = (off + 255) & ~(size_t)255;
+  L.counters = off;
+  off += (size_t)BH * 4;
+  L.err = off;
+  off += 4;
+  L.total = (off + 255) & ~(size_t)255;
+  return L;
+}
+
+}  // namespace
+
+bool large_chunk_swiglu_supported(int64_t d, int64_t dh, int64_t chunk, int dtype) {
+  (void)chunk;
+  return dtype == 1 && d == SW_D && dh == SW_DH;
+}
+
+size_t large_chunk_swiglu_workspace(int64_t B, int64_t H, int64_t T, int64_t d, int64_t dh, int64_t chunk) {
+  (void)d;
+  (void)dh;
+  return sw_layout(B * H, (T + chunk - 1) / chunk).total;
+}
+
+hipError_t launch_large_chunk_swiglu(const LargeChunkArgs& a, hipStream_t stream) {
+  const int BH = (int)(a.B * a.H);
+  const int T = (int)a.T, chunk = (int)a.chunk;
+  const int nchunks = (int)((a.T + a.chunk - 1) / a.chunk);
+  const SwLayout lay = sw_layout(BH, nchunks);
+  unsigned char* ws = (unsigned char*)a.ws;
+  bf16* states = (bf16*)(ws + lay.states);
+  float* ss2 = (float*)(ws + lay.ss2);
+  unsigned* counters = (unsigned*)(ws + lay.counters);
+  unsigned* err = (unsigned*)(ws + lay.err);
+
+  const int nz = BH + 1;
+  hipLaunchKernelGGL(zero_u32_kernel, dim3((nz + 255) / 256), dim3(256), 0, stream, counters, nz);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+
+  // the recurrence needs every workgroup of a head resident at once
+  const size_t lds_r = sizeof(RecurLds);
+  e = hipFuncSetAttribute((const void*)swiglu_recur_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_r);
+  if (e != hipSuccess) return e;
+  int dev = 0, ncu = 0, per_cu = 0;
+  if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
+  if ((e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
+  if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)swiglu_recur_kernel, 256, lds_r)) !=
+      hipSuccess)
+    return e;
+  const int heads_per_launch = (per_cu * ncu) / SW_NSL;
+  if (heads_per_launch < 1) return hipErrorCooperativeLaunchTooLarge;
+  const bf16* Kp = (const bf16*)a.K;
+  const bf16* Vp = (const bf16*)a.V;
+  const float* Ep = a.eta;
+  const float* W0p = a.W0;
+  float* Wo = a.W_out;
+  for (int h0 = 0; h0 < BH; h0 += heads_per_launch) {
+    const int nh = std::min(heads_per_launch, BH - h0);
+    int Ti = T, ci = chunk, nci = nchunks, hi = h0;
+    void* args[] = {(void*)&Kp, (void*)&Vp, (void*)&Ep, (void*)&W0p, (void*)&Wo, (void*)&states, (void*)&ss2,
+                    (void*)&counters, (void*)&err, (void*)&Ti, (void*)&ci, (void*)&nci, (void*)&hi};
+    e = hipLaunchCooperativeKernel((const void*)swiglu_recur_kernel, dim3(nh * SW_NSL), dim3(256), args,
+                                   (unsigned)lds_r, stream);
+    if (e != hipSuccess) return e;
+  }
+  if (nchunks == 0) return hipSuccess;
+  const size_t lds_o = sizeof(ReadLds);
+  e = hipFuncSetAttribute((const void*)swiglu_read_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_o);
+  if (e != hipSuccess) return e;
+  const int tiles = (chunk + SW_TT - 1) / SW_TT;
+  hipLaunchKernelGGL(swiglu_read_kernel, dim3(BH * nchunks * tiles), dim3(256), lds_o, stream, (const bf16*)a.Q,
+                     (const bf16*)states, (bf16*)a.O, T, chunk, nchunks, tiles);
+  return hipGetLastError();
+}
+
+}  // namespace ttt

@@ -1,4 +1,6 @@
 """Shared helpers for the GPU parity tests (imports torch and the binding)."""
+import os
+
 import numpy as np
 import torch
 
@@ -65,7 +67,11 @@ def check(s, x, O, W, heads=None, label=""):
     Or, Wr = oracle_heads(x, s, heads)
     eo = err(gpu_heads(O, heads), Or, s["dtype"])
     ew = err(gpu_heads(W, heads), Wr, s["dtype"])
-    print(f"[{label}] err_O={eo:.3e} err_W={ew:.3e} tol={tol(s['dtype'])}", flush=True)
+    line = f"[{s['mode']} {label}] err_O={eo:.3e} err_W={ew:.3e} tol={tol(s['dtype'])}"
+    print(line, flush=True)
+    if os.environ.get("TTT_ERRLOG"):
+        with open(os.environ["TTT_ERRLOG"], "a") as f:
+            f.write(line + "\n")
     assert eo <= tol(s["dtype"]), f"O error {eo} > {tol(s['dtype'])}"
     assert ew <= tol(s["dtype"]), f"W error {ew} > {tol(s['dtype'])}"
     return eo, ew

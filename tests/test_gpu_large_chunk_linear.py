@@ -1,0 +1,60 @@
+"""GPU parity of the large-chunk (LaCT) linear mode against the fp64 oracle."""
+import numpy as np
+import pytest
+import torch
+
+from helpers import check, err, la, run, to_device, tol, workloads
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("B,H,T,d,chunk", [
+    (1, 2, 300, 64, 128),     # ragged last chunk
+    (2, 2, 512, 64, 256),
+    (1, 3, 1000, 128, 300),   # chunk not a multiple of the tiles
+    (1, 1, 2500, 64, 2048),   # several token slices per chunk, ragged
+    (1, 2, 97, 64, 1),        # one token per chunk
+    (1, 2, 50, 64, 7),
+    (1, 2, 100, 64, 100),     # a single chunk
+    (1, 2, 100, 64, 4096),    # chunk longer than the sequence
+])
+def test_large_chunk_linear_small(B, H, T, d, chunk):
+    s = workloads.make_spec("large_chunk_linear", B, H, T, d, chunk=chunk, dtype="bf16", eta_scale=0.05)
+    x = workloads.generate(s, seed=2)
+    O, W = run(to_device(x, s), s)
+    check(s, x, O, W, label=f"{B},{H},{T},{d},c{chunk}")
+    assert np.allclose(np.linalg.norm(W.cpu().numpy().astype(np.float64), axis=-2), 1.0, atol=1e-5)
+
+
+def test_large_chunk_linear_empty():
+    s = workloads.make_spec("large_chunk_linear", 1, 2, 0, 64, chunk=64, dtype="bf16")
+    x = workloads.generate(s, seed=0)
+    O, W = run(to_device(x, s), s)
+    assert torch.equal(W.cpu(), torch.from_numpy(x["W0"]))
+
+
+def test_large_chunk_linear_workload_B1H12T196608_sampled_heads():
+    s = workloads.spec("large_chunk_linear_bf16_B1H12T196608_d64_c4096")
+    x = workloads.generate(s, seed=0)
+    O, W = run(to_device(x, s), s)
+    check(s, x, O, W, heads=[0, 7, 11], label="B1H12T196608 heads 0,7,11")
+
+
+def test_large_chunk_linear_deterministic_resume_in_place():
+    s = workloads.make_spec("large_chunk_linear", 1, 3, 700, 64, chunk=128, dtype="bf16", eta_scale=0.05)
+    x = workloads.generate(s, seed=3)
+    t = to_device(x, s)
+    O1, W1 = run(t, s)
+    O2, W2 = run(t, s)
+    assert torch.equal(O1, O2) and torch.equal(W1, W2)
+    t1 = 256                          # a chunk boundary
+    a = {k: (v[:, :, :t1].contiguous() if k != "W0" else v) for k, v in t.items()}
+    Oa, Wm = run(a, s)
+    b = {k: (v[:, :, t1:].contiguous() if k != "W0" else Wm) for k, v in t.items()}
+    Ob, Wb = run(b, s)
+    assert err(torch.cat([Oa, Ob], 2).float().cpu().numpy(), O1.float().cpu().numpy(), "bf16") <= tol("bf16")
+    assert err(Wb.cpu().numpy(), W1.cpu().numpy(), "bf16") <= tol("bf16")
+    Ws = t["W0"].clone()
+    O3, W3 = la.forward(t["Q"], t["K"], t["V"], t["eta"], Ws, 128, "large_chunk_linear", W_out=Ws)
+    torch.cuda.synchronize()
+    assert torch.equal(O3, O1) and torch.equal(W3, W1)

@@ -1,0 +1,63 @@
+"""GPU parity of the large-chunk (LaCT) SwiGLU mode against the fp64 oracle."""
+import numpy as np
+import pytest
+import torch
+
+from helpers import check, err, la, run, to_device, tol, workloads
+from oracle import swiglu_unpack
+
+pytestmark = pytest.mark.gpu
+
+
+def unit_columns(W, d, dh):
+    W1, W3, W2 = swiglu_unpack(W.cpu().numpy().astype(np.float64), d, dh)
+    return all(np.allclose(np.linalg.norm(M, axis=-2), 1.0, atol=1e-5) for M in (W1, W3, W2))
+
+
+@pytest.mark.parametrize("B,H,T,chunk", [
+    (1, 1, 300, 128),      # ragged last chunk and sub-block
+    (1, 2, 1024, 256),
+    (2, 1, 700, 2048),     # a single chunk longer than the sequence
+    (1, 1, 200, 37),       # chunk not a multiple of the sub-block
+    (1, 1, 40, 1),         # one token per chunk
+])
+def test_large_chunk_swiglu_small(B, H, T, chunk):
+    s = workloads.make_spec("large_chunk_swiglu", B, H, T, 128, d_h=256, chunk=chunk, dtype="bf16", eta_scale=0.02)
+    x = workloads.generate(s, seed=4)
+    O, W = run(to_device(x, s), s)
+    check(s, x, O, W, label=f"{B},{H},{T},c{chunk}")
+    assert unit_columns(W, 128, 256)
+
+
+def test_large_chunk_swiglu_empty():
+    s = workloads.make_spec("large_chunk_swiglu", 1, 2, 0, 128, d_h=256, chunk=64, dtype="bf16")
+    x = workloads.generate(s, seed=0)
+    O, W = run(to_device(x, s), s)
+    assert torch.equal(W.cpu(), torch.from_numpy(x["W0"]))
+
+
+def test_large_chunk_swiglu_workload_B2H8T32768_sampled_heads():
+    s = workloads.spec("large_chunk_swiglu_bf16_B2H8T32768_d128_dh256_c2048")
+    x = workloads.generate(s, seed=0)
+    O, W = run(to_device(x, s), s)
+    check(s, x, O, W, heads=[0, 9, 15], label="B2H8T32768 heads 0,9,15")
+
+
+def test_large_chunk_swiglu_deterministic_resume_in_place():
+    s = workloads.make_spec("large_chunk_swiglu", 1, 2, 600, 128, d_h=256, chunk=128, dtype="bf16", eta_scale=0.02)
+    x = workloads.generate(s, seed=5)
+    t = to_device(x, s)
+    O1, W1 = run(t, s)
+    O2, W2 = run(t, s)
+    assert torch.equal(O1, O2) and torch.equal(W1, W2)
+    t1 = 256
+    a = {k: (v[:, :, :t1].contiguous() if k != "W0" else v) for k, v in t.items()}
+    Oa, Wm = run(a, s)
+    b = {k: (v[:, :, t1:].contiguous() if k != "W0" else Wm) for k, v in t.items()}
+    Ob, Wb = run(b, s)
+    assert err(torch.cat([Oa, Ob], 2).float().cpu().numpy(), O1.float().cpu().numpy(), "bf16") <= tol("bf16")
+    assert err(Wb.cpu().numpy(), W1.cpu().numpy(), "bf16") <= tol("bf16")
+    Ws = t["W0"].clone()
+    O3, W3 = la.forward(t["Q"], t["K"], t["V"], t["eta"], Ws, 128, "large_chunk_swiglu", W_out=Ws)
+    torch.cuda.synchronize()
+    assert torch.equal(O3, O1) and torch.equal(W3, W1)
