@@ -21,6 +21,8 @@ ARCH = "gfx950"
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
          # packed fp32 vector ops stay off: only scalar and MFMA fp32 paths
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         # keep MFMA accumulators in VGPRs (no AGPR copies around the VALU work)
+         "-mllvm", "-amdgpu-mfma-vgpr-form",
          "-I", os.path.join(ROOT, "include"), "-I", CSRC]
 
 

@@ -70,6 +70,29 @@ __device__ __forceinline__ void g2lds4(const void* gsrc, void* lds_wave_base) {
   __builtin_amdgcn_global_load_lds(gsrc, (lds_void*)(uintptr_t)lds_wave_base, 4, 0, 0);
 }
 
+// Buffer resources: raw (stride 0) view of `nbytes` bytes from `base`;
+// accesses at or beyond nbytes read 0 and drop writes, which is how the
+// kernels treat the ragged end of a sequence.
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned uint2v __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, long long nbytes) {
+  const int n = nbytes <= 0 ? 0 : (nbytes > 0x7fffffffLL ? 0x7fffffff : (int)nbytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, 0x00020000);
+}
+// 16 bytes per lane from a buffer straight into LDS (lane l -> lds_wave_base + 16*l).
+__device__ __forceinline__ void buf2lds16(__amdgpu_buffer_rsrc_t r, unsigned voff, void* lds_wave_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(uintptr_t)lds_wave_base, 16, voff, 0, 0, 0);
+}
+__device__ __forceinline__ void buf2lds4(__amdgpu_buffer_rsrc_t r, unsigned voff, void* lds_wave_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(uintptr_t)lds_wave_base, 4, voff, 0, 0, 0);
+}
+__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, unsigned voff) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0);
+}
+__device__ __forceinline__ void buf_store16(__amdgpu_buffer_rsrc_t r, unsigned voff, u32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, voff, 0, 0);
+}
+
 // s_waitcnt vmcnt(N) (other counters untouched) followed by a workgroup
 // barrier.  The "memory" clobber keeps the compiler from moving LDS or
 // global accesses across it.

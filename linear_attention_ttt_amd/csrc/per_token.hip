@@ -26,328 +26,391 @@
 //    with the LDS transpose read; eta is applied to V when it is read
 //    (diag(eta) V rounded once to bf16 and used by both products).
 //  * The outputs go LDS -> HBM as 16-byte row pieces one chunk later.
+#include <type_traits>
+
 #include "device_common.h"
 #include "kernels.h"
 
 namespace ttt {
 
-template <int DK, int C, int TV, int STAGES>
+// bf16 kernel, one 64-token tile per step, two phases per step:
+//   phase 1: the 10 score tiles P^T(jb, ib) = K_jb Q_ib^T (jb <= ib) are
+//            spread evenly over the 4 waves, scaled by eta_j, masked and
+//            split into bf16 hi + lo in LDS; each wave w starts its outputs
+//            O_w^T = S_{c-1}^T Q_w^T for the queries 16w..16w+15; the
+//            diag(eta) V planes of the next tile are prepared.
+//   phase 2: O_w^T += V^T A_w^T (A from the score tiles), stored to HBM;
+//            S += K^T (diag(eta) V) on the wave's DK/4-row slab; the new S is
+//            written to LDS for the next step.
+// Outputs are computed transposed so one lane holds 4 consecutive output
+// columns of one token: an 8-byte store per lane.  Each wave runs its own
+// instantiation of the program (the wave index is a template parameter) so
+// every tile index and LDS offset is a compile-time constant added to a
+// handful of per-lane offsets computed once.
+template <int DK, int TV, int NW_>
 struct PerTokenCfg {
-  static constexpr int NW = 4;
+  static constexpr int C = 64;                 // tokens per tile
+  static constexpr int NW = NW_;               // 4 waves, or 8 (two per SIMD) when there are >= 2 column tiles
   static constexpr int THREADS = NW * WAVE;
-  static constexpr int IB = C / 16;
-  static constexpr int IBW = IB / NW;
+  static constexpr int QKSTAGES = 3;           // Q and K rings
+  static constexpr int VSTAGES = 4;            // V / eta ring: prefetched one tile further
   static constexpr int NT = TV / 16;
+  static constexpr int GW = NW / 4;            // waves sharing one query block / state slab
+  static constexpr int NTW = NT / GW;          // 16-column tiles per wave
   static constexpr int KT = DK / 32;
-  static constexpr int KC = C / 32;
-  static constexpr int SROWS = DK / NW;
-  static constexpr int MT = SROWS / 16;
-  static constexpr int CPR = DK / 8;          // 16-byte pieces per Q/K row
-  static constexpr int Q_BYTES = C * DK * 2;
+  static constexpr int MTW = DK / 64;          // 16-row m-tiles of S per wave
+  static constexpr int CPR = DK / 8;           // 16-byte pieces per Q/K row
+  static constexpr int SWZ = CPR >= 16 ? 15 : CPR - 1;  // XOR swizzle of 16-byte pieces by row
+  static constexpr int ROWB = DK * 2;
+  static constexpr int QK_BYTES = C * ROWB;
   static constexpr int V_BYTES = C * TV * 2;
   static constexpr int E_BYTES = C * 4;
-  static constexpr int STAGE_BYTES = 2 * Q_BYTES + V_BYTES + E_BYTES;
-  static constexpr int S_ROW = DK * 2 + 16;   // padded bf16 row of S^T
-  static constexpr int S_BYTES = TV * S_ROW;
-  static constexpr int O_ROW = TV * 2 + 16;
-  static constexpr int O_BYTES = C * O_ROW;
-  // S^T is exchanged as a pair of bf16 planes (hi + lo), double-buffered
-  static constexpr int LDS_BYTES = STAGES * STAGE_BYTES + 4 * S_BYTES + 2 * O_BYTES;
-  // per-wave memory instructions per chunk
-  static constexpr int QI = Q_BYTES / 1024 / NW;
-  static constexpr int VPW = C * TV / 8 / NW;   // 16-byte V pieces per wave
+  static constexpr int S_BYTES = TV * ROWB;    // one bf16 plane of S^T [TV][DK], swizzled like Q/K
+  static constexpr int P_BYTES = 10 * 64 * 8;  // one plane of the 10 score tiles, 8 bytes per lane
+  static constexpr int OFF_Q = 0;
+  static constexpr int OFF_K = OFF_Q + QKSTAGES * QK_BYTES;
+  static constexpr int OFF_V = OFF_K + QKSTAGES * QK_BYTES;
+  static constexpr int OFF_E = OFF_V + VSTAGES * V_BYTES;
+  static constexpr int OFF_EV = OFF_E + VSTAGES * E_BYTES;   // [2 buffers][hi, lo]
+  static constexpr int OFF_S = OFF_EV + 4 * V_BYTES;         // [hi, lo]
+  static constexpr int OFF_P = OFF_S + 2 * S_BYTES;          // [hi, lo]
+  static constexpr int LDS_BYTES = OFF_P + 2 * P_BYTES;
+  // per-wave vector-memory instructions issued every step
+  static constexpr int QI = QK_BYTES / 1024 / NW;
+  static constexpr int VPW = C * TV / 8 / NW;  // 16-byte V pieces per wave
   static constexpr int VI = (VPW + 63) / 64;
-  static constexpr int LOADS = 2 * QI + VI + 1;
-  static constexpr int OI = VI;                 // O pieces per wave equal V pieces
-  static constexpr int STEADY_VMCNT = (STAGES - 2) * (LOADS + OI);
-  static_assert(IB % NW == 0, "C must be a multiple of 64");
-  static_assert(Q_BYTES % (1024 * NW) == 0, "Q tile must split into whole wave loads");
-  static_assert(C / NW / 4 <= 64, "eta split");
-  static_assert(STEADY_VMCNT < 64, "vmcnt range");
+  static constexpr int OPS = 2 * QI + VI + 1 /*eta*/ + NTW /*O stores*/;
+  static_assert(NT % GW == 0, "column tiles must split evenly over the waves of a block");
+  static_assert(QK_BYTES % (1024 * NW) == 0, "Q/K tile must split into whole wave loads");
+  static_assert(OPS < 64, "vmcnt range");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
 };
 
-template <int DK, int C, int TV, int STAGES>
-__global__ __launch_bounds__(256, 1) void per_token_bf16_kernel(
+// score tile t (0..9) <-> (jb, ib), jb <= ib; wave w owns tiles [tile_begin(w), tile_begin(w+1))
+__host__ __device__ constexpr int ptile_jb(int t) { return t < 1 ? 0 : t < 3 ? t - 1 : t < 6 ? t - 3 : t - 6; }
+__host__ __device__ constexpr int ptile_ib(int t) { return t < 1 ? 0 : t < 3 ? 1 : t < 6 ? 2 : 3; }
+__host__ __device__ constexpr int ptile_index(int jb, int ib) { return ib * (ib + 1) / 2 + jb; }
+__host__ __device__ constexpr int tile_begin4(int w) { return w == 0 ? 0 : w == 1 ? 3 : w == 2 ? 6 : w == 3 ? 8 : 10; }
+__host__ __device__ constexpr int tile_begin8(int w) { return w <= 3 ? 2 * w : w <= 7 ? w + 3 : 10; }
+template <int NW>
+__host__ __device__ constexpr int tile_begin(int w) { return NW == 4 ? tile_begin4(w) : tile_begin8(w); }
+
+struct PerTokenPtrs {
+  const bf16* Qh;
+  const bf16* Kh;
+  const bf16* Vh;
+  const float* Eh;
+  bf16* Oh;
+  const float* W0h;
+  float* Wh;
+  int T, DV, tv0;
+};
+
+template <int DK, int TV, int NW, int W>
+__device__ __forceinline__ void per_token_wave(const PerTokenPtrs& P, unsigned char* smem, int l) {
+  using Cfg = PerTokenCfg<DK, TV, NW>;
+  constexpr int C = Cfg::C;
+  constexpr int ROWB = Cfg::ROWB;
+  constexpr int SWZ = Cfg::SWZ;
+  constexpr int IB = W / Cfg::GW;              // this wave's query block (16 queries)
+  constexpr int NT0 = (W % Cfg::GW) * Cfg::NTW;  // first of this wave's column tiles
+  constexpr int SLAB = DK / 4 * IB;            // first state row of this wave
+  const int g = l >> 4;
+  const int li = l & 15;
+  const int tid = W * 64 + l;
+  const int T = P.T, DV = P.DV, tv0 = P.tv0;
+  const int nchunks = (T + C - 1) / C;
+
+  // ---- per-lane byte offsets, fixed for the whole sequence ----
+  unsigned qkoff[Cfg::QI];                     // DMA: global offset of LDS slot (W*QI + k)*64 + l
+#pragma unroll
+  for (int k = 0; k < Cfg::QI; ++k) {
+    const int s = (W * Cfg::QI + k) * 64 + l;
+    const int row = s / Cfg::CPR;
+    qkoff[k] = (unsigned)(row * ROWB + (((s % Cfg::CPR) ^ (row & SWZ)) << 4));
+  }
+  unsigned voff[Cfg::VI];
+#pragma unroll
+  for (int k = 0; k < Cfg::VI; ++k) {
+    const int p = W * Cfg::VPW + k * 64 + l;
+    voff[k] = (unsigned)((p / (TV / 8)) * DV * 2 + (tv0 + (p % (TV / 8)) * 8) * 2);
+  }
+  // natural 16-byte operand reads: row 16*blk + li, d = 32*ks + 8g  ->  blk*16*ROWB + nat[ks]
+  int nat[Cfg::KT];
+#pragma unroll
+  for (int ks = 0; ks < Cfg::KT; ++ks) nat[ks] = li * ROWB + ((((4 * ks + g) ^ (li & SWZ))) << 4);
+  // S^T plane writes: row n = 16nt + li, d_k = SLAB + 16j + 4g  ->  nt*16*ROWB + swr[j]
+  int swr[Cfg::MTW];
+#pragma unroll
+  for (int j = 0; j < Cfg::MTW; ++j) {
+    const int k = SLAB + 16 * j + 4 * g;
+    swr[j] = li * ROWB + ((((k >> 3) ^ (li & SWZ))) << 4) + (k & 7) * 2;
+  }
+  // transposed K reads for the state update: rows 32kc + 16h + 4g + li/4, cols SLAB + 16j + 4(li%4)
+  int ktr[Cfg::MTW];
+#pragma unroll
+  for (int j = 0; j < Cfg::MTW; ++j) {
+    const int r = 4 * g + (li >> 2), col = SLAB + 16 * j + 4 * (li & 3);
+    ktr[j] = r * ROWB + ((((col >> 3) ^ (r & SWZ))) << 4) + (col & 7) * 2;
+  }
+  const int vtr = (4 * g + (li >> 2)) * (TV * 2) + 4 * (li & 3) * 2;   // + (32kc + 16h)*TV*2 + 32nt
+  const unsigned ooff = (unsigned)((16 * IB + li) * DV * 2 + (tv0 + 16 * NT0 + 4 * g) * 2);
+
+  auto issue_qk = [&](int c, int slot) {
+    const long long rem = (long long)T - (long long)c * C;
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(P.Qh + (size_t)c * C * DK, rem * ROWB);
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(P.Kh + (size_t)c * C * DK, rem * ROWB);
+    unsigned char* dq = smem + Cfg::OFF_Q + slot * Cfg::QK_BYTES + W * Cfg::QI * 1024;
+    unsigned char* dk = smem + Cfg::OFF_K + slot * Cfg::QK_BYTES + W * Cfg::QI * 1024;
+#pragma unroll
+    for (int k = 0; k < Cfg::QI; ++k) buf2lds16(rq, qkoff[k], dq + k * 1024);
+#pragma unroll
+    for (int k = 0; k < Cfg::QI; ++k) buf2lds16(rk, qkoff[k], dk + k * 1024);
+  };
+  auto issue_ve = [&](int c, int slot) {
+    const long long rem = (long long)T - (long long)c * C;
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(P.Vh + (size_t)c * C * DV, rem * DV * 2);
+    unsigned char* dst = smem + Cfg::OFF_V + slot * Cfg::V_BYTES + W * Cfg::VPW * 16;
+#pragma unroll
+    for (int k = 0; k < Cfg::VI; ++k)
+      if (k * 64 + l < Cfg::VPW) buf2lds16(rv, voff[k], dst + k * 1024);
+    const __amdgpu_buffer_rsrc_t re = make_rsrc(P.Eh + (size_t)c * C, rem * 4);
+    if (l < C / Cfg::NW)
+      buf2lds4(re, (unsigned)((W * (C / Cfg::NW) + l) * 4), smem + Cfg::OFF_E + slot * Cfg::E_BYTES + W * (C / Cfg::NW) * 4);
+  };
+  // diag(eta) V of one tile as bf16 hi + lo planes (same layout as the V tile)
+  auto convert_ev = [&](int vslot, int buf) {
+    const unsigned char* vs = smem + Cfg::OFF_V + vslot * Cfg::V_BYTES;
+    const float* es = (const float*)(smem + Cfg::OFF_E + vslot * Cfg::E_BYTES);
+    unsigned char* eh = smem + Cfg::OFF_EV + buf * 2 * Cfg::V_BYTES;
+#pragma unroll
+    for (int p0 = 0; p0 < C * TV / 8; p0 += Cfg::THREADS) {
+      const int p = p0 + tid;
+      if (p < C * TV / 8) {
+        const bf16x8 v = *(const bf16x8*)(vs + p * 16);
+        const float e = es[p / (TV / 8)];
+        bf16x8 hi, lo;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float f = e * (float)v[j];
+          hi[j] = (bf16)f;
+          lo[j] = (bf16)(f - (float)hi[j]);
+        }
+        *(bf16x8*)(eh + p * 16) = hi;
+        *(bf16x8*)(eh + Cfg::V_BYTES + p * 16) = lo;
+      }
+    }
+  };
+
+  // ---- state: S[j][n] holds rows SLAB + 16j + 4g + r, column 16(NT0 + n) + li ----
+  floatx4 S[Cfg::MTW][Cfg::NTW];
+#pragma unroll
+  for (int j = 0; j < Cfg::MTW; ++j)
+#pragma unroll
+    for (int n = 0; n < Cfg::NTW; ++n)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        S[j][n][r] = P.W0h[(size_t)(SLAB + 16 * j + 4 * g + r) * DV + tv0 + 16 * (NT0 + n) + li];
+  auto write_s_lds = [&]() {
+    unsigned char* sb = smem + Cfg::OFF_S;
+#pragma unroll
+    for (int j = 0; j < Cfg::MTW; ++j)
+#pragma unroll
+      for (int n = 0; n < Cfg::NTW; ++n) {
+        const int nt = NT0 + n;
+        bf16x4 hi, lo;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          hi[r] = (bf16)S[j][n][r];
+          lo[r] = (bf16)(S[j][n][r] - (float)hi[r]);
+        }
+        *(bf16x4*)(sb + nt * 16 * ROWB + swr[j]) = hi;
+        *(bf16x4*)(sb + Cfg::S_BYTES + nt * 16 * ROWB + swr[j]) = lo;
+      }
+  };
+
+  if (nchunks > 0) {
+    write_s_lds();
+    issue_qk(0, 0);
+    issue_ve(0, 0);
+    issue_qk(1, 1);
+    issue_ve(1, 1);
+    issue_ve(2, 2);
+    wait_vm_barrier<0>();
+    convert_ev(0, 0);
+  }
+
+  int qslot = 0, vslot = 0;
+  for (int c = 0; c < nchunks; ++c) {
+    // loads of tile c landed, and V/eta of tile c+1; all of step c-1 done
+    if (c >= 1)
+      wait_vm_barrier<Cfg::OPS>();
+    else
+      wait_vm_barrier<0>();
+    const int qslot2 = qslot == 0 ? 2 : qslot - 1;          // (c + 2) % 3
+    const int vslot1 = (vslot + 1) & 3, vslot3 = (vslot + 3) & 3;
+    // prefetch: Q/K of tile c+2, V/eta of tile c+3 (past the end: empty resources)
+    issue_qk(c + 2, qslot2);
+    issue_ve(c + 3, vslot3);
+
+    const unsigned char* qst = smem + Cfg::OFF_Q + qslot * Cfg::QK_BYTES;
+    const unsigned char* kst = smem + Cfg::OFF_K + qslot * Cfg::QK_BYTES;
+    const unsigned char* vs = smem + Cfg::OFF_V + vslot * Cfg::V_BYTES;
+    const float* es = (const float*)(smem + Cfg::OFF_E + vslot * Cfg::E_BYTES);
+    const unsigned char* evb = smem + Cfg::OFF_EV + (c & 1) * 2 * Cfg::V_BYTES;
+    const unsigned char* sb = smem + Cfg::OFF_S;
+    unsigned char* pb = smem + Cfg::OFF_P;
+
+    // ---- phase 1a: this wave's score tiles ----
+#pragma unroll
+    for (int t = tile_begin<NW>(W); t < tile_begin<NW>(W + 1); ++t) {
+      const int jb = ptile_jb(t), ib = ptile_ib(t);
+      floatx4 p = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < Cfg::KT; ++ks) {
+        const bf16x8 kop = *(const bf16x8*)(kst + jb * 16 * ROWB + nat[ks]);
+        const bf16x8 qop = *(const bf16x8*)(qst + ib * 16 * ROWB + nat[ks]);
+        p = mfma16(kop, qop, p);
+      }
+      const floatx4 e4 = *(const floatx4*)(es + 16 * jb + 4 * g);
+      bf16x4 hi, lo;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float f = p[r] * e4[r];
+        if (jb == ib && 4 * g + r > li) f = 0.f;
+        hi[r] = (bf16)f;
+        lo[r] = (bf16)(f - (float)hi[r]);
+      }
+      *(bf16x4*)(pb + t * 512 + l * 8) = hi;
+      *(bf16x4*)(pb + Cfg::P_BYTES + t * 512 + l * 8) = lo;
+    }
+    // ---- phase 1b: O_w^T = S^T Q_w^T (S as bf16 hi + lo) ----
+    bf16x8 qop[Cfg::KT];
+#pragma unroll
+    for (int ks = 0; ks < Cfg::KT; ++ks) qop[ks] = *(const bf16x8*)(qst + IB * 16 * ROWB + nat[ks]);
+    floatx4 acc[Cfg::NTW];
+#pragma unroll
+    for (int n = 0; n < Cfg::NTW; ++n) {
+      const int nt = NT0 + n;
+      acc[n] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < Cfg::KT; ++ks) {
+        acc[n] = mfma16(*(const bf16x8*)(sb + nt * 16 * ROWB + nat[ks]), qop[ks], acc[n]);
+        acc[n] = mfma16(*(const bf16x8*)(sb + Cfg::S_BYTES + nt * 16 * ROWB + nat[ks]), qop[ks], acc[n]);
+      }
+    }
+    // ---- phase 1c: diag(eta) V planes of tile c+1 ----
+    if (c + 1 < nchunks) convert_ev(vslot1, (c + 1) & 1);
+    barrier();
+
+    // ---- phase 2a: O_w^T += V^T A_w^T over key blocks 0..IB ----
+#pragma unroll
+    for (int kc = 0; 2 * kc <= IB; ++kc) {
+      const int t0i = ptile_index(2 * kc, IB);
+      const bf16x4 h0 = *(const bf16x4*)(pb + t0i * 512 + l * 8);
+      const bf16x4 l0 = *(const bf16x4*)(pb + Cfg::P_BYTES + t0i * 512 + l * 8);
+      bf16x4 h1 = bf16x4{(bf16)0.f, (bf16)0.f, (bf16)0.f, (bf16)0.f}, l1 = h1;
+      if (2 * kc + 1 <= IB) {
+        const int t1i = ptile_index(2 * kc + 1, IB);
+        h1 = *(const bf16x4*)(pb + t1i * 512 + l * 8);
+        l1 = *(const bf16x4*)(pb + Cfg::P_BYTES + t1i * 512 + l * 8);
+      }
+      const bf16x8 bh_ = join(h0, h1), bl_ = join(l0, l1);
+#pragma unroll
+      for (int n = 0; n < Cfg::NTW; ++n) {
+        const int o0 = vtr + 32 * kc * TV * 2 + 32 * (NT0 + n), o1 = o0 + 16 * TV * 2;
+        const bf16x8 vt = join(lds_read_tr16(vs + o0), lds_read_tr16(vs + o1));
+        acc[n] = mfma16(vt, bh_, acc[n]);
+        acc[n] = mfma16(vt, bl_, acc[n]);
+      }
+    }
+    {
+      const long long rem = (long long)T - (long long)c * C;
+      const __amdgpu_buffer_rsrc_t ro = make_rsrc(P.Oh + (size_t)c * C * DV, rem * DV * 2);
+#pragma unroll
+      for (int n = 0; n < Cfg::NTW; ++n) {
+        const bf16x4 o = to_bf16x4(acc[n][0], acc[n][1], acc[n][2], acc[n][3]);
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(uint2v, o), ro, ooff + n * 32, 0, 0);
+      }
+    }
+    // ---- phase 2b: S += K^T (diag(eta) V)_hi + K^T (diag(eta) V)_lo on this wave's slab ----
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc) {
+      bf16x8 evh[Cfg::NTW], evl[Cfg::NTW];
+#pragma unroll
+      for (int n = 0; n < Cfg::NTW; ++n) {
+        const int o0 = vtr + 32 * kc * TV * 2 + 32 * (NT0 + n), o1 = o0 + 16 * TV * 2;
+        evh[n] = join(lds_read_tr16(evb + o0), lds_read_tr16(evb + o1));
+        evl[n] = join(lds_read_tr16(evb + Cfg::V_BYTES + o0), lds_read_tr16(evb + Cfg::V_BYTES + o1));
+      }
+#pragma unroll
+      for (int j = 0; j < Cfg::MTW; ++j) {
+        const int o0 = ktr[j] + 32 * kc * ROWB, o1 = o0 + 16 * ROWB;
+        const bf16x8 a = join(lds_read_tr16(kst + o0), lds_read_tr16(kst + o1));
+#pragma unroll
+        for (int n = 0; n < Cfg::NTW; ++n) {
+          S[j][n] = mfma16(a, evh[n], S[j][n]);
+          S[j][n] = mfma16(a, evl[n], S[j][n]);
+        }
+      }
+    }
+    write_s_lds();
+    qslot = qslot == 2 ? 0 : qslot + 1;
+    vslot = vslot1;
+  }
+
+  wait_vm_barrier<0>();
+#pragma unroll
+  for (int j = 0; j < Cfg::MTW; ++j)
+#pragma unroll
+    for (int n = 0; n < Cfg::NTW; ++n)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        P.Wh[(size_t)(SLAB + 16 * j + 4 * g + r) * DV + tv0 + 16 * (NT0 + n) + li] = S[j][n][r];
+}
+
+template <int DK, int TV, int NW>
+__global__ __launch_bounds__(NW * 64, 1) void per_token_bf16_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     const float* __restrict__ eta, const float* __restrict__ W0, bf16* __restrict__ O,
     float* __restrict__ Wout, int T, int DV) {
-  using Cfg = PerTokenCfg<DK, C, TV, STAGES>;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int NV = DV / TV;
   const int nblocks = gridDim.x;
   const int logical = (nblocks % 8 == 0) ? xcd_logical_block(blockIdx.x, nblocks) : blockIdx.x;
   const int bh = logical / NV;
-  const int tv0 = (logical % NV) * TV;
-  const int tid = threadIdx.x;
-  const int w = tid >> 6;
-  const int l = tid & 63;
-  const int g = l >> 4;
-  const int li = l & 15;
-  const int nchunks = (T + C - 1) / C;
-
-  const bf16* Qh = Q + (size_t)bh * T * DK;
-  const bf16* Kh = K + (size_t)bh * T * DK;
-  const bf16* Vh = V + (size_t)bh * T * DV;
-  const float* Eh = eta + (size_t)bh * T;
-  bf16* Oh = O + (size_t)bh * T * DV;
-
-  unsigned char* stage_base = smem;
-  unsigned char* s_lds = smem + STAGES * Cfg::STAGE_BYTES;
-  unsigned char* o_lds = s_lds + 4 * Cfg::S_BYTES;
-
-  // ---- issue the asynchronous loads of one chunk into one stage ----
-  auto issue_loads = [&](int c, int stage) {
-    unsigned char* st = stage_base + stage * Cfg::STAGE_BYTES;
-    const int t0 = c * C;
-    // Q and K: slot s (16 B) -> row s / CPR, physical piece s % CPR, logical piece p ^ (row & 7)
-#pragma unroll
-    for (int k = 0; k < Cfg::QI; ++k) {
-      const int s = (w * Cfg::QI + k) * 64 + l;
-      const int row = s / Cfg::CPR;
-      const int lp = (s % Cfg::CPR) ^ (row & 7);
-      const int t = min(t0 + row, T - 1);
-      g2lds16(Qh + (size_t)t * DK + lp * 8, st + (w * Cfg::QI + k) * 1024);
+  PerTokenPtrs P;
+  P.Qh = Q + (size_t)bh * T * DK;
+  P.Kh = K + (size_t)bh * T * DK;
+  P.Vh = V + (size_t)bh * T * DV;
+  P.Eh = eta + (size_t)bh * T;
+  P.Oh = O + (size_t)bh * T * DV;
+  P.W0h = W0 + (size_t)bh * DK * DV;
+  P.Wh = Wout + (size_t)bh * DK * DV;
+  P.T = T;
+  P.DV = DV;
+  P.tv0 = (logical % NV) * TV;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int l = threadIdx.x & 63;
+  if constexpr (NW == 4) {
+    switch (w) {
+      case 0: per_token_wave<DK, TV, NW, 0>(P, smem, l); break;
+      case 1: per_token_wave<DK, TV, NW, 1>(P, smem, l); break;
+      case 2: per_token_wave<DK, TV, NW, 2>(P, smem, l); break;
+      default: per_token_wave<DK, TV, NW, 3>(P, smem, l); break;
     }
-#pragma unroll
-    for (int k = 0; k < Cfg::QI; ++k) {
-      const int s = (w * Cfg::QI + k) * 64 + l;
-      const int row = s / Cfg::CPR;
-      const int lp = (s % Cfg::CPR) ^ (row & 7);
-      const int t = min(t0 + row, T - 1);
-      g2lds16(Kh + (size_t)t * DK + lp * 8, st + Cfg::Q_BYTES + (w * Cfg::QI + k) * 1024);
+  } else {
+    switch (w) {
+      case 0: per_token_wave<DK, TV, NW, 0>(P, smem, l); break;
+      case 1: per_token_wave<DK, TV, NW, 1>(P, smem, l); break;
+      case 2: per_token_wave<DK, TV, NW, 2>(P, smem, l); break;
+      case 3: per_token_wave<DK, TV, NW, 3>(P, smem, l); break;
+      case 4: per_token_wave<DK, TV, NW, 4>(P, smem, l); break;
+      case 5: per_token_wave<DK, TV, NW, 5>(P, smem, l); break;
+      case 6: per_token_wave<DK, TV, NW, 6>(P, smem, l); break;
+      default: per_token_wave<DK, TV, NW, 7>(P, smem, l); break;
     }
-    // V tile: pieces in row-major order, TV/8 pieces per row
-#pragma unroll
-    for (int k = 0; k < Cfg::VI; ++k) {
-      const int pw = k * 64 + l;
-      if (pw < Cfg::VPW) {
-        const int p = w * Cfg::VPW + pw;
-        const int row = p / (TV / 8);
-        const int col = (p % (TV / 8)) * 8;
-        const int t = min(t0 + row, T - 1);
-        g2lds16(Vh + (size_t)t * DV + tv0 + col, st + 2 * Cfg::Q_BYTES + (w * Cfg::VPW + k * 64) * 16);
-      }
-    }
-    // eta: C/4 tokens per wave, 4 bytes per lane
-    if (l < C / Cfg::NW) {
-      const int t = min(t0 + w * (C / Cfg::NW) + l, T - 1);
-      g2lds4(Eh + t, st + 2 * Cfg::Q_BYTES + Cfg::V_BYTES + w * (C / Cfg::NW) * 4);
-    }
-  };
-
-  // ---- state: S[mt][nt] holds rows w*SROWS + 16mt + 4g + r, column 16nt + li ----
-  floatx4 S[Cfg::MT][Cfg::NT];
-  const float* W0h = W0 + (size_t)bh * DK * DV;
-#pragma unroll
-  for (int mt = 0; mt < Cfg::MT; ++mt)
-#pragma unroll
-    for (int nt = 0; nt < Cfg::NT; ++nt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        S[mt][nt][r] = W0h[(size_t)(w * Cfg::SROWS + 16 * mt + 4 * g + r) * DV + tv0 + 16 * nt + li];
-
-  // bf16 hi/lo planes of S^T: S = hi + lo up to 2^-16 relative
-  auto write_s_lds = [&](int buf) {
-    unsigned char* sb = s_lds + buf * 2 * Cfg::S_BYTES;
-#pragma unroll
-    for (int mt = 0; mt < Cfg::MT; ++mt)
-#pragma unroll
-      for (int nt = 0; nt < Cfg::NT; ++nt) {
-        bf16x4 hi, lo;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          hi[r] = (bf16)S[mt][nt][r];
-          lo[r] = (bf16)(S[mt][nt][r] - (float)hi[r]);
-        }
-        const int off = (16 * nt + li) * Cfg::S_ROW + (w * Cfg::SROWS + 16 * mt + 4 * g) * 2;
-        *(bf16x4*)(sb + off) = hi;
-        *(bf16x4*)(sb + Cfg::S_BYTES + off) = lo;
-      }
-  };
-  write_s_lds(0);
-
-  auto store_o = [&](int c) {
-    const unsigned char* ob = o_lds + (c & 1) * Cfg::O_BYTES;
-    const int t0 = c * C;
-#pragma unroll
-    for (int k = 0; k < Cfg::OI; ++k) {
-      const int pw = k * 64 + l;
-      if (pw < Cfg::VPW) {
-        const int p = w * Cfg::VPW + pw;
-        const int row = p / (TV / 8);
-        const int col = (p % (TV / 8)) * 8;
-        const uint4 v = *(const uint4*)(ob + row * Cfg::O_ROW + col * 2);
-        if (t0 + row < T) *(uint4*)(Oh + (size_t)(t0 + row) * DV + tv0 + col) = v;
-      }
-    }
-  };
-
-#pragma unroll
-  for (int s = 0; s < STAGES - 1; ++s)
-    if (s < nchunks) issue_loads(s, s);
-
-  for (int c = 0; c < nchunks; ++c) {
-    if (c >= STAGES - 1 && c + STAGES - 1 <= nchunks)
-      wait_vm_barrier<Cfg::STEADY_VMCNT>();
-    else
-      wait_vm_barrier<0>();
-    if (c >= 1) store_o(c - 1);
-    if (c + STAGES - 1 < nchunks) issue_loads(c + STAGES - 1, (c + STAGES - 1) % STAGES);
-
-    const unsigned char* st = stage_base + (c % STAGES) * Cfg::STAGE_BYTES;
-    const unsigned char* qst = st;
-    const unsigned char* kst = st + Cfg::Q_BYTES;
-    const unsigned char* vs = st + 2 * Cfg::Q_BYTES;
-    const float* es = (const float*)(st + 2 * Cfg::Q_BYTES + Cfg::V_BYTES);
-    const unsigned char* sb = s_lds + (c & 1) * 2 * Cfg::S_BYTES;
-    const int t0 = c * C;
-
-    // eta of every token row this lane touches (zero past the end of the
-    // sequence), raw V operands for A V, and hi/lo bf16 pairs of diag(eta) V
-    // for the state update.  Row order of a 32-token step: rows 4g..4g+3
-    // then 16+4g..16+4g+3 (the transposed-read order).
-    float e[Cfg::KC][2][4];
-    bf16x8 vop[Cfg::KC][Cfg::NT], evh[Cfg::KC][Cfg::NT], evl[Cfg::KC][Cfg::NT];
-#pragma unroll
-    for (int kc = 0; kc < Cfg::KC; ++kc) {
-      bf16x4 half[2][Cfg::NT];
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int rb = 32 * kc + 16 * h + 4 * g;
-        const floatx4 e4 = *(const floatx4*)(es + rb);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) e[kc][h][r] = (t0 + rb + r < T) ? e4[r] : 0.0f;
-#pragma unroll
-        for (int nt = 0; nt < Cfg::NT; ++nt) {
-          const int row = rb + (li >> 2);
-          half[h][nt] = lds_read_tr16(vs + row * (TV * 2) + (16 * nt + 4 * (li & 3)) * 2);
-        }
-      }
-#pragma unroll
-      for (int nt = 0; nt < Cfg::NT; ++nt) {
-        vop[kc][nt] = join(half[0][nt], half[1][nt]);
-        bf16x8 hi, lo;
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float f = e[kc][h][r] * (float)half[h][nt][r];
-            hi[4 * h + r] = (bf16)f;
-            lo[4 * h + r] = (bf16)(f - (float)hi[4 * h + r]);
-          }
-        evh[kc][nt] = hi;
-        evl[kc][nt] = lo;
-      }
-    }
-
-    // outputs of this wave's i-blocks
-#pragma unroll
-    for (int ibw = 0; ibw < Cfg::IBW; ++ibw) {
-      const int ib = (ibw == 0) ? w : (Cfg::IB - 1 - w);
-      bf16x8 qop[Cfg::KT];
-#pragma unroll
-      for (int ks = 0; ks < Cfg::KT; ++ks) {
-        const int row = 16 * ib + li;
-        const int piece = (4 * ks + g) ^ (row & 7);
-        qop[ks] = *(const bf16x8*)(qst + row * (DK * 2) + piece * 16);
-      }
-      floatx4 acc[Cfg::NT];
-#pragma unroll
-      for (int nt = 0; nt < Cfg::NT; ++nt) acc[nt] = floatx4{0.f, 0.f, 0.f, 0.f};
-      // intra-chunk: P^T tiles (key rows j, query columns i) for j-blocks
-      // 0..ib, scaled by eta_j, causally masked, split into bf16 hi + lo
-#pragma unroll
-      for (int kc = 0; kc < Cfg::KC; ++kc) {
-        if (32 * kc > 16 * ib + 15) break;
-        bf16x4 ph[2], pl[2];
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int jb = 2 * kc + h;
-          if (jb > ib) {
-            ph[h] = bf16x4{(bf16)0.f, (bf16)0.f, (bf16)0.f, (bf16)0.f};
-            pl[h] = ph[h];
-            continue;
-          }
-          floatx4 p = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int ks = 0; ks < Cfg::KT; ++ks) {
-            const int row = 16 * jb + li;
-            const int piece = (4 * ks + g) ^ (row & 7);
-            const bf16x8 kop = *(const bf16x8*)(kst + row * (DK * 2) + piece * 16);
-            p = mfma16(kop, qop[ks], p);
-          }
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            float f = p[r] * e[kc][h][r];
-            if (jb == ib && 4 * g + r > li) f = 0.f;
-            ph[h][r] = (bf16)f;
-            pl[h][r] = (bf16)(f - (float)ph[h][r]);
-          }
-        }
-        const bf16x8 ah = join(ph[0], ph[1]);
-        const bf16x8 al = join(pl[0], pl[1]);
-#pragma unroll
-        for (int nt = 0; nt < Cfg::NT; ++nt) {
-          acc[nt] = mfma16(ah, vop[kc][nt], acc[nt]);
-          acc[nt] = mfma16(al, vop[kc][nt], acc[nt]);
-        }
-      }
-      // inter-chunk: Q (S_hi + S_lo)
-#pragma unroll
-      for (int nt = 0; nt < Cfg::NT; ++nt)
-#pragma unroll
-        for (int ks = 0; ks < Cfg::KT; ++ks) {
-          const int off = (16 * nt + li) * Cfg::S_ROW + (32 * ks + 8 * g) * 2;
-          const bf16x8 sh = *(const bf16x8*)(sb + off);
-          const bf16x8 sl = *(const bf16x8*)(sb + Cfg::S_BYTES + off);
-          acc[nt] = mfma16(qop[ks], sh, acc[nt]);
-          acc[nt] = mfma16(qop[ks], sl, acc[nt]);
-        }
-      // stage the outputs (bf16) for the coalesced store one chunk later
-      unsigned char* ob = o_lds + (c & 1) * Cfg::O_BYTES;
-#pragma unroll
-      for (int nt = 0; nt < Cfg::NT; ++nt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          *(bf16*)(ob + (16 * ib + 4 * g + r) * Cfg::O_ROW + (16 * nt + li) * 2) = (bf16)acc[nt][r];
-    }
-
-    // state update: S += K^T diag(eta) V on this wave's rows
-#pragma unroll
-    for (int mt = 0; mt < Cfg::MT; ++mt) {
-      const int m0 = w * Cfg::SROWS + 16 * mt;
-#pragma unroll
-      for (int kc = 0; kc < Cfg::KC; ++kc) {
-        bf16x4 kh[2];
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int row = 32 * kc + 16 * h + 4 * g + (li >> 2);
-          const int col = m0 + 4 * (li & 3);
-          const int piece = (col >> 3) ^ (row & 7);
-          kh[h] = lds_read_tr16(kst + row * (DK * 2) + piece * 16 + (col & 7) * 2);
-        }
-        const bf16x8 a = join(kh[0], kh[1]);
-#pragma unroll
-        for (int nt = 0; nt < Cfg::NT; ++nt) {
-          S[mt][nt] = mfma16(a, evh[kc][nt], S[mt][nt]);
-          S[mt][nt] = mfma16(a, evl[kc][nt], S[mt][nt]);
-        }
-      }
-    }
-    write_s_lds((c + 1) & 1);
   }
-
-  wait_vm_barrier<0>();
-  if (nchunks > 0) store_o(nchunks - 1);
-  float* Wh = Wout + (size_t)bh * DK * DV;
-#pragma unroll
-  for (int mt = 0; mt < Cfg::MT; ++mt)
-#pragma unroll
-    for (int nt = 0; nt < Cfg::NT; ++nt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        Wh[(size_t)(w * Cfg::SROWS + 16 * mt + 4 * g + r) * DV + tv0 + 16 * nt + li] = S[mt][nt][r];
 }
 
 // ---------------------------------------------------------------------------
@@ -433,10 +496,10 @@ static size_t fp32_lds_bytes() {
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
-template <int DK, int C, int TV, int STAGES>
+template <int DK, int TV, int NW = (TV >= 32 ? 8 : 4)>
 static hipError_t launch_bf16(const PerTokenArgs& a, hipStream_t stream) {
-  using Cfg = PerTokenCfg<DK, C, TV, STAGES>;
-  auto kern = per_token_bf16_kernel<DK, C, TV, STAGES>;
+  using Cfg = PerTokenCfg<DK, TV, NW>;
+  auto kern = per_token_bf16_kernel<DK, TV, NW>;
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, Cfg::LDS_BYTES);
   if (e != hipSuccess) return e;
   const int grid = (int)(a.B * a.H * (a.DV / TV));
@@ -480,13 +543,10 @@ hipError_t launch_per_token(const PerTokenArgs& a, hipStream_t stream) {
     return c == 16 ? launch_fp32<128, 16>(a, stream) : c == 32 ? launch_fp32<128, 32>(a, stream) : launch_fp32<128, 64>(a, stream);
   }
   const int tv = per_token_bf16_tv(a.B * a.H, a.DV);
-  if (a.DK == 128) {
-    if (tv == 16) return launch_bf16<128, 64, 16, 3>(a, stream);
-    return launch_bf16<128, 64, 32, 3>(a, stream);
-  }
-  if (tv == 16) return launch_bf16<64, 64, 16, 4>(a, stream);
-  if (tv == 64) return launch_bf16<64, 64, 64, 4>(a, stream);
-  return launch_bf16<64, 64, 32, 4>(a, stream);
+  if (a.DK == 128) return tv == 16 ? launch_bf16<128, 16>(a, stream) : launch_bf16<128, 32>(a, stream);
+  if (tv == 16) return launch_bf16<64, 16>(a, stream);
+  if (tv == 64) return launch_bf16<64, 64>(a, stream);
+  return launch_bf16<64, 32>(a, stream);
 }
 
 }  // namespace ttt
