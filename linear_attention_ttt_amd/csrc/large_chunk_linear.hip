@@ -9,13 +9,17 @@
 // max(||column||_2, 1e-12).
 //
 // The update K_c^T diag(eta_c) V_c does not depend on W, so it is computed
-// for every chunk in parallel; only the normalise-scan is sequential:
-//   1. lact_delta_kernel  - partial dW over token slices of every chunk
-//                           (bf16 MFMA, diag(eta) V split into bf16 hi+lo)
-//   2. lact_scan_kernel   - per head: sum the partials, add, normalise,
-//                           keep W_{c-1} of every chunk (transposed, fp32)
-//   3. lact_read_kernel   - O_c = Q_c W_{c-1} for all chunks in parallel
-//                           (W split into bf16 hi+lo)
+// for every chunk in parallel; the normalisation acts on each column of W
+// separately, so the sequential part is a scan per column:
+//   1. lact_delta_kernel - partial updates over token slices of every chunk
+//                          (bf16 MFMA, diag(eta) V split into bf16 hi + lo),
+//                          written transposed [out][in]
+//   2. lact_scan_kernel  - one wave per (head, column): sums the slices,
+//                          adds, normalises, and keeps W_{c-1} of every
+//                          chunk (transposed, fp32)
+//   3. lact_read_kernel  - O_c = Q_c W_{c-1}, a quarter chunk per workgroup,
+//                          W staged once in LDS as bf16 hi + lo, queries
+//                          streamed per wave through a direct-to-LDS ring
 #include "device_common.h"
 #include "kernels.h"
 
@@ -23,35 +27,44 @@ namespace ttt {
 
 namespace {
 
-constexpr int LC_STEP = 64;     // tokens per LDS step in the update kernel
-constexpr int LC_SLICE = 1024;  // tokens per workgroup slice of a chunk
-constexpr int LC_READ_TILE = 64;
+constexpr int LC_STEP = 64;       // tokens per LDS step in the update kernel
+constexpr int LC_MAXSPLIT = 4;    // token slices per chunk
+constexpr int LC_MINSLICE = 1024;
 
-inline int64_t nsplit_of(int64_t chunk) { return (chunk + LC_SLICE - 1) / LC_SLICE; }
+inline int64_t nsplit_of(int64_t chunk) {
+  int64_t n = (chunk + LC_MINSLICE - 1) / LC_MINSLICE;
+  return n < 1 ? 1 : (n > LC_MAXSPLIT ? LC_MAXSPLIT : n);
+}
+inline int64_t slice_of(int64_t chunk) {
+  const int64_t n = nsplit_of(chunk);
+  return ((chunk + n - 1) / n + LC_STEP - 1) / LC_STEP * LC_STEP;
+}
 
 // ---------------------------------------------------------------------------
 // 1. partial dW = sum_{t in slice} k_t^T (eta_t v_t), one slice per workgroup
 // ---------------------------------------------------------------------------
 template <int D>
-__global__ __launch_bounds__(256) void lact_delta_kernel(const bf16* __restrict__ K, const bf16* __restrict__ V,
-                                                         const float* __restrict__ eta, float* __restrict__ part,
-                                                         int T, int chunk, int nchunks, int nsplit) {
+__global__ __launch_bounds__(256, 4) void lact_delta_kernel(const bf16* __restrict__ K, const bf16* __restrict__ V,
+                                                            const float* __restrict__ eta, float* __restrict__ part,
+                                                            int T, int chunk, int nchunks, int nsplit, int slice) {
   constexpr int ROW = D * 2 + 32;              // padded LDS row (bytes)
   constexpr int PIECES = LC_STEP * D / 8;      // 16-byte pieces per tile
   constexpr int PPT = PIECES / 256;            // pieces per thread
   constexpr int QW = D / 2;                    // quadrant width per wave
   constexpr int TW = QW / 32;                  // 32x32 tiles per quadrant side
-  __shared__ __attribute__((aligned(16))) unsigned char ks[2][LC_STEP * ROW];
-  __shared__ __attribute__((aligned(16))) unsigned char vh[2][LC_STEP * ROW];
-  __shared__ __attribute__((aligned(16))) unsigned char vl[2][LC_STEP * ROW];
+  __shared__ __attribute__((aligned(16))) unsigned char lds[3 * LC_STEP * ROW];
+  unsigned char* ks = lds;
+  unsigned char* vh = lds + LC_STEP * ROW;
+  unsigned char* vl = lds + 2 * LC_STEP * ROW;
+  static_assert(64 * (D + 1) * 4 <= 3 * LC_STEP * ROW, "transpose buffer");
 
   const int split = blockIdx.x % nsplit;
   const int c = (blockIdx.x / nsplit) % nchunks;
   const int bh = blockIdx.x / (nsplit * nchunks);
   const int cstart = c * chunk;
   const int cend = min(cstart + chunk, T);
-  const int s0 = cstart + split * LC_SLICE;
-  const int s1 = min(s0 + LC_SLICE, cend);
+  const int s0 = cstart + split * slice;
+  const int s1 = min(s0 + slice, cend);
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, G = l >> 4, L = l & 15;
   const bf16* Kh = K + (size_t)bh * T * D;
   const bf16* Vh = V + (size_t)bh * T * D;
@@ -71,12 +84,12 @@ __global__ __launch_bounds__(256) void lact_delta_kernel(const bf16* __restrict_
       ereg[k] = t < s1 ? Eh[tc] : 0.f;
     }
   };
-  auto store = [&](int buf) {
+  auto store = [&]() {
 #pragma unroll
     for (int k = 0; k < PPT; ++k) {
       const int p = k * 256 + tid;
       const int row = p / (D / 8), col = (p % (D / 8)) * 8;
-      *(uint4*)(ks[buf] + row * ROW + col * 2) = kreg[k];
+      *(uint4*)(ks + row * ROW + col * 2) = kreg[k];
       const bf16x8 v = __builtin_bit_cast(bf16x8, vreg[k]);
       bf16x8 hi, lo;
 #pragma unroll
@@ -85,8 +98,8 @@ __global__ __launch_bounds__(256) void lact_delta_kernel(const bf16* __restrict_
         hi[j] = (bf16)f;
         lo[j] = (bf16)(f - (float)hi[j]);
       }
-      *(bf16x8*)(vh[buf] + row * ROW + col * 2) = hi;
-      *(bf16x8*)(vl[buf] + row * ROW + col * 2) = lo;
+      *(bf16x8*)(vh + row * ROW + col * 2) = hi;
+      *(bf16x8*)(vl + row * ROW + col * 2) = lo;
     }
   };
 
@@ -96,14 +109,12 @@ __global__ __launch_bounds__(256) void lact_delta_kernel(const bf16* __restrict_
 #pragma unroll
     for (int j = 0; j < TW; ++j) acc[i][j] = floatx16{};
   const int a0 = (w >> 1) * QW, b0 = (w & 1) * QW;
-  const int nsteps = (s1 - s0 + LC_STEP - 1) / LC_STEP;
-  if (nsteps > 0) {
-    load(s0);
-    store(0);
-  }
-  __syncthreads();
+  const int nsteps = s1 > s0 ? (s1 - s0 + LC_STEP - 1) / LC_STEP : 0;
+  if (nsteps > 0) load(s0);
   for (int st = 0; st < nsteps; ++st) {
-    const int buf = st & 1;
+    if (st > 0) __syncthreads();               // everyone is done with the previous tile
+    store();
+    __syncthreads();
     if (st + 1 < nsteps) load(s0 + (st + 1) * LC_STEP);
 #pragma unroll
     for (int k0 = 0; k0 < LC_STEP; k0 += 16) {
@@ -113,10 +124,10 @@ __global__ __launch_bounds__(256) void lact_delta_kernel(const bf16* __restrict_
 #pragma unroll
       for (int i = 0; i < TW; ++i) {
         const int ca = a0 + 32 * i + 16 * (G & 1) + 4 * (L & 3);
-        A[i] = join(lds_read_tr16(ks[buf] + r0 * ROW + ca * 2), lds_read_tr16(ks[buf] + (r0 + 4) * ROW + ca * 2));
+        A[i] = join(lds_read_tr16(ks + r0 * ROW + ca * 2), lds_read_tr16(ks + (r0 + 4) * ROW + ca * 2));
         const int cb = b0 + 32 * i + 16 * (G & 1) + 4 * (L & 3);
-        Bh[i] = join(lds_read_tr16(vh[buf] + r0 * ROW + cb * 2), lds_read_tr16(vh[buf] + (r0 + 4) * ROW + cb * 2));
-        Bl[i] = join(lds_read_tr16(vl[buf] + r0 * ROW + cb * 2), lds_read_tr16(vl[buf] + (r0 + 4) * ROW + cb * 2));
+        Bh[i] = join(lds_read_tr16(vh + r0 * ROW + cb * 2), lds_read_tr16(vh + (r0 + 4) * ROW + cb * 2));
+        Bl[i] = join(lds_read_tr16(vl + r0 * ROW + cb * 2), lds_read_tr16(vl + (r0 + 4) * ROW + cb * 2));
       }
 #pragma unroll
       for (int i = 0; i < TW; ++i)
@@ -126,131 +137,199 @@ __global__ __launch_bounds__(256) void lact_delta_kernel(const bf16* __restrict_
           acc[i][j] = mfma32(A[i], Bl[j], acc[i][j]);
         }
     }
-    if (st + 1 < nsteps) store(buf ^ 1);
-    __syncthreads();
   }
+  // transpose through LDS, 64 output columns b at a time (fp32 [b][a], padded),
+  // so the partial is written [out][in] with coalesced stores
   float* P = part + (((size_t)bh * nchunks + c) * nsplit + split) * D * D;
+  float* tr = reinterpret_cast<float*>(lds);
 #pragma unroll
-  for (int i = 0; i < TW; ++i)
+  for (int bp = 0; bp < D / 64; ++bp) {
+    __syncthreads();
 #pragma unroll
-    for (int j = 0; j < TW; ++j)
+    for (int i = 0; i < TW; ++i)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int a = a0 + 32 * i + 8 * (r >> 2) + 4 * (l >> 5) + (r & 3);
+      for (int j = 0; j < TW; ++j) {
         const int b = b0 + 32 * j + (l & 31);
-        P[(size_t)a * D + b] = acc[i][j][r];
+        if (b / 64 != bp) continue;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int a = a0 + 32 * i + 8 * (r >> 2) + 4 * (l >> 5) + (r & 3);
+          tr[(b - 64 * bp) * (D + 1) + a] = acc[i][j][r];
+        }
       }
+    __syncthreads();
+    for (int i = tid; i < 64 * D; i += 256) P[(size_t)(64 * bp) * D + i] = tr[(i / D) * (D + 1) + (i % D)];
+  }
 }
 
 // ---------------------------------------------------------------------------
-// 2. normalise-scan, one workgroup per (b,h).  Wave w owns columns
-//    [w*D/4, (w+1)*D/4); a column's rows are spread over 64/(D/4) lanes.
+// 2. normalise-scan: one wave per (head, column j).  Lane l holds rows
+//    l, l+64, ... of the column.  Updates of a window of chunks are loaded
+//    in one burst (they do not depend on W), then scanned.
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256) void lact_scan_kernel(const float* __restrict__ W0, const float* __restrict__ part,
                                                         float* __restrict__ wprev_t, float* __restrict__ Wout,
                                                         int nchunks, int nsplit) {
-  constexpr int CPW = D / 4;          // columns per wave
-  constexpr int LPC = 64 / CPW;       // lanes per column
-  constexpr int RPL = D / LPC;        // rows per lane
-  const int bh = blockIdx.x;
+  constexpr int RPL = D / 64;
+  constexpr int WIN = D == 64 ? 12 : 6;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
-  const int col = w * CPW + (l % CPW);
-  const int rbase = (l / CPW) * RPL;
-  float Wr[RPL];
+  const int j = (blockIdx.x % (D / 4)) * 4 + w;
+  const int bh = blockIdx.x / (D / 4);
+  float Wc[RPL];
   const float* W0h = W0 + (size_t)bh * D * D;
 #pragma unroll
-  for (int r = 0; r < RPL; ++r) Wr[r] = W0h[(size_t)(rbase + r) * D + col];
-  float nxt[RPL];
-  auto fetch = [&](int c) {
+  for (int r = 0; r < RPL; ++r) Wc[r] = W0h[(size_t)(l + 64 * r) * D + j];
+  for (int c0 = 0; c0 < nchunks; c0 += WIN) {
+    float d[WIN][RPL];
 #pragma unroll
-    for (int r = 0; r < RPL; ++r) nxt[r] = 0.f;
-    for (int s = 0; s < nsplit; ++s) {
-      const float* P = part + (((size_t)bh * nchunks + c) * nsplit + s) * D * D;
+    for (int i = 0; i < WIN; ++i)
 #pragma unroll
-      for (int r = 0; r < RPL; ++r) nxt[r] += P[(size_t)(rbase + r) * D + col];
-    }
-  };
-  if (nchunks > 0) fetch(0);
-  for (int c = 0; c < nchunks; ++c) {
-    // keep W_{c-1} for the read kernel, transposed: wprev_t[c][col][row]
-    float* Wt = wprev_t + ((size_t)bh * nchunks + c) * D * D + (size_t)col * D + rbase;
+      for (int r = 0; r < RPL; ++r) d[i][r] = 0.f;
+    // unconditional (clamped) loads so the whole window is in flight at once
 #pragma unroll
-    for (int r = 0; r < RPL; r += 4) *(floatx4*)(Wt + r) = floatx4{Wr[r], Wr[r + 1], Wr[r + 2], Wr[r + 3]};
-    float d[RPL];
+    for (int s = 0; s < LC_MAXSPLIT; ++s) {
+      const int sc = min(s, nsplit - 1);
 #pragma unroll
-    for (int r = 0; r < RPL; ++r) d[r] = nxt[r];
-    if (c + 1 < nchunks) fetch(c + 1);
-    float ss = 0.f;
+      for (int i = 0; i < WIN; ++i) {
+        const int cc = min(c0 + i, nchunks - 1);
+        const bool use = s < nsplit && c0 + i < nchunks;
+        const float* Pc = part + ((((size_t)bh * nchunks + cc) * nsplit + sc) * D + j) * D;
 #pragma unroll
-    for (int r = 0; r < RPL; ++r) {
-      Wr[r] += d[r];
-      ss = fmaf(Wr[r], Wr[r], ss);
+        for (int r = 0; r < RPL; ++r) {
+          const float v = Pc[l + 64 * r];
+          d[i][r] += use ? v : 0.f;
+        }
+      }
     }
 #pragma unroll
-    for (int m = CPW; m < 64; m <<= 1) ss += __shfl_xor(ss, m);
-    const float inv = 1.0f / fmaxf(sqrtf(ss), 1e-12f);
+    for (int i = 0; i < WIN; ++i) {
+      const int c = c0 + i;
+      if (c >= nchunks) break;
+      float* Wt = wprev_t + (((size_t)bh * nchunks + c) * D + j) * D;   // W_{c-1}, transposed
+      float ss = 0.f;
 #pragma unroll
-    for (int r = 0; r < RPL; ++r) Wr[r] *= inv;
+      for (int r = 0; r < RPL; ++r) {
+        Wt[l + 64 * r] = Wc[r];
+        Wc[r] += d[i][r];
+        ss = fmaf(Wc[r], Wc[r], ss);
+      }
+#pragma unroll
+      for (int m = 1; m < 64; m <<= 1) ss += __shfl_xor(ss, m);
+      const float inv = 1.0f / fmaxf(sqrtf(ss), 1e-12f);
+#pragma unroll
+      for (int r = 0; r < RPL; ++r) Wc[r] *= inv;
+    }
   }
   float* Wo = Wout + (size_t)bh * D * D;
 #pragma unroll
-  for (int r = 0; r < RPL; ++r) Wo[(size_t)(rbase + r) * D + col] = Wr[r];
+  for (int r = 0; r < RPL; ++r) Wo[(size_t)(l + 64 * r) * D + j] = Wc[r];
 }
 
 // ---------------------------------------------------------------------------
-// 3. O_c = Q_c W_{c-1}.  One workgroup per 64-token tile of a chunk; wave w
-//    computes output columns [w*D/4, (w+1)*D/4) as O^T = W^T Q^T with W in
-//    bf16 hi+lo.
+// 3. O_c = Q_c W_{c-1}.  One workgroup per (head, chunk, part of a chunk);
+//    W_{c-1} staged once in LDS as bf16 hi + lo (rows = output unit); each
+//    wave streams its own 16-token rows of every 64-token tile through a
+//    private direct-to-LDS ring and computes O^T = W^T Q^T for them.
 // ---------------------------------------------------------------------------
+constexpr int LR_STAGES = 4;
 template <int D>
-__global__ __launch_bounds__(256) void lact_read_kernel(const bf16* __restrict__ Q, const float* __restrict__ wprev_t,
-                                                        bf16* __restrict__ O, int T, int chunk, int nchunks,
-                                                        int tiles_per_chunk) {
-  constexpr int MTW = D / 64;   // 16-row M tiles (output columns) per wave
-  constexpr int KS = D / 32;
-  const int tile = blockIdx.x % tiles_per_chunk;
-  const int c = (blockIdx.x / tiles_per_chunk) % nchunks;
-  const int bh = blockIdx.x / (tiles_per_chunk * nchunks);
+struct LactReadCfg {
+  static constexpr int ROWB = D * 2;
+  static constexpr int W_BYTES = D * D * 2;                  // one bf16 plane of W^T, swizzled
+  static constexpr int QW_BYTES = 16 * ROWB;                 // one wave's 16 rows of a tile
+  static constexpr int QI = QW_BYTES / 1024;                 // DMA instructions per wave per tile
+  static constexpr int LDS = 2 * W_BYTES + 4 * LR_STAGES * QW_BYTES;
+  static constexpr int KT = D / 32;
+  static constexpr int MT = D / 16;
+  static constexpr int SWZ = D / 8 >= 16 ? 15 : D / 8 - 1;
+};
+
+template <int D>
+__global__ __launch_bounds__(256, 2) void lact_read_kernel(const bf16* __restrict__ Q, const float* __restrict__ wprev_t,
+                                                           bf16* __restrict__ O, int T, int chunk, int nchunks,
+                                                           int parts, int part_len) {
+  using Cfg = LactReadCfg<D>;
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  const int part = blockIdx.x % parts;
+  const int c = (blockIdx.x / parts) % nchunks;
+  const int bh = blockIdx.x / (parts * nchunks);
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g = l >> 4, li = l & 15;
   const int cend = min((c + 1) * chunk, T);
-  const int t0 = c * chunk + tile * LC_READ_TILE;
-  if (t0 >= cend) return;
+  const int t0 = c * chunk + part * part_len;
+  const int t1 = min(t0 + part_len, cend);
+  if (t0 >= t1) return;
+
+  // ---- W^T of this chunk as bf16 hi + lo planes [n][a], 16-byte pieces swizzled by n ----
   const float* Wt = wprev_t + ((size_t)bh * nchunks + c) * D * D;
-  bf16x8 wh[MTW][KS], wl[MTW][KS];
+  for (int p = tid; p < D * D / 8; p += 256) {
+    const int n = p / (D / 8), pc = p % (D / 8);
+    const floatx4 x0 = *(const floatx4*)(Wt + (size_t)n * D + pc * 8);
+    const floatx4 x1 = *(const floatx4*)(Wt + (size_t)n * D + pc * 8 + 4);
+    bf16x8 hi, lo;
 #pragma unroll
-  for (int m = 0; m < MTW; ++m)
-#pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      const float* p = Wt + (size_t)(w * (D / 4) + 16 * m + li) * D + 32 * s + 8 * g;
-      const floatx4 x0 = *(const floatx4*)p, x1 = *(const floatx4*)(p + 4);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float f = j < 4 ? x0[j] : x1[j - 4];
-        wh[m][s][j] = (bf16)f;
-        wl[m][s][j] = (bf16)(f - (float)wh[m][s][j]);
-      }
+    for (int j = 0; j < 8; ++j) {
+      const float f = j < 4 ? x0[j] : x1[j - 4];
+      hi[j] = (bf16)f;
+      lo[j] = (bf16)(f - (float)hi[j]);
     }
+    const int off = n * Cfg::ROWB + ((pc ^ (n & Cfg::SWZ)) << 4);
+    *(bf16x8*)(smem + off) = hi;
+    *(bf16x8*)(smem + Cfg::W_BYTES + off) = lo;
+  }
+  // per-lane offsets: natural operand reads (row 16*blk + li, k = 32ks + 8g)
+  int nat[Cfg::KT];
+#pragma unroll
+  for (int ks = 0; ks < Cfg::KT; ++ks) nat[ks] = li * Cfg::ROWB + (((4 * ks + g) ^ (li & Cfg::SWZ)) << 4);
+  // this wave's DMA: 16 rows of a tile = QI instructions; slot (lane) -> (row, piece)
+  unsigned qoff[Cfg::QI];
+#pragma unroll
+  for (int k = 0; k < Cfg::QI; ++k) {
+    const int s = k * 64 + l;
+    const int row = s / (D / 8);
+    qoff[k] = (unsigned)((16 * w + row) * Cfg::ROWB + (((s % (D / 8)) ^ (row & Cfg::SWZ)) << 4));
+  }
+  unsigned char* ring = smem + 2 * Cfg::W_BYTES + w * LR_STAGES * Cfg::QW_BYTES;
   const bf16* Qh = Q + (size_t)bh * T * D;
   bf16* Oh = O + (size_t)bh * T * D;
+  const int ntiles = (t1 - t0 + 63) / 64;
+  auto issue = [&](int i) {
+    const long long rem = (long long)t1 - (long long)(t0 + 64 * i);
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(Qh + (size_t)(t0 + 64 * i) * D, rem * Cfg::ROWB);
+    unsigned char* dst = ring + (i % LR_STAGES) * Cfg::QW_BYTES;
 #pragma unroll
-  for (int nt = 0; nt < LC_READ_TILE / 16; ++nt) {
-    const int t = t0 + 16 * nt + li;
-    const int tc = min(t, cend - 1);
-    bf16x8 qop[KS];
+    for (int k = 0; k < Cfg::QI; ++k) buf2lds16(r, qoff[k], dst + k * 1024);
+  };
 #pragma unroll
-    for (int s = 0; s < KS; ++s) qop[s] = *(const bf16x8*)(Qh + (size_t)tc * D + 32 * s + 8 * g);
+  for (int i = 0; i < LR_STAGES - 1; ++i) issue(i);
+  __syncthreads();                                  // W planes complete
+  const unsigned char* wh = smem;
+  const unsigned char* wl = smem + Cfg::W_BYTES;
+  for (int i = 0; i < ntiles; ++i) {
+    // this wave's rows of tile i have landed (later tiles may still be in flight)
+    wait_vm<(LR_STAGES - 2) * Cfg::QI>();
+    issue(i + LR_STAGES - 1);
+    const unsigned char* qs = ring + (i % LR_STAGES) * Cfg::QW_BYTES;   // this wave's 16 rows
+    bf16x8 qop[Cfg::KT];
 #pragma unroll
-    for (int m = 0; m < MTW; ++m) {
+    for (int ks = 0; ks < Cfg::KT; ++ks) qop[ks] = *(const bf16x8*)(qs + nat[ks]);
+    const long long rem = (long long)t1 - (long long)(t0 + 64 * i);
+    const __amdgpu_buffer_rsrc_t ro = make_rsrc(Oh + (size_t)(t0 + 64 * i) * D, rem * Cfg::ROWB);
+#pragma unroll
+    for (int m = 0; m < Cfg::MT; ++m) {
       floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        acc = mfma16(wh[m][s], qop[s], acc);
-        acc = mfma16(wl[m][s], qop[s], acc);
+      for (int ks = 0; ks < Cfg::KT; ++ks) {
+        acc = mfma16(*(const bf16x8*)(wh + m * 16 * Cfg::ROWB + nat[ks]), qop[ks], acc);
+        acc = mfma16(*(const bf16x8*)(wl + m * 16 * Cfg::ROWB + nat[ks]), qop[ks], acc);
       }
-      if (t < cend) *(bf16x4*)(Oh + (size_t)t * D + w * (D / 4) + 16 * m + 4 * g) = to_bf16x4(acc[0], acc[1], acc[2], acc[3]);
+      // lane holds O[16w + li][16m + 4g .. +3]
+      const bf16x4 o = to_bf16x4(acc[0], acc[1], acc[2], acc[3]);
+      __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(uint2v, o), ro,
+                                            (unsigned)((16 * w + li) * Cfg::ROWB + (16 * m + 4 * g) * 2), 0, 0);
     }
   }
+  wait_vm<0>();
 }
 
 template <int D>
@@ -258,22 +337,30 @@ hipError_t launch_lact(const LargeChunkArgs& a, hipStream_t stream) {
   const int T = (int)a.T, chunk = (int)a.chunk;
   const int nchunks = (int)((a.T + a.chunk - 1) / a.chunk);
   const int nsplit = (int)nsplit_of(a.chunk);
+  const int slice = (int)slice_of(a.chunk);
   const int BH = (int)(a.B * a.H);
   float* part = (float*)a.ws;
   float* wprev = part + (size_t)BH * nchunks * nsplit * D * D;
   if (nchunks > 0) {
-    hipLaunchKernelGGL(lact_delta_kernel<D>, dim3(BH * nchunks * nsplit), dim3(256), 0, stream,
-                       (const bf16*)a.K, (const bf16*)a.V, a.eta, part, T, chunk, nchunks, nsplit);
+    hipLaunchKernelGGL(lact_delta_kernel<D>, dim3(BH * nchunks * nsplit), dim3(256), 0, stream, (const bf16*)a.K,
+                       (const bf16*)a.V, a.eta, part, T, chunk, nchunks, nsplit, slice);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(lact_scan_kernel<D>, dim3(BH), dim3(256), 0, stream, a.W0, part, wprev, a.W_out, nchunks,
-                     nsplit);
+  hipLaunchKernelGGL(lact_scan_kernel<D>, dim3(BH * D / 4), dim3(256), 0, stream, a.W0, part, wprev, a.W_out,
+                     nchunks, nsplit);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || nchunks == 0) return e;
-  const int tiles = (chunk + LC_READ_TILE - 1) / LC_READ_TILE;
-  hipLaunchKernelGGL(lact_read_kernel<D>, dim3(BH * nchunks * tiles), dim3(256), 0, stream, (const bf16*)a.Q, wprev,
-                     (bf16*)a.O, T, chunk, nchunks, tiles);
+  using Cfg = LactReadCfg<D>;
+  e = hipFuncSetAttribute((const void*)lact_read_kernel<D>, hipFuncAttributeMaxDynamicSharedMemorySize, Cfg::LDS);
+  if (e != hipSuccess) return e;
+  // about a quarter chunk (at least 256 tokens) per workgroup
+  int part_len = (chunk + 3) / 4;
+  part_len = part_len < 256 ? 256 : part_len;
+  part_len = (part_len + 63) / 64 * 64;
+  const int parts = (chunk + part_len - 1) / part_len;
+  hipLaunchKernelGGL(lact_read_kernel<D>, dim3(BH * nchunks * parts), dim3(256), Cfg::LDS, stream, (const bf16*)a.Q,
+                     wprev, (bf16*)a.O, T, chunk, nchunks, parts, part_len);
   return hipGetLastError();
 }
 
