@@ -56,6 +56,96 @@ __device__ __forceinline__ bf16x4 lds_read_tr16(const void* p) {
   return __builtin_bit_cast(bf16x4, v);
 }
 
+// 32-bit LDS address of a pointer into LDS (the low half of its generic address).
+__device__ __forceinline__ unsigned lds_addr(const void* p) { return (unsigned)(uintptr_t)p; }
+
+// Sixteen transposed reads issued from one inline-asm statement:
+// o[4*k + t] = transposed read at LDS byte address a_k + t*STRIDE.
+// When the compiler emits this instruction itself it first waits for every
+// outstanding global->LDS copy (it cannot tell that they do not overlap),
+// which empties a copy pipeline at each use.  Here the batch is issued and
+// waited for (lgkmcnt(0)) inside the same statement, so no output register
+// is visible to the compiler before its data has arrived.
+template <int STRIDE>
+__device__ __forceinline__ void lds_tr16_4x4(bf16x4 (&o)[16], unsigned a0, unsigned a1, unsigned a2, unsigned a3) {
+  static_assert(STRIDE >= 0 && 3 * STRIDE < 65536, "ds offset out of range");
+  uint2 r[16];
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %16\n\t"
+      "ds_read_b64_tr_b16 %1, %16 offset:%20\n\t"
+      "ds_read_b64_tr_b16 %2, %16 offset:%21\n\t"
+      "ds_read_b64_tr_b16 %3, %16 offset:%22\n\t"
+      "ds_read_b64_tr_b16 %4, %17\n\t"
+      "ds_read_b64_tr_b16 %5, %17 offset:%20\n\t"
+      "ds_read_b64_tr_b16 %6, %17 offset:%21\n\t"
+      "ds_read_b64_tr_b16 %7, %17 offset:%22\n\t"
+      "ds_read_b64_tr_b16 %8, %18\n\t"
+      "ds_read_b64_tr_b16 %9, %18 offset:%20\n\t"
+      "ds_read_b64_tr_b16 %10, %18 offset:%21\n\t"
+      "ds_read_b64_tr_b16 %11, %18 offset:%22\n\t"
+      "ds_read_b64_tr_b16 %12, %19\n\t"
+      "ds_read_b64_tr_b16 %13, %19 offset:%20\n\t"
+      "ds_read_b64_tr_b16 %14, %19 offset:%21\n\t"
+      "ds_read_b64_tr_b16 %15, %19 offset:%22\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7]),
+        "=&v"(r[8]), "=&v"(r[9]), "=&v"(r[10]), "=&v"(r[11]), "=&v"(r[12]), "=&v"(r[13]), "=&v"(r[14]),
+        "=&v"(r[15])
+      : "v"(a0), "v"(a1), "v"(a2), "v"(a3), "n"(STRIDE), "n"(2 * STRIDE), "n"(3 * STRIDE));
+#pragma unroll
+  for (int i = 0; i < 16; ++i) o[i] = __builtin_bit_cast(bf16x4, r[i]);
+}
+
+// Batches of transposed reads at arbitrary LDS byte addresses, issued and
+// waited for inside one asm statement each (same reason as above):
+// o[i] = transposed read at a[i], i < N.
+__device__ __forceinline__ void lds_tr16_x8(bf16x4* o, const unsigned* a) {
+  uint2 r0, r1, r2, r3, r4, r5, r6, r7;
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %8\n\tds_read_b64_tr_b16 %1, %9\n\t"
+      "ds_read_b64_tr_b16 %2, %10\n\tds_read_b64_tr_b16 %3, %11\n\t"
+      "ds_read_b64_tr_b16 %4, %12\n\tds_read_b64_tr_b16 %5, %13\n\t"
+      "ds_read_b64_tr_b16 %6, %14\n\tds_read_b64_tr_b16 %7, %15\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3), "=&v"(r4), "=&v"(r5), "=&v"(r6), "=&v"(r7)
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7]));
+  o[0] = __builtin_bit_cast(bf16x4, r0); o[1] = __builtin_bit_cast(bf16x4, r1);
+  o[2] = __builtin_bit_cast(bf16x4, r2); o[3] = __builtin_bit_cast(bf16x4, r3);
+  o[4] = __builtin_bit_cast(bf16x4, r4); o[5] = __builtin_bit_cast(bf16x4, r5);
+  o[6] = __builtin_bit_cast(bf16x4, r6); o[7] = __builtin_bit_cast(bf16x4, r7);
+}
+__device__ __forceinline__ void lds_tr16_x4(bf16x4* o, const unsigned* a) {
+  uint2 r0, r1, r2, r3;
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %4\n\tds_read_b64_tr_b16 %1, %5\n\t"
+      "ds_read_b64_tr_b16 %2, %6\n\tds_read_b64_tr_b16 %3, %7\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3)
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]));
+  o[0] = __builtin_bit_cast(bf16x4, r0); o[1] = __builtin_bit_cast(bf16x4, r1);
+  o[2] = __builtin_bit_cast(bf16x4, r2); o[3] = __builtin_bit_cast(bf16x4, r3);
+}
+__device__ __forceinline__ void lds_tr16_x2(bf16x4* o, const unsigned* a) {
+  uint2 r0, r1;
+  asm volatile("ds_read_b64_tr_b16 %0, %2\n\tds_read_b64_tr_b16 %1, %3\n\ts_waitcnt lgkmcnt(0)"
+               : "=&v"(r0), "=&v"(r1)
+               : "v"(a[0]), "v"(a[1]));
+  o[0] = __builtin_bit_cast(bf16x4, r0); o[1] = __builtin_bit_cast(bf16x4, r1);
+}
+template <int N>
+__device__ __forceinline__ void lds_tr16_batch(bf16x4* o, const unsigned* a) {
+  static_assert(N % 2 == 0, "even batch sizes only");
+  if constexpr (N >= 8) {
+    lds_tr16_x8(o, a);
+    lds_tr16_batch<N - 8>(o + 8, a + 8);
+  } else if constexpr (N >= 4) {
+    lds_tr16_x4(o, a);
+    lds_tr16_batch<N - 4>(o + 4, a + 4);
+  } else if constexpr (N == 2) {
+    lds_tr16_x2(o, a);
+  }
+}
+
 __device__ __forceinline__ bf16x8 join(const bf16x4& lo, const bf16x4& hi) {
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }

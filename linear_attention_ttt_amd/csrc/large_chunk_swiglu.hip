@@ -38,21 +38,29 @@ constexpr int SW_DH = 256;
 constexpr int SW_NS = 16;                 // hidden units per recurrence workgroup
 constexpr int SW_NSL = SW_DH / SW_NS;     // workgroups per head
 constexpr int SW_SB = 64;                 // tokens per LDS sub-block
-constexpr int SW_ROW = SW_D * 2 + 32;     // padded bf16 row of K / V in LDS
-constexpr int SW_TT = 128;                // tokens per read workgroup
+constexpr int SW_TT = 256;                // tokens per read workgroup (8 waves x 32)
 constexpr int SW_US = 32;                 // hidden units per read slice
 constexpr int SW_SPIN_LIMIT = 1 << 24;
 constexpr size_t SW_STATE = (size_t)6 * SW_D * SW_DH;  // bf16 elements per stored state
 
+constexpr int SW_RING = 4;                // K/V/eta sub-blocks resident in the recurrence ring
+constexpr int SW_KROW = SW_D * 2;         // unpadded bf16 row of K / V in LDS (swizzled pieces)
+
 struct RecurLds {
-  unsigned char k[2][SW_SB * SW_ROW];
-  unsigned char v[2][SW_SB * SW_ROW];
-  float eta[2][SW_SB];
+  unsigned char kv[SW_RING][2][SW_SB * SW_KROW];  // K, V sub-blocks
+  float eta[SW_RING][SW_SB];
+  unsigned char dx[3][4][64 * 8];                  // da, db, eh operand tiles of each wave's 16 tokens
   float w1[SW_D * SW_NS];   // [d][u]
   float w3[SW_D * SW_NS];   // [d][u]
   float w2[SW_NS * SW_D];   // [u][d]
-  float red[4][SW_D * SW_NS];
 };
+static_assert(sizeof(RecurLds) <= 160 * 1024, "recurrence LDS exceeds 160 KB");
+
+// Position of the 16-byte piece of a 256-byte K/V row in LDS: the piece
+// index is XORed with a 1-bit rotation of (row & 15).  Rows 0..15 then land
+// on distinct pieces for the row-wise operand reads, and the transposed
+// 8-byte reads of 4 rows x 2 pieces by each half-wave hit distinct banks.
+__device__ __forceinline__ int sw_swz(int row) { return ((row & 7) << 1) | ((row >> 3) & 1); }
 
 __device__ __forceinline__ void split_store8(bf16* hi, bf16* lo, const float* f) {
   bf16x8 h, l;
@@ -131,43 +139,65 @@ __global__ __launch_bounds__(256, 1) void swiglu_recur_kernel(
   };
   if (nchunks > 0) store_state(0);
 
-  // ---- token sub-blocks, prefetched one ahead through registers ----
+  // ---- token sub-blocks through a ring of SW_RING LDS stages ----
+  // Stage loads go straight from global memory to LDS; each wave loads its
+  // own 16 tokens of K, V and eta (9 loads per stage), so the per-wave
+  // vector-memory count tells when a stage has landed.
   const int nsb = (chunk + SW_SB - 1) / SW_SB;
   const int last_len = T - (nchunks - 1) * chunk;
   const int total = nchunks > 0 ? (nchunks - 1) * nsb + (last_len + SW_SB - 1) / SW_SB : 0;
-  uint4 kr[4], vr[4];
-  float er = 0.f;
-  auto load_regs = [&](int gsb) {
+  // Each slice walks a chunk's sub-blocks from its own starting point, so the
+  // head's workgroups request different sub-blocks at any moment (repeats
+  // are served by L2).  The chunk's gradient sums do not depend on the order.
+  auto sub_of = [&](int gsb) {
     const int c = gsb / nsb, i = gsb % nsb;
-    const int t0 = c * chunk + i * SW_SB;
-    const int tend = min(c * chunk + chunk, T);
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int p = k * 256 + tid;
-      const int row = p >> 4, col = (p & 15) * 8;
-      const int tc = min(t0 + row, tend - 1);
-      kr[k] = *(const uint4*)(Kh + (size_t)tc * D + col);
-      vr[k] = *(const uint4*)(Vh + (size_t)tc * D + col);
-    }
-    if (tid < SW_SB) er = (t0 + tid < tend) ? Eh[min(t0 + tid, tend - 1)] : 0.f;
+    const int n = min(nsb, (min(c * chunk + chunk, T) - c * chunk + SW_SB - 1) / SW_SB);
+    return (i + 2 * sl) % n;
   };
-  auto store_regs = [&](int buf) {
+  unsigned dma_off[4];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int p = k * 256 + tid;
-      const int row = p >> 4, col = (p & 15) * 8;
-      *(uint4*)(S.k[buf] + row * SW_ROW + col * 2) = kr[k];
-      *(uint4*)(S.v[buf] + row * SW_ROW + col * 2) = vr[k];
-    }
-    if (tid < SW_SB) S.eta[buf][tid] = er;
+  for (int j = 0; j < 4; ++j) {
+    const int row = 16 * w + 4 * j + (l >> 4);
+    dma_off[j] = (unsigned)(row * SW_KROW + (((l & 15) ^ sw_swz(row)) << 4));
+  }
+  auto issue_stage = [&](int gsb) {
+    const int c = gsb / nsb;
+    const int t0 = c * chunk + sub_of(gsb) * SW_SB;
+    const int n = min(c * chunk + chunk, T) - t0;   // valid tokens; rows beyond read as 0
+    const int slot = gsb % SW_RING;
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kh + (size_t)t0 * D, (long long)n * SW_KROW);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vh + (size_t)t0 * D, (long long)n * SW_KROW);
+    const __amdgpu_buffer_rsrc_t re = make_rsrc(Eh + t0, (long long)n * 4);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) buf2lds16(rk, dma_off[j], S.kv[slot][0] + (16 * w + 4 * j) * SW_KROW);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) buf2lds16(rv, dma_off[j], S.kv[slot][1] + (16 * w + 4 * j) * SW_KROW);
+    if (l < 16) buf2lds4(re, (unsigned)((16 * w + l) * 4), &S.eta[slot][16 * w]);
   };
+  // per-lane LDS offsets: forward operand reads (row 16w+li, piece 4ks+g) and
+  // transposed reads (rows 4g..4g+3 of a 16-token block, d-tile 2w+j)
+  unsigned fwd_off[4], tr_off[2];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) fwd_off[ks] = (unsigned)((16 * w + li) * SW_KROW + (((4 * ks + g) ^ sw_swz(li)) << 4));
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int row = 4 * g + (li >> 2), m = 2 * w + j;
+    tr_off[j] = (unsigned)(row * SW_KROW + (((2 * m + ((li >> 1) & 1)) ^ sw_swz(row)) << 4) + (li & 1) * 8);
+  }
 
   bf16x8 w1op[4], w3op[4], w2op[4];
-  floatx4 dW1[8], dW3[8], dW2[8];
-  if (total > 0) load_regs(0);
+  floatx4 dW1[2], dW3[2], dW2[2];   // this wave's d-tiles 2w, 2w+1
+#pragma unroll
+  for (int k = 0; k < SW_RING - 1; ++k)
+    if (k < total) issue_stage(k);
 
   for (int gsb = 0; gsb < total; ++gsb) {
     const int c = gsb / nsb, i = gsb % nsb;
+    // stage gsb has landed once at most the loads of the later issued stages are outstanding
+    if (gsb + 2 < total) wait_vm_barrier<18>();
+    else if (gsb + 1 < total) wait_vm_barrier<9>();
+    else wait_vm_barrier<0>();
+    if (gsb + SW_RING - 1 < total) issue_stage(gsb + SW_RING - 1);   // into the slot read last iteration
     if (i == 0) {
       // operands of this chunk's weights (B operands: col = unit li, k = 8 consecutive d)
 #pragma unroll
@@ -180,27 +210,23 @@ __global__ __launch_bounds__(256, 1) void swiglu_recur_kernel(
           w2op[ks][j] = (bf16)S.w2[li * D + d];
         }
 #pragma unroll
-      for (int m = 0; m < 8; ++m) dW1[m] = dW3[m] = dW2[m] = floatx4{0.f, 0.f, 0.f, 0.f};
+      for (int m = 0; m < 2; ++m) dW1[m] = dW3[m] = dW2[m] = floatx4{0.f, 0.f, 0.f, 0.f};
     }
-    const int buf = gsb & 1;
-    store_regs(buf);
-    __syncthreads();
-    if (gsb + 1 < total) load_regs(gsb + 1);
+    const int slot = gsb % SW_RING;
+    const unsigned char* kb = S.kv[slot][0];
+    const unsigned char* vb = S.kv[slot][1];
 
-    // ---- forward of the 16 tokens of this wave, and the chunk gradient ----
-    const unsigned char* kb = S.k[buf];
-    const unsigned char* vb = S.v[buf];
+    // ---- forward of this wave's 16 tokens: A = K W1, B = K W3, Dh = V W2^T ----
     floatx4 A = {0.f, 0.f, 0.f, 0.f}, Bv = A, Dh = A;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      const int off = (16 * w + li) * SW_ROW + (32 * ks + 8 * g) * 2;
-      const bf16x8 kop = *(const bf16x8*)(kb + off);
-      const bf16x8 vop = *(const bf16x8*)(vb + off);
+      const bf16x8 kop = *(const bf16x8*)(kb + fwd_off[ks]);
+      const bf16x8 vop = *(const bf16x8*)(vb + fwd_off[ks]);
       A = mfma16(kop, w1op[ks], A);
       Bv = mfma16(kop, w3op[ks], Bv);
       Dh = mfma16(vop, w2op[ks], Dh);
     }
-    const floatx4 e4 = *(const floatx4*)(&S.eta[buf][16 * w + 4 * g]);
+    const floatx4 e4 = *(const floatx4*)(&S.eta[slot][16 * w + 4 * g]);
     bf16x4 daop, dbop, ehop;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -212,52 +238,46 @@ __global__ __launch_bounds__(256, 1) void swiglu_recur_kernel(
       dbop[r] = (bf16)(dh * sa);
       ehop[r] = (bf16)(e4[r] * sa * b);
     }
-    const int trow = (16 * w + 4 * g + (li >> 2)) * SW_ROW;
+    // lane (g, li) holds rows 4g..4g+3 (tokens) of unit li: exactly the
+    // operand layout of the k = token products below, for every wave
+    *(bf16x4*)(S.dx[0][w] + l * 8) = daop;
+    *(bf16x4*)(S.dx[1][w] + l * 8) = dbop;
+    *(bf16x4*)(S.dx[2][w] + l * 8) = ehop;
+    barrier();
+
+    // ---- gradient rows of this wave over all 64 tokens ----
+    // dW1[d][u] += K^T da, dW3[d][u] += K^T db, dW2[u][d] += eh^T V
+    // transposed K, V blocks: tr[4*k + tb], k = (K, j0), (K, j1), (V, j0), (V, j1)
+    bf16x4 tr[16];
+    lds_tr16_4x4<16 * SW_KROW>(tr, lds_addr(kb) + tr_off[0], lds_addr(kb) + tr_off[1], lds_addr(vb) + tr_off[0],
+                               lds_addr(vb) + tr_off[1]);
 #pragma unroll
-    for (int m = 0; m < 8; ++m) {
-      const bf16x4 kt = lds_read_tr16(kb + trow + (16 * m + 4 * (li & 3)) * 2);
-      dW1[m] = mfma16k16(kt, daop, dW1[m]);
-      dW3[m] = mfma16k16(kt, dbop, dW3[m]);
-      const bf16x4 vt = lds_read_tr16(vb + trow + (16 * m + 4 * (li & 3)) * 2);
-      dW2[m] = mfma16k16(ehop, vt, dW2[m]);
+    for (int tb = 0; tb < 4; ++tb) {
+      const bf16x4 da = *(const bf16x4*)(S.dx[0][tb] + l * 8);
+      const bf16x4 db = *(const bf16x4*)(S.dx[1][tb] + l * 8);
+      const bf16x4 eh = *(const bf16x4*)(S.dx[2][tb] + l * 8);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        dW1[j] = mfma16k16(tr[4 * j + tb], da, dW1[j]);
+        dW3[j] = mfma16k16(tr[4 * j + tb], db, dW3[j]);
+        dW2[j] = mfma16k16(eh, tr[8 + 4 * j + tb], dW2[j]);
+      }
     }
 
     const bool chunk_end = (i == nsb - 1) || (gsb == total - 1);
     if (!chunk_end) continue;
 
-    // ---- end of chunk: sum the waves' partial gradients and update ----
+    // ---- end of chunk: each wave adds its own rows, then normalise ----
     // dW1 lane layout: [d = 16m + 4g + r][u = li]; dW2: [u = 4g + r][d = 16m + li]
 #pragma unroll
-    for (int m = 0; m < 8; ++m)
+    for (int j = 0; j < 2; ++j) {
+      const int m = 2 * w + j;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) S.red[w][(16 * m + 4 * g + r) * NS + li] = dW1[m][r];
-    __syncthreads();
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int idx = tid * 8 + e;
-      S.w1[idx] += S.red[0][idx] + S.red[1][idx] + S.red[2][idx] + S.red[3][idx];
-    }
-    __syncthreads();
-#pragma unroll
-    for (int m = 0; m < 8; ++m)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) S.red[w][(16 * m + 4 * g + r) * NS + li] = dW3[m][r];
-    __syncthreads();
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int idx = tid * 8 + e;
-      S.w3[idx] += S.red[0][idx] + S.red[1][idx] + S.red[2][idx] + S.red[3][idx];
-    }
-    __syncthreads();
-#pragma unroll
-    for (int m = 0; m < 8; ++m)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) S.red[w][(4 * g + r) * D + 16 * m + li] = dW2[m][r];
-    __syncthreads();
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int idx = tid * 8 + e;
-      S.w2[idx] += S.red[0][idx] + S.red[1][idx] + S.red[2][idx] + S.red[3][idx];
+      for (int r = 0; r < 4; ++r) {
+        S.w1[(16 * m + 4 * g + r) * NS + li] += dW1[j][r];
+        S.w3[(16 * m + 4 * g + r) * NS + li] += dW3[j][r];
+        S.w2[(4 * g + r) * D + 16 * m + li] += dW2[j][r];
+      }
     }
     __syncthreads();
     // W1, W3: unit columns over d, local (waves 0 and 1)
@@ -334,7 +354,7 @@ struct ReadLds {
 constexpr int RW13_ROW = SW_D * 2 + 16;
 constexpr int RW2_ROW = SW_US * 2 + 8;
 
-__global__ __launch_bounds__(256, 1) void swiglu_read_kernel(const bf16* __restrict__ Q,
+__global__ __launch_bounds__(512, 1) void swiglu_read_kernel(const bf16* __restrict__ Q,
                                                              const bf16* __restrict__ states, bf16* __restrict__ O,
                                                              int T, int chunk, int nchunks, int tiles) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
@@ -346,7 +366,7 @@ __global__ __launch_bounds__(256, 1) void swiglu_read_kernel(const bf16* __restr
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g = l >> 4, li = l & 15;
   const int cend = min((c + 1) * chunk, T);
   const int t0 = c * chunk + tile * SW_TT;
-  if (t0 >= cend) return;
+  if (t0 >= cend) return;   // uniform over the workgroup, before any barrier
   const bf16* st = states + ((size_t)bh * nchunks + c) * SW_STATE;
   const size_t P = (size_t)D * DH;
 
@@ -360,37 +380,37 @@ __global__ __launch_bounds__(256, 1) void swiglu_read_kernel(const bf16* __restr
     for (int ks = 0; ks < 4; ++ks) qop[tt][ks] = *(const bf16x8*)(Qh + (size_t)t * D + 32 * ks + 8 * g);
   }
 
-  // weight slice staging: 12 x 16 bytes per thread
-  uint4 wr[12];
+  // weight slice staging: 6 x 16 bytes per thread (512 threads)
+  uint4 wr0, wr1, wr2, wr3, wr4, wr5;
+  auto wsrc13 = [&](int k, int s) {        // W1T/W3T hi/lo planes: 4 x 32 rows x 16 pieces
+    const int p = k * 512 + tid;
+    const int plane = p >> 9, row = (p >> 4) & 31, pc = p & 15;
+    return (const uint4*)(st + (size_t)plane * P + (size_t)(SW_US * s + row) * D + pc * 8);
+  };
+  auto wsrc2 = [&](int k, int s) {         // W2T hi/lo: 2 x 128 rows x 4 pieces
+    const int p = k * 512 + tid;
+    const int plane = p >> 9, n = (p >> 2) & 127, pc = p & 3;
+    return (const uint4*)(st + (size_t)(4 + plane) * P + (size_t)n * DH + SW_US * s + pc * 8);
+  };
   auto load_slice = [&](int s) {
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {          // W1T/W3T hi/lo planes: 4 x 32 rows x 16 pieces
-      const int p = k * 256 + tid;
-      const int plane = p >> 9, row = (p >> 4) & 31, pc = p & 15;
-      wr[k] = *(const uint4*)(st + (size_t)plane * P + (size_t)(SW_US * s + row) * D + pc * 8);
-    }
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {          // W2T hi/lo: 2 x 128 rows x 4 pieces
-      const int p = k * 256 + tid;
-      const int plane = p >> 9, n = (p >> 2) & 127, pc = p & 3;
-      wr[8 + k] = *(const uint4*)(st + (size_t)(4 + plane) * P + (size_t)n * DH + SW_US * s + pc * 8);
-    }
+    wr0 = *wsrc13(0, s); wr1 = *wsrc13(1, s); wr2 = *wsrc13(2, s); wr3 = *wsrc13(3, s);
+    wr4 = *wsrc2(0, s); wr5 = *wsrc2(1, s);
+  };
+  auto put13 = [&](int k, int buf, uint4 v) {
+    const int p = k * 512 + tid;
+    const int plane = p >> 9, row = (p >> 4) & 31, pc = p & 15;
+    *(uint4*)(L.w13[buf][plane] + row * RW13_ROW + pc * 16) = v;
+  };
+  auto put2 = [&](int k, int buf, uint4 v) {
+    const int p = k * 512 + tid;
+    const int plane = p >> 9, n = (p >> 2) & 127, pc = p & 3;
+    unsigned char* dst = L.w2[buf][plane] + n * RW2_ROW + pc * 16;
+    *(uint2*)dst = uint2{v.x, v.y};
+    *(uint2*)(dst + 8) = uint2{v.z, v.w};
   };
   auto store_slice = [&](int buf) {
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const int p = k * 256 + tid;
-      const int plane = p >> 9, row = (p >> 4) & 31, pc = p & 15;
-      *(uint4*)(L.w13[buf][plane] + row * RW13_ROW + pc * 16) = wr[k];
-    }
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int p = k * 256 + tid;
-      const int plane = p >> 9, n = (p >> 2) & 127, pc = p & 3;
-      unsigned char* dst = L.w2[buf][plane] + n * RW2_ROW + pc * 16;
-      *(uint2*)dst = uint2{wr[8 + k].x, wr[8 + k].y};
-      *(uint2*)(dst + 8) = uint2{wr[8 + k].z, wr[8 + k].w};
-    }
+    put13(0, buf, wr0); put13(1, buf, wr1); put13(2, buf, wr2); put13(3, buf, wr3);
+    put2(0, buf, wr4); put2(1, buf, wr5);
   };
 
   floatx4 oacc[8][2];
@@ -459,16 +479,15 @@ __global__ __launch_bounds__(256, 1) void swiglu_read_kernel(const bf16* __restr
     __syncthreads();
   }
   bf16* Oh = O + (size_t)bh * T * D;
+  const __amdgpu_buffer_rsrc_t ro = make_rsrc(Oh + (size_t)t0 * D, ((long long)cend - t0) * D * 2);
 #pragma unroll
-  for (int tt = 0; tt < 2; ++tt) {
-    const int t = t0 + 32 * w + 16 * tt + li;
-    if (t < cend) {
+  for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-      for (int nt = 0; nt < 8; ++nt)
-        *(bf16x4*)(Oh + (size_t)t * D + 16 * nt + 4 * g) =
-            to_bf16x4(oacc[nt][tt][0], oacc[nt][tt][1], oacc[nt][tt][2], oacc[nt][tt][3]);
+    for (int nt = 0; nt < 8; ++nt) {
+      const bf16x4 o = to_bf16x4(oacc[nt][tt][0], oacc[nt][tt][1], oacc[nt][tt][2], oacc[nt][tt][3]);
+      __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(uint2v, o), ro,
+                                            (unsigned)((32 * w + 16 * tt + li) * D * 2 + (16 * nt + 4 * g) * 2), 0, 0);
     }
-  }
 }
 
 struct SwLayout {
@@ -551,7 +570,7 @@ hipError_t launch_large_chunk_swiglu(const LargeChunkArgs& a, hipStream_t stream
   e = hipFuncSetAttribute((const void*)swiglu_read_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_o);
   if (e != hipSuccess) return e;
   const int tiles = (chunk + SW_TT - 1) / SW_TT;
-  hipLaunchKernelGGL(swiglu_read_kernel, dim3(BH * nchunks * tiles), dim3(256), lds_o, stream, (const bf16*)a.Q,
+  hipLaunchKernelGGL(swiglu_read_kernel, dim3(BH * nchunks * tiles), dim3(512), lds_o, stream, (const bf16*)a.Q,
                      (const bf16*)states, (bf16*)a.O, T, chunk, nchunks, tiles);
   return hipGetLastError();
 }

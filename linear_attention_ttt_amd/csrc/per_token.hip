@@ -304,8 +304,23 @@ __device__ __forceinline__ void per_token_wave(const PerTokenPtrs& P, unsigned c
     barrier();
 
     // ---- phase 2a: O_w^T += V^T A_w^T over key blocks 0..IB ----
+    constexpr int NKC = IB / 2 + 1;
+    bf16x4 vtr_[NKC * Cfg::NTW * 2];
+    {
+      unsigned ad[NKC * Cfg::NTW * 2];
+      const unsigned vb0 = lds_addr(vs) + vtr;
 #pragma unroll
-    for (int kc = 0; 2 * kc <= IB; ++kc) {
+      for (int kc = 0; kc < NKC; ++kc)
+#pragma unroll
+        for (int n = 0; n < Cfg::NTW; ++n) {
+          const unsigned o0 = vb0 + 32 * kc * TV * 2 + 32 * (NT0 + n);
+          ad[(kc * Cfg::NTW + n) * 2] = o0;
+          ad[(kc * Cfg::NTW + n) * 2 + 1] = o0 + 16 * TV * 2;
+        }
+      lds_tr16_batch<NKC * Cfg::NTW * 2>(vtr_, ad);
+    }
+#pragma unroll
+    for (int kc = 0; kc < NKC; ++kc) {
       const int t0i = ptile_index(2 * kc, IB);
       const bf16x4 h0 = *(const bf16x4*)(pb + t0i * 512 + l * 8);
       const bf16x4 l0 = *(const bf16x4*)(pb + Cfg::P_BYTES + t0i * 512 + l * 8);
@@ -318,8 +333,7 @@ __device__ __forceinline__ void per_token_wave(const PerTokenPtrs& P, unsigned c
       const bf16x8 bh_ = join(h0, h1), bl_ = join(l0, l1);
 #pragma unroll
       for (int n = 0; n < Cfg::NTW; ++n) {
-        const int o0 = vtr + 32 * kc * TV * 2 + 32 * (NT0 + n), o1 = o0 + 16 * TV * 2;
-        const bf16x8 vt = join(lds_read_tr16(vs + o0), lds_read_tr16(vs + o1));
+        const bf16x8 vt = join(vtr_[(kc * Cfg::NTW + n) * 2], vtr_[(kc * Cfg::NTW + n) * 2 + 1]);
         acc[n] = mfma16(vt, bh_, acc[n]);
         acc[n] = mfma16(vt, bl_, acc[n]);
       }
@@ -334,23 +348,43 @@ __device__ __forceinline__ void per_token_wave(const PerTokenPtrs& P, unsigned c
       }
     }
     // ---- phase 2b: S += K^T (diag(eta) V)_hi + K^T (diag(eta) V)_lo on this wave's slab ----
+    // operands of both 32-token halves: per half, diag(eta)V hi/lo (2 reads
+    // each per column tile) then K^T (2 reads per m-tile)
+    constexpr int NE = 4 * Cfg::NTW, NKR = 2 * Cfg::MTW, NH = NE + NKR;
+    bf16x4 opb[2 * NH];
+    {
+      unsigned ad[2 * NH];
+      const unsigned eb0 = lds_addr(evb) + vtr, kb0 = lds_addr(kst);
 #pragma unroll
-    for (int kc = 0; kc < 2; ++kc) {
-      bf16x8 evh[Cfg::NTW], evl[Cfg::NTW];
-#pragma unroll
-      for (int n = 0; n < Cfg::NTW; ++n) {
-        const int o0 = vtr + 32 * kc * TV * 2 + 32 * (NT0 + n), o1 = o0 + 16 * TV * 2;
-        evh[n] = join(lds_read_tr16(evb + o0), lds_read_tr16(evb + o1));
-        evl[n] = join(lds_read_tr16(evb + Cfg::V_BYTES + o0), lds_read_tr16(evb + Cfg::V_BYTES + o1));
-      }
-#pragma unroll
-      for (int j = 0; j < Cfg::MTW; ++j) {
-        const int o0 = ktr[j] + 32 * kc * ROWB, o1 = o0 + 16 * ROWB;
-        const bf16x8 a = join(lds_read_tr16(kst + o0), lds_read_tr16(kst + o1));
+      for (int kc = 0; kc < 2; ++kc) {
 #pragma unroll
         for (int n = 0; n < Cfg::NTW; ++n) {
-          S[j][n] = mfma16(a, evh[n], S[j][n]);
-          S[j][n] = mfma16(a, evl[n], S[j][n]);
+          const unsigned o0 = eb0 + 32 * kc * TV * 2 + 32 * (NT0 + n), o1 = o0 + 16 * TV * 2;
+          ad[kc * NH + 4 * n + 0] = o0;
+          ad[kc * NH + 4 * n + 1] = o1;
+          ad[kc * NH + 4 * n + 2] = o0 + Cfg::V_BYTES;
+          ad[kc * NH + 4 * n + 3] = o1 + Cfg::V_BYTES;
+        }
+#pragma unroll
+        for (int j = 0; j < Cfg::MTW; ++j) {
+          const unsigned o0 = kb0 + ktr[j] + 32 * kc * ROWB;
+          ad[kc * NH + NE + 2 * j] = o0;
+          ad[kc * NH + NE + 2 * j + 1] = o0 + 16 * ROWB;
+        }
+      }
+      lds_tr16_batch<2 * NH>(opb, ad);
+    }
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc) {
+#pragma unroll
+      for (int j = 0; j < Cfg::MTW; ++j) {
+        const bf16x8 a = join(opb[kc * NH + NE + 2 * j], opb[kc * NH + NE + 2 * j + 1]);
+#pragma unroll
+        for (int n = 0; n < Cfg::NTW; ++n) {
+          const bf16x8 evh = join(opb[kc * NH + 4 * n], opb[kc * NH + 4 * n + 1]);
+          const bf16x8 evl = join(opb[kc * NH + 4 * n + 2], opb[kc * NH + 4 * n + 3]);
+          S[j][n] = mfma16(a, evh, S[j][n]);
+          S[j][n] = mfma16(a, evl, S[j][n]);
         }
       }
     }
