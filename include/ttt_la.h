@@ -110,9 +110,12 @@ typedef struct ttt_la_desc {
  *
  * Supported set (ERR_UNSUPPORTED otherwise):
  *   per-token:    d_k = d_v in {64, 128}; bf16 or fp32; chunk in
- *                 {16, 32, 64, 128} (the bf16 kernel always works in
+ *                 {16, 32, 64, 128} (the bf16 kernels always work in
  *                 64-token tiles, the fp32 kernel in tiles of `chunk`
- *                 tokens and needs chunk <= 64);
+ *                 tokens and needs chunk <= 64).  bf16 cuts each head's
+ *                 sequence into segments of whole tiles and keeps one fp32
+ *                 d_k x d_v state per segment in the workspace (none when
+ *                 each head is one segment);
  *   large-chunk linear: d_k = d_v in {64, 128}; bf16; any chunk;
  *   large-chunk SwiGLU: d = 128, d_h = 256; bf16; any chunk.
  *   T = 0 is accepted: O is empty and W_out = W0.

@@ -96,6 +96,21 @@ __device__ __forceinline__ void lds_tr16_4x4(bf16x4 (&o)[16], unsigned a0, unsig
   for (int i = 0; i < 16; ++i) o[i] = __builtin_bit_cast(bf16x4, r[i]);
 }
 
+// Four transposed reads from one base: o[t] = read at a + t*STRIDE.
+template <int STRIDE>
+__device__ __forceinline__ void lds_tr16_1x4(bf16x4 (&o)[4], unsigned a) {
+  static_assert(STRIDE >= 0 && 3 * STRIDE < 65536, "ds offset out of range");
+  uint2 r0, r1, r2, r3;
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %4\n\tds_read_b64_tr_b16 %1, %4 offset:%5\n\t"
+      "ds_read_b64_tr_b16 %2, %4 offset:%6\n\tds_read_b64_tr_b16 %3, %4 offset:%7\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3)
+      : "v"(a), "n"(STRIDE), "n"(2 * STRIDE), "n"(3 * STRIDE));
+  o[0] = __builtin_bit_cast(bf16x4, r0); o[1] = __builtin_bit_cast(bf16x4, r1);
+  o[2] = __builtin_bit_cast(bf16x4, r2); o[3] = __builtin_bit_cast(bf16x4, r3);
+}
+
 // Batches of transposed reads at arbitrary LDS byte addresses, issued and
 // waited for inside one asm statement each (same reason as above):
 // o[i] = transposed read at a[i], i < N.
@@ -176,6 +191,27 @@ __device__ __forceinline__ void buf2lds16(__amdgpu_buffer_rsrc_t r, unsigned vof
 __device__ __forceinline__ void buf2lds4(__amdgpu_buffer_rsrc_t r, unsigned voff, void* lds_wave_base) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(uintptr_t)lds_wave_base, 4, voff, 0, 0, 0);
 }
+// The same direct-to-LDS loads issued from inline asm.  The compiler then
+// does not see that LDS is written asynchronously and adds no waits of its
+// own before LDS reads (its rule for compiler-issued copies is to wait for
+// all of them before any LDS read it cannot prove disjoint, transposed reads
+// included).  Every read of the destination must therefore be ordered by an
+// explicit wait_vm_barrier / wait_vm.  M0 holds the wave's LDS destination;
+// it is saved and restored around the load (the compiler treats M0 as
+// reserved), and one wait state separates its write from the load.
+#define TTT_DMA_ASM(op)                                                                                      \
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\t" op " %1, %2, 0 offen lds\n\ts_mov_b32 m0, %0" \
+               : "=&s"(saved)                                                                               \
+               : "v"(voff), "s"(r), "s"(__builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)lds_wave_base)))
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, unsigned voff, const void* lds_wave_base) {
+  unsigned saved;
+  TTT_DMA_ASM("buffer_load_dwordx4");
+}
+__device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, unsigned voff, const void* lds_wave_base) {
+  unsigned saved;
+  TTT_DMA_ASM("buffer_load_dword");
+}
+#undef TTT_DMA_ASM
 __device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, unsigned voff) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0);
 }
@@ -183,13 +219,14 @@ __device__ __forceinline__ void buf_store16(__amdgpu_buffer_rsrc_t r, unsigned v
   __builtin_amdgcn_raw_buffer_store_b128(v, r, voff, 0, 0);
 }
 
-// s_waitcnt vmcnt(N) (other counters untouched) followed by a workgroup
-// barrier.  The "memory" clobber keeps the compiler from moving LDS or
-// global accesses across it.
+// s_waitcnt vmcnt(N) lgkmcnt(0) followed by a workgroup barrier: this
+// wave's LDS accesses are complete and at most N of its vector-memory
+// operations are outstanding when it arrives.  The "memory" clobber keeps
+// the compiler from moving LDS or global accesses across it.
 template <int N>
 __device__ __forceinline__ void wait_vm_barrier() {
   static_assert(N >= 0 && N < 64, "vmcnt out of range");
-  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 template <int N>
 __device__ __forceinline__ void wait_vm() {
@@ -197,6 +234,26 @@ __device__ __forceinline__ void wait_vm() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 __device__ __forceinline__ void barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// bf16 hi + lo split of two floats at once: hi = bf16(f) (round to nearest
+// even), lo = bf16(f - hi); f = hi + lo to about 16 significant bits.
+typedef float floatx2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+// Returns {hi, lo}, each a packed bf16 pair (a in the low half).
+__device__ __forceinline__ uint2 split2(float a, float b) {
+  const unsigned h = __builtin_bit_cast(unsigned, __builtin_convertvector(floatx2{a, b}, bf16x2));
+  const float ah = __builtin_bit_cast(float, h << 16), bh = __builtin_bit_cast(float, h & 0xffff0000u);
+  return uint2{h, __builtin_bit_cast(unsigned, __builtin_convertvector(floatx2{a - ah, b - bh}, bf16x2))};
+}
+// Four splits into bf16x8 hi and lo operands (element order a0..a7).
+__device__ __forceinline__ void split8(const floatx4& a, const floatx4& b, bf16x8& hi, bf16x8& lo) {
+  const uint2 s0 = split2(a[0], a[1]), s1 = split2(a[2], a[3]), s2 = split2(b[0], b[1]), s3 = split2(b[2], b[3]);
+  hi = __builtin_bit_cast(bf16x8, u32x4{s0.x, s1.x, s2.x, s3.x});
+  lo = __builtin_bit_cast(bf16x8, u32x4{s0.y, s1.y, s2.y, s3.y});
+}
+// bf16 -> float of the two halves of a packed pair
+__device__ __forceinline__ float bf16lo_f(unsigned x) { return __builtin_bit_cast(float, x << 16); }
+__device__ __forceinline__ float bf16hi_f(unsigned x) { return __builtin_bit_cast(float, x & 0xffff0000u); }
 
 __device__ __forceinline__ bf16x4 to_bf16x4(float a, float b, float c, float d) {
   bf16x4 r;

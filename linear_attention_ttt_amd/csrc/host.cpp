@@ -70,6 +70,8 @@ bool supported(const ttt_la_desc& d, int64_t chunk, int32_t mode) {
 
 size_t workspace_for(const ttt_la_desc& d, int64_t chunk, int32_t mode) {
   switch (mode) {
+    case TTT_LA_PER_TOKEN_LINEAR:
+      return ttt::per_token_workspace(d.B, d.H, d.T, d.d_k, d.d_v, d.io_dtype);
     case TTT_LA_LARGE_CHUNK_LINEAR:
       return ttt::large_chunk_linear_workspace(d.B, d.H, d.T, d.d_k, d.d_v, chunk);
     case TTT_LA_LARGE_CHUNK_SWIGLU:
@@ -139,7 +141,7 @@ int ttt_la_forward(const void* Q, const void* K, const void* V, const float* eta
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = hipSuccess;
   if (mode == TTT_LA_PER_TOKEN_LINEAR) {
-    ttt::PerTokenArgs a{Q, K, V, eta, W0, O, W_out, d.B, d.H, d.T, d.d_k, d.d_v, chunk, d.io_dtype};
+    ttt::PerTokenArgs a{Q, K, V, eta, W0, O, W_out, workspace, d.B, d.H, d.T, d.d_k, d.d_v, chunk, d.io_dtype};
     e = ttt::launch_per_token(a, s);
   } else {
     ttt::LargeChunkArgs a{Q, K, V, eta, W0, O, W_out, workspace, d.B, d.H, d.T, d.d_k, d.d_v, d.d_h, chunk, d.io_dtype};

@@ -15,11 +15,18 @@ struct PerTokenArgs {
   const float* W0;
   void* O;
   float* W_out;
+  void* ws;
   int64_t B, H, T, DK, DV, chunk;
   int dtype;  // 0 = fp32, 1 = bf16
 };
 
+// Sequence segments of the bf16 per-token path (segments per head, 64-token tiles per segment).
+struct SegPlan {
+  int nseg, tiles;
+};
+SegPlan per_token_seg_plan(int64_t BH, int64_t T);
 bool per_token_supported(int64_t dk, int64_t dv, int64_t chunk, int dtype);
+size_t per_token_workspace(int64_t B, int64_t H, int64_t T, int64_t dk, int64_t dv, int dtype);
 hipError_t launch_per_token(const PerTokenArgs& a, hipStream_t stream);
 
 struct LargeChunkArgs {

@@ -10,81 +10,35 @@
 //     O_c = tril(Q_c K_c^T) (diag(eta_c) V_c) + Q_c S_{c-1}
 //     S_c = S_{c-1} + K_c^T diag(eta_c) V_c.
 //
-// bf16 kernel design (gfx950):
-//  * one workgroup = one (b,h) pair x one TV-wide tile of d_v; the columns
-//    of S are independent, so tiles need no communication.  The tiles of a
-//    head are placed on one XCD so their repeated Q/K reads hit that XCD's
-//    L2.  The chunk loop is sequential inside the workgroup; S (fp32) lives
-//    in MFMA accumulators for the whole sequence.
-//  * 4 waves.  Wave w owns i-blocks (16 query tokens) of the chunk for the
-//    output and a DK/4-row slab of S for the state update.  A bf16 copy of
-//    S is exchanged through LDS (double-buffered) for the Q S product.
-//  * Q, K, V, eta of a chunk are streamed HBM -> LDS with asynchronous
-//    direct-to-LDS loads through a STAGES-deep ring; waits are explicit
-//    vmcnt counts.  Q and K rows are XOR-swizzled in 16-byte units.
-//  * Products contracting over tokens (A V and K^T V) read their operands
-//    with the LDS transpose read; eta is applied to V when it is read
-//    (diag(eta) V rounded once to bf16 and used by both products).
-//  * The outputs go LDS -> HBM as 16-byte row pieces one chunk later.
-#include <type_traits>
+// bf16 design (gfx950): the sequence of each head is cut into P segments of
+// whole 64-token tiles so that heads x segments cover the compute units.
+//  1. pt_seg_kernel<D, false>: for every segment but the last, its state
+//     increment dS_s = K_s^T diag(eta_s) V_s (fp32) into the workspace;
+//  2. pt_seg_kernel<D, true>: segment s starts from
+//     S = W0 + sum_{s' < s} dS_s' and runs the chunked form over its tiles;
+//     the last segment writes W_out.
+// A workgroup has D/16 waves; wave w owns columns 16w..16w+15 of S and O for
+// all D rows of S, which stay in MFMA accumulators for the whole segment, so
+// no state is exchanged between waves.  Q, K, V and eta go HBM -> LDS with
+// asynchronous direct-to-LDS loads through a 3-stage ring (explicit vmcnt
+// waits).  Per 64-token tile:
+//   phase 1: the 10 causal score tiles P^T(jb, ib) = K_jb Q_ib^T (jb <= ib),
+//            spread over the waves, scaled by eta of the key, masked and
+//            split bf16 hi + lo into LDS; O_w^T = S_w^T Q^T with S_w as bf16
+//            hi + lo built in registers from the accumulators (the
+//            contraction index follows the accumulator row order and Q is
+//            read in the same order);
+//   phase 2: V_w (4 transposed reads) serves as the operand of
+//            O_w^T += V_w^T A^T and, scaled by eta in registers and split
+//            hi + lo, of the state update S_w += K^T diag(eta) V_w.
+// Outputs are computed transposed, so a lane holds 4 consecutive columns of
+// one token: an 8-byte store.
+#include <algorithm>
 
 #include "device_common.h"
 #include "kernels.h"
 
 namespace ttt {
-
-// bf16 kernel, one 64-token tile per step, two phases per step:
-//   phase 1: the 10 score tiles P^T(jb, ib) = K_jb Q_ib^T (jb <= ib) are
-//            spread evenly over the 4 waves, scaled by eta_j, masked and
-//            split into bf16 hi + lo in LDS; each wave w starts its outputs
-//            O_w^T = S_{c-1}^T Q_w^T for the queries 16w..16w+15; the
-//            diag(eta) V planes of the next tile are prepared.
-//   phase 2: O_w^T += V^T A_w^T (A from the score tiles), stored to HBM;
-//            S += K^T (diag(eta) V) on the wave's DK/4-row slab; the new S is
-//            written to LDS for the next step.
-// Outputs are computed transposed so one lane holds 4 consecutive output
-// columns of one token: an 8-byte store per lane.  Each wave runs its own
-// instantiation of the program (the wave index is a template parameter) so
-// every tile index and LDS offset is a compile-time constant added to a
-// handful of per-lane offsets computed once.
-template <int DK, int TV, int NW_>
-struct PerTokenCfg {
-  static constexpr int C = 64;                 // tokens per tile
-  static constexpr int NW = NW_;               // 4 waves, or 8 (two per SIMD) when there are >= 2 column tiles
-  static constexpr int THREADS = NW * WAVE;
-  static constexpr int QKSTAGES = 3;           // Q and K rings
-  static constexpr int VSTAGES = 4;            // V / eta ring: prefetched one tile further
-  static constexpr int NT = TV / 16;
-  static constexpr int GW = NW / 4;            // waves sharing one query block / state slab
-  static constexpr int NTW = NT / GW;          // 16-column tiles per wave
-  static constexpr int KT = DK / 32;
-  static constexpr int MTW = DK / 64;          // 16-row m-tiles of S per wave
-  static constexpr int CPR = DK / 8;           // 16-byte pieces per Q/K row
-  static constexpr int SWZ = CPR >= 16 ? 15 : CPR - 1;  // XOR swizzle of 16-byte pieces by row
-  static constexpr int ROWB = DK * 2;
-  static constexpr int QK_BYTES = C * ROWB;
-  static constexpr int V_BYTES = C * TV * 2;
-  static constexpr int E_BYTES = C * 4;
-  static constexpr int S_BYTES = TV * ROWB;    // one bf16 plane of S^T [TV][DK], swizzled like Q/K
-  static constexpr int P_BYTES = 10 * 64 * 8;  // one plane of the 10 score tiles, 8 bytes per lane
-  static constexpr int OFF_Q = 0;
-  static constexpr int OFF_K = OFF_Q + QKSTAGES * QK_BYTES;
-  static constexpr int OFF_V = OFF_K + QKSTAGES * QK_BYTES;
-  static constexpr int OFF_E = OFF_V + VSTAGES * V_BYTES;
-  static constexpr int OFF_EV = OFF_E + VSTAGES * E_BYTES;   // [2 buffers][hi, lo]
-  static constexpr int OFF_S = OFF_EV + 4 * V_BYTES;         // [hi, lo]
-  static constexpr int OFF_P = OFF_S + 2 * S_BYTES;          // [hi, lo]
-  static constexpr int LDS_BYTES = OFF_P + 2 * P_BYTES;
-  // per-wave vector-memory instructions issued every step
-  static constexpr int QI = QK_BYTES / 1024 / NW;
-  static constexpr int VPW = C * TV / 8 / NW;  // 16-byte V pieces per wave
-  static constexpr int VI = (VPW + 63) / 64;
-  static constexpr int OPS = 2 * QI + VI + 1 /*eta*/ + NTW /*O stores*/;
-  static_assert(NT % GW == 0, "column tiles must split evenly over the waves of a block");
-  static_assert(QK_BYTES % (1024 * NW) == 0, "Q/K tile must split into whole wave loads");
-  static_assert(OPS < 64, "vmcnt range");
-  static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
-};
 
 // score tile t (0..9) <-> (jb, ib), jb <= ib; wave w owns tiles [tile_begin(w), tile_begin(w+1))
 __host__ __device__ constexpr int ptile_jb(int t) { return t < 1 ? 0 : t < 3 ? t - 1 : t < 6 ? t - 3 : t - 6; }
@@ -95,356 +49,425 @@ __host__ __device__ constexpr int tile_begin8(int w) { return w <= 3 ? 2 * w : w
 template <int NW>
 __host__ __device__ constexpr int tile_begin(int w) { return NW == 4 ? tile_begin4(w) : tile_begin8(w); }
 
-struct PerTokenPtrs {
-  const bf16* Qh;
-  const bf16* Kh;
-  const bf16* Vh;
-  const float* Eh;
-  bf16* Oh;
-  const float* W0h;
-  float* Wh;
-  int T, DV, tv0;
+template <int D, bool FULL>
+struct SegCfg {
+  static constexpr int C = 64;                   // tokens per tile
+  static constexpr int NW = D / 16;              // waves; wave w owns columns 16w..16w+15
+  static constexpr int THREADS = NW * WAVE;
+  static constexpr int MT = D / 16;              // 16-row tiles of S per wave
+  static constexpr int KP = D / 32;              // 32-deep contraction steps over d
+  static constexpr int ROWB = D * 2;             // bytes per token row of Q, K, V, O
+  static constexpr int MAT = C * ROWB;           // one matrix of a tile
+  // ring slot: [Q (FULL only; reused for the tile's outputs)] K V eta
+  static constexpr int NMAT = FULL ? 3 : 2;
+  static constexpr int STAGES = FULL ? 3 : 4;
+  static constexpr int OFF_K = FULL ? MAT : 0;
+  static constexpr int OFF_V = OFF_K + MAT;
+  static constexpr int OFF_E = OFF_V + MAT;
+  static constexpr int STAGE = NMAT * MAT + C * 4;
+  static constexpr int OFF_P = STAGES * STAGE;   // score tiles [hi, lo][10][64 lanes x 8 bytes]
+  static constexpr int P_PLANE = 10 * 512;
+  static constexpr int LDS_BYTES = OFF_P + (FULL ? 2 * P_PLANE : 0);
+  static constexpr int EPW = C / NW;             // eta values loaded by each wave
+  static constexpr int MAT_LOADS = MAT / 1024 / NW;  // 16-byte direct-to-LDS loads per wave per matrix
+  static constexpr int LOADS = NMAT * MAT_LOADS + 1;
+  static constexpr int OUT_STORES = MAT_LOADS;   // 16-byte output stores per wave per tile
+  static_assert(MAT % (1024 * NW) == 0, "tile matrix must split into whole wave loads");
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
 };
 
-template <int DK, int TV, int NW, int W>
-__device__ __forceinline__ void per_token_wave(const PerTokenPtrs& P, unsigned char* smem, int l) {
-  using Cfg = PerTokenCfg<DK, TV, NW>;
-  constexpr int C = Cfg::C;
-  constexpr int ROWB = Cfg::ROWB;
-  constexpr int SWZ = Cfg::SWZ;
-  constexpr int IB = W / Cfg::GW;              // this wave's query block (16 queries)
-  constexpr int NT0 = (W % Cfg::GW) * Cfg::NTW;  // first of this wave's column tiles
-  constexpr int SLAB = DK / 4 * IB;            // first state row of this wave
-  const int g = l >> 4;
-  const int li = l & 15;
-  const int tid = W * 64 + l;
-  const int T = P.T, DV = P.DV, tv0 = P.tv0;
-  const int nchunks = (T + C - 1) / C;
-
-  // ---- per-lane byte offsets, fixed for the whole sequence ----
-  unsigned qkoff[Cfg::QI];                     // DMA: global offset of LDS slot (W*QI + k)*64 + l
-#pragma unroll
-  for (int k = 0; k < Cfg::QI; ++k) {
-    const int s = (W * Cfg::QI + k) * 64 + l;
-    const int row = s / Cfg::CPR;
-    qkoff[k] = (unsigned)(row * ROWB + (((s % Cfg::CPR) ^ (row & SWZ)) << 4));
-  }
-  unsigned voff[Cfg::VI];
-#pragma unroll
-  for (int k = 0; k < Cfg::VI; ++k) {
-    const int p = W * Cfg::VPW + k * 64 + l;
-    voff[k] = (unsigned)((p / (TV / 8)) * DV * 2 + (tv0 + (p % (TV / 8)) * 8) * 2);
-  }
-  // natural 16-byte operand reads: row 16*blk + li, d = 32*ks + 8g  ->  blk*16*ROWB + nat[ks]
-  int nat[Cfg::KT];
-#pragma unroll
-  for (int ks = 0; ks < Cfg::KT; ++ks) nat[ks] = li * ROWB + ((((4 * ks + g) ^ (li & SWZ))) << 4);
-  // S^T plane writes: row n = 16nt + li, d_k = SLAB + 16j + 4g  ->  nt*16*ROWB + swr[j]
-  int swr[Cfg::MTW];
-#pragma unroll
-  for (int j = 0; j < Cfg::MTW; ++j) {
-    const int k = SLAB + 16 * j + 4 * g;
-    swr[j] = li * ROWB + ((((k >> 3) ^ (li & SWZ))) << 4) + (k & 7) * 2;
-  }
-  // transposed K reads for the state update: rows 32kc + 16h + 4g + li/4, cols SLAB + 16j + 4(li%4)
-  int ktr[Cfg::MTW];
-#pragma unroll
-  for (int j = 0; j < Cfg::MTW; ++j) {
-    const int r = 4 * g + (li >> 2), col = SLAB + 16 * j + 4 * (li & 3);
-    ktr[j] = r * ROWB + ((((col >> 3) ^ (r & SWZ))) << 4) + (col & 7) * 2;
-  }
-  const int vtr = (4 * g + (li >> 2)) * (TV * 2) + 4 * (li & 3) * 2;   // + (32kc + 16h)*TV*2 + 32nt
-  const unsigned ooff = (unsigned)((16 * IB + li) * DV * 2 + (tv0 + 16 * NT0 + 4 * g) * 2);
-
-  auto issue_qk = [&](int c, int slot) {
-    const long long rem = (long long)T - (long long)c * C;
-    const __amdgpu_buffer_rsrc_t rq = make_rsrc(P.Qh + (size_t)c * C * DK, rem * ROWB);
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(P.Kh + (size_t)c * C * DK, rem * ROWB);
-    unsigned char* dq = smem + Cfg::OFF_Q + slot * Cfg::QK_BYTES + W * Cfg::QI * 1024;
-    unsigned char* dk = smem + Cfg::OFF_K + slot * Cfg::QK_BYTES + W * Cfg::QI * 1024;
-#pragma unroll
-    for (int k = 0; k < Cfg::QI; ++k) buf2lds16(rq, qkoff[k], dq + k * 1024);
-#pragma unroll
-    for (int k = 0; k < Cfg::QI; ++k) buf2lds16(rk, qkoff[k], dk + k * 1024);
-  };
-  auto issue_ve = [&](int c, int slot) {
-    const long long rem = (long long)T - (long long)c * C;
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(P.Vh + (size_t)c * C * DV, rem * DV * 2);
-    unsigned char* dst = smem + Cfg::OFF_V + slot * Cfg::V_BYTES + W * Cfg::VPW * 16;
-#pragma unroll
-    for (int k = 0; k < Cfg::VI; ++k)
-      if (k * 64 + l < Cfg::VPW) buf2lds16(rv, voff[k], dst + k * 1024);
-    const __amdgpu_buffer_rsrc_t re = make_rsrc(P.Eh + (size_t)c * C, rem * 4);
-    if (l < C / Cfg::NW)
-      buf2lds4(re, (unsigned)((W * (C / Cfg::NW) + l) * 4), smem + Cfg::OFF_E + slot * Cfg::E_BYTES + W * (C / Cfg::NW) * 4);
-  };
-  // diag(eta) V of one tile as bf16 hi + lo planes (same layout as the V tile)
-  auto convert_ev = [&](int vslot, int buf) {
-    const unsigned char* vs = smem + Cfg::OFF_V + vslot * Cfg::V_BYTES;
-    const float* es = (const float*)(smem + Cfg::OFF_E + vslot * Cfg::E_BYTES);
-    unsigned char* eh = smem + Cfg::OFF_EV + buf * 2 * Cfg::V_BYTES;
-#pragma unroll
-    for (int p0 = 0; p0 < C * TV / 8; p0 += Cfg::THREADS) {
-      const int p = p0 + tid;
-      if (p < C * TV / 8) {
-        const bf16x8 v = *(const bf16x8*)(vs + p * 16);
-        const float e = es[p / (TV / 8)];
-        bf16x8 hi, lo;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const float f = e * (float)v[j];
-          hi[j] = (bf16)f;
-          lo[j] = (bf16)(f - (float)hi[j]);
-        }
-        *(bf16x8*)(eh + p * 16) = hi;
-        *(bf16x8*)(eh + Cfg::V_BYTES + p * 16) = lo;
-      }
-    }
-  };
-
-  // ---- state: S[j][n] holds rows SLAB + 16j + 4g + r, column 16(NT0 + n) + li ----
-  floatx4 S[Cfg::MTW][Cfg::NTW];
-#pragma unroll
-  for (int j = 0; j < Cfg::MTW; ++j)
-#pragma unroll
-    for (int n = 0; n < Cfg::NTW; ++n)
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        S[j][n][r] = P.W0h[(size_t)(SLAB + 16 * j + 4 * g + r) * DV + tv0 + 16 * (NT0 + n) + li];
-  auto write_s_lds = [&]() {
-    unsigned char* sb = smem + Cfg::OFF_S;
-#pragma unroll
-    for (int j = 0; j < Cfg::MTW; ++j)
-#pragma unroll
-      for (int n = 0; n < Cfg::NTW; ++n) {
-        const int nt = NT0 + n;
-        bf16x4 hi, lo;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          hi[r] = (bf16)S[j][n][r];
-          lo[r] = (bf16)(S[j][n][r] - (float)hi[r]);
-        }
-        *(bf16x4*)(sb + nt * 16 * ROWB + swr[j]) = hi;
-        *(bf16x4*)(sb + Cfg::S_BYTES + nt * 16 * ROWB + swr[j]) = lo;
-      }
-  };
-
-  if (nchunks > 0) {
-    write_s_lds();
-    issue_qk(0, 0);
-    issue_ve(0, 0);
-    issue_qk(1, 1);
-    issue_ve(1, 1);
-    issue_ve(2, 2);
-    wait_vm_barrier<0>();
-    convert_ev(0, 0);
-  }
-
-  int qslot = 0, vslot = 0;
-  for (int c = 0; c < nchunks; ++c) {
-    // loads of tile c landed, and V/eta of tile c+1; all of step c-1 done
-    if (c >= 1)
-      wait_vm_barrier<Cfg::OPS>();
-    else
-      wait_vm_barrier<0>();
-    const int qslot2 = qslot == 0 ? 2 : qslot - 1;          // (c + 2) % 3
-    const int vslot1 = (vslot + 1) & 3, vslot3 = (vslot + 3) & 3;
-    // prefetch: Q/K of tile c+2, V/eta of tile c+3 (past the end: empty resources)
-    issue_qk(c + 2, qslot2);
-    issue_ve(c + 3, vslot3);
-
-    const unsigned char* qst = smem + Cfg::OFF_Q + qslot * Cfg::QK_BYTES;
-    const unsigned char* kst = smem + Cfg::OFF_K + qslot * Cfg::QK_BYTES;
-    const unsigned char* vs = smem + Cfg::OFF_V + vslot * Cfg::V_BYTES;
-    const float* es = (const float*)(smem + Cfg::OFF_E + vslot * Cfg::E_BYTES);
-    const unsigned char* evb = smem + Cfg::OFF_EV + (c & 1) * 2 * Cfg::V_BYTES;
-    const unsigned char* sb = smem + Cfg::OFF_S;
-    unsigned char* pb = smem + Cfg::OFF_P;
-
-    // ---- phase 1a: this wave's score tiles ----
-#pragma unroll
-    for (int t = tile_begin<NW>(W); t < tile_begin<NW>(W + 1); ++t) {
-      const int jb = ptile_jb(t), ib = ptile_ib(t);
-      floatx4 p = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < Cfg::KT; ++ks) {
-        const bf16x8 kop = *(const bf16x8*)(kst + jb * 16 * ROWB + nat[ks]);
-        const bf16x8 qop = *(const bf16x8*)(qst + ib * 16 * ROWB + nat[ks]);
-        p = mfma16(kop, qop, p);
-      }
-      const floatx4 e4 = *(const floatx4*)(es + 16 * jb + 4 * g);
-      bf16x4 hi, lo;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        float f = p[r] * e4[r];
-        if (jb == ib && 4 * g + r > li) f = 0.f;
-        hi[r] = (bf16)f;
-        lo[r] = (bf16)(f - (float)hi[r]);
-      }
-      *(bf16x4*)(pb + t * 512 + l * 8) = hi;
-      *(bf16x4*)(pb + Cfg::P_BYTES + t * 512 + l * 8) = lo;
-    }
-    // ---- phase 1b: O_w^T = S^T Q_w^T (S as bf16 hi + lo) ----
-    bf16x8 qop[Cfg::KT];
-#pragma unroll
-    for (int ks = 0; ks < Cfg::KT; ++ks) qop[ks] = *(const bf16x8*)(qst + IB * 16 * ROWB + nat[ks]);
-    floatx4 acc[Cfg::NTW];
-#pragma unroll
-    for (int n = 0; n < Cfg::NTW; ++n) {
-      const int nt = NT0 + n;
-      acc[n] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < Cfg::KT; ++ks) {
-        acc[n] = mfma16(*(const bf16x8*)(sb + nt * 16 * ROWB + nat[ks]), qop[ks], acc[n]);
-        acc[n] = mfma16(*(const bf16x8*)(sb + Cfg::S_BYTES + nt * 16 * ROWB + nat[ks]), qop[ks], acc[n]);
-      }
-    }
-    // ---- phase 1c: diag(eta) V planes of tile c+1 ----
-    if (c + 1 < nchunks) convert_ev(vslot1, (c + 1) & 1);
-    barrier();
-
-    // ---- phase 2a: O_w^T += V^T A_w^T over key blocks 0..IB ----
-    constexpr int NKC = IB / 2 + 1;
-    bf16x4 vtr_[NKC * Cfg::NTW * 2];
-    {
-      unsigned ad[NKC * Cfg::NTW * 2];
-      const unsigned vb0 = lds_addr(vs) + vtr;
-#pragma unroll
-      for (int kc = 0; kc < NKC; ++kc)
-#pragma unroll
-        for (int n = 0; n < Cfg::NTW; ++n) {
-          const unsigned o0 = vb0 + 32 * kc * TV * 2 + 32 * (NT0 + n);
-          ad[(kc * Cfg::NTW + n) * 2] = o0;
-          ad[(kc * Cfg::NTW + n) * 2 + 1] = o0 + 16 * TV * 2;
-        }
-      lds_tr16_batch<NKC * Cfg::NTW * 2>(vtr_, ad);
-    }
-#pragma unroll
-    for (int kc = 0; kc < NKC; ++kc) {
-      const int t0i = ptile_index(2 * kc, IB);
-      const bf16x4 h0 = *(const bf16x4*)(pb + t0i * 512 + l * 8);
-      const bf16x4 l0 = *(const bf16x4*)(pb + Cfg::P_BYTES + t0i * 512 + l * 8);
-      bf16x4 h1 = bf16x4{(bf16)0.f, (bf16)0.f, (bf16)0.f, (bf16)0.f}, l1 = h1;
-      if (2 * kc + 1 <= IB) {
-        const int t1i = ptile_index(2 * kc + 1, IB);
-        h1 = *(const bf16x4*)(pb + t1i * 512 + l * 8);
-        l1 = *(const bf16x4*)(pb + Cfg::P_BYTES + t1i * 512 + l * 8);
-      }
-      const bf16x8 bh_ = join(h0, h1), bl_ = join(l0, l1);
-#pragma unroll
-      for (int n = 0; n < Cfg::NTW; ++n) {
-        const bf16x8 vt = join(vtr_[(kc * Cfg::NTW + n) * 2], vtr_[(kc * Cfg::NTW + n) * 2 + 1]);
-        acc[n] = mfma16(vt, bh_, acc[n]);
-        acc[n] = mfma16(vt, bl_, acc[n]);
-      }
-    }
-    {
-      const long long rem = (long long)T - (long long)c * C;
-      const __amdgpu_buffer_rsrc_t ro = make_rsrc(P.Oh + (size_t)c * C * DV, rem * DV * 2);
-#pragma unroll
-      for (int n = 0; n < Cfg::NTW; ++n) {
-        const bf16x4 o = to_bf16x4(acc[n][0], acc[n][1], acc[n][2], acc[n][3]);
-        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(uint2v, o), ro, ooff + n * 32, 0, 0);
-      }
-    }
-    // ---- phase 2b: S += K^T (diag(eta) V)_hi + K^T (diag(eta) V)_lo on this wave's slab ----
-    // operands of both 32-token halves: per half, diag(eta)V hi/lo (2 reads
-    // each per column tile) then K^T (2 reads per m-tile)
-    constexpr int NE = 4 * Cfg::NTW, NKR = 2 * Cfg::MTW, NH = NE + NKR;
-    bf16x4 opb[2 * NH];
-    {
-      unsigned ad[2 * NH];
-      const unsigned eb0 = lds_addr(evb) + vtr, kb0 = lds_addr(kst);
-#pragma unroll
-      for (int kc = 0; kc < 2; ++kc) {
-#pragma unroll
-        for (int n = 0; n < Cfg::NTW; ++n) {
-          const unsigned o0 = eb0 + 32 * kc * TV * 2 + 32 * (NT0 + n), o1 = o0 + 16 * TV * 2;
-          ad[kc * NH + 4 * n + 0] = o0;
-          ad[kc * NH + 4 * n + 1] = o1;
-          ad[kc * NH + 4 * n + 2] = o0 + Cfg::V_BYTES;
-          ad[kc * NH + 4 * n + 3] = o1 + Cfg::V_BYTES;
-        }
-#pragma unroll
-        for (int j = 0; j < Cfg::MTW; ++j) {
-          const unsigned o0 = kb0 + ktr[j] + 32 * kc * ROWB;
-          ad[kc * NH + NE + 2 * j] = o0;
-          ad[kc * NH + NE + 2 * j + 1] = o0 + 16 * ROWB;
-        }
-      }
-      lds_tr16_batch<2 * NH>(opb, ad);
-    }
-#pragma unroll
-    for (int kc = 0; kc < 2; ++kc) {
-#pragma unroll
-      for (int j = 0; j < Cfg::MTW; ++j) {
-        const bf16x8 a = join(opb[kc * NH + NE + 2 * j], opb[kc * NH + NE + 2 * j + 1]);
-#pragma unroll
-        for (int n = 0; n < Cfg::NTW; ++n) {
-          const bf16x8 evh = join(opb[kc * NH + 4 * n], opb[kc * NH + 4 * n + 1]);
-          const bf16x8 evl = join(opb[kc * NH + 4 * n + 2], opb[kc * NH + 4 * n + 3]);
-          S[j][n] = mfma16(a, evh, S[j][n]);
-          S[j][n] = mfma16(a, evl, S[j][n]);
-        }
-      }
-    }
-    write_s_lds();
-    qslot = qslot == 2 ? 0 : qslot + 1;
-    vslot = vslot1;
-  }
-
-  wait_vm_barrier<0>();
-#pragma unroll
-  for (int j = 0; j < Cfg::MTW; ++j)
-#pragma unroll
-    for (int n = 0; n < Cfg::NTW; ++n)
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        P.Wh[(size_t)(SLAB + 16 * j + 4 * g + r) * DV + tv0 + 16 * (NT0 + n) + li] = S[j][n][r];
+// LDS layout of the 64-token tiles: row-major, with 16-byte piece p of row r
+// stored at piece p ^ seg_swz(r).  The products that contract over d read
+// their operands in the k order in which the S accumulators hold their rows
+// (d = 32p+4g..+3 and 32p+16+4g..+3 for lane group g): two 8-byte reads per
+// operand.  With this swizzle those reads, the transposed reads over rows
+// 4g..4g+3 and the output staging writes run without bank conflicts
+// (measured on gfx950).
+template <int D>
+__device__ __forceinline__ int seg_swz(int r) {
+  return D == 128 ? (((r & 7) << 1) | ((r >> 3) & 1)) : ((r & 6) | ((r >> 3) & 1));
 }
 
-template <int DK, int TV, int NW>
-__global__ __launch_bounds__(NW * 64, 1) void per_token_bf16_kernel(
-    const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
-    const float* __restrict__ eta, const float* __restrict__ W0, bf16* __restrict__ O,
-    float* __restrict__ Wout, int T, int DV) {
-  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  const int NV = DV / TV;
-  const int nblocks = gridDim.x;
-  const int logical = (nblocks % 8 == 0) ? xcd_logical_block(blockIdx.x, nblocks) : blockIdx.x;
-  const int bh = logical / NV;
-  PerTokenPtrs P;
-  P.Qh = Q + (size_t)bh * T * DK;
-  P.Kh = K + (size_t)bh * T * DK;
-  P.Vh = V + (size_t)bh * T * DV;
-  P.Eh = eta + (size_t)bh * T;
-  P.Oh = O + (size_t)bh * T * DV;
-  P.W0h = W0 + (size_t)bh * DK * DV;
-  P.Wh = Wout + (size_t)bh * DK * DV;
-  P.T = T;
-  P.DV = DV;
-  P.tv0 = (logical % NV) * TV;
-  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int l = threadIdx.x & 63;
-  if constexpr (NW == 4) {
-    switch (w) {
-      case 0: per_token_wave<DK, TV, NW, 0>(P, smem, l); break;
-      case 1: per_token_wave<DK, TV, NW, 1>(P, smem, l); break;
-      case 2: per_token_wave<DK, TV, NW, 2>(P, smem, l); break;
-      default: per_token_wave<DK, TV, NW, 3>(P, smem, l); break;
+// S_w += K^T diag(eta) V_w over the tile's 64 keys, in pieces that can be
+// placed on either side of a barrier: A operand rows 16m + li of K^T with keys
+// 16kb + 4g + j (transposed reads, one key half at a time); B operand
+// diag(eta) V_w built from the V_w fragments vt (same key order), split bf16
+// hi + lo.
+template <class Cfg>
+struct SegUpdate {
+  bf16x8 evh[2], evl[2];            // diag(eta) V_w, keys of half kc, bf16 hi + lo
+};
+template <class Cfg>
+__device__ __forceinline__ void seg_update_eta(SegUpdate<Cfg>& U, const float* es, const bf16x4 (&vt)[4], int g) {
+#pragma unroll
+  for (int kc = 0; kc < 2; ++kc) {
+    const floatx4 e0 = *(const floatx4*)(es + 32 * kc + 4 * g);
+    const floatx4 e1 = *(const floatx4*)(es + 32 * kc + 16 + 4 * g);
+    const uint2 v0 = __builtin_bit_cast(uint2, vt[2 * kc]), v1 = __builtin_bit_cast(uint2, vt[2 * kc + 1]);
+    split8(floatx4{e0[0] * bf16lo_f(v0.x), e0[1] * bf16hi_f(v0.x), e0[2] * bf16lo_f(v0.y), e0[3] * bf16hi_f(v0.y)},
+           floatx4{e1[0] * bf16lo_f(v1.x), e1[1] * bf16hi_f(v1.x), e1[2] * bf16lo_f(v1.y), e1[3] * bf16hi_f(v1.y)},
+           U.evh[kc], U.evl[kc]);
+  }
+}
+// transposed K operands of key half kc: rows 16m + li of K^T, keys 32kc + 16h + 4g + j
+template <class Cfg>
+__device__ __forceinline__ void seg_update_k(bf16x8 (&a)[Cfg::MT], const unsigned char* ks,
+                                             const unsigned (&ktr)[Cfg::MT], int kc) {
+#pragma unroll
+  for (int m = 0; m < Cfg::MT; ++m)
+    a[m] = join(lds_read_tr16(ks + (2 * kc) * 16 * Cfg::ROWB + ktr[m]),
+                lds_read_tr16(ks + (2 * kc + 1) * 16 * Cfg::ROWB + ktr[m]));
+}
+// hi products of every m-tile before the lo products: consecutive MFMAs never depend on each other
+template <class Cfg>
+__device__ __forceinline__ void seg_update_mfma(floatx4 (&S)[Cfg::MT], const bf16x8 (&a)[Cfg::MT],
+                                                const SegUpdate<Cfg>& U, int kc) {
+#pragma unroll
+  for (int m = 0; m < Cfg::MT; ++m) S[m] = mfma16(a[m], U.evh[kc], S[m]);
+#pragma unroll
+  for (int m = 0; m < Cfg::MT; ++m) S[m] = mfma16(a[m], U.evl[kc], S[m]);
+}
+
+struct SegArgs {
+  const bf16* Q;
+  const bf16* K;
+  const bf16* V;
+  const float* eta;
+  const float* W0;
+  floatx4* part;
+  bf16* O;
+  float* Wout;
+  int T, nseg, seg_tiles;
+  int scanned;                      // 1: workspace slot s already holds the start state of segment s
+};
+
+// The program of wave W (wave-uniform).  One program for all waves keeps the
+// code within the instruction cache.
+template <int D, bool FULL>
+__device__ __forceinline__ void seg_wave(const SegArgs& A, unsigned char* smem, int bh, int s, int W, int l) {
+  using Cfg = SegCfg<D, FULL>;
+  constexpr int C = Cfg::C, ROWB = Cfg::ROWB, MT = Cfg::MT, KP = Cfg::KP, NW = Cfg::NW, MAT = Cfg::MAT;
+  constexpr int LOADS = Cfg::LOADS;
+  const int g = l >> 4, li = l & 15;
+  const int T = A.T, nseg = A.nseg;
+  const int nchunks = (int)(((long long)T + C - 1) / C);
+  const int c0 = s * A.seg_tiles, c1 = min(c0 + A.seg_tiles, nchunks);
+  const int nt = c1 > c0 ? c1 - c0 : 0;
+  const long long seg_end = min((long long)c1 * C, (long long)T);
+  const bf16* Qh = A.Q + (size_t)bh * T * D;
+  const bf16* Kh = A.K + (size_t)bh * T * D;
+  const bf16* Vh = A.V + (size_t)bh * T * D;
+  const float* Eh = A.eta + (size_t)bh * T;
+  bf16* Oh = A.O + (size_t)bh * T * D;
+
+  // ---- per-lane byte offsets, fixed for the whole segment ----
+  // this wave's share of a tile matrix: LDS bytes [W*MAT_LOADS*1024, +MAT_LOADS*1024), i.e. whole rows
+  unsigned gofs[Cfg::MAT_LOADS];    // global offset of the 16 bytes lane l moves per load
+  unsigned lofs[Cfg::MAT_LOADS];    // their (swizzled) LDS offset
+#pragma unroll
+  for (int k = 0; k < Cfg::MAT_LOADS; ++k) {
+    const int b = (W * Cfg::MAT_LOADS + k) * 1024 + 16 * l;
+    const int row = b / ROWB, ph = (b % ROWB) >> 4;
+    gofs[k] = (unsigned)(row * ROWB + ((ph ^ seg_swz<D>(row)) << 4));
+    lofs[k] = (unsigned)b;
+  }
+  unsigned ksb[KP][2];              // operand reads in the S row order: row li, d = 32p + 4g.. and 32p + 16 + 4g..
+#pragma unroll
+  for (int p = 0; p < KP; ++p)
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      ksb[p][h] = (unsigned)(li * ROWB + (((4 * p + 2 * h + (g >> 1)) ^ seg_swz<D>(li)) << 4) + (g & 1) * 8);
+  const int trow = 4 * g + (li >> 2);   // transposed reads: rows 4g..4g+3, column 16m + li
+  unsigned ktr[MT];
+#pragma unroll
+  for (int m = 0; m < MT; ++m)
+    ktr[m] = (unsigned)(trow * ROWB + (((2 * m + ((li >> 1) & 1)) ^ seg_swz<D>(trow)) << 4) + (li & 1) * 8);
+  const unsigned vtr = (unsigned)(trow * ROWB + (((2 * W + ((li >> 1) & 1)) ^ seg_swz<D>(trow)) << 4) + (li & 1) * 8);
+  // output fragment (row 16ib + li, columns 16W + 4g..+3) in the swizzled staging rows
+  const unsigned ofr = (unsigned)(li * ROWB + (((2 * W + (g >> 1)) ^ seg_swz<D>(li)) << 4) + (g & 1) * 8);
+
+  auto issue = [&](int i) {         // tile i of the segment into ring slot i % STAGES (empty past the segment)
+    const long long t0 = (long long)(c0 + i) * C;
+    const long long rem = seg_end - t0;
+    unsigned char* st = smem + (i % Cfg::STAGES) * Cfg::STAGE + W * Cfg::MAT_LOADS * 1024;
+    if constexpr (FULL) {
+      const __amdgpu_buffer_rsrc_t rq = make_rsrc(Qh + (rem > 0 ? t0 * D : 0), rem * ROWB);
+#pragma unroll
+      for (int k = 0; k < Cfg::MAT_LOADS; ++k) dma16(rq, gofs[k], st + k * 1024);
+    }
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kh + (rem > 0 ? t0 * D : 0), rem * ROWB);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vh + (rem > 0 ? t0 * D : 0), rem * ROWB);
+#pragma unroll
+    for (int k = 0; k < Cfg::MAT_LOADS; ++k) dma16(rk, gofs[k], st + Cfg::OFF_K + k * 1024);
+#pragma unroll
+    for (int k = 0; k < Cfg::MAT_LOADS; ++k) dma16(rv, gofs[k], st + Cfg::OFF_V + k * 1024);
+    const __amdgpu_buffer_rsrc_t re = make_rsrc(Eh + (rem > 0 ? t0 : 0), rem * 4);
+    unsigned char* ed = smem + (i % Cfg::STAGES) * Cfg::STAGE + Cfg::OFF_E + W * Cfg::EPW * 4;
+    if (l < Cfg::EPW) dma4(re, (unsigned)((W * Cfg::EPW + l) * 4), ed);
+  };
+  // rows of tile i's outputs staged in its (dead) Q region -> HBM, 16 bytes per lane, whole rows
+  auto write_out = [&](int i) {
+    const long long t0 = (long long)(c0 + i) * C;
+    const unsigned char* st = smem + (i % Cfg::STAGES) * Cfg::STAGE;
+    const __amdgpu_buffer_rsrc_t ro = make_rsrc(Oh + t0 * D, ((long long)T - t0) * ROWB);
+    u32x4 v[Cfg::MAT_LOADS];
+#pragma unroll
+    for (int k = 0; k < Cfg::MAT_LOADS; ++k) v[k] = *(const u32x4*)(st + lofs[k]);
+#pragma unroll
+    for (int k = 0; k < Cfg::MAT_LOADS; ++k) buf_store16(ro, gofs[k], v[k]);
+  };
+
+  // ---- state: S[m][r] = S[16m + 4g + r][16W + li] ----
+  floatx4 S[MT];
+  if constexpr (FULL) {
+    const floatx4* pp = A.part + ((size_t)bh * nseg * NW + W) * MT * 64 + l;   // slot 0 of this head
+    constexpr int SLOT = NW * MT * 64;                                         // floatx4 per slot
+    if (A.scanned) {
+      // start state of this segment, prepared by pt_seg_scan_kernel in the same fragment layout
+#pragma unroll
+      for (int m = 0; m < MT; ++m) S[m] = pp[(size_t)s * SLOT + m * 64];
+    } else {
+      // W0 [D][D] fp32 -> LDS with coalesced 16-byte copies (the ring is still empty), then this lane's
+      // fragment; the increments of earlier segments are added, 4 segments per memory round trip
+      const float* W0h = A.W0 + (size_t)bh * D * D;
+      const __amdgpu_buffer_rsrc_t rw = make_rsrc(W0h, (long long)D * D * 4);
+#pragma unroll
+      for (int k = 0; k < D * D * 4 / 1024 / NW; ++k) {
+        const unsigned b = (unsigned)((W * (D * D * 4 / 1024 / NW) + k) * 1024);
+        dma16(rw, b + 16 * l, smem + b);
+      }
+      floatx4 d[4][MT];             // increments of segments s0..s0+3 (clamped; only those < s are added)
+      auto load_incr = [&](int s0) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int sp = min(s0 + k, max(s - 1, 0));
+#pragma unroll
+          for (int m = 0; m < MT; ++m) d[k][m] = pp[(size_t)sp * SLOT + m * 64];
+        }
+      };
+      if (s > 0) load_incr(0);      // in flight together with the W0 copy
+      wait_vm_barrier<0>();
+      const float* wl = (const float*)smem;
+#pragma unroll
+      for (int m = 0; m < MT; ++m)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) S[m][r] = wl[(16 * m + 4 * g + r) * D + 16 * W + li];
+      for (int s0 = 0; s0 < s; s0 += 4) {
+        if (s0 > 0) load_incr(s0);
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          if (s0 + k < s)
+#pragma unroll
+            for (int m = 0; m < MT; ++m) S[m] += d[k][m];
+      }
+      barrier();                    // everyone has read W0 before the ring overwrites it
     }
   } else {
-    switch (w) {
-      case 0: per_token_wave<DK, TV, NW, 0>(P, smem, l); break;
-      case 1: per_token_wave<DK, TV, NW, 1>(P, smem, l); break;
-      case 2: per_token_wave<DK, TV, NW, 2>(P, smem, l); break;
-      case 3: per_token_wave<DK, TV, NW, 3>(P, smem, l); break;
-      case 4: per_token_wave<DK, TV, NW, 4>(P, smem, l); break;
-      case 5: per_token_wave<DK, TV, NW, 5>(P, smem, l); break;
-      case 6: per_token_wave<DK, TV, NW, 6>(P, smem, l); break;
-      default: per_token_wave<DK, TV, NW, 7>(P, smem, l); break;
+#pragma unroll
+    for (int m = 0; m < MT; ++m) S[m] = floatx4{0.f, 0.f, 0.f, 0.f};
+  }
+
+#pragma unroll
+  for (int k = 0; k < Cfg::STAGES - 1; ++k)
+    if (nt > 0) issue(k);
+  for (int i = 0; i < nt; ++i) {
+    // tile i has landed once only later-issued loads (and output stores) may be outstanding
+    if constexpr (FULL) {
+      if (i < 2)
+        wait_vm_barrier<LOADS>();
+      else
+        wait_vm_barrier<LOADS + Cfg::OUT_STORES>();
+      if (i >= 1) {
+        write_out(i - 1);           // from the slot the next load overwrites: read it first
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      }
+    } else {
+      wait_vm_barrier<(Cfg::STAGES - 2) * LOADS>();
+    }
+    issue(i + Cfg::STAGES - 1);     // into the slot read during tile i-1
+    const unsigned char* st = smem + (i % Cfg::STAGES) * Cfg::STAGE;
+    const unsigned char* ks = st + Cfg::OFF_K;
+    const unsigned char* vs = st + Cfg::OFF_V;
+    const float* es = (const float*)(st + Cfg::OFF_E);
+
+    if constexpr (FULL) {
+      const unsigned char* qs = st;
+      unsigned char* pb = smem + Cfg::OFF_P;
+      floatx4 acc[4];
+      bf16x4 vt[4];                 // vt[kb][j] = V[16kb + 4g + j][16W + li]
+      SegUpdate<Cfg> U;
+      // Q operand of block ib, step p (k order of the S accumulators)
+      auto qop = [&](int p, int ib) {
+        const unsigned char* qrow = qs + ib * 16 * ROWB;
+        return join(*(const bf16x4*)(qrow + ksb[p][0]), *(const bf16x4*)(qrow + ksb[p][1]));
+      };
+      // this wave's score tiles P^T(jb, ib) = K_jb Q_ib^T, scaled by eta of the key, masked, bf16 hi + lo
+      auto scores = [&]() {
+        const int tb = tile_begin<NW>(W), te = tile_begin<NW>(W + 1);
+#pragma unroll
+        for (int t = 0; t < 10; ++t) {
+          if (t < tb || t >= te) continue;    // wave-uniform
+          const int jb = ptile_jb(t), ib = ptile_ib(t);
+          floatx4 p = {0.f, 0.f, 0.f, 0.f};
+          const unsigned char* krow = ks + jb * 16 * ROWB;
+#pragma unroll
+          for (int kk = 0; kk < KP; ++kk) {
+            const bf16x8 ka = join(*(const bf16x4*)(krow + ksb[kk][0]), *(const bf16x4*)(krow + ksb[kk][1]));
+            p = mfma16(ka, qop(kk, ib), p);
+          }
+          const floatx4 e4 = *(const floatx4*)(es + 16 * jb + 4 * g);
+          floatx4 f;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) f[r] = (jb == ib && 4 * g + r > li) ? 0.f : p[r] * e4[r];
+          const uint2 s01 = split2(f[0], f[1]), s23 = split2(f[2], f[3]);
+          *(uint2*)(pb + t * 512 + l * 8) = uint2{s01.x, s23.x};
+          *(uint2*)(pb + Cfg::P_PLANE + t * 512 + l * 8) = uint2{s01.y, s23.y};
+        }
+      };
+      // O_W^T = S_W^T Q^T with S_W as bf16 hi + lo
+      auto qs_mfma = [&]() {
+#pragma unroll
+        for (int ib = 0; ib < 4; ++ib) acc[ib] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int p = 0; p < KP; ++p) {
+          bf16x8 ah, al, qv[4];
+#pragma unroll
+          for (int ib = 0; ib < 4; ++ib) qv[ib] = qop(p, ib);
+          split8(S[2 * p], S[2 * p + 1], ah, al);
+#pragma unroll
+          for (int ib = 0; ib < 4; ++ib) acc[ib] = mfma16(ah, qv[ib], acc[ib]);
+#pragma unroll
+          for (int ib = 0; ib < 4; ++ib) acc[ib] = mfma16(al, qv[ib], acc[ib]);
+          __builtin_amdgcn_sched_barrier(0);   // keep each step's Q loads next to their use (register pressure)
+        }
+      };
+      // operands of phase 2 that do not depend on the score tiles
+      bf16x8 ka0[MT];               // transposed K operands of the first key half
+      auto load_update = [&]() {
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) vt[kb] = lds_read_tr16(vs + kb * 16 * ROWB + vtr);
+        seg_update_eta<Cfg>(U, es, vt, g);
+        seg_update_k<Cfg>(ka0, ks, ktr, 0);
+      };
+      // The two waves of a SIMD take phase 1 in opposite orders so that one
+      // issues MFMAs while the other reads LDS.
+      scores();
+      if (W < NW / 2) {
+        qs_mfma();
+        load_update();
+      } else {
+        load_update();
+        qs_mfma();
+      }
+      barrier();                    // score tiles visible; everyone is done reading Q of this tile
+
+      // ---- phase 2a: O_W^T += V_W^T A^T over key blocks 0..ib ----
+#pragma unroll
+      for (int ib = 0; ib < 4; ++ib)
+#pragma unroll
+        for (int kc = 0; 2 * kc <= ib; ++kc) {
+          const int t0i = ptile_index(2 * kc, ib);
+          bf16x4 h1 = bf16x4{(bf16)0.f, (bf16)0.f, (bf16)0.f, (bf16)0.f}, l1 = h1;
+          if (2 * kc + 1 <= ib) {
+            const int t1i = ptile_index(2 * kc + 1, ib);
+            h1 = *(const bf16x4*)(pb + t1i * 512 + l * 8);
+            l1 = *(const bf16x4*)(pb + Cfg::P_PLANE + t1i * 512 + l * 8);
+          }
+          const bf16x8 bh_ = join(*(const bf16x4*)(pb + t0i * 512 + l * 8), h1);
+          const bf16x8 bl_ = join(*(const bf16x4*)(pb + Cfg::P_PLANE + t0i * 512 + l * 8), l1);
+          const bf16x8 av = join(vt[2 * kc], vt[2 * kc + 1]);
+          acc[ib] = mfma16(av, bh_, acc[ib]);
+          acc[ib] = mfma16(av, bl_, acc[ib]);
+        }
+      // outputs into the Q region of this slot (written out after the next barrier)
+      unsigned char* ob = smem + (i % Cfg::STAGES) * Cfg::STAGE;
+#pragma unroll
+      for (int ib = 0; ib < 4; ++ib)
+        *(bf16x4*)(ob + ib * 16 * ROWB + ofr) = to_bf16x4(acc[ib][0], acc[ib][1], acc[ib][2], acc[ib][3]);
+      bf16x8 ka1[MT];
+      seg_update_k<Cfg>(ka1, ks, ktr, 1);
+      seg_update_mfma<Cfg>(S, ka0, U, 0);
+      seg_update_mfma<Cfg>(S, ka1, U, 1);
+    } else {
+      bf16x4 vt[4];
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) vt[kb] = lds_read_tr16(vs + kb * 16 * ROWB + vtr);
+      SegUpdate<Cfg> U;
+      seg_update_eta<Cfg>(U, es, vt, g);
+      bf16x8 ka[MT];
+#pragma unroll
+      for (int kc = 0; kc < 2; ++kc) {
+        seg_update_k<Cfg>(ka, ks, ktr, kc);
+        seg_update_mfma<Cfg>(S, ka, U, kc);
+      }
     }
   }
+  if constexpr (FULL) {
+    if (nt > 0) {
+      wait_vm_barrier<0>();
+      write_out(nt - 1);
+    }
+  }
+  wait_vm<0>();
+
+  if constexpr (FULL) {
+    if (s == nseg - 1) {
+      float* Wh = A.Wout + (size_t)bh * D * D;
+#pragma unroll
+      for (int m = 0; m < MT; ++m)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) Wh[(size_t)(16 * m + 4 * g + r) * D + 16 * W + li] = S[m][r];
+    }
+  } else {
+    floatx4* pp = A.part + (((size_t)bh * nseg + s) * NW + W) * MT * 64 + l;
+#pragma unroll
+    for (int m = 0; m < MT; ++m) pp[m * 64] = S[m];
+  }
+}
+
+// FULL = false: dS of segment s (grid BH x (nseg - 1)) -> part.
+// FULL = true : outputs of segment s (grid BH x nseg); starts from W0 plus
+//               the increments of the earlier segments of the head.
+template <int D, bool FULL>
+__global__ __launch_bounds__(D / 16 * WAVE, 1) void pt_seg_kernel(SegArgs A) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  const int segs_here = FULL ? A.nseg : A.nseg - 1;
+  const int bh = blockIdx.x / segs_here, s = blockIdx.x % segs_here;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  seg_wave<D, FULL>(A, smem, bh, s, w, threadIdx.x & 63);
+}
+
+// Start states of the segments of one head, in place: slot s holds dS_s
+// (s < nseg-1) on entry and S_start(s) = W0 + sum_{s' < s} dS_s' on exit.
+// Layout of a slot: [wave W][m-tile][lane][4] floats, lane (g, li) of wave W
+// holding rows 16m + 4g + r, column 16W + li.  One thread per 4 floats.
+template <int D>
+__global__ __launch_bounds__(256) void pt_seg_scan_kernel(const float* __restrict__ W0, floatx4* __restrict__ part,
+                                                          int nseg) {
+  constexpr int MT = D / 16, PER = D * D / 4;   // floatx4 per slot
+  const int per_head_blocks = PER / 256;
+  const int bh = blockIdx.x / per_head_blocks;
+  const int f = (blockIdx.x % per_head_blocks) * 256 + threadIdx.x;
+  const int W = f / (MT * 64), m = (f / 64) % MT, l = f % 64, g = l >> 4, li = l & 15;
+  const float* W0h = W0 + (size_t)bh * D * D;
+  floatx4 run;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) run[r] = W0h[(size_t)(16 * m + 4 * g + r) * D + 16 * W + li];
+  floatx4* ph = part + (size_t)bh * nseg * PER + f;
+  // up to 8 increments are loaded before any slot is rewritten (one memory round trip per 8 segments)
+  for (int s0 = 0; s0 < nseg - 1; s0 += 8) {
+    const int n = min(8, nseg - 1 - s0);
+    floatx4 d[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) d[k] = ph[(size_t)(s0 + min(k, n - 1)) * PER];
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      if (k < n) {
+        ph[(size_t)(s0 + k) * PER] = run;
+        run += d[k];
+      }
+  }
+  ph[(size_t)(nseg - 1) * PER] = run;
 }
 
 // ---------------------------------------------------------------------------
@@ -530,19 +553,6 @@ static size_t fp32_lds_bytes() {
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
-template <int DK, int TV, int NW = (TV >= 32 ? 8 : 4)>
-static hipError_t launch_bf16(const PerTokenArgs& a, hipStream_t stream) {
-  using Cfg = PerTokenCfg<DK, TV, NW>;
-  auto kern = per_token_bf16_kernel<DK, TV, NW>;
-  hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, Cfg::LDS_BYTES);
-  if (e != hipSuccess) return e;
-  const int grid = (int)(a.B * a.H * (a.DV / TV));
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(Cfg::THREADS), Cfg::LDS_BYTES, stream,
-                     (const bf16*)a.Q, (const bf16*)a.K, (const bf16*)a.V, a.eta, a.W0, (bf16*)a.O, a.W_out,
-                     (int)a.T, (int)a.DV);
-  return hipGetLastError();
-}
-
 template <int DK, int C>
 static hipError_t launch_fp32(const PerTokenArgs& a, hipStream_t stream) {
   auto kern = per_token_fp32_kernel<DK, C>;
@@ -562,12 +572,54 @@ bool per_token_supported(int64_t dk, int64_t dv, int64_t chunk, int dtype) {
   return true;
 }
 
-// Tile plan for the bf16 kernel: enough workgroups to cover the CUs while
-// keeping the per-tile recomputation of Q K^T small.
-int per_token_bf16_tv(int64_t BH, int64_t dv) {
-  if (BH * (dv / 32) < 256) return 16;
-  if (dv == 64 && BH * (dv / 64) >= 512) return 64;
-  return 32;
+// Segment plan of the bf16 path: about one workgroup per compute unit
+// (256 on MI355X) over heads x segments, each segment whole 64-token tiles.
+SegPlan per_token_seg_plan(int64_t BH, int64_t T) {
+  const int64_t nchunks = (T + 63) / 64;
+  int64_t p = BH >= 256 ? 1 : 256 / BH;
+  p = std::max<int64_t>(1, std::min(p, nchunks));
+  const int64_t tiles = nchunks > 0 ? (nchunks + p - 1) / p : 0;
+  const int64_t nseg = tiles > 0 ? (nchunks + tiles - 1) / tiles : 1;
+  return SegPlan{(int)nseg, (int)tiles};
+}
+
+size_t per_token_workspace(int64_t B, int64_t H, int64_t T, int64_t dk, int64_t dv, int dtype) {
+  if (dtype != 1) return 0;
+  const SegPlan sp = per_token_seg_plan(B * H, T);
+  return sp.nseg > 1 ? (size_t)sp.nseg * (size_t)(B * H) * (size_t)dk * (size_t)dv * sizeof(float) : 0;
+}
+
+template <int D>
+static hipError_t launch_seg(const PerTokenArgs& a, hipStream_t stream) {
+  using CfgD = SegCfg<D, false>;
+  using CfgF = SegCfg<D, true>;
+  const int BH = (int)(a.B * a.H);
+  const SegPlan sp = per_token_seg_plan(BH, a.T);
+  // With few segments every workgroup adds the earlier increments itself (one or two memory round
+  // trips); with many, a scan kernel turns them into start states first (linear instead of
+  // quadratic traffic, at the price of one more kernel boundary).
+  SegArgs A{(const bf16*)a.Q, (const bf16*)a.K, (const bf16*)a.V, a.eta, a.W0, (floatx4*)a.ws,
+            (bf16*)a.O, a.W_out, (int)a.T, sp.nseg, sp.tiles, sp.nseg > 8 ? 1 : 0};
+  hipError_t e;
+  if (sp.nseg > 1) {
+    auto kd = pt_seg_kernel<D, false>;
+    if ((e = hipFuncSetAttribute((const void*)kd, hipFuncAttributeMaxDynamicSharedMemorySize, CfgD::LDS_BYTES)) !=
+        hipSuccess)
+      return e;
+    hipLaunchKernelGGL(kd, dim3(BH * (sp.nseg - 1)), dim3(CfgD::THREADS), CfgD::LDS_BYTES, stream, A);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (A.scanned) {
+      hipLaunchKernelGGL(pt_seg_scan_kernel<D>, dim3(BH * (D * D / 4 / 256)), dim3(256), 0, stream, a.W0,
+                         (floatx4*)a.ws, sp.nseg);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+  }
+  auto kf = pt_seg_kernel<D, true>;
+  if ((e = hipFuncSetAttribute((const void*)kf, hipFuncAttributeMaxDynamicSharedMemorySize, CfgF::LDS_BYTES)) !=
+      hipSuccess)
+    return e;
+  hipLaunchKernelGGL(kf, dim3(BH * sp.nseg), dim3(CfgF::THREADS), CfgF::LDS_BYTES, stream, A);
+  return hipGetLastError();
 }
 
 hipError_t launch_per_token(const PerTokenArgs& a, hipStream_t stream) {
@@ -576,11 +628,7 @@ hipError_t launch_per_token(const PerTokenArgs& a, hipStream_t stream) {
     if (a.DK == 64) return c == 16 ? launch_fp32<64, 16>(a, stream) : c == 32 ? launch_fp32<64, 32>(a, stream) : launch_fp32<64, 64>(a, stream);
     return c == 16 ? launch_fp32<128, 16>(a, stream) : c == 32 ? launch_fp32<128, 32>(a, stream) : launch_fp32<128, 64>(a, stream);
   }
-  const int tv = per_token_bf16_tv(a.B * a.H, a.DV);
-  if (a.DK == 128) return tv == 16 ? launch_bf16<128, 16>(a, stream) : launch_bf16<128, 32>(a, stream);
-  if (tv == 16) return launch_bf16<64, 16>(a, stream);
-  if (tv == 64) return launch_bf16<64, 64>(a, stream);
-  return launch_bf16<64, 32>(a, stream);
+  return a.DK == 128 ? launch_seg<128>(a, stream) : launch_seg<64>(a, stream);
 }
 
 }  // namespace ttt

@@ -127,6 +127,19 @@ def test_workspace_query_and_check():
 
 
 @needs_lib
-def test_per_token_needs_no_workspace():
-    d = la.make_desc(4, 16, 4096, 128, 128, 0, la.BF16)
-    assert la.workspace_bytes(d, 64, "per_token_linear") == 0
+def test_per_token_workspace():
+    # fp32 needs none; bf16 splits a head's sequence into segments of whole
+    # 64-token tiles so that heads x segments reach 256 workgroups, and keeps
+    # one fp32 d_k x d_v state per segment when there is more than one
+    assert la.workspace_bytes(la.make_desc(4, 16, 4096, 128, 128, 0, la.FP32), 64, "per_token_linear") == 0
+    assert la.workspace_bytes(la.make_desc(16, 16, 4096, 128, 128, 0, la.BF16), 64, "per_token_linear") == 0
+    assert la.workspace_bytes(la.make_desc(1, 1, 64, 64, 64, 0, la.BF16), 64, "per_token_linear") == 0
+    d = la.make_desc(4, 16, 4096, 128, 128, 0, la.BF16)        # 64 heads x 4 segments of 16 tiles
+    n = la.workspace_bytes(d, 64, "per_token_linear")
+    assert n == 4 * 64 * 128 * 128 * 4
+    assert la.workspace_bytes(la.make_desc(1, 32, 32768, 128, 128, 0, la.BF16), 128, "per_token_linear") == \
+        8 * 32 * 128 * 128 * 4                                  # 32 heads x 8 segments
+    assert la.workspace_bytes(la.make_desc(1, 1, 300, 64, 64, 0, la.BF16), 64, "per_token_linear") == \
+        5 * 64 * 64 * 4                                         # 5 tiles -> 5 segments of one tile
+    assert call(desc=d, mode=0, chunk=64, ws=None, ws_bytes=0) == 8
+    assert call(desc=d, mode=0, chunk=64, ws_bytes=n - 1) == 8
