@@ -1,7 +1,7 @@
 """Throughput of the TTT-layer forward pass (libttt_la) on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                    [--no-others] [--no-cpu] [--flush-mb 512]
+                    [--no-others] [--no-cpu] [--flush-mb 512] [--calibrate-copy-mb N]
 
 A step is one ttt_la_forward call over one batch of synthetic inputs that
 are already resident in HBM.  Before every step a 512 MB buffer is
@@ -54,6 +54,27 @@ def algorithmic(s: dict) -> tuple[int, float]:
     return nbytes, float(flops)
 
 
+def dominant_kernel(s: dict) -> tuple[str, float, str]:
+    """The kernel ttt_la_forward_timed brackets for this mode, the algorithmic
+    units it processes per launch (bytes for an HBM-bound kernel, flops for
+    an MFMA-bound one) and its bound.
+
+    per-token: the chunked-form pass over the sequence moves all of the
+      method's bytes (reads Q, K, V, eta, W0; writes O, W_out).
+    large-chunk linear: the chunk update reads K, V and eta.
+    SwiGLU: the recurrence does the K forward (4 d d_h) and the four
+      gradient products (8 d d_h) of every token-head."""
+    B, H, T, dk, dv, dh = s["B"], s["H"], s["T"], s["d_k"], s["d_v"], s["d_h"]
+    es = 2 if s["dtype"] == "bf16" else 4
+    n = B * H * T
+    if s["mode"] == "per_token_linear":
+        return ("pt_seg_kernel (output pass)" if s["dtype"] == "bf16" else "per_token_fp32_kernel",
+                float(algorithmic(s)[0]), "hbm")
+    if s["mode"] == "large_chunk_linear":
+        return "lact_delta_kernel (chunk update)", float(n * ((dk + dv) * es + 4)), "hbm"
+    return "swiglu_recur_kernel (recurrence)", float(n * 12 * dk * dh), "mfma"
+
+
 def run_workload(name: str, steps: int, warmup: int, flush_mb: int):
     import torch
     import linear_attention_ttt_amd as la
@@ -75,9 +96,22 @@ def run_workload(name: str, steps: int, warmup: int, flush_mb: int):
     flush = torch.empty(flush_mb << 20, dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
 
-    def step():
-        la.forward(t["Q"], t["K"], t["V"], t["eta"], t["W0"], s["chunk"], s["mode"], out=O, W_out=Wout,
-                   workspace=ws)
+    # arguments prepared once: each step is one library call (no Python-side checks inside the timed region)
+    ptrs = [t[k].data_ptr() for k in ("Q", "K", "V", "eta", "W0")]
+    sptr = stream.cuda_stream
+
+    def step(timing=None):
+        if timing is None:
+            st = la.forward_raw(*ptrs, s["chunk"], s["mode"], desc, O.data_ptr(), Wout.data_ptr(), ws.data_ptr(),
+                                ws.numel(), sptr)
+        else:
+            st = la.forward_timed_raw(*ptrs, s["chunk"], s["mode"], desc, O.data_ptr(), Wout.data_ptr(),
+                                      ws.data_ptr(), ws.numel(), sptr, timing[0].cuda_event, timing[1].cuda_event)
+        if st != 0:
+            raise RuntimeError(f"ttt_la_forward failed: {la.status_string(st)}")
+
+    # reference call through the checked binding (also validates the raw arguments above)
+    la.forward(t["Q"], t["K"], t["V"], t["eta"], t["W0"], s["chunk"], s["mode"], out=O, W_out=Wout, workspace=ws)
 
     for _ in range(warmup):
         flush.fill_(1)
@@ -85,17 +119,25 @@ def run_workload(name: str, steps: int, warmup: int, flush_mb: int):
     torch.cuda.synchronize()
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    # recorded by the library around the dominant kernel of each call, on the same stream
+    kstarts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    kends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    for ev in kstarts + kends:      # torch creates its events lazily, on the first record
+        ev.record(stream)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     for i in range(steps):
         flush.fill_(i & 0xFF)
         starts[i].record(stream)
-        step()
+        step(timing=(kstarts[i], kends[i]))
         ends[i].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms = np.array([a.elapsed_time(b) for a, b in zip(starts, ends)])
+    kms = np.array([a.elapsed_time(b) for a, b in zip(kstarts, kends)])
     nbytes, flops = algorithmic(s)
+    kname, kunits, kbound = dominant_kernel(s)
+    kmean_s = float(kms.mean()) * 1e-3
     mean_s = float(ms.mean()) * 1e-3
     rec = dict(workload=name, mode=s["mode"], B=B, H=H, T=T, d=s["d_k"], d_h=s["d_h"], chunk=s["chunk"],
                dtype=s["dtype"], ms_per_step=float(ms.mean()), ms_min=float(ms.min()), ms_median=float(np.median(ms)),
@@ -103,10 +145,34 @@ def run_workload(name: str, steps: int, warmup: int, flush_mb: int):
                algorithmic_bytes=nbytes, algorithmic_flops=flops,
                hbm_GBps=nbytes / mean_s / 1e9, hbm_frac=nbytes / mean_s / 1e9 / HBM_PEAK_GBS,
                bf16_mfma_TFLOPs=flops / mean_s / 1e12, bf16_mfma_frac=flops / mean_s / 1e12 / BF16_PEAK_TFLOPS,
-               wall_s_including_flush=wall)
+               wall_s_including_flush=wall,
+               kernel=dict(name=kname, ms_mean=float(kms.mean()), ms_min=float(kms.min()), bound=kbound,
+                           units_per_launch=kunits,
+                           achieved=kunits / kmean_s / (1e9 if kbound == "hbm" else 1e12),
+                           unit="GB/s" if kbound == "hbm" else "TFLOP/s"))
     del t, O, Wout, ws, flush
     torch.cuda.empty_cache()
     return rec
+
+
+def traffic_per_launch(kernel: str):
+    """HBM bytes per launch of the dominant kernel from the committed counter
+    summary (FETCH_SIZE + WRITE_SIZE, calibrated against a copy of known
+    size), or None when there is none or the kernel source changed since."""
+    import hashlib
+    import re
+    path = os.path.join(ROOT, "profiles", "traffic_per_token_output_pass_B4H16T4096_d128.md")
+    src = os.path.join(ROOT, "linear_attention_ttt_amd", "csrc", "per_token.hip")
+    if not kernel.startswith("pt_seg_kernel") or not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_sha = re.search(r"source_sha256:\s*([0-9a-f]{64})", text)
+    m_bytes = re.search(r"hbm_bytes_per_launch:\s*([0-9]+)", text)
+    if not m_sha or not m_bytes:
+        return None
+    if hashlib.sha256(open(src, "rb").read()).hexdigest() != m_sha.group(1):
+        return None
+    return int(m_bytes.group(1))
 
 
 def cpu_baseline(name: str, target_s: float = 12.0):
@@ -151,6 +217,9 @@ def main():
     ap.add_argument("--no-others", action="store_true", help="skip the other workloads' sub-records")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--flush-mb", type=int, default=512)
+    ap.add_argument("--calibrate-copy-mb", type=int, default=0,
+                    help="first copy a buffer of this size 3 times (untimed), as a known-size reference for "
+                         "FETCH_SIZE / WRITE_SIZE counter runs")
     a = ap.parse_args()
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -160,6 +229,13 @@ def main():
 
     import torch
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if a.calibrate_copy_mb > 0:
+        src = torch.ones(a.calibrate_copy_mb << 18, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     head = run_workload(a.workload, a.steps, a.warmup, a.flush_mb)
     others = {}
     if not a.no_others:
@@ -171,15 +247,12 @@ def main():
             except Exception as e:  # a mode not built yet is reported, not fatal
                 others[name] = {"error": str(e)[:200]}
     s = workloads.spec(a.workload)
-    nbytes, flops = head["algorithmic_bytes"], head["algorithmic_flops"]
-    kernel_s = head["ms_per_step"] * 1e-3
-    roof = {"kernel": "per_token_bf16_kernel" if s["mode"] == "per_token_linear" else s["mode"],
-            "bound": "hbm", "achieved": nbytes / kernel_s / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": nbytes / kernel_s / 1e9 / HBM_PEAK_GBS, "traffic": None,
-            "algorithmic_bytes_per_launch": nbytes}
-    if s["mode"] == "large_chunk_swiglu":
-        roof.update(bound="mfma", achieved=flops / kernel_s / 1e12, peak=BF16_PEAK_TFLOPS, unit="TFLOP/s",
-                    frac=flops / kernel_s / 1e12 / BF16_PEAK_TFLOPS)
+    k = head["kernel"]
+    peak = HBM_PEAK_GBS if k["bound"] == "hbm" else BF16_PEAK_TFLOPS
+    roof = {"bound": k["bound"], "achieved": k["achieved"], "peak": peak, "unit": k["unit"],
+            "frac": k["achieved"] / peak, "traffic": traffic_per_launch(k["name"]),
+            "kernel": k["name"], "kernel_ms": k["ms_mean"], "units_per_launch": k["units_per_launch"],
+            "step_frac": head["hbm_frac"] if k["bound"] == "hbm" else head["bf16_mfma_frac"]}
     line = {
         "metric": METRIC,
         "value": head["tokens_per_s"],

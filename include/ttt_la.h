@@ -129,6 +129,25 @@ int ttt_la_forward(const void* Q, const void* K, const void* V, const float* eta
                    void* O, float* W_out, void* workspace, size_t workspace_bytes,
                    void* stream);
 
+/*
+ * ttt_la_forward_timed: ttt_la_forward (same arguments, checks, results and
+ * status codes) that additionally records two HIP events on `stream`
+ * immediately before and after the dominant kernel of the call, for
+ * measuring that kernel alone:
+ *   per-token      the chunked-form kernel over the sequence (bf16: the
+ *                  output pass over the segments; fp32: the whole kernel)
+ *   large-chunk    the chunk-update kernel (streams K and V)
+ *   SwiGLU         the recurrence over the chunks
+ * ev_start, ev_stop: hipEvent_t created by the caller (hipEventCreate), or
+ * NULL to skip; the library only records them.  Nothing is recorded when
+ * the call returns an error before enqueueing, nor by large-chunk linear
+ * with T = 0 (no chunk to update).
+ */
+int ttt_la_forward_timed(const void* Q, const void* K, const void* V, const float* eta,
+                         const float* W0, int64_t chunk, int32_t mode, const ttt_la_desc* desc,
+                         void* O, float* W_out, void* workspace, size_t workspace_bytes,
+                         void* stream, void* ev_start, void* ev_stop);
+
 /* Bytes of device workspace ttt_la_forward needs for this problem (0 if
  * none).  Returns 0 as well for invalid arguments (ttt_la_forward reports
  * those). */

@@ -15,7 +15,7 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["forward", "workspace_bytes", "TTTLAError", "MODES", "Desc", "lib", "library_path",
+__all__ = ["forward", "forward_timed_raw", "workspace_bytes", "TTTLAError", "MODES", "Desc", "lib", "library_path",
            "PER_TOKEN_LINEAR", "LARGE_CHUNK_LINEAR", "LARGE_CHUNK_SWIGLU"]
 
 PER_TOKEN_LINEAR = 0
@@ -56,6 +56,9 @@ def lib() -> ctypes.CDLL:
         L.ttt_la_forward.argtypes = [vp, vp, vp, vp, vp, i64, i32, ctypes.POINTER(Desc), vp, vp, vp,
                                      ctypes.c_size_t, vp]
         L.ttt_la_forward.restype = ctypes.c_int
+        L.ttt_la_forward_timed.argtypes = [vp, vp, vp, vp, vp, i64, i32, ctypes.POINTER(Desc), vp, vp, vp,
+                                           ctypes.c_size_t, vp, vp, vp]
+        L.ttt_la_forward_timed.restype = ctypes.c_int
         L.ttt_la_workspace_bytes.argtypes = [ctypes.POINTER(Desc), i64, i32]
         L.ttt_la_workspace_bytes.restype = ctypes.c_size_t
         L.ttt_la_status_string.argtypes = [ctypes.c_int]
@@ -89,14 +92,25 @@ def forward_raw(Q, K, V, eta, W0, chunk, mode, desc: Desc, O, W_out, workspace, 
                                     workspace, int(workspace_bytes_), stream))
 
 
-def forward(Q, K, V, eta, W0, chunk: int, mode, *, out=None, W_out=None, workspace=None, stream=None):
+def forward_timed_raw(Q, K, V, eta, W0, chunk, mode, desc: Desc, O, W_out, workspace, workspace_bytes_,
+                      stream, ev_start, ev_stop) -> int:
+    """ttt_la_forward_timed with raw addresses and raw hipEvent_t handles; returns the status."""
+    return int(lib().ttt_la_forward_timed(Q, K, V, eta, W0, int(chunk), _mode(mode), ctypes.byref(desc), O, W_out,
+                                          workspace, int(workspace_bytes_), stream, ev_start, ev_stop))
+
+
+def forward(Q, K, V, eta, W0, chunk: int, mode, *, out=None, W_out=None, workspace=None, stream=None,
+            timing=None):
     """Run the TTT forward pass.
 
     Q, K ``[B,H,T,d_k]`` and V ``[B,H,T,d_v]`` (bfloat16 or float32, same
     dtype), eta ``[B,H,T]`` float32, W0 float32 (``[B,H,d_k,d_v]`` for the
     linear modes, ``[B,H,3*d*d_h]`` packed W1|W3|W2 for SwiGLU), all
     contiguous CUDA tensors on one device.  Returns ``(O, W_out)``.
-    Passing ``W_out=W0`` updates the state in place."""
+    Passing ``W_out=W0`` updates the state in place.  ``timing=(start, stop)``
+    (two ``torch.cuda.Event(enable_timing=True)``) has the library record
+    them around the call's dominant kernel; ``start.elapsed_time(stop)``
+    then gives that kernel's duration."""
     import torch
 
     m = _mode(mode)
@@ -136,8 +150,18 @@ def forward(Q, K, V, eta, W0, chunk: int, mode, *, out=None, W_out=None, workspa
     ws_ptr = ws.data_ptr() if (ws is not None and nbytes > 0) else None
     ws_len = ws.numel() * ws.element_size() if ws_ptr else 0
     st = stream if stream is not None else torch.cuda.current_stream(dev).cuda_stream
-    status = forward_raw(Q.data_ptr(), K.data_ptr(), V.data_ptr(), eta.data_ptr(), W0.data_ptr(), chunk, m,
-                         desc, O.data_ptr(), Wo.data_ptr(), ws_ptr, ws_len, st)
+    if timing is None:
+        status = forward_raw(Q.data_ptr(), K.data_ptr(), V.data_ptr(), eta.data_ptr(), W0.data_ptr(), chunk, m,
+                             desc, O.data_ptr(), Wo.data_ptr(), ws_ptr, ws_len, st)
+    else:
+        e0, e1 = timing
+        sobj = torch.cuda.ExternalStream(st) if stream is not None else torch.cuda.current_stream(dev)
+        for ev in (e0, e1):          # torch creates its events lazily, on the first record
+            if not ev.cuda_event:
+                ev.record(sobj)
+        status = forward_timed_raw(Q.data_ptr(), K.data_ptr(), V.data_ptr(), eta.data_ptr(), W0.data_ptr(), chunk,
+                                   m, desc, O.data_ptr(), Wo.data_ptr(), ws_ptr, ws_len, st, e0.cuda_event,
+                                   e1.cuda_event)
     if status != 0:
         raise TTTLAError(status, status_string(status))
     return O, Wo

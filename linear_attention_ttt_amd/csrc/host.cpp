@@ -108,9 +108,9 @@ size_t ttt_la_workspace_bytes(const ttt_la_desc* desc, int64_t chunk, int32_t mo
   return workspace_for(*desc, chunk, mode);
 }
 
-int ttt_la_forward(const void* Q, const void* K, const void* V, const float* eta, const float* W0,
-                   int64_t chunk, int32_t mode, const ttt_la_desc* desc, void* O, float* W_out,
-                   void* workspace, size_t workspace_bytes, void* stream) {
+int ttt_la_forward_timed(const void* Q, const void* K, const void* V, const float* eta, const float* W0,
+                         int64_t chunk, int32_t mode, const ttt_la_desc* desc, void* O, float* W_out,
+                         void* workspace, size_t workspace_bytes, void* stream, void* ev_start, void* ev_stop) {
   int st = check_problem(desc, chunk, mode);
   if (st != TTT_LA_OK) return st;
   const ttt_la_desc d = *desc;
@@ -139,15 +139,26 @@ int ttt_la_forward(const void* Q, const void* K, const void* V, const float* eta
   if (overlap(rO, rWo) || overlap(rO, rWs) || overlap(rWo, rWs)) return TTT_LA_ERR_ALIAS;
 
   hipStream_t s = (hipStream_t)stream;
+  ttt::Timing tm;
+  tm.start = (hipEvent_t)ev_start;
+  tm.stop = (hipEvent_t)ev_stop;
   hipError_t e = hipSuccess;
   if (mode == TTT_LA_PER_TOKEN_LINEAR) {
     ttt::PerTokenArgs a{Q, K, V, eta, W0, O, W_out, workspace, d.B, d.H, d.T, d.d_k, d.d_v, chunk, d.io_dtype};
-    e = ttt::launch_per_token(a, s);
+    e = ttt::launch_per_token(a, s, tm);
   } else {
     ttt::LargeChunkArgs a{Q, K, V, eta, W0, O, W_out, workspace, d.B, d.H, d.T, d.d_k, d.d_v, d.d_h, chunk, d.io_dtype};
-    e = mode == TTT_LA_LARGE_CHUNK_LINEAR ? ttt::launch_large_chunk_linear(a, s) : ttt::launch_large_chunk_swiglu(a, s);
+    e = mode == TTT_LA_LARGE_CHUNK_LINEAR ? ttt::launch_large_chunk_linear(a, s, tm)
+                                          : ttt::launch_large_chunk_swiglu(a, s, tm);
   }
   return e == hipSuccess ? TTT_LA_OK : TTT_LA_ERR_HIP;
+}
+
+int ttt_la_forward(const void* Q, const void* K, const void* V, const float* eta, const float* W0,
+                   int64_t chunk, int32_t mode, const ttt_la_desc* desc, void* O, float* W_out,
+                   void* workspace, size_t workspace_bytes, void* stream) {
+  return ttt_la_forward_timed(Q, K, V, eta, W0, chunk, mode, desc, O, W_out, workspace, workspace_bytes, stream,
+                              nullptr, nullptr);
 }
 
 }  // extern "C"

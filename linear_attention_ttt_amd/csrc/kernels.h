@@ -7,6 +7,13 @@
 
 namespace ttt {
 
+// Events recorded on the launch stream immediately before and after the
+// dominant kernel of a forward call (either may be null).
+struct Timing {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+inline hipError_t mark(hipEvent_t e, hipStream_t s) { return e ? hipEventRecord(e, s) : hipSuccess; }
+
 struct PerTokenArgs {
   const void* Q;
   const void* K;
@@ -27,7 +34,7 @@ struct SegPlan {
 SegPlan per_token_seg_plan(int64_t BH, int64_t T);
 bool per_token_supported(int64_t dk, int64_t dv, int64_t chunk, int dtype);
 size_t per_token_workspace(int64_t B, int64_t H, int64_t T, int64_t dk, int64_t dv, int dtype);
-hipError_t launch_per_token(const PerTokenArgs& a, hipStream_t stream);
+hipError_t launch_per_token(const PerTokenArgs& a, hipStream_t stream, const Timing& tm);
 
 struct LargeChunkArgs {
   const void* Q;
@@ -44,10 +51,10 @@ struct LargeChunkArgs {
 
 bool large_chunk_linear_supported(int64_t dk, int64_t dv, int64_t chunk, int dtype);
 size_t large_chunk_linear_workspace(int64_t B, int64_t H, int64_t T, int64_t dk, int64_t dv, int64_t chunk);
-hipError_t launch_large_chunk_linear(const LargeChunkArgs& a, hipStream_t stream);
+hipError_t launch_large_chunk_linear(const LargeChunkArgs& a, hipStream_t stream, const Timing& tm);
 
 bool large_chunk_swiglu_supported(int64_t d, int64_t dh, int64_t chunk, int dtype);
 size_t large_chunk_swiglu_workspace(int64_t B, int64_t H, int64_t T, int64_t d, int64_t dh, int64_t chunk);
-hipError_t launch_large_chunk_swiglu(const LargeChunkArgs& a, hipStream_t stream);
+hipError_t launch_large_chunk_swiglu(const LargeChunkArgs& a, hipStream_t stream, const Timing& tm);
 
 }  // namespace ttt

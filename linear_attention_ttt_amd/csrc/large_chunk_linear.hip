@@ -333,7 +333,7 @@ __global__ __launch_bounds__(256, 2) void lact_read_kernel(const bf16* __restric
 }
 
 template <int D>
-hipError_t launch_lact(const LargeChunkArgs& a, hipStream_t stream) {
+hipError_t launch_lact(const LargeChunkArgs& a, hipStream_t stream, const Timing& tm) {
   const int T = (int)a.T, chunk = (int)a.chunk;
   const int nchunks = (int)((a.T + a.chunk - 1) / a.chunk);
   const int nsplit = (int)nsplit_of(a.chunk);
@@ -342,10 +342,12 @@ hipError_t launch_lact(const LargeChunkArgs& a, hipStream_t stream) {
   float* part = (float*)a.ws;
   float* wprev = part + (size_t)BH * nchunks * nsplit * D * D;
   if (nchunks > 0) {
+    hipError_t e = mark(tm.start, stream);   // the update kernel streams K and V: the largest share of the bytes
+    if (e != hipSuccess) return e;
     hipLaunchKernelGGL(lact_delta_kernel<D>, dim3(BH * nchunks * nsplit), dim3(256), 0, stream, (const bf16*)a.K,
                        (const bf16*)a.V, a.eta, part, T, chunk, nchunks, nsplit, slice);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if ((e = mark(tm.stop, stream)) != hipSuccess) return e;
   }
   hipLaunchKernelGGL(lact_scan_kernel<D>, dim3(BH * D / 4), dim3(256), 0, stream, a.W0, part, wprev, a.W_out,
                      nchunks, nsplit);
@@ -376,9 +378,9 @@ size_t large_chunk_linear_workspace(int64_t B, int64_t H, int64_t T, int64_t dk,
   return (size_t)(B * H * nchunks * (nsplit_of(chunk) + 1) * dk * dv * 4);
 }
 
-hipError_t launch_large_chunk_linear(const LargeChunkArgs& a, hipStream_t stream) {
-  if (a.DK == 64) return launch_lact<64>(a, stream);
-  return launch_lact<128>(a, stream);
+hipError_t launch_large_chunk_linear(const LargeChunkArgs& a, hipStream_t stream, const Timing& tm) {
+  if (a.DK == 64) return launch_lact<64>(a, stream, tm);
+  return launch_lact<128>(a, stream, tm);
 }
 
 }  // namespace ttt

@@ -523,7 +523,7 @@ size_t large_chunk_swiglu_workspace(int64_t B, int64_t H, int64_t T, int64_t d, 
   return sw_layout(B * H, (T + chunk - 1) / chunk).total;
 }
 
-hipError_t launch_large_chunk_swiglu(const LargeChunkArgs& a, hipStream_t stream) {
+hipError_t launch_large_chunk_swiglu(const LargeChunkArgs& a, hipStream_t stream, const Timing& tm) {
   const int BH = (int)(a.B * a.H);
   const int T = (int)a.T, chunk = (int)a.chunk;
   const int nchunks = (int)((a.T + a.chunk - 1) / a.chunk);
@@ -556,6 +556,7 @@ hipError_t launch_large_chunk_swiglu(const LargeChunkArgs& a, hipStream_t stream
   const float* Ep = a.eta;
   const float* W0p = a.W0;
   float* Wo = a.W_out;
+  if ((e = mark(tm.start, stream)) != hipSuccess) return e;   // the recurrence: the sequential part
   for (int h0 = 0; h0 < BH; h0 += heads_per_launch) {
     const int nh = std::min(heads_per_launch, BH - h0);
     int Ti = T, ci = chunk, nci = nchunks, hi = h0;
@@ -565,6 +566,7 @@ hipError_t launch_large_chunk_swiglu(const LargeChunkArgs& a, hipStream_t stream
                                    (unsigned)lds_r, stream);
     if (e != hipSuccess) return e;
   }
+  if ((e = mark(tm.stop, stream)) != hipSuccess) return e;
   if (nchunks == 0) return hipSuccess;
   const size_t lds_o = sizeof(ReadLds);
   e = hipFuncSetAttribute((const void*)swiglu_read_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_o);

@@ -554,15 +554,17 @@ static size_t fp32_lds_bytes() {
 // launchers
 // ---------------------------------------------------------------------------
 template <int DK, int C>
-static hipError_t launch_fp32(const PerTokenArgs& a, hipStream_t stream) {
+static hipError_t launch_fp32(const PerTokenArgs& a, hipStream_t stream, const Timing& tm) {
   auto kern = per_token_fp32_kernel<DK, C>;
   const size_t lds = fp32_lds_bytes<DK, C>();
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
   const int grid = (int)(a.B * a.H * (a.DV / 32));
+  if ((e = mark(tm.start, stream)) != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3(grid), dim3(256), lds, stream, (const float*)a.Q, (const float*)a.K,
                      (const float*)a.V, a.eta, a.W0, (float*)a.O, a.W_out, (int)a.T, (int)a.DV);
-  return hipGetLastError();
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  return mark(tm.stop, stream);
 }
 
 bool per_token_supported(int64_t dk, int64_t dv, int64_t chunk, int dtype) {
@@ -590,7 +592,7 @@ size_t per_token_workspace(int64_t B, int64_t H, int64_t T, int64_t dk, int64_t 
 }
 
 template <int D>
-static hipError_t launch_seg(const PerTokenArgs& a, hipStream_t stream) {
+static hipError_t launch_seg(const PerTokenArgs& a, hipStream_t stream, const Timing& tm) {
   using CfgD = SegCfg<D, false>;
   using CfgF = SegCfg<D, true>;
   const int BH = (int)(a.B * a.H);
@@ -618,17 +620,19 @@ static hipError_t launch_seg(const PerTokenArgs& a, hipStream_t stream) {
   if ((e = hipFuncSetAttribute((const void*)kf, hipFuncAttributeMaxDynamicSharedMemorySize, CfgF::LDS_BYTES)) !=
       hipSuccess)
     return e;
+  if ((e = mark(tm.start, stream)) != hipSuccess) return e;
   hipLaunchKernelGGL(kf, dim3(BH * sp.nseg), dim3(CfgF::THREADS), CfgF::LDS_BYTES, stream, A);
-  return hipGetLastError();
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  return mark(tm.stop, stream);
 }
 
-hipError_t launch_per_token(const PerTokenArgs& a, hipStream_t stream) {
+hipError_t launch_per_token(const PerTokenArgs& a, hipStream_t stream, const Timing& tm) {
   if (a.dtype == 0) {
     const int c = a.chunk <= 16 ? 16 : a.chunk <= 32 ? 32 : 64;
-    if (a.DK == 64) return c == 16 ? launch_fp32<64, 16>(a, stream) : c == 32 ? launch_fp32<64, 32>(a, stream) : launch_fp32<64, 64>(a, stream);
-    return c == 16 ? launch_fp32<128, 16>(a, stream) : c == 32 ? launch_fp32<128, 32>(a, stream) : launch_fp32<128, 64>(a, stream);
+    if (a.DK == 64) return c == 16 ? launch_fp32<64, 16>(a, stream, tm) : c == 32 ? launch_fp32<64, 32>(a, stream, tm) : launch_fp32<64, 64>(a, stream, tm);
+    return c == 16 ? launch_fp32<128, 16>(a, stream, tm) : c == 32 ? launch_fp32<128, 32>(a, stream, tm) : launch_fp32<128, 64>(a, stream, tm);
   }
-  return a.DK == 128 ? launch_seg<128>(a, stream) : launch_seg<64>(a, stream);
+  return a.DK == 128 ? launch_seg<128>(a, stream, tm) : launch_seg<64>(a, stream, tm);
 }
 
 }  // namespace ttt
