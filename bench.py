@@ -5,9 +5,10 @@
 
 A step is one ttt_la_forward call over one batch of synthetic inputs that
 are already resident in HBM.  Before every step a 512 MB buffer is
-overwritten so the 256 MB last-level cache and the L2s hold none of the
-inputs; each step is timed with HIP events on the stream the kernels run
-on, and the K steps are bracketed by device synchronisation.  Prints ONE
+overwritten and another 512 MB buffer read, so the 256 MB last-level cache
+and the L2s hold none of the inputs and no dirty lines; each step is timed
+with HIP events on the stream the kernels run on, and the K steps are
+bracketed by device synchronisation.  Prints ONE
 JSON line (the headline workload, plus sub-records for the other
 workloads of the method under "workloads").
 """
@@ -93,7 +94,16 @@ def run_workload(name: str, steps: int, warmup: int, flush_mb: int):
     desc = la.make_desc(B, H, T, s["d_k"], dv, s["d_h"], la.BF16 if dt == torch.bfloat16 else la.FP32)
     nws = la.workspace_bytes(desc, s["chunk"], s["mode"])
     ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
+    # cache eviction before every step, outside the timed region: overwrite one buffer, then read
+    # another, so that the last-level cache and the L2s hold neither the inputs nor dirty lines whose
+    # write-back would otherwise land in the next timed step
     flush = torch.empty(flush_mb << 20, dtype=torch.uint8, device=dev)
+    flush_rd = torch.ones((flush_mb << 20) // 4, dtype=torch.int32, device=dev)
+
+    def evict(v):
+        flush.fill_(v)
+        flush_rd.sum()
+
     stream = torch.cuda.current_stream(dev)
 
     # arguments prepared once: each step is one library call (no Python-side checks inside the timed region)
@@ -114,7 +124,7 @@ def run_workload(name: str, steps: int, warmup: int, flush_mb: int):
     la.forward(t["Q"], t["K"], t["V"], t["eta"], t["W0"], s["chunk"], s["mode"], out=O, W_out=Wout, workspace=ws)
 
     for _ in range(warmup):
-        flush.fill_(1)
+        evict(1)
         step()
     torch.cuda.synchronize()
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
@@ -127,7 +137,7 @@ def run_workload(name: str, steps: int, warmup: int, flush_mb: int):
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     for i in range(steps):
-        flush.fill_(i & 0xFF)
+        evict(i & 0xFF)
         starts[i].record(stream)
         step(timing=(kstarts[i], kends[i]))
         ends[i].record(stream)
@@ -150,7 +160,7 @@ def run_workload(name: str, steps: int, warmup: int, flush_mb: int):
                            units_per_launch=kunits,
                            achieved=kunits / kmean_s / (1e9 if kbound == "hbm" else 1e12),
                            unit="GB/s" if kbound == "hbm" else "TFLOP/s"))
-    del t, O, Wout, ws, flush
+    del t, O, Wout, ws, flush, flush_rd
     torch.cuda.empty_cache()
     return rec
 

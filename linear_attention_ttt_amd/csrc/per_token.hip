@@ -12,9 +12,11 @@
 //
 // bf16 design (gfx950): the sequence of each head is cut into P segments of
 // whole 64-token tiles so that heads x segments cover the compute units.
-//  1. pt_seg_kernel<D, false>: for every segment but the last, its state
-//     increment dS_s = K_s^T diag(eta_s) V_s (fp32) into the workspace;
-//  2. pt_seg_kernel<D, true>: segment s starts from
+//  1. pt_incr_kernel<D>: for every segment but the last, its state
+//     increment dS_s = K_s^T diag(eta_s) V_s (fp32) into the workspace
+//     (pt_seg_scan_kernel<D> turns them into start states when there are
+//     many segments);
+//  2. pt_seg_kernel<D>: segment s starts from
 //     S = W0 + sum_{s' < s} dS_s' and runs the chunked form over its tiles;
 //     the last segment writes W_out.
 // A workgroup has D/16 waves; wave w owns columns 16w..16w+15 of S and O for
@@ -49,7 +51,7 @@ __host__ __device__ constexpr int tile_begin8(int w) { return w <= 3 ? 2 * w : w
 template <int NW>
 __host__ __device__ constexpr int tile_begin(int w) { return NW == 4 ? tile_begin4(w) : tile_begin8(w); }
 
-template <int D, bool FULL>
+template <int D>
 struct SegCfg {
   static constexpr int C = 64;                   // tokens per tile
   static constexpr int NW = D / 16;              // waves; wave w owns columns 16w..16w+15
@@ -58,19 +60,18 @@ struct SegCfg {
   static constexpr int KP = D / 32;              // 32-deep contraction steps over d
   static constexpr int ROWB = D * 2;             // bytes per token row of Q, K, V, O
   static constexpr int MAT = C * ROWB;           // one matrix of a tile
-  // ring slot: [Q (FULL only; reused for the tile's outputs)] K V eta
-  static constexpr int NMAT = FULL ? 3 : 2;
-  static constexpr int STAGES = FULL ? 3 : 4;
-  static constexpr int OFF_K = FULL ? MAT : 0;
+  // ring slot: Q (reused for the tile's outputs), K, V, eta
+  static constexpr int STAGES = 3;
+  static constexpr int OFF_K = MAT;
   static constexpr int OFF_V = OFF_K + MAT;
   static constexpr int OFF_E = OFF_V + MAT;
-  static constexpr int STAGE = NMAT * MAT + C * 4;
+  static constexpr int STAGE = 3 * MAT + C * 4;
   static constexpr int OFF_P = STAGES * STAGE;   // score tiles [hi, lo][10][64 lanes x 8 bytes]
   static constexpr int P_PLANE = 10 * 512;
-  static constexpr int LDS_BYTES = OFF_P + (FULL ? 2 * P_PLANE : 0);
+  static constexpr int LDS_BYTES = OFF_P + 2 * P_PLANE;
   static constexpr int EPW = C / NW;             // eta values loaded by each wave
   static constexpr int MAT_LOADS = MAT / 1024 / NW;  // 16-byte direct-to-LDS loads per wave per matrix
-  static constexpr int LOADS = NMAT * MAT_LOADS + 1;
+  static constexpr int LOADS = 3 * MAT_LOADS + 1;
   static constexpr int OUT_STORES = MAT_LOADS;   // 16-byte output stores per wave per tile
   static_assert(MAT % (1024 * NW) == 0, "tile matrix must split into whole wave loads");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
@@ -143,10 +144,10 @@ struct SegArgs {
 
 // The program of wave W (wave-uniform).  One program for all waves keeps the
 // code within the instruction cache.
-template <int D, bool FULL>
+template <int D>
 __device__ __forceinline__ void seg_wave(const SegArgs& A, unsigned char* smem, int bh, int s, int W, int l) {
-  using Cfg = SegCfg<D, FULL>;
-  constexpr int C = Cfg::C, ROWB = Cfg::ROWB, MT = Cfg::MT, KP = Cfg::KP, NW = Cfg::NW, MAT = Cfg::MAT;
+  using Cfg = SegCfg<D>;
+  constexpr int C = Cfg::C, ROWB = Cfg::ROWB, MT = Cfg::MT, KP = Cfg::KP, NW = Cfg::NW;
   constexpr int LOADS = Cfg::LOADS;
   const int g = l >> 4, li = l & 15;
   const int T = A.T, nseg = A.nseg;
@@ -190,11 +191,10 @@ __device__ __forceinline__ void seg_wave(const SegArgs& A, unsigned char* smem, 
     const long long t0 = (long long)(c0 + i) * C;
     const long long rem = seg_end - t0;
     unsigned char* st = smem + (i % Cfg::STAGES) * Cfg::STAGE + W * Cfg::MAT_LOADS * 1024;
-    if constexpr (FULL) {
-      const __amdgpu_buffer_rsrc_t rq = make_rsrc(Qh + (rem > 0 ? t0 * D : 0), rem * ROWB);
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(Qh + (rem > 0 ? t0 * D : 0), rem * ROWB);
 #pragma unroll
-      for (int k = 0; k < Cfg::MAT_LOADS; ++k) dma16(rq, gofs[k], st + k * 1024);
-    }
+    for (int k = 0; k < Cfg::MAT_LOADS; ++k) dma16(rq, gofs[k], st + k * 1024);
+
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kh + (rem > 0 ? t0 * D : 0), rem * ROWB);
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vh + (rem > 0 ? t0 * D : 0), rem * ROWB);
 #pragma unroll
@@ -219,70 +219,62 @@ __device__ __forceinline__ void seg_wave(const SegArgs& A, unsigned char* smem, 
 
   // ---- state: S[m][r] = S[16m + 4g + r][16W + li] ----
   floatx4 S[MT];
-  if constexpr (FULL) {
-    const floatx4* pp = A.part + ((size_t)bh * nseg * NW + W) * MT * 64 + l;   // slot 0 of this head
-    constexpr int SLOT = NW * MT * 64;                                         // floatx4 per slot
-    if (A.scanned) {
-      // start state of this segment, prepared by pt_seg_scan_kernel in the same fragment layout
+  const floatx4* pp = A.part + ((size_t)bh * nseg * NW + W) * MT * 64 + l;   // slot 0 of this head
+  constexpr int SLOT = NW * MT * 64;                                         // floatx4 per slot
+  if (A.scanned) {
+    // start state of this segment, prepared by pt_seg_scan_kernel in the same fragment layout
 #pragma unroll
-      for (int m = 0; m < MT; ++m) S[m] = pp[(size_t)s * SLOT + m * 64];
-    } else {
-      // W0 [D][D] fp32 -> LDS with coalesced 16-byte copies (the ring is still empty), then this lane's
-      // fragment; the increments of earlier segments are added, 4 segments per memory round trip
-      const float* W0h = A.W0 + (size_t)bh * D * D;
-      const __amdgpu_buffer_rsrc_t rw = make_rsrc(W0h, (long long)D * D * 4);
-#pragma unroll
-      for (int k = 0; k < D * D * 4 / 1024 / NW; ++k) {
-        const unsigned b = (unsigned)((W * (D * D * 4 / 1024 / NW) + k) * 1024);
-        dma16(rw, b + 16 * l, smem + b);
-      }
-      floatx4 d[4][MT];             // increments of segments s0..s0+3 (clamped; only those < s are added)
-      auto load_incr = [&](int s0) {
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const int sp = min(s0 + k, max(s - 1, 0));
-#pragma unroll
-          for (int m = 0; m < MT; ++m) d[k][m] = pp[(size_t)sp * SLOT + m * 64];
-        }
-      };
-      if (s > 0) load_incr(0);      // in flight together with the W0 copy
-      wait_vm_barrier<0>();
-      const float* wl = (const float*)smem;
-#pragma unroll
-      for (int m = 0; m < MT; ++m)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) S[m][r] = wl[(16 * m + 4 * g + r) * D + 16 * W + li];
-      for (int s0 = 0; s0 < s; s0 += 4) {
-        if (s0 > 0) load_incr(s0);
-#pragma unroll
-        for (int k = 0; k < 4; ++k)
-          if (s0 + k < s)
-#pragma unroll
-            for (int m = 0; m < MT; ++m) S[m] += d[k][m];
-      }
-      barrier();                    // everyone has read W0 before the ring overwrites it
-    }
+    for (int m = 0; m < MT; ++m) S[m] = pp[(size_t)s * SLOT + m * 64];
   } else {
+    // W0 [D][D] fp32 -> LDS with coalesced 16-byte copies (the ring is still empty), then this lane's
+    // fragment; the increments of earlier segments are added, 4 segments per memory round trip
+    const float* W0h = A.W0 + (size_t)bh * D * D;
+    const __amdgpu_buffer_rsrc_t rw = make_rsrc(W0h, (long long)D * D * 4);
 #pragma unroll
-    for (int m = 0; m < MT; ++m) S[m] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int k = 0; k < D * D * 4 / 1024 / NW; ++k) {
+      const unsigned b = (unsigned)((W * (D * D * 4 / 1024 / NW) + k) * 1024);
+      dma16(rw, b + 16 * l, smem + b);
+    }
+    floatx4 d[4][MT];             // increments of segments s0..s0+3 (clamped; only those < s are added)
+    auto load_incr = [&](int s0) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int sp = min(s0 + k, max(s - 1, 0));
+#pragma unroll
+        for (int m = 0; m < MT; ++m) d[k][m] = pp[(size_t)sp * SLOT + m * 64];
+      }
+    };
+    if (s > 0) load_incr(0);      // in flight together with the W0 copy
+    wait_vm_barrier<0>();
+    const float* wl = (const float*)smem;
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) S[m][r] = wl[(16 * m + 4 * g + r) * D + 16 * W + li];
+    for (int s0 = 0; s0 < s; s0 += 4) {
+      if (s0 > 0) load_incr(s0);
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        if (s0 + k < s)
+#pragma unroll
+          for (int m = 0; m < MT; ++m) S[m] += d[k][m];
+    }
+    barrier();                    // everyone has read W0 before the ring overwrites it
   }
+
 
 #pragma unroll
   for (int k = 0; k < Cfg::STAGES - 1; ++k)
     if (nt > 0) issue(k);
   for (int i = 0; i < nt; ++i) {
     // tile i has landed once only later-issued loads (and output stores) may be outstanding
-    if constexpr (FULL) {
-      if (i < 2)
-        wait_vm_barrier<LOADS>();
-      else
-        wait_vm_barrier<LOADS + Cfg::OUT_STORES>();
-      if (i >= 1) {
-        write_out(i - 1);           // from the slot the next load overwrites: read it first
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-      }
-    } else {
-      wait_vm_barrier<(Cfg::STAGES - 2) * LOADS>();
+    if (i < 2)
+      wait_vm_barrier<LOADS>();
+    else
+      wait_vm_barrier<LOADS + Cfg::OUT_STORES>();
+    if (i >= 1) {
+      write_out(i - 1);           // from the slot the next load overwrites: read it first
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     }
     issue(i + Cfg::STAGES - 1);     // into the slot read during tile i-1
     const unsigned char* st = smem + (i % Cfg::STAGES) * Cfg::STAGE;
@@ -290,151 +282,245 @@ __device__ __forceinline__ void seg_wave(const SegArgs& A, unsigned char* smem, 
     const unsigned char* vs = st + Cfg::OFF_V;
     const float* es = (const float*)(st + Cfg::OFF_E);
 
-    if constexpr (FULL) {
-      const unsigned char* qs = st;
-      unsigned char* pb = smem + Cfg::OFF_P;
-      floatx4 acc[4];
-      bf16x4 vt[4];                 // vt[kb][j] = V[16kb + 4g + j][16W + li]
-      SegUpdate<Cfg> U;
-      // Q operand of block ib, step p (k order of the S accumulators)
-      auto qop = [&](int p, int ib) {
-        const unsigned char* qrow = qs + ib * 16 * ROWB;
-        return join(*(const bf16x4*)(qrow + ksb[p][0]), *(const bf16x4*)(qrow + ksb[p][1]));
-      };
-      // this wave's score tiles P^T(jb, ib) = K_jb Q_ib^T, scaled by eta of the key, masked, bf16 hi + lo
-      auto scores = [&]() {
-        const int tb = tile_begin<NW>(W), te = tile_begin<NW>(W + 1);
+    const unsigned char* qs = st;
+    unsigned char* pb = smem + Cfg::OFF_P;
+    floatx4 acc[4];
+    bf16x4 vt[4];                 // vt[kb][j] = V[16kb + 4g + j][16W + li]
+    SegUpdate<Cfg> U;
+    // Q operand of block ib, step p (k order of the S accumulators)
+    auto qop = [&](int p, int ib) {
+      const unsigned char* qrow = qs + ib * 16 * ROWB;
+      return join(*(const bf16x4*)(qrow + ksb[p][0]), *(const bf16x4*)(qrow + ksb[p][1]));
+    };
+    // this wave's score tiles P^T(jb, ib) = K_jb Q_ib^T, scaled by eta of the key, masked, bf16 hi + lo
+    auto scores = [&]() {
+      const int tb = tile_begin<NW>(W), te = tile_begin<NW>(W + 1);
 #pragma unroll
-        for (int t = 0; t < 10; ++t) {
-          if (t < tb || t >= te) continue;    // wave-uniform
-          const int jb = ptile_jb(t), ib = ptile_ib(t);
-          floatx4 p = {0.f, 0.f, 0.f, 0.f};
-          const unsigned char* krow = ks + jb * 16 * ROWB;
+      for (int t = 0; t < 10; ++t) {
+        if (t < tb || t >= te) continue;    // wave-uniform
+        const int jb = ptile_jb(t), ib = ptile_ib(t);
+        floatx4 p = {0.f, 0.f, 0.f, 0.f};
+        const unsigned char* krow = ks + jb * 16 * ROWB;
 #pragma unroll
-          for (int kk = 0; kk < KP; ++kk) {
-            const bf16x8 ka = join(*(const bf16x4*)(krow + ksb[kk][0]), *(const bf16x4*)(krow + ksb[kk][1]));
-            p = mfma16(ka, qop(kk, ib), p);
-          }
-          const floatx4 e4 = *(const floatx4*)(es + 16 * jb + 4 * g);
-          floatx4 f;
-#pragma unroll
-          for (int r = 0; r < 4; ++r) f[r] = (jb == ib && 4 * g + r > li) ? 0.f : p[r] * e4[r];
-          const uint2 s01 = split2(f[0], f[1]), s23 = split2(f[2], f[3]);
-          *(uint2*)(pb + t * 512 + l * 8) = uint2{s01.x, s23.x};
-          *(uint2*)(pb + Cfg::P_PLANE + t * 512 + l * 8) = uint2{s01.y, s23.y};
+        for (int kk = 0; kk < KP; ++kk) {
+          const bf16x8 ka = join(*(const bf16x4*)(krow + ksb[kk][0]), *(const bf16x4*)(krow + ksb[kk][1]));
+          p = mfma16(ka, qop(kk, ib), p);
         }
-      };
-      // O_W^T = S_W^T Q^T with S_W as bf16 hi + lo
-      auto qs_mfma = [&]() {
+        const floatx4 e4 = *(const floatx4*)(es + 16 * jb + 4 * g);
+        floatx4 f;
 #pragma unroll
-        for (int ib = 0; ib < 4; ++ib) acc[ib] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int p = 0; p < KP; ++p) {
-          bf16x8 ah, al, qv[4];
-#pragma unroll
-          for (int ib = 0; ib < 4; ++ib) qv[ib] = qop(p, ib);
-          split8(S[2 * p], S[2 * p + 1], ah, al);
-#pragma unroll
-          for (int ib = 0; ib < 4; ++ib) acc[ib] = mfma16(ah, qv[ib], acc[ib]);
-#pragma unroll
-          for (int ib = 0; ib < 4; ++ib) acc[ib] = mfma16(al, qv[ib], acc[ib]);
-          __builtin_amdgcn_sched_barrier(0);   // keep each step's Q loads next to their use (register pressure)
-        }
-      };
-      // operands of phase 2 that do not depend on the score tiles
-      bf16x8 ka0[MT];               // transposed K operands of the first key half
-      auto load_update = [&]() {
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) vt[kb] = lds_read_tr16(vs + kb * 16 * ROWB + vtr);
-        seg_update_eta<Cfg>(U, es, vt, g);
-        seg_update_k<Cfg>(ka0, ks, ktr, 0);
-      };
-      // The two waves of a SIMD take phase 1 in opposite orders so that one
-      // issues MFMAs while the other reads LDS.
-      scores();
-      if (W < NW / 2) {
-        qs_mfma();
-        load_update();
-      } else {
-        load_update();
-        qs_mfma();
+        for (int r = 0; r < 4; ++r) f[r] = (jb == ib && 4 * g + r > li) ? 0.f : p[r] * e4[r];
+        const uint2 s01 = split2(f[0], f[1]), s23 = split2(f[2], f[3]);
+        *(uint2*)(pb + t * 512 + l * 8) = uint2{s01.x, s23.x};
+        *(uint2*)(pb + Cfg::P_PLANE + t * 512 + l * 8) = uint2{s01.y, s23.y};
       }
-      barrier();                    // score tiles visible; everyone is done reading Q of this tile
-
-      // ---- phase 2a: O_W^T += V_W^T A^T over key blocks 0..ib ----
+    };
+    // O_W^T = S_W^T Q^T with S_W as bf16 hi + lo
+    auto qs_mfma = [&]() {
 #pragma unroll
-      for (int ib = 0; ib < 4; ++ib)
+      for (int ib = 0; ib < 4; ++ib) acc[ib] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kc = 0; 2 * kc <= ib; ++kc) {
-          const int t0i = ptile_index(2 * kc, ib);
-          bf16x4 h1 = bf16x4{(bf16)0.f, (bf16)0.f, (bf16)0.f, (bf16)0.f}, l1 = h1;
-          if (2 * kc + 1 <= ib) {
-            const int t1i = ptile_index(2 * kc + 1, ib);
-            h1 = *(const bf16x4*)(pb + t1i * 512 + l * 8);
-            l1 = *(const bf16x4*)(pb + Cfg::P_PLANE + t1i * 512 + l * 8);
-          }
-          const bf16x8 bh_ = join(*(const bf16x4*)(pb + t0i * 512 + l * 8), h1);
-          const bf16x8 bl_ = join(*(const bf16x4*)(pb + Cfg::P_PLANE + t0i * 512 + l * 8), l1);
-          const bf16x8 av = join(vt[2 * kc], vt[2 * kc + 1]);
-          acc[ib] = mfma16(av, bh_, acc[ib]);
-          acc[ib] = mfma16(av, bl_, acc[ib]);
-        }
-      // outputs into the Q region of this slot (written out after the next barrier)
-      unsigned char* ob = smem + (i % Cfg::STAGES) * Cfg::STAGE;
+      for (int p = 0; p < KP; ++p) {
+        bf16x8 ah, al, qv[4];
 #pragma unroll
-      for (int ib = 0; ib < 4; ++ib)
-        *(bf16x4*)(ob + ib * 16 * ROWB + ofr) = to_bf16x4(acc[ib][0], acc[ib][1], acc[ib][2], acc[ib][3]);
-      bf16x8 ka1[MT];
-      seg_update_k<Cfg>(ka1, ks, ktr, 1);
-      seg_update_mfma<Cfg>(S, ka0, U, 0);
-      seg_update_mfma<Cfg>(S, ka1, U, 1);
-    } else {
-      bf16x4 vt[4];
+        for (int ib = 0; ib < 4; ++ib) qv[ib] = qop(p, ib);
+        split8(S[2 * p], S[2 * p + 1], ah, al);
+#pragma unroll
+        for (int ib = 0; ib < 4; ++ib) acc[ib] = mfma16(ah, qv[ib], acc[ib]);
+#pragma unroll
+        for (int ib = 0; ib < 4; ++ib) acc[ib] = mfma16(al, qv[ib], acc[ib]);
+        __builtin_amdgcn_sched_barrier(0);   // keep each step's Q loads next to their use (register pressure)
+      }
+    };
+    // operands of phase 2 that do not depend on the score tiles
+    bf16x8 ka0[MT];               // transposed K operands of the first key half
+    auto load_update = [&]() {
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) vt[kb] = lds_read_tr16(vs + kb * 16 * ROWB + vtr);
-      SegUpdate<Cfg> U;
       seg_update_eta<Cfg>(U, es, vt, g);
-      bf16x8 ka[MT];
-#pragma unroll
-      for (int kc = 0; kc < 2; ++kc) {
-        seg_update_k<Cfg>(ka, ks, ktr, kc);
-        seg_update_mfma<Cfg>(S, ka, U, kc);
-      }
+      seg_update_k<Cfg>(ka0, ks, ktr, 0);
+    };
+    // The two waves of a SIMD take phase 1 in opposite orders so that one
+    // issues MFMAs while the other reads LDS.
+    scores();
+    if (W < NW / 2) {
+      qs_mfma();
+      load_update();
+    } else {
+      load_update();
+      qs_mfma();
     }
+    barrier();                    // score tiles visible; everyone is done reading Q of this tile
+
+    // ---- phase 2a: O_W^T += V_W^T A^T over key blocks 0..ib ----
+#pragma unroll
+    for (int ib = 0; ib < 4; ++ib)
+#pragma unroll
+      for (int kc = 0; 2 * kc <= ib; ++kc) {
+        const int t0i = ptile_index(2 * kc, ib);
+        bf16x4 h1 = bf16x4{(bf16)0.f, (bf16)0.f, (bf16)0.f, (bf16)0.f}, l1 = h1;
+        if (2 * kc + 1 <= ib) {
+          const int t1i = ptile_index(2 * kc + 1, ib);
+          h1 = *(const bf16x4*)(pb + t1i * 512 + l * 8);
+          l1 = *(const bf16x4*)(pb + Cfg::P_PLANE + t1i * 512 + l * 8);
+        }
+        const bf16x8 bh_ = join(*(const bf16x4*)(pb + t0i * 512 + l * 8), h1);
+        const bf16x8 bl_ = join(*(const bf16x4*)(pb + Cfg::P_PLANE + t0i * 512 + l * 8), l1);
+        const bf16x8 av = join(vt[2 * kc], vt[2 * kc + 1]);
+        acc[ib] = mfma16(av, bh_, acc[ib]);
+        acc[ib] = mfma16(av, bl_, acc[ib]);
+      }
+    // outputs into the Q region of this slot (written out after the next barrier)
+    unsigned char* ob = smem + (i % Cfg::STAGES) * Cfg::STAGE;
+#pragma unroll
+    for (int ib = 0; ib < 4; ++ib)
+      *(bf16x4*)(ob + ib * 16 * ROWB + ofr) = to_bf16x4(acc[ib][0], acc[ib][1], acc[ib][2], acc[ib][3]);
+    bf16x8 ka1[MT];
+    seg_update_k<Cfg>(ka1, ks, ktr, 1);
+    seg_update_mfma<Cfg>(S, ka0, U, 0);
+    seg_update_mfma<Cfg>(S, ka1, U, 1);
+
   }
-  if constexpr (FULL) {
-    if (nt > 0) {
-      wait_vm_barrier<0>();
-      write_out(nt - 1);
+  if (nt > 0) {
+    wait_vm_barrier<0>();
+    write_out(nt - 1);
+  }
+
+  wait_vm<0>();
+
+  if (s == nseg - 1) {
+    float* Wh = A.Wout + (size_t)bh * D * D;
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) Wh[(size_t)(16 * m + 4 * g + r) * D + 16 * W + li] = S[m][r];
+  }
+
+}
+
+// Outputs of segment s of head bh (grid BH x nseg), starting from W0 plus
+// the increments of the earlier segments of the head.
+template <int D>
+__global__ __launch_bounds__(D / 16 * WAVE, 1) void pt_seg_kernel(SegArgs A) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  const int bh = blockIdx.x / A.nseg, s = blockIdx.x % A.nseg;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  seg_wave<D>(A, smem, bh, s, w, threadIdx.x & 63);
+}
+
+// Segment increments dS_s = K_s^T diag(eta_s) V_s for every segment but the
+// last of each head (grid BH x (nseg - 1)), in the fragment layout the
+// output pass reads.  2*D/16 waves, 4 per SIMD: wave w owns column tile
+// c = w % (D/16) for half h = w / (D/16) of the rows, so each wave carries
+// half the accumulators of the output pass and twice as many waves hide the
+// latency.  K, V and eta stream through a 4-stage direct-to-LDS ring.
+template <int D>
+struct IncrCfg {
+  static constexpr int C = 64;
+  static constexpr int NC = D / 16;              // column tiles
+  static constexpr int NW = 2 * NC;              // waves
+  static constexpr int THREADS = NW * WAVE;
+  static constexpr int MT = D / 16;              // row tiles of a column tile
+  static constexpr int MH = MT / 2;              // row tiles per wave
+  static constexpr int ROWB = D * 2;
+  static constexpr int MAT = C * ROWB;
+  static constexpr int STAGES = 4;
+  static constexpr int STAGE = 2 * MAT + C * 4;  // K, V, eta
+  static constexpr int LDS_BYTES = STAGES * STAGE;
+  static constexpr int MAT_LOADS = MAT / 1024 / NW;
+  static constexpr int EPW = C / NW;
+  static constexpr int LOADS = 2 * MAT_LOADS + 1;
+  static_assert(MAT % (1024 * NW) == 0, "tile matrix must split into whole wave loads");
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+};
+
+template <int D>
+__global__ __launch_bounds__(2 * D / 16 * WAVE, 1) void pt_incr_kernel(SegArgs A) {
+  using Cfg = IncrCfg<D>;
+  constexpr int C = Cfg::C, ROWB = Cfg::ROWB, MT = Cfg::MT, MH = Cfg::MH, NC = Cfg::NC, MAT = Cfg::MAT;
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  const int nseg = A.nseg, T = A.T;
+  const int bh = blockIdx.x / (nseg - 1), s = blockIdx.x % (nseg - 1);
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int l = threadIdx.x & 63, g = l >> 4, li = l & 15;
+  const int c = w % NC, h = w / NC;
+  const int nchunks = (int)(((long long)T + C - 1) / C);
+  const int c0 = s * A.seg_tiles, c1 = min(c0 + A.seg_tiles, nchunks);
+  const int nt = c1 > c0 ? c1 - c0 : 0;
+  const long long seg_end = min((long long)c1 * C, (long long)T);
+  const bf16* Kh = A.K + (size_t)bh * T * D;
+  const bf16* Vh = A.V + (size_t)bh * T * D;
+  const float* Eh = A.eta + (size_t)bh * T;
+
+  unsigned gofs[Cfg::MAT_LOADS];
+#pragma unroll
+  for (int k = 0; k < Cfg::MAT_LOADS; ++k) {
+    const int b = (w * Cfg::MAT_LOADS + k) * 1024 + 16 * l;
+    const int row = b / ROWB, ph = (b % ROWB) >> 4;
+    gofs[k] = (unsigned)(row * ROWB + ((ph ^ seg_swz<D>(row)) << 4));
+  }
+  const int trow = 4 * g + (li >> 2);
+  unsigned ktr[MH];
+#pragma unroll
+  for (int j = 0; j < MH; ++j) {
+    const int m = h * MH + j;
+    ktr[j] = (unsigned)(trow * ROWB + (((2 * m + ((li >> 1) & 1)) ^ seg_swz<D>(trow)) << 4) + (li & 1) * 8);
+  }
+  const unsigned vtr = (unsigned)(trow * ROWB + (((2 * c + ((li >> 1) & 1)) ^ seg_swz<D>(trow)) << 4) + (li & 1) * 8);
+
+  auto issue = [&](int i) {
+    const long long t0 = (long long)(c0 + i) * C;
+    const long long rem = seg_end - t0;
+    unsigned char* st = smem + (i % Cfg::STAGES) * Cfg::STAGE;
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kh + (rem > 0 ? t0 * D : 0), rem * ROWB);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vh + (rem > 0 ? t0 * D : 0), rem * ROWB);
+#pragma unroll
+    for (int k = 0; k < Cfg::MAT_LOADS; ++k) dma16(rk, gofs[k], st + (w * Cfg::MAT_LOADS + k) * 1024);
+#pragma unroll
+    for (int k = 0; k < Cfg::MAT_LOADS; ++k) dma16(rv, gofs[k], st + MAT + (w * Cfg::MAT_LOADS + k) * 1024);
+    const __amdgpu_buffer_rsrc_t re = make_rsrc(Eh + (rem > 0 ? t0 : 0), rem * 4);
+    if (l < Cfg::EPW) dma4(re, (unsigned)((w * Cfg::EPW + l) * 4), st + 2 * MAT + w * Cfg::EPW * 4);
+  };
+
+  floatx4 S[MH];
+#pragma unroll
+  for (int j = 0; j < MH; ++j) S[j] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int k = 0; k < Cfg::STAGES - 1; ++k)
+    if (nt > 0) issue(k);
+  for (int i = 0; i < nt; ++i) {
+    wait_vm_barrier<(Cfg::STAGES - 2) * Cfg::LOADS>();   // tile i landed; slot of tile i-1 free
+    issue(i + Cfg::STAGES - 1);
+    const unsigned char* st = smem + (i % Cfg::STAGES) * Cfg::STAGE;
+    const unsigned char* ks = st;
+    const unsigned char* vs = st + MAT;
+    const float* es = (const float*)(st + 2 * MAT);
+    bf16x4 vt[4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) vt[kb] = lds_read_tr16(vs + kb * 16 * ROWB + vtr);
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc) {
+      const floatx4 e0 = *(const floatx4*)(es + 32 * kc + 4 * g);
+      const floatx4 e1 = *(const floatx4*)(es + 32 * kc + 16 + 4 * g);
+      const uint2 v0 = __builtin_bit_cast(uint2, vt[2 * kc]), v1 = __builtin_bit_cast(uint2, vt[2 * kc + 1]);
+      bf16x8 evh, evl;
+      split8(floatx4{e0[0] * bf16lo_f(v0.x), e0[1] * bf16hi_f(v0.x), e0[2] * bf16lo_f(v0.y), e0[3] * bf16hi_f(v0.y)},
+             floatx4{e1[0] * bf16lo_f(v1.x), e1[1] * bf16hi_f(v1.x), e1[2] * bf16lo_f(v1.y), e1[3] * bf16hi_f(v1.y)},
+             evh, evl);
+      bf16x8 a[MH];
+#pragma unroll
+      for (int j = 0; j < MH; ++j)
+        a[j] = join(lds_read_tr16(ks + (2 * kc) * 16 * ROWB + ktr[j]), lds_read_tr16(ks + (2 * kc + 1) * 16 * ROWB + ktr[j]));
+#pragma unroll
+      for (int j = 0; j < MH; ++j) S[j] = mfma16(a[j], evh, S[j]);
+#pragma unroll
+      for (int j = 0; j < MH; ++j) S[j] = mfma16(a[j], evl, S[j]);
     }
   }
   wait_vm<0>();
-
-  if constexpr (FULL) {
-    if (s == nseg - 1) {
-      float* Wh = A.Wout + (size_t)bh * D * D;
+  floatx4* pp = A.part + (((size_t)bh * nseg + s) * NC + c) * MT * 64 + l;
 #pragma unroll
-      for (int m = 0; m < MT; ++m)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) Wh[(size_t)(16 * m + 4 * g + r) * D + 16 * W + li] = S[m][r];
-    }
-  } else {
-    floatx4* pp = A.part + (((size_t)bh * nseg + s) * NW + W) * MT * 64 + l;
-#pragma unroll
-    for (int m = 0; m < MT; ++m) pp[m * 64] = S[m];
-  }
-}
-
-// FULL = false: dS of segment s (grid BH x (nseg - 1)) -> part.
-// FULL = true : outputs of segment s (grid BH x nseg); starts from W0 plus
-//               the increments of the earlier segments of the head.
-template <int D, bool FULL>
-__global__ __launch_bounds__(D / 16 * WAVE, 1) void pt_seg_kernel(SegArgs A) {
-  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  const int segs_here = FULL ? A.nseg : A.nseg - 1;
-  const int bh = blockIdx.x / segs_here, s = blockIdx.x % segs_here;
-  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  seg_wave<D, FULL>(A, smem, bh, s, w, threadIdx.x & 63);
+  for (int j = 0; j < MH; ++j) pp[(h * MH + j) * 64] = S[j];
 }
 
 // Start states of the segments of one head, in place: slot s holds dS_s
@@ -593,8 +679,8 @@ size_t per_token_workspace(int64_t B, int64_t H, int64_t T, int64_t dk, int64_t 
 
 template <int D>
 static hipError_t launch_seg(const PerTokenArgs& a, hipStream_t stream, const Timing& tm) {
-  using CfgD = SegCfg<D, false>;
-  using CfgF = SegCfg<D, true>;
+  using CfgD = IncrCfg<D>;
+  using CfgF = SegCfg<D>;
   const int BH = (int)(a.B * a.H);
   const SegPlan sp = per_token_seg_plan(BH, a.T);
   // With few segments every workgroup adds the earlier increments itself (one or two memory round
@@ -604,7 +690,7 @@ static hipError_t launch_seg(const PerTokenArgs& a, hipStream_t stream, const Ti
             (bf16*)a.O, a.W_out, (int)a.T, sp.nseg, sp.tiles, sp.nseg > 8 ? 1 : 0};
   hipError_t e;
   if (sp.nseg > 1) {
-    auto kd = pt_seg_kernel<D, false>;
+    auto kd = pt_incr_kernel<D>;
     if ((e = hipFuncSetAttribute((const void*)kd, hipFuncAttributeMaxDynamicSharedMemorySize, CfgD::LDS_BYTES)) !=
         hipSuccess)
       return e;
@@ -616,7 +702,7 @@ static hipError_t launch_seg(const PerTokenArgs& a, hipStream_t stream, const Ti
       if ((e = hipGetLastError()) != hipSuccess) return e;
     }
   }
-  auto kf = pt_seg_kernel<D, true>;
+  auto kf = pt_seg_kernel<D>;
   if ((e = hipFuncSetAttribute((const void*)kf, hipFuncAttributeMaxDynamicSharedMemorySize, CfgF::LDS_BYTES)) !=
       hipSuccess)
     return e;
