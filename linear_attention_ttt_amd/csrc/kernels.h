@@ -27,11 +27,11 @@ struct PerTokenArgs {
   int dtype;  // 0 = fp32, 1 = bf16
 };
 
-// Sequence segments of the bf16 per-token path (segments per head, 64-token tiles per segment).
+// Sequence segments of the bf16 per-token path (segments per head, tokens per segment).
 struct SegPlan {
-  int nseg, tiles;
+  int nseg, seg_len;
 };
-SegPlan per_token_seg_plan(int64_t BH, int64_t T);
+SegPlan per_token_seg_plan(int64_t BH, int64_t T, int64_t dk);
 bool per_token_supported(int64_t dk, int64_t dv, int64_t chunk, int dtype);
 size_t per_token_workspace(int64_t B, int64_t H, int64_t T, int64_t dk, int64_t dv, int dtype);
 hipError_t launch_per_token(const PerTokenArgs& a, hipStream_t stream, const Timing& tm);

@@ -51,9 +51,19 @@ __host__ __device__ constexpr int tile_begin8(int w) { return w <= 3 ? 2 * w : w
 template <int NW>
 __host__ __device__ constexpr int tile_begin(int w) { return NW == 4 ? tile_begin4(w) : tile_begin8(w); }
 
+// Tile length of the output pass.  The wave program also supports 32-token
+// tiles, whose workgroups take under half a CU's LDS (two workgroups, 4 waves
+// per SIMD, per CU); at d = 128 that measured slower overall on gfx950 (the
+// per-token split and barrier costs double and more segments are needed).
 template <int D>
+__host__ __device__ constexpr int seg_tile() { return 64; }
+
+template <int D, int CT>
 struct SegCfg {
-  static constexpr int C = 64;                   // tokens per tile
+  static constexpr int C = CT;                   // tokens per tile
+  static constexpr int NB = C / 16;              // 16-token blocks per tile
+  static constexpr int NT = NB * (NB + 1) / 2;   // causal score tiles per tile
+  static constexpr int KC = C / 32;              // 32-key halves of the state update
   static constexpr int NW = D / 16;              // waves; wave w owns columns 16w..16w+15
   static constexpr int THREADS = NW * WAVE;
   static constexpr int MT = D / 16;              // 16-row tiles of S per wave
@@ -66,42 +76,68 @@ struct SegCfg {
   static constexpr int OFF_V = OFF_K + MAT;
   static constexpr int OFF_E = OFF_V + MAT;
   static constexpr int STAGE = 3 * MAT + C * 4;
-  static constexpr int OFF_P = STAGES * STAGE;   // score tiles [hi, lo][10][64 lanes x 8 bytes]
-  static constexpr int P_PLANE = 10 * 512;
+  static constexpr int OFF_P = STAGES * STAGE;   // score tiles [hi, lo][NT][64 lanes x 8 bytes]
+  static constexpr int P_PLANE = NT * 512;
   static constexpr int LDS_BYTES = OFF_P + 2 * P_PLANE;
+  static constexpr int WG_PER_CU = (160 * 1024) / LDS_BYTES >= 2 ? 2 : 1;
+  static constexpr int WAVES_PER_SIMD = NW * WG_PER_CU / 4;
+  static constexpr int PRO_BATCH = WAVES_PER_SIMD >= 4 ? 2 : 4;   // increments loaded per round trip (registers)
   static constexpr int EPW = C / NW;             // eta values loaded by each wave
   static constexpr int MAT_LOADS = MAT / 1024 / NW;  // 16-byte direct-to-LDS loads per wave per matrix
   static constexpr int LOADS = 3 * MAT_LOADS + 1;
   static constexpr int OUT_STORES = MAT_LOADS;   // 16-byte output stores per wave per tile
+  static_assert(C == 32 || C == 64, "tile length");
   static_assert(MAT % (1024 * NW) == 0, "tile matrix must split into whole wave loads");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+  static_assert(LDS_BYTES >= D * D * 4, "W0 is staged through the ring");
 };
-
-// LDS layout of the 64-token tiles: row-major, with 16-byte piece p of row r
-// stored at piece p ^ seg_swz(r).  The products that contract over d read
-// their operands in the k order in which the S accumulators hold their rows
-// (d = 32p+4g..+3 and 32p+16+4g..+3 for lane group g): two 8-byte reads per
-// operand.  With this swizzle those reads, the transposed reads over rows
-// 4g..4g+3 and the output staging writes run without bank conflicts
-// (measured on gfx950).
-template <int D>
-__device__ __forceinline__ int seg_swz(int r) {
-  return D == 128 ? (((r & 7) << 1) | ((r >> 3) & 1)) : ((r & 6) | ((r >> 3) & 1));
+// wave w computes score tiles [seg_tile_begin(w), seg_tile_begin(w+1))
+template <class Cfg>
+__device__ __forceinline__ int seg_tile_begin(int w) {
+  if constexpr (Cfg::C == 64) return tile_begin<Cfg::NW>(w);
+  else return min(w, Cfg::NT);
 }
 
-// S_w += K^T diag(eta) V_w over the tile's 64 keys, in pieces that can be
-// placed on either side of a barrier: A operand rows 16m + li of K^T with keys
+// Row order of the state held in MFMA accumulators: accumulator row 4g + r
+// of row tile m = 2p + h holds row d = 32p + 8g + 4h + r of S.  Then tiles
+// 2p and 2p + 1 of a lane together hold 8 consecutive rows 32p + 8g .. + 7,
+// so the products that contract over d (scores, Q S) read their Q and K
+// operands as one 16-byte piece per lane in natural order.
+__host__ __device__ constexpr int seg_srow(int m, int g, int r) { return 32 * (m >> 1) + 8 * g + 4 * (m & 1) + r; }
+
+// LDS layout of the tiles: row-major, with 16-byte piece c of row r stored
+// at piece c ^ seg_swz(r).  For d = 128 the map (a linear map of the row's
+// low 4 bits, as a table) was chosen by measuring LDS throughput on gfx950
+// so that the 16-byte operand reads (16 rows, one piece), the transposed
+// reads of K for the state update (4 rows x 4 pieces 16 bytes apart, one
+// half) and of V (4 rows x 32 bytes) all run without bank conflicts; simple
+// XOR maps of the row leave one or the other 2-way conflicted.
+template <int D>
+__host__ __device__ constexpr int seg_swz(int r) {
+  return D == 128 ? (int)((0x159DAE2673FBC840ull >> (4 * (r & 15))) & 15) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
+}
+// LDS byte offset, within a tile matrix, of the transposed read that gives
+// lane (g, li) its A operand of the state update for row tile m: key row
+// 4g + li/4, the 4 columns 32p + 8(li%4) + 4h .. + 3 (m = 2p + h)
+template <int D>
+__host__ __device__ constexpr unsigned seg_ktr(int m, int g, int li) {
+  return (unsigned)((4 * g + (li >> 2)) * 2 * D + (((4 * (m >> 1) + (li & 3)) ^ seg_swz<D>(4 * g + (li >> 2))) << 4) +
+                    8 * (m & 1));
+}
+
+// S_w += K^T diag(eta) V_w over the tile's keys, in pieces that can be
+// placed on either side of a barrier: A operand rows seg_srow(m, li/4, li%4) of K^T with keys
 // 16kb + 4g + j (transposed reads, one key half at a time); B operand
 // diag(eta) V_w built from the V_w fragments vt (same key order), split bf16
 // hi + lo.
 template <class Cfg>
 struct SegUpdate {
-  bf16x8 evh[2], evl[2];            // diag(eta) V_w, keys of half kc, bf16 hi + lo
+  bf16x8 evh[Cfg::KC], evl[Cfg::KC];  // diag(eta) V_w, keys of half kc, bf16 hi + lo
 };
 template <class Cfg>
-__device__ __forceinline__ void seg_update_eta(SegUpdate<Cfg>& U, const float* es, const bf16x4 (&vt)[4], int g) {
+__device__ __forceinline__ void seg_update_eta(SegUpdate<Cfg>& U, const float* es, const bf16x4 (&vt)[Cfg::NB], int g) {
 #pragma unroll
-  for (int kc = 0; kc < 2; ++kc) {
+  for (int kc = 0; kc < Cfg::KC; ++kc) {
     const floatx4 e0 = *(const floatx4*)(es + 32 * kc + 4 * g);
     const floatx4 e1 = *(const floatx4*)(es + 32 * kc + 16 + 4 * g);
     const uint2 v0 = __builtin_bit_cast(uint2, vt[2 * kc]), v1 = __builtin_bit_cast(uint2, vt[2 * kc + 1]);
@@ -110,7 +146,7 @@ __device__ __forceinline__ void seg_update_eta(SegUpdate<Cfg>& U, const float* e
            U.evh[kc], U.evl[kc]);
   }
 }
-// transposed K operands of key half kc: rows 16m + li of K^T, keys 32kc + 16h + 4g + j
+// transposed K operands of key half kc: rows seg_srow(m, li/4, li%4) of K^T, keys 32kc + 16h + 4g + j
 template <class Cfg>
 __device__ __forceinline__ void seg_update_k(bf16x8 (&a)[Cfg::MT], const unsigned char* ks,
                                              const unsigned (&ktr)[Cfg::MT], int kc) {
@@ -138,21 +174,23 @@ struct SegArgs {
   floatx4* part;
   bf16* O;
   float* Wout;
-  int T, nseg, seg_tiles;
+  int T, nseg, seg_len;             // segment s covers tokens [s*seg_len, (s+1)*seg_len), whole tiles of both passes
   int scanned;                      // 1: workspace slot s already holds the start state of segment s
 };
 
 // The program of wave W (wave-uniform).  One program for all waves keeps the
 // code within the instruction cache.
-template <int D>
+template <int D, int CT>
 __device__ __forceinline__ void seg_wave(const SegArgs& A, unsigned char* smem, int bh, int s, int W, int l) {
-  using Cfg = SegCfg<D>;
+  using Cfg = SegCfg<D, CT>;
+  constexpr int NB = Cfg::NB;
   constexpr int C = Cfg::C, ROWB = Cfg::ROWB, MT = Cfg::MT, KP = Cfg::KP, NW = Cfg::NW;
   constexpr int LOADS = Cfg::LOADS;
   const int g = l >> 4, li = l & 15;
   const int T = A.T, nseg = A.nseg;
   const int nchunks = (int)(((long long)T + C - 1) / C);
-  const int c0 = s * A.seg_tiles, c1 = min(c0 + A.seg_tiles, nchunks);
+  const int seg_tiles = A.seg_len / C;
+  const int c0 = s * seg_tiles, c1 = min(c0 + seg_tiles, nchunks);
   const int nt = c1 > c0 ? c1 - c0 : 0;
   const long long seg_end = min((long long)c1 * C, (long long)T);
   const bf16* Qh = A.Q + (size_t)bh * T * D;
@@ -172,29 +210,32 @@ __device__ __forceinline__ void seg_wave(const SegArgs& A, unsigned char* smem, 
     gofs[k] = (unsigned)(row * ROWB + ((ph ^ seg_swz<D>(row)) << 4));
     lofs[k] = (unsigned)b;
   }
-  unsigned ksb[KP][2];              // operand reads in the S row order: row li, d = 32p + 4g.. and 32p + 16 + 4g..
+  unsigned ksb[KP];                 // operand reads: row li, d = 32p + 8g .. + 7
 #pragma unroll
-  for (int p = 0; p < KP; ++p)
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-      ksb[p][h] = (unsigned)(li * ROWB + (((4 * p + 2 * h + (g >> 1)) ^ seg_swz<D>(li)) << 4) + (g & 1) * 8);
+  for (int p = 0; p < KP; ++p) ksb[p] = (unsigned)(li * ROWB + (((4 * p + g) ^ seg_swz<D>(li)) << 4));
   const int trow = 4 * g + (li >> 2);   // transposed reads: rows 4g..4g+3, column 16m + li
   unsigned ktr[MT];
 #pragma unroll
-  for (int m = 0; m < MT; ++m)
-    ktr[m] = (unsigned)(trow * ROWB + (((2 * m + ((li >> 1) & 1)) ^ seg_swz<D>(trow)) << 4) + (li & 1) * 8);
+  for (int m = 0; m < MT; ++m) ktr[m] = seg_ktr<D>(m, g, li);
   const unsigned vtr = (unsigned)(trow * ROWB + (((2 * W + ((li >> 1) & 1)) ^ seg_swz<D>(trow)) << 4) + (li & 1) * 8);
   // output fragment (row 16ib + li, columns 16W + 4g..+3) in the swizzled staging rows
   const unsigned ofr = (unsigned)(li * ROWB + (((2 * W + (g >> 1)) ^ seg_swz<D>(li)) << 4) + (g & 1) * 8);
 
-  auto issue = [&](int i) {         // tile i of the segment into ring slot i % STAGES (empty past the segment)
+  // Tile i of the segment into ring slot i % STAGES (empty past the segment), in two parts: Q, and
+  // K, V, eta.  The parts are issued at different points of a tile so that the workgroup's vector
+  // memory instructions do not all queue at the tile boundary.
+  auto issue_q = [&](int i) {
     const long long t0 = (long long)(c0 + i) * C;
     const long long rem = seg_end - t0;
     unsigned char* st = smem + (i % Cfg::STAGES) * Cfg::STAGE + W * Cfg::MAT_LOADS * 1024;
     const __amdgpu_buffer_rsrc_t rq = make_rsrc(Qh + (rem > 0 ? t0 * D : 0), rem * ROWB);
 #pragma unroll
     for (int k = 0; k < Cfg::MAT_LOADS; ++k) dma16(rq, gofs[k], st + k * 1024);
-
+  };
+  auto issue_kve = [&](int i) {
+    const long long t0 = (long long)(c0 + i) * C;
+    const long long rem = seg_end - t0;
+    unsigned char* st = smem + (i % Cfg::STAGES) * Cfg::STAGE + W * Cfg::MAT_LOADS * 1024;
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kh + (rem > 0 ? t0 * D : 0), rem * ROWB);
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vh + (rem > 0 ? t0 * D : 0), rem * ROWB);
 #pragma unroll
@@ -217,7 +258,7 @@ __device__ __forceinline__ void seg_wave(const SegArgs& A, unsigned char* smem, 
     for (int k = 0; k < Cfg::MAT_LOADS; ++k) buf_store16(ro, gofs[k], v[k]);
   };
 
-  // ---- state: S[m][r] = S[16m + 4g + r][16W + li] ----
+  // ---- state: S[m][r] = S[seg_srow(m, g, r)][16W + li] ----
   floatx4 S[MT];
   const floatx4* pp = A.part + ((size_t)bh * nseg * NW + W) * MT * 64 + l;   // slot 0 of this head
   constexpr int SLOT = NW * MT * 64;                                         // floatx4 per slot
@@ -227,7 +268,7 @@ __device__ __forceinline__ void seg_wave(const SegArgs& A, unsigned char* smem, 
     for (int m = 0; m < MT; ++m) S[m] = pp[(size_t)s * SLOT + m * 64];
   } else {
     // W0 [D][D] fp32 -> LDS with coalesced 16-byte copies (the ring is still empty), then this lane's
-    // fragment; the increments of earlier segments are added, 4 segments per memory round trip
+    // fragment; the increments of earlier segments are added, PRO_BATCH segments per memory round trip
     const float* W0h = A.W0 + (size_t)bh * D * D;
     const __amdgpu_buffer_rsrc_t rw = make_rsrc(W0h, (long long)D * D * 4);
 #pragma unroll
@@ -235,10 +276,11 @@ __device__ __forceinline__ void seg_wave(const SegArgs& A, unsigned char* smem, 
       const unsigned b = (unsigned)((W * (D * D * 4 / 1024 / NW) + k) * 1024);
       dma16(rw, b + 16 * l, smem + b);
     }
-    floatx4 d[4][MT];             // increments of segments s0..s0+3 (clamped; only those < s are added)
+    constexpr int PB = Cfg::PRO_BATCH;
+    floatx4 d[PB][MT];            // increments of segments s0..s0+PB-1 (clamped; only those < s are added)
     auto load_incr = [&](int s0) {
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
+      for (int k = 0; k < PB; ++k) {
         const int sp = min(s0 + k, max(s - 1, 0));
 #pragma unroll
         for (int m = 0; m < MT; ++m) d[k][m] = pp[(size_t)sp * SLOT + m * 64];
@@ -250,11 +292,11 @@ __device__ __forceinline__ void seg_wave(const SegArgs& A, unsigned char* smem, 
 #pragma unroll
     for (int m = 0; m < MT; ++m)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) S[m][r] = wl[(16 * m + 4 * g + r) * D + 16 * W + li];
-    for (int s0 = 0; s0 < s; s0 += 4) {
+      for (int r = 0; r < 4; ++r) S[m][r] = wl[seg_srow(m, g, r) * D + 16 * W + li];
+    for (int s0 = 0; s0 < s; s0 += PB) {
       if (s0 > 0) load_incr(s0);
 #pragma unroll
-      for (int k = 0; k < 4; ++k)
+      for (int k = 0; k < PB; ++k)
         if (s0 + k < s)
 #pragma unroll
           for (int m = 0; m < MT; ++m) S[m] += d[k][m];
@@ -265,9 +307,14 @@ __device__ __forceinline__ void seg_wave(const SegArgs& A, unsigned char* smem, 
 
 #pragma unroll
   for (int k = 0; k < Cfg::STAGES - 1; ++k)
-    if (nt > 0) issue(k);
+    if (nt > 0) {
+      issue_q(k);
+      issue_kve(k);
+    }
+  static_assert(Cfg::STAGES == 3, "the vmcnt waits below count the loads of two tiles in flight");
   for (int i = 0; i < nt; ++i) {
-    // tile i has landed once only later-issued loads (and output stores) may be outstanding
+    // Tile i has landed once only later-issued loads (and output stores) may be outstanding: per
+    // wave the order is stores(i-2), Q(i+1) [tile i-1 start], K/V/eta(i+1) [tile i-1 middle].
     if (i < 2)
       wait_vm_barrier<LOADS>();
     else
@@ -276,7 +323,7 @@ __device__ __forceinline__ void seg_wave(const SegArgs& A, unsigned char* smem, 
       write_out(i - 1);           // from the slot the next load overwrites: read it first
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     }
-    issue(i + Cfg::STAGES - 1);     // into the slot read during tile i-1
+    issue_q(i + Cfg::STAGES - 1);   // into the slot read during tile i-1
     const unsigned char* st = smem + (i % Cfg::STAGES) * Cfg::STAGE;
     const unsigned char* ks = st + Cfg::OFF_K;
     const unsigned char* vs = st + Cfg::OFF_V;
@@ -284,26 +331,26 @@ __device__ __forceinline__ void seg_wave(const SegArgs& A, unsigned char* smem, 
 
     const unsigned char* qs = st;
     unsigned char* pb = smem + Cfg::OFF_P;
-    floatx4 acc[4];
-    bf16x4 vt[4];                 // vt[kb][j] = V[16kb + 4g + j][16W + li]
+    floatx4 acc[NB];
+    bf16x4 vt[NB];                 // vt[kb][j] = V[16kb + 4g + j][16W + li]
     SegUpdate<Cfg> U;
     // Q operand of block ib, step p (k order of the S accumulators)
     auto qop = [&](int p, int ib) {
       const unsigned char* qrow = qs + ib * 16 * ROWB;
-      return join(*(const bf16x4*)(qrow + ksb[p][0]), *(const bf16x4*)(qrow + ksb[p][1]));
+      return *(const bf16x8*)(qrow + ksb[p]);
     };
     // this wave's score tiles P^T(jb, ib) = K_jb Q_ib^T, scaled by eta of the key, masked, bf16 hi + lo
     auto scores = [&]() {
-      const int tb = tile_begin<NW>(W), te = tile_begin<NW>(W + 1);
+      const int tb = seg_tile_begin<Cfg>(W), te = seg_tile_begin<Cfg>(W + 1);
 #pragma unroll
-      for (int t = 0; t < 10; ++t) {
+      for (int t = 0; t < Cfg::NT; ++t) {
         if (t < tb || t >= te) continue;    // wave-uniform
         const int jb = ptile_jb(t), ib = ptile_ib(t);
         floatx4 p = {0.f, 0.f, 0.f, 0.f};
         const unsigned char* krow = ks + jb * 16 * ROWB;
 #pragma unroll
         for (int kk = 0; kk < KP; ++kk) {
-          const bf16x8 ka = join(*(const bf16x4*)(krow + ksb[kk][0]), *(const bf16x4*)(krow + ksb[kk][1]));
+          const bf16x8 ka = *(const bf16x8*)(krow + ksb[kk]);
           p = mfma16(ka, qop(kk, ib), p);
         }
         const floatx4 e4 = *(const floatx4*)(es + 16 * jb + 4 * g);
@@ -318,27 +365,34 @@ __device__ __forceinline__ void seg_wave(const SegArgs& A, unsigned char* smem, 
     // O_W^T = S_W^T Q^T with S_W as bf16 hi + lo
     auto qs_mfma = [&]() {
 #pragma unroll
-      for (int ib = 0; ib < 4; ++ib) acc[ib] = floatx4{0.f, 0.f, 0.f, 0.f};
+      for (int ib = 0; ib < NB; ++ib) acc[ib] = floatx4{0.f, 0.f, 0.f, 0.f};
+      // the split of step p + 1 is interleaved with the MFMAs of step p
+      bf16x8 ah[2], al[2], qv[2][NB];
+      split8(S[0], S[1], ah[0], al[0]);
+#pragma unroll
+      for (int ib = 0; ib < NB; ++ib) qv[0][ib] = qop(0, ib);
 #pragma unroll
       for (int p = 0; p < KP; ++p) {
-        bf16x8 ah, al, qv[4];
+        const int c = p & 1, n = c ^ 1;
+        if (p + 1 < KP) {
 #pragma unroll
-        for (int ib = 0; ib < 4; ++ib) qv[ib] = qop(p, ib);
-        split8(S[2 * p], S[2 * p + 1], ah, al);
+          for (int ib = 0; ib < NB; ++ib) qv[n][ib] = qop(p + 1, ib);
+          split8(S[2 * p + 2], S[2 * p + 3], ah[n], al[n]);
+        }
 #pragma unroll
-        for (int ib = 0; ib < 4; ++ib) acc[ib] = mfma16(ah, qv[ib], acc[ib]);
+        for (int ib = 0; ib < NB; ++ib) acc[ib] = mfma16(ah[c], qv[c][ib], acc[ib]);
 #pragma unroll
-        for (int ib = 0; ib < 4; ++ib) acc[ib] = mfma16(al, qv[ib], acc[ib]);
-        __builtin_amdgcn_sched_barrier(0);   // keep each step's Q loads next to their use (register pressure)
+        for (int ib = 0; ib < NB; ++ib) acc[ib] = mfma16(al[c], qv[c][ib], acc[ib]);
+        __builtin_amdgcn_sched_barrier(0);
       }
     };
     // operands of phase 2 that do not depend on the score tiles
     bf16x8 ka0[MT];               // transposed K operands of the first key half
     auto load_update = [&]() {
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) vt[kb] = lds_read_tr16(vs + kb * 16 * ROWB + vtr);
+      for (int kb = 0; kb < NB; ++kb) vt[kb] = lds_read_tr16(vs + kb * 16 * ROWB + vtr);
       seg_update_eta<Cfg>(U, es, vt, g);
-      seg_update_k<Cfg>(ka0, ks, ktr, 0);
+      if constexpr (Cfg::KC == 2) seg_update_k<Cfg>(ka0, ks, ktr, 0);
     };
     // The two waves of a SIMD take phase 1 in opposite orders so that one
     // issues MFMAs while the other reads LDS.
@@ -351,10 +405,11 @@ __device__ __forceinline__ void seg_wave(const SegArgs& A, unsigned char* smem, 
       qs_mfma();
     }
     barrier();                    // score tiles visible; everyone is done reading Q of this tile
+    issue_kve(i + Cfg::STAGES - 1);
 
     // ---- phase 2a: O_W^T += V_W^T A^T over key blocks 0..ib ----
 #pragma unroll
-    for (int ib = 0; ib < 4; ++ib)
+    for (int ib = 0; ib < NB; ++ib)
 #pragma unroll
       for (int kc = 0; 2 * kc <= ib; ++kc) {
         const int t0i = ptile_index(2 * kc, ib);
@@ -373,12 +428,17 @@ __device__ __forceinline__ void seg_wave(const SegArgs& A, unsigned char* smem, 
     // outputs into the Q region of this slot (written out after the next barrier)
     unsigned char* ob = smem + (i % Cfg::STAGES) * Cfg::STAGE;
 #pragma unroll
-    for (int ib = 0; ib < 4; ++ib)
+    for (int ib = 0; ib < NB; ++ib)
       *(bf16x4*)(ob + ib * 16 * ROWB + ofr) = to_bf16x4(acc[ib][0], acc[ib][1], acc[ib][2], acc[ib][3]);
-    bf16x8 ka1[MT];
-    seg_update_k<Cfg>(ka1, ks, ktr, 1);
-    seg_update_mfma<Cfg>(S, ka0, U, 0);
-    seg_update_mfma<Cfg>(S, ka1, U, 1);
+    if constexpr (Cfg::KC == 2) {
+      bf16x8 ka1[MT];
+      seg_update_k<Cfg>(ka1, ks, ktr, 1);
+      seg_update_mfma<Cfg>(S, ka0, U, 0);
+      seg_update_mfma<Cfg>(S, ka1, U, 1);
+    } else {                      // one key half: its K operands are read here, within the register budget
+      seg_update_k<Cfg>(ka0, ks, ktr, 0);
+      seg_update_mfma<Cfg>(S, ka0, U, 0);
+    }
 
   }
   if (nt > 0) {
@@ -393,19 +453,20 @@ __device__ __forceinline__ void seg_wave(const SegArgs& A, unsigned char* smem, 
 #pragma unroll
     for (int m = 0; m < MT; ++m)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) Wh[(size_t)(16 * m + 4 * g + r) * D + 16 * W + li] = S[m][r];
+      for (int r = 0; r < 4; ++r) Wh[(size_t)seg_srow(m, g, r) * D + 16 * W + li] = S[m][r];
   }
 
 }
 
 // Outputs of segment s of head bh (grid BH x nseg), starting from W0 plus
 // the increments of the earlier segments of the head.
-template <int D>
-__global__ __launch_bounds__(D / 16 * WAVE, 1) void pt_seg_kernel(SegArgs A) {
+template <int D, int CT>
+__global__ __attribute__((amdgpu_flat_work_group_size(1, D / 16 * WAVE),
+                          amdgpu_waves_per_eu(SegCfg<D, CT>::WAVES_PER_SIMD))) void pt_seg_kernel(SegArgs A) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int bh = blockIdx.x / A.nseg, s = blockIdx.x % A.nseg;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  seg_wave<D>(A, smem, bh, s, w, threadIdx.x & 63);
+  seg_wave<D, CT>(A, smem, bh, s, w, threadIdx.x & 63);
 }
 
 // Segment increments dS_s = K_s^T diag(eta_s) V_s for every segment but the
@@ -444,10 +505,9 @@ __global__ __launch_bounds__(2 * D / 16 * WAVE, 1) void pt_incr_kernel(SegArgs A
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l = threadIdx.x & 63, g = l >> 4, li = l & 15;
   const int c = w % NC, h = w / NC;
-  const int nchunks = (int)(((long long)T + C - 1) / C);
-  const int c0 = s * A.seg_tiles, c1 = min(c0 + A.seg_tiles, nchunks);
-  const int nt = c1 > c0 ? c1 - c0 : 0;
-  const long long seg_end = min((long long)c1 * C, (long long)T);
+  const long long seg_begin = (long long)s * A.seg_len;
+  const long long seg_end = min(seg_begin + A.seg_len, (long long)T);
+  const int nt = seg_end > seg_begin ? (int)((seg_end - seg_begin + C - 1) / C) : 0;
   const bf16* Kh = A.K + (size_t)bh * T * D;
   const bf16* Vh = A.V + (size_t)bh * T * D;
   const float* Eh = A.eta + (size_t)bh * T;
@@ -462,14 +522,11 @@ __global__ __launch_bounds__(2 * D / 16 * WAVE, 1) void pt_incr_kernel(SegArgs A
   const int trow = 4 * g + (li >> 2);
   unsigned ktr[MH];
 #pragma unroll
-  for (int j = 0; j < MH; ++j) {
-    const int m = h * MH + j;
-    ktr[j] = (unsigned)(trow * ROWB + (((2 * m + ((li >> 1) & 1)) ^ seg_swz<D>(trow)) << 4) + (li & 1) * 8);
-  }
+  for (int j = 0; j < MH; ++j) ktr[j] = seg_ktr<D>(h * MH + j, g, li);
   const unsigned vtr = (unsigned)(trow * ROWB + (((2 * c + ((li >> 1) & 1)) ^ seg_swz<D>(trow)) << 4) + (li & 1) * 8);
 
   auto issue = [&](int i) {
-    const long long t0 = (long long)(c0 + i) * C;
+    const long long t0 = seg_begin + (long long)i * C;
     const long long rem = seg_end - t0;
     unsigned char* st = smem + (i % Cfg::STAGES) * Cfg::STAGE;
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kh + (rem > 0 ? t0 * D : 0), rem * ROWB);
@@ -526,7 +583,7 @@ __global__ __launch_bounds__(2 * D / 16 * WAVE, 1) void pt_incr_kernel(SegArgs A
 // Start states of the segments of one head, in place: slot s holds dS_s
 // (s < nseg-1) on entry and S_start(s) = W0 + sum_{s' < s} dS_s' on exit.
 // Layout of a slot: [wave W][m-tile][lane][4] floats, lane (g, li) of wave W
-// holding rows 16m + 4g + r, column 16W + li.  One thread per 4 floats.
+// holding rows seg_srow(m, g, r), column 16W + li.  One thread per 4 floats.
 template <int D>
 __global__ __launch_bounds__(256) void pt_seg_scan_kernel(const float* __restrict__ W0, floatx4* __restrict__ part,
                                                           int nseg) {
@@ -538,7 +595,7 @@ __global__ __launch_bounds__(256) void pt_seg_scan_kernel(const float* __restric
   const float* W0h = W0 + (size_t)bh * D * D;
   floatx4 run;
 #pragma unroll
-  for (int r = 0; r < 4; ++r) run[r] = W0h[(size_t)(16 * m + 4 * g + r) * D + 16 * W + li];
+  for (int r = 0; r < 4; ++r) run[r] = W0h[(size_t)seg_srow(m, g, r) * D + 16 * W + li];
   floatx4* ph = part + (size_t)bh * nseg * PER + f;
   // up to 8 increments are loaded before any slot is rewritten (one memory round trip per 8 segments)
   for (int s0 = 0; s0 < nseg - 1; s0 += 8) {
@@ -660,34 +717,36 @@ bool per_token_supported(int64_t dk, int64_t dv, int64_t chunk, int dtype) {
   return true;
 }
 
-// Segment plan of the bf16 path: about one workgroup per compute unit
-// (256 on MI355X) over heads x segments, each segment whole 64-token tiles.
-SegPlan per_token_seg_plan(int64_t BH, int64_t T) {
+// Segment plan of the bf16 path: about one workgroup per workgroup slot of
+// the chip (256 compute units x workgroups per CU) over heads x segments,
+// each segment whole tiles of both passes (multiples of 64 tokens).
+SegPlan per_token_seg_plan(int64_t BH, int64_t T, int64_t dk) {
+  const int64_t slots = 256 * (dk == 128 ? SegCfg<128, seg_tile<128>()>::WG_PER_CU : SegCfg<64, seg_tile<64>()>::WG_PER_CU);
   const int64_t nchunks = (T + 63) / 64;
-  int64_t p = BH >= 256 ? 1 : 256 / BH;
+  int64_t p = BH >= slots ? 1 : slots / BH;
   p = std::max<int64_t>(1, std::min(p, nchunks));
   const int64_t tiles = nchunks > 0 ? (nchunks + p - 1) / p : 0;
   const int64_t nseg = tiles > 0 ? (nchunks + tiles - 1) / tiles : 1;
-  return SegPlan{(int)nseg, (int)tiles};
+  return SegPlan{(int)nseg, (int)(tiles * 64)};
 }
 
 size_t per_token_workspace(int64_t B, int64_t H, int64_t T, int64_t dk, int64_t dv, int dtype) {
   if (dtype != 1) return 0;
-  const SegPlan sp = per_token_seg_plan(B * H, T);
+  const SegPlan sp = per_token_seg_plan(B * H, T, dk);
   return sp.nseg > 1 ? (size_t)sp.nseg * (size_t)(B * H) * (size_t)dk * (size_t)dv * sizeof(float) : 0;
 }
 
 template <int D>
 static hipError_t launch_seg(const PerTokenArgs& a, hipStream_t stream, const Timing& tm) {
   using CfgD = IncrCfg<D>;
-  using CfgF = SegCfg<D>;
+  using CfgF = SegCfg<D, seg_tile<D>()>;
   const int BH = (int)(a.B * a.H);
-  const SegPlan sp = per_token_seg_plan(BH, a.T);
+  const SegPlan sp = per_token_seg_plan(BH, a.T, D);
   // With few segments every workgroup adds the earlier increments itself (one or two memory round
   // trips); with many, a scan kernel turns them into start states first (linear instead of
   // quadratic traffic, at the price of one more kernel boundary).
   SegArgs A{(const bf16*)a.Q, (const bf16*)a.K, (const bf16*)a.V, a.eta, a.W0, (floatx4*)a.ws,
-            (bf16*)a.O, a.W_out, (int)a.T, sp.nseg, sp.tiles, sp.nseg > 8 ? 1 : 0};
+            (bf16*)a.O, a.W_out, (int)a.T, sp.nseg, sp.seg_len, sp.nseg > 8 ? 1 : 0};
   hipError_t e;
   if (sp.nseg > 1) {
     auto kd = pt_incr_kernel<D>;
@@ -702,7 +761,7 @@ static hipError_t launch_seg(const PerTokenArgs& a, hipStream_t stream, const Ti
       if ((e = hipGetLastError()) != hipSuccess) return e;
     }
   }
-  auto kf = pt_seg_kernel<D>;
+  auto kf = pt_seg_kernel<D, seg_tile<D>()>;
   if ((e = hipFuncSetAttribute((const void*)kf, hipFuncAttributeMaxDynamicSharedMemorySize, CfgF::LDS_BYTES)) !=
       hipSuccess)
     return e;
