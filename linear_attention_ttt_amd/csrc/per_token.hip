@@ -26,21 +26,29 @@
 // waits).  Per 64-token tile:
 //   phase 1: the 10 causal score tiles P^T(jb, ib) = K_jb Q_ib^T (jb <= ib),
 //            spread over the waves, scaled by eta of the key, masked and
-//            split bf16 hi + lo into LDS; O_w^T = S_w^T Q^T with S_w as bf16
-//            hi + lo built in registers from the accumulators (the
-//            contraction index follows the accumulator row order and Q is
-//            read in the same order);
-//   phase 2: V_w (4 transposed reads) serves as the operand of
-//            O_w^T += V_w^T A^T and, scaled by eta in registers and split
-//            hi + lo, of the state update S_w += K^T diag(eta) V_w.
+//            split bf16 hi + lo into LDS; the wave's V columns (transposed
+//            reads) scaled by eta and split hi + lo, and the first K^T
+//            operands of the state update;
+//   phase 2: O_w^T = S_w^T Q^T with S_w as bf16 hi + lo built in registers
+//            from the accumulators (the contraction index follows the
+//            accumulator row order and Q is read in the same order), plus
+//            V_w^T A^T from the score tiles; then S_w += K^T diag(eta) V_w.
 // Outputs are computed transposed, so a lane holds 4 consecutive columns of
-// one token: an 8-byte store.
+// one token; they are staged as whole rows in the tile's dead V region and
+// leave with 16-byte stores after the next barrier.
 #include <algorithm>
 
 #include "device_common.h"
 #include "kernels.h"
 
 namespace ttt {
+
+// Q, K, V and eta are streamed with non-temporal loads in both passes.  On
+// gfx950 this keeps their throughput when the caches hold many dirty lines
+// (measured: about 1.2x faster for the two passes together), and costs about
+// 3% when the caches are clean, where the output pass would otherwise find
+// some K/V lines the increment pass left behind.
+constexpr bool PT_STREAM = true;
 
 // score tile t (0..9) <-> (jb, ib), jb <= ib; wave w owns tiles [tile_begin(w), tile_begin(w+1))
 __host__ __device__ constexpr int ptile_jb(int t) { return t < 1 ? 0 : t < 3 ? t - 1 : t < 6 ? t - 3 : t - 6; }
@@ -70,7 +78,7 @@ struct SegCfg {
   static constexpr int KP = D / 32;              // 32-deep contraction steps over d
   static constexpr int ROWB = D * 2;             // bytes per token row of Q, K, V, O
   static constexpr int MAT = C * ROWB;           // one matrix of a tile
-  // ring slot: Q (reused for the tile's outputs), K, V, eta
+  // ring slot: Q, K, V (reused for the tile's outputs), eta
   static constexpr int STAGES = 3;
   static constexpr int OFF_K = MAT;
   static constexpr int OFF_V = OFF_K + MAT;
@@ -230,7 +238,7 @@ __device__ __forceinline__ void seg_wave(const SegArgs& A, unsigned char* smem, 
     unsigned char* st = smem + (i % Cfg::STAGES) * Cfg::STAGE + W * Cfg::MAT_LOADS * 1024;
     const __amdgpu_buffer_rsrc_t rq = make_rsrc(Qh + (rem > 0 ? t0 * D : 0), rem * ROWB);
 #pragma unroll
-    for (int k = 0; k < Cfg::MAT_LOADS; ++k) dma16(rq, gofs[k], st + k * 1024);
+    for (int k = 0; k < Cfg::MAT_LOADS; ++k) dma16<PT_STREAM>(rq, gofs[k], st + k * 1024);
   };
   auto issue_kve = [&](int i) {
     const long long t0 = (long long)(c0 + i) * C;
@@ -239,17 +247,17 @@ __device__ __forceinline__ void seg_wave(const SegArgs& A, unsigned char* smem, 
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kh + (rem > 0 ? t0 * D : 0), rem * ROWB);
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vh + (rem > 0 ? t0 * D : 0), rem * ROWB);
 #pragma unroll
-    for (int k = 0; k < Cfg::MAT_LOADS; ++k) dma16(rk, gofs[k], st + Cfg::OFF_K + k * 1024);
+    for (int k = 0; k < Cfg::MAT_LOADS; ++k) dma16<PT_STREAM>(rk, gofs[k], st + Cfg::OFF_K + k * 1024);
 #pragma unroll
-    for (int k = 0; k < Cfg::MAT_LOADS; ++k) dma16(rv, gofs[k], st + Cfg::OFF_V + k * 1024);
+    for (int k = 0; k < Cfg::MAT_LOADS; ++k) dma16<PT_STREAM>(rv, gofs[k], st + Cfg::OFF_V + k * 1024);
     const __amdgpu_buffer_rsrc_t re = make_rsrc(Eh + (rem > 0 ? t0 : 0), rem * 4);
     unsigned char* ed = smem + (i % Cfg::STAGES) * Cfg::STAGE + Cfg::OFF_E + W * Cfg::EPW * 4;
-    if (l < Cfg::EPW) dma4(re, (unsigned)((W * Cfg::EPW + l) * 4), ed);
+    if (l < Cfg::EPW) dma4<PT_STREAM>(re, (unsigned)((W * Cfg::EPW + l) * 4), ed);
   };
-  // rows of tile i's outputs staged in its (dead) Q region -> HBM, 16 bytes per lane, whole rows
+  // rows of tile i's outputs staged in its (dead) V region -> HBM, 16 bytes per lane, whole rows
   auto write_out = [&](int i) {
     const long long t0 = (long long)(c0 + i) * C;
-    const unsigned char* st = smem + (i % Cfg::STAGES) * Cfg::STAGE;
+    const unsigned char* st = smem + (i % Cfg::STAGES) * Cfg::STAGE + Cfg::OFF_V;
     const __amdgpu_buffer_rsrc_t ro = make_rsrc(Oh + t0 * D, ((long long)T - t0) * ROWB);
     u32x4 v[Cfg::MAT_LOADS];
 #pragma unroll
@@ -364,8 +372,6 @@ __device__ __forceinline__ void seg_wave(const SegArgs& A, unsigned char* smem, 
     };
     // O_W^T = S_W^T Q^T with S_W as bf16 hi + lo
     auto qs_mfma = [&]() {
-#pragma unroll
-      for (int ib = 0; ib < NB; ++ib) acc[ib] = floatx4{0.f, 0.f, 0.f, 0.f};
       // the split of step p + 1 is interleaved with the MFMAs of step p
       bf16x8 ah[2], al[2], qv[2][NB];
       split8(S[0], S[1], ah[0], al[0]);
@@ -394,20 +400,9 @@ __device__ __forceinline__ void seg_wave(const SegArgs& A, unsigned char* smem, 
       seg_update_eta<Cfg>(U, es, vt, g);
       if constexpr (Cfg::KC == 2) seg_update_k<Cfg>(ka0, ks, ktr, 0);
     };
-    // The two waves of a SIMD take phase 1 in opposite orders so that one
-    // issues MFMAs while the other reads LDS.
-    scores();
-    if (W < NW / 2) {
-      qs_mfma();
-      load_update();
-    } else {
-      load_update();
-      qs_mfma();
-    }
-    barrier();                    // score tiles visible; everyone is done reading Q of this tile
-    issue_kve(i + Cfg::STAGES - 1);
-
-    // ---- phase 2a: O_W^T += V_W^T A^T over key blocks 0..ib ----
+#pragma unroll
+    for (int ib = 0; ib < NB; ++ib) acc[ib] = floatx4{0.f, 0.f, 0.f, 0.f};
+    auto av_mfma = [&]() {        // O_W^T += V_W^T A^T over key blocks 0..ib
 #pragma unroll
     for (int ib = 0; ib < NB; ++ib)
 #pragma unroll
@@ -425,8 +420,23 @@ __device__ __forceinline__ void seg_wave(const SegArgs& A, unsigned char* smem, 
         acc[ib] = mfma16(av, bh_, acc[ib]);
         acc[ib] = mfma16(av, bl_, acc[ib]);
       }
-    // outputs into the Q region of this slot (written out after the next barrier)
-    unsigned char* ob = smem + (i % Cfg::STAGES) * Cfg::STAGE;
+    };
+    // phase 1: score tiles and the operands of the state update; phase 2: the
+    // two waves of a SIMD take Q S and the intra-tile product in opposite
+    // orders so that one issues MFMAs while the other waits on LDS
+    scores();
+    load_update();
+    barrier();                    // score tiles visible; V of this tile read by everyone
+    issue_kve(i + Cfg::STAGES - 1);
+    if (W < NW / 2) {
+      qs_mfma();
+      av_mfma();
+    } else {
+      av_mfma();
+      qs_mfma();
+    }
+    // outputs into the V region of this slot (written out after the next barrier)
+    unsigned char* ob = smem + (i % Cfg::STAGES) * Cfg::STAGE + Cfg::OFF_V;
 #pragma unroll
     for (int ib = 0; ib < NB; ++ib)
       *(bf16x4*)(ob + ib * 16 * ROWB + ofr) = to_bf16x4(acc[ib][0], acc[ib][1], acc[ib][2], acc[ib][3]);
@@ -532,11 +542,11 @@ __global__ __launch_bounds__(2 * D / 16 * WAVE, 1) void pt_incr_kernel(SegArgs A
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kh + (rem > 0 ? t0 * D : 0), rem * ROWB);
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vh + (rem > 0 ? t0 * D : 0), rem * ROWB);
 #pragma unroll
-    for (int k = 0; k < Cfg::MAT_LOADS; ++k) dma16(rk, gofs[k], st + (w * Cfg::MAT_LOADS + k) * 1024);
+    for (int k = 0; k < Cfg::MAT_LOADS; ++k) dma16<PT_STREAM>(rk, gofs[k], st + (w * Cfg::MAT_LOADS + k) * 1024);
 #pragma unroll
-    for (int k = 0; k < Cfg::MAT_LOADS; ++k) dma16(rv, gofs[k], st + MAT + (w * Cfg::MAT_LOADS + k) * 1024);
+    for (int k = 0; k < Cfg::MAT_LOADS; ++k) dma16<PT_STREAM>(rv, gofs[k], st + MAT + (w * Cfg::MAT_LOADS + k) * 1024);
     const __amdgpu_buffer_rsrc_t re = make_rsrc(Eh + (rem > 0 ? t0 : 0), rem * 4);
-    if (l < Cfg::EPW) dma4(re, (unsigned)((w * Cfg::EPW + l) * 4), st + 2 * MAT + w * Cfg::EPW * 4);
+    if (l < Cfg::EPW) dma4<PT_STREAM>(re, (unsigned)((w * Cfg::EPW + l) * 4), st + 2 * MAT + w * Cfg::EPW * 4);
   };
 
   floatx4 S[MH];
