@@ -17,7 +17,10 @@
 //    slice.  With that split dW1[:, s], dW3[:, s], dW2[s, :] and the W1/W3
 //    normalisation are local to the slice; only the W2 column norms need a
 //    128-float sum across the head's workgroups, exchanged through global
-//    memory with an acquire/release counter.  Each workgroup stores the
+//    memory with an acquire/release counter.  Within a workgroup each wave
+//    streams its own 32-token groups of the chunk (private LDS ring, no
+//    barriers) and keeps its partial gradients in registers; the waves'
+//    partials are added at the chunk end.  Each workgroup stores the
 //    weights every chunk reads (bf16 hi + lo planes, transposed for the
 //    read kernel's operands).
 //  * swiglu_read_kernel (fully parallel): O_c = f_{W_{c-1}}(Q_c) for every
@@ -37,30 +40,41 @@ constexpr int SW_D = 128;
 constexpr int SW_DH = 256;
 constexpr int SW_NS = 16;                 // hidden units per recurrence workgroup
 constexpr int SW_NSL = SW_DH / SW_NS;     // workgroups per head
-constexpr int SW_SB = 64;                 // tokens per LDS sub-block
 constexpr int SW_TT = 256;                // tokens per read workgroup (8 waves x 32)
 constexpr int SW_US = 32;                 // hidden units per read slice
 constexpr int SW_SPIN_LIMIT = 1 << 24;
 constexpr size_t SW_STATE = (size_t)6 * SW_D * SW_DH;  // bf16 elements per stored state
 
-constexpr int SW_RING = 4;                // K/V/eta sub-blocks resident in the recurrence ring
-constexpr int SW_KROW = SW_D * 2;         // unpadded bf16 row of K / V in LDS (swizzled pieces)
+// Recurrence: each wave streams its own 32-token groups of the chunk through
+// a private 2-stage LDS ring and keeps its partial chunk gradients in
+// registers; the 4 waves' partials are added at the chunk end.
+constexpr int SW_WAVES = 4;
+constexpr int SW_GT = 32;                 // tokens per wave step
+constexpr int SW_KROW = SW_D * 2;         // bf16 row of K / V in LDS (swizzled 16-byte pieces)
+constexpr int SW_STAGE = SW_GT * SW_KROW; // one matrix of one stage
+constexpr int SW_LOADS = 2 * SW_STAGE / 1024 + 1;   // direct-to-LDS loads per wave per stage: K, V, eta
 
 struct RecurLds {
-  unsigned char kv[SW_RING][2][SW_SB * SW_KROW];  // K, V sub-blocks
-  float eta[SW_RING][SW_SB];
-  unsigned char dx[3][4][64 * 8];                  // da, db, eh operand tiles of each wave's 16 tokens
-  float w1[SW_D * SW_NS];   // [d][u]
-  float w3[SW_D * SW_NS];   // [d][u]
-  float w2[SW_NS * SW_D];   // [u][d]
+  unsigned char kv[SW_WAVES][2][2][SW_STAGE];   // [wave][stage][K, V]
+  float eta[SW_WAVES][2][SW_GT];
+  float w1[SW_D * SW_NS];   // W1[d][u] at w13i(d, u)
+  float w3[SW_D * SW_NS];   // W3[d][u] at w13i(d, u)
+  float w2[SW_NS * SW_D];   // W2[u][d] at w2i(u, d)
 };
 static_assert(sizeof(RecurLds) <= 160 * 1024, "recurrence LDS exceeds 160 KB");
 
-// Position of the 16-byte piece of a 256-byte K/V row in LDS: the piece
-// index is XORed with a 1-bit rotation of (row & 15).  Rows 0..15 then land
-// on distinct pieces for the row-wise operand reads, and the transposed
-// 8-byte reads of 4 rows x 2 pieces by each half-wave hit distinct banks.
-__device__ __forceinline__ int sw_swz(int row) { return ((row & 7) << 1) | ((row >> 3) & 1); }
+// Position of the 16-byte piece of a 256-byte K/V row in LDS: piece c of row
+// r sits at c ^ sw_swz(r & 15), a map chosen by measuring LDS throughput on
+// gfx950: the row-wise 16-byte operand reads (16 rows, one piece) and the
+// transposed 8-byte reads (4 rows x 32 bytes per 16 lanes) are both free of
+// bank conflicts.
+__device__ __forceinline__ int sw_swz(int row) { return (int)((0x159DAE2673FBC840ull >> (4 * (row & 15))) & 15); }
+// The slice's fp32 weights in LDS are kept in the MFMA accumulator order of
+// the gradients, so a wave adds its partial chunk gradient with one 16-byte
+// read-modify-write per 4 values: W1[d][u], W3[d][u] at ((d/4)*16 + u)*4 + d%4
+// and W2[u][d] at (((d/16)*4 + u/4)*16 + d%16)*4 + u%4.
+__device__ __forceinline__ int w13i(int d, int u) { return ((d >> 2) * 16 + u) * 4 + (d & 3); }
+__device__ __forceinline__ int w2i(int u, int d) { return (((d >> 4) * 4 + (u >> 2)) * 16 + (d & 15)) * 4 + (u & 3); }
 
 __device__ __forceinline__ void split_store8(bf16* hi, bf16* lo, const float* f) {
   bf16x8 h, l;
@@ -78,18 +92,20 @@ __global__ void zero_u32_kernel(unsigned* p, int n) {
   if (i < n) p[i] = 0u;
 }
 
-__global__ __launch_bounds__(256, 1) void swiglu_recur_kernel(
+__global__ __launch_bounds__(SW_WAVES * 64, 1) void swiglu_recur_kernel(
     const bf16* __restrict__ K, const bf16* __restrict__ V, const float* __restrict__ eta,
     const float* __restrict__ W0, float* __restrict__ Wout, bf16* __restrict__ states, float* __restrict__ ss2,
     unsigned* __restrict__ counters, unsigned* __restrict__ errflag, int T, int chunk, int nchunks, int head0) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
   RecurLds& S = *reinterpret_cast<RecurLds*>(smem_raw);
+  constexpr int NT = SW_WAVES * 64;
   const int nblocks = gridDim.x;
   const int logical = (nblocks % 8 == 0) ? xcd_logical_block(blockIdx.x, nblocks) : blockIdx.x;
   const int bh = head0 + logical / SW_NSL;
   const int sl = logical % SW_NSL;
   const int u0 = sl * SW_NS;
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g = l >> 4, li = l & 15;
+  const int tid = threadIdx.x, l = tid & 63, g = l >> 4, li = l & 15;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   constexpr int D = SW_D, DH = SW_DH, NS = SW_NS;
 
   const bf16* Kh = K + (size_t)bh * T * D;
@@ -99,19 +115,20 @@ __global__ __launch_bounds__(256, 1) void swiglu_recur_kernel(
   bf16* St = states + (size_t)bh * nchunks * SW_STATE;
 
   // ---- load this slice of the initial weights ----
-  for (int i = tid; i < D * NS; i += 256) {
+  for (int i = tid; i < D * NS; i += NT) {
     const int d = i / NS, u = i % NS;
-    S.w1[i] = W0h[(size_t)d * DH + u0 + u];
-    S.w3[i] = W0h[(size_t)D * DH + (size_t)d * DH + u0 + u];
+    S.w1[w13i(d, u)] = W0h[(size_t)d * DH + u0 + u];
+    S.w3[w13i(d, u)] = W0h[(size_t)D * DH + (size_t)d * DH + u0 + u];
   }
-  for (int i = tid; i < NS * D; i += 256) {
+  for (int i = tid; i < NS * D; i += NT) {
     const int u = i / D, d = i % D;
-    S.w2[i] = W0h[(size_t)2 * D * DH + (size_t)(u0 + u) * D + d];
+    S.w2[w2i(u, d)] = W0h[(size_t)2 * D * DH + (size_t)(u0 + u) * D + d];
   }
   __syncthreads();
 
   // the weights chunk `slot` reads: W1^T, W3^T [DH][D] and W2^T [D][DH], bf16 hi + lo
   auto store_state = [&](int slot) {
+    if (tid >= 256) return;
     bf16* base = St + (size_t)slot * SW_STATE;
     const size_t P = (size_t)D * DH;
     {
@@ -120,8 +137,8 @@ __global__ __launch_bounds__(256, 1) void swiglu_recur_kernel(
       float f1[8], f3[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        f1[j] = S.w1[(d + j) * NS + u];
-        f3[j] = S.w3[(d + j) * NS + u];
+        f1[j] = S.w1[w13i(d + j, u)];
+        f3[j] = S.w3[w13i(d + j, u)];
       }
       const size_t o = (size_t)(u0 + u) * D + d;
       split_store8(base + o, base + P + o, f1);
@@ -132,172 +149,199 @@ __global__ __launch_bounds__(256, 1) void swiglu_recur_kernel(
       const int n = idx / NS, u = idx % NS;
       float f2[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) f2[j] = S.w2[(u + j) * D + n];
+      for (int j = 0; j < 8; ++j) f2[j] = S.w2[w2i(u + j, n)];
       const size_t o = (size_t)n * DH + u0 + u;
       split_store8(base + 4 * P + o, base + 5 * P + o, f2);
     }
   };
   if (nchunks > 0) store_state(0);
 
-  // ---- token sub-blocks through a ring of SW_RING LDS stages ----
-  // Stage loads go straight from global memory to LDS; each wave loads its
-  // own 16 tokens of K, V and eta (9 loads per stage), so the per-wave
-  // vector-memory count tells when a stage has landed.
-  const int nsb = (chunk + SW_SB - 1) / SW_SB;
-  const int last_len = T - (nchunks - 1) * chunk;
-  const int total = nchunks > 0 ? (nchunks - 1) * nsb + (last_len + SW_SB - 1) / SW_SB : 0;
-  // Each slice walks a chunk's sub-blocks from its own starting point, so the
-  // head's workgroups request different sub-blocks at any moment (repeats
-  // are served by L2).  The chunk's gradient sums do not depend on the order.
-  auto sub_of = [&](int gsb) {
-    const int c = gsb / nsb, i = gsb % nsb;
-    const int n = min(nsb, (min(c * chunk + chunk, T) - c * chunk + SW_SB - 1) / SW_SB);
-    return (i + 2 * sl) % n;
+  // ---- this wave's 32-token groups: in chunk c, groups w + 4k for k < count(c) ----
+  // All slices of a head walk a chunk in the same order, so they request the
+  // same lines at about the same time (measured on gfx950: faster than
+  // spreading the slices over the chunk, which raises L2 misses).
+  auto count = [&](int c) {
+    const int ng = (min(c * chunk + chunk, T) - c * chunk + SW_GT - 1) / SW_GT;
+    return ng > w ? (ng - w + SW_WAVES - 1) / SW_WAVES : 0;
   };
-  unsigned dma_off[4];
+  auto advance = [&](int& c, int& k) {       // next step of this wave (c == nchunks: none left)
+    ++k;
+    while (c < nchunks && k >= count(c)) {
+      ++c;
+      k = 0;
+    }
+  };
+  auto group_of = [&](int c, int k) {
+    (void)c;
+    return w + SW_WAVES * k;
+  };
+  // per-lane byte offsets: direct-to-LDS rows (4 per load), row-wise operand reads (row 16tt + li,
+  // piece 4ks + g) and transposed reads (rows 16tt + 4g .. + 3, columns 16m + li)
+  unsigned dma_off[SW_STAGE / 1024];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int row = 16 * w + 4 * j + (l >> 4);
+  for (int j = 0; j < SW_STAGE / 1024; ++j) {
+    const int row = 4 * j + (l >> 4);
     dma_off[j] = (unsigned)(row * SW_KROW + (((l & 15) ^ sw_swz(row)) << 4));
   }
-  auto issue_stage = [&](int gsb) {
-    const int c = gsb / nsb;
-    const int t0 = c * chunk + sub_of(gsb) * SW_SB;
+  unsigned fwd_off[4], tr_off[8];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) fwd_off[ks] = (unsigned)(li * SW_KROW + (((4 * ks + g) ^ sw_swz(li)) << 4));
+  const int trow = 4 * g + (li >> 2);
+#pragma unroll
+  for (int m = 0; m < 8; ++m)
+    tr_off[m] = (unsigned)(trow * SW_KROW + (((2 * m + ((li >> 1) & 1)) ^ sw_swz(trow)) << 4) + (li & 1) * 8);
+
+  auto issue = [&](int c, int gi, int slot) {
+    const int t0 = c * chunk + gi * SW_GT;
     const int n = min(c * chunk + chunk, T) - t0;   // valid tokens; rows beyond read as 0
-    const int slot = gsb % SW_RING;
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kh + (size_t)t0 * D, (long long)n * SW_KROW);
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vh + (size_t)t0 * D, (long long)n * SW_KROW);
     const __amdgpu_buffer_rsrc_t re = make_rsrc(Eh + t0, (long long)n * 4);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) buf2lds16(rk, dma_off[j], S.kv[slot][0] + (16 * w + 4 * j) * SW_KROW);
+    for (int j = 0; j < SW_STAGE / 1024; ++j) dma16<true>(rk, dma_off[j], S.kv[w][slot][0] + j * 1024);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) buf2lds16(rv, dma_off[j], S.kv[slot][1] + (16 * w + 4 * j) * SW_KROW);
-    if (l < 16) buf2lds4(re, (unsigned)((16 * w + l) * 4), &S.eta[slot][16 * w]);
+    for (int j = 0; j < SW_STAGE / 1024; ++j) dma16<true>(rv, dma_off[j], S.kv[w][slot][1] + j * 1024);
+    if (l < SW_GT) dma4<true>(re, (unsigned)(l * 4), S.eta[w][slot]);
   };
-  // per-lane LDS offsets: forward operand reads (row 16w+li, piece 4ks+g) and
-  // transposed reads (rows 4g..4g+3 of a 16-token block, d-tile 2w+j)
-  unsigned fwd_off[4], tr_off[2];
-#pragma unroll
-  for (int ks = 0; ks < 4; ++ks) fwd_off[ks] = (unsigned)((16 * w + li) * SW_KROW + (((4 * ks + g) ^ sw_swz(li)) << 4));
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int row = 4 * g + (li >> 2), m = 2 * w + j;
-    tr_off[j] = (unsigned)(row * SW_KROW + (((2 * m + ((li >> 1) & 1)) ^ sw_swz(row)) << 4) + (li & 1) * 8);
-  }
 
   bf16x8 w1op[4], w3op[4], w2op[4];
-  floatx4 dW1[2], dW3[2], dW2[2];   // this wave's d-tiles 2w, 2w+1
-#pragma unroll
-  for (int k = 0; k < SW_RING - 1; ++k)
-    if (k < total) issue_stage(k);
+  floatx4 dW1[8], dW3[8], dW2[8];
+  int ic = 0, ik = -1;                       // issue cursor: chunk, step within the chunk
+  advance(ic, ik);
+  int cc = ic, ck = ik;                      // compute cursor
+  int step = 0;
+  if (ic < nchunks) {
+    issue(ic, group_of(ic, ik), 0);
+    advance(ic, ik);
+  }
 
-  for (int gsb = 0; gsb < total; ++gsb) {
-    const int c = gsb / nsb, i = gsb % nsb;
-    // stage gsb has landed once at most the loads of the later issued stages are outstanding
-    if (gsb + 2 < total) wait_vm_barrier<18>();
-    else if (gsb + 1 < total) wait_vm_barrier<9>();
-    else wait_vm_barrier<0>();
-    if (gsb + SW_RING - 1 < total) issue_stage(gsb + SW_RING - 1);   // into the slot read last iteration
-    if (i == 0) {
-      // operands of this chunk's weights (B operands: col = unit li, k = 8 consecutive d)
+  for (int c = 0; c < nchunks; ++c) {
+    // operands of this chunk's weights (B operands: col = unit li, k = 8 consecutive d)
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int d = 32 * ks + 8 * g + j;
+        w1op[ks][j] = (bf16)S.w1[w13i(d, li)];
+        w3op[ks][j] = (bf16)S.w3[w13i(d, li)];
+        w2op[ks][j] = (bf16)S.w2[w2i(li, d)];
+      }
+#pragma unroll
+    for (int m = 0; m < 8; ++m) dW1[m] = dW3[m] = dW2[m] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+    for (; cc == c; advance(cc, ck), ++step) {
+      const int slot = step & 1;
+      // the next stage goes into the one read during the previous step; this step's stage has
+      // landed once only the next stage's loads are outstanding
+      if (ic < nchunks) {
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        issue(ic, group_of(ic, ik), slot ^ 1);
+        advance(ic, ik);
+        wait_vm<SW_LOADS>();
+      } else {
+        wait_vm<0>();
+      }
+      const unsigned char* kb = S.kv[w][slot][0];
+      const unsigned char* vb = S.kv[w][slot][1];
+
+      // ---- forward of the 32 tokens: A = K W1, B = K W3, Dh = V W2^T (rows: tokens 16tt + 4g + r) ----
+      floatx4 A[2], Bv[2], Dh[2];
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) A[tt] = Bv[tt] = Dh[tt] = floatx4{0.f, 0.f, 0.f, 0.f};
+      bf16x8 kop[4][2], vop[4][2];
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int d = 32 * ks + 8 * g + j;
-          w1op[ks][j] = (bf16)S.w1[d * NS + li];
-          w3op[ks][j] = (bf16)S.w3[d * NS + li];
-          w2op[ks][j] = (bf16)S.w2[li * D + d];
+        for (int tt = 0; tt < 2; ++tt) {
+          kop[ks][tt] = *(const bf16x8*)(kb + tt * 16 * SW_KROW + fwd_off[ks]);
+          vop[ks][tt] = *(const bf16x8*)(vb + tt * 16 * SW_KROW + fwd_off[ks]);
+        }
+      // transposed operands of the gradient products (k slot (g, j) = token 16(j/4) + 4g + j%4),
+      // read while the forward products run
+      bf16x4 ktr[8][2], vtr[8][2];
+#pragma unroll
+      for (int m = 0; m < 8; ++m)
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+          ktr[m][tt] = lds_read_tr16(kb + tt * 16 * SW_KROW + tr_off[m]);
+          vtr[m][tt] = lds_read_tr16(vb + tt * 16 * SW_KROW + tr_off[m]);
         }
 #pragma unroll
-      for (int m = 0; m < 2; ++m) dW1[m] = dW3[m] = dW2[m] = floatx4{0.f, 0.f, 0.f, 0.f};
-    }
-    const int slot = gsb % SW_RING;
-    const unsigned char* kb = S.kv[slot][0];
-    const unsigned char* vb = S.kv[slot][1];
-
-    // ---- forward of this wave's 16 tokens: A = K W1, B = K W3, Dh = V W2^T ----
-    floatx4 A = {0.f, 0.f, 0.f, 0.f}, Bv = A, Dh = A;
+      for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const bf16x8 kop = *(const bf16x8*)(kb + fwd_off[ks]);
-      const bf16x8 vop = *(const bf16x8*)(vb + fwd_off[ks]);
-      A = mfma16(kop, w1op[ks], A);
-      Bv = mfma16(kop, w3op[ks], Bv);
-      Dh = mfma16(vop, w2op[ks], Dh);
-    }
-    const floatx4 e4 = *(const floatx4*)(&S.eta[slot][16 * w + 4 * g]);
-    bf16x4 daop, dbop, ehop;
+        for (int tt = 0; tt < 2; ++tt) {
+          A[tt] = mfma16(kop[ks][tt], w1op[ks], A[tt]);
+          Bv[tt] = mfma16(kop[ks][tt], w3op[ks], Bv[tt]);
+          Dh[tt] = mfma16(vop[ks][tt], w2op[ks], Dh[tt]);
+        }
+      // ---- elementwise: the operands of the gradient products ----
+      bf16x8 daop, dbop, ehop;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float a = A[r], b = Bv[r];
-      const float sg = 1.0f / (1.0f + __expf(-a));
-      const float sa = a * sg;
-      const float dh = e4[r] * Dh[r];
-      daop[r] = (bf16)(dh * b * sg * (1.0f + a * (1.0f - sg)));
-      dbop[r] = (bf16)(dh * sa);
-      ehop[r] = (bf16)(e4[r] * sa * b);
-    }
-    // lane (g, li) holds rows 4g..4g+3 (tokens) of unit li: exactly the
-    // operand layout of the k = token products below, for every wave
-    *(bf16x4*)(S.dx[0][w] + l * 8) = daop;
-    *(bf16x4*)(S.dx[1][w] + l * 8) = dbop;
-    *(bf16x4*)(S.dx[2][w] + l * 8) = ehop;
-    barrier();
-
-    // ---- gradient rows of this wave over all 64 tokens ----
-    // dW1[d][u] += K^T da, dW3[d][u] += K^T db, dW2[u][d] += eh^T V
-    // transposed K, V blocks: tr[4*k + tb], k = (K, j0), (K, j1), (V, j0), (V, j1)
-    bf16x4 tr[16];
-    lds_tr16_4x4<16 * SW_KROW>(tr, lds_addr(kb) + tr_off[0], lds_addr(kb) + tr_off[1], lds_addr(vb) + tr_off[0],
-                               lds_addr(vb) + tr_off[1]);
+      for (int tt = 0; tt < 2; ++tt) {
+        const floatx4 e4 = *(const floatx4*)(&S.eta[w][slot][16 * tt + 4 * g]);
 #pragma unroll
-    for (int tb = 0; tb < 4; ++tb) {
-      const bf16x4 da = *(const bf16x4*)(S.dx[0][tb] + l * 8);
-      const bf16x4 db = *(const bf16x4*)(S.dx[1][tb] + l * 8);
-      const bf16x4 eh = *(const bf16x4*)(S.dx[2][tb] + l * 8);
+        for (int r = 0; r < 4; ++r) {
+          const float a = A[tt][r], b = Bv[tt][r];
+          const float sg = 1.0f / (1.0f + __expf(-a));
+          const float sa = a * sg;
+          const float dh = e4[r] * Dh[tt][r];
+          daop[4 * tt + r] = (bf16)(dh * b * sg * (1.0f + a * (1.0f - sg)));
+          dbop[4 * tt + r] = (bf16)(dh * sa);
+          ehop[4 * tt + r] = (bf16)(e4[r] * sa * b);
+        }
+      }
+      // ---- partial chunk gradients over the 32 tokens ----
+      // dW1[d][u] += K^T da, dW3[d][u] += K^T db, dW2[u][d] += eh^T V
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        dW1[j] = mfma16k16(tr[4 * j + tb], da, dW1[j]);
-        dW3[j] = mfma16k16(tr[4 * j + tb], db, dW3[j]);
-        dW2[j] = mfma16k16(eh, tr[8 + 4 * j + tb], dW2[j]);
+      for (int m = 0; m < 8; ++m) {
+        const bf16x8 kt = join(ktr[m][0], ktr[m][1]);
+        const bf16x8 vt = join(vtr[m][0], vtr[m][1]);
+        dW1[m] = mfma16(kt, daop, dW1[m]);
+        dW3[m] = mfma16(kt, dbop, dW3[m]);
+        dW2[m] = mfma16(ehop, vt, dW2[m]);
       }
     }
 
-    const bool chunk_end = (i == nsb - 1) || (gsb == total - 1);
-    if (!chunk_end) continue;
-
-    // ---- end of chunk: each wave adds its own rows, then normalise ----
+    // ---- end of chunk: the waves add their partial gradients in a fixed order, then normalise ----
     // dW1 lane layout: [d = 16m + 4g + r][u = li]; dW2: [u = 4g + r][d = 16m + li]
+    for (int k = 0; k < SW_WAVES; ++k) {
+      if (w == k) {
+        floatx4 o1[8], o3[8], o2[8];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int m = 2 * w + j;
+        for (int m = 0; m < 8; ++m) {
+          const int f = ((m * 4 + g) * 16 + li) * 4;   // = w13i(16m + 4g, li) = w2i(4g, 16m + li)
+          o1[m] = *(const floatx4*)(S.w1 + f);
+          o3[m] = *(const floatx4*)(S.w3 + f);
+          o2[m] = *(const floatx4*)(S.w2 + f);
+        }
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        S.w1[(16 * m + 4 * g + r) * NS + li] += dW1[j][r];
-        S.w3[(16 * m + 4 * g + r) * NS + li] += dW3[j][r];
-        S.w2[(4 * g + r) * D + 16 * m + li] += dW2[j][r];
+        for (int m = 0; m < 8; ++m) {
+          const int f = ((m * 4 + g) * 16 + li) * 4;
+          *(floatx4*)(S.w1 + f) = o1[m] + dW1[m];
+          *(floatx4*)(S.w3 + f) = o3[m] + dW3[m];
+          *(floatx4*)(S.w2 + f) = o2[m] + dW2[m];
+        }
       }
+      __syncthreads();
     }
-    __syncthreads();
     // W1, W3: unit columns over d, local (waves 0 and 1)
     if (w < 2) {
       float* Wm = w == 0 ? S.w1 : S.w3;
       const int u = l & 15, r0 = (l >> 4) * 32;
       float ss = 0.f;
 #pragma unroll 8
-      for (int r = 0; r < 32; ++r) ss = fmaf(Wm[(r0 + r) * NS + u], Wm[(r0 + r) * NS + u], ss);
+      for (int r = 0; r < 32; ++r) ss = fmaf(Wm[w13i(r0 + r, u)], Wm[w13i(r0 + r, u)], ss);
       ss += __shfl_xor(ss, 16);
       ss += __shfl_xor(ss, 32);
       const float inv = 1.0f / fmaxf(sqrtf(ss), 1e-12f);
 #pragma unroll 8
-      for (int r = 0; r < 32; ++r) Wm[(r0 + r) * NS + u] *= inv;
-    } else {
+      for (int r = 0; r < 32; ++r) Wm[w13i(r0 + r, u)] *= inv;
+    } else if (w < 4) {
       // W2 column d: partial sum of squares over this slice's units
       const int d = (w - 2) * 64 + l;
       float ss = 0.f;
 #pragma unroll
-      for (int u = 0; u < NS; ++u) ss = fmaf(S.w2[u * D + d], S.w2[u * D + d], ss);
+      for (int u = 0; u < NS; ++u) ss = fmaf(S.w2[w2i(u, d)], S.w2[w2i(u, d)], ss);
       __hip_atomic_store(&ss2[(((size_t)bh * 2 + (c & 1)) * SW_NSL + sl) * D + d], ss, __ATOMIC_RELAXED,
                          __HIP_MEMORY_SCOPE_AGENT);
     }
@@ -315,7 +359,7 @@ __global__ __launch_bounds__(256, 1) void swiglu_recur_kernel(
       }
     }
     __syncthreads();
-    if (w >= 2) {
+    if (w >= 2 && w < 4) {
       const int d = (w - 2) * 64 + l;
       float ss = 0.f;
       for (int s = 0; s < SW_NSL; ++s)
@@ -323,22 +367,23 @@ __global__ __launch_bounds__(256, 1) void swiglu_recur_kernel(
                                 __HIP_MEMORY_SCOPE_AGENT);
       const float inv = 1.0f / fmaxf(sqrtf(ss), 1e-12f);
 #pragma unroll
-      for (int u = 0; u < NS; ++u) S.w2[u * D + d] *= inv;
+      for (int u = 0; u < NS; ++u) S.w2[w2i(u, d)] *= inv;
     }
     __syncthreads();
     if (c + 1 < nchunks) store_state(c + 1);
   }
+  wait_vm<0>();
 
   // ---- final weights, packed W1 | W3 | W2 ----
   float* Wo = Wout + (size_t)bh * 3 * D * DH;
-  for (int i = tid; i < D * NS; i += 256) {
+  for (int i = tid; i < D * NS; i += NT) {
     const int d = i / NS, u = i % NS;
-    Wo[(size_t)d * DH + u0 + u] = S.w1[i];
-    Wo[(size_t)D * DH + (size_t)d * DH + u0 + u] = S.w3[i];
+    Wo[(size_t)d * DH + u0 + u] = S.w1[w13i(d, u)];
+    Wo[(size_t)D * DH + (size_t)d * DH + u0 + u] = S.w3[w13i(d, u)];
   }
-  for (int i = tid; i < NS * D; i += 256) {
+  for (int i = tid; i < NS * D; i += NT) {
     const int u = i / D, d = i % D;
-    Wo[(size_t)2 * D * DH + (size_t)(u0 + u) * D + d] = S.w2[i];
+    Wo[(size_t)2 * D * DH + (size_t)(u0 + u) * D + d] = S.w2[w2i(u, d)];
   }
 }
 
@@ -546,7 +591,7 @@ hipError_t launch_large_chunk_swiglu(const LargeChunkArgs& a, hipStream_t stream
   int dev = 0, ncu = 0, per_cu = 0;
   if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
   if ((e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
-  if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)swiglu_recur_kernel, 256, lds_r)) !=
+  if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)swiglu_recur_kernel, SW_WAVES * 64, lds_r)) !=
       hipSuccess)
     return e;
   const int heads_per_launch = (per_cu * ncu) / SW_NSL;
@@ -562,7 +607,7 @@ hipError_t launch_large_chunk_swiglu(const LargeChunkArgs& a, hipStream_t stream
     int Ti = T, ci = chunk, nci = nchunks, hi = h0;
     void* args[] = {(void*)&Kp, (void*)&Vp, (void*)&Ep, (void*)&W0p, (void*)&Wo, (void*)&states, (void*)&ss2,
                     (void*)&counters, (void*)&err, (void*)&Ti, (void*)&ci, (void*)&nci, (void*)&hi};
-    e = hipLaunchCooperativeKernel((const void*)swiglu_recur_kernel, dim3(nh * SW_NSL), dim3(256), args,
+    e = hipLaunchCooperativeKernel((const void*)swiglu_recur_kernel, dim3(nh * SW_NSL), dim3(SW_WAVES * 64), args,
                                    (unsigned)lds_r, stream);
     if (e != hipSuccess) return e;
   }
