@@ -13,9 +13,9 @@
 // bf16 design (gfx950): the sequence of each head is cut into P segments of
 // whole 64-token tiles so that heads x segments cover the compute units.
 //  1. pt_incr_kernel<D>: for every segment but the last, its state
-//     increment dS_s = K_s^T diag(eta_s) V_s (fp32) into the workspace
-//     (pt_seg_scan_kernel<D> turns them into start states when there are
-//     many segments);
+//     increment dS_s = K_s^T diag(eta_s) V_s (fp32) into the workspace, the
+//     first one as W0 + dS_0 (pt_seg_scan_kernel<D> turns plain increments
+//     into start states when there are many segments);
 //  2. pt_seg_kernel<D>: segment s starts from
 //     S = W0 + sum_{s' < s} dS_s' and runs the chunked form over its tiles;
 //     the last segment writes W_out.
@@ -266,6 +266,16 @@ __device__ __forceinline__ void seg_wave(const SegArgs& A, unsigned char* smem, 
     for (int k = 0; k < Cfg::MAT_LOADS; ++k) buf_store16(ro, gofs[k], v[k]);
   };
 
+  // The first two tiles go out to LDS first; the loads of the start state
+  // (registers only) follow, so both are in flight together.  (Compiler-issued
+  // loads after the asynchronous copies only make its own waits conservative.)
+#pragma unroll
+  for (int k = 0; k < Cfg::STAGES - 1; ++k)
+    if (nt > 0) {
+      issue_q(k);
+      issue_kve(k);
+    }
+
   // ---- state: S[m][r] = S[seg_srow(m, g, r)][16W + li] ----
   floatx4 S[MT];
   const floatx4* pp = A.part + ((size_t)bh * nseg * NW + W) * MT * 64 + l;   // slot 0 of this head
@@ -274,51 +284,34 @@ __device__ __forceinline__ void seg_wave(const SegArgs& A, unsigned char* smem, 
     // start state of this segment, prepared by pt_seg_scan_kernel in the same fragment layout
 #pragma unroll
     for (int m = 0; m < MT; ++m) S[m] = pp[(size_t)s * SLOT + m * 64];
-  } else {
-    // W0 [D][D] fp32 -> LDS with coalesced 16-byte copies (the ring is still empty), then this lane's
-    // fragment; the increments of earlier segments are added, PRO_BATCH segments per memory round trip
+  } else if (s == 0) {
     const float* W0h = A.W0 + (size_t)bh * D * D;
-    const __amdgpu_buffer_rsrc_t rw = make_rsrc(W0h, (long long)D * D * 4);
-#pragma unroll
-    for (int k = 0; k < D * D * 4 / 1024 / NW; ++k) {
-      const unsigned b = (unsigned)((W * (D * D * 4 / 1024 / NW) + k) * 1024);
-      dma16(rw, b + 16 * l, smem + b);
-    }
-    constexpr int PB = Cfg::PRO_BATCH;
-    floatx4 d[PB][MT];            // increments of segments s0..s0+PB-1 (clamped; only those < s are added)
-    auto load_incr = [&](int s0) {
-#pragma unroll
-      for (int k = 0; k < PB; ++k) {
-        const int sp = min(s0 + k, max(s - 1, 0));
-#pragma unroll
-        for (int m = 0; m < MT; ++m) d[k][m] = pp[(size_t)sp * SLOT + m * 64];
-      }
-    };
-    if (s > 0) load_incr(0);      // in flight together with the W0 copy
-    wait_vm_barrier<0>();
-    const float* wl = (const float*)smem;
 #pragma unroll
     for (int m = 0; m < MT; ++m)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) S[m][r] = wl[seg_srow(m, g, r) * D + 16 * W + li];
+      for (int r = 0; r < 4; ++r) S[m][r] = W0h[seg_srow(m, g, r) * D + 16 * W + li];
+  } else {
+    // slot 0 holds W0 + dS_0 (the increment pass adds W0), slots 1.. hold dS_1..; the slots of the
+    // earlier segments are added PRO_BATCH per memory round trip
+    constexpr int PB = Cfg::PRO_BATCH;
+#pragma unroll
+    for (int m = 0; m < MT; ++m) S[m] = floatx4{0.f, 0.f, 0.f, 0.f};
     for (int s0 = 0; s0 < s; s0 += PB) {
-      if (s0 > 0) load_incr(s0);
+      floatx4 d[PB][MT];          // slots s0..s0+PB-1 (clamped; only those < s are added)
+#pragma unroll
+      for (int k = 0; k < PB; ++k) {
+        const int sp = min(s0 + k, s - 1);
+#pragma unroll
+        for (int m = 0; m < MT; ++m) d[k][m] = pp[(size_t)sp * SLOT + m * 64];
+      }
 #pragma unroll
       for (int k = 0; k < PB; ++k)
         if (s0 + k < s)
 #pragma unroll
           for (int m = 0; m < MT; ++m) S[m] += d[k][m];
     }
-    barrier();                    // everyone has read W0 before the ring overwrites it
   }
 
-
-#pragma unroll
-  for (int k = 0; k < Cfg::STAGES - 1; ++k)
-    if (nt > 0) {
-      issue_q(k);
-      issue_kve(k);
-    }
   static_assert(Cfg::STAGES == 3, "the vmcnt waits below count the loads of two tiles in flight");
   for (int i = 0; i < nt; ++i) {
     // Tile i has landed once only later-issued loads (and output stores) may be outstanding: per
@@ -585,6 +578,13 @@ __global__ __launch_bounds__(2 * D / 16 * WAVE, 1) void pt_incr_kernel(SegArgs A
     }
   }
   wait_vm<0>();
+  if (!A.scanned && s == 0) {      // the first slot carries W0 as well: later segments start from the slot sums
+    const float* W0h = A.W0 + (size_t)bh * D * D;
+#pragma unroll
+    for (int j = 0; j < MH; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) S[j][r] += W0h[seg_srow(h * MH + j, g, r) * D + 16 * c + li];
+  }
   floatx4* pp = A.part + (((size_t)bh * nseg + s) * NC + c) * MT * 64 + l;
 #pragma unroll
   for (int j = 0; j < MH; ++j) pp[(h * MH + j) * 64] = S[j];
