@@ -185,11 +185,14 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, lo
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, 0x00020000);
 }
 // 16 bytes per lane from a buffer straight into LDS (lane l -> lds_wave_base + 16*l).
+// STREAM: non-temporal load (data read once).
+template <bool STREAM = false>
 __device__ __forceinline__ void buf2lds16(__amdgpu_buffer_rsrc_t r, unsigned voff, void* lds_wave_base) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(uintptr_t)lds_wave_base, 16, voff, 0, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(uintptr_t)lds_wave_base, 16, voff, 0, 0, STREAM ? 2 : 0);
 }
+template <bool STREAM = false>
 __device__ __forceinline__ void buf2lds4(__amdgpu_buffer_rsrc_t r, unsigned voff, void* lds_wave_base) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(uintptr_t)lds_wave_base, 4, voff, 0, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(uintptr_t)lds_wave_base, 4, voff, 0, 0, STREAM ? 2 : 0);
 }
 // The same direct-to-LDS loads issued from inline asm.  The compiler then
 // does not see that LDS is written asynchronously and adds no waits of its

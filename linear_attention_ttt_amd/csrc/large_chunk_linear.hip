@@ -79,8 +79,8 @@ __global__ __launch_bounds__(256, 4) void lact_delta_kernel(const bf16* __restri
       const int row = p / (D / 8), col = (p % (D / 8)) * 8;
       const int t = t0 + row;
       const int tc = min(t, s1 - 1);
-      kreg[k] = *(const uint4*)(Kh + (size_t)tc * D + col);
-      vreg[k] = *(const uint4*)(Vh + (size_t)tc * D + col);
+      kreg[k] = __builtin_bit_cast(uint4, __builtin_nontemporal_load((const u32x4*)(Kh + (size_t)tc * D + col)));
+      vreg[k] = __builtin_bit_cast(uint4, __builtin_nontemporal_load((const u32x4*)(Vh + (size_t)tc * D + col)));
       ereg[k] = t < s1 ? Eh[tc] : 0.f;
     }
   };
@@ -298,7 +298,7 @@ __global__ __launch_bounds__(256, 2) void lact_read_kernel(const bf16* __restric
     const __amdgpu_buffer_rsrc_t r = make_rsrc(Qh + (size_t)(t0 + 64 * i) * D, rem * Cfg::ROWB);
     unsigned char* dst = ring + (i % LR_STAGES) * Cfg::QW_BYTES;
 #pragma unroll
-    for (int k = 0; k < Cfg::QI; ++k) buf2lds16(r, qoff[k], dst + k * 1024);
+    for (int k = 0; k < Cfg::QI; ++k) buf2lds16<true>(r, qoff[k], dst + k * 1024);
   };
 #pragma unroll
   for (int i = 0; i < LR_STAGES - 1; ++i) issue(i);
