@@ -76,6 +76,11 @@ __device__ __forceinline__ int sw_swz(int row) { return (int)((0x159DAE2673FBC84
 __device__ __forceinline__ int w13i(int d, int u) { return ((d >> 2) * 16 + u) * 4 + (d & 3); }
 __device__ __forceinline__ int w2i(int u, int d) { return (((d >> 4) * 4 + (u >> 2)) * 16 + (d & 15)) * 4 + (u & 3); }
 
+// logistic function with the hardware reciprocal (about 1 ulp): its value
+// only feeds bf16 operands or a bf16 hi + lo pair, so a correctly rounded
+// division buys nothing here
+__device__ __forceinline__ float sigmoid_fast(float a) { return __builtin_amdgcn_rcpf(1.0f + __expf(-a)); }
+
 __device__ __forceinline__ void split_store8(bf16* hi, bf16* lo, const float* f) {
   bf16x8 h, l;
 #pragma unroll
@@ -282,7 +287,7 @@ __global__ __launch_bounds__(SW_WAVES * 64, 1) void swiglu_recur_kernel(
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const float a = A[tt][r], b = Bv[tt][r];
-          const float sg = 1.0f / (1.0f + __expf(-a));
+          const float sg = sigmoid_fast(a);
           const float sa = a * sg;
           const float dh = e4[r] * Dh[tt][r];
           daop[4 * tt + r] = (bf16)(dh * b * sg * (1.0f + a * (1.0f - sg)));
@@ -392,12 +397,17 @@ __global__ __launch_bounds__(SW_WAVES * 64, 1) void swiglu_recur_kernel(
 // column index) so that H^T from one product is directly the B operand of
 // the next.
 // ---------------------------------------------------------------------------
+// Weight slices in LDS without padding: a W1T/W3T row (one unit, 256 bytes)
+// has its 16-byte pieces at c ^ sw_swz(row); a W2T row (32 units, 64 bytes)
+// has its 8-byte pieces at c ^ ((row >> 2) & 3).  Both make the operand reads
+// (16 rows per 16 lanes) conflict-free.
 struct ReadLds {
-  unsigned char w13[2][4][SW_US * (SW_D * 2 + 16)];   // W1T hi, W1T lo, W3T hi, W3T lo; padded rows
-  unsigned char w2[2][2][SW_D * (SW_US * 2 + 8)];     // W2T hi, lo: [n][32 units], padded rows
+  unsigned char w13[2][4][SW_US * SW_D * 2];   // W1T hi, W1T lo, W3T hi, W3T lo: [32 units][128 d]
+  unsigned char w2[2][2][SW_D * SW_US * 2];    // W2T hi, lo: [n][32 units]
 };
-constexpr int RW13_ROW = SW_D * 2 + 16;
-constexpr int RW2_ROW = SW_US * 2 + 8;
+constexpr int RW13_ROW = SW_D * 2;
+constexpr int RW2_ROW = SW_US * 2;
+__device__ __forceinline__ int w2_swz(int row) { return (row >> 2) & 3; }
 
 __global__ __launch_bounds__(512, 1) void swiglu_read_kernel(const bf16* __restrict__ Q,
                                                              const bf16* __restrict__ states, bf16* __restrict__ O,
@@ -422,7 +432,8 @@ __global__ __launch_bounds__(512, 1) void swiglu_read_kernel(const bf16* __restr
   for (int tt = 0; tt < 2; ++tt) {
     const int t = min(t0 + 32 * w + 16 * tt + li, cend - 1);
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) qop[tt][ks] = *(const bf16x8*)(Qh + (size_t)t * D + 32 * ks + 8 * g);
+    for (int ks = 0; ks < 4; ++ks)
+      qop[tt][ks] = __builtin_bit_cast(bf16x8, __builtin_nontemporal_load((const u32x4*)(Qh + (size_t)t * D + 32 * ks + 8 * g)));
   }
 
   // weight slice staging: 6 x 16 bytes per thread (512 threads)
@@ -444,14 +455,14 @@ __global__ __launch_bounds__(512, 1) void swiglu_read_kernel(const bf16* __restr
   auto put13 = [&](int k, int buf, uint4 v) {
     const int p = k * 512 + tid;
     const int plane = p >> 9, row = (p >> 4) & 31, pc = p & 15;
-    *(uint4*)(L.w13[buf][plane] + row * RW13_ROW + pc * 16) = v;
+    *(uint4*)(L.w13[buf][plane] + row * RW13_ROW + ((pc ^ sw_swz(row)) << 4)) = v;
   };
   auto put2 = [&](int k, int buf, uint4 v) {
     const int p = k * 512 + tid;
     const int plane = p >> 9, n = (p >> 2) & 127, pc = p & 3;
-    unsigned char* dst = L.w2[buf][plane] + n * RW2_ROW + pc * 16;
-    *(uint2*)dst = uint2{v.x, v.y};
-    *(uint2*)(dst + 8) = uint2{v.z, v.w};
+    unsigned char* dst = L.w2[buf][plane] + n * RW2_ROW;
+    *(uint2*)(dst + (((2 * pc) ^ w2_swz(n)) << 3)) = uint2{v.x, v.y};
+    *(uint2*)(dst + (((2 * pc + 1) ^ w2_swz(n)) << 3)) = uint2{v.z, v.w};
   };
   auto store_slice = [&](int buf) {
     put13(0, buf, wr0); put13(1, buf, wr1); put13(2, buf, wr2); put13(3, buf, wr3);
@@ -479,7 +490,7 @@ __global__ __launch_bounds__(512, 1) void swiglu_read_kernel(const bf16* __restr
     for (int ut = 0; ut < 2; ++ut)
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        const int off = (16 * ut + li) * RW13_ROW + (32 * ks + 8 * g) * 2;
+        const int off = (16 * ut + li) * RW13_ROW + (((4 * ks + g) ^ sw_swz(16 * ut + li)) << 4);
         const bf16x8 w1h = *(const bf16x8*)(L.w13[buf][0] + off);
         const bf16x8 w1l = *(const bf16x8*)(L.w13[buf][1] + off);
         const bf16x8 w3h = *(const bf16x8*)(L.w13[buf][2] + off);
@@ -502,7 +513,7 @@ __global__ __launch_bounds__(512, 1) void swiglu_read_kernel(const bf16* __restr
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const float a = at[ut][tt][r];
-          const float h = a / (1.0f + __expf(-a)) * bt[ut][tt][r];
+          const float h = a * sigmoid_fast(a) * bt[ut][tt][r];
           const bf16 hb = (bf16)h;
           hh[tt][4 * ut + r] = hb;
           hl[tt][4 * ut + r] = (bf16)(h - (float)hb);
@@ -512,8 +523,9 @@ __global__ __launch_bounds__(512, 1) void swiglu_read_kernel(const bf16* __restr
     for (int nt = 0; nt < 8; ++nt) {
       const unsigned char* rowh = L.w2[buf][0] + (16 * nt + li) * RW2_ROW;
       const unsigned char* rowl = L.w2[buf][1] + (16 * nt + li) * RW2_ROW;
-      const bf16x8 w2h = join(*(const bf16x4*)(rowh + 8 * g), *(const bf16x4*)(rowh + 32 + 8 * g));
-      const bf16x8 w2l = join(*(const bf16x4*)(rowl + 8 * g), *(const bf16x4*)(rowl + 32 + 8 * g));
+      const int p0 = (g ^ w2_swz(16 * nt + li)) << 3, p1 = ((4 + g) ^ w2_swz(16 * nt + li)) << 3;
+      const bf16x8 w2h = join(*(const bf16x4*)(rowh + p0), *(const bf16x4*)(rowh + p1));
+      const bf16x8 w2l = join(*(const bf16x4*)(rowl + p0), *(const bf16x4*)(rowl + p1));
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
         oacc[nt][tt] = mfma16(w2h, hh[tt], oacc[nt][tt]);
