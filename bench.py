@@ -98,7 +98,7 @@ def run_workload(name: str, steps: int, warmup: int, flush_mb: int):
     # another, so that the last-level cache and the L2s hold neither the inputs nor dirty lines whose
     # write-back would otherwise land in the next timed step
     flush = torch.empty(flush_mb << 20, dtype=torch.uint8, device=dev)
-    flush_rd = torch.ones((flush_mb << 20) // 4, dtype=torch.int32, device=dev)
+    flush_rd = torch.ones((flush_mb << 20) // 4, dtype=torch.float32, device=dev)   # fp32: summed without a converted copy
 
     def evict(v):
         flush.fill_(v)
