@@ -116,7 +116,7 @@ def run_workload(name: str, steps: int, warmup: int, flush_mb: int):
                                 ws.numel(), sptr)
         else:
             st = la.forward_timed_raw(*ptrs, s["chunk"], s["mode"], desc, O.data_ptr(), Wout.data_ptr(),
-                                      ws.data_ptr(), ws.numel(), sptr, timing[0].cuda_event, timing[1].cuda_event)
+                                      ws.data_ptr(), ws.numel(), sptr, timing[0].handle, timing[1].handle)
         if st != 0:
             raise RuntimeError(f"ttt_la_forward failed: {la.status_string(st)}")
 
@@ -129,11 +129,11 @@ def run_workload(name: str, steps: int, warmup: int, flush_mb: int):
     torch.cuda.synchronize()
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    # recorded by the library around the dominant kernel of each call, on the same stream
-    kstarts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    kends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    for ev in kstarts + kends:      # torch creates its events lazily, on the first record
-        ev.record(stream)
+    # recorded by the library around the dominant kernel of each call, on the same stream; fence-free
+    # events (ttt_la_event_create), so the timestamps between the kernels do not write back and
+    # invalidate the caches inside the step (an ordinary event there costs several microseconds)
+    kstarts = [la.TimingEvent() for _ in range(steps)]
+    kends = [la.TimingEvent() for _ in range(steps)]
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     for i in range(steps):
@@ -144,7 +144,7 @@ def run_workload(name: str, steps: int, warmup: int, flush_mb: int):
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms = np.array([a.elapsed_time(b) for a, b in zip(starts, ends)])
-    kms = np.array([a.elapsed_time(b) for a, b in zip(kstarts, kends)])
+    kms = np.array([a.elapsed_ms(b) for a, b in zip(kstarts, kends)])
     nbytes, flops = algorithmic(s)
     kname, kunits, kbound = dominant_kernel(s)
     kmean_s = float(kms.mean()) * 1e-3

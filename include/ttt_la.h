@@ -138,8 +138,9 @@ int ttt_la_forward(const void* Q, const void* K, const void* V, const float* eta
  *                  output pass over the segments; fp32: the whole kernel)
  *   large-chunk    the chunk-update kernel (streams K and V)
  *   SwiGLU         the recurrence over the chunks
- * ev_start, ev_stop: hipEvent_t created by the caller (hipEventCreate), or
- * NULL to skip; the library only records them.  Nothing is recorded when
+ * ev_start, ev_stop: hipEvent_t created by the caller (ttt_la_event_create
+ * for fence-free timestamps, or hipEventCreate), or NULL to skip; the
+ * library only records them.  Nothing is recorded when
  * the call returns an error before enqueueing, nor by large-chunk linear
  * with T = 0 (no chunk to update).
  */
@@ -147,6 +148,27 @@ int ttt_la_forward_timed(const void* Q, const void* K, const void* V, const floa
                          const float* W0, int64_t chunk, int32_t mode, const ttt_la_desc* desc,
                          void* O, float* W_out, void* workspace, size_t workspace_bytes,
                          void* stream, void* ev_start, void* ev_stop);
+
+/* Timing events for ttt_la_forward_timed and for timing calls on a stream.
+ * ttt_la_event_create makes a hipEvent_t (returned through *event) that
+ * records a timestamp without the system-scope memory fence an ordinary
+ * event performs (that fence writes back and invalidates caches, which costs
+ * several microseconds between two kernels and perturbs the work after it).
+ * Such an event only serves timing: wait for the stream (or a fenced event)
+ * before reading it with ttt_la_event_elapsed_ms.
+ *   ttt_la_event_create     event != NULL; TTT_LA_ERR_NULL otherwise,
+ *                           TTT_LA_ERR_HIP if HIP fails.  The caller owns
+ *                           the event and frees it with ttt_la_event_destroy.
+ *   ttt_la_event_record     records `event` on `stream` (hipStream_t, NULL =
+ *                           the null stream).
+ *   ttt_la_event_elapsed_ms *ms = time from `start` to `stop` in
+ *                           milliseconds; both must have completed.
+ *   ttt_la_event_destroy    frees an event from ttt_la_event_create (NULL
+ *                           is ignored). */
+int ttt_la_event_create(void** event);
+int ttt_la_event_record(void* event, void* stream);
+int ttt_la_event_elapsed_ms(void* start, void* stop, float* ms);
+int ttt_la_event_destroy(void* event);
 
 /* Bytes of device workspace ttt_la_forward needs for this problem (0 if
  * none).  Returns 0 as well for invalid arguments (ttt_la_forward reports

@@ -15,7 +15,7 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["forward", "forward_timed_raw", "workspace_bytes", "TTTLAError", "MODES", "Desc", "lib", "library_path",
+__all__ = ["forward", "forward_timed_raw", "TimingEvent", "workspace_bytes", "TTTLAError", "MODES", "Desc", "lib", "library_path",
            "PER_TOKEN_LINEAR", "LARGE_CHUNK_LINEAR", "LARGE_CHUNK_SWIGLU"]
 
 PER_TOKEN_LINEAR = 0
@@ -65,6 +65,14 @@ def lib() -> ctypes.CDLL:
         L.ttt_la_status_string.restype = ctypes.c_char_p
         L.ttt_la_abi_version.argtypes = []
         L.ttt_la_abi_version.restype = ctypes.c_int
+        L.ttt_la_event_create.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        L.ttt_la_event_create.restype = ctypes.c_int
+        L.ttt_la_event_record.argtypes = [vp, vp]
+        L.ttt_la_event_record.restype = ctypes.c_int
+        L.ttt_la_event_elapsed_ms.argtypes = [vp, vp, ctypes.POINTER(ctypes.c_float)]
+        L.ttt_la_event_elapsed_ms.restype = ctypes.c_int
+        L.ttt_la_event_destroy.argtypes = [vp]
+        L.ttt_la_event_destroy.restype = ctypes.c_int
         _LIB = L
     return _LIB
 
@@ -99,6 +107,34 @@ def forward_timed_raw(Q, K, V, eta, W0, chunk, mode, desc: Desc, O, W_out, works
                                           workspace, int(workspace_bytes_), stream, ev_start, ev_stop))
 
 
+class TimingEvent:
+    """A fence-free timing event from ttt_la_event_create (a raw hipEvent_t in ``.handle``)."""
+
+    def __init__(self):
+        h = ctypes.c_void_p()
+        st = int(lib().ttt_la_event_create(ctypes.byref(h)))
+        if st != 0:
+            raise TTTLAError(st, status_string(st))
+        self.handle = h.value
+
+    def record(self, stream) -> None:
+        st = int(lib().ttt_la_event_record(self.handle, stream))
+        if st != 0:
+            raise TTTLAError(st, status_string(st))
+
+    def elapsed_ms(self, stop: "TimingEvent") -> float:
+        ms = ctypes.c_float()
+        st = int(lib().ttt_la_event_elapsed_ms(self.handle, stop.handle, ctypes.byref(ms)))
+        if st != 0:
+            raise TTTLAError(st, status_string(st))
+        return float(ms.value)
+
+    def __del__(self):
+        if getattr(self, "handle", None) and _LIB is not None:
+            _LIB.ttt_la_event_destroy(self.handle)
+            self.handle = None
+
+
 def forward(Q, K, V, eta, W0, chunk: int, mode, *, out=None, W_out=None, workspace=None, stream=None,
             timing=None):
     """Run the TTT forward pass.
@@ -108,9 +144,11 @@ def forward(Q, K, V, eta, W0, chunk: int, mode, *, out=None, W_out=None, workspa
     linear modes, ``[B,H,3*d*d_h]`` packed W1|W3|W2 for SwiGLU), all
     contiguous CUDA tensors on one device.  Returns ``(O, W_out)``.
     Passing ``W_out=W0`` updates the state in place.  ``timing=(start, stop)``
-    (two ``torch.cuda.Event(enable_timing=True)``) has the library record
-    them around the call's dominant kernel; ``start.elapsed_time(stop)``
-    then gives that kernel's duration."""
+    (two ``TimingEvent`` or two ``torch.cuda.Event(enable_timing=True)``)
+    has the library record them around the call's dominant kernel;
+    ``start.elapsed_ms(stop)`` (``elapsed_time`` for torch events) then gives
+    that kernel's duration.  ``stream`` is a raw hipStream_t (default: torch's
+    current stream)."""
     import torch
 
     m = _mode(mode)
@@ -155,13 +193,16 @@ def forward(Q, K, V, eta, W0, chunk: int, mode, *, out=None, W_out=None, workspa
                              desc, O.data_ptr(), Wo.data_ptr(), ws_ptr, ws_len, st)
     else:
         e0, e1 = timing
-        sobj = torch.cuda.ExternalStream(st) if stream is not None else torch.cuda.current_stream(dev)
-        for ev in (e0, e1):          # torch creates its events lazily, on the first record
-            if not ev.cuda_event:
-                ev.record(sobj)
+        if isinstance(e0, TimingEvent) and isinstance(e1, TimingEvent):
+            h0, h1 = e0.handle, e1.handle
+        else:
+            sobj = torch.cuda.ExternalStream(st) if stream is not None else torch.cuda.current_stream(dev)
+            for ev in (e0, e1):      # torch creates its events lazily, on the first record
+                if not ev.cuda_event:
+                    ev.record(sobj)
+            h0, h1 = e0.cuda_event, e1.cuda_event
         status = forward_timed_raw(Q.data_ptr(), K.data_ptr(), V.data_ptr(), eta.data_ptr(), W0.data_ptr(), chunk,
-                                   m, desc, O.data_ptr(), Wo.data_ptr(), ws_ptr, ws_len, st, e0.cuda_event,
-                                   e1.cuda_event)
+                                   m, desc, O.data_ptr(), Wo.data_ptr(), ws_ptr, ws_len, st, h0, h1)
     if status != 0:
         raise TTTLAError(status, status_string(status))
     return O, Wo

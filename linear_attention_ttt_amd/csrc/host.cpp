@@ -161,4 +161,27 @@ int ttt_la_forward(const void* Q, const void* K, const void* V, const float* eta
                               nullptr, nullptr);
 }
 
+int ttt_la_event_create(void** event) {
+  if (!event) return TTT_LA_ERR_NULL;
+  hipEvent_t e = nullptr;
+  if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess) return TTT_LA_ERR_HIP;
+  *event = (void*)e;
+  return TTT_LA_OK;
+}
+
+int ttt_la_event_record(void* event, void* stream) {
+  if (!event) return TTT_LA_ERR_NULL;
+  return hipEventRecord((hipEvent_t)event, (hipStream_t)stream) == hipSuccess ? TTT_LA_OK : TTT_LA_ERR_HIP;
+}
+
+int ttt_la_event_elapsed_ms(void* start, void* stop, float* ms) {
+  if (!start || !stop || !ms) return TTT_LA_ERR_NULL;
+  return hipEventElapsedTime(ms, (hipEvent_t)start, (hipEvent_t)stop) == hipSuccess ? TTT_LA_OK : TTT_LA_ERR_HIP;
+}
+
+int ttt_la_event_destroy(void* event) {
+  if (!event) return TTT_LA_OK;
+  return hipEventDestroy((hipEvent_t)event) == hipSuccess ? TTT_LA_OK : TTT_LA_ERR_HIP;
+}
+
 }  // extern "C"

@@ -37,7 +37,9 @@ def declared_functions():
 def test_exports_every_declared_symbol():
     L = la.lib()
     names = declared_functions()
-    assert {"ttt_la_forward", "ttt_la_workspace_bytes", "ttt_la_status_string", "ttt_la_abi_version"} <= set(names)
+    assert {"ttt_la_forward", "ttt_la_workspace_bytes", "ttt_la_status_string", "ttt_la_abi_version",
+            "ttt_la_event_create", "ttt_la_event_record", "ttt_la_event_elapsed_ms",
+            "ttt_la_event_destroy"} <= set(names)
     for n in names:
         assert hasattr(L, n), f"{n} not exported"
 
@@ -143,3 +145,13 @@ def test_per_token_workspace():
         5 * 64 * 64 * 4                                         # 5 tiles -> 5 segments of one tile
     assert call(desc=d, mode=0, chunk=64, ws=None, ws_bytes=0) == 8
     assert call(desc=d, mode=0, chunk=64, ws_bytes=n - 1) == 8
+
+
+@needs_lib
+def test_event_helpers_reject_null():
+    # argument checks happen before any HIP call, so they run without a GPU
+    L = la.lib()
+    assert L.ttt_la_event_create(None) == 1
+    assert L.ttt_la_event_record(None, None) == 1
+    assert L.ttt_la_event_elapsed_ms(None, None, None) == 1
+    assert L.ttt_la_event_destroy(None) == 0

@@ -29,3 +29,25 @@ def test_timed_matches_untimed(s):
     ms = e0.elapsed_time(e1)
     print(f"[timed {s['mode']} {s['dtype']}] dominant kernel {ms * 1e3:.1f} us", flush=True)
     assert ms > 0
+
+
+@pytest.mark.gpu
+def test_fence_free_timing_events():
+    """ttt_la_event_create/record/elapsed_ms: fence-free events passed to
+    ttt_la_forward_timed bracket the dominant kernel, which lies inside an
+    ordinary pair of events around the whole call."""
+    s = CASES[0]
+    x = workloads.generate(s, seed=5)
+    t = to_device(x, s)
+    O1, W1 = la.forward(t["Q"], t["K"], t["V"], t["eta"], t["W0"], s["chunk"], s["mode"])
+    stream = torch.cuda.current_stream()
+    k0, k1 = la.TimingEvent(), la.TimingEvent()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    O2, W2 = la.forward(t["Q"], t["K"], t["V"], t["eta"], t["W0"], s["chunk"], s["mode"], timing=(k0, k1))
+    b.record(stream)
+    torch.cuda.synchronize()
+    assert torch.equal(O1.view(torch.int16), O2.view(torch.int16)) and torch.equal(W1, W2)
+    kms, total = k0.elapsed_ms(k1), a.elapsed_time(b)
+    print(f"[fence-free events] kernel {kms * 1e3:.1f} us of {total * 1e3:.1f} us", flush=True)
+    assert 0 < kms <= total
