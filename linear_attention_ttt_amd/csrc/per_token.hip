@@ -13,9 +13,8 @@
 // bf16 design (gfx950): the sequence of each head is cut into P segments of
 // whole 64-token tiles so that heads x segments cover the compute units.
 //  1. pt_incr_kernel<D>: for every segment but the last, its state
-//     increment dS_s = K_s^T diag(eta_s) V_s (fp32) into the workspace, the
-//     first one as W0 + dS_0 (pt_seg_scan_kernel<D> turns plain increments
-//     into start states when there are many segments);
+//     increment dS_s = K_s^T diag(eta_s) V_s (fp32) into the workspace;
+//     pt_seg_scan_kernel<D> turns them into start states in place;
 //  2. pt_seg_kernel<D>: segment s starts from
 //     S = W0 + sum_{s' < s} dS_s' and runs the chunked form over its tiles;
 //     the last segment writes W_out.
@@ -89,7 +88,6 @@ struct SegCfg {
   static constexpr int LDS_BYTES = OFF_P + 2 * P_PLANE;
   static constexpr int WG_PER_CU = (160 * 1024) / LDS_BYTES >= 2 ? 2 : 1;
   static constexpr int WAVES_PER_SIMD = NW * WG_PER_CU / 4;
-  static constexpr int PRO_BATCH = WAVES_PER_SIMD >= 4 ? 2 : 4;   // increments loaded per round trip (registers)
   static constexpr int EPW = C / NW;             // eta values loaded by each wave
   static constexpr int MAT_LOADS = MAT / 1024 / NW;  // 16-byte direct-to-LDS loads per wave per matrix
   static constexpr int LOADS = 3 * MAT_LOADS + 1;
@@ -183,7 +181,6 @@ struct SegArgs {
   bf16* O;
   float* Wout;
   int T, nseg, seg_len;             // segment s covers tokens [s*seg_len, (s+1)*seg_len), whole tiles of both passes
-  int scanned;                      // 1: workspace slot s already holds the start state of segment s
 };
 
 // The program of wave W (wave-uniform).  One program for all waves keeps the
@@ -267,7 +264,7 @@ __device__ __forceinline__ void seg_wave(const SegArgs& A, unsigned char* smem, 
   };
 
   // The first two tiles go out to LDS first; the loads of the start state
-  // (registers only) follow, so both are in flight together.  (Compiler-issued
+  // (one workspace slot, registers only) follow, so both are in flight together.  (Compiler-issued
   // loads after the asynchronous copies only make its own waits conservative.)
 #pragma unroll
   for (int k = 0; k < Cfg::STAGES - 1; ++k)
@@ -280,36 +277,16 @@ __device__ __forceinline__ void seg_wave(const SegArgs& A, unsigned char* smem, 
   floatx4 S[MT];
   const floatx4* pp = A.part + ((size_t)bh * nseg * NW + W) * MT * 64 + l;   // slot 0 of this head
   constexpr int SLOT = NW * MT * 64;                                         // floatx4 per slot
-  if (A.scanned) {
+  if (nseg > 1) {
     // start state of this segment, prepared by pt_seg_scan_kernel in the same fragment layout
 #pragma unroll
     for (int m = 0; m < MT; ++m) S[m] = pp[(size_t)s * SLOT + m * 64];
-  } else if (s == 0) {
+  } else {
     const float* W0h = A.W0 + (size_t)bh * D * D;
 #pragma unroll
     for (int m = 0; m < MT; ++m)
 #pragma unroll
       for (int r = 0; r < 4; ++r) S[m][r] = W0h[seg_srow(m, g, r) * D + 16 * W + li];
-  } else {
-    // slot 0 holds W0 + dS_0 (the increment pass adds W0), slots 1.. hold dS_1..; the slots of the
-    // earlier segments are added PRO_BATCH per memory round trip
-    constexpr int PB = Cfg::PRO_BATCH;
-#pragma unroll
-    for (int m = 0; m < MT; ++m) S[m] = floatx4{0.f, 0.f, 0.f, 0.f};
-    for (int s0 = 0; s0 < s; s0 += PB) {
-      floatx4 d[PB][MT];          // slots s0..s0+PB-1 (clamped; only those < s are added)
-#pragma unroll
-      for (int k = 0; k < PB; ++k) {
-        const int sp = min(s0 + k, s - 1);
-#pragma unroll
-        for (int m = 0; m < MT; ++m) d[k][m] = pp[(size_t)sp * SLOT + m * 64];
-      }
-#pragma unroll
-      for (int k = 0; k < PB; ++k)
-        if (s0 + k < s)
-#pragma unroll
-          for (int m = 0; m < MT; ++m) S[m] += d[k][m];
-    }
   }
 
   static_assert(Cfg::STAGES == 3, "the vmcnt waits below count the loads of two tiles in flight");
@@ -578,13 +555,6 @@ __global__ __launch_bounds__(2 * D / 16 * WAVE, 1) void pt_incr_kernel(SegArgs A
     }
   }
   wait_vm<0>();
-  if (!A.scanned && s == 0) {      // the first slot carries W0 as well: later segments start from the slot sums
-    const float* W0h = A.W0 + (size_t)bh * D * D;
-#pragma unroll
-    for (int j = 0; j < MH; ++j)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) S[j][r] += W0h[seg_srow(h * MH + j, g, r) * D + 16 * c + li];
-  }
   floatx4* pp = A.part + (((size_t)bh * nseg + s) * NC + c) * MT * 64 + l;
 #pragma unroll
   for (int j = 0; j < MH; ++j) pp[(h * MH + j) * 64] = S[j];
@@ -752,11 +722,11 @@ static hipError_t launch_seg(const PerTokenArgs& a, hipStream_t stream, const Ti
   using CfgF = SegCfg<D, seg_tile<D>()>;
   const int BH = (int)(a.B * a.H);
   const SegPlan sp = per_token_seg_plan(BH, a.T, D);
-  // With few segments every workgroup adds the earlier increments itself (one or two memory round
-  // trips); with many, a scan kernel turns them into start states first (linear instead of
-  // quadratic traffic, at the price of one more kernel boundary).
+  // The scan kernel turns the increments into start states, so each output workgroup loads one
+  // slot (measured: cheaper than summing the earlier slots in every workgroup's prologue, the
+  // increments are still in the last-level cache when the scan reads them).
   SegArgs A{(const bf16*)a.Q, (const bf16*)a.K, (const bf16*)a.V, a.eta, a.W0, (floatx4*)a.ws,
-            (bf16*)a.O, a.W_out, (int)a.T, sp.nseg, sp.seg_len, sp.nseg > 8 ? 1 : 0};
+            (bf16*)a.O, a.W_out, (int)a.T, sp.nseg, sp.seg_len};
   hipError_t e;
   if (sp.nseg > 1) {
     auto kd = pt_incr_kernel<D>;
@@ -765,11 +735,9 @@ static hipError_t launch_seg(const PerTokenArgs& a, hipStream_t stream, const Ti
       return e;
     hipLaunchKernelGGL(kd, dim3(BH * (sp.nseg - 1)), dim3(CfgD::THREADS), CfgD::LDS_BYTES, stream, A);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    if (A.scanned) {
-      hipLaunchKernelGGL(pt_seg_scan_kernel<D>, dim3(BH * (D * D / 4 / 256)), dim3(256), 0, stream, a.W0,
-                         (floatx4*)a.ws, sp.nseg);
-      if ((e = hipGetLastError()) != hipSuccess) return e;
-    }
+    hipLaunchKernelGGL(pt_seg_scan_kernel<D>, dim3(BH * (D * D / 4 / 256)), dim3(256), 0, stream, a.W0,
+                       (floatx4*)a.ws, sp.nseg);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   auto kf = pt_seg_kernel<D, seg_tile<D>()>;
   if ((e = hipFuncSetAttribute((const void*)kf, hipFuncAttributeMaxDynamicSharedMemorySize, CfgF::LDS_BYTES)) !=
