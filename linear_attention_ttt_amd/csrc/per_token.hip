@@ -226,41 +226,44 @@ __device__ __forceinline__ void seg_wave(const SegArgs& A, unsigned char* smem, 
   // output fragment (row 16ib + li, columns 16W + 4g..+3) in the swizzled staging rows
   const unsigned ofr = (unsigned)(li * ROWB + (((2 * W + (g >> 1)) ^ seg_swz<D>(li)) << 4) + (g & 1) * 8);
 
+  // One buffer view per matrix for the whole segment (rows past its end read 0, stores there are
+  // dropped); a tile is addressed by its 32-bit offset.
+  const long long tok0 = (long long)c0 * C;
+  const long long seg_toks = seg_end > tok0 ? seg_end - tok0 : 0;
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(Qh + (nt > 0 ? tok0 * D : 0), seg_toks * ROWB);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kh + (nt > 0 ? tok0 * D : 0), seg_toks * ROWB);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vh + (nt > 0 ? tok0 * D : 0), seg_toks * ROWB);
+  const __amdgpu_buffer_rsrc_t re = make_rsrc(Eh + (nt > 0 ? tok0 : 0), seg_toks * 4);
+  const __amdgpu_buffer_rsrc_t ro = make_rsrc(Oh + (nt > 0 ? tok0 * D : 0), seg_toks * ROWB);
+  const unsigned eofs = (unsigned)((W * Cfg::EPW + l) * 4);
   // Tile i of the segment into ring slot i % STAGES (empty past the segment), in two parts: Q, and
   // K, V, eta.  The parts are issued at different points of a tile so that the workgroup's vector
   // memory instructions do not all queue at the tile boundary.
   auto issue_q = [&](int i) {
-    const long long t0 = (long long)(c0 + i) * C;
-    const long long rem = seg_end - t0;
     unsigned char* st = smem + (i % Cfg::STAGES) * Cfg::STAGE + W * Cfg::MAT_LOADS * 1024;
-    const __amdgpu_buffer_rsrc_t rq = make_rsrc(Qh + (rem > 0 ? t0 * D : 0), rem * ROWB);
+    const unsigned t = (unsigned)i * Cfg::MAT;
 #pragma unroll
-    for (int k = 0; k < Cfg::MAT_LOADS; ++k) dma16<PT_STREAM>(rq, gofs[k], st + k * 1024);
+    for (int k = 0; k < Cfg::MAT_LOADS; ++k) dma16<PT_STREAM>(rq, t + gofs[k], st + k * 1024);
   };
   auto issue_kve = [&](int i) {
-    const long long t0 = (long long)(c0 + i) * C;
-    const long long rem = seg_end - t0;
     unsigned char* st = smem + (i % Cfg::STAGES) * Cfg::STAGE + W * Cfg::MAT_LOADS * 1024;
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kh + (rem > 0 ? t0 * D : 0), rem * ROWB);
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vh + (rem > 0 ? t0 * D : 0), rem * ROWB);
+    const unsigned t = (unsigned)i * Cfg::MAT;
 #pragma unroll
-    for (int k = 0; k < Cfg::MAT_LOADS; ++k) dma16<PT_STREAM>(rk, gofs[k], st + Cfg::OFF_K + k * 1024);
+    for (int k = 0; k < Cfg::MAT_LOADS; ++k) dma16<PT_STREAM>(rk, t + gofs[k], st + Cfg::OFF_K + k * 1024);
 #pragma unroll
-    for (int k = 0; k < Cfg::MAT_LOADS; ++k) dma16<PT_STREAM>(rv, gofs[k], st + Cfg::OFF_V + k * 1024);
-    const __amdgpu_buffer_rsrc_t re = make_rsrc(Eh + (rem > 0 ? t0 : 0), rem * 4);
+    for (int k = 0; k < Cfg::MAT_LOADS; ++k) dma16<PT_STREAM>(rv, t + gofs[k], st + Cfg::OFF_V + k * 1024);
     unsigned char* ed = smem + (i % Cfg::STAGES) * Cfg::STAGE + Cfg::OFF_E + W * Cfg::EPW * 4;
-    if (l < Cfg::EPW) dma4<PT_STREAM>(re, (unsigned)((W * Cfg::EPW + l) * 4), ed);
+    if (l < Cfg::EPW) dma4<PT_STREAM>(re, (unsigned)i * (C * 4) + eofs, ed);
   };
   // rows of tile i's outputs staged in its (dead) V region -> HBM, 16 bytes per lane, whole rows
   auto write_out = [&](int i) {
-    const long long t0 = (long long)(c0 + i) * C;
     const unsigned char* st = smem + (i % Cfg::STAGES) * Cfg::STAGE + Cfg::OFF_V;
-    const __amdgpu_buffer_rsrc_t ro = make_rsrc(Oh + t0 * D, ((long long)T - t0) * ROWB);
+    const unsigned t = (unsigned)i * Cfg::MAT;
     u32x4 v[Cfg::MAT_LOADS];
 #pragma unroll
     for (int k = 0; k < Cfg::MAT_LOADS; ++k) v[k] = *(const u32x4*)(st + lofs[k]);
 #pragma unroll
-    for (int k = 0; k < Cfg::MAT_LOADS; ++k) buf_store16(ro, gofs[k], v[k]);
+    for (int k = 0; k < Cfg::MAT_LOADS; ++k) buf_store16(ro, t + gofs[k], v[k]);
   };
 
   // The first two tiles go out to LDS first; the loads of the start state
@@ -451,18 +454,18 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, D / 16 * WAVE),
 
 // Segment increments dS_s = K_s^T diag(eta_s) V_s for every segment but the
 // last of each head (grid BH x (nseg - 1)), in the fragment layout the
-// output pass reads.  2*D/16 waves, 4 per SIMD: wave w owns column tile
-// c = w % (D/16) for half h = w / (D/16) of the rows, so each wave carries
-// half the accumulators of the output pass and twice as many waves hide the
-// latency.  K, V and eta stream through a 4-stage direct-to-LDS ring.
+// output pass reads.  2*D/16 waves, 4 per SIMD: wave w takes column tile
+// c = w / 2 of the increment over key half kc = w % 2 of every tile, for all
+// D rows, so each wave scales and splits only its own 32 keys of diag(eta) V;
+// the two key halves of a column tile are added once, at the end.  K, V and
+// eta stream through a 4-stage direct-to-LDS ring.
 template <int D>
 struct IncrCfg {
   static constexpr int C = 64;
   static constexpr int NC = D / 16;              // column tiles
   static constexpr int NW = 2 * NC;              // waves
   static constexpr int THREADS = NW * WAVE;
-  static constexpr int MT = D / 16;              // row tiles of a column tile
-  static constexpr int MH = MT / 2;              // row tiles per wave
+  static constexpr int MT = D / 16;              // row tiles
   static constexpr int ROWB = D * 2;
   static constexpr int MAT = C * ROWB;
   static constexpr int STAGES = 4;
@@ -473,24 +476,27 @@ struct IncrCfg {
   static constexpr int LOADS = 2 * MAT_LOADS + 1;
   static_assert(MAT % (1024 * NW) == 0, "tile matrix must split into whole wave loads");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+  static_assert(LDS_BYTES >= NC * MT * WAVE * 16, "the key-half reduction is staged through the ring");
 };
 
 template <int D>
 __global__ __launch_bounds__(2 * D / 16 * WAVE, 1) void pt_incr_kernel(SegArgs A) {
   using Cfg = IncrCfg<D>;
-  constexpr int C = Cfg::C, ROWB = Cfg::ROWB, MT = Cfg::MT, MH = Cfg::MH, NC = Cfg::NC, MAT = Cfg::MAT;
+  constexpr int C = Cfg::C, ROWB = Cfg::ROWB, MT = Cfg::MT, NC = Cfg::NC, MAT = Cfg::MAT;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int nseg = A.nseg, T = A.T;
   const int bh = blockIdx.x / (nseg - 1), s = blockIdx.x % (nseg - 1);
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l = threadIdx.x & 63, g = l >> 4, li = l & 15;
-  const int c = w % NC, h = w / NC;
+  const int c = w >> 1, kc = w & 1;
   const long long seg_begin = (long long)s * A.seg_len;
   const long long seg_end = min(seg_begin + A.seg_len, (long long)T);
-  const int nt = seg_end > seg_begin ? (int)((seg_end - seg_begin + C - 1) / C) : 0;
-  const bf16* Kh = A.K + (size_t)bh * T * D;
-  const bf16* Vh = A.V + (size_t)bh * T * D;
-  const float* Eh = A.eta + (size_t)bh * T;
+  const long long seg_toks = seg_end > seg_begin ? seg_end - seg_begin : 0;
+  const int nt = (int)((seg_toks + C - 1) / C);
+  // one buffer view per matrix for the whole segment: rows past its end read 0
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(A.K + ((size_t)bh * T + seg_begin) * D, seg_toks * ROWB);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(A.V + ((size_t)bh * T + seg_begin) * D, seg_toks * ROWB);
+  const __amdgpu_buffer_rsrc_t re = make_rsrc(A.eta + (size_t)bh * T + seg_begin, seg_toks * 4);
 
   unsigned gofs[Cfg::MAT_LOADS];
 #pragma unroll
@@ -499,29 +505,30 @@ __global__ __launch_bounds__(2 * D / 16 * WAVE, 1) void pt_incr_kernel(SegArgs A
     const int row = b / ROWB, ph = (b % ROWB) >> 4;
     gofs[k] = (unsigned)(row * ROWB + ((ph ^ seg_swz<D>(row)) << 4));
   }
+  const unsigned eofs = (unsigned)((w * Cfg::EPW + l) * 4);
+  // transposed reads of this wave's key half: K rows 32kc + 4g + li/4 (+16), V likewise
   const int trow = 4 * g + (li >> 2);
-  unsigned ktr[MH];
+  const unsigned khalf = (unsigned)(2 * kc * 16 * ROWB);
+  unsigned ktr[MT];
 #pragma unroll
-  for (int j = 0; j < MH; ++j) ktr[j] = seg_ktr<D>(h * MH + j, g, li);
-  const unsigned vtr = (unsigned)(trow * ROWB + (((2 * c + ((li >> 1) & 1)) ^ seg_swz<D>(trow)) << 4) + (li & 1) * 8);
+  for (int m = 0; m < MT; ++m) ktr[m] = khalf + seg_ktr<D>(m, g, li);
+  const unsigned vtr =
+      khalf + (unsigned)(trow * ROWB + (((2 * c + ((li >> 1) & 1)) ^ seg_swz<D>(trow)) << 4) + (li & 1) * 8);
 
   auto issue = [&](int i) {
-    const long long t0 = seg_begin + (long long)i * C;
-    const long long rem = seg_end - t0;
     unsigned char* st = smem + (i % Cfg::STAGES) * Cfg::STAGE;
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kh + (rem > 0 ? t0 * D : 0), rem * ROWB);
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vh + (rem > 0 ? t0 * D : 0), rem * ROWB);
+    const unsigned t = (unsigned)i * MAT;
 #pragma unroll
-    for (int k = 0; k < Cfg::MAT_LOADS; ++k) dma16<PT_STREAM>(rk, gofs[k], st + (w * Cfg::MAT_LOADS + k) * 1024);
+    for (int k = 0; k < Cfg::MAT_LOADS; ++k) dma16<PT_STREAM>(rk, t + gofs[k], st + (w * Cfg::MAT_LOADS + k) * 1024);
 #pragma unroll
-    for (int k = 0; k < Cfg::MAT_LOADS; ++k) dma16<PT_STREAM>(rv, gofs[k], st + MAT + (w * Cfg::MAT_LOADS + k) * 1024);
-    const __amdgpu_buffer_rsrc_t re = make_rsrc(Eh + (rem > 0 ? t0 : 0), rem * 4);
-    if (l < Cfg::EPW) dma4<PT_STREAM>(re, (unsigned)((w * Cfg::EPW + l) * 4), st + 2 * MAT + w * Cfg::EPW * 4);
+    for (int k = 0; k < Cfg::MAT_LOADS; ++k)
+      dma16<PT_STREAM>(rv, t + gofs[k], st + MAT + (w * Cfg::MAT_LOADS + k) * 1024);
+    if (l < Cfg::EPW) dma4<PT_STREAM>(re, (unsigned)i * (C * 4) + eofs, st + 2 * MAT + w * Cfg::EPW * 4);
   };
 
-  floatx4 S[MH];
+  floatx4 S[MT];
 #pragma unroll
-  for (int j = 0; j < MH; ++j) S[j] = floatx4{0.f, 0.f, 0.f, 0.f};
+  for (int m = 0; m < MT; ++m) S[m] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int k = 0; k < Cfg::STAGES - 1; ++k)
     if (nt > 0) issue(k);
@@ -532,32 +539,36 @@ __global__ __launch_bounds__(2 * D / 16 * WAVE, 1) void pt_incr_kernel(SegArgs A
     const unsigned char* ks = st;
     const unsigned char* vs = st + MAT;
     const float* es = (const float*)(st + 2 * MAT);
-    bf16x4 vt[4];
+    // diag(eta) V for keys 32kc + 4g + j (first 16) and 32kc + 16 + 4g + j, column 16c + li
+    const uint2 v0 = __builtin_bit_cast(uint2, lds_read_tr16(vs + vtr));
+    const uint2 v1 = __builtin_bit_cast(uint2, lds_read_tr16(vs + 16 * ROWB + vtr));
+    const floatx4 e0 = *(const floatx4*)(es + 32 * kc + 4 * g);
+    const floatx4 e1 = *(const floatx4*)(es + 32 * kc + 16 + 4 * g);
+    bf16x8 evh, evl;
+    split8(floatx4{e0[0] * bf16lo_f(v0.x), e0[1] * bf16hi_f(v0.x), e0[2] * bf16lo_f(v0.y), e0[3] * bf16hi_f(v0.y)},
+           floatx4{e1[0] * bf16lo_f(v1.x), e1[1] * bf16hi_f(v1.x), e1[2] * bf16lo_f(v1.y), e1[3] * bf16hi_f(v1.y)},
+           evh, evl);
+    bf16x8 a[MT];
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) vt[kb] = lds_read_tr16(vs + kb * 16 * ROWB + vtr);
+    for (int m = 0; m < MT; ++m) a[m] = join(lds_read_tr16(ks + ktr[m]), lds_read_tr16(ks + 16 * ROWB + ktr[m]));
 #pragma unroll
-    for (int kc = 0; kc < 2; ++kc) {
-      const floatx4 e0 = *(const floatx4*)(es + 32 * kc + 4 * g);
-      const floatx4 e1 = *(const floatx4*)(es + 32 * kc + 16 + 4 * g);
-      const uint2 v0 = __builtin_bit_cast(uint2, vt[2 * kc]), v1 = __builtin_bit_cast(uint2, vt[2 * kc + 1]);
-      bf16x8 evh, evl;
-      split8(floatx4{e0[0] * bf16lo_f(v0.x), e0[1] * bf16hi_f(v0.x), e0[2] * bf16lo_f(v0.y), e0[3] * bf16hi_f(v0.y)},
-             floatx4{e1[0] * bf16lo_f(v1.x), e1[1] * bf16hi_f(v1.x), e1[2] * bf16lo_f(v1.y), e1[3] * bf16hi_f(v1.y)},
-             evh, evl);
-      bf16x8 a[MH];
+    for (int m = 0; m < MT; ++m) S[m] = mfma16(a[m], evh, S[m]);
 #pragma unroll
-      for (int j = 0; j < MH; ++j)
-        a[j] = join(lds_read_tr16(ks + (2 * kc) * 16 * ROWB + ktr[j]), lds_read_tr16(ks + (2 * kc + 1) * 16 * ROWB + ktr[j]));
-#pragma unroll
-      for (int j = 0; j < MH; ++j) S[j] = mfma16(a[j], evh, S[j]);
-#pragma unroll
-      for (int j = 0; j < MH; ++j) S[j] = mfma16(a[j], evl, S[j]);
-    }
+    for (int m = 0; m < MT; ++m) S[m] = mfma16(a[m], evl, S[m]);
   }
-  wait_vm<0>();
-  floatx4* pp = A.part + (((size_t)bh * nseg + s) * NC + c) * MT * 64 + l;
+  // key half 1 of each column tile -> LDS (the ring is idle once every copy has landed), half 0 adds it
+  wait_vm_barrier<0>();
+  floatx4* red = (floatx4*)smem + (size_t)c * MT * WAVE + l;
+  if (kc == 1) {
 #pragma unroll
-  for (int j = 0; j < MH; ++j) pp[(h * MH + j) * 64] = S[j];
+    for (int m = 0; m < MT; ++m) red[m * WAVE] = S[m];
+  }
+  barrier();
+  if (kc == 0) {
+    floatx4* pp = A.part + (((size_t)bh * nseg + s) * NC + c) * MT * 64 + l;
+#pragma unroll
+    for (int m = 0; m < MT; ++m) pp[m * 64] = S[m] + red[m * WAVE];
+  }
 }
 
 // Start states of the segments of one head, in place: slot s holds dS_s
