@@ -280,11 +280,11 @@ __device__ __forceinline__ void seg_wave(const SegArgs& A, unsigned char* smem, 
   floatx4 S[MT];
   const floatx4* pp = A.part + ((size_t)bh * nseg * NW + W) * MT * 64 + l;   // slot 0 of this head
   constexpr int SLOT = NW * MT * 64;                                         // floatx4 per slot
-  if (nseg > 1) {
+  if (s > 0) {
     // start state of this segment, prepared by pt_seg_scan_kernel in the same fragment layout
 #pragma unroll
     for (int m = 0; m < MT; ++m) S[m] = pp[(size_t)s * SLOT + m * 64];
-  } else {
+  } else {                        // the first segment starts from W0
     const float* W0h = A.W0 + (size_t)bh * D * D;
 #pragma unroll
     for (int m = 0; m < MT; ++m)
@@ -567,12 +567,14 @@ __global__ __launch_bounds__(2 * D / 16 * WAVE, 1) void pt_incr_kernel(SegArgs A
   if (kc == 0) {
     floatx4* pp = A.part + (((size_t)bh * nseg + s) * NC + c) * MT * 64 + l;
 #pragma unroll
-    for (int m = 0; m < MT; ++m) pp[m * 64] = S[m] + red[m * WAVE];
+    for (int m = 0; m < MT; ++m) __builtin_nontemporal_store(S[m] + red[m * WAVE], pp + m * 64);
   }
 }
 
 // Start states of the segments of one head, in place: slot s holds dS_s
-// (s < nseg-1) on entry and S_start(s) = W0 + sum_{s' < s} dS_s' on exit.
+// (s < nseg-1) on entry and S_start(s) = W0 + sum_{s' < s} dS_s' on exit,
+// for s >= 1 (the first segment reads W0 itself, slot 0 is left as it is).
+// Non-temporal stores: the states are read once, by the output pass.
 // Layout of a slot: [wave W][m-tile][lane][4] floats, lane (g, li) of wave W
 // holding rows seg_srow(m, g, r), column 16W + li.  One thread per 4 floats.
 template <int D>
@@ -597,11 +599,11 @@ __global__ __launch_bounds__(256) void pt_seg_scan_kernel(const float* __restric
 #pragma unroll
     for (int k = 0; k < 8; ++k)
       if (k < n) {
-        ph[(size_t)(s0 + k) * PER] = run;
+        if (s0 + k > 0) __builtin_nontemporal_store(run, ph + (size_t)(s0 + k) * PER);
         run += d[k];
       }
   }
-  ph[(size_t)(nseg - 1) * PER] = run;
+  __builtin_nontemporal_store(run, ph + (size_t)(nseg - 1) * PER);
 }
 
 // ---------------------------------------------------------------------------
