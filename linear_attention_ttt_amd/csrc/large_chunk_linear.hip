@@ -260,6 +260,34 @@ __global__ __launch_bounds__(256, 2) void lact_read_kernel(const bf16* __restric
   const int t1 = min(t0 + part_len, cend);
   if (t0 >= t1) return;
 
+  // per-lane offsets: natural operand reads (row 16*blk + li, k = 32ks + 8g)
+  int nat[Cfg::KT];
+#pragma unroll
+  for (int ks = 0; ks < Cfg::KT; ++ks) nat[ks] = li * Cfg::ROWB + (((4 * ks + g) ^ (li & Cfg::SWZ)) << 4);
+  // this wave's DMA: 16 rows of a tile = QI instructions; slot (lane) -> (row, piece)
+  unsigned qoff[Cfg::QI];
+#pragma unroll
+  for (int k = 0; k < Cfg::QI; ++k) {
+    const int s = k * 64 + l;
+    const int row = s / (D / 8);
+    qoff[k] = (unsigned)((16 * w + row) * Cfg::ROWB + (((s % (D / 8)) ^ (row & Cfg::SWZ)) << 4));
+  }
+  unsigned char* ring = smem + 2 * Cfg::W_BYTES + w * LR_STAGES * Cfg::QW_BYTES;
+  const bf16* Qh = Q + (size_t)bh * T * D;
+  bf16* Oh = O + (size_t)bh * T * D;
+  const int ntiles = (t1 - t0 + 63) / 64;
+  // one buffer view of this part's queries and outputs (rows past its end read 0 / are dropped)
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(Qh + (size_t)t0 * D, (long long)(t1 - t0) * Cfg::ROWB);
+  const __amdgpu_buffer_rsrc_t ro = make_rsrc(Oh + (size_t)t0 * D, (long long)(t1 - t0) * Cfg::ROWB);
+  auto issue = [&](int i) {
+    unsigned char* dst = ring + (i % LR_STAGES) * Cfg::QW_BYTES;
+    const unsigned t = (unsigned)i * 64 * Cfg::ROWB;
+#pragma unroll
+    for (int k = 0; k < Cfg::QI; ++k) buf2lds16<true>(rq, t + qoff[k], dst + k * 1024);
+  };
+  // the first query tiles are in flight while W is staged
+#pragma unroll
+  for (int i = 0; i < LR_STAGES - 1; ++i) issue(i);
   // ---- W^T of this chunk as bf16 hi + lo planes [n][a], 16-byte pieces swizzled by n ----
   const float* Wt = wprev_t + ((size_t)bh * nchunks + c) * D * D;
   for (int p = tid; p < D * D / 8; p += 256) {
@@ -277,44 +305,27 @@ __global__ __launch_bounds__(256, 2) void lact_read_kernel(const bf16* __restric
     *(bf16x8*)(smem + off) = hi;
     *(bf16x8*)(smem + Cfg::W_BYTES + off) = lo;
   }
-  // per-lane offsets: natural operand reads (row 16*blk + li, k = 32ks + 8g)
-  int nat[Cfg::KT];
-#pragma unroll
-  for (int ks = 0; ks < Cfg::KT; ++ks) nat[ks] = li * Cfg::ROWB + (((4 * ks + g) ^ (li & Cfg::SWZ)) << 4);
-  // this wave's DMA: 16 rows of a tile = QI instructions; slot (lane) -> (row, piece)
-  unsigned qoff[Cfg::QI];
-#pragma unroll
-  for (int k = 0; k < Cfg::QI; ++k) {
-    const int s = k * 64 + l;
-    const int row = s / (D / 8);
-    qoff[k] = (unsigned)((16 * w + row) * Cfg::ROWB + (((s % (D / 8)) ^ (row & Cfg::SWZ)) << 4));
-  }
-  unsigned char* ring = smem + 2 * Cfg::W_BYTES + w * LR_STAGES * Cfg::QW_BYTES;
-  const bf16* Qh = Q + (size_t)bh * T * D;
-  bf16* Oh = O + (size_t)bh * T * D;
-  const int ntiles = (t1 - t0 + 63) / 64;
-  auto issue = [&](int i) {
-    const long long rem = (long long)t1 - (long long)(t0 + 64 * i);
-    const __amdgpu_buffer_rsrc_t r = make_rsrc(Qh + (size_t)(t0 + 64 * i) * D, rem * Cfg::ROWB);
-    unsigned char* dst = ring + (i % LR_STAGES) * Cfg::QW_BYTES;
-#pragma unroll
-    for (int k = 0; k < Cfg::QI; ++k) buf2lds16<true>(r, qoff[k], dst + k * 1024);
-  };
-#pragma unroll
-  for (int i = 0; i < LR_STAGES - 1; ++i) issue(i);
   __syncthreads();                                  // W planes complete
   const unsigned char* wh = smem;
   const unsigned char* wl = smem + Cfg::W_BYTES;
   for (int i = 0; i < ntiles; ++i) {
-    // this wave's rows of tile i have landed (later tiles may still be in flight)
-    wait_vm<(LR_STAGES - 2) * Cfg::QI>();
+    // This wave's rows of tile i have landed once only later operations are outstanding: the copies of
+    // tiles i+1 and i+2 and the output stores of up to three earlier tiles (issued after tile i's copy).
+    if (i == 0)
+      wait_vm<2 * Cfg::QI>();
+    else if (i == 1)
+      wait_vm<3 * Cfg::QI>();
+    else if (i == 2)
+      wait_vm<4 * Cfg::QI>();
+    else
+      wait_vm<5 * Cfg::QI>();
     issue(i + LR_STAGES - 1);
-    const unsigned char* qs = ring + (i % LR_STAGES) * Cfg::QW_BYTES;   // this wave's 16 rows
+    unsigned char* qs = ring + (i % LR_STAGES) * Cfg::QW_BYTES;   // this wave's 16 rows
     bf16x8 qop[Cfg::KT];
 #pragma unroll
     for (int ks = 0; ks < Cfg::KT; ++ks) qop[ks] = *(const bf16x8*)(qs + nat[ks]);
-    const long long rem = (long long)t1 - (long long)(t0 + 64 * i);
-    const __amdgpu_buffer_rsrc_t ro = make_rsrc(Oh + (size_t)(t0 + 64 * i) * D, rem * Cfg::ROWB);
+    // O^T = W^T Q^T: lane holds O[16w + li][16m + 4g .. +3], staged over the dead query rows (same
+    // swizzled layout) and written out as whole rows, 16 bytes per lane
 #pragma unroll
     for (int m = 0; m < Cfg::MT; ++m) {
       floatx4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -323,11 +334,16 @@ __global__ __launch_bounds__(256, 2) void lact_read_kernel(const bf16* __restric
         acc = mfma16(*(const bf16x8*)(wh + m * 16 * Cfg::ROWB + nat[ks]), qop[ks], acc);
         acc = mfma16(*(const bf16x8*)(wl + m * 16 * Cfg::ROWB + nat[ks]), qop[ks], acc);
       }
-      // lane holds O[16w + li][16m + 4g .. +3]
-      const bf16x4 o = to_bf16x4(acc[0], acc[1], acc[2], acc[3]);
-      __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(uint2v, o), ro,
-                                            (unsigned)((16 * w + li) * Cfg::ROWB + (16 * m + 4 * g) * 2), 0, 0);
+      const int piece = 2 * m + (g >> 1);
+      *(bf16x4*)(qs + li * Cfg::ROWB + ((piece ^ (li & Cfg::SWZ)) << 4) + (g & 1) * 8) =
+          to_bf16x4(acc[0], acc[1], acc[2], acc[3]);
     }
+    const unsigned t = (unsigned)i * 64 * Cfg::ROWB;
+    u32x4 v[Cfg::QI];
+#pragma unroll
+    for (int k = 0; k < Cfg::QI; ++k) v[k] = *(const u32x4*)(qs + k * 1024 + 16 * l);
+#pragma unroll
+    for (int k = 0; k < Cfg::QI; ++k) buf_store16(ro, t + qoff[k], v[k]);
   }
   wait_vm<0>();
 }
