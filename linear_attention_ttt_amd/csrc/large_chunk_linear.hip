@@ -251,9 +251,11 @@ __global__ __launch_bounds__(256, 2) void lact_read_kernel(const bf16* __restric
                                                            int parts, int part_len) {
   using Cfg = LactReadCfg<D>;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  const int part = blockIdx.x % parts;
-  const int c = (blockIdx.x / parts) % nchunks;
-  const int bh = blockIdx.x / (parts * nchunks);
+  // the parts of one chunk run on one XCD, so its W is fetched into one L2
+  const int lb = (gridDim.x & 7) == 0 ? xcd_logical_block(blockIdx.x, gridDim.x) : blockIdx.x;
+  const int part = lb % parts;
+  const int c = (lb / parts) % nchunks;
+  const int bh = lb / (parts * nchunks);
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g = l >> 4, li = l & 15;
   const int cend = min((c + 1) * chunk, T);
   const int t0 = c * chunk + part * part_len;

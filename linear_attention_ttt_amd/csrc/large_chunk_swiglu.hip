@@ -415,9 +415,11 @@ __global__ __launch_bounds__(512, 1) void swiglu_read_kernel(const bf16* __restr
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
   ReadLds& L = *reinterpret_cast<ReadLds*>(smem_raw);
   constexpr int D = SW_D, DH = SW_DH;
-  const int tile = blockIdx.x % tiles;
-  const int c = (blockIdx.x / tiles) % nchunks;
-  const int bh = blockIdx.x / (tiles * nchunks);
+  // the token tiles of one chunk run on one XCD, so its weights are fetched into one L2
+  const int lb = (gridDim.x & 7) == 0 ? xcd_logical_block(blockIdx.x, gridDim.x) : blockIdx.x;
+  const int tile = lb % tiles;
+  const int c = (lb / tiles) % nchunks;
+  const int bh = lb / (tiles * nchunks);
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g = l >> 4, li = l & 15;
   const int cend = min((c + 1) * chunk, T);
   const int t0 = c * chunk + tile * SW_TT;
