@@ -275,6 +275,26 @@ __device__ __forceinline__ bf16x4 to_bf16x4(float a, float b, float c, float d) 
   return r;
 }
 
+// Sum of x over the 64 lanes of a wave, the same value in every lane, in a
+// fixed order: within each row of 16 lanes by DPP moves (pair, quad, half-row
+// mirror, row mirror), then the four row sums read from lanes 0, 16, 32, 48.
+// No LDS traffic, unlike a shuffle butterfly.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float wave_sum(float x) {
+  x += dpp_f32<0xB1>(x);    // quad_perm [1,0,3,2]: lane ^ 1
+  x += dpp_f32<0x4E>(x);    // quad_perm [2,3,0,1]: lane ^ 2
+  x += dpp_f32<0x141>(x);   // row_half_mirror: the other quad of the half row
+  x += dpp_f32<0x140>(x);   // row_mirror: the other half of the row
+  const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 0));
+  const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 16));
+  const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 32));
+  const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 48));
+  return (r0 + r1) + (r2 + r3);
+}
+
 // Map a flat block index to a logical index such that consecutive logical
 // indices share an XCD (blocks are dispatched round-robin over 8 XCDs).
 // Requires nblocks % 8 == 0.

@@ -164,8 +164,9 @@ __global__ __launch_bounds__(256, 4) void lact_delta_kernel(const bf16* __restri
 
 // ---------------------------------------------------------------------------
 // 2. normalise-scan: one wave per (head, column j).  Lane l holds rows
-//    l, l+64, ... of the column.  Updates of a window of chunks are loaded
-//    in one burst (they do not depend on W), then scanned.
+//    l, l+64, ... of the column.  The updates do not depend on W, so those of
+//    the next window of chunks are loaded while the current window is
+//    scanned (two register buffers); the column norm is a DPP wave sum.
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256) void lact_scan_kernel(const float* __restrict__ W0, const float* __restrict__ part,
@@ -180,28 +181,22 @@ __global__ __launch_bounds__(256) void lact_scan_kernel(const float* __restrict_
   const float* W0h = W0 + (size_t)bh * D * D;
 #pragma unroll
   for (int r = 0; r < RPL; ++r) Wc[r] = W0h[(size_t)(l + 64 * r) * D + j];
-  for (int c0 = 0; c0 < nchunks; c0 += WIN) {
-    float d[WIN][RPL];
-#pragma unroll
-    for (int i = 0; i < WIN; ++i)
-#pragma unroll
-      for (int r = 0; r < RPL; ++r) d[i][r] = 0.f;
-    // unconditional (clamped) loads so the whole window is in flight at once
+  // slice updates of chunks c0 .. c0+WIN-1, loaded unconditionally (indices clamped) so that every window
+  // issues the same loads and the waits for one window never cover the next one's
+  auto issue = [&](int c0, float (&raw)[LC_MAXSPLIT][WIN][RPL]) {
 #pragma unroll
     for (int s = 0; s < LC_MAXSPLIT; ++s) {
       const int sc = min(s, nsplit - 1);
 #pragma unroll
       for (int i = 0; i < WIN; ++i) {
         const int cc = min(c0 + i, nchunks - 1);
-        const bool use = s < nsplit && c0 + i < nchunks;
         const float* Pc = part + ((((size_t)bh * nchunks + cc) * nsplit + sc) * D + j) * D;
 #pragma unroll
-        for (int r = 0; r < RPL; ++r) {
-          const float v = Pc[l + 64 * r];
-          d[i][r] += use ? v : 0.f;
-        }
+        for (int r = 0; r < RPL; ++r) raw[s][i][r] = Pc[l + 64 * r];
       }
     }
+  };
+  auto scan_win = [&](int c0, const float (&raw)[LC_MAXSPLIT][WIN][RPL]) {
 #pragma unroll
     for (int i = 0; i < WIN; ++i) {
       const int c = c0 + i;
@@ -210,15 +205,31 @@ __global__ __launch_bounds__(256) void lact_scan_kernel(const float* __restrict_
       float ss = 0.f;
 #pragma unroll
       for (int r = 0; r < RPL; ++r) {
+        float d = raw[0][i][r];
+#pragma unroll
+        for (int s = 1; s < LC_MAXSPLIT; ++s) d += s < nsplit ? raw[s][i][r] : 0.f;
         Wt[l + 64 * r] = Wc[r];
-        Wc[r] += d[i][r];
+        Wc[r] += d;
         ss = fmaf(Wc[r], Wc[r], ss);
       }
-#pragma unroll
-      for (int m = 1; m < 64; m <<= 1) ss += __shfl_xor(ss, m);
-      const float inv = 1.0f / fmaxf(sqrtf(ss), 1e-12f);
+      const float inv = 1.0f / fmaxf(sqrtf(wave_sum(ss)), 1e-12f);
 #pragma unroll
       for (int r = 0; r < RPL; ++r) Wc[r] *= inv;
+    }
+  };
+  // two register buffers: the next window is in flight while the current one is scanned
+  float ra[LC_MAXSPLIT][WIN][RPL], rb[LC_MAXSPLIT][WIN][RPL];
+  if (nchunks > 0) {
+    issue(0, ra);
+    for (int c0 = 0;;) {
+      issue(c0 + WIN, rb);
+      __builtin_amdgcn_sched_barrier(0);
+      scan_win(c0, ra);
+      if ((c0 += WIN) >= nchunks) break;
+      issue(c0 + WIN, ra);
+      __builtin_amdgcn_sched_barrier(0);
+      scan_win(c0, rb);
+      if ((c0 += WIN) >= nchunks) break;
     }
   }
   float* Wo = Wout + (size_t)bh * D * D;
