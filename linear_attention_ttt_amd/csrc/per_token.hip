@@ -609,22 +609,40 @@ __global__ __launch_bounds__(256) void pt_seg_scan_kernel(const float* __restric
 // ---------------------------------------------------------------------------
 // fp32 kernel: same chunked form on the vector ALUs, everything staged in
 // LDS.  Used for float32 inputs where bf16 rounding would exceed the fp32
-// accuracy budget.  One workgroup per (b,h) x 32-column tile of d_v.
+// accuracy budget.  One workgroup per (b,h) x 32-column tile of d_v.  Each
+// product is register-blocked (a thread owns a small block of its result and
+// reads its operands as 16-byte pieces), so the inner loops issue one LDS
+// read per 4 FMAs or better, with independent accumulators.
 // ---------------------------------------------------------------------------
+template <int DK, int C>
+struct Fp32Cfg {
+  static constexpr int TV = 32;                 // state / output columns per workgroup
+  static constexpr int QP = DK + 4;             // padded rows of q, k (16-byte aligned, conflict-free blocks)
+  static constexpr int PP = C + 4;              // padded rows of the score tile
+  static constexpr int SB = C / 16;             // score block per thread: SB x SB (256 threads cover C x C)
+  static constexpr int OFF_K = C * QP;
+  static constexpr int OFF_V = 2 * C * QP;
+  static constexpr int OFF_E = OFF_V + C * TV;
+  static constexpr int OFF_P = OFF_E + C;
+  static constexpr int OFF_S = OFF_P + C * PP;
+  static constexpr int FLOATS = OFF_S + DK * TV;
+  static_assert(C % 16 == 0 && DK % 32 == 0, "tile shape");
+};
+
 template <int DK, int C>
 __global__ __launch_bounds__(256) void per_token_fp32_kernel(
     const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
     const float* __restrict__ eta, const float* __restrict__ W0, float* __restrict__ O,
     float* __restrict__ Wout, int T, int DV) {
-  constexpr int TV = 32;
-  constexpr int QP = DK + 1;  // padded rows
+  using Cfg = Fp32Cfg<DK, C>;
+  constexpr int TV = Cfg::TV, QP = Cfg::QP, PP = Cfg::PP, SB = Cfg::SB;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   float* q = (float*)smem;              // [C][QP]
-  float* k = q + C * QP;                // [C][QP]
-  float* v = k + C * QP;                // [C][TV]
-  float* e = v + C * TV;                // [C]
-  float* p = e + C;                     // [C][C+1]
-  float* s = p + C * (C + 1);           // [DK][TV]
+  float* k = q + Cfg::OFF_K;            // [C][QP]
+  float* v = q + Cfg::OFF_V;            // [C][TV]
+  float* e = q + Cfg::OFF_E;            // [C]
+  float* p = q + Cfg::OFF_P;            // [C][PP]: eta_j * (q_i . k_j) for j <= i, else 0
+  float* s = q + Cfg::OFF_S;            // [DK][TV]
   const int NV = DV / TV;
   const int bh = blockIdx.x / NV;
   const int tv0 = (blockIdx.x % NV) * TV;
@@ -634,56 +652,108 @@ __global__ __launch_bounds__(256) void per_token_fp32_kernel(
   const float* Vh = V + (size_t)bh * T * DV;
   const float* Eh = eta + (size_t)bh * T;
   float* Oh = O + (size_t)bh * T * DV;
-  for (int i = tid; i < DK * TV; i += 256) s[i] = W0[(size_t)bh * DK * DV + (size_t)(i / TV) * DV + tv0 + i % TV];
+  for (int i = tid; i < DK * TV / 4; i += 256) {
+    const int a = i / (TV / 4), n4 = i % (TV / 4);
+    *(floatx4*)(s + a * TV + 4 * n4) = *(const floatx4*)(W0 + (size_t)bh * DK * DV + (size_t)a * DV + tv0 + 4 * n4);
+  }
+  // thread roles: score block (rows SB*bi.., cols SB*bj..); output / state column group cg (4 columns)
+  const int bi = tid / 16, bj = tid % 16;
+  const int cg = tid % 8, r8 = tid / 8;
   const int nchunks = (T + C - 1) / C;
   for (int c = 0; c < nchunks; ++c) {
     const int t0 = c * C;
     __syncthreads();
-    for (int i = tid; i < C * DK; i += 256) {
-      const int r = i / DK, a = i % DK;
+    for (int i = tid; i < C * DK / 4; i += 256) {
+      const int r = i / (DK / 4), a4 = i % (DK / 4);
       const bool ok = t0 + r < T;
-      q[r * QP + a] = ok ? Qh[(size_t)(t0 + r) * DK + a] : 0.f;
-      k[r * QP + a] = ok ? Kh[(size_t)(t0 + r) * DK + a] : 0.f;
+      const floatx4 z = {0.f, 0.f, 0.f, 0.f};
+      *(floatx4*)(q + r * QP + 4 * a4) = ok ? *(const floatx4*)(Qh + (size_t)(t0 + r) * DK + 4 * a4) : z;
+      *(floatx4*)(k + r * QP + 4 * a4) = ok ? *(const floatx4*)(Kh + (size_t)(t0 + r) * DK + 4 * a4) : z;
     }
-    for (int i = tid; i < C * TV; i += 256) {
-      const int r = i / TV, n = i % TV;
-      v[i] = (t0 + r < T) ? Vh[(size_t)(t0 + r) * DV + tv0 + n] : 0.f;
+    for (int i = tid; i < C * TV / 4; i += 256) {
+      const int r = i / (TV / 4), n4 = i % (TV / 4);
+      const floatx4 z = {0.f, 0.f, 0.f, 0.f};
+      *(floatx4*)(v + r * TV + 4 * n4) = (t0 + r < T) ? *(const floatx4*)(Vh + (size_t)(t0 + r) * DV + tv0 + 4 * n4) : z;
     }
     for (int i = tid; i < C; i += 256) e[i] = (t0 + i < T) ? Eh[t0 + i] : 0.f;
     __syncthreads();
-    // scores with the causal mask (diagonal included) and eta of the key token
-    for (int idx = tid; idx < C * C; idx += 256) {
-      const int i = idx / C, j = idx % C;
-      float acc = 0.f;
-      if (j <= i) {
-        for (int a = 0; a < DK; ++a) acc = fmaf(q[i * QP + a], k[j * QP + a], acc);
-        acc *= e[j];
+    // scores with the causal mask (diagonal included) and eta of the key token: SB x SB block per thread
+    if (bj <= bi) {
+      float acc[SB][SB];
+#pragma unroll
+      for (int r = 0; r < SB; ++r)
+#pragma unroll
+        for (int cc = 0; cc < SB; ++cc) acc[r][cc] = 0.f;
+#pragma unroll 2
+      for (int a = 0; a < DK; a += 4) {
+        floatx4 qa[SB], ka[SB];
+#pragma unroll
+        for (int r = 0; r < SB; ++r) qa[r] = *(const floatx4*)(q + (SB * bi + r) * QP + a);
+#pragma unroll
+        for (int cc = 0; cc < SB; ++cc) ka[cc] = *(const floatx4*)(k + (SB * bj + cc) * QP + a);
+#pragma unroll
+        for (int r = 0; r < SB; ++r)
+#pragma unroll
+          for (int cc = 0; cc < SB; ++cc)
+#pragma unroll
+            for (int x = 0; x < 4; ++x) acc[r][cc] = fmaf(qa[r][x], ka[cc][x], acc[r][cc]);
       }
-      p[i * (C + 1) + j] = acc;
+#pragma unroll
+      for (int r = 0; r < SB; ++r)
+#pragma unroll
+        for (int cc = 0; cc < SB; ++cc) {
+          const int i = SB * bi + r, j = SB * bj + cc;
+          p[i * PP + j] = j <= i ? acc[r][cc] * e[j] : 0.f;
+        }
+    } else {
+#pragma unroll
+      for (int r = 0; r < SB; ++r)
+#pragma unroll
+        for (int cc = 0; cc < SB; ++cc) p[(SB * bi + r) * PP + SB * bj + cc] = 0.f;
     }
     __syncthreads();
-    for (int idx = tid; idx < C * TV; idx += 256) {
-      const int i = idx / TV, n = idx % TV;
-      float acc = 0.f;
-      for (int j = 0; j <= i; ++j) acc = fmaf(p[i * (C + 1) + j], v[j * TV + n], acc);
-      for (int a = 0; a < DK; ++a) acc = fmaf(q[i * QP + a], s[a * TV + n], acc);
-      if (t0 + i < T) Oh[(size_t)(t0 + i) * DV + tv0 + n] = acc;
+    // outputs: rows r8 + 32m, columns 4cg..4cg+3
+#pragma unroll 1
+    for (int i = r8; i < C; i += 32) {
+      floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
+      for (int j = 0; j < C; ++j) acc += p[i * PP + j] * *(const floatx4*)(v + j * TV + 4 * cg);
+      floatx4 acc2 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+      for (int a = 0; a < DK; a += 4) {
+        const floatx4 qa = *(const floatx4*)(q + i * QP + a);
+#pragma unroll
+        for (int x = 0; x < 4; ++x) acc2 += qa[x] * *(const floatx4*)(s + (a + x) * TV + 4 * cg);
+      }
+      if (t0 + i < T) *(floatx4*)(Oh + (size_t)(t0 + i) * DV + tv0 + 4 * cg) = acc + acc2;
     }
     __syncthreads();
-    for (int idx = tid; idx < DK * TV; idx += 256) {
-      const int a = idx / TV, n = idx % TV;
-      float acc = s[idx];
-      for (int j = 0; j < C; ++j) acc = fmaf(k[j * QP + a] * e[j], v[j * TV + n], acc);
-      s[idx] = acc;
+    // state: rows r8 + 32m of s, columns 4cg..4cg+3, over the chunk's keys
+    {
+      constexpr int RS = DK / 32;
+      floatx4 acc[RS];
+#pragma unroll
+      for (int m = 0; m < RS; ++m) acc[m] = *(const floatx4*)(s + (r8 + 32 * m) * TV + 4 * cg);
+#pragma unroll 4
+      for (int j = 0; j < C; ++j) {
+        const floatx4 ev = e[j] * *(const floatx4*)(v + j * TV + 4 * cg);
+#pragma unroll
+        for (int m = 0; m < RS; ++m) acc[m] += k[j * QP + r8 + 32 * m] * ev;
+      }
+#pragma unroll
+      for (int m = 0; m < RS; ++m) *(floatx4*)(s + (r8 + 32 * m) * TV + 4 * cg) = acc[m];
     }
   }
   __syncthreads();
-  for (int i = tid; i < DK * TV; i += 256) Wout[(size_t)bh * DK * DV + (size_t)(i / TV) * DV + tv0 + i % TV] = s[i];
+  for (int i = tid; i < DK * TV / 4; i += 256) {
+    const int a = i / (TV / 4), n4 = i % (TV / 4);
+    *(floatx4*)(Wout + (size_t)bh * DK * DV + (size_t)a * DV + tv0 + 4 * n4) = *(const floatx4*)(s + a * TV + 4 * n4);
+  }
 }
 
 template <int DK, int C>
 static size_t fp32_lds_bytes() {
-  return sizeof(float) * (2 * C * (DK + 1) + C * 32 + C + C * (C + 1) + DK * 32);
+  return sizeof(float) * Fp32Cfg<DK, C>::FLOATS;
 }
 
 // ---------------------------------------------------------------------------
