@@ -17,6 +17,8 @@ pytestmark = pytest.mark.gpu
     (1, 2, 50, 64, 7),
     (1, 2, 100, 64, 100),     # a single chunk
     (1, 2, 100, 64, 4096),    # chunk longer than the sequence
+    (1, 2, 700, 128, 32),     # d = 128 over several scan windows of chunks, ragged
+    (1, 1, 1500, 64, 50),     # d = 64 over three scan windows, the last one partial
 ])
 def test_large_chunk_linear_small(B, H, T, d, chunk):
     s = workloads.make_spec("large_chunk_linear", B, H, T, d, chunk=chunk, dtype="bf16", eta_scale=0.05)

@@ -20,6 +20,8 @@ pytestmark = pytest.mark.gpu
     (1, 1, 256, 64, 64, "fp32"),
     (2, 2, 203, 128, 32, "fp32"),
     (1, 2, 90, 64, 16, "fp32"),
+    (1, 2, 200, 128, 64, "fp32"),      # fp32, d = 128 with 64-token chunks, ragged
+    (1, 1, 37, 64, 32, "fp32"),        # fp32, one partial chunk
 ])
 def test_per_token_small(B, H, T, d, chunk, dtype):
     s = workloads.make_spec("per_token_linear", B, H, T, d, chunk=chunk, dtype=dtype, eta="sigmoid")
