@@ -40,7 +40,7 @@ constexpr int SW_D = 128;
 constexpr int SW_DH = 256;
 constexpr int SW_NS = 16;                 // hidden units per recurrence workgroup
 constexpr int SW_NSL = SW_DH / SW_NS;     // workgroups per head
-constexpr int SW_TT = 256;                // tokens per read workgroup (8 waves x 32)
+constexpr int SW_TT = 256;                // tokens per read workgroup (4 waves x 64)
 constexpr int SW_US = 32;                 // hidden units per read slice
 constexpr int SW_SPIN_LIMIT = 1 << 24;
 constexpr size_t SW_STATE = (size_t)6 * SW_D * SW_DH;  // bf16 elements per stored state
@@ -404,8 +404,9 @@ __global__ __launch_bounds__(SW_WAVES * 64, 1) void swiglu_recur_kernel(
 // ---------------------------------------------------------------------------
 // Weight slices in LDS without padding: a W1T/W3T row (one unit, 256 bytes)
 // has its 16-byte pieces at c ^ sw_swz(row); a W2T row (32 units, 64 bytes)
-// has its 8-byte pieces at c ^ ((row >> 2) & 3).  Both make the operand reads
-// (16 rows per 16 lanes) conflict-free.
+// has its 16-byte pieces at c ^ ((row >> 2) & 3).  Both make the operand reads
+// (16 rows per 16 lanes) conflict-free, and both are written by direct-to-LDS
+// copies (the permutation is applied to the global addresses).
 struct ReadLds {
   unsigned char w13[2][4][SW_US * SW_D * 2];   // W1T hi, W1T lo, W3T hi, W3T lo: [32 units][128 d]
   unsigned char w2[2][2][SW_D * SW_US * 2];    // W2T hi, lo: [n][32 units]
@@ -414,12 +415,18 @@ constexpr int RW13_ROW = SW_D * 2;
 constexpr int RW2_ROW = SW_US * 2;
 __device__ __forceinline__ int w2_swz(int row) { return (row >> 2) & 3; }
 
-__global__ __launch_bounds__(512, 1) void swiglu_read_kernel(const bf16* __restrict__ Q,
-                                                             const bf16* __restrict__ states, bf16* __restrict__ O,
-                                                             int T, int chunk, int nchunks, int tiles) {
+// Two waves per SIMD, 32 tokens per wave (measured against one wave per SIMD
+// with 64 tokens each, which halves the LDS reads of the weights per token:
+// ~6 % slower, the lone wave waits on its own LDS reads).
+constexpr int SW_RW = 8;                  // waves per read workgroup
+constexpr int SW_RT = SW_TT / SW_RW;      // tokens per wave (2 tiles of 16)
+__global__ __launch_bounds__(SW_RW * 64, 1) void swiglu_read_kernel(const bf16* __restrict__ Q,
+                                                                    const bf16* __restrict__ states,
+                                                                    bf16* __restrict__ O, int T, int chunk,
+                                                                    int nchunks, int tiles) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
   ReadLds& L = *reinterpret_cast<ReadLds*>(smem_raw);
-  constexpr int D = SW_D, DH = SW_DH;
+  constexpr int D = SW_D, DH = SW_DH, NTH = SW_RW * 64, TT = SW_RT / 16;
   // the token tiles of one chunk run on one XCD, so its weights are fetched into one L2
   const int lb = (gridDim.x & 7) == 0 ? xcd_logical_block(blockIdx.x, gridDim.x) : blockIdx.x;
   const int tile = lb % tiles;
@@ -434,67 +441,67 @@ __global__ __launch_bounds__(512, 1) void swiglu_read_kernel(const bf16* __restr
 
   // this wave's queries as B operands (col = token, k = 8 consecutive d)
   const bf16* Qh = Q + (size_t)bh * T * D;
-  bf16x8 qop[2][4];
+  bf16x8 qop[TT][4];
 #pragma unroll
-  for (int tt = 0; tt < 2; ++tt) {
-    const int t = min(t0 + 32 * w + 16 * tt + li, cend - 1);
+  for (int tt = 0; tt < TT; ++tt) {
+    const int t = min(t0 + SW_RT * w + 16 * tt + li, cend - 1);
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
       qop[tt][ks] = __builtin_bit_cast(bf16x8, __builtin_nontemporal_load((const u32x4*)(Qh + (size_t)t * D + 32 * ks + 8 * g)));
   }
 
-  // weight slice staging: 6 x 16 bytes per thread (512 threads)
-  uint4 wr0, wr1, wr2, wr3, wr4, wr5;
-  auto wsrc13 = [&](int k, int s) {        // W1T/W3T hi/lo planes: 4 x 32 rows x 16 pieces
-    const int p = k * 512 + tid;
-    const int plane = p >> 9, row = (p >> 4) & 31, pc = p & 15;
-    return (const uint4*)(st + (size_t)plane * P + (size_t)(SW_US * s + row) * D + pc * 8);
-  };
-  auto wsrc2 = [&](int k, int s) {         // W2T hi/lo: 2 x 128 rows x 4 pieces
-    const int p = k * 512 + tid;
-    const int plane = p >> 9, n = (p >> 2) & 127, pc = p & 3;
-    return (const uint4*)(st + (size_t)(4 + plane) * P + (size_t)n * DH + SW_US * s + pc * 8);
-  };
-  auto load_slice = [&](int s) {
-    wr0 = *wsrc13(0, s); wr1 = *wsrc13(1, s); wr2 = *wsrc13(2, s); wr3 = *wsrc13(3, s);
-    wr4 = *wsrc2(0, s); wr5 = *wsrc2(1, s);
-  };
-  auto put13 = [&](int k, int buf, uint4 v) {
-    const int p = k * 512 + tid;
-    const int plane = p >> 9, row = (p >> 4) & 31, pc = p & 15;
-    *(uint4*)(L.w13[buf][plane] + row * RW13_ROW + ((pc ^ sw_swz(row)) << 4)) = v;
-  };
-  auto put2 = [&](int k, int buf, uint4 v) {
-    const int p = k * 512 + tid;
-    const int plane = p >> 9, n = (p >> 2) & 127, pc = p & 3;
-    unsigned char* dst = L.w2[buf][plane] + n * RW2_ROW;
-    *(uint2*)(dst + (((2 * pc) ^ w2_swz(n)) << 3)) = uint2{v.x, v.y};
-    *(uint2*)(dst + (((2 * pc + 1) ^ w2_swz(n)) << 3)) = uint2{v.z, v.w};
-  };
-  auto store_slice = [&](int buf) {
-    put13(0, buf, wr0); put13(1, buf, wr1); put13(2, buf, wr2); put13(3, buf, wr3);
-    put2(0, buf, wr4); put2(1, buf, wr5);
+  // weight slice s -> LDS buffer buf by direct-to-LDS copies: each wave copies 4 KB of the W1T/W3T
+  // planes (4 x 1 KB) and 2 KB of the W2T planes (2 x 1 KB)
+  constexpr int J13 = 4 * SW_US * SW_D * 2 / 1024 / SW_RW, J2 = 2 * SW_D * SW_US * 2 / 1024 / SW_RW;
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(st, (long long)SW_STATE * 2);
+  unsigned off13[J13], off2[J2];
+#pragma unroll
+  for (int j = 0; j < J13; ++j) {
+    const int k = w * J13 + j, plane = k >> 3, b = (k & 7) * 1024 + 16 * l, row = b >> 8, q = (b & 255) >> 4;
+    off13[j] = (unsigned)(((size_t)plane * P + (size_t)row * D + ((q ^ sw_swz(row)) << 3)) * 2);
+  }
+#pragma unroll
+  for (int j = 0; j < J2; ++j) {
+    const int k2 = w * J2 + j, plane = k2 >> 3, b = (k2 & 7) * 1024 + 16 * l, n = b >> 6, q = (b & 63) >> 4;
+    off2[j] = (unsigned)(((size_t)(4 + plane) * P + (size_t)n * DH + ((q ^ w2_swz(n)) << 3)) * 2);
+  }
+  auto load_slice = [&](int sl, int buf) {
+    const unsigned u13 = (unsigned)(SW_US * sl * D * 2), u2 = (unsigned)(SW_US * sl * 2);
+#pragma unroll
+    for (int j = 0; j < J13; ++j) {
+      const int k = w * J13 + j;
+      dma16<false>(rs, u13 + off13[j], L.w13[buf][k >> 3] + (k & 7) * 1024);
+    }
+#pragma unroll
+    for (int j = 0; j < J2; ++j) {
+      const int k2 = w * J2 + j;
+      dma16<false>(rs, u2 + off2[j], L.w2[buf][k2 >> 3] + (k2 & 7) * 1024);
+    }
   };
 
-  floatx4 oacc[8][2];
+  floatx4 oacc[8][TT];
 #pragma unroll
-  for (int nt = 0; nt < 8; ++nt) oacc[nt][0] = oacc[nt][1] = floatx4{0.f, 0.f, 0.f, 0.f};
+  for (int nt = 0; nt < 8; ++nt)
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt) oacc[nt][tt] = floatx4{0.f, 0.f, 0.f, 0.f};
 
   constexpr int NSLICE = DH / SW_US;
-  load_slice(0);
+  load_slice(0, 0);
   for (int s = 0; s < NSLICE; ++s) {
     const int buf = s & 1;
-    store_slice(buf);
-    __syncthreads();
-    if (s + 1 < NSLICE) load_slice(s + 1);
-    // A^T, B^T [unit][token] for 2 unit tiles x 2 token tiles
-    floatx4 at[2][2], bt[2][2];
+    // slice s has landed and every wave is done with slice s-1, whose buffer the next copy reuses
+    // (the query loads issued before the first copy are complete too)
+    wait_vm_barrier<0>();
+    if (s + 1 < NSLICE) load_slice(s + 1, buf ^ 1);
+    // H^T = silu(A^T) * B^T as bf16 hi + lo, k-slot order of the 32 units: 4g..4g+3 of unit tile 0,
+    // then of unit tile 1
+    bf16x8 hh[TT], hl[TT];
 #pragma unroll
-    for (int ut = 0; ut < 2; ++ut)
+    for (int ut = 0; ut < 2; ++ut) {
+      // A^T, B^T [unit][token] for one 16-unit tile x the wave's 4 token tiles
+      floatx4 at[TT], bt[TT];
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt) at[ut][tt] = bt[ut][tt] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ut = 0; ut < 2; ++ut)
+      for (int tt = 0; tt < TT; ++tt) at[tt] = bt[tt] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         const int off = (16 * ut + li) * RW13_ROW + (((4 * ks + g) ^ sw_swz(16 * ut + li)) << 4);
@@ -503,54 +510,51 @@ __global__ __launch_bounds__(512, 1) void swiglu_read_kernel(const bf16* __restr
         const bf16x8 w3h = *(const bf16x8*)(L.w13[buf][2] + off);
         const bf16x8 w3l = *(const bf16x8*)(L.w13[buf][3] + off);
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-          at[ut][tt] = mfma16(w1h, qop[tt][ks], at[ut][tt]);
-          at[ut][tt] = mfma16(w1l, qop[tt][ks], at[ut][tt]);
-          bt[ut][tt] = mfma16(w3h, qop[tt][ks], bt[ut][tt]);
-          bt[ut][tt] = mfma16(w3l, qop[tt][ks], bt[ut][tt]);
+        for (int tt = 0; tt < TT; ++tt) {
+          at[tt] = mfma16(w1h, qop[tt][ks], at[tt]);
+          at[tt] = mfma16(w1l, qop[tt][ks], at[tt]);
+          bt[tt] = mfma16(w3h, qop[tt][ks], bt[tt]);
+          bt[tt] = mfma16(w3l, qop[tt][ks], bt[tt]);
         }
       }
-    // H^T = silu(A^T) * B^T, split into bf16 hi + lo; k-slot order of the
-    // 32 units: 4g..4g+3 of unit tile 0, then of unit tile 1
-    bf16x8 hh[2], hl[2];
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-      for (int ut = 0; ut < 2; ++ut)
+      for (int tt = 0; tt < TT; ++tt)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const float a = at[ut][tt][r];
-          const float h = a * sigmoid_fast(a) * bt[ut][tt][r];
+          const float a = at[tt][r];
+          const float h = a * sigmoid_fast(a) * bt[tt][r];
           const bf16 hb = (bf16)h;
           hh[tt][4 * ut + r] = hb;
           hl[tt][4 * ut + r] = (bf16)(h - (float)hb);
         }
+    }
     // O^T[n][t] += W2^T[n][units] H^T[units][t]
 #pragma unroll
     for (int nt = 0; nt < 8; ++nt) {
       const unsigned char* rowh = L.w2[buf][0] + (16 * nt + li) * RW2_ROW;
       const unsigned char* rowl = L.w2[buf][1] + (16 * nt + li) * RW2_ROW;
-      const int p0 = (g ^ w2_swz(16 * nt + li)) << 3, p1 = ((4 + g) ^ w2_swz(16 * nt + li)) << 3;
+      // units 4g..4g+3 and 16+4g..16+4g+3: halves of the 16-byte pieces g/2 and 2+g/2
+      const int p0 = (((g >> 1) ^ w2_swz(16 * nt + li)) << 4) + (g & 1) * 8;
+      const int p1 = (((2 + (g >> 1)) ^ w2_swz(16 * nt + li)) << 4) + (g & 1) * 8;
       const bf16x8 w2h = join(*(const bf16x4*)(rowh + p0), *(const bf16x4*)(rowh + p1));
       const bf16x8 w2l = join(*(const bf16x4*)(rowl + p0), *(const bf16x4*)(rowl + p1));
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
+      for (int tt = 0; tt < TT; ++tt) {
         oacc[nt][tt] = mfma16(w2h, hh[tt], oacc[nt][tt]);
         oacc[nt][tt] = mfma16(w2h, hl[tt], oacc[nt][tt]);
         oacc[nt][tt] = mfma16(w2l, hh[tt], oacc[nt][tt]);
       }
     }
-    __syncthreads();
   }
   bf16* Oh = O + (size_t)bh * T * D;
   const __amdgpu_buffer_rsrc_t ro = make_rsrc(Oh + (size_t)t0 * D, ((long long)cend - t0) * D * 2);
 #pragma unroll
-  for (int tt = 0; tt < 2; ++tt)
+  for (int tt = 0; tt < TT; ++tt)
 #pragma unroll
     for (int nt = 0; nt < 8; ++nt) {
       const bf16x4 o = to_bf16x4(oacc[nt][tt][0], oacc[nt][tt][1], oacc[nt][tt][2], oacc[nt][tt][3]);
       __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(uint2v, o), ro,
-                                            (unsigned)((32 * w + 16 * tt + li) * D * 2 + (16 * nt + 4 * g) * 2), 0, 0);
+                                            (unsigned)((SW_RT * w + 16 * tt + li) * D * 2 + (16 * nt + 4 * g) * 2), 0, 0);
     }
 }
 
@@ -636,7 +640,7 @@ hipError_t launch_large_chunk_swiglu(const LargeChunkArgs& a, hipStream_t stream
   e = hipFuncSetAttribute((const void*)swiglu_read_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_o);
   if (e != hipSuccess) return e;
   const int tiles = (chunk + SW_TT - 1) / SW_TT;
-  hipLaunchKernelGGL(swiglu_read_kernel, dim3(BH * nchunks * tiles), dim3(512), lds_o, stream, (const bf16*)a.Q,
+  hipLaunchKernelGGL(swiglu_read_kernel, dim3(BH * nchunks * tiles), dim3(SW_RW * 64), lds_o, stream, (const bf16*)a.Q,
                      (const bf16*)states, (bf16*)a.O, T, chunk, nchunks, tiles);
   return hipGetLastError();
 }
