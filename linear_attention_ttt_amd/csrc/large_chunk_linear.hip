@@ -29,14 +29,23 @@ namespace {
 
 constexpr int LC_STEP = 64;       // tokens per LDS step in the update kernel
 constexpr int LC_MAXSPLIT = 4;    // token slices per chunk
-constexpr int LC_MINSLICE = 1024;
+constexpr int LC_WG_TARGET = 512;  // update workgroups wanted: about two per CU
 
-inline int64_t nsplit_of(int64_t chunk) {
-  int64_t n = (chunk + LC_MINSLICE - 1) / LC_MINSLICE;
-  return n < 1 ? 1 : (n > LC_MAXSPLIT ? LC_MAXSPLIT : n);
+// Token slices per chunk of the update kernel: as few as give about two
+// workgroups per CU (each slice writes a d x d partial, so fewer slices move
+// fewer bytes: at the 196K-token workload one slice per 4096-token chunk ran
+// 101 us against 108 us with two and 113 us with four), at most LC_MAXSPLIT,
+// each at least one 64-token step.
+inline int64_t nsplit_of(int64_t BH, int64_t nchunks, int64_t chunk) {
+  const int64_t units = BH * nchunks > 0 ? BH * nchunks : 1;
+  int64_t n = (LC_WG_TARGET + units - 1) / units;
+  const int64_t steps = (chunk + LC_STEP - 1) / LC_STEP;
+  n = n > LC_MAXSPLIT ? LC_MAXSPLIT : n;
+  n = n > steps ? steps : n;
+  return n < 1 ? 1 : n;
 }
-inline int64_t slice_of(int64_t chunk) {
-  const int64_t n = nsplit_of(chunk);
+inline int64_t slice_of(int64_t BH, int64_t nchunks, int64_t chunk) {
+  const int64_t n = nsplit_of(BH, nchunks, chunk);
   return ((chunk + n - 1) / n + LC_STEP - 1) / LC_STEP * LC_STEP;
 }
 
@@ -365,8 +374,8 @@ template <int D>
 hipError_t launch_lact(const LargeChunkArgs& a, hipStream_t stream, const Timing& tm) {
   const int T = (int)a.T, chunk = (int)a.chunk;
   const int nchunks = (int)((a.T + a.chunk - 1) / a.chunk);
-  const int nsplit = (int)nsplit_of(a.chunk);
-  const int slice = (int)slice_of(a.chunk);
+  const int nsplit = (int)nsplit_of(a.B * a.H, nchunks, a.chunk);
+  const int slice = (int)slice_of(a.B * a.H, nchunks, a.chunk);
   const int BH = (int)(a.B * a.H);
   float* part = (float*)a.ws;
   float* wprev = part + (size_t)BH * nchunks * nsplit * D * D;
@@ -404,7 +413,7 @@ bool large_chunk_linear_supported(int64_t dk, int64_t dv, int64_t chunk, int dty
 
 size_t large_chunk_linear_workspace(int64_t B, int64_t H, int64_t T, int64_t dk, int64_t dv, int64_t chunk) {
   const int64_t nchunks = (T + chunk - 1) / chunk;
-  return (size_t)(B * H * nchunks * (nsplit_of(chunk) + 1) * dk * dv * 4);
+  return (size_t)(B * H * nchunks * (nsplit_of(B * H, nchunks, chunk) + 1) * dk * dv * 4);
 }
 
 hipError_t launch_large_chunk_linear(const LargeChunkArgs& a, hipStream_t stream, const Timing& tm) {
