@@ -53,6 +53,9 @@ constexpr bool PT_STREAM = true;
 __host__ __device__ constexpr int ptile_jb(int t) { return t < 1 ? 0 : t < 3 ? t - 1 : t < 6 ? t - 3 : t - 6; }
 __host__ __device__ constexpr int ptile_ib(int t) { return t < 1 ? 0 : t < 3 ? 1 : t < 6 ? 2 : 3; }
 __host__ __device__ constexpr int ptile_index(int jb, int ib) { return ib * (ib + 1) / 2 + jb; }
+// LDS slot of the score-tile pair (2kc, 2kc+1) of query block ib: the pairs of all query blocks in order
+// (ib + 2) / 2 pairs for block ib); a pair whose second tile lies above the diagonal keeps zeros there
+__host__ __device__ constexpr int ppair_slot(int ib, int kc) { return (ib / 2) * (ib / 2 + 1) + (ib & 1) * (ib / 2 + 1) + kc; }
 __host__ __device__ constexpr int tile_begin4(int w) { return w == 0 ? 0 : w == 1 ? 3 : w == 2 ? 6 : w == 3 ? 8 : 10; }
 __host__ __device__ constexpr int tile_begin8(int w) { return w <= 3 ? 2 * w : w <= 7 ? w + 3 : 10; }
 template <int NW>
@@ -83,9 +86,15 @@ struct SegCfg {
   static constexpr int OFF_V = OFF_K + MAT;
   static constexpr int OFF_E = OFF_V + MAT;
   static constexpr int STAGE = 3 * MAT + C * 4;
-  static constexpr int OFF_P = STAGES * STAGE;   // score tiles [hi, lo][NT][64 lanes x 8 bytes]
-  static constexpr int P_PLANE = NT * 512;
-  static constexpr int LDS_BYTES = OFF_P + 2 * P_PLANE;
+  // The score tiles come first, so that their addresses (lane offset plus constants below 64 KB) take
+  // the LDS instructions' immediate offsets instead of one address add per read.  They are stored as
+  // pairs (2kc, 2kc+1) of one query block, 16 bytes per lane, so that each operand of the intra-tile
+  // product is one 16-byte read.
+  static constexpr int NPAIR = ppair_slot(NB, 0);  // pair slots (6 for 64-token tiles)
+  static constexpr int OFF_P = 0;                 // score pairs [hi, lo][NPAIR][64 lanes x 16 bytes]
+  static constexpr int P_PLANE = NPAIR * 1024;
+  static constexpr int OFF_RING = 2 * P_PLANE;
+  static constexpr int LDS_BYTES = OFF_RING + STAGES * STAGE;
   static constexpr int WG_PER_CU = (160 * 1024) / LDS_BYTES >= 2 ? 2 : 1;
   static constexpr int WAVES_PER_SIMD = NW * WG_PER_CU / 4;
   static constexpr int EPW = C / NW;             // eta values loaded by each wave
@@ -240,24 +249,24 @@ __device__ __forceinline__ void seg_wave(const SegArgs& A, unsigned char* smem, 
   // K, V, eta.  The parts are issued at different points of a tile so that the workgroup's vector
   // memory instructions do not all queue at the tile boundary.
   auto issue_q = [&](int i) {
-    unsigned char* st = smem + (i % Cfg::STAGES) * Cfg::STAGE + W * Cfg::MAT_LOADS * 1024;
+    unsigned char* st = smem + Cfg::OFF_RING + (i % Cfg::STAGES) * Cfg::STAGE + W * Cfg::MAT_LOADS * 1024;
     const unsigned t = (unsigned)i * Cfg::MAT;
 #pragma unroll
     for (int k = 0; k < Cfg::MAT_LOADS; ++k) dma16<PT_STREAM>(rq, t + gofs[k], st + k * 1024);
   };
   auto issue_kve = [&](int i) {
-    unsigned char* st = smem + (i % Cfg::STAGES) * Cfg::STAGE + W * Cfg::MAT_LOADS * 1024;
+    unsigned char* st = smem + Cfg::OFF_RING + (i % Cfg::STAGES) * Cfg::STAGE + W * Cfg::MAT_LOADS * 1024;
     const unsigned t = (unsigned)i * Cfg::MAT;
 #pragma unroll
     for (int k = 0; k < Cfg::MAT_LOADS; ++k) dma16<PT_STREAM>(rk, t + gofs[k], st + Cfg::OFF_K + k * 1024);
 #pragma unroll
     for (int k = 0; k < Cfg::MAT_LOADS; ++k) dma16<PT_STREAM>(rv, t + gofs[k], st + Cfg::OFF_V + k * 1024);
-    unsigned char* ed = smem + (i % Cfg::STAGES) * Cfg::STAGE + Cfg::OFF_E + W * Cfg::EPW * 4;
+    unsigned char* ed = smem + Cfg::OFF_RING + (i % Cfg::STAGES) * Cfg::STAGE + Cfg::OFF_E + W * Cfg::EPW * 4;
     if (l < Cfg::EPW) dma4<PT_STREAM>(re, (unsigned)i * (C * 4) + eofs, ed);
   };
   // rows of tile i's outputs staged in its (dead) V region -> HBM, 16 bytes per lane, whole rows
   auto write_out = [&](int i) {
-    const unsigned char* st = smem + (i % Cfg::STAGES) * Cfg::STAGE + Cfg::OFF_V;
+    const unsigned char* st = smem + Cfg::OFF_RING + (i % Cfg::STAGES) * Cfg::STAGE + Cfg::OFF_V;
     const unsigned t = (unsigned)i * Cfg::MAT;
     u32x4 v[Cfg::MAT_LOADS];
 #pragma unroll
@@ -292,6 +301,17 @@ __device__ __forceinline__ void seg_wave(const SegArgs& A, unsigned char* smem, 
       for (int r = 0; r < 4; ++r) S[m][r] = W0h[seg_srow(m, g, r) * D + 16 * W + li];
   }
 
+  // second halves of the pair slots that hold a single tile (an even query block's diagonal tile):
+  // zero once, never written again (visible to every wave after the first barrier of the loop)
+  if (W == 0) {
+#pragma unroll
+    for (int ib = 0; ib < NB; ib += 2) {
+      const int po = ppair_slot(ib, ib / 2) * 1024 + 8 + l * 16;
+      *(uint2*)(smem + Cfg::OFF_P + po) = uint2{0u, 0u};
+      *(uint2*)(smem + Cfg::OFF_P + Cfg::P_PLANE + po) = uint2{0u, 0u};
+    }
+  }
+
   static_assert(Cfg::STAGES == 3, "the vmcnt waits below count the loads of two tiles in flight");
   for (int i = 0; i < nt; ++i) {
     // Tile i has landed once only later-issued loads (and output stores) may be outstanding: per
@@ -305,7 +325,7 @@ __device__ __forceinline__ void seg_wave(const SegArgs& A, unsigned char* smem, 
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     }
     issue_q(i + Cfg::STAGES - 1);   // into the slot read during tile i-1
-    const unsigned char* st = smem + (i % Cfg::STAGES) * Cfg::STAGE;
+    const unsigned char* st = smem + Cfg::OFF_RING + (i % Cfg::STAGES) * Cfg::STAGE;
     const unsigned char* ks = st + Cfg::OFF_K;
     const unsigned char* vs = st + Cfg::OFF_V;
     const float* es = (const float*)(st + Cfg::OFF_E);
@@ -339,8 +359,9 @@ __device__ __forceinline__ void seg_wave(const SegArgs& A, unsigned char* smem, 
 #pragma unroll
         for (int r = 0; r < 4; ++r) f[r] = (jb == ib && 4 * g + r > li) ? 0.f : p[r] * e4[r];
         const uint2 s01 = split2(f[0], f[1]), s23 = split2(f[2], f[3]);
-        *(uint2*)(pb + t * 512 + l * 8) = uint2{s01.x, s23.x};
-        *(uint2*)(pb + Cfg::P_PLANE + t * 512 + l * 8) = uint2{s01.y, s23.y};
+        const int po = ppair_slot(ib, jb >> 1) * 1024 + (jb & 1) * 8 + l * 16;
+        *(uint2*)(pb + po) = uint2{s01.x, s23.x};
+        *(uint2*)(pb + Cfg::P_PLANE + po) = uint2{s01.y, s23.y};
       }
     };
     // O_W^T = S_W^T Q^T with S_W as bf16 hi + lo
@@ -380,15 +401,9 @@ __device__ __forceinline__ void seg_wave(const SegArgs& A, unsigned char* smem, 
     for (int ib = 0; ib < NB; ++ib)
 #pragma unroll
       for (int kc = 0; 2 * kc <= ib; ++kc) {
-        const int t0i = ptile_index(2 * kc, ib);
-        bf16x4 h1 = bf16x4{(bf16)0.f, (bf16)0.f, (bf16)0.f, (bf16)0.f}, l1 = h1;
-        if (2 * kc + 1 <= ib) {
-          const int t1i = ptile_index(2 * kc + 1, ib);
-          h1 = *(const bf16x4*)(pb + t1i * 512 + l * 8);
-          l1 = *(const bf16x4*)(pb + Cfg::P_PLANE + t1i * 512 + l * 8);
-        }
-        const bf16x8 bh_ = join(*(const bf16x4*)(pb + t0i * 512 + l * 8), h1);
-        const bf16x8 bl_ = join(*(const bf16x4*)(pb + Cfg::P_PLANE + t0i * 512 + l * 8), l1);
+        const int po = ppair_slot(ib, kc) * 1024 + l * 16;
+        const bf16x8 bh_ = *(const bf16x8*)(pb + po);
+        const bf16x8 bl_ = *(const bf16x8*)(pb + Cfg::P_PLANE + po);
         const bf16x8 av = join(vt[2 * kc], vt[2 * kc + 1]);
         acc[ib] = mfma16(av, bh_, acc[ib]);
         acc[ib] = mfma16(av, bl_, acc[ib]);
@@ -409,7 +424,7 @@ __device__ __forceinline__ void seg_wave(const SegArgs& A, unsigned char* smem, 
       qs_mfma();
     }
     // outputs into the V region of this slot (written out after the next barrier)
-    unsigned char* ob = smem + (i % Cfg::STAGES) * Cfg::STAGE + Cfg::OFF_V;
+    unsigned char* ob = smem + Cfg::OFF_RING + (i % Cfg::STAGES) * Cfg::STAGE + Cfg::OFF_V;
 #pragma unroll
     for (int ib = 0; ib < NB; ++ib)
       *(bf16x4*)(ob + ib * 16 * ROWB + ofr) = to_bf16x4(acc[ib][0], acc[ib][1], acc[ib][2], acc[ib][3]);
