@@ -415,13 +415,17 @@ __device__ __forceinline__ void seg_wave(const SegArgs& A, unsigned char* smem, 
     scores();
     load_update();
     barrier();                    // score tiles visible; V of this tile read by everyone
-    issue_kve(i + Cfg::STAGES - 1);
+    // The two waves of a SIMD take Q S and the intra-tile product in opposite orders, and issue the
+    // next K/V/eta copies at different points (measured on gfx950: with all eight waves issuing them
+    // right after the barrier, the second wave of each SIMD stalled ~1000 cycles on the issue)
     if (W < NW / 2) {
+      issue_kve(i + Cfg::STAGES - 1);
       qs_mfma();
       av_mfma();
     } else {
       av_mfma();
       qs_mfma();
+      issue_kve(i + Cfg::STAGES - 1);
     }
     // outputs into the V region of this slot (written out after the next barrier)
     unsigned char* ob = smem + Cfg::OFF_RING + (i % Cfg::STAGES) * Cfg::STAGE + Cfg::OFF_V;
