@@ -259,7 +259,7 @@ def main():
             if name == a.workload:
                 continue
             try:
-                others[name] = run_workload(name, max(3, a.steps // 4), 2, a.flush_mb)
+                others[name] = run_workload(name, max(10, a.steps // 2), 3, a.flush_mb)
             except Exception as e:  # a mode not built yet is reported, not fatal
                 others[name] = {"error": str(e)[:200]}
     s = workloads.spec(a.workload)
