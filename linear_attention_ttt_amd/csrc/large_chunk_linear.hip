@@ -398,6 +398,7 @@ hipError_t launch_lact(const LargeChunkArgs& a, hipStream_t stream, const Timing
   int part_len = (chunk + 3) / 4;
   part_len = part_len < 256 ? 256 : part_len;
   part_len = (part_len + 63) / 64 * 64;
+  part_len = part_len > (1 << 20) ? (1 << 20) : part_len;   // 32-bit byte offsets within a part
   const int parts = (chunk + part_len - 1) / part_len;
   hipLaunchKernelGGL(lact_read_kernel<D>, dim3(BH * nchunks * parts), dim3(256), Cfg::LDS, stream, (const bf16*)a.Q,
                      wprev, (bf16*)a.O, T, chunk, nchunks, parts, part_len);

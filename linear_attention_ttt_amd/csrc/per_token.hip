@@ -807,6 +807,8 @@ SegPlan per_token_seg_plan(int64_t BH, int64_t T, int64_t dk) {
   const int64_t nchunks = (T + 63) / 64;
   int64_t p = BH >= slots ? 1 : slots / BH;
   p = std::max<int64_t>(1, std::min(p, nchunks));
+  // a segment's bytes are addressed with 32-bit offsets: at most 2^22 tokens (1 GB at d = 128) each
+  p = std::max<int64_t>(p, (nchunks + (1 << 16) - 1) >> 16);
   const int64_t tiles = nchunks > 0 ? (nchunks + p - 1) / p : 0;
   const int64_t nseg = tiles > 0 ? (nchunks + tiles - 1) / tiles : 1;
   return SegPlan{(int)nseg, (int)(tiles * 64)};

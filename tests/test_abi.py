@@ -143,6 +143,10 @@ def test_per_token_workspace():
         8 * 32 * 128 * 128 * 4                                  # 32 heads x 8 segments
     assert la.workspace_bytes(la.make_desc(1, 1, 300, 64, 64, 0, la.BF16), 64, "per_token_linear") == \
         5 * 64 * 64 * 4                                         # 5 tiles -> 5 segments of one tile
+    # enough heads for one segment each, but a segment holds at most 2^22 tokens (32-bit byte offsets)
+    assert la.workspace_bytes(la.make_desc(256, 1, 1 << 22, 128, 128, 0, la.BF16), 64, "per_token_linear") == 0
+    assert la.workspace_bytes(la.make_desc(256, 1, (1 << 22) + 64, 128, 128, 0, la.BF16), 64, "per_token_linear") == \
+        2 * 256 * 128 * 128 * 4
     assert call(desc=d, mode=0, chunk=64, ws=None, ws_bytes=0) == 8
     assert call(desc=d, mode=0, chunk=64, ws_bytes=n - 1) == 8
 
