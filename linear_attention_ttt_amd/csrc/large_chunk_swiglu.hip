@@ -308,23 +308,29 @@ __global__ __launch_bounds__(SW_WAVES * 64, 1) void swiglu_recur_kernel(
     }
 
     // ---- end of chunk: the waves add their partial gradients in a fixed order, then normalise ----
-    // dW1 lane layout: [d = 16m + 4g + r][u = li]; dW2: [u = 4g + r][d = 16m + li]
-    for (int k = 0; k < SW_WAVES; ++k) {
-      if (w == k) {
-        floatx4 o1[8], o3[8], o2[8];
+    // dW1 lane layout: [d = 16m + 4g + r][u = li]; dW2: [u = 4g + r][d = 16m + li].  Every weight is
+    // updated as (((W + P0) + P1) + P2) + P3 (P_k: wave k's partial), pipelined over quarters of the
+    // weights: in pass p wave k adds its partial to quarter p - k (row tiles 2q, 2q+1 of the three
+    // matrices), so the 4 adds of a quarter stay in wave order and 7 short passes replace 4 full ones.
 #pragma unroll
-        for (int m = 0; m < 8; ++m) {
-          const int f = ((m * 4 + g) * 16 + li) * 4;   // = w13i(16m + 4g, li) = w2i(4g, 16m + li)
-          o1[m] = *(const floatx4*)(S.w1 + f);
-          o3[m] = *(const floatx4*)(S.w3 + f);
-          o2[m] = *(const floatx4*)(S.w2 + f);
+    for (int p = 0; p < SW_WAVES + 3; ++p) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (q != p - w) continue;        // wave-uniform
+        floatx4 o1[2], o3[2], o2[2];
+#pragma unroll
+        for (int mm = 0; mm < 2; ++mm) {
+          const int f = (((2 * q + mm) * 4 + g) * 16 + li) * 4;   // = w13i(16m + 4g, li) = w2i(4g, 16m + li)
+          o1[mm] = *(const floatx4*)(S.w1 + f);
+          o3[mm] = *(const floatx4*)(S.w3 + f);
+          o2[mm] = *(const floatx4*)(S.w2 + f);
         }
 #pragma unroll
-        for (int m = 0; m < 8; ++m) {
-          const int f = ((m * 4 + g) * 16 + li) * 4;
-          *(floatx4*)(S.w1 + f) = o1[m] + dW1[m];
-          *(floatx4*)(S.w3 + f) = o3[m] + dW3[m];
-          *(floatx4*)(S.w2 + f) = o2[m] + dW2[m];
+        for (int mm = 0; mm < 2; ++mm) {
+          const int f = (((2 * q + mm) * 4 + g) * 16 + li) * 4;
+          *(floatx4*)(S.w1 + f) = o1[mm] + dW1[2 * q + mm];
+          *(floatx4*)(S.w3 + f) = o3[mm] + dW3[2 * q + mm];
+          *(floatx4*)(S.w2 + f) = o2[mm] + dW2[2 * q + mm];
         }
       }
       __syncthreads();
