@@ -339,20 +339,30 @@ __global__ __launch_bounds__(SW_WAVES * 64, 1) void swiglu_recur_kernel(
     if (w < 2) {
       float* Wm = w == 0 ? S.w1 : S.w3;
       const int u = l & 15, r0 = (l >> 4) * 32;
+      // rows r0 .. r0+31 of unit u as 8 groups of 4 consecutive rows (16 bytes each in this layout)
+      floatx4 x[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) x[k] = *(const floatx4*)(Wm + w13i(r0 + 4 * k, u));
       float ss = 0.f;
-#pragma unroll 8
-      for (int r = 0; r < 32; ++r) ss = fmaf(Wm[w13i(r0 + r, u)], Wm[w13i(r0 + r, u)], ss);
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) ss = fmaf(x[k][j], x[k][j], ss);
       ss += __shfl_xor(ss, 16);
       ss += __shfl_xor(ss, 32);
       const float inv = 1.0f / fmaxf(sqrtf(ss), 1e-12f);
-#pragma unroll 8
-      for (int r = 0; r < 32; ++r) Wm[w13i(r0 + r, u)] *= inv;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) *(floatx4*)(Wm + w13i(r0 + 4 * k, u)) = x[k] * inv;
     } else if (w < 4) {
       // W2 column d: partial sum of squares over this slice's units
       const int d = (w - 2) * 64 + l;
       float ss = 0.f;
 #pragma unroll
-      for (int u = 0; u < NS; ++u) ss = fmaf(S.w2[w2i(u, d)], S.w2[w2i(u, d)], ss);
+      for (int k = 0; k < NS / 4; ++k) {   // units 4k .. 4k+3 of column d: 16 bytes in this layout
+        const floatx4 x = *(const floatx4*)(S.w2 + w2i(4 * k, d));
+#pragma unroll
+        for (int j = 0; j < 4; ++j) ss = fmaf(x[j], x[j], ss);
+      }
       __hip_atomic_store(&ss2[(((size_t)bh * 2 + (c & 1)) * SW_NSL + sl) * D + d], ss, __ATOMIC_RELAXED,
                          __HIP_MEMORY_SCOPE_AGENT);
       // The partial norms are the only data exchanged, and every access to them is a device-scope
@@ -383,7 +393,7 @@ __global__ __launch_bounds__(SW_WAVES * 64, 1) void swiglu_recur_kernel(
                                 __HIP_MEMORY_SCOPE_AGENT);
       const float inv = 1.0f / fmaxf(sqrtf(ss), 1e-12f);
 #pragma unroll
-      for (int u = 0; u < NS; ++u) S.w2[w2i(u, d)] *= inv;
+      for (int k = 0; k < NS / 4; ++k) *(floatx4*)(S.w2 + w2i(4 * k, d)) *= inv;
     }
     __syncthreads();
     if (c + 1 < nchunks) store_state(c + 1);
