@@ -238,7 +238,7 @@ def main():
                          "FETCH_SIZE / WRITE_SIZE counter runs")
     a = ap.parse_args()
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: libttt_la has no multi-GPU path "
               "(every (b,h) recurrence is independent; sharding B*H across GPUs needs no communication)",
               file=sys.stderr)
         sys.exit(2)

@@ -123,7 +123,7 @@ def test_workspace_query_and_check():
     d = la.make_desc(1, 12, 196608, 64, 64, 0, la.BF16)
     n = la.workspace_bytes(d, 4096, "large_chunk_linear")
     if n == 0:
-        pytest.skip("large-chunk linear needs no workspace in this build")
+        pytest.skip("large-chunk linear needs no workspace for this problem")
     assert call(desc=d, mode=1, chunk=4096, ws=None, ws_bytes=0) == 8
     assert call(desc=d, mode=1, chunk=4096, ws_bytes=n - 1) == 8
 
