@@ -28,7 +28,7 @@ what the cited passage says in words):
   are L2-normalised after the update.  Memory is either a linear map or a
   SwiGLU MLP with three matrices.
 
-Readings taken where the pages are silent (each also listed in the design doc):
+Readings taken where the pages are silent:
 row-vector convention ``o = q W`` with ``W`` stored ``[d_in, d_out]``; the
 post-update normalisation gives every output unit's fan-in vector (a column
 of the ``[d_in, d_out]`` store) unit L2 norm, dividing by
