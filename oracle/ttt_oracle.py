@@ -26,7 +26,11 @@ what the cited passage says in words):
   chunk reads the memory left by the previous chunks, then one summed,
   eta-weighted gradient step is applied for the whole chunk and the weights
   are L2-normalised after the update.  Memory is either a linear map or a
-  SwiGLU MLP with three matrices.
+  SwiGLU MLP with three matrices.  ``read_first=False`` gives the
+  update-then-read order the LaCT review's read-order section describes for
+  posed-image view synthesis (the input set is absorbed, then queried),
+  applied chunk by chunk: a chunk first updates and normalises the weights,
+  then its queries read the result.
 
 Readings taken where the pages are silent:
 row-vector convention ``o = q W`` with ``W`` stored ``[d_in, d_out]``; the
@@ -160,7 +164,7 @@ def per_token_linear(Q, K, V, eta, W0, inclusive=True):
     return O, W
 
 
-def large_chunk_linear(Q, K, V, eta, W0, chunk, normalize=True):
+def large_chunk_linear(Q, K, V, eta, W0, chunk, normalize=True, read_first=True):
     """LaCT with a linear fast weight.  For each chunk (the last may be
     shorter): every query of the chunk reads W (the state left by earlier
     chunks); then W takes one step on the chunk's summed, eta-weighted
@@ -170,6 +174,7 @@ def large_chunk_linear(Q, K, V, eta, W0, chunk, normalize=True):
     non-linear-memory section (summed per-token-rate gradients, L2
     normalisation after the update), read-order section (a chunk reads
     the memory of earlier chunks and only then updates it).
+    ``read_first=False``: the chunk's queries read W after its update.
     ``normalize=False`` is an oracle-only switch used by the pins."""
     Q, K, V, eta, W = map(_f64, (Q, K, V, eta, W0))
     W = W.copy()
@@ -177,16 +182,19 @@ def large_chunk_linear(Q, K, V, eta, W0, chunk, normalize=True):
     O = np.zeros(Q.shape[:-1] + (V.shape[-1],))
     for s in range(0, T, chunk):
         e = min(s + chunk, T)
-        O[:, :, s:e, :] = np.matmul(Q[:, :, s:e, :], W)
+        if read_first:
+            O[:, :, s:e, :] = np.matmul(Q[:, :, s:e, :], W)
         g = linear_binding_grad(K[:, :, s:e, :], V[:, :, s:e, :], eta[:, :, s:e])
         W = W - g
         if normalize:
             W = normalize_columns(W)
+        if not read_first:
+            O[:, :, s:e, :] = np.matmul(Q[:, :, s:e, :], W)
     return O, W
 
 
 def large_chunk_swiglu(Q, K, V, eta, W1, W3, W2, chunk, normalize=True,
-                       update_w1w3=True):
+                       update_w1w3=True, read_first=True):
     """LaCT with a SwiGLU fast-weight MLP.  For each chunk: the chunk's
     queries read ``f_W``; the eta-weighted binding-loss gradient of the
     chunk is taken at those same weights; one descent step is applied to
@@ -194,6 +202,8 @@ def large_chunk_swiglu(Q, K, V, eta, W1, W3, W2, chunk, normalize=True,
     d, W2 columns over d_h).
 
     LaCT review, non-linear memory and read-order sections.
+    ``read_first=False``: the chunk's queries read the weights after its
+    update (the gradient is still taken at the weights before it).
     ``normalize=False`` and ``update_w1w3=False`` are oracle-only switches
     used by the pins.  Returns (O, (W1, W3, W2))."""
     Q, K, V, eta, W1, W3, W2 = map(_f64, (Q, K, V, eta, W1, W3, W2))
@@ -202,7 +212,8 @@ def large_chunk_swiglu(Q, K, V, eta, W1, W3, W2, chunk, normalize=True,
     O = np.zeros(Q.shape[:-1] + (W2.shape[-1],))
     for s in range(0, T, chunk):
         e = min(s + chunk, T)
-        O[:, :, s:e, :] = swiglu_forward(Q[:, :, s:e, :], W1, W3, W2)
+        if read_first:
+            O[:, :, s:e, :] = swiglu_forward(Q[:, :, s:e, :], W1, W3, W2)
         g1, g3, g2 = swiglu_binding_grad(K[:, :, s:e, :], V[:, :, s:e, :],
                                          eta[:, :, s:e], W1, W3, W2)
         if update_w1w3:
@@ -214,6 +225,8 @@ def large_chunk_swiglu(Q, K, V, eta, W1, W3, W2, chunk, normalize=True,
                 W1 = normalize_columns(W1)
                 W3 = normalize_columns(W3)
             W2 = normalize_columns(W2)
+        if not read_first:
+            O[:, :, s:e, :] = swiglu_forward(Q[:, :, s:e, :], W1, W3, W2)
     return O, (W1, W3, W2)
 
 
@@ -241,16 +254,20 @@ def forward(Q, K, V, eta, W0, chunk, mode, d_h=None):
     """Dispatch by mode name, with the library's argument order.
 
     ``mode``: "per_token_linear", "large_chunk_linear" or
-    "large_chunk_swiglu".  For per-token mode ``chunk`` does not change the
-    result and is ignored.  For SwiGLU, W0 is the packed state and ``d_h``
-    is required.  Returns (O, W_final) with W_final in W0's layout."""
-    if mode == "per_token_linear":
-        return per_token_linear(Q, K, V, eta, W0)
-    if mode == "large_chunk_linear":
-        return large_chunk_linear(Q, K, V, eta, W0, chunk)
-    if mode == "large_chunk_swiglu":
+    "large_chunk_swiglu", and the ordering variants
+    "per_token_linear_exclusive" (a query reads before its token's update),
+    "large_chunk_linear_update_first" and "large_chunk_swiglu_update_first"
+    (a chunk updates, then reads).  For per-token mode ``chunk`` does not
+    change the result and is ignored.  For SwiGLU, W0 is the packed state and
+    ``d_h`` is required.  Returns (O, W_final) with W_final in W0's layout."""
+    if mode in ("per_token_linear", "per_token_linear_exclusive"):
+        return per_token_linear(Q, K, V, eta, W0, inclusive=(mode == "per_token_linear"))
+    if mode in ("large_chunk_linear", "large_chunk_linear_update_first"):
+        return large_chunk_linear(Q, K, V, eta, W0, chunk, read_first=(mode == "large_chunk_linear"))
+    if mode in ("large_chunk_swiglu", "large_chunk_swiglu_update_first"):
         d = Q.shape[-1]
         W1, W3, W2 = swiglu_unpack(_f64(W0), d, d_h)
-        O, (W1, W3, W2) = large_chunk_swiglu(Q, K, V, eta, W1, W3, W2, chunk)
+        O, (W1, W3, W2) = large_chunk_swiglu(Q, K, V, eta, W1, W3, W2, chunk,
+                                             read_first=(mode == "large_chunk_swiglu"))
         return O, swiglu_pack(W1, W3, W2)
     raise ValueError(f"unknown mode {mode!r}")

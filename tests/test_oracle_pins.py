@@ -343,6 +343,92 @@ def test_p6_last_layer_only_is_linear_attention_in_feature_space(chunk):
     assert np.allclose(W2T, W2 + np.einsum("bhti,bht,bhtj->bhij", fk, eta, V), atol=1e-11)
 
 
+# ---------------------------------------------------------------------------
+# Ordering variant: a chunk updates, then reads (LaCT review, read-order section)
+# ---------------------------------------------------------------------------
+
+def test_update_first_linear_single_chunk():
+    Q, K, V, eta, W0 = rand_case(seed=21)
+    T = Q.shape[2]
+    O, W = TO.large_chunk_linear(Q, K, V, eta, W0, T, read_first=False)
+    M = W0 + np.einsum("bhti,bht,bhtj->bhij", K, eta, V)
+    Mn = M / np.linalg.norm(M, axis=-2, keepdims=True)
+    assert np.allclose(W, Mn, atol=1e-13)
+    assert np.allclose(O, Q @ Mn, atol=1e-13)
+
+
+@pytest.mark.parametrize("chunk", [1, 3, 4, 13, 20])
+def test_update_first_unnormalised_is_inclusive_block_linear_attention(chunk):
+    Q, K, V, eta, W0 = rand_case(seed=22)
+    T = Q.shape[2]
+    O, _ = TO.large_chunk_linear(Q, K, V, eta, W0, chunk, normalize=False, read_first=False)
+    c = np.arange(T) // chunk
+    mask = (c[None, :] <= c[:, None]).astype(np.float64)         # earlier chunks and the own chunk
+    P = np.matmul(Q, np.swapaxes(K, -1, -2)) * mask * eta[:, :, None, :]
+    assert np.allclose(O, Q @ W0 + P @ V, atol=1e-11)
+    if chunk == 1:
+        Oin, _ = TO.per_token_linear(Q, K, V, eta, W0, inclusive=True)
+        assert np.allclose(O, Oin, atol=1e-12)
+
+
+@pytest.mark.parametrize("chunk", [1, 3, 10])
+def test_update_first_leaves_the_state_sequence_unchanged(chunk):
+    Q, K, V, eta, W0 = rand_case(seed=23)
+    _, Wa = TO.large_chunk_linear(Q, K, V, eta, W0, chunk)
+    _, Wb = TO.large_chunk_linear(Q, K, V, eta, W0, chunk, read_first=False)
+    assert np.array_equal(Wa, Wb)
+    Q, K, V, eta, W1, W3, W2 = rand_swiglu(seed=24)
+    _, Sa = TO.large_chunk_swiglu(Q, K, V, eta, W1, W3, W2, chunk)
+    _, Sb = TO.large_chunk_swiglu(Q, K, V, eta, W1, W3, W2, chunk, read_first=False)
+    for a, b in zip(Sa, Sb):
+        assert np.array_equal(a, b)
+
+
+def test_update_first_swiglu_single_chunk_reads_the_stepped_weights():
+    Q, K, V, eta, W1, W3, W2 = rand_swiglu(seed=25)
+    T = Q.shape[2]
+    O, (N1, N3, N2) = TO.large_chunk_swiglu(Q, K, V, eta, W1, W3, W2, T, read_first=False)
+    ws = [torch.tensor(w, requires_grad=True) for w in (W1, W3, W2)]
+    torch_swiglu_loss(*map(torch.tensor, (K, V, eta)), *ws).sum().backward()
+    stepped = []
+    for w in ws:
+        st = w.detach().numpy() - w.grad.numpy()
+        stepped.append(st / np.linalg.norm(st, axis=-2, keepdims=True))
+    for new, ref in zip((N1, N3, N2), stepped):
+        assert np.allclose(new, ref, atol=1e-12)
+    assert np.allclose(O, torch_mlp(Q, *stepped), atol=1e-12)
+
+
+@pytest.mark.parametrize("chunk", [1, 3, 10])
+def test_update_first_swiglu_last_layer_only_is_inclusive_feature_attention(chunk):
+    Q, K, V, eta, W1, W3, W2 = rand_swiglu(seed=26)
+    T = Q.shape[2]
+    O, _ = TO.large_chunk_swiglu(Q, K, V, eta, W1, W3, W2, chunk, normalize=False, update_w1w3=False,
+                                 read_first=False)
+    phi = lambda X: (torch.nn.functional.silu(torch.tensor(X) @ torch.tensor(W1))  # noqa: E731
+                     * (torch.tensor(X) @ torch.tensor(W3))).numpy()
+    fq, fk = phi(Q), phi(K)
+    c = np.arange(T) // chunk
+    mask = (c[None, :] <= c[:, None]).astype(np.float64)
+    P = np.matmul(fq, np.swapaxes(fk, -1, -2)) * mask * eta[:, :, None, :]
+    assert np.allclose(O, fq @ W2 + P @ V, atol=1e-11)
+
+
+def test_variant_mode_names_dispatch():
+    Q, K, V, eta, W0 = rand_case(seed=27)
+    O1, W1 = oracle.forward(Q, K, V, eta, W0, 5, "per_token_linear_exclusive")
+    O2, W2 = TO.per_token_linear(Q, K, V, eta, W0, inclusive=False)
+    assert np.array_equal(O1, O2) and np.array_equal(W1, W2)
+    O1, W1 = oracle.forward(Q, K, V, eta, W0, 5, "large_chunk_linear_update_first")
+    O2, W2 = TO.large_chunk_linear(Q, K, V, eta, W0, 5, read_first=False)
+    assert np.array_equal(O1, O2) and np.array_equal(W1, W2)
+    Q, K, V, eta, A1, A3, A2 = rand_swiglu(seed=28)
+    Wp = TO.swiglu_pack(A1, A3, A2)
+    O1, Wf = oracle.forward(Q, K, V, eta, Wp, 3, "large_chunk_swiglu_update_first", d_h=6)
+    O2, Ws = TO.large_chunk_swiglu(Q, K, V, eta, A1, A3, A2, 3, read_first=False)
+    assert np.array_equal(O1, O2) and np.array_equal(Wf, TO.swiglu_pack(*Ws))
+
+
 def test_swiglu_pack_roundtrip_and_dispatch():
     Q, K, V, eta, W1, W3, W2 = rand_swiglu(seed=16)
     Wp = TO.swiglu_pack(W1, W3, W2)
