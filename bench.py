@@ -33,6 +33,19 @@ BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 FP32_VALU_PEAK_TFLOPS = 157.3  # MI355X fp32 vector
 
 
+# each method's other read order (exclusive per-token read, update-then-read chunks): same kernels and work
+OTHER_ORDER = {"per_token_linear": "per_token_linear_exclusive",
+               "large_chunk_linear": "large_chunk_linear_update_first",
+               "large_chunk_swiglu": "large_chunk_swiglu_update_first"}
+
+
+def method_of(mode: str) -> str:
+    for base, other in OTHER_ORDER.items():
+        if mode == other:
+            return base
+    return mode
+
+
 def algorithmic(s: dict) -> tuple[int, float]:
     """Bytes the method must move and flops it must do for one forward pass.
 
@@ -44,11 +57,12 @@ def algorithmic(s: dict) -> tuple[int, float]:
     B, H, T, dk, dv, dh, C = s["B"], s["H"], s["T"], s["d_k"], s["d_v"], s["d_h"], s["chunk"]
     es = 2 if s["dtype"] == "bf16" else 4
     n = B * H * T
-    state = B * H * (3 * dk * dh if s["mode"] == "large_chunk_swiglu" else dk * dv) * 4
+    m = method_of(s["mode"])
+    state = B * H * (3 * dk * dh if m == "large_chunk_swiglu" else dk * dv) * 4
     nbytes = n * (2 * dk + 2 * dv) * es + n * 4 + 2 * state
-    if s["mode"] == "per_token_linear":
+    if m == "per_token_linear":
         flops = n * (4 * dk * dv + (C + 1) * (dk + dv))
-    elif s["mode"] == "large_chunk_linear":
+    elif m == "large_chunk_linear":
         flops = n * 4 * dk * dv + B * H * (-(-T // C)) * 3 * dk * dv
     else:
         flops = n * 18 * dk * dh
@@ -68,19 +82,22 @@ def dominant_kernel(s: dict) -> tuple[str, float, str]:
     B, H, T, dk, dv, dh = s["B"], s["H"], s["T"], s["d_k"], s["d_v"], s["d_h"]
     es = 2 if s["dtype"] == "bf16" else 4
     n = B * H * T
-    if s["mode"] == "per_token_linear":
+    m = method_of(s["mode"])
+    if m == "per_token_linear":
         return ("pt_seg_kernel (output pass)" if s["dtype"] == "bf16" else "per_token_fp32_kernel",
                 float(algorithmic(s)[0]), "hbm")
-    if s["mode"] == "large_chunk_linear":
+    if m == "large_chunk_linear":
         return "lact_delta_kernel (chunk update)", float(n * ((dk + dv) * es + 4)), "hbm"
     return "swiglu_recur_kernel (recurrence)", float(n * 12 * dk * dh), "mfma"
 
 
-def run_workload(name: str, steps: int, warmup: int, flush_mb: int):
+def run_workload(name: str, steps: int, warmup: int, flush_mb: int, other_order: bool = False):
     import torch
     import linear_attention_ttt_amd as la
 
     s = workloads.spec(name)
+    if other_order:
+        s["mode"] = OTHER_ORDER[s["mode"]]
     x = workloads.generate(s, seed=0)
     dev = torch.device("cuda:0")
     dt = torch.bfloat16 if s["dtype"] == "bf16" else torch.float32
@@ -191,13 +208,13 @@ def traffic_per_launch(kernel: str):
     return int(m_bytes.group(1))
 
 
-def cpu_baseline(name: str, target_s: float = 12.0):
+def cpu_baseline(name: str, mode: str, target_s: float = 12.0):
     """Time the fp64 oracle on a bounded sample of the workload: whole
     sequences of a subset of the (independent) heads, scaled to the full
     workload's tokens/s."""
     import oracle
 
-    s = workloads.spec(name)
+    s = workloads.spec(name, mode=mode)
     x = workloads.generate(s, seed=0)
     BH = s["B"] * s["H"]
 
@@ -233,6 +250,9 @@ def main():
     ap.add_argument("--no-others", action="store_true", help="skip the other workloads' sub-records")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--flush-mb", type=int, default=512)
+    ap.add_argument("--other-order", action="store_true",
+                    help="run every workload in its method's other read order (exclusive per-token read, "
+                         "update-then-read chunks)")
     ap.add_argument("--calibrate-copy-mb", type=int, default=0,
                     help="first copy a buffer of this size 3 times (untimed), as a known-size reference for "
                          "FETCH_SIZE / WRITE_SIZE counter runs")
@@ -252,21 +272,21 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    head = run_workload(a.workload, a.steps, a.warmup, a.flush_mb)
+    head = run_workload(a.workload, a.steps, a.warmup, a.flush_mb, a.other_order)
     others = {}
     if not a.no_others:
         for name in workloads.WORKLOADS:
             if name == a.workload:
                 continue
             try:
-                others[name] = run_workload(name, max(10, a.steps // 2), 3, a.flush_mb)
+                others[name] = run_workload(name, max(10, a.steps // 2), 3, a.flush_mb, a.other_order)
             except Exception as e:  # a mode not built yet is reported, not fatal
                 others[name] = {"error": str(e)[:200]}
-    s = workloads.spec(a.workload)
+    s = workloads.spec(a.workload, mode=head["mode"])
     k = head["kernel"]
     peak = HBM_PEAK_GBS if k["bound"] == "hbm" else BF16_PEAK_TFLOPS
     roof = {"bound": k["bound"], "achieved": k["achieved"], "peak": peak, "unit": k["unit"],
-            "frac": k["achieved"] / peak, "traffic": traffic_per_launch(k["name"]),
+            "frac": k["achieved"] / peak, "traffic": None if a.other_order else traffic_per_launch(k["name"]),
             "kernel": k["name"], "kernel_ms": k["ms_mean"], "units_per_launch": k["units_per_launch"],
             "step_frac": head["hbm_frac"] if k["bound"] == "hbm" else head["bf16_mfma_frac"]}
     line = {
@@ -287,7 +307,7 @@ def main():
         "bf16_mfma_frac": head["bf16_mfma_frac"],
         "token_heads_per_s": head["token_heads_per_s"],
         "roofline": roof,
-        "cpu_baseline": None if a.no_cpu else cpu_baseline(a.workload),
+        "cpu_baseline": None if a.no_cpu else cpu_baseline(a.workload, head["mode"]),
         "workloads": others,
     }
     print(json.dumps(line), flush=True)

@@ -29,6 +29,15 @@
  *     W1, W3, W2; then columns of W1 and W3 (over d) and of W2 (over d_h)
  *     are divided by max(norm, 1e-12).
  *
+ *   Ordering variants (the other read orders the pages describe):
+ *   TTT_LA_PER_TOKEN_LINEAR_EXCLUSIVE: a query reads before its own token's
+ *     step: o_t = q_t (W0 + sum_{i<t} eta_i k_i^T v_i); W_out as above.
+ *   TTT_LA_LARGE_CHUNK_LINEAR_UPDATE_FIRST, TTT_LA_LARGE_CHUNK_SWIGLU_UPDATE_FIRST:
+ *     each chunk first takes its step (gradient at the weights before it)
+ *     and is normalised, then its queries read the result (the update-then-
+ *     read order of the LaCT review's read-order section, applied chunk by
+ *     chunk).  W_out is the same as in the read-first mode.
+ *
  * Conventions: row vectors, W stored [d_in, d_out] row-major; every tensor
  * contiguous with the last dimension fastest.
  *
@@ -67,7 +76,10 @@ enum {
 enum {
     TTT_LA_PER_TOKEN_LINEAR = 0,
     TTT_LA_LARGE_CHUNK_LINEAR = 1,
-    TTT_LA_LARGE_CHUNK_SWIGLU = 2
+    TTT_LA_LARGE_CHUNK_SWIGLU = 2,
+    TTT_LA_PER_TOKEN_LINEAR_EXCLUSIVE = 3,
+    TTT_LA_LARGE_CHUNK_LINEAR_UPDATE_FIRST = 4,
+    TTT_LA_LARGE_CHUNK_SWIGLU_UPDATE_FIRST = 5
 };
 
 /* Element type of Q, K, V and O.  eta and the fast-weight state are always
@@ -96,7 +108,9 @@ typedef struct ttt_la_desc {
  *            SwiGLU        [B,H, d*d_h + d*d_h + d_h*d] = W1 [d,d_h] | W3 [d,d_h] | W2 [d_h,d]
  *                          per (b,h), with d = d_k = d_v
  *   chunk  tokens per chunk (>= 1)
- *   mode   TTT_LA_PER_TOKEN_LINEAR | TTT_LA_LARGE_CHUNK_LINEAR | TTT_LA_LARGE_CHUNK_SWIGLU
+ *   mode   TTT_LA_PER_TOKEN_LINEAR | TTT_LA_LARGE_CHUNK_LINEAR | TTT_LA_LARGE_CHUNK_SWIGLU,
+ *          or an ordering variant (3 | 4 | 5: same shapes, support and workspace as
+ *          modes 0 | 1 | 2)
  *   desc   sizes and io_dtype (host pointer)
  *   O      [B,H,T,d_v]  io_dtype, device (written)
  *   W_out  same layout as W0, float32, device (written); W_out == W0 (in
@@ -181,7 +195,7 @@ const char* ttt_la_status_string(int status);
 /* ABI version of this header (incremented on incompatible change). */
 int ttt_la_abi_version(void);
 
-#define TTT_LA_ABI_VERSION 1
+#define TTT_LA_ABI_VERSION 2
 
 #ifdef __cplusplus
 }

@@ -30,25 +30,43 @@ bool mul_ok(int64_t a, int64_t b, int64_t* out) {
   return true;
 }
 
-int64_t state_elems(const ttt_la_desc& d, int mode) {
-  if (mode == TTT_LA_LARGE_CHUNK_SWIGLU) return d.B * d.H * 3 * d.d_k * d.d_h;
+// The three methods, and whether the mode is the method's other read order (exclusive per-token read,
+// update-then-read chunks).  -1 for an unknown mode.
+int32_t method_of(int32_t mode) {
+  switch (mode) {
+    case TTT_LA_PER_TOKEN_LINEAR:
+    case TTT_LA_PER_TOKEN_LINEAR_EXCLUSIVE: return TTT_LA_PER_TOKEN_LINEAR;
+    case TTT_LA_LARGE_CHUNK_LINEAR:
+    case TTT_LA_LARGE_CHUNK_LINEAR_UPDATE_FIRST: return TTT_LA_LARGE_CHUNK_LINEAR;
+    case TTT_LA_LARGE_CHUNK_SWIGLU:
+    case TTT_LA_LARGE_CHUNK_SWIGLU_UPDATE_FIRST: return TTT_LA_LARGE_CHUNK_SWIGLU;
+  }
+  return -1;
+}
+bool other_order(int32_t mode) {
+  return mode == TTT_LA_PER_TOKEN_LINEAR_EXCLUSIVE || mode == TTT_LA_LARGE_CHUNK_LINEAR_UPDATE_FIRST ||
+         mode == TTT_LA_LARGE_CHUNK_SWIGLU_UPDATE_FIRST;
+}
+
+int64_t state_elems(const ttt_la_desc& d, int method) {
+  if (method == TTT_LA_LARGE_CHUNK_SWIGLU) return d.B * d.H * 3 * d.d_k * d.d_h;
   return d.B * d.H * d.d_k * d.d_v;
 }
 
 // Shape, mode, dtype and chunk checks shared by forward and workspace sizing.
 int check_problem(const ttt_la_desc* d, int64_t chunk, int32_t mode) {
   if (!d) return TTT_LA_ERR_NULL;
-  if (mode != TTT_LA_PER_TOKEN_LINEAR && mode != TTT_LA_LARGE_CHUNK_LINEAR && mode != TTT_LA_LARGE_CHUNK_SWIGLU)
-    return TTT_LA_ERR_MODE;
+  const int32_t method = method_of(mode);
+  if (method < 0) return TTT_LA_ERR_MODE;
   if (d->io_dtype != TTT_LA_FP32 && d->io_dtype != TTT_LA_BF16) return TTT_LA_ERR_DTYPE;
   if (d->reserved != 0) return TTT_LA_ERR_SHAPE;
   if (d->B < 1 || d->H < 1 || d->T < 0 || d->d_k < 1 || d->d_v < 1) return TTT_LA_ERR_SHAPE;
-  if (mode == TTT_LA_LARGE_CHUNK_SWIGLU && (d->d_h < 1 || d->d_k != d->d_v)) return TTT_LA_ERR_SHAPE;
+  if (method == TTT_LA_LARGE_CHUNK_SWIGLU && (d->d_h < 1 || d->d_k != d->d_v)) return TTT_LA_ERR_SHAPE;
   int64_t x;
   const int64_t dmax = d->d_k > d->d_v ? d->d_k : d->d_v;
   if (!mul_ok(d->B, d->H, &x) || !mul_ok(x, d->T, &x) || !mul_ok(x, dmax, &x) || !mul_ok(x, 4, &x))
     return TTT_LA_ERR_SHAPE;
-  if (mode == TTT_LA_LARGE_CHUNK_SWIGLU &&
+  if (method == TTT_LA_LARGE_CHUNK_SWIGLU &&
       (!mul_ok(d->B * d->H, 3 * d->d_k, &x) || !mul_ok(x, d->d_h, &x) || !mul_ok(x, 4, &x)))
     return TTT_LA_ERR_SHAPE;
   if (chunk < 1) return TTT_LA_ERR_CHUNK;
@@ -57,7 +75,7 @@ int check_problem(const ttt_la_desc* d, int64_t chunk, int32_t mode) {
 
 bool supported(const ttt_la_desc& d, int64_t chunk, int32_t mode) {
   if (d.T > INT32_MAX || d.B * d.H > (int64_t)1 << 24) return false;
-  switch (mode) {
+  switch (method_of(mode)) {
     case TTT_LA_PER_TOKEN_LINEAR:
       return ttt::per_token_supported(d.d_k, d.d_v, chunk, d.io_dtype);
     case TTT_LA_LARGE_CHUNK_LINEAR:
@@ -69,7 +87,7 @@ bool supported(const ttt_la_desc& d, int64_t chunk, int32_t mode) {
 }
 
 size_t workspace_for(const ttt_la_desc& d, int64_t chunk, int32_t mode) {
-  switch (mode) {
+  switch (method_of(mode)) {
     case TTT_LA_PER_TOKEN_LINEAR:
       return ttt::per_token_workspace(d.B, d.H, d.T, d.d_k, d.d_v, d.io_dtype);
     case TTT_LA_LARGE_CHUNK_LINEAR:
@@ -125,9 +143,10 @@ int ttt_la_forward_timed(const void* Q, const void* K, const void* V, const floa
   const size_t ntok = (size_t)(d.B * d.H * d.T);
   const Range rQ = range(Q, ntok * d.d_k * es), rK = range(K, ntok * d.d_k * es);
   const Range rV = range(V, ntok * d.d_v * es), rE = range(eta, ntok * 4);
-  const Range rW0 = range(W0, (size_t)state_elems(d, mode) * 4);
+  const int32_t method = method_of(mode);
+  const Range rW0 = range(W0, (size_t)state_elems(d, method) * 4);
   const Range rO = range(O, ntok * d.d_v * es);
-  const Range rWo = range(W_out, (size_t)state_elems(d, mode) * 4);
+  const Range rWo = range(W_out, (size_t)state_elems(d, method) * 4);
   const Range rWs = range(workspace, need);
   const Range ins[5] = {rQ, rK, rV, rE, rW0};
   for (const Range& in : ins) {
@@ -143,13 +162,16 @@ int ttt_la_forward_timed(const void* Q, const void* K, const void* V, const floa
   tm.start = (hipEvent_t)ev_start;
   tm.stop = (hipEvent_t)ev_stop;
   hipError_t e = hipSuccess;
-  if (mode == TTT_LA_PER_TOKEN_LINEAR) {
-    ttt::PerTokenArgs a{Q, K, V, eta, W0, O, W_out, workspace, d.B, d.H, d.T, d.d_k, d.d_v, chunk, d.io_dtype};
+  const int other = other_order(mode) ? 1 : 0;
+  if (method == TTT_LA_PER_TOKEN_LINEAR) {
+    ttt::PerTokenArgs a{Q, K, V, eta, W0, O, W_out, workspace, d.B, d.H, d.T, d.d_k, d.d_v, chunk, d.io_dtype,
+                        other};
     e = ttt::launch_per_token(a, s, tm);
   } else {
-    ttt::LargeChunkArgs a{Q, K, V, eta, W0, O, W_out, workspace, d.B, d.H, d.T, d.d_k, d.d_v, d.d_h, chunk, d.io_dtype};
-    e = mode == TTT_LA_LARGE_CHUNK_LINEAR ? ttt::launch_large_chunk_linear(a, s, tm)
-                                          : ttt::launch_large_chunk_swiglu(a, s, tm);
+    ttt::LargeChunkArgs a{Q, K, V, eta, W0, O, W_out, workspace, d.B, d.H, d.T, d.d_k, d.d_v, d.d_h, chunk, d.io_dtype,
+                          other};
+    e = method == TTT_LA_LARGE_CHUNK_LINEAR ? ttt::launch_large_chunk_linear(a, s, tm)
+                                            : ttt::launch_large_chunk_swiglu(a, s, tm);
   }
   return e == hipSuccess ? TTT_LA_OK : TTT_LA_ERR_HIP;
 }

@@ -24,7 +24,8 @@ struct PerTokenArgs {
   float* W_out;
   void* ws;
   int64_t B, H, T, DK, DV, chunk;
-  int dtype;  // 0 = fp32, 1 = bf16
+  int dtype;      // 0 = fp32, 1 = bf16
+  int exclusive;  // 1: a query reads before its own token's step
 };
 
 // Sequence segments of the bf16 per-token path (segments per head, tokens per segment).
@@ -47,6 +48,7 @@ struct LargeChunkArgs {
   void* ws;
   int64_t B, H, T, DK, DV, DH, chunk;
   int dtype;
+  int update_first;  // 1: a chunk takes its step, then its queries read the result
 };
 
 bool large_chunk_linear_supported(int64_t dk, int64_t dv, int64_t chunk, int dtype);

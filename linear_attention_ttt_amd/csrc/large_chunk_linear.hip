@@ -177,7 +177,7 @@ __global__ __launch_bounds__(256, 4) void lact_delta_kernel(const bf16* __restri
 //    the next window of chunks are loaded while the current window is
 //    scanned (two register buffers); the column norm is a DPP wave sum.
 // ---------------------------------------------------------------------------
-template <int D>
+template <int D, bool UF>
 __global__ __launch_bounds__(256) void lact_scan_kernel(const float* __restrict__ W0, const float* __restrict__ part,
                                                         float* __restrict__ wprev_t, float* __restrict__ Wout,
                                                         int nchunks, int nsplit) {
@@ -210,20 +210,24 @@ __global__ __launch_bounds__(256) void lact_scan_kernel(const float* __restrict_
     for (int i = 0; i < WIN; ++i) {
       const int c = c0 + i;
       if (c >= nchunks) break;
-      float* Wt = wprev_t + (((size_t)bh * nchunks + c) * D + j) * D;   // W_{c-1}, transposed
+      // the state chunk c reads, transposed: W_{c-1}, or W_c when a chunk updates first
+      float* Wt = wprev_t + (((size_t)bh * nchunks + c) * D + j) * D;
       float ss = 0.f;
 #pragma unroll
       for (int r = 0; r < RPL; ++r) {
         float d = raw[0][i][r];
 #pragma unroll
         for (int s = 1; s < LC_MAXSPLIT; ++s) d += s < nsplit ? raw[s][i][r] : 0.f;
-        Wt[l + 64 * r] = Wc[r];
+        if (!UF) Wt[l + 64 * r] = Wc[r];
         Wc[r] += d;
         ss = fmaf(Wc[r], Wc[r], ss);
       }
       const float inv = 1.0f / fmaxf(sqrtf(wave_sum(ss)), 1e-12f);
 #pragma unroll
-      for (int r = 0; r < RPL; ++r) Wc[r] *= inv;
+      for (int r = 0; r < RPL; ++r) {
+        Wc[r] *= inv;
+        if (UF) Wt[l + 64 * r] = Wc[r];
+      }
     }
   };
   // two register buffers: the next window is in flight while the current one is scanned
@@ -387,8 +391,8 @@ hipError_t launch_lact(const LargeChunkArgs& a, hipStream_t stream, const Timing
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if ((e = mark(tm.stop, stream)) != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(lact_scan_kernel<D>, dim3(BH * D / 4), dim3(256), 0, stream, a.W0, part, wprev, a.W_out,
-                     nchunks, nsplit);
+  auto kscan = a.update_first ? lact_scan_kernel<D, true> : lact_scan_kernel<D, false>;
+  hipLaunchKernelGGL(kscan, dim3(BH * D / 4), dim3(256), 0, stream, a.W0, part, wprev, a.W_out, nchunks, nsplit);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || nchunks == 0) return e;
   using Cfg = LactReadCfg<D>;

@@ -100,7 +100,8 @@ __global__ void zero_u32_kernel(unsigned* p, int n) {
 __global__ __launch_bounds__(SW_WAVES * 64, 1) void swiglu_recur_kernel(
     const bf16* __restrict__ K, const bf16* __restrict__ V, const float* __restrict__ eta,
     const float* __restrict__ W0, float* __restrict__ Wout, bf16* __restrict__ states, float* __restrict__ ss2,
-    unsigned* __restrict__ counters, unsigned* __restrict__ errflag, int T, int chunk, int nchunks, int head0) {
+    unsigned* __restrict__ counters, unsigned* __restrict__ errflag, int T, int chunk, int nchunks, int head0,
+    int update_first) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
   RecurLds& S = *reinterpret_cast<RecurLds*>(smem_raw);
   constexpr int NT = SW_WAVES * 64;
@@ -159,7 +160,8 @@ __global__ __launch_bounds__(SW_WAVES * 64, 1) void swiglu_recur_kernel(
       split_store8(base + 4 * P + o, base + 5 * P + o, f2);
     }
   };
-  if (nchunks > 0) store_state(0);
+  // state slot c holds the weights chunk c reads: W_{c-1} (W0 for chunk 0), or W_c when a chunk updates first
+  if (nchunks > 0 && !update_first) store_state(0);
 
   // ---- this wave's 32-token groups: in chunk c, groups w + 4k for k < count(c) ----
   // All slices of a head walk a chunk in the same order, so they request the
@@ -396,7 +398,10 @@ __global__ __launch_bounds__(SW_WAVES * 64, 1) void swiglu_recur_kernel(
       for (int k = 0; k < NS / 4; ++k) *(floatx4*)(S.w2 + w2i(4 * k, d)) *= inv;
     }
     __syncthreads();
-    if (c + 1 < nchunks) store_state(c + 1);
+    if (update_first)
+      store_state(c);
+    else if (c + 1 < nchunks)
+      store_state(c + 1);
   }
   wait_vm<0>();
 
@@ -643,9 +648,9 @@ hipError_t launch_large_chunk_swiglu(const LargeChunkArgs& a, hipStream_t stream
   if ((e = mark(tm.start, stream)) != hipSuccess) return e;   // the recurrence: the sequential part
   for (int h0 = 0; h0 < BH; h0 += heads_per_launch) {
     const int nh = std::min(heads_per_launch, BH - h0);
-    int Ti = T, ci = chunk, nci = nchunks, hi = h0;
+    int Ti = T, ci = chunk, nci = nchunks, hi = h0, uf = a.update_first ? 1 : 0;
     void* args[] = {(void*)&Kp, (void*)&Vp, (void*)&Ep, (void*)&W0p, (void*)&Wo, (void*)&states, (void*)&ss2,
-                    (void*)&counters, (void*)&err, (void*)&Ti, (void*)&ci, (void*)&nci, (void*)&hi};
+                    (void*)&counters, (void*)&err, (void*)&Ti, (void*)&ci, (void*)&nci, (void*)&hi, (void*)&uf};
     e = hipLaunchCooperativeKernel((const void*)swiglu_recur_kernel, dim3(nh * SW_NSL), dim3(SW_WAVES * 64), args,
                                    (unsigned)lds_r, stream);
     if (e != hipSuccess) return e;

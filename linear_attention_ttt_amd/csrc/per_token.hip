@@ -194,7 +194,7 @@ struct SegArgs {
 
 // The program of wave W (wave-uniform).  One program for all waves keeps the
 // code within the instruction cache.
-template <int D, int CT>
+template <int D, int CT, bool EXCL>
 __device__ __forceinline__ void seg_wave(const SegArgs& A, unsigned char* smem, int bh, int s, int W, int l) {
   using Cfg = SegCfg<D, CT>;
   constexpr int NB = Cfg::NB;
@@ -357,7 +357,12 @@ __device__ __forceinline__ void seg_wave(const SegArgs& A, unsigned char* smem, 
         const floatx4 e4 = *(const floatx4*)(es + 16 * jb + 4 * g);
         floatx4 f;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) f[r] = (jb == ib && 4 * g + r > li) ? 0.f : p[r] * e4[r];
+        for (int r = 0; r < 4; ++r) {
+          // key 16jb + 4g + r against query 16ib + li: a key after the query (or the query's own key,
+          // for the read before the token's step) is masked
+          const bool masked = jb == ib && (EXCL ? 4 * g + r >= li : 4 * g + r > li);
+          f[r] = masked ? 0.f : p[r] * e4[r];
+        }
         const uint2 s01 = split2(f[0], f[1]), s23 = split2(f[2], f[3]);
         const int po = ppair_slot(ib, jb >> 1) * 1024 + (jb & 1) * 8 + l * 16;
         *(uint2*)(pb + po) = uint2{s01.x, s23.x};
@@ -462,13 +467,13 @@ __device__ __forceinline__ void seg_wave(const SegArgs& A, unsigned char* smem, 
 
 // Outputs of segment s of head bh (grid BH x nseg), starting from W0 plus
 // the increments of the earlier segments of the head.
-template <int D, int CT>
+template <int D, int CT, bool EXCL>
 __global__ __attribute__((amdgpu_flat_work_group_size(1, D / 16 * WAVE),
                           amdgpu_waves_per_eu(SegCfg<D, CT>::WAVES_PER_SIMD))) void pt_seg_kernel(SegArgs A) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int bh = blockIdx.x / A.nseg, s = blockIdx.x % A.nseg;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  seg_wave<D, CT>(A, smem, bh, s, w, threadIdx.x & 63);
+  seg_wave<D, CT, EXCL>(A, smem, bh, s, w, threadIdx.x & 63);
 }
 
 // Segment increments dS_s = K_s^T diag(eta_s) V_s for every segment but the
@@ -648,7 +653,7 @@ struct Fp32Cfg {
   static_assert(C % 16 == 0 && DK % 32 == 0, "tile shape");
 };
 
-template <int DK, int C>
+template <int DK, int C, bool EXCL>
 __global__ __launch_bounds__(256) void per_token_fp32_kernel(
     const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
     const float* __restrict__ eta, const float* __restrict__ W0, float* __restrict__ O,
@@ -722,7 +727,7 @@ __global__ __launch_bounds__(256) void per_token_fp32_kernel(
 #pragma unroll
         for (int cc = 0; cc < SB; ++cc) {
           const int i = SB * bi + r, j = SB * bj + cc;
-          p[i * PP + j] = j <= i ? acc[r][cc] * e[j] : 0.f;
+          p[i * PP + j] = (EXCL ? j < i : j <= i) ? acc[r][cc] * e[j] : 0.f;
         }
     } else {
 #pragma unroll
@@ -780,7 +785,7 @@ static size_t fp32_lds_bytes() {
 // ---------------------------------------------------------------------------
 template <int DK, int C>
 static hipError_t launch_fp32(const PerTokenArgs& a, hipStream_t stream, const Timing& tm) {
-  auto kern = per_token_fp32_kernel<DK, C>;
+  auto kern = a.exclusive ? per_token_fp32_kernel<DK, C, true> : per_token_fp32_kernel<DK, C, false>;
   const size_t lds = fp32_lds_bytes<DK, C>();
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
@@ -843,7 +848,7 @@ static hipError_t launch_seg(const PerTokenArgs& a, hipStream_t stream, const Ti
                        (floatx4*)a.ws, sp.nseg);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  auto kf = pt_seg_kernel<D, seg_tile<D>()>;
+  auto kf = a.exclusive ? pt_seg_kernel<D, seg_tile<D>(), true> : pt_seg_kernel<D, seg_tile<D>(), false>;
   if ((e = hipFuncSetAttribute((const void*)kf, hipFuncAttributeMaxDynamicSharedMemorySize, CfgF::LDS_BYTES)) !=
       hipSuccess)
     return e;

@@ -46,7 +46,7 @@ def test_exports_every_declared_symbol():
 
 @needs_lib
 def test_version_and_status_strings():
-    assert la.lib().ttt_la_abi_version() == 1
+    assert la.lib().ttt_la_abi_version() == 2
     for s in range(10):
         assert la.status_string(s) and la.status_string(s) != "unknown status"
     assert la.status_string(99) == "unknown status"
@@ -57,7 +57,7 @@ def test_version_and_status_strings():
     (dict(Q=None), 1), (dict(K=None), 1), (dict(V=None), 1), (dict(eta=None), 1), (dict(O=None), 1),
     (dict(W0=None), 1), (dict(W_out=None), 1),
     (dict(chunk=0), 3), (dict(chunk=-5), 3),
-    (dict(mode=3), 5), (dict(mode=-1), 5),
+    (dict(mode=6), 5), (dict(mode=-1), 5),
 ])
 def test_invalid_arguments(kw, code):
     assert call(**kw) == code
@@ -80,6 +80,8 @@ def test_null_desc():
     (la.make_desc(1, 1, 8, 64, 0), 0, 2),
     (la.make_desc(1, 1, 8, 128, 64, 256), 2, 2),       # SwiGLU needs d_k == d_v
     (la.make_desc(1, 1, 8, 128, 128, 0), 2, 2),        # SwiGLU needs d_h
+    (la.make_desc(1, 1, 8, 128, 64, 256), 5, 2),       # so does its update-first variant
+    (la.make_desc(1, 1, 8, 128, 128, 0), 5, 2),
     (la.make_desc(1, 1, 8, 64, 64, 0, 7), 0, 4),       # bad dtype
     (la.make_desc(1, 1, 8, 96, 96), 0, 6),             # d not compiled
     (la.make_desc(1, 1, 8, 64, 128), 0, 6),            # d_k != d_v not compiled
@@ -129,6 +131,20 @@ def test_workspace_query_and_check():
 
 
 @needs_lib
+def test_ordering_variants_share_support_and_workspace():
+    # modes 3, 4, 5 are the other read orders of modes 0, 1, 2: same shapes, support and workspace
+    for base, var, desc, chunk in [
+            (0, 3, la.make_desc(4, 16, 4096, 128, 128, 0, la.BF16), 64),
+            (0, 3, la.make_desc(1, 1, 256, 64, 64, 0, la.FP32), 64),
+            (1, 4, la.make_desc(1, 12, 196608, 64, 64, 0, la.BF16), 4096),
+            (2, 5, la.make_desc(2, 8, 32768, 128, 128, 256, la.BF16), 2048)]:
+        assert la.workspace_bytes(desc, chunk, var) == la.workspace_bytes(desc, chunk, base)
+    assert la.MODES["per_token_linear_exclusive"] == 3
+    assert la.MODES["large_chunk_linear_update_first"] == 4
+    assert la.MODES["large_chunk_swiglu_update_first"] == 5
+    assert call(desc=la.make_desc(1, 1, 8, 96, 96), mode=3) == 6
+
+
 def test_per_token_workspace():
     # fp32 needs none; bf16 splits a head's sequence into segments of whole
     # 64-token tiles so that heads x segments reach 256 workgroups, and keeps

@@ -60,3 +60,29 @@ def test_large_chunk_linear_deterministic_resume_in_place():
     O3, W3 = la.forward(t["Q"], t["K"], t["V"], t["eta"], Ws, 128, "large_chunk_linear", W_out=Ws)
     torch.cuda.synchronize()
     assert torch.equal(O3, O1) and torch.equal(W3, W1)
+
+
+@pytest.mark.parametrize("B,H,T,d,chunk", [
+    (1, 2, 300, 64, 128),     # ragged last chunk
+    (1, 3, 1000, 128, 300),
+    (1, 1, 2500, 64, 2048),   # several token slices per chunk
+    (1, 2, 97, 64, 1),        # one token per chunk
+    (1, 2, 100, 64, 4096),    # a single chunk
+    (1, 2, 700, 128, 32),     # several scan windows
+])
+def test_large_chunk_linear_update_first_small(B, H, T, d, chunk):
+    s = workloads.make_spec("large_chunk_linear_update_first", B, H, T, d, chunk=chunk, dtype="bf16",
+                            eta_scale=0.05)
+    x = workloads.generate(s, seed=8)
+    t = to_device(x, s)
+    O, W = run(t, s)
+    check(s, x, O, W, label=f"{B},{H},{T},{d},c{chunk}")
+    _, Wr = run(t, dict(s, mode="large_chunk_linear"))
+    assert torch.equal(W, Wr)
+
+
+def test_large_chunk_linear_update_first_workload_sampled_heads():
+    s = workloads.spec("large_chunk_linear_bf16_B1H12T196608_d64_c4096", mode="large_chunk_linear_update_first")
+    x = workloads.generate(s, seed=0)
+    O, W = run(to_device(x, s), s)
+    check(s, x, O, W, heads=[3, 11], label="B1H12T196608 heads 3,11")

@@ -61,3 +61,27 @@ def test_large_chunk_swiglu_deterministic_resume_in_place():
     O3, W3 = la.forward(t["Q"], t["K"], t["V"], t["eta"], Ws, 128, "large_chunk_swiglu", W_out=Ws)
     torch.cuda.synchronize()
     assert torch.equal(O3, O1) and torch.equal(W3, W1)
+
+
+@pytest.mark.parametrize("B,H,T,chunk", [
+    (1, 1, 300, 128),      # ragged last chunk
+    (2, 1, 700, 2048),     # a single chunk
+    (1, 1, 200, 37),
+    (1, 1, 40, 1),         # one token per chunk
+])
+def test_large_chunk_swiglu_update_first_small(B, H, T, chunk):
+    s = workloads.make_spec("large_chunk_swiglu_update_first", B, H, T, 128, d_h=256, chunk=chunk,
+                            dtype="bf16", eta_scale=0.02)
+    x = workloads.generate(s, seed=9)
+    t = to_device(x, s)
+    O, W = run(t, s)
+    check(s, x, O, W, label=f"{B},{H},{T},c{chunk}")
+    _, Wr = run(t, dict(s, mode="large_chunk_swiglu"))
+    assert torch.equal(W, Wr)
+
+
+def test_large_chunk_swiglu_update_first_workload_sampled_heads():
+    s = workloads.spec("large_chunk_swiglu_bf16_B2H8T32768_d128_dh256_c2048", mode="large_chunk_swiglu_update_first")
+    x = workloads.generate(s, seed=0)
+    O, W = run(to_device(x, s), s)
+    check(s, x, O, W, heads=[4, 15], label="B2H8T32768 heads 4,15")

@@ -110,3 +110,32 @@ def test_per_token_gradient_ascent_and_zero_rate():
     O, W = run(to_device(x0, s), s)
     check(s, x0, O, W, label="zero eta")
     assert torch.equal(W.cpu(), torch.from_numpy(x["W0"]))
+
+
+@pytest.mark.parametrize("B,H,T,d,chunk,dtype", [
+    (1, 2, 256, 128, 64, "bf16"),
+    (2, 3, 333, 128, 64, "bf16"),      # ragged tail, several segments
+    (1, 1, 300, 64, 64, "bf16"),       # five one-tile segments
+    (1, 3, 150, 64, 16, "bf16"),
+    (1, 4, 500, 128, 128, "bf16"),
+    (1, 1, 1, 128, 64, "bf16"),        # single token: its output is W0's read
+    (1, 1, 256, 64, 64, "fp32"),
+    (2, 2, 203, 128, 32, "fp32"),
+    (1, 1, 37, 64, 32, "fp32"),
+])
+def test_per_token_exclusive_small(B, H, T, d, chunk, dtype):
+    s = workloads.make_spec("per_token_linear_exclusive", B, H, T, d, chunk=chunk, dtype=dtype, eta="sigmoid")
+    x = workloads.generate(s, seed=7)
+    t = to_device(x, s)
+    O, W = run(t, s)
+    check(s, x, O, W, label=f"{B},{H},{T},{d},c{chunk},{dtype}")
+    # the read order does not touch the state sequence: same kernels, same final state
+    _, Wi = run(t, dict(s, mode="per_token_linear"))
+    assert torch.equal(W, Wi)
+
+
+def test_per_token_exclusive_workload_B4H16T4096_sampled_heads():
+    s = workloads.spec("per_token_bf16_B4H16T4096_d128_c64", mode="per_token_linear_exclusive")
+    x = workloads.generate(s, seed=0)
+    O, W = run(to_device(x, s), s)
+    check(s, x, O, W, heads=[0, 17, 38, 63], label="bf16 B4H16T4096 heads 0,17,38,63")

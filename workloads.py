@@ -22,7 +22,9 @@ from __future__ import annotations
 
 import numpy as np
 
-MODES = ("per_token_linear", "large_chunk_linear", "large_chunk_swiglu")
+MODES = ("per_token_linear", "large_chunk_linear", "large_chunk_swiglu",
+         # the other read orders: a query before its token's step; a chunk's step before its reads
+         "per_token_linear_exclusive", "large_chunk_linear_update_first", "large_chunk_swiglu_update_first")
 
 # Named workloads.  Shapes follow the configurations the method is measured
 # on; T is the sequence length, d the head width, d_h the SwiGLU hidden width.
@@ -106,7 +108,7 @@ def generate(s: dict, seed: int = 0) -> dict:
             w = (s["w0_std"] * rng.standard_normal((H,) + shape)).astype(np.float32)
         return np.ascontiguousarray(np.broadcast_to(w[None], (B, H) + shape))
 
-    if s["mode"] == "large_chunk_swiglu":
+    if s["mode"].startswith("large_chunk_swiglu"):
         assert dk == dv and dh > 0
         W1, W3, W2 = draw((dk, dh)), draw((dk, dh)), draw((dh, dk))
         out.update(W1=W1, W3=W3, W2=W2, W0=np.concatenate(
@@ -118,6 +120,6 @@ def generate(s: dict, seed: int = 0) -> dict:
 
 def state_shape(s: dict) -> tuple:
     """Shape of the fast-weight state buffer (W0 and W_out) for ``s``."""
-    if s["mode"] == "large_chunk_swiglu":
+    if s["mode"].startswith("large_chunk_swiglu"):
         return (s["B"], s["H"], 3 * s["d_k"] * s["d_h"])
     return (s["B"], s["H"], s["d_k"], s["d_v"])
