@@ -1,10 +1,12 @@
-"""fp64 CPU oracle for the TTT-with-KV-binding forward pass.
+"""fp64 CPU oracle for the TTT-with-KV-binding forward pass and the
+per-token backward.
 
 Test infrastructure only: imported by the tests, the smoke check and the
 benchmark's CPU-baseline leg, never by the library or its binding.
 """
 from .ttt_oracle import (  # noqa: F401
     NORM_EPS,
+    backward,
     forward,
     large_chunk_linear,
     large_chunk_swiglu,
@@ -12,6 +14,7 @@ from .ttt_oracle import (  # noqa: F401
     linear_binding_loss,
     normalize_columns,
     per_token_linear,
+    per_token_linear_backward,
     silu,
     silu_prime,
     swiglu_binding_grad,

@@ -1,4 +1,4 @@
-"""Plain fp64 CPU oracle for the TTT-with-KV-binding forward pass.
+"""Plain fp64 CPU oracle for the TTT-with-KV-binding forward pass (and the per-token backward).
 
 TEST INFRASTRUCTURE ONLY. Nothing on the product path imports, calls or
 links this module: only the tests, the smoke check and the CPU-baseline leg
@@ -162,6 +162,56 @@ def per_token_linear(Q, K, V, eta, W0, inclusive=True):
         if inclusive:
             O[:, :, t, :] = np.matmul(Q[:, :, t:t + 1, :], W)[:, :, 0, :]
     return O, W
+
+
+def per_token_linear_backward(Q, K, V, eta, W0, dO, dW_T, inclusive=True):
+    """Reverse-mode gradients of :func:`per_token_linear`: given the
+    upstream gradients ``dO`` (of O) and ``dW_T`` (of the final memory),
+    return ``(dQ, dK, dV, deta, dW0)``.
+
+    Training the outer model through the per-token inner loop (the paper
+    summary reports training speed-ups of the parallel form, technical
+    section 4; podcast at 14:17) needs these.  They are derived by hand from
+    the token loop, walked backwards: the forward step is
+    ``W_t = W_{t-1} + eta_t k_t^T v_t`` and the read is ``o_t = q_t W_t``
+    (``W_{t-1}`` when not ``inclusive``).  With ``G`` the gradient with
+    respect to the current memory (``dW_T`` at the end):
+      read:  ``dq_t = dO_t W^T`` for the memory the query read, and
+             ``G += q_t^T dO_t``;
+      step:  ``deta_t = <G, k_t^T v_t> = k_t G v_t^T``,
+             ``dk_t = eta_t v_t G^T``, ``dv_t = eta_t k_t G``;
+             the memory before the step receives ``G`` unchanged.
+    Memories are recovered exactly in reverse by undoing the steps from the
+    final one.  ``dW0`` is ``G`` after the first token."""
+    Q, K, V, eta, W0, dO, dW_T = map(_f64, (Q, K, V, eta, W0, dO, dW_T))
+    _, W = per_token_linear(Q, K, V, eta, W0, inclusive=inclusive)
+    G = dW_T.copy()
+    dQ, dK, dV = np.zeros_like(Q), np.zeros_like(K), np.zeros_like(V)
+    deta = np.zeros_like(eta)
+    T = Q.shape[2]
+    for t in range(T - 1, -1, -1):
+        q, k, v = Q[:, :, t:t + 1, :], K[:, :, t:t + 1, :], V[:, :, t:t + 1, :]
+        do = dO[:, :, t:t + 1, :]
+        e = eta[:, :, t][..., None, None]
+        if inclusive:                                     # o_t = q_t W_t
+            dQ[:, :, t, :] = np.matmul(do, np.swapaxes(W, -1, -2))[:, :, 0, :]
+            G = G + np.matmul(np.swapaxes(q, -1, -2), do)
+        deta[:, :, t] = np.matmul(np.matmul(k, G), np.swapaxes(v, -1, -2))[:, :, 0, 0]
+        dK[:, :, t, :] = (e * np.matmul(v, np.swapaxes(G, -1, -2)))[:, :, 0, :]
+        dV[:, :, t, :] = (e * np.matmul(k, G))[:, :, 0, :]
+        W = W - e * np.matmul(np.swapaxes(k, -1, -2), v)  # undo step t: W_{t-1}
+        if not inclusive:                                 # o_t = q_t W_{t-1}
+            dQ[:, :, t, :] = np.matmul(do, np.swapaxes(W, -1, -2))[:, :, 0, :]
+            G = G + np.matmul(np.swapaxes(q, -1, -2), do)
+    return dQ, dK, dV, deta, G
+
+
+def backward(Q, K, V, eta, W0, dO, dW_T, chunk, mode):
+    """Gradients ``(dQ, dK, dV, deta, dW0)`` by mode name, with the
+    library's argument order.  Only the per-token modes have a backward."""
+    if mode in ("per_token_linear", "per_token_linear_exclusive"):
+        return per_token_linear_backward(Q, K, V, eta, W0, dO, dW_T, inclusive=(mode == "per_token_linear"))
+    raise ValueError(f"no backward for mode {mode!r}")
 
 
 def large_chunk_linear(Q, K, V, eta, W0, chunk, normalize=True, read_first=True):

@@ -1,0 +1,155 @@
+"""Pins of the oracle's per-token backward (CPU only).
+
+The hand-derived reverse loop is checked against things it does not share
+code with: torch autograd of the per-token closed form written here with
+cumulative sums, central finite differences of the oracle's own forward
+loop, the closed form of dW0, and the zero-rate special case.  Shapes use
+d_k != d_v so that a transposed operand cannot pass.  Mutation tests plant
+typical mistakes in copies of the backward and check that a pin catches each.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import ttt_oracle as TO
+
+
+def case(B=2, H=2, T=11, dk=5, dv=3, seed=0, eta_scale=0.4):
+    rng = np.random.default_rng(seed)
+    Q = rng.standard_normal((B, H, T, dk))
+    K = rng.standard_normal((B, H, T, dk))
+    V = rng.standard_normal((B, H, T, dv))
+    eta = eta_scale * rng.standard_normal((B, H, T))
+    W0 = 0.3 * rng.standard_normal((B, H, dk, dv))
+    dO = rng.standard_normal((B, H, T, dv))
+    dW = rng.standard_normal((B, H, dk, dv))
+    return Q, K, V, eta, W0, dO, dW
+
+
+def autograd_grads(Q, K, V, eta, W0, dO, dW, inclusive):
+    """Gradients of sum(O * dO) + sum(W_T * dW) through the closed form
+    S_t = W0 + sum_{i<=t} eta_i k_i^T v_i, o_t = q_t S_t (S_{t-1} when not inclusive)."""
+    xs = [torch.tensor(a, dtype=torch.float64, requires_grad=True) for a in (Q, K, V, eta, W0)]
+    q, k, v, e, w0 = xs
+    outer = (e[..., None, None] * k[..., :, None]) * v[..., None, :]          # [B,H,T,dk,dv]
+    S = w0[:, :, None] + torch.cumsum(outer, dim=2)                          # S_t, t = 0..T-1
+    if not inclusive:
+        S = torch.cat([w0[:, :, None], S[:, :, :-1]], dim=2)                 # S_{t-1}
+    O = torch.matmul(q[..., None, :], S)[..., 0, :]
+    WT = w0 + outer.sum(dim=2)
+    loss = (O * torch.from_numpy(dO)).sum() + (WT * torch.from_numpy(dW)).sum()
+    loss.backward()
+    return [x.grad.numpy() for x in xs]
+
+
+def check_autograd(bwd=TO.per_token_linear_backward, inclusive=True, seed=0, **kw):
+    Q, K, V, eta, W0, dO, dW = case(seed=seed, **kw)
+    got = bwd(Q, K, V, eta, W0, dO, dW, inclusive=inclusive)
+    ref = autograd_grads(Q, K, V, eta, W0, dO, dW, inclusive)
+    return all(np.allclose(g, r, rtol=1e-10, atol=1e-10) for g, r in zip(got, ref))
+
+
+def check_finite_differences(bwd=TO.per_token_linear_backward, inclusive=True, seed=1):
+    """<grad_X, delta> against a central difference of the forward loop's loss, for every input."""
+    args = list(case(B=1, H=2, T=7, dk=4, dv=3, seed=seed))
+    dO, dW = args[5], args[6]
+    grads = bwd(*args, inclusive=inclusive)
+    rng = np.random.default_rng(seed + 100)
+
+    def loss(a):
+        O, WT = TO.per_token_linear(*a[:5], inclusive=inclusive)
+        return float(np.sum(O * dO) + np.sum(WT * dW))
+
+    h = 1e-6
+    ok = True
+    for i in range(5):
+        delta = rng.standard_normal(args[i].shape)
+        ap, am = list(args), list(args)
+        ap[i] = args[i] + h * delta
+        am[i] = args[i] - h * delta
+        fd = (loss(ap) - loss(am)) / (2 * h)
+        an = float(np.sum(grads[i] * delta))
+        ok &= abs(fd - an) <= 1e-6 * max(1.0, abs(an))
+    return ok
+
+
+@pytest.mark.parametrize("inclusive", [True, False])
+@pytest.mark.parametrize("seed", [0, 1])
+def test_backward_matches_autograd_of_the_closed_form(inclusive, seed):
+    assert check_autograd(inclusive=inclusive, seed=seed)
+
+
+@pytest.mark.parametrize("inclusive", [True, False])
+def test_backward_matches_autograd_single_token_and_square(inclusive):
+    assert check_autograd(inclusive=inclusive, T=1)
+    assert check_autograd(inclusive=inclusive, dk=4, dv=4, T=6)
+
+
+@pytest.mark.parametrize("inclusive", [True, False])
+def test_backward_matches_finite_differences_of_the_forward_loop(inclusive):
+    assert check_finite_differences(inclusive=inclusive)
+
+
+@pytest.mark.parametrize("inclusive", [True, False])
+def test_dW0_closed_form(inclusive):
+    # W0 enters every read and the final memory once: dW0 = dW + sum_t q_t^T dO_t
+    Q, K, V, eta, W0, dO, dW = case(seed=3)
+    dW0 = TO.per_token_linear_backward(Q, K, V, eta, W0, dO, dW, inclusive=inclusive)[4]
+    assert np.allclose(dW0, dW + np.swapaxes(Q, -1, -2) @ dO, rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("inclusive", [True, False])
+def test_zero_rate(inclusive):
+    # eta = 0: the memory stays W0, so dQ = dO W0^T and no gradient reaches K or V; deta_t is
+    # k_t G_t v_t^T with G_t = dW + sum over the reads that come after step t
+    Q, K, V, eta, W0, dO, dW = case(seed=4)
+    eta = np.zeros_like(eta)
+    dQ, dK, dV, deta, _ = TO.per_token_linear_backward(Q, K, V, eta, W0, dO, dW, inclusive=inclusive)
+    assert np.allclose(dQ, dO @ np.swapaxes(W0, -1, -2), rtol=1e-12, atol=1e-12)
+    assert not dK.any() and not dV.any()
+    T = Q.shape[2]
+    for t in range(T):
+        lo = t if inclusive else t + 1
+        G = dW + np.swapaxes(Q[:, :, lo:], -1, -2) @ dO[:, :, lo:]
+        ref = (K[:, :, t, None, :] @ G @ V[:, :, t, :, None])[..., 0, 0]
+        assert np.allclose(deta[:, :, t], ref, rtol=1e-12, atol=1e-12)
+
+
+def test_backward_dispatch():
+    Q, K, V, eta, W0, dO, dW = case(seed=5)
+    for mode, inc in (("per_token_linear", True), ("per_token_linear_exclusive", False)):
+        a = TO.backward(Q, K, V, eta, W0, dO, dW, 64, mode)
+        b = TO.per_token_linear_backward(Q, K, V, eta, W0, dO, dW, inclusive=inc)
+        assert all(np.array_equal(x, y) for x, y in zip(a, b))
+    with pytest.raises(ValueError):
+        TO.backward(Q, K, V, eta, W0, dO, dW, 64, "large_chunk_linear")
+
+
+# ---------------------------------------------------------------------------
+# Mutation tests
+# ---------------------------------------------------------------------------
+
+def _mutant(kind):
+    def bwd(Q, K, V, eta, W0, dO, dW, inclusive=True):
+        dQ, dK, dV, deta, dW0 = TO.per_token_linear_backward(Q, K, V, eta, W0, dO, dW, inclusive=inclusive)
+        if kind == "dk_without_eta":
+            dK = np.where(np.abs(eta[..., None]) > 0, dK / eta[..., None], 0.0)
+        elif kind == "dv_sign":
+            dV = -dV
+        elif kind == "dropped_final_state_gradient":
+            dQ, dK, dV, deta, dW0 = TO.per_token_linear_backward(Q, K, V, eta, W0, dO, 0 * dW, inclusive=inclusive)
+        elif kind == "other_read_order":
+            dQ, dK, dV, deta, dW0 = TO.per_token_linear_backward(Q, K, V, eta, W0, dO, dW, inclusive=not inclusive)
+        elif kind == "deta_sign":
+            deta = -deta
+        elif kind == "dq_from_initial_memory":
+            dQ = dO @ np.swapaxes(W0, -1, -2)
+        return dQ, dK, dV, deta, dW0
+    return bwd
+
+
+@pytest.mark.parametrize("kind", ["dk_without_eta", "dv_sign", "dropped_final_state_gradient", "other_read_order",
+                                  "deta_sign", "dq_from_initial_memory"])
+def test_backward_mutants_are_caught(kind):
+    m = _mutant(kind)
+    assert not (check_autograd(bwd=m, inclusive=True) and check_finite_differences(bwd=m, inclusive=True))

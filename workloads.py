@@ -118,6 +118,20 @@ def generate(s: dict, seed: int = 0) -> dict:
     return out
 
 
+def generate_grads(s: dict, seed: int = 0) -> dict:
+    """Upstream gradients for a backward pass over the inputs of ``s``:
+    ``dO`` ``[B,H,T,d_v]`` ~ N(0, 1) (bf16-representable for bf16 inputs)
+    and ``dW`` ~ N(0, 1) in the linear state's shape, from a generator
+    stream of their own (the forward inputs do not change)."""
+    B, H, T, dv = s["B"], s["H"], s["T"], s["d_v"]
+    rng = np.random.default_rng([seed, 1])
+    dO = rng.standard_normal((B, H, T, dv), dtype=np.float32)
+    if s["dtype"] == "bf16":
+        dO = bf16_round(dO)
+    dW = rng.standard_normal((B, H, s["d_k"], dv), dtype=np.float32)
+    return dict(dO=dO, dW=dW)
+
+
 def state_shape(s: dict) -> tuple:
     """Shape of the fast-weight state buffer (W0 and W_out) for ``s``."""
     if s["mode"].startswith("large_chunk_swiglu"):
