@@ -1,6 +1,7 @@
 /*
  * libttt_la - forward pass of a test-time-training (TTT) layer with
- * key-value binding, for AMD Instinct MI355X (gfx950).
+ * key-value binding, and the backward pass of its per-token form, for AMD
+ * Instinct MI355X (gfx950).
  *
  * The method (pages on "Test-Time Training with KV Binding Is Secretly
  * Linear Attention", paper summary technical sections 2B and 3, and the
@@ -184,6 +185,52 @@ int ttt_la_event_record(void* event, void* stream);
 int ttt_la_event_elapsed_ms(void* start, void* stop, float* ms);
 int ttt_la_event_destroy(void* event);
 
+/*
+ * ttt_la_backward(Q, K, V, eta, W0, dO, dW_out, chunk, mode) -> (dQ, dK, dV, deta, dW0)
+ *
+ * Gradients of a scalar loss through ttt_la_forward in the per-token modes,
+ * for training the model around the layer (the paper summary reports the
+ * parallel form's speed-up for training as well as inference, technical
+ * section 4).  With G_t = dW_out + sum of q_j^T dO_j over the reads j at or
+ * after token t (strictly after it for TTT_LA_PER_TOKEN_LINEAR_EXCLUSIVE),
+ * and S_t the memory token t's query reads:
+ *     dq_t = dO_t S_t^T,   dk_t = eta_t v_t G_t^T,   dv_t = eta_t k_t G_t,
+ *     deta_t = k_t G_t v_t^T,   dW0 = dW_out + sum_t q_t^T dO_t.
+ *
+ *   Q, K, V, eta, W0, chunk, desc   as passed to ttt_la_forward (the forward
+ *                  outputs are not needed: the memories are recomputed)
+ *   mode           TTT_LA_PER_TOKEN_LINEAR or TTT_LA_PER_TOKEN_LINEAR_EXCLUSIVE
+ *                  (ERR_UNSUPPORTED for the large-chunk modes)
+ *   dO             [B,H,T,d_v] io_dtype, device: gradient of O
+ *   dW_out         [B,H,d_k,d_v] float32, device: gradient of W_out (pass
+ *                  zeros if the final memory does not reach the loss)
+ *   dQ, dK         [B,H,T,d_k] float32, device (written)
+ *   dV             [B,H,T,d_v] float32, device (written)
+ *                  (float32 whatever io_dtype is: rounding these heavy-tailed
+ *                  gradients to bf16 alone would use up the accuracy budget)
+ *   deta           [B,H,T] float32, device (written)
+ *   dW0            [B,H,d_k,d_v] float32, device (written)
+ *   workspace, workspace_bytes
+ *                  at least ttt_la_backward_workspace_bytes(desc, chunk, mode)
+ *                  bytes of device scratch (contents on entry do not matter)
+ *   stream         hipStream_t (NULL = the default stream)
+ *
+ * Supported set: d_k = d_v in {64, 128}, bf16, chunk in {16, 32, 64, 128}.
+ * Every pointer is required (ERR_NULL), except that the per-token arrays
+ * may be NULL when T = 0 (then dW0 = dW_out); no output may overlap an input,
+ * another output or the workspace (ERR_ALIAS).  Checks, ownership and
+ * enqueue-only behaviour are those of ttt_la_forward.
+ */
+int ttt_la_backward(const void* Q, const void* K, const void* V, const float* eta,
+                    const float* W0, const void* dO, const float* dW_out, int64_t chunk,
+                    int32_t mode, const ttt_la_desc* desc, void* dQ, void* dK, void* dV,
+                    float* deta, float* dW0, void* workspace, size_t workspace_bytes,
+                    void* stream);
+
+/* Bytes of device workspace ttt_la_backward needs (0 for invalid or
+ * unsupported arguments). */
+size_t ttt_la_backward_workspace_bytes(const ttt_la_desc* desc, int64_t chunk, int32_t mode);
+
 /* Bytes of device workspace ttt_la_forward needs for this problem (0 if
  * none).  Returns 0 as well for invalid arguments (ttt_la_forward reports
  * those). */
@@ -195,7 +242,7 @@ const char* ttt_la_status_string(int status);
 /* ABI version of this header (incremented on incompatible change). */
 int ttt_la_abi_version(void);
 
-#define TTT_LA_ABI_VERSION 2
+#define TTT_LA_ABI_VERSION 3
 
 #ifdef __cplusplus
 }

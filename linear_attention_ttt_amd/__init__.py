@@ -17,7 +17,7 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["forward", "forward_timed_raw", "TimingEvent", "workspace_bytes", "TTTLAError", "MODES", "Desc", "lib", "library_path",
+__all__ = ["forward", "backward", "backward_raw", "backward_workspace_bytes", "forward_timed_raw", "TimingEvent", "workspace_bytes", "TTTLAError", "MODES", "Desc", "lib", "library_path",
            "PER_TOKEN_LINEAR", "LARGE_CHUNK_LINEAR", "LARGE_CHUNK_SWIGLU", "PER_TOKEN_LINEAR_EXCLUSIVE",
            "LARGE_CHUNK_LINEAR_UPDATE_FIRST", "LARGE_CHUNK_SWIGLU_UPDATE_FIRST"]
 
@@ -67,6 +67,11 @@ def lib() -> ctypes.CDLL:
         L.ttt_la_forward_timed.argtypes = [vp, vp, vp, vp, vp, i64, i32, ctypes.POINTER(Desc), vp, vp, vp,
                                            ctypes.c_size_t, vp, vp, vp]
         L.ttt_la_forward_timed.restype = ctypes.c_int
+        L.ttt_la_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i32, ctypes.POINTER(Desc), vp, vp, vp, vp,
+                                      vp, vp, ctypes.c_size_t, vp]
+        L.ttt_la_backward.restype = ctypes.c_int
+        L.ttt_la_backward_workspace_bytes.argtypes = [ctypes.POINTER(Desc), i64, i32]
+        L.ttt_la_backward_workspace_bytes.restype = ctypes.c_size_t
         L.ttt_la_workspace_bytes.argtypes = [ctypes.POINTER(Desc), i64, i32]
         L.ttt_la_workspace_bytes.restype = ctypes.c_size_t
         L.ttt_la_status_string.argtypes = [ctypes.c_int]
@@ -95,6 +100,17 @@ def make_desc(B, H, T, d_k, d_v, d_h=0, io_dtype=BF16) -> Desc:
 
 def workspace_bytes(desc: Desc, chunk: int, mode) -> int:
     return int(lib().ttt_la_workspace_bytes(ctypes.byref(desc), int(chunk), _mode(mode)))
+
+
+def backward_workspace_bytes(desc: Desc, chunk: int, mode) -> int:
+    return int(lib().ttt_la_backward_workspace_bytes(ctypes.byref(desc), int(chunk), _mode(mode)))
+
+
+def backward_raw(Q, K, V, eta, W0, dO, dW_out, chunk, mode, desc: Desc, dQ, dK, dV, deta, dW0, workspace,
+                 workspace_bytes_, stream) -> int:
+    """ttt_la_backward on raw device addresses (ints or None); returns the status code."""
+    return lib().ttt_la_backward(Q, K, V, eta, W0, dO, dW_out, int(chunk), _mode(mode), ctypes.byref(desc), dQ, dK,
+                                 dV, deta, dW0, workspace, workspace_bytes_, stream)
 
 
 def status_string(status: int) -> str:
@@ -214,3 +230,50 @@ def forward(Q, K, V, eta, W0, chunk: int, mode, *, out=None, W_out=None, workspa
     if status != 0:
         raise TTTLAError(status, status_string(status))
     return O, Wo
+
+
+def backward(Q, K, V, eta, W0, dO, dW_out, chunk: int, mode="per_token_linear", *, workspace=None, stream=None):
+    """Gradients of the per-token forward: given the inputs of ``forward``,
+    ``dO`` (gradient of O, like V) and ``dW_out`` (gradient of the final
+    memory, float32 like W0), return ``(dQ, dK, dV, deta, dW0)``, all
+    float32.  bfloat16 inputs only; argument checks as in ``forward``."""
+    import torch
+
+    m = _mode(mode)
+    tensors = dict(Q=Q, K=K, V=V, eta=eta, W0=W0, dO=dO, dW_out=dW_out)
+    dev = Q.device
+    for name, t in tensors.items():
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name} must be a torch.Tensor")
+        if t.device != dev or dev.type != "cuda":
+            raise ValueError(f"{name} must be on the same CUDA device as Q")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if Q.dtype != torch.bfloat16 or K.dtype != Q.dtype or V.dtype != Q.dtype or dO.dtype != Q.dtype:
+        raise ValueError("Q, K, V, dO must be bfloat16")
+    if eta.dtype != torch.float32 or W0.dtype != torch.float32 or dW_out.dtype != torch.float32:
+        raise ValueError("eta, W0 and dW_out must be float32")
+    if Q.dim() != 4 or K.shape != Q.shape or V.dim() != 4 or V.shape[:3] != Q.shape[:3] or dO.shape != V.shape:
+        raise ValueError("Q, K must be [B,H,T,d_k], V and dO [B,H,T,d_v]")
+    B, H, T, dk = Q.shape
+    dv = V.shape[3]
+    if tuple(eta.shape) != (B, H, T) or tuple(W0.shape) != (B, H, dk, dv) or dW_out.shape != W0.shape:
+        raise ValueError("eta must be [B,H,T], W0 and dW_out [B,H,d_k,d_v]")
+    desc = make_desc(B, H, T, dk, dv, 0, BF16)
+    f32 = dict(dtype=torch.float32, device=dev)
+    dQ, dK, dV = torch.empty(Q.shape, **f32), torch.empty(K.shape, **f32), torch.empty(V.shape, **f32)
+    deta, dW0 = torch.empty_like(eta), torch.empty_like(W0)
+    nbytes = backward_workspace_bytes(desc, chunk, m)
+    ws = workspace
+    if ws is None or ws.numel() * ws.element_size() < nbytes:
+        ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    st = stream if stream is not None else torch.cuda.current_stream(dev).cuda_stream
+
+    def p(t):
+        return t.data_ptr() if t.numel() > 0 else None
+
+    status = backward_raw(p(Q), p(K), p(V), p(eta), W0.data_ptr(), p(dO), dW_out.data_ptr(), chunk, m, desc, p(dQ),
+                          p(dK), p(dV), p(deta), dW0.data_ptr(), ws.data_ptr(), ws.numel() * ws.element_size(), st)
+    if status != 0:
+        raise TTTLAError(status, status_string(status))
+    return dQ, dK, dV, deta, dW0

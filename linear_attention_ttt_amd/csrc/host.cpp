@@ -183,6 +183,49 @@ int ttt_la_forward(const void* Q, const void* K, const void* V, const float* eta
                               nullptr, nullptr);
 }
 
+static bool backward_ok(const ttt_la_desc& d, int64_t chunk, int32_t mode) {
+  return method_of(mode) == TTT_LA_PER_TOKEN_LINEAR && supported(d, chunk, mode) &&
+         ttt::per_token_backward_supported(d.d_k, d.d_v, chunk, d.io_dtype);
+}
+
+size_t ttt_la_backward_workspace_bytes(const ttt_la_desc* desc, int64_t chunk, int32_t mode) {
+  if (check_problem(desc, chunk, mode) != TTT_LA_OK || !backward_ok(*desc, chunk, mode)) return 0;
+  return ttt::per_token_backward_workspace(desc->B, desc->H, desc->T, desc->d_k);
+}
+
+int ttt_la_backward(const void* Q, const void* K, const void* V, const float* eta, const float* W0,
+                    const void* dO, const float* dW_out, int64_t chunk, int32_t mode, const ttt_la_desc* desc,
+                    void* dQ, void* dK, void* dV, float* deta, float* dW0, void* workspace, size_t workspace_bytes,
+                    void* stream) {
+  int st = check_problem(desc, chunk, mode);
+  if (st != TTT_LA_OK) return st;
+  const ttt_la_desc d = *desc;
+  if (!W0 || !dW_out || !dW0 || !workspace) return TTT_LA_ERR_NULL;
+  if (d.T > 0 && (!Q || !K || !V || !eta || !dO || !dQ || !dK || !dV || !deta)) return TTT_LA_ERR_NULL;
+  if (!backward_ok(d, chunk, mode)) return TTT_LA_ERR_UNSUPPORTED;
+  const size_t need = ttt::per_token_backward_workspace(d.B, d.H, d.T, d.d_k);
+  if (workspace_bytes < need) return TTT_LA_ERR_WORKSPACE;
+
+  const size_t es = 2;
+  const size_t ntok = (size_t)(d.B * d.H * d.T);
+  const size_t st_bytes = (size_t)state_elems(d, TTT_LA_PER_TOKEN_LINEAR) * 4;
+  const Range ins[7] = {range(Q, ntok * d.d_k * es), range(K, ntok * d.d_k * es), range(V, ntok * d.d_v * es),
+                        range(eta, ntok * 4), range(W0, st_bytes), range(dO, ntok * d.d_v * es),
+                        range(dW_out, st_bytes)};
+  const Range outs[6] = {range(dQ, ntok * d.d_k * 4), range(dK, ntok * d.d_k * 4), range(dV, ntok * d.d_v * 4),
+                         range(deta, ntok * 4), range(dW0, st_bytes), range(workspace, need)};
+  for (int i = 0; i < 6; ++i) {
+    for (const Range& in : ins)
+      if (overlap(outs[i], in)) return TTT_LA_ERR_ALIAS;
+    for (int j = i + 1; j < 6; ++j)
+      if (overlap(outs[i], outs[j])) return TTT_LA_ERR_ALIAS;
+  }
+
+  ttt::PerTokenBwdArgs a{Q,  K,  V,    eta, W0,        dO,  dW_out, dQ,  dK,  dV,          deta,
+                         dW0, workspace, d.B, d.H, d.T, d.d_k, d.d_v, chunk, d.io_dtype, other_order(mode) ? 1 : 0};
+  return ttt::launch_per_token_backward(a, (hipStream_t)stream) == hipSuccess ? TTT_LA_OK : TTT_LA_ERR_HIP;
+}
+
 int ttt_la_event_create(void** event) {
   if (!event) return TTT_LA_ERR_NULL;
   hipEvent_t e = nullptr;

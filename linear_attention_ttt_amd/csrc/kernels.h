@@ -32,10 +32,35 @@ struct PerTokenArgs {
 struct SegPlan {
   int nseg, seg_len;
 };
-SegPlan per_token_seg_plan(int64_t BH, int64_t T, int64_t dk);
+// a segment holds at most max_seg_tokens tokens (its views are addressed with 32-bit offsets)
+SegPlan per_token_seg_plan(int64_t BH, int64_t T, int64_t dk, int64_t max_seg_tokens = (int64_t)1 << 22);
 bool per_token_supported(int64_t dk, int64_t dv, int64_t chunk, int dtype);
 size_t per_token_workspace(int64_t B, int64_t H, int64_t T, int64_t dk, int64_t dv, int dtype);
 hipError_t launch_per_token(const PerTokenArgs& a, hipStream_t stream, const Timing& tm);
+
+// Backward of the per-token mode (bf16): gradients of O and of the final memory in, gradients of
+// Q, K, V, eta and W0 out.
+struct PerTokenBwdArgs {
+  const void* Q;
+  const void* K;
+  const void* V;
+  const float* eta;
+  const float* W0;
+  const void* dO;
+  const float* dW;
+  void* dQ;
+  void* dK;
+  void* dV;
+  float* deta;
+  float* dW0;
+  void* ws;
+  int64_t B, H, T, DK, DV, chunk;
+  int dtype;
+  int exclusive;
+};
+bool per_token_backward_supported(int64_t dk, int64_t dv, int64_t chunk, int dtype);
+size_t per_token_backward_workspace(int64_t B, int64_t H, int64_t T, int64_t dk);
+hipError_t launch_per_token_backward(const PerTokenBwdArgs& a, hipStream_t stream);
 
 struct LargeChunkArgs {
   const void* Q;

@@ -161,6 +161,12 @@ __device__ __forceinline__ void seg_update_eta(SegUpdate<Cfg>& U, const float* e
            U.evh[kc], U.evl[kc]);
   }
 }
+// the same without rates: V_w itself (bf16, so no lo part)
+template <class Cfg>
+__device__ __forceinline__ void seg_update_unit(SegUpdate<Cfg>& U, const bf16x4 (&vt)[Cfg::NB]) {
+#pragma unroll
+  for (int kc = 0; kc < Cfg::KC; ++kc) U.evh[kc] = join(vt[2 * kc], vt[2 * kc + 1]);
+}
 // transposed K operands of key half kc: rows seg_srow(m, li/4, li%4) of K^T, keys 32kc + 16h + 4g + j
 template <class Cfg>
 __device__ __forceinline__ void seg_update_k(bf16x8 (&a)[Cfg::MT], const unsigned char* ks,
@@ -171,13 +177,15 @@ __device__ __forceinline__ void seg_update_k(bf16x8 (&a)[Cfg::MT], const unsigne
                 lds_read_tr16(ks + (2 * kc + 1) * 16 * Cfg::ROWB + ktr[m]));
 }
 // hi products of every m-tile before the lo products: consecutive MFMAs never depend on each other
-template <class Cfg>
+template <class Cfg, bool LO = true>
 __device__ __forceinline__ void seg_update_mfma(floatx4 (&S)[Cfg::MT], const bf16x8 (&a)[Cfg::MT],
                                                 const SegUpdate<Cfg>& U, int kc) {
 #pragma unroll
   for (int m = 0; m < Cfg::MT; ++m) S[m] = mfma16(a[m], U.evh[kc], S[m]);
+  if constexpr (LO) {
 #pragma unroll
-  for (int m = 0; m < Cfg::MT; ++m) S[m] = mfma16(a[m], U.evl[kc], S[m]);
+    for (int m = 0; m < Cfg::MT; ++m) S[m] = mfma16(a[m], U.evl[kc], S[m]);
+  }
 }
 
 struct SegArgs {
@@ -194,7 +202,20 @@ struct SegArgs {
 
 // The program of wave W (wave-uniform).  One program for all waves keeps the
 // code within the instruction cache.
-template <int D, int CT, bool EXCL>
+// REV runs the same recurrence over the head's sequence in reverse token
+// order (the backward pass's suffix sums): the segment of reversed tokens
+// [tok0, seg_end) is the original range [T - seg_end, T - tok0), and row r
+// of tile i is original segment row seg_toks - 1 - (C i + r).  A row before
+// the segment's start gets the offset 2^31, past any view's size, so it
+// reads 0 and its store is dropped, as a row past the end does in forward
+// order.
+// EM places the rates: 0 on the keys (the method's recurrence); 1 on the
+// queries (keys unit-rate, each output row scaled by its own token's rate);
+// 2 nowhere (unit rates; eta is still streamed but unused).
+// OF32: the outputs are float32 (A.O points to floats) and leave straight
+// from the accumulators, 16 bytes per lane (4 columns of one token), instead
+// of as bf16 rows staged in LDS.
+template <int D, int CT, bool EXCL, bool REV, int EM, bool OF32>
 __device__ __forceinline__ void seg_wave(const SegArgs& A, unsigned char* smem, int bh, int s, int W, int l) {
   using Cfg = SegCfg<D, CT>;
   constexpr int NB = Cfg::NB;
@@ -215,13 +236,17 @@ __device__ __forceinline__ void seg_wave(const SegArgs& A, unsigned char* smem, 
 
   // ---- per-lane byte offsets, fixed for the whole segment ----
   // this wave's share of a tile matrix: LDS bytes [W*MAT_LOADS*1024, +MAT_LOADS*1024), i.e. whole rows
-  unsigned gofs[Cfg::MAT_LOADS];    // global offset of the 16 bytes lane l moves per load
+  unsigned gofs[Cfg::MAT_LOADS];    // global offset of the 16 bytes lane l moves per load (forward order)
+  int grow[Cfg::MAT_LOADS];         // REV: their tile row and byte offset within the row
+  unsigned gpc[Cfg::MAT_LOADS];
   unsigned lofs[Cfg::MAT_LOADS];    // their (swizzled) LDS offset
 #pragma unroll
   for (int k = 0; k < Cfg::MAT_LOADS; ++k) {
     const int b = (W * Cfg::MAT_LOADS + k) * 1024 + 16 * l;
     const int row = b / ROWB, ph = (b % ROWB) >> 4;
     gofs[k] = (unsigned)(row * ROWB + ((ph ^ seg_swz<D>(row)) << 4));
+    grow[k] = row;
+    gpc[k] = (unsigned)((ph ^ seg_swz<D>(row)) << 4);
     lofs[k] = (unsigned)b;
   }
   unsigned ksb[KP];                 // operand reads: row li, d = 32p + 8g .. + 7
@@ -239,40 +264,69 @@ __device__ __forceinline__ void seg_wave(const SegArgs& A, unsigned char* smem, 
   // dropped); a tile is addressed by its 32-bit offset.
   const long long tok0 = (long long)c0 * C;
   const long long seg_toks = seg_end > tok0 ? seg_end - tok0 : 0;
-  const __amdgpu_buffer_rsrc_t rq = make_rsrc(Qh + (nt > 0 ? tok0 * D : 0), seg_toks * ROWB);
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kh + (nt > 0 ? tok0 * D : 0), seg_toks * ROWB);
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vh + (nt > 0 ? tok0 * D : 0), seg_toks * ROWB);
-  const __amdgpu_buffer_rsrc_t re = make_rsrc(Eh + (nt > 0 ? tok0 : 0), seg_toks * 4);
-  const __amdgpu_buffer_rsrc_t ro = make_rsrc(Oh + (nt > 0 ? tok0 * D : 0), seg_toks * ROWB);
-  const unsigned eofs = (unsigned)((W * Cfg::EPW + l) * 4);
+  const long long first = nt > 0 ? (REV ? (long long)T - seg_end : tok0) : 0;   // first original token
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(Qh + first * D, seg_toks * ROWB);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kh + first * D, seg_toks * ROWB);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vh + first * D, seg_toks * ROWB);
+  const __amdgpu_buffer_rsrc_t re = make_rsrc(Eh + first, seg_toks * 4);
+  const __amdgpu_buffer_rsrc_t ro = make_rsrc(Oh + first * D, seg_toks * ROWB);
+  const __amdgpu_buffer_rsrc_t ro32 =
+      make_rsrc((float*)(void*)A.O + ((size_t)bh * T + first) * D, OF32 ? seg_toks * D * 4 : 0);
+  const int erow = W * Cfg::EPW + l;   // the tile row whose eta lane l moves
+  constexpr unsigned OOB = 0x80000000u;
+  // byte offset in the segment's views of load k of tile i (of its eta value)
+  auto mat_ofs = [&](int i, int k) -> unsigned {
+    if constexpr (REV) {
+      const long long r = seg_toks - 1 - (long long)i * C - grow[k];
+      return r >= 0 ? (unsigned)(r * ROWB) + gpc[k] : OOB;
+    } else {
+      return (unsigned)i * Cfg::MAT + gofs[k];
+    }
+  };
+  // OF32: byte offset of lane (g, li)'s 16 output bytes of token 16ib + li of tile i
+  auto out32_ofs = [&](int i, int ib) -> unsigned {
+    const int row = 16 * ib + li;
+    const unsigned col = (unsigned)(16 * W + 4 * g) * 4;
+    if constexpr (REV) {
+      const long long r = seg_toks - 1 - (long long)i * C - row;
+      return r >= 0 ? (unsigned)(r * D * 4) + col : OOB;
+    } else {
+      return (unsigned)(((long long)i * C + row) * D * 4) + col;
+    }
+  };
+  auto eta_ofs = [&](int i) -> unsigned {
+    if constexpr (REV) {
+      const long long r = seg_toks - 1 - (long long)i * C - erow;
+      return r >= 0 ? (unsigned)(r * 4) : OOB;
+    } else {
+      return (unsigned)i * (C * 4) + (unsigned)(erow * 4);
+    }
+  };
   // Tile i of the segment into ring slot i % STAGES (empty past the segment), in two parts: Q, and
   // K, V, eta.  The parts are issued at different points of a tile so that the workgroup's vector
   // memory instructions do not all queue at the tile boundary.
   auto issue_q = [&](int i) {
     unsigned char* st = smem + Cfg::OFF_RING + (i % Cfg::STAGES) * Cfg::STAGE + W * Cfg::MAT_LOADS * 1024;
-    const unsigned t = (unsigned)i * Cfg::MAT;
 #pragma unroll
-    for (int k = 0; k < Cfg::MAT_LOADS; ++k) dma16<PT_STREAM>(rq, t + gofs[k], st + k * 1024);
+    for (int k = 0; k < Cfg::MAT_LOADS; ++k) dma16<PT_STREAM>(rq, mat_ofs(i, k), st + k * 1024);
   };
   auto issue_kve = [&](int i) {
     unsigned char* st = smem + Cfg::OFF_RING + (i % Cfg::STAGES) * Cfg::STAGE + W * Cfg::MAT_LOADS * 1024;
-    const unsigned t = (unsigned)i * Cfg::MAT;
 #pragma unroll
-    for (int k = 0; k < Cfg::MAT_LOADS; ++k) dma16<PT_STREAM>(rk, t + gofs[k], st + Cfg::OFF_K + k * 1024);
+    for (int k = 0; k < Cfg::MAT_LOADS; ++k) dma16<PT_STREAM>(rk, mat_ofs(i, k), st + Cfg::OFF_K + k * 1024);
 #pragma unroll
-    for (int k = 0; k < Cfg::MAT_LOADS; ++k) dma16<PT_STREAM>(rv, t + gofs[k], st + Cfg::OFF_V + k * 1024);
+    for (int k = 0; k < Cfg::MAT_LOADS; ++k) dma16<PT_STREAM>(rv, mat_ofs(i, k), st + Cfg::OFF_V + k * 1024);
     unsigned char* ed = smem + Cfg::OFF_RING + (i % Cfg::STAGES) * Cfg::STAGE + Cfg::OFF_E + W * Cfg::EPW * 4;
-    if (l < Cfg::EPW) dma4<PT_STREAM>(re, (unsigned)i * (C * 4) + eofs, ed);
+    if (l < Cfg::EPW) dma4<PT_STREAM>(re, eta_ofs(i), ed);
   };
   // rows of tile i's outputs staged in its (dead) V region -> HBM, 16 bytes per lane, whole rows
   auto write_out = [&](int i) {
     const unsigned char* st = smem + Cfg::OFF_RING + (i % Cfg::STAGES) * Cfg::STAGE + Cfg::OFF_V;
-    const unsigned t = (unsigned)i * Cfg::MAT;
     u32x4 v[Cfg::MAT_LOADS];
 #pragma unroll
     for (int k = 0; k < Cfg::MAT_LOADS; ++k) v[k] = *(const u32x4*)(st + lofs[k]);
 #pragma unroll
-    for (int k = 0; k < Cfg::MAT_LOADS; ++k) buf_store16(ro, t + gofs[k], v[k]);
+    for (int k = 0; k < Cfg::MAT_LOADS; ++k) buf_store16(ro, mat_ofs(i, k), v[k]);
   };
 
   // The first two tiles go out to LDS first; the loads of the start state
@@ -316,11 +370,21 @@ __device__ __forceinline__ void seg_wave(const SegArgs& A, unsigned char* smem, 
   for (int i = 0; i < nt; ++i) {
     // Tile i has landed once only later-issued loads (and output stores) may be outstanding: per
     // wave the order is stores(i-2), Q(i+1) [tile i-1 start], K/V/eta(i+1) [tile i-1 middle].
-    if (i < 2)
+    // With OF32 a tile's NB stores follow its K/V/eta issue: after tile i's loads come
+    // stores(i-2), Q(i+1), K/V/eta(i+1), stores(i-1).
+    if constexpr (OF32) {
+      if (i == 0)
+        wait_vm_barrier<LOADS>();
+      else if (i == 1)
+        wait_vm_barrier<LOADS + NB>();
+      else
+        wait_vm_barrier<LOADS + 2 * NB>();
+    } else if (i < 2) {
       wait_vm_barrier<LOADS>();
-    else
+    } else {
       wait_vm_barrier<LOADS + Cfg::OUT_STORES>();
-    if (i >= 1) {
+    }
+    if (!OF32 && i >= 1) {
       write_out(i - 1);           // from the slot the next load overwrites: read it first
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     }
@@ -354,7 +418,7 @@ __device__ __forceinline__ void seg_wave(const SegArgs& A, unsigned char* smem, 
           const bf16x8 ka = *(const bf16x8*)(krow + ksb[kk]);
           p = mfma16(ka, qop(kk, ib), p);
         }
-        const floatx4 e4 = *(const floatx4*)(es + 16 * jb + 4 * g);
+        const floatx4 e4 = EM == 0 ? *(const floatx4*)(es + 16 * jb + 4 * g) : floatx4{1.f, 1.f, 1.f, 1.f};
         floatx4 f;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -396,7 +460,10 @@ __device__ __forceinline__ void seg_wave(const SegArgs& A, unsigned char* smem, 
     auto load_update = [&]() {
 #pragma unroll
       for (int kb = 0; kb < NB; ++kb) vt[kb] = lds_read_tr16(vs + kb * 16 * ROWB + vtr);
-      seg_update_eta<Cfg>(U, es, vt, g);
+      if constexpr (EM == 0)
+        seg_update_eta<Cfg>(U, es, vt, g);
+      else
+        seg_update_unit<Cfg>(U, vt);
       if constexpr (Cfg::KC == 2) seg_update_k<Cfg>(ka0, ks, ktr, 0);
     };
 #pragma unroll
@@ -432,23 +499,29 @@ __device__ __forceinline__ void seg_wave(const SegArgs& A, unsigned char* smem, 
       qs_mfma();
       issue_kve(i + Cfg::STAGES - 1);
     }
-    // outputs into the V region of this slot (written out after the next barrier)
+    // outputs into the V region of this slot (written out after the next barrier), or straight out
     unsigned char* ob = smem + Cfg::OFF_RING + (i % Cfg::STAGES) * Cfg::STAGE + Cfg::OFF_V;
 #pragma unroll
-    for (int ib = 0; ib < NB; ++ib)
-      *(bf16x4*)(ob + ib * 16 * ROWB + ofr) = to_bf16x4(acc[ib][0], acc[ib][1], acc[ib][2], acc[ib][3]);
+    for (int ib = 0; ib < NB; ++ib) {
+      const float eq = EM == 1 ? es[16 * ib + li] : 1.f;   // rate of the output row's own token
+      if constexpr (OF32)
+        buf_store16(ro32, out32_ofs(i, ib), __builtin_bit_cast(u32x4, eq * acc[ib]));
+      else
+        *(bf16x4*)(ob + ib * 16 * ROWB + ofr) = to_bf16x4(eq * acc[ib][0], eq * acc[ib][1], eq * acc[ib][2],
+                                                          eq * acc[ib][3]);
+    }
     if constexpr (Cfg::KC == 2) {
       bf16x8 ka1[MT];
       seg_update_k<Cfg>(ka1, ks, ktr, 1);
-      seg_update_mfma<Cfg>(S, ka0, U, 0);
-      seg_update_mfma<Cfg>(S, ka1, U, 1);
+      seg_update_mfma<Cfg, EM == 0>(S, ka0, U, 0);
+      seg_update_mfma<Cfg, EM == 0>(S, ka1, U, 1);
     } else {                      // one key half: its K operands are read here, within the register budget
       seg_update_k<Cfg>(ka0, ks, ktr, 0);
-      seg_update_mfma<Cfg>(S, ka0, U, 0);
+      seg_update_mfma<Cfg, EM == 0>(S, ka0, U, 0);
     }
 
   }
-  if (nt > 0) {
+  if (!OF32 && nt > 0) {
     wait_vm_barrier<0>();
     write_out(nt - 1);
   }
@@ -467,13 +540,13 @@ __device__ __forceinline__ void seg_wave(const SegArgs& A, unsigned char* smem, 
 
 // Outputs of segment s of head bh (grid BH x nseg), starting from W0 plus
 // the increments of the earlier segments of the head.
-template <int D, int CT, bool EXCL>
+template <int D, int CT, bool EXCL, bool REV, int EM, bool OF32>
 __global__ __attribute__((amdgpu_flat_work_group_size(1, D / 16 * WAVE),
                           amdgpu_waves_per_eu(SegCfg<D, CT>::WAVES_PER_SIMD))) void pt_seg_kernel(SegArgs A) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int bh = blockIdx.x / A.nseg, s = blockIdx.x % A.nseg;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  seg_wave<D, CT, EXCL>(A, smem, bh, s, w, threadIdx.x & 63);
+  seg_wave<D, CT, EXCL, REV, EM, OF32>(A, smem, bh, s, w, threadIdx.x & 63);
 }
 
 // Segment increments dS_s = K_s^T diag(eta_s) V_s for every segment but the
@@ -503,7 +576,10 @@ struct IncrCfg {
   static_assert(LDS_BYTES >= NC * MT * WAVE * 16, "the key-half reduction is staged through the ring");
 };
 
-template <int D>
+// REV: segment s holds the reversed tokens [s*seg_len, ...), i.e. the original range
+// [T - seg_end, T - seg_begin); the sum over its tokens does not depend on their order.
+// UNIT: unit rates, K_s^T V_s.
+template <int D, bool REV, bool UNIT>
 __global__ __launch_bounds__(2 * D / 16 * WAVE, 1) void pt_incr_kernel(SegArgs A) {
   using Cfg = IncrCfg<D>;
   constexpr int C = Cfg::C, ROWB = Cfg::ROWB, MT = Cfg::MT, NC = Cfg::NC, MAT = Cfg::MAT;
@@ -517,10 +593,11 @@ __global__ __launch_bounds__(2 * D / 16 * WAVE, 1) void pt_incr_kernel(SegArgs A
   const long long seg_end = min(seg_begin + A.seg_len, (long long)T);
   const long long seg_toks = seg_end > seg_begin ? seg_end - seg_begin : 0;
   const int nt = (int)((seg_toks + C - 1) / C);
+  const long long first = seg_toks > 0 ? (REV ? (long long)T - seg_end : seg_begin) : 0;
   // one buffer view per matrix for the whole segment: rows past its end read 0
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc(A.K + ((size_t)bh * T + seg_begin) * D, seg_toks * ROWB);
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc(A.V + ((size_t)bh * T + seg_begin) * D, seg_toks * ROWB);
-  const __amdgpu_buffer_rsrc_t re = make_rsrc(A.eta + (size_t)bh * T + seg_begin, seg_toks * 4);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(A.K + ((size_t)bh * T + first) * D, seg_toks * ROWB);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(A.V + ((size_t)bh * T + first) * D, seg_toks * ROWB);
+  const __amdgpu_buffer_rsrc_t re = make_rsrc(A.eta + (size_t)bh * T + first, seg_toks * 4);
 
   unsigned gofs[Cfg::MAT_LOADS];
 #pragma unroll
@@ -566,19 +643,25 @@ __global__ __launch_bounds__(2 * D / 16 * WAVE, 1) void pt_incr_kernel(SegArgs A
     // diag(eta) V for keys 32kc + 4g + j (first 16) and 32kc + 16 + 4g + j, column 16c + li
     const uint2 v0 = __builtin_bit_cast(uint2, lds_read_tr16(vs + vtr));
     const uint2 v1 = __builtin_bit_cast(uint2, lds_read_tr16(vs + 16 * ROWB + vtr));
-    const floatx4 e0 = *(const floatx4*)(es + 32 * kc + 4 * g);
-    const floatx4 e1 = *(const floatx4*)(es + 32 * kc + 16 + 4 * g);
     bf16x8 evh, evl;
-    split8(floatx4{e0[0] * bf16lo_f(v0.x), e0[1] * bf16hi_f(v0.x), e0[2] * bf16lo_f(v0.y), e0[3] * bf16hi_f(v0.y)},
-           floatx4{e1[0] * bf16lo_f(v1.x), e1[1] * bf16hi_f(v1.x), e1[2] * bf16lo_f(v1.y), e1[3] * bf16hi_f(v1.y)},
-           evh, evl);
+    if constexpr (UNIT) {
+      evh = join(__builtin_bit_cast(bf16x4, v0), __builtin_bit_cast(bf16x4, v1));
+    } else {
+      const floatx4 e0 = *(const floatx4*)(es + 32 * kc + 4 * g);
+      const floatx4 e1 = *(const floatx4*)(es + 32 * kc + 16 + 4 * g);
+      split8(floatx4{e0[0] * bf16lo_f(v0.x), e0[1] * bf16hi_f(v0.x), e0[2] * bf16lo_f(v0.y), e0[3] * bf16hi_f(v0.y)},
+             floatx4{e1[0] * bf16lo_f(v1.x), e1[1] * bf16hi_f(v1.x), e1[2] * bf16lo_f(v1.y), e1[3] * bf16hi_f(v1.y)},
+             evh, evl);
+    }
     bf16x8 a[MT];
 #pragma unroll
     for (int m = 0; m < MT; ++m) a[m] = join(lds_read_tr16(ks + ktr[m]), lds_read_tr16(ks + 16 * ROWB + ktr[m]));
 #pragma unroll
     for (int m = 0; m < MT; ++m) S[m] = mfma16(a[m], evh, S[m]);
+    if constexpr (!UNIT) {
 #pragma unroll
-    for (int m = 0; m < MT; ++m) S[m] = mfma16(a[m], evl, S[m]);
+      for (int m = 0; m < MT; ++m) S[m] = mfma16(a[m], evl, S[m]);
+    }
   }
   // key half 1 of each column tile -> LDS (the ring is idle once every copy has landed), half 0 adds it
   wait_vm_barrier<0>();
@@ -807,13 +890,14 @@ bool per_token_supported(int64_t dk, int64_t dv, int64_t chunk, int dtype) {
 // Segment plan of the bf16 path: about one workgroup per workgroup slot of
 // the chip (256 compute units x workgroups per CU) over heads x segments,
 // each segment whole tiles of both passes (multiples of 64 tokens).
-SegPlan per_token_seg_plan(int64_t BH, int64_t T, int64_t dk) {
+SegPlan per_token_seg_plan(int64_t BH, int64_t T, int64_t dk, int64_t max_seg_tokens) {
   const int64_t slots = 256 * (dk == 128 ? SegCfg<128, seg_tile<128>()>::WG_PER_CU : SegCfg<64, seg_tile<64>()>::WG_PER_CU);
   const int64_t nchunks = (T + 63) / 64;
   int64_t p = BH >= slots ? 1 : slots / BH;
   p = std::max<int64_t>(1, std::min(p, nchunks));
-  // a segment's bytes are addressed with 32-bit offsets: at most 2^22 tokens (1 GB at d = 128) each
-  p = std::max<int64_t>(p, (nchunks + (1 << 16) - 1) >> 16);
+  // a segment's bytes are addressed with 32-bit offsets below 2^31: at most max_seg_tokens tokens each
+  const int64_t max_tiles = max_seg_tokens / 64;
+  p = std::max<int64_t>(p, (nchunks + max_tiles - 1) / max_tiles);
   const int64_t tiles = nchunks > 0 ? (nchunks + p - 1) / p : 0;
   const int64_t nseg = tiles > 0 ? (nchunks + tiles - 1) / tiles : 1;
   return SegPlan{(int)nseg, (int)(tiles * 64)};
@@ -825,37 +909,44 @@ size_t per_token_workspace(int64_t B, int64_t H, int64_t T, int64_t dk, int64_t 
   return sp.nseg > 1 ? (size_t)sp.nseg * (size_t)(B * H) * (size_t)dk * (size_t)dv * sizeof(float) : 0;
 }
 
-template <int D>
-static hipError_t launch_seg(const PerTokenArgs& a, hipStream_t stream, const Timing& tm) {
+// The three kernels of one bf16 pass over every head (forward order, or reversed with REV).
+template <int D, bool REV, int EM, bool OF32 = false>
+static hipError_t launch_seg_pass(const SegArgs& A, int BH, bool excl, hipStream_t stream, const Timing& tm) {
   using CfgD = IncrCfg<D>;
   using CfgF = SegCfg<D, seg_tile<D>()>;
-  const int BH = (int)(a.B * a.H);
-  const SegPlan sp = per_token_seg_plan(BH, a.T, D);
   // The scan kernel turns the increments into start states, so each output workgroup loads one
   // slot (measured: cheaper than summing the earlier slots in every workgroup's prologue, the
   // increments are still in the last-level cache when the scan reads them).
-  SegArgs A{(const bf16*)a.Q, (const bf16*)a.K, (const bf16*)a.V, a.eta, a.W0, (floatx4*)a.ws,
-            (bf16*)a.O, a.W_out, (int)a.T, sp.nseg, sp.seg_len};
   hipError_t e;
-  if (sp.nseg > 1) {
-    auto kd = pt_incr_kernel<D>;
+  if (A.nseg > 1) {
+    auto kd = pt_incr_kernel<D, REV, EM != 0>;
     if ((e = hipFuncSetAttribute((const void*)kd, hipFuncAttributeMaxDynamicSharedMemorySize, CfgD::LDS_BYTES)) !=
         hipSuccess)
       return e;
-    hipLaunchKernelGGL(kd, dim3(BH * (sp.nseg - 1)), dim3(CfgD::THREADS), CfgD::LDS_BYTES, stream, A);
+    hipLaunchKernelGGL(kd, dim3(BH * (A.nseg - 1)), dim3(CfgD::THREADS), CfgD::LDS_BYTES, stream, A);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(pt_seg_scan_kernel<D>, dim3(BH * (D * D / 4 / 256)), dim3(256), 0, stream, a.W0,
-                       (floatx4*)a.ws, sp.nseg);
+    hipLaunchKernelGGL(pt_seg_scan_kernel<D>, dim3(BH * (D * D / 4 / 256)), dim3(256), 0, stream, A.W0, A.part,
+                       A.nseg);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  auto kf = a.exclusive ? pt_seg_kernel<D, seg_tile<D>(), true> : pt_seg_kernel<D, seg_tile<D>(), false>;
+  auto kf = excl ? pt_seg_kernel<D, seg_tile<D>(), true, REV, EM, OF32>
+                 : pt_seg_kernel<D, seg_tile<D>(), false, REV, EM, OF32>;
   if ((e = hipFuncSetAttribute((const void*)kf, hipFuncAttributeMaxDynamicSharedMemorySize, CfgF::LDS_BYTES)) !=
       hipSuccess)
     return e;
   if ((e = mark(tm.start, stream)) != hipSuccess) return e;
-  hipLaunchKernelGGL(kf, dim3(BH * sp.nseg), dim3(CfgF::THREADS), CfgF::LDS_BYTES, stream, A);
+  hipLaunchKernelGGL(kf, dim3(BH * A.nseg), dim3(CfgF::THREADS), CfgF::LDS_BYTES, stream, A);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   return mark(tm.stop, stream);
+}
+
+template <int D>
+static hipError_t launch_seg(const PerTokenArgs& a, hipStream_t stream, const Timing& tm) {
+  const int BH = (int)(a.B * a.H);
+  const SegPlan sp = per_token_seg_plan(BH, a.T, D);
+  const SegArgs A{(const bf16*)a.Q, (const bf16*)a.K, (const bf16*)a.V, a.eta, a.W0, (floatx4*)a.ws,
+                  (bf16*)a.O, a.W_out, (int)a.T, sp.nseg, sp.seg_len};
+  return launch_seg_pass<D, false, 0>(A, BH, a.exclusive != 0, stream, tm);
 }
 
 hipError_t launch_per_token(const PerTokenArgs& a, hipStream_t stream, const Timing& tm) {
@@ -865,6 +956,139 @@ hipError_t launch_per_token(const PerTokenArgs& a, hipStream_t stream, const Tim
     return c == 16 ? launch_fp32<128, 16>(a, stream, tm) : c == 32 ? launch_fp32<128, 32>(a, stream, tm) : launch_fp32<128, 64>(a, stream, tm);
   }
   return a.DK == 128 ? launch_seg<128>(a, stream, tm) : launch_seg<64>(a, stream, tm);
+}
+
+
+// ---------------------------------------------------------------------------
+// Backward of the bf16 per-token form.  With G_t = dW_T + sum over the reads
+// at or after step t (strictly after for the exclusive read) of q^T dO, the
+// gradients are dq_t = dO_t S_t^T, dk_t = eta_t v_t G_t^T, dv_t = eta_t k_t G_t,
+// deta_t = <k_t G_t, v_t> and dW0 = G_0 (the memory's gradient after the
+// first token).  Each is the forward recurrence with other operands and the
+// rates placed elsewhere, so every output is rounded to bf16 once:
+//   dQ:  queries dO, keys V, values K, rates on the keys, from W0^T  (forward order)
+//   dV:  queries K, keys Q, values dO, rates on the outputs, from dW_T
+//        (reverse order: dv_t = eta_t k_t G_t; the final memory is dW0)
+//   dK:  queries V, keys dO, values Q, rates on the outputs, from dW_T^T
+//        (reverse order: dk_t = eta_t v_t G_t^T)
+//   u:   as dV without rates, u_t = k_t G_t, then deta_t = <u_t, v_t>.
+// The gradients and u are written as float32 (a bf16 result could not be
+// more accurate than its own rounding, which for these heavy-tailed rows is
+// about the size of the accuracy budget).
+// Workspace: the segment slots (shared by the passes, which run in stream
+// order), W0^T, dW_T^T, a discarded final memory and u (fp32).
+// ---------------------------------------------------------------------------
+// float32 rows of a segment must stay below 2^31 bytes: 2^21 tokens at d = 128
+constexpr int64_t BWD_MAX_SEG_TOKENS = (int64_t)1 << 21;
+struct BwdLayout {
+  size_t slots, w0t, dwt, junk, u, total;
+};
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+static BwdLayout bwd_layout(int64_t B, int64_t H, int64_t T, int64_t D) {
+  BwdLayout L;
+  const size_t BH = (size_t)(B * H), st = BH * D * D * 4, ntok = BH * (size_t)T;
+  size_t o = 0;
+  const SegPlan sp = per_token_seg_plan(B * H, T, D, BWD_MAX_SEG_TOKENS);
+  L.slots = o; o += align256(sp.nseg > 1 ? (size_t)sp.nseg * st : 0);
+  L.w0t = o; o += align256(st);
+  L.dwt = o; o += align256(st);
+  L.junk = o; o += align256(st);
+  L.u = o; o += align256(ntok * D * 4);
+  L.total = o;
+  return L;
+}
+
+size_t per_token_backward_workspace(int64_t B, int64_t H, int64_t T, int64_t dk) {
+  return bwd_layout(B, H, T, dk).total;
+}
+
+// at[bh] = a[bh]^T and bt[bh] = b[bh]^T for D x D fp32 matrices, one output element per thread
+template <int D>
+__global__ __launch_bounds__(256) void pt_transpose2_kernel(const float* __restrict__ a, const float* __restrict__ b,
+                                                            float* __restrict__ at, float* __restrict__ bt, int BH) {
+  const long long f = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (f >= (long long)BH * D * D) return;
+  const long long h = f / (D * D);
+  const int r = (int)((f / D) % D), c = (int)(f % D);
+  const long long src = h * D * D + (long long)c * D + r;
+  at[f] = a[src];
+  bt[f] = b[src];
+}
+
+// deta = <u, v> per token (u fp32, V bf16).  A token's row is covered by
+// D/8 consecutive lanes, 8 values each; the products are summed over those
+// lanes.
+template <int D>
+__global__ __launch_bounds__(256) void pt_bwd_rate_grad_kernel(const float* __restrict__ u, const bf16* __restrict__ V,
+                                                               float* __restrict__ deta, long long ntok) {
+  constexpr int LPT = D / 8;          // lanes per token
+  constexpr int TPB = 256 / LPT;      // tokens per block and step
+  const int sub = threadIdx.x % LPT;
+  for (long long t = (long long)blockIdx.x * TPB + threadIdx.x / LPT; t < ntok; t += (long long)gridDim.x * TPB) {
+    const size_t o = (size_t)t * D + sub * 8;
+    const floatx4 u0 = *(const floatx4*)(u + o), u1 = *(const floatx4*)(u + o + 4);
+    const u32x4 vv = *(const u32x4*)(V + o);
+    float dot = 0.f;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      dot = fmaf(u0[2 * j], bf16lo_f(vv[j]), dot);
+      dot = fmaf(u0[2 * j + 1], bf16hi_f(vv[j]), dot);
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      dot = fmaf(u1[2 * j], bf16lo_f(vv[2 + j]), dot);
+      dot = fmaf(u1[2 * j + 1], bf16hi_f(vv[2 + j]), dot);
+    }
+#pragma unroll
+    for (int m = LPT / 2; m >= 1; m >>= 1) dot += __shfl_xor(dot, m);   // within the token's lanes
+    if (sub == 0) deta[t] = dot;
+  }
+}
+
+template <int D>
+static hipError_t launch_bwd(const PerTokenBwdArgs& a, hipStream_t stream) {
+  const int BH = (int)(a.B * a.H);
+  const long long ntok = (long long)BH * a.T;
+  const BwdLayout L = bwd_layout(a.B, a.H, a.T, D);
+  char* ws = (char*)a.ws;
+  float* w0t = (float*)(ws + L.w0t);
+  float* dwt = (float*)(ws + L.dwt);
+  float* junk = (float*)(ws + L.junk);
+  float* u = (float*)(ws + L.u);
+  floatx4* slots = (floatx4*)(ws + L.slots);
+  const bf16 *Q = (const bf16*)a.Q, *K = (const bf16*)a.K, *V = (const bf16*)a.V, *dO = (const bf16*)a.dO;
+  hipError_t e;
+  hipLaunchKernelGGL(pt_transpose2_kernel<D>, dim3((BH * D * D + 255) / 256), dim3(256), 0, stream, a.W0, a.dW, w0t,
+                     dwt, BH);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const SegPlan sp = per_token_seg_plan(BH, a.T, D, BWD_MAX_SEG_TOKENS);
+  const int T = (int)a.T;
+  const bool excl = a.exclusive != 0;
+  const Timing none;
+  // (SegArgs.O is typed bf16; the OF32 passes write floats through it)
+  const SegArgs Aq{dO, V, K, a.eta, w0t, slots, (bf16*)a.dQ, junk, T, sp.nseg, sp.seg_len};
+  if ((e = launch_seg_pass<D, false, 0, true>(Aq, BH, excl, stream, none)) != hipSuccess) return e;
+  const SegArgs Av{K, Q, dO, a.eta, a.dW, slots, (bf16*)a.dV, a.dW0, T, sp.nseg, sp.seg_len};
+  if ((e = launch_seg_pass<D, true, 1, true>(Av, BH, excl, stream, none)) != hipSuccess) return e;
+  const SegArgs Ak{V, dO, Q, a.eta, dwt, slots, (bf16*)a.dK, junk, T, sp.nseg, sp.seg_len};
+  if ((e = launch_seg_pass<D, true, 1, true>(Ak, BH, excl, stream, none)) != hipSuccess) return e;
+  if (ntok > 0) {
+    const SegArgs Au{K, Q, dO, a.eta, a.dW, slots, (bf16*)(void*)u, junk, T, sp.nseg, sp.seg_len};
+    if ((e = launch_seg_pass<D, true, 2, true>(Au, BH, excl, stream, none)) != hipSuccess) return e;
+    constexpr int TPB = 256 / (D / 8);
+    const unsigned grid = (unsigned)std::min<long long>((ntok + TPB - 1) / TPB, 8192);
+    hipLaunchKernelGGL(pt_bwd_rate_grad_kernel<D>, dim3(grid), dim3(256), 0, stream, u, V, a.deta, ntok);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+bool per_token_backward_supported(int64_t dk, int64_t dv, int64_t chunk, int dtype) {
+  return dtype == 1 && per_token_supported(dk, dv, chunk, dtype);
+}
+
+hipError_t launch_per_token_backward(const PerTokenBwdArgs& a, hipStream_t stream) {
+  return a.DK == 128 ? launch_bwd<128>(a, stream) : launch_bwd<64>(a, stream);
 }
 
 }  // namespace ttt

@@ -39,14 +39,14 @@ def test_exports_every_declared_symbol():
     names = declared_functions()
     assert {"ttt_la_forward", "ttt_la_workspace_bytes", "ttt_la_status_string", "ttt_la_abi_version",
             "ttt_la_event_create", "ttt_la_event_record", "ttt_la_event_elapsed_ms",
-            "ttt_la_event_destroy"} <= set(names)
+            "ttt_la_event_destroy", "ttt_la_backward", "ttt_la_backward_workspace_bytes"} <= set(names)
     for n in names:
         assert hasattr(L, n), f"{n} not exported"
 
 
 @needs_lib
 def test_version_and_status_strings():
-    assert la.lib().ttt_la_abi_version() == 2
+    assert la.lib().ttt_la_abi_version() == 3
     for s in range(10):
         assert la.status_string(s) and la.status_string(s) != "unknown status"
     assert la.status_string(99) == "unknown status"
@@ -175,3 +175,47 @@ def test_event_helpers_reject_null():
     assert L.ttt_la_event_record(None, None) == 1
     assert L.ttt_la_event_elapsed_ms(None, None, None) == 1
     assert L.ttt_la_event_destroy(None) == 0
+
+
+def bcall(desc=None, mode=0, chunk=64, ws_bytes=1 << 34, **kw):
+    if desc is None:
+        desc = la.make_desc(1, 2, 128, 64, 64, 0, la.BF16)
+    p = dict(Q=ptr(0), K=ptr(1), V=ptr(2), eta=ptr(3), W0=ptr(4), dO=ptr(5), dW=ptr(6), dQ=ptr(7), dK=ptr(8),
+             dV=ptr(9), deta=ptr(10), dW0=ptr(11), ws=ptr(12))
+    p.update(kw)
+    return la.backward_raw(p["Q"], p["K"], p["V"], p["eta"], p["W0"], p["dO"], p["dW"], chunk, mode, desc, p["dQ"],
+                           p["dK"], p["dV"], p["deta"], p["dW0"], p["ws"], ws_bytes, None)
+
+
+@needs_lib
+@pytest.mark.parametrize("kw,code", [
+    (dict(Q=None), 1), (dict(dO=None), 1), (dict(dW=None), 1), (dict(dQ=None), 1), (dict(deta=None), 1),
+    (dict(dW0=None), 1), (dict(ws=None), 1), (dict(W0=None), 1),
+    (dict(mode=1), 6), (dict(mode=2), 2), (dict(mode=4), 6), (dict(mode=6), 5), (dict(chunk=0), 3),
+    (dict(desc=la.make_desc(1, 2, 128, 64, 64, 0, la.FP32)), 6),       # bf16 only
+    (dict(desc=la.make_desc(1, 2, 128, 96, 96, 0, la.BF16)), 6),
+    (dict(chunk=256), 6),
+    (dict(ws_bytes=0), 8),
+    (dict(dQ=ptr(0)), 7), (dict(dK=ptr(5) + 64), 7), (dict(dW0=ptr(6)), 7), (dict(deta=ptr(7) + 4), 7),
+    (dict(dW0=ptr(4) + 8), 7), (dict(dV=ptr(12)), 7),
+])
+def test_backward_invalid_arguments(kw, code):
+    assert bcall(**kw) == code
+
+
+@needs_lib
+def test_backward_workspace():
+    # segment slots (4 segments per head here, as in the forward), W0^T, dW^T and a discarded memory,
+    # one fp32 token array
+    d = la.make_desc(4, 16, 4096, 128, 128, 0, la.BF16)
+    st = 64 * 128 * 128 * 4
+    n = la.workspace_bytes(d, 64, "per_token_linear") + 3 * st + 64 * 4096 * 128 * 4
+    assert la.backward_workspace_bytes(d, 64, "per_token_linear") == n
+    assert la.backward_workspace_bytes(d, 64, "per_token_linear_exclusive") == n
+    assert la.backward_workspace_bytes(d, 64, "large_chunk_linear") == 0
+    assert la.backward_workspace_bytes(la.make_desc(1, 1, 64, 64, 64, 0, la.FP32), 64, 0) == 0
+    assert bcall(desc=d, ws_bytes=n - 1) == 8
+    # a backward segment holds at most 2^21 tokens (float32 rows addressed below 2^31 bytes)
+    d1 = la.make_desc(256, 1, 1 << 22, 128, 128, 0, la.BF16)
+    st1 = 256 * 128 * 128 * 4
+    assert la.backward_workspace_bytes(d1, 64, 0) == 2 * st1 + 3 * st1 + 256 * (1 << 22) * 128 * 4
