@@ -188,6 +188,69 @@ def run_workload(name: str, steps: int, warmup: int, flush_mb: int, other_order:
     return rec
 
 
+def run_backward(name: str, steps: int, warmup: int, flush_mb: int, mode: str):
+    """Time ttt_la_backward (per-token modes) on a workload's inputs and
+    seeded upstream gradients, each call bracketed by events with the caches
+    flushed in between, as for the forward.  Algorithmic bytes: read Q, K,
+    V, dO (bf16), eta, W0, dW; write dQ, dK, dV (fp32), deta, dW0."""
+    import torch
+    import linear_attention_ttt_amd as la
+
+    s = workloads.spec(name, mode=mode)
+    x = workloads.generate(s, seed=0)
+    gr = workloads.generate_grads(s, seed=0)
+    dev = torch.device("cuda:0")
+    t = {k: torch.from_numpy(x[k]).to(dev) for k in ("Q", "K", "V", "eta", "W0")}
+    for k in ("Q", "K", "V"):
+        t[k] = t[k].to(torch.bfloat16)
+    dO = torch.from_numpy(gr["dO"]).to(dev).to(torch.bfloat16)
+    dW = torch.from_numpy(gr["dW"]).to(dev)
+    del x, gr
+    B, H, T, d = s["B"], s["H"], s["T"], s["d_k"]
+    desc = la.make_desc(B, H, T, d, d, 0, la.BF16)
+    ws = torch.empty(la.backward_workspace_bytes(desc, s["chunk"], s["mode"]), dtype=torch.uint8, device=dev)
+    outs = [torch.empty((B, H, T, d), dtype=torch.float32, device=dev) for _ in range(3)]
+    deta = torch.empty((B, H, T), dtype=torch.float32, device=dev)
+    dW0 = torch.empty_like(t["W0"])
+    flush = torch.empty(flush_mb << 20, dtype=torch.uint8, device=dev)
+    flush_rd = torch.ones((flush_mb << 20) // 4, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    ptrs = [t[k].data_ptr() for k in ("Q", "K", "V", "eta", "W0")]
+
+    def step():
+        st = la.backward_raw(*ptrs, dO.data_ptr(), dW.data_ptr(), s["chunk"], s["mode"], desc,
+                             *[o.data_ptr() for o in outs], deta.data_ptr(), dW0.data_ptr(), ws.data_ptr(),
+                             ws.numel(), stream.cuda_stream)
+        if st != 0:
+            raise RuntimeError(f"ttt_la_backward failed: {la.status_string(st)}")
+
+    for _ in range(warmup):
+        flush.fill_(1)
+        flush_rd.sum()
+        step()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        flush.fill_(i & 0xFF)
+        flush_rd.sum()
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    ms = np.array([a.elapsed_time(b) for a, b in zip(starts, ends)])
+    n = B * H * T
+    nbytes = n * (4 * d * 2 + 4) + n * (3 * d * 4 + 4) + 3 * B * H * d * d * 4
+    mean_s = float(ms.mean()) * 1e-3
+    rec = dict(workload=name, mode=s["mode"], ms_per_step=float(ms.mean()), ms_min=float(ms.min()),
+               tokens_per_s=B * T / mean_s, algorithmic_bytes=nbytes, hbm_GBps=nbytes / mean_s / 1e9,
+               hbm_frac=nbytes / mean_s / 1e9 / HBM_PEAK_GBS,
+               note="four passes of the segmented recurrence plus the rate-gradient reduction; float32 gradients")
+    del t, dO, dW, ws, outs, deta, dW0, flush, flush_rd
+    torch.cuda.empty_cache()
+    return rec
+
+
 def traffic_per_launch(kernel: str):
     """HBM bytes per launch of the dominant kernel from the committed counter
     summary (FETCH_SIZE + WRITE_SIZE, calibrated against a copy of known
@@ -250,6 +313,7 @@ def main():
     ap.add_argument("--no-others", action="store_true", help="skip the other workloads' sub-records")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--flush-mb", type=int, default=512)
+    ap.add_argument("--no-backward", action="store_true", help="skip the per-token backward sub-record")
     ap.add_argument("--other-order", action="store_true",
                     help="run every workload in its method's other read order (exclusive per-token read, "
                          "update-then-read chunks)")
@@ -282,6 +346,12 @@ def main():
                 others[name] = run_workload(name, max(10, a.steps // 2), 3, a.flush_mb, a.other_order)
             except Exception as e:  # a mode not built yet is reported, not fatal
                 others[name] = {"error": str(e)[:200]}
+    backward = None
+    if not a.no_backward and method_of(head["mode"]) == "per_token_linear" and head["dtype"] == "bf16":
+        try:
+            backward = run_backward(a.workload, max(10, a.steps // 2), 3, a.flush_mb, head["mode"])
+        except Exception as e:  # reported, not fatal
+            backward = {"error": str(e)[:200]}
     s = workloads.spec(a.workload, mode=head["mode"])
     k = head["kernel"]
     peak = HBM_PEAK_GBS if k["bound"] == "hbm" else BF16_PEAK_TFLOPS
@@ -309,6 +379,7 @@ def main():
         "roofline": roof,
         "cpu_baseline": None if a.no_cpu else cpu_baseline(a.workload, head["mode"]),
         "workloads": others,
+        "backward": backward,
     }
     print(json.dumps(line), flush=True)
 

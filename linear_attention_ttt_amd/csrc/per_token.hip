@@ -965,35 +965,34 @@ hipError_t launch_per_token(const PerTokenArgs& a, hipStream_t stream, const Tim
 // gradients are dq_t = dO_t S_t^T, dk_t = eta_t v_t G_t^T, dv_t = eta_t k_t G_t,
 // deta_t = <k_t G_t, v_t> and dW0 = G_0 (the memory's gradient after the
 // first token).  Each is the forward recurrence with other operands and the
-// rates placed elsewhere, so every output is rounded to bf16 once:
+// rates placed elsewhere:
 //   dQ:  queries dO, keys V, values K, rates on the keys, from W0^T  (forward order)
-//   dV:  queries K, keys Q, values dO, rates on the outputs, from dW_T
-//        (reverse order: dv_t = eta_t k_t G_t; the final memory is dW0)
+//   u:   queries K, keys Q, values dO, unit rates, from dW_T
+//        (reverse order: u_t = k_t G_t, written into dV; the final memory is dW0)
 //   dK:  queries V, keys dO, values Q, rates on the outputs, from dW_T^T
 //        (reverse order: dk_t = eta_t v_t G_t^T)
-//   u:   as dV without rates, u_t = k_t G_t, then deta_t = <u_t, v_t>.
-// The gradients and u are written as float32 (a bf16 result could not be
-// more accurate than its own rounding, which for these heavy-tailed rows is
-// about the size of the accuracy budget).
+// then one elementwise pass turns u into dV = eta u and deta = <u, v>.
+// The gradients are written as float32 (a bf16 result could not be more
+// accurate than its own rounding, which for these heavy-tailed rows is about
+// the size of the accuracy budget).
 // Workspace: the segment slots (shared by the passes, which run in stream
-// order), W0^T, dW_T^T, a discarded final memory and u (fp32).
+// order), W0^T, dW_T^T and a discarded final memory.
 // ---------------------------------------------------------------------------
 // float32 rows of a segment must stay below 2^31 bytes: 2^21 tokens at d = 128
 constexpr int64_t BWD_MAX_SEG_TOKENS = (int64_t)1 << 21;
 struct BwdLayout {
-  size_t slots, w0t, dwt, junk, u, total;
+  size_t slots, w0t, dwt, junk, total;
 };
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 static BwdLayout bwd_layout(int64_t B, int64_t H, int64_t T, int64_t D) {
   BwdLayout L;
-  const size_t BH = (size_t)(B * H), st = BH * D * D * 4, ntok = BH * (size_t)T;
+  const size_t BH = (size_t)(B * H), st = BH * D * D * 4;
   size_t o = 0;
   const SegPlan sp = per_token_seg_plan(B * H, T, D, BWD_MAX_SEG_TOKENS);
   L.slots = o; o += align256(sp.nseg > 1 ? (size_t)sp.nseg * st : 0);
   L.w0t = o; o += align256(st);
   L.dwt = o; o += align256(st);
   L.junk = o; o += align256(st);
-  L.u = o; o += align256(ntok * D * 4);
   L.total = o;
   return L;
 }
@@ -1002,25 +1001,33 @@ size_t per_token_backward_workspace(int64_t B, int64_t H, int64_t T, int64_t dk)
   return bwd_layout(B, H, T, dk).total;
 }
 
-// at[bh] = a[bh]^T and bt[bh] = b[bh]^T for D x D fp32 matrices, one output element per thread
+// at[bh] = a[bh]^T and bt[bh] = b[bh]^T for D x D fp32 matrices: one 64 x 64
+// tile of one matrix per workgroup (grid BH x 2 x (D/64)^2), read and written
+// in whole rows through LDS.
 template <int D>
 __global__ __launch_bounds__(256) void pt_transpose2_kernel(const float* __restrict__ a, const float* __restrict__ b,
-                                                            float* __restrict__ at, float* __restrict__ bt, int BH) {
-  const long long f = (long long)blockIdx.x * 256 + threadIdx.x;
-  if (f >= (long long)BH * D * D) return;
-  const long long h = f / (D * D);
-  const int r = (int)((f / D) % D), c = (int)(f % D);
-  const long long src = h * D * D + (long long)c * D + r;
-  at[f] = a[src];
-  bt[f] = b[src];
+                                                            float* __restrict__ at, float* __restrict__ bt) {
+  constexpr int NT = D / 64;
+  __shared__ float tile[64][65];
+  const int bh = blockIdx.x / (2 * NT * NT), which = (blockIdx.x / (NT * NT)) % 2, tt = blockIdx.x % (NT * NT);
+  const int tr = tt / NT, tc = tt % NT;            // source tile row, column
+  const float* src = (which ? b : a) + (size_t)bh * D * D;
+  float* dst = (which ? bt : at) + (size_t)bh * D * D;
+  const int x = threadIdx.x & 63, y0 = threadIdx.x >> 6;
+#pragma unroll
+  for (int y = y0; y < 64; y += 4) tile[y][x] = src[(size_t)(64 * tr + y) * D + 64 * tc + x];
+  __syncthreads();
+#pragma unroll
+  for (int y = y0; y < 64; y += 4) dst[(size_t)(64 * tc + y) * D + 64 * tr + x] = tile[x][y];
 }
 
-// deta = <u, v> per token (u fp32, V bf16).  A token's row is covered by
-// D/8 consecutive lanes, 8 values each; the products are summed over those
-// lanes.
+// In place: u -> dV = eta u, and deta = <u, v> per token (u fp32, V bf16).
+// A token's row is covered by D/8 consecutive lanes, 8 values each; the
+// products are summed over those lanes.
 template <int D>
-__global__ __launch_bounds__(256) void pt_bwd_rate_grad_kernel(const float* __restrict__ u, const bf16* __restrict__ V,
-                                                               float* __restrict__ deta, long long ntok) {
+__global__ __launch_bounds__(256) void pt_bwd_rate_grad_kernel(float* __restrict__ u, const bf16* __restrict__ V,
+                                                               const float* __restrict__ eta, float* __restrict__ deta,
+                                                               long long ntok) {
   constexpr int LPT = D / 8;          // lanes per token
   constexpr int TPB = 256 / LPT;      // tokens per block and step
   const int sub = threadIdx.x % LPT;
@@ -1028,6 +1035,9 @@ __global__ __launch_bounds__(256) void pt_bwd_rate_grad_kernel(const float* __re
     const size_t o = (size_t)t * D + sub * 8;
     const floatx4 u0 = *(const floatx4*)(u + o), u1 = *(const floatx4*)(u + o + 4);
     const u32x4 vv = *(const u32x4*)(V + o);
+    const float e = eta[t];
+    *(floatx4*)(u + o) = e * u0;
+    *(floatx4*)(u + o + 4) = e * u1;
     float dot = 0.f;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
@@ -1054,12 +1064,11 @@ static hipError_t launch_bwd(const PerTokenBwdArgs& a, hipStream_t stream) {
   float* w0t = (float*)(ws + L.w0t);
   float* dwt = (float*)(ws + L.dwt);
   float* junk = (float*)(ws + L.junk);
-  float* u = (float*)(ws + L.u);
   floatx4* slots = (floatx4*)(ws + L.slots);
   const bf16 *Q = (const bf16*)a.Q, *K = (const bf16*)a.K, *V = (const bf16*)a.V, *dO = (const bf16*)a.dO;
   hipError_t e;
-  hipLaunchKernelGGL(pt_transpose2_kernel<D>, dim3((BH * D * D + 255) / 256), dim3(256), 0, stream, a.W0, a.dW, w0t,
-                     dwt, BH);
+  hipLaunchKernelGGL(pt_transpose2_kernel<D>, dim3(BH * 2 * (D / 64) * (D / 64)), dim3(256), 0, stream, a.W0, a.dW,
+                     w0t, dwt);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const SegPlan sp = per_token_seg_plan(BH, a.T, D, BWD_MAX_SEG_TOKENS);
   const int T = (int)a.T;
@@ -1068,16 +1077,15 @@ static hipError_t launch_bwd(const PerTokenBwdArgs& a, hipStream_t stream) {
   // (SegArgs.O is typed bf16; the OF32 passes write floats through it)
   const SegArgs Aq{dO, V, K, a.eta, w0t, slots, (bf16*)a.dQ, junk, T, sp.nseg, sp.seg_len};
   if ((e = launch_seg_pass<D, false, 0, true>(Aq, BH, excl, stream, none)) != hipSuccess) return e;
-  const SegArgs Av{K, Q, dO, a.eta, a.dW, slots, (bf16*)a.dV, a.dW0, T, sp.nseg, sp.seg_len};
-  if ((e = launch_seg_pass<D, true, 1, true>(Av, BH, excl, stream, none)) != hipSuccess) return e;
+  const SegArgs Au{K, Q, dO, a.eta, a.dW, slots, (bf16*)a.dV, a.dW0, T, sp.nseg, sp.seg_len};
+  if ((e = launch_seg_pass<D, true, 2, true>(Au, BH, excl, stream, none)) != hipSuccess) return e;
   const SegArgs Ak{V, dO, Q, a.eta, dwt, slots, (bf16*)a.dK, junk, T, sp.nseg, sp.seg_len};
   if ((e = launch_seg_pass<D, true, 1, true>(Ak, BH, excl, stream, none)) != hipSuccess) return e;
   if (ntok > 0) {
-    const SegArgs Au{K, Q, dO, a.eta, a.dW, slots, (bf16*)(void*)u, junk, T, sp.nseg, sp.seg_len};
-    if ((e = launch_seg_pass<D, true, 2, true>(Au, BH, excl, stream, none)) != hipSuccess) return e;
     constexpr int TPB = 256 / (D / 8);
     const unsigned grid = (unsigned)std::min<long long>((ntok + TPB - 1) / TPB, 8192);
-    hipLaunchKernelGGL(pt_bwd_rate_grad_kernel<D>, dim3(grid), dim3(256), 0, stream, u, V, a.deta, ntok);
+    hipLaunchKernelGGL(pt_bwd_rate_grad_kernel<D>, dim3(grid), dim3(256), 0, stream, (float*)a.dV, V, a.eta, a.deta,
+                       ntok);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   return hipSuccess;
