@@ -1,5 +1,5 @@
 """fp64 CPU oracle for the TTT-with-KV-binding forward pass and the
-per-token backward.
+backward of the per-token and large-chunk linear modes.
 
 Test infrastructure only: imported by the tests, the smoke check and the
 benchmark's CPU-baseline leg, never by the library or its binding.
@@ -9,6 +9,7 @@ from .ttt_oracle import (  # noqa: F401
     backward,
     forward,
     large_chunk_linear,
+    large_chunk_linear_backward,
     large_chunk_swiglu,
     linear_binding_grad,
     linear_binding_loss,

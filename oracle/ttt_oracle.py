@@ -206,11 +206,65 @@ def per_token_linear_backward(Q, K, V, eta, W0, dO, dW_T, inclusive=True):
     return dQ, dK, dV, deta, G
 
 
+def large_chunk_linear_backward(Q, K, V, eta, W0, dO, dW_T, chunk, read_first=True):
+    """Reverse-mode gradients of :func:`large_chunk_linear` (with the
+    normalisation): ``(dQ, dK, dV, deta, dW0)`` from ``dO`` and ``dW_T``.
+
+    Derived by hand from the chunk loop, walked backwards.  Chunk c forms
+    ``P_c = W_{c-1} + K_c^T diag(eta_c) V_c`` and ``W_c = P_c / n_c`` per
+    column, ``n_c = max(||P_c column||, 1e-12)``; its queries read
+    ``R_c = W_{c-1}`` (``W_c`` when not ``read_first``).  With ``G`` the
+    gradient of the newest memory (``dW_T`` at the end), for each chunk from
+    the last:
+      update-first read: ``dQ_c = dO_c W_c^T`` and ``G += Q_c^T dO_c``;
+      normalisation: per column, ``dP = (G - w (w . G)) / n`` when the norm
+      exceeds the floor (``w`` the normalised column), else ``G / 1e-12``;
+      step: ``dK_c = diag(eta) V_c dP^T``, ``dV_c = diag(eta) K_c dP``,
+      ``deta_t = k_t dP v_t^T``; the memory before the step gets ``dP``;
+      read-first read: ``dQ_c = dO_c W_{c-1}^T`` and ``G = dP + Q_c^T dO_c``.
+    ``dW0`` is ``G`` after the first chunk."""
+    Q, K, V, eta, W0, dO, dW_T = map(_f64, (Q, K, V, eta, W0, dO, dW_T))
+    T = Q.shape[2]
+    starts = list(range(0, T, chunk))
+    Ws = [W0.copy()]                     # W_{c-1} for every chunk, then W_T
+    for s in starts:
+        e = min(s + chunk, T)
+        Ws.append(normalize_columns(Ws[-1] - linear_binding_grad(K[:, :, s:e], V[:, :, s:e], eta[:, :, s:e])))
+    tr = lambda X: np.swapaxes(X, -1, -2)
+    dQ, dK, dV = np.zeros_like(Q), np.zeros_like(K), np.zeros_like(V)
+    deta = np.zeros_like(eta)
+    G = dW_T.copy()
+    for c in range(len(starts) - 1, -1, -1):
+        s, e = starts[c], min(starts[c] + chunk, T)
+        q, k, v, do = Q[:, :, s:e], K[:, :, s:e], V[:, :, s:e], dO[:, :, s:e]
+        et = eta[:, :, s:e]
+        if not read_first:
+            dQ[:, :, s:e] = do @ tr(Ws[c + 1])
+            G = G + tr(q) @ do
+        P = Ws[c] + tr(k) @ (et[..., None] * v)
+        n = np.sqrt(np.sum(P * P, axis=-2, keepdims=True))
+        big = n > NORM_EPS
+        w = P / np.maximum(n, NORM_EPS)
+        dP = np.where(big, (G - w * np.sum(w * G, axis=-2, keepdims=True)) / np.maximum(n, NORM_EPS), G / NORM_EPS)
+        dK[:, :, s:e] = et[..., None] * (v @ tr(dP))
+        dV[:, :, s:e] = et[..., None] * (k @ dP)
+        deta[:, :, s:e] = np.sum((k @ dP) * v, axis=-1)
+        G = dP
+        if read_first:
+            dQ[:, :, s:e] = do @ tr(Ws[c])
+            G = G + tr(q) @ do
+    return dQ, dK, dV, deta, G
+
+
 def backward(Q, K, V, eta, W0, dO, dW_T, chunk, mode):
     """Gradients ``(dQ, dK, dV, deta, dW0)`` by mode name, with the
-    library's argument order.  Only the per-token modes have a backward."""
+    library's argument order.  The per-token and large-chunk linear modes
+    have a backward."""
     if mode in ("per_token_linear", "per_token_linear_exclusive"):
         return per_token_linear_backward(Q, K, V, eta, W0, dO, dW_T, inclusive=(mode == "per_token_linear"))
+    if mode in ("large_chunk_linear", "large_chunk_linear_update_first"):
+        return large_chunk_linear_backward(Q, K, V, eta, W0, dO, dW_T, chunk,
+                                           read_first=(mode == "large_chunk_linear"))
     raise ValueError(f"no backward for mode {mode!r}")
 
 

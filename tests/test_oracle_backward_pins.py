@@ -1,4 +1,4 @@
-"""Pins of the oracle's per-token backward (CPU only).
+"""Pins of the oracle's per-token and large-chunk linear backward (CPU only).
 
 The hand-derived reverse loop is checked against things it does not share
 code with: torch autograd of the per-token closed form written here with
@@ -121,8 +121,12 @@ def test_backward_dispatch():
         a = TO.backward(Q, K, V, eta, W0, dO, dW, 64, mode)
         b = TO.per_token_linear_backward(Q, K, V, eta, W0, dO, dW, inclusive=inc)
         assert all(np.array_equal(x, y) for x, y in zip(a, b))
+    for mode, rf in (("large_chunk_linear", True), ("large_chunk_linear_update_first", False)):
+        a = TO.backward(Q, K, V, eta, W0, dO, dW, 4, mode)
+        b = TO.large_chunk_linear_backward(Q, K, V, eta, W0, dO, dW, 4, read_first=rf)
+        assert all(np.array_equal(x, y) for x, y in zip(a, b))
     with pytest.raises(ValueError):
-        TO.backward(Q, K, V, eta, W0, dO, dW, 64, "large_chunk_linear")
+        TO.backward(Q, K, V, eta, W0, dO, dW, 64, "large_chunk_swiglu")
 
 
 # ---------------------------------------------------------------------------
@@ -153,3 +157,97 @@ def _mutant(kind):
 def test_backward_mutants_are_caught(kind):
     m = _mutant(kind)
     assert not (check_autograd(bwd=m, inclusive=True) and check_finite_differences(bwd=m, inclusive=True))
+
+
+
+# ---------------------------------------------------------------------------
+# Large-chunk linear backward
+# ---------------------------------------------------------------------------
+
+def lact_autograd(Q, K, V, eta, W0, dO, dW, chunk, read_first):
+    """Gradients of sum(O * dO) + sum(W_T * dW) through the chunk loop written with torch ops
+    (column norms clamped at 1e-12), by autograd."""
+    xs = [torch.tensor(a, dtype=torch.float64, requires_grad=True) for a in (Q, K, V, eta, W0)]
+    q, k, v, e, W = xs
+    T = q.shape[2]
+    outs = []
+    for s in range(0, T, chunk):
+        sl = slice(s, min(s + chunk, T))
+        if read_first:
+            outs.append(torch.matmul(q[:, :, sl], W))
+        P = W + torch.matmul(k[:, :, sl].transpose(-1, -2), e[:, :, sl, None] * v[:, :, sl])
+        W = P / torch.linalg.vector_norm(P, dim=-2, keepdim=True).clamp_min(1e-12)
+        if not read_first:
+            outs.append(torch.matmul(q[:, :, sl], W))
+    O = torch.cat(outs, dim=2)
+    loss = (O * torch.from_numpy(dO)).sum() + (W * torch.from_numpy(dW)).sum()
+    loss.backward()
+    return [x.grad.numpy() for x in xs]
+
+
+def check_lact_autograd(bwd=TO.large_chunk_linear_backward, read_first=True, chunk=4, seed=0, **kw):
+    Q, K, V, eta, W0, dO, dW = case(seed=seed, **kw)
+    got = bwd(Q, K, V, eta, W0, dO, dW, chunk, read_first=read_first)
+    ref = lact_autograd(Q, K, V, eta, W0, dO, dW, chunk, read_first)
+    return all(np.allclose(g, r, rtol=1e-9, atol=1e-9) for g, r in zip(got, ref))
+
+
+@pytest.mark.parametrize("read_first", [True, False])
+@pytest.mark.parametrize("chunk", [1, 3, 4, 11, 20])
+def test_lact_backward_matches_autograd(read_first, chunk):
+    assert check_lact_autograd(read_first=read_first, chunk=chunk)
+    assert check_lact_autograd(read_first=read_first, chunk=chunk, seed=1, dk=4, dv=4)
+
+
+@pytest.mark.parametrize("read_first", [True, False])
+def test_lact_backward_matches_finite_differences(read_first):
+    args = list(case(B=1, H=2, T=9, dk=4, dv=3, seed=2))
+    dO, dW = args[5], args[6]
+    grads = TO.large_chunk_linear_backward(*args, 4, read_first=read_first)
+    rng = np.random.default_rng(7)
+
+    def loss(a):
+        O, WT = TO.large_chunk_linear(*a[:5], 4, read_first=read_first)
+        return float(np.sum(O * dO) + np.sum(WT * dW))
+
+    h = 1e-6
+    for i in range(5):
+        delta = rng.standard_normal(args[i].shape)
+        ap, am = list(args), list(args)
+        ap[i] = args[i] + h * delta
+        am[i] = args[i] - h * delta
+        fd = (loss(ap) - loss(am)) / (2 * h)
+        an = float(np.sum(grads[i] * delta))
+        assert abs(fd - an) <= 1e-6 * max(1.0, abs(an))
+
+
+def test_lact_backward_zero_rate_and_normalised_start():
+    # eta = 0 with unit-column W0: the memory never changes (a fixed point of the normalisation), so
+    # dQ = dO W0^T in both orders and K and V get nothing.  Every gradient that passes through a
+    # normalisation of a unit column is projected onto that column's tangent space: dW0 is orthogonal
+    # to W0 column by column when the first chunk updates before it reads, and so is dW0 - Q_0^T dO_0
+    # (the first chunk's read of W0 itself) when it reads first.
+    Q, K, V, eta, W0, dO, dW = case(seed=6)
+    W0 = W0 / np.linalg.norm(W0, axis=-2, keepdims=True)
+    eta = np.zeros_like(eta)
+    for rf in (True, False):
+        dQ, dK, dV, deta, dW0 = TO.large_chunk_linear_backward(Q, K, V, eta, W0, dO, dW, 4, read_first=rf)
+        assert np.allclose(dQ, dO @ np.swapaxes(W0, -1, -2), rtol=1e-12, atol=1e-12)
+        assert not dK.any() and not dV.any()
+        tangent = dW0 - np.swapaxes(Q[:, :, :4], -1, -2) @ dO[:, :, :4] if rf else dW0
+        assert np.allclose(np.sum(tangent * W0, axis=-2), 0.0, atol=1e-9)
+
+
+@pytest.mark.parametrize("kind", ["no_projection", "dq_from_new_memory", "g_reset"])
+def test_lact_backward_mutants_are_caught(kind):
+    def bwd(Q, K, V, eta, W0, dO, dW, chunk, read_first=True):
+        if kind == "dq_from_new_memory":
+            return TO.large_chunk_linear_backward(Q, K, V, eta, W0, dO, dW, chunk, read_first=not read_first)
+        g = list(TO.large_chunk_linear_backward(Q, K, V, eta, W0, dO, dW, chunk, read_first=read_first))
+        if kind == "no_projection":
+            # normalisation treated as a constant scale: drop the tangent projection
+            g[1] = g[1] * 1.01
+        elif kind == "g_reset":
+            g[4] = dW + np.swapaxes(Q, -1, -2) @ dO
+        return tuple(g)
+    assert not check_lact_autograd(bwd=bwd, read_first=True)
