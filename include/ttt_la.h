@@ -1,7 +1,7 @@
 /*
  * libttt_la - forward pass of a test-time-training (TTT) layer with
- * key-value binding, and the backward pass of its per-token form, for AMD
- * Instinct MI355X (gfx950).
+ * key-value binding, and the backward pass of its per-token and large-chunk
+ * linear forms, for AMD Instinct MI355X (gfx950).
  *
  * The method (pages on "Test-Time Training with KV Binding Is Secretly
  * Linear Attention", paper summary technical sections 2B and 3, and the
@@ -188,19 +188,29 @@ int ttt_la_event_destroy(void* event);
 /*
  * ttt_la_backward(Q, K, V, eta, W0, dO, dW_out, chunk, mode) -> (dQ, dK, dV, deta, dW0)
  *
- * Gradients of a scalar loss through ttt_la_forward in the per-token modes,
- * for training the model around the layer (the paper summary reports the
- * parallel form's speed-up for training as well as inference, technical
- * section 4).  With G_t = dW_out + sum of q_j^T dO_j over the reads j at or
- * after token t (strictly after it for TTT_LA_PER_TOKEN_LINEAR_EXCLUSIVE),
- * and S_t the memory token t's query reads:
+ * Gradients of a scalar loss through ttt_la_forward in the per-token and
+ * large-chunk linear modes, for training the model around the layer (the
+ * paper summary reports the parallel form's speed-up for training as well as
+ * inference, technical section 4).
+ *   Per-token: with G_t = dW_out + sum of q_j^T dO_j over the reads j at or
+ *   after token t (strictly after it for TTT_LA_PER_TOKEN_LINEAR_EXCLUSIVE),
+ *   and S_t the memory token t's query reads:
  *     dq_t = dO_t S_t^T,   dk_t = eta_t v_t G_t^T,   dv_t = eta_t k_t G_t,
  *     deta_t = k_t G_t v_t^T,   dW0 = dW_out + sum_t q_t^T dO_t.
+ *   Large-chunk linear: chunk c forms P_c = W_{c-1} + K_c^T diag(eta_c) V_c
+ *   and W_c = P_c / n_c per column; its queries read R_c (W_{c-1}, or W_c
+ *   for TTT_LA_LARGE_CHUNK_LINEAR_UPDATE_FIRST).  From the last chunk back,
+ *   with G = dW_out at the end and A_c = Q_c^T dO_c: (update-first) G += A_c;
+ *   dP_c = (G - w (w . G)) / n_c per column (G / 1e-12 when the norm is at
+ *   the floor); G = dP_c; (read-first) G += A_c.  Then dQ_c = dO_c R_c^T,
+ *   dK_c = diag(eta) V_c dP_c^T, dV_c = diag(eta) K_c dP_c,
+ *   deta_t = k_t dP_c v_t^T, and dW0 = G.
  *
  *   Q, K, V, eta, W0, chunk, desc   as passed to ttt_la_forward (the forward
  *                  outputs are not needed: the memories are recomputed)
- *   mode           TTT_LA_PER_TOKEN_LINEAR or TTT_LA_PER_TOKEN_LINEAR_EXCLUSIVE
- *                  (ERR_UNSUPPORTED for the large-chunk modes)
+ *   mode           TTT_LA_PER_TOKEN_LINEAR, TTT_LA_PER_TOKEN_LINEAR_EXCLUSIVE,
+ *                  TTT_LA_LARGE_CHUNK_LINEAR or TTT_LA_LARGE_CHUNK_LINEAR_UPDATE_FIRST
+ *                  (ERR_UNSUPPORTED for the SwiGLU modes)
  *   dO             [B,H,T,d_v] io_dtype, device: gradient of O
  *   dW_out         [B,H,d_k,d_v] float32, device: gradient of W_out (pass
  *                  zeros if the final memory does not reach the loss)
@@ -215,7 +225,8 @@ int ttt_la_event_destroy(void* event);
  *                  bytes of device scratch (contents on entry do not matter)
  *   stream         hipStream_t (NULL = the default stream)
  *
- * Supported set: d_k = d_v in {64, 128}, bf16, chunk in {16, 32, 64, 128}.
+ * Supported set: bf16; per-token d_k = d_v in {64, 128}, chunk in
+ * {16, 32, 64, 128}; large-chunk linear d_k = d_v in {64, 128}, any chunk.
  * Every pointer is required (ERR_NULL), except that the per-token arrays
  * may be NULL when T = 0 (then dW0 = dW_out); no output may overlap an input,
  * another output or the workspace (ERR_ALIAS).  Checks, ownership and

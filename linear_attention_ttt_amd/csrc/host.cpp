@@ -184,13 +184,22 @@ int ttt_la_forward(const void* Q, const void* K, const void* V, const float* eta
 }
 
 static bool backward_ok(const ttt_la_desc& d, int64_t chunk, int32_t mode) {
-  return method_of(mode) == TTT_LA_PER_TOKEN_LINEAR && supported(d, chunk, mode) &&
-         ttt::per_token_backward_supported(d.d_k, d.d_v, chunk, d.io_dtype);
+  if (!supported(d, chunk, mode) || d.io_dtype != TTT_LA_BF16) return false;
+  switch (method_of(mode)) {
+    case TTT_LA_PER_TOKEN_LINEAR: return ttt::per_token_backward_supported(d.d_k, d.d_v, chunk, d.io_dtype);
+    case TTT_LA_LARGE_CHUNK_LINEAR: return true;
+  }
+  return false;
+}
+
+static size_t backward_workspace(const ttt_la_desc& d, int64_t chunk, int32_t mode) {
+  if (method_of(mode) == TTT_LA_PER_TOKEN_LINEAR) return ttt::per_token_backward_workspace(d.B, d.H, d.T, d.d_k);
+  return ttt::large_chunk_linear_backward_workspace(d.B, d.H, d.T, d.d_k, chunk);
 }
 
 size_t ttt_la_backward_workspace_bytes(const ttt_la_desc* desc, int64_t chunk, int32_t mode) {
   if (check_problem(desc, chunk, mode) != TTT_LA_OK || !backward_ok(*desc, chunk, mode)) return 0;
-  return ttt::per_token_backward_workspace(desc->B, desc->H, desc->T, desc->d_k);
+  return backward_workspace(*desc, chunk, mode);
 }
 
 int ttt_la_backward(const void* Q, const void* K, const void* V, const float* eta, const float* W0,
@@ -203,7 +212,7 @@ int ttt_la_backward(const void* Q, const void* K, const void* V, const float* et
   if (!W0 || !dW_out || !dW0 || !workspace) return TTT_LA_ERR_NULL;
   if (d.T > 0 && (!Q || !K || !V || !eta || !dO || !dQ || !dK || !dV || !deta)) return TTT_LA_ERR_NULL;
   if (!backward_ok(d, chunk, mode)) return TTT_LA_ERR_UNSUPPORTED;
-  const size_t need = ttt::per_token_backward_workspace(d.B, d.H, d.T, d.d_k);
+  const size_t need = backward_workspace(d, chunk, mode);
   if (workspace_bytes < need) return TTT_LA_ERR_WORKSPACE;
 
   const size_t es = 2;
@@ -221,9 +230,12 @@ int ttt_la_backward(const void* Q, const void* K, const void* V, const float* et
       if (overlap(outs[i], outs[j])) return TTT_LA_ERR_ALIAS;
   }
 
-  ttt::PerTokenBwdArgs a{Q,  K,  V,    eta, W0,        dO,  dW_out, dQ,  dK,  dV,          deta,
+  ttt::BackwardArgs a{Q,  K,  V,    eta, W0,        dO,  dW_out, dQ,  dK,  dV,          deta,
                          dW0, workspace, d.B, d.H, d.T, d.d_k, d.d_v, chunk, d.io_dtype, other_order(mode) ? 1 : 0};
-  return ttt::launch_per_token_backward(a, (hipStream_t)stream) == hipSuccess ? TTT_LA_OK : TTT_LA_ERR_HIP;
+  const hipError_t e = method_of(mode) == TTT_LA_PER_TOKEN_LINEAR
+                           ? ttt::launch_per_token_backward(a, (hipStream_t)stream)
+                           : ttt::launch_large_chunk_linear_backward(a, (hipStream_t)stream);
+  return e == hipSuccess ? TTT_LA_OK : TTT_LA_ERR_HIP;
 }
 
 int ttt_la_event_create(void** event) {

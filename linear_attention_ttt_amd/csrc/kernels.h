@@ -38,9 +38,9 @@ bool per_token_supported(int64_t dk, int64_t dv, int64_t chunk, int dtype);
 size_t per_token_workspace(int64_t B, int64_t H, int64_t T, int64_t dk, int64_t dv, int dtype);
 hipError_t launch_per_token(const PerTokenArgs& a, hipStream_t stream, const Timing& tm);
 
-// Backward of the per-token mode (bf16): gradients of O and of the final memory in, gradients of
-// Q, K, V, eta and W0 out.
-struct PerTokenBwdArgs {
+// Backward (bf16 inputs): gradients of O and of the final memory in, float32 gradients of Q, K, V,
+// eta and W0 out.  other_order: the exclusive per-token read, or update-then-read chunks.
+struct BackwardArgs {
   const void* Q;
   const void* K;
   const void* V;
@@ -56,11 +56,11 @@ struct PerTokenBwdArgs {
   void* ws;
   int64_t B, H, T, DK, DV, chunk;
   int dtype;
-  int exclusive;
+  int other_order;
 };
 bool per_token_backward_supported(int64_t dk, int64_t dv, int64_t chunk, int dtype);
 size_t per_token_backward_workspace(int64_t B, int64_t H, int64_t T, int64_t dk);
-hipError_t launch_per_token_backward(const PerTokenBwdArgs& a, hipStream_t stream);
+hipError_t launch_per_token_backward(const BackwardArgs& a, hipStream_t stream);
 
 struct LargeChunkArgs {
   const void* Q;
@@ -79,6 +79,8 @@ struct LargeChunkArgs {
 bool large_chunk_linear_supported(int64_t dk, int64_t dv, int64_t chunk, int dtype);
 size_t large_chunk_linear_workspace(int64_t B, int64_t H, int64_t T, int64_t dk, int64_t dv, int64_t chunk);
 hipError_t launch_large_chunk_linear(const LargeChunkArgs& a, hipStream_t stream, const Timing& tm);
+size_t large_chunk_linear_backward_workspace(int64_t B, int64_t H, int64_t T, int64_t d, int64_t chunk);
+hipError_t launch_large_chunk_linear_backward(const BackwardArgs& a, hipStream_t stream);
 
 bool large_chunk_swiglu_supported(int64_t d, int64_t dh, int64_t chunk, int dtype);
 size_t large_chunk_swiglu_workspace(int64_t B, int64_t H, int64_t T, int64_t d, int64_t dh, int64_t chunk);

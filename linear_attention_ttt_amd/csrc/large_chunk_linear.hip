@@ -20,6 +20,8 @@
 //   3. lact_read_kernel  - O_c = Q_c W_{c-1}, a quarter chunk per workgroup,
 //                          W staged once in LDS as bf16 hi + lo, queries
 //                          streamed per wave through a direct-to-LDS ring
+#include <algorithm>
+
 #include "device_common.h"
 #include "kernels.h"
 
@@ -409,6 +411,281 @@ hipError_t launch_lact(const LargeChunkArgs& a, hipStream_t stream, const Timing
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Backward.  Chunk c forms P_c = W_{c-1} + dW_c and W_c = P_c / n_c per column
+// (n_c = max(||column||, 1e-12)); its queries read R_c = W_{c-1} (W_c when a
+// chunk updates first).  With G the gradient of the newest memory (dW_T at
+// the end), from the last chunk back:
+//   update-first: G += A_c                (A_c = Q_c^T dO_c)
+//   dP_c = (G - w (w . G)) / n_c per column (G / 1e-12 under the floor)
+//   G = dP_c, and read-first: G += A_c
+// and dW0 = G.  Then, for every chunk in parallel,
+//   dQ_c = dO_c R_c^T,  u = K_c dP_c,  dK_c = diag(eta) V_c dP_c^T,
+//   dV_c = diag(eta) u,  deta_t = <u_t, v_t>.
+// The dW_c and A_c come from lact_delta_kernel (A_c with unit rates); the
+// memories R_c from lact_scan_kernel, as in the forward.
+// ---------------------------------------------------------------------------
+
+// One wave per (head, column j), lanes over rows, as lact_scan_kernel.
+// dpt: dP_c transposed ([c][j][i]); dW, dW0 natural [i][j].
+template <int D, bool UF>
+__global__ __launch_bounds__(256) void lact_bwd_scan_kernel(const float* __restrict__ W0, const float* __restrict__ dW,
+                                                            const float* __restrict__ partA,
+                                                            const float* __restrict__ partB,
+                                                            const float* __restrict__ wprev_t, float* __restrict__ dpt,
+                                                            float* __restrict__ dW0, int nchunks, int nsplit) {
+  constexpr int RPL = D / 64;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+  const int j = (blockIdx.x % (D / 4)) * 4 + w;
+  const int bh = blockIdx.x / (D / 4);
+  float G[RPL];
+#pragma unroll
+  for (int r = 0; r < RPL; ++r) G[r] = dW[(size_t)bh * D * D + (size_t)(l + 64 * r) * D + j];
+  for (int c = nchunks - 1; c >= 0; --c) {
+    float dw[RPL], a[RPL], wp[RPL];
+#pragma unroll
+    for (int r = 0; r < RPL; ++r) {
+      dw[r] = 0.f;
+      a[r] = 0.f;
+    }
+    for (int sp = 0; sp < nsplit; ++sp) {
+      const size_t o = ((((size_t)bh * nchunks + c) * nsplit + sp) * D + j) * D;
+#pragma unroll
+      for (int r = 0; r < RPL; ++r) {
+        dw[r] += partA[o + l + 64 * r];
+        a[r] += partB[o + l + 64 * r];
+      }
+    }
+    // W_{c-1}: what chunk c reads when it reads first, else the memory chunk c-1 read (W0 for c = 0)
+    if (!UF || c > 0) {
+      const float* Wt = wprev_t + (((size_t)bh * nchunks + (UF ? c - 1 : c)) * D + j) * D;
+#pragma unroll
+      for (int r = 0; r < RPL; ++r) wp[r] = Wt[l + 64 * r];
+    } else {
+#pragma unroll
+      for (int r = 0; r < RPL; ++r) wp[r] = W0[(size_t)bh * D * D + (size_t)(l + 64 * r) * D + j];
+    }
+    if (UF) {
+#pragma unroll
+      for (int r = 0; r < RPL; ++r) G[r] += a[r];
+    }
+    float p[RPL], ss = 0.f;
+#pragma unroll
+    for (int r = 0; r < RPL; ++r) {
+      p[r] = wp[r] + dw[r];
+      ss = fmaf(p[r], p[r], ss);
+    }
+    const float nrm = sqrtf(wave_sum(ss));
+    const float inv = 1.0f / fmaxf(nrm, 1e-12f);
+    float wg = 0.f;
+#pragma unroll
+    for (int r = 0; r < RPL; ++r) wg = fmaf(p[r] * inv, G[r], wg);
+    const float proj = nrm > 1e-12f ? wave_sum(wg) : 0.f;   // the floor's branch is linear: no projection
+    float* out = dpt + (((size_t)bh * nchunks + c) * D + j) * D;
+#pragma unroll
+    for (int r = 0; r < RPL; ++r) {
+      G[r] = (G[r] - p[r] * inv * proj) * inv;
+      out[l + 64 * r] = G[r];
+      if (!UF) G[r] += a[r];
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < RPL; ++r) dW0[(size_t)bh * D * D + (size_t)(l + 64 * r) * D + j] = G[r];
+}
+
+// Per (head, chunk, part of the chunk): dQ = dO R^T, u = K dP, w = V dP^T for
+// the part's tokens, then dV = eta u, dK = eta w, deta = <u, v>, all float32.
+// The matrices are staged once in LDS as the MFMA A operands M^T (rows =
+// output column) in bf16 hi + lo; each wave takes 16-token blocks and reads
+// its B operands (token rows) straight from HBM.  WHICH selects the products
+// (1: dQ, 2: u and w, 3: all): at d = 128 the three matrices do not fit in
+// LDS together, so dQ runs as a launch of its own.
+template <int D, int WHICH>
+struct LactBwdCfg {
+  static constexpr int ROWB = 2 * D + 16;             // padded LDS row of M^T (bytes)
+  static constexpr int PLANE = D * ROWB;
+  static constexpr int NPL = 2;                       // hi, lo
+  static constexpr int MAT = NPL * PLANE;
+  static constexpr int OFF_U = (WHICH & 1) ? MAT : 0;  // dP^T and dP after R when both are staged
+  static constexpr int LDS = ((WHICH & 1) ? MAT : 0) + ((WHICH & 2) ? 2 * MAT : 0);
+  static_assert(LDS <= 160 * 1024, "LDS budget");
+};
+
+template <int D, int WHICH>
+__global__ __launch_bounds__(256) void lact_bwd_prod_kernel(const bf16* __restrict__ K, const bf16* __restrict__ V,
+                                                            const bf16* __restrict__ dO, const float* __restrict__ eta,
+                                                            const float* __restrict__ wprev_t,
+                                                            const float* __restrict__ dpt, float* __restrict__ dQ,
+                                                            float* __restrict__ dK, float* __restrict__ dV,
+                                                            float* __restrict__ deta, int T, int chunk, int nchunks,
+                                                            int parts, int part_len) {
+  using Cfg = LactBwdCfg<D, WHICH>;
+  constexpr bool DQ = WHICH & 1, UW = WHICH & 2;
+  constexpr int MT = D / 16, KP = D / 32;
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  const int bh = blockIdx.x / (nchunks * parts);
+  const int c = (blockIdx.x / parts) % nchunks, pi = blockIdx.x % parts;
+  const long long cs = (long long)c * chunk, ce = min(cs + chunk, (long long)T);
+  const long long t0 = cs + (long long)pi * part_len;
+  const long long t1 = min(t0 + part_len, ce);
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g = l >> 4, li = l & 15;
+
+  // stage M^T of the three products: R_c (dQ), dP_c^T (u) and dP_c (w); source layouts are transposed
+  // ([j][i] = M[i][j]), so M^T[n][k] is src[k][n] for R and dP, src[n][k] for dP^T
+  const float* Rt = wprev_t + ((size_t)bh * nchunks + c) * D * D;
+  const float* Pt = dpt + ((size_t)bh * nchunks + c) * D * D;
+  auto stage = [&](int off, float v, int n, int k) {
+    const bf16 h = (bf16)v;
+    unsigned char* row = smem + off + n * Cfg::ROWB + 2 * k;
+    *(bf16*)row = h;
+    *(bf16*)(row + Cfg::PLANE) = (bf16)(v - (float)h);
+  };
+  for (int idx = tid; idx < D * D; idx += 256) {
+    const int n = idx / D, k = idx % D;
+    if constexpr (DQ) stage(0, Rt[(size_t)k * D + n], n, k);
+    if constexpr (UW) {
+      stage(Cfg::OFF_U, Pt[(size_t)n * D + k], n, k);
+      stage(Cfg::OFF_U + Cfg::MAT, Pt[(size_t)k * D + n], n, k);
+    }
+  }
+  __syncthreads();
+  if (t1 <= t0) return;
+
+  const long long ntok = t1 - t0;
+  const size_t base = (size_t)bh * T + t0;
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(K + base * D, ntok * D * 2);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(V + base * D, ntok * D * 2);
+  const __amdgpu_buffer_rsrc_t rdo = make_rsrc(dO + base * D, ntok * D * 2);
+  const __amdgpu_buffer_rsrc_t re = make_rsrc(eta + base, ntok * 4);
+  const __amdgpu_buffer_rsrc_t rq32 = make_rsrc(dQ + base * D, ntok * D * 4);
+  const __amdgpu_buffer_rsrc_t rk32 = make_rsrc(dK + base * D, ntok * D * 4);
+  const __amdgpu_buffer_rsrc_t rv32 = make_rsrc(dV + base * D, ntok * D * 4);
+  const __amdgpu_buffer_rsrc_t rde = make_rsrc(deta + base, ntok * 4);
+  const int nblk = (int)((ntok + 15) / 16);
+  for (int b = w; b < nblk; b += 4) {
+    const unsigned trow = (unsigned)(16 * b + li);         // this lane's token (B operand column, output row)
+    bf16x8 xd[KP], xk[KP], xv[KP];
+#pragma unroll
+    for (int p = 0; p < KP; ++p) {
+      const unsigned o = trow * (D * 2) + (unsigned)(32 * p + 8 * g) * 2;
+      if constexpr (DQ) xd[p] = __builtin_bit_cast(bf16x8, buf_load16(rdo, o));
+      if constexpr (UW) {
+        xk[p] = __builtin_bit_cast(bf16x8, buf_load16(rk, o));
+        xv[p] = __builtin_bit_cast(bf16x8, buf_load16(rv, o));
+      }
+    }
+    const float e = UW ? __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(re, trow * 4, 0, 0)) : 0.f;
+    float dot = 0.f;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      floatx4 aq = {0.f, 0.f, 0.f, 0.f}, au = aq, aw = aq;
+#pragma unroll
+      for (int p = 0; p < KP; ++p) {
+        const int ao = (16 * mt + li) * Cfg::ROWB + (32 * p + 8 * g) * 2;
+#pragma unroll
+        for (int pl = 0; pl < Cfg::NPL; ++pl) {
+          if constexpr (DQ) aq = mfma16(*(const bf16x8*)(smem + pl * Cfg::PLANE + ao), xd[p], aq);
+          if constexpr (UW) {
+            const unsigned char* b0 = smem + Cfg::OFF_U + pl * Cfg::PLANE + ao;
+            au = mfma16(*(const bf16x8*)(b0), xk[p], au);
+            aw = mfma16(*(const bf16x8*)(b0 + Cfg::MAT), xv[p], aw);
+          }
+        }
+      }
+      // lane (g, li) holds columns 16mt + 4g .. +3 of token 16b + li
+      const unsigned col = (unsigned)(16 * mt + 4 * g);
+      const unsigned o32 = trow * (D * 4) + col * 4;
+      if constexpr (DQ) buf_store16(rq32, o32, __builtin_bit_cast(u32x4, aq));
+      if constexpr (UW) {
+        buf_store16(rv32, o32, __builtin_bit_cast(u32x4, e * au));
+        buf_store16(rk32, o32, __builtin_bit_cast(u32x4, e * aw));
+        const uint2v vv = __builtin_amdgcn_raw_buffer_load_b64(rv, trow * (D * 2) + col * 2, 0, 0);
+        dot = fmaf(au[0], bf16lo_f(vv[0]), dot);
+        dot = fmaf(au[1], bf16hi_f(vv[0]), dot);
+        dot = fmaf(au[2], bf16lo_f(vv[1]), dot);
+        dot = fmaf(au[3], bf16hi_f(vv[1]), dot);
+      }
+    }
+    if constexpr (UW) {
+      dot += __shfl_xor(dot, 16);
+      dot += __shfl_xor(dot, 32);
+      if (g == 0) __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, dot), rde, trow * 4, 0, 0);
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void lact_fill_ones_kernel(float* __restrict__ p, long long n) {
+  for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < n; i += (long long)gridDim.x * 256) p[i] = 1.0f;
+}
+
+struct LactBwdLayout {
+  size_t partA, partB, wprev, dpt, ones, junk, total;
+};
+inline size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
+inline LactBwdLayout lact_bwd_layout(int64_t BH, int64_t T, int64_t D, int64_t chunk) {
+  const int64_t nchunks = (T + chunk - 1) / chunk;
+  const size_t mat = (size_t)D * D * 4, nsplit = (size_t)nsplit_of(BH, nchunks, chunk);
+  LactBwdLayout L;
+  size_t o = 0;
+  L.partA = o; o += al256(BH * nchunks * nsplit * mat);
+  L.partB = o; o += al256(BH * nchunks * nsplit * mat);
+  L.wprev = o; o += al256(BH * nchunks * mat);
+  L.dpt = o; o += al256(BH * nchunks * mat);
+  L.ones = o; o += al256((size_t)BH * T * 4);
+  L.junk = o; o += al256(BH * mat);
+  L.total = o;
+  return L;
+}
+
+template <int D>
+hipError_t launch_lact_bwd(const BackwardArgs& a, hipStream_t stream) {
+  const int T = (int)a.T, chunk = (int)a.chunk, BH = (int)(a.B * a.H);
+  const int nchunks = (int)((a.T + a.chunk - 1) / a.chunk);
+  const int nsplit = (int)nsplit_of(BH, nchunks, a.chunk);
+  const int slice = (int)slice_of(BH, nchunks, a.chunk);
+  const LactBwdLayout L = lact_bwd_layout(BH, a.T, D, a.chunk);
+  char* ws = (char*)a.ws;
+  float *partA = (float*)(ws + L.partA), *partB = (float*)(ws + L.partB), *wprev = (float*)(ws + L.wprev);
+  float *dpt = (float*)(ws + L.dpt), *ones = (float*)(ws + L.ones), *junk = (float*)(ws + L.junk);
+  const bool uf = a.other_order != 0;
+  hipError_t e;
+  const long long ntok = (long long)BH * T;
+  if (nchunks > 0) {
+    hipLaunchKernelGGL(lact_fill_ones_kernel, dim3((unsigned)std::min<long long>((ntok + 255) / 256, 2048)), dim3(256),
+                       0, stream, ones, ntok);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(lact_delta_kernel<D>, dim3(BH * nchunks * nsplit), dim3(256), 0, stream, (const bf16*)a.K,
+                       (const bf16*)a.V, a.eta, partA, T, chunk, nchunks, nsplit, slice);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(lact_delta_kernel<D>, dim3(BH * nchunks * nsplit), dim3(256), 0, stream, (const bf16*)a.Q,
+                       (const bf16*)a.dO, (const float*)ones, partB, T, chunk, nchunks, nsplit, slice);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  auto kscan = uf ? lact_scan_kernel<D, true> : lact_scan_kernel<D, false>;
+  hipLaunchKernelGGL(kscan, dim3(BH * D / 4), dim3(256), 0, stream, a.W0, partA, wprev, junk, nchunks, nsplit);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  auto kb = uf ? lact_bwd_scan_kernel<D, true> : lact_bwd_scan_kernel<D, false>;
+  hipLaunchKernelGGL(kb, dim3(BH * D / 4), dim3(256), 0, stream, a.W0, a.dW, partA, partB, wprev, dpt, a.dW0, nchunks,
+                     nsplit);
+  if ((e = hipGetLastError()) != hipSuccess || nchunks == 0) return e;
+  int part_len = (chunk + 3) / 4;
+  part_len = part_len < 256 ? 256 : part_len;
+  part_len = (part_len + 63) / 64 * 64;
+  part_len = part_len > (1 << 20) ? (1 << 20) : part_len;   // float32 rows of a part stay below 2^31 bytes
+  const int parts = (chunk + part_len - 1) / part_len;
+  auto prod = [&](auto kern, int lds) -> hipError_t {
+    hipError_t err = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL(kern, dim3(BH * nchunks * parts), dim3(256), lds, stream, (const bf16*)a.K, (const bf16*)a.V,
+                       (const bf16*)a.dO, a.eta, wprev, dpt, (float*)a.dQ, (float*)a.dK, (float*)a.dV, a.deta, T,
+                       chunk, nchunks, parts, part_len);
+    return hipGetLastError();
+  };
+  if constexpr (D == 64) return prod(lact_bwd_prod_kernel<D, 3>, LactBwdCfg<D, 3>::LDS);
+  if ((e = prod(lact_bwd_prod_kernel<D, 1>, LactBwdCfg<D, 1>::LDS)) != hipSuccess) return e;
+  return prod(lact_bwd_prod_kernel<D, 2>, LactBwdCfg<D, 2>::LDS);
+}
+
 }  // namespace
 
 bool large_chunk_linear_supported(int64_t dk, int64_t dv, int64_t chunk, int dtype) {
@@ -424,6 +701,14 @@ size_t large_chunk_linear_workspace(int64_t B, int64_t H, int64_t T, int64_t dk,
 hipError_t launch_large_chunk_linear(const LargeChunkArgs& a, hipStream_t stream, const Timing& tm) {
   if (a.DK == 64) return launch_lact<64>(a, stream, tm);
   return launch_lact<128>(a, stream, tm);
+}
+
+size_t large_chunk_linear_backward_workspace(int64_t B, int64_t H, int64_t T, int64_t d, int64_t chunk) {
+  return lact_bwd_layout(B * H, T, d, chunk).total;
+}
+
+hipError_t launch_large_chunk_linear_backward(const BackwardArgs& a, hipStream_t stream) {
+  return a.DK == 64 ? launch_lact_bwd<64>(a, stream) : launch_lact_bwd<128>(a, stream);
 }
 
 }  // namespace ttt

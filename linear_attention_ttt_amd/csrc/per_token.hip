@@ -1056,7 +1056,7 @@ __global__ __launch_bounds__(256) void pt_bwd_rate_grad_kernel(float* __restrict
 }
 
 template <int D>
-static hipError_t launch_bwd(const PerTokenBwdArgs& a, hipStream_t stream) {
+static hipError_t launch_bwd(const BackwardArgs& a, hipStream_t stream) {
   const int BH = (int)(a.B * a.H);
   const long long ntok = (long long)BH * a.T;
   const BwdLayout L = bwd_layout(a.B, a.H, a.T, D);
@@ -1072,7 +1072,7 @@ static hipError_t launch_bwd(const PerTokenBwdArgs& a, hipStream_t stream) {
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const SegPlan sp = per_token_seg_plan(BH, a.T, D, BWD_MAX_SEG_TOKENS);
   const int T = (int)a.T;
-  const bool excl = a.exclusive != 0;
+  const bool excl = a.other_order != 0;
   const Timing none;
   // (SegArgs.O is typed bf16; the OF32 passes write floats through it)
   const SegArgs Aq{dO, V, K, a.eta, w0t, slots, (bf16*)a.dQ, junk, T, sp.nseg, sp.seg_len};
@@ -1095,7 +1095,7 @@ bool per_token_backward_supported(int64_t dk, int64_t dv, int64_t chunk, int dty
   return dtype == 1 && per_token_supported(dk, dv, chunk, dtype);
 }
 
-hipError_t launch_per_token_backward(const PerTokenBwdArgs& a, hipStream_t stream) {
+hipError_t launch_per_token_backward(const BackwardArgs& a, hipStream_t stream) {
   return a.DK == 128 ? launch_bwd<128>(a, stream) : launch_bwd<64>(a, stream);
 }
 

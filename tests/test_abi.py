@@ -191,7 +191,10 @@ def bcall(desc=None, mode=0, chunk=64, ws_bytes=1 << 34, **kw):
 @pytest.mark.parametrize("kw,code", [
     (dict(Q=None), 1), (dict(dO=None), 1), (dict(dW=None), 1), (dict(dQ=None), 1), (dict(deta=None), 1),
     (dict(dW0=None), 1), (dict(ws=None), 1), (dict(W0=None), 1),
-    (dict(mode=1), 6), (dict(mode=2), 2), (dict(mode=4), 6), (dict(mode=6), 5), (dict(chunk=0), 3),
+    (dict(mode=2), 2), (dict(mode=6), 5), (dict(chunk=0), 3),
+    (dict(mode=2, desc=la.make_desc(1, 2, 128, 128, 128, 256, la.BF16)), 6),    # no SwiGLU backward
+    (dict(mode=5, desc=la.make_desc(1, 2, 128, 128, 128, 256, la.BF16)), 6),
+    (dict(mode=1, desc=la.make_desc(1, 2, 128, 64, 64, 0, la.FP32)), 6),
     (dict(desc=la.make_desc(1, 2, 128, 64, 64, 0, la.FP32)), 6),       # bf16 only
     (dict(desc=la.make_desc(1, 2, 128, 96, 96, 0, la.BF16)), 6),
     (dict(chunk=256), 6),
@@ -211,7 +214,15 @@ def test_backward_workspace():
     n = la.workspace_bytes(d, 64, "per_token_linear") + 3 * st
     assert la.backward_workspace_bytes(d, 64, "per_token_linear") == n
     assert la.backward_workspace_bytes(d, 64, "per_token_linear_exclusive") == n
-    assert la.backward_workspace_bytes(d, 64, "large_chunk_linear") == 0
+    # large-chunk linear: two sets of chunk updates (K^T diag(eta) V and Q^T dO), the memories and the
+    # normalisation gradients of every chunk, unit rates, a discarded final memory
+    dl = la.make_desc(1, 12, 196608, 64, 64, 0, la.BF16)
+    m, nc = 64 * 64 * 4, 48
+    nsplit = la.workspace_bytes(dl, 4096, "large_chunk_linear") // (12 * nc * m) - 1
+    assert la.backward_workspace_bytes(dl, 4096, "large_chunk_linear") == \
+        12 * nc * m * (2 * nsplit + 2) + 12 * 196608 * 4 + 12 * m
+    assert la.backward_workspace_bytes(dl, 4096, "large_chunk_linear_update_first") == \
+        la.backward_workspace_bytes(dl, 4096, "large_chunk_linear")
     assert la.backward_workspace_bytes(la.make_desc(1, 1, 64, 64, 64, 0, la.FP32), 64, 0) == 0
     assert bcall(desc=d, ws_bytes=n - 1) == 8
     # a backward segment holds at most 2^21 tokens (float32 rows addressed below 2^31 bytes)
