@@ -189,7 +189,7 @@ def run_workload(name: str, steps: int, warmup: int, flush_mb: int, other_order:
 
 
 def run_backward(name: str, steps: int, warmup: int, flush_mb: int, mode: str):
-    """Time ttt_la_backward (per-token modes) on a workload's inputs and
+    """Time ttt_la_backward (per-token and large-chunk linear modes) on a workload's inputs and
     seeded upstream gradients, each call bracketed by events with the caches
     flushed in between, as for the forward.  Algorithmic bytes: read Q, K,
     V, dO (bf16), eta, W0, dW; write dQ, dK, dV (fp32), deta, dW0."""
@@ -245,7 +245,7 @@ def run_backward(name: str, steps: int, warmup: int, flush_mb: int, mode: str):
     rec = dict(workload=name, mode=s["mode"], ms_per_step=float(ms.mean()), ms_min=float(ms.min()),
                tokens_per_s=B * T / mean_s, algorithmic_bytes=nbytes, hbm_GBps=nbytes / mean_s / 1e9,
                hbm_frac=nbytes / mean_s / 1e9 / HBM_PEAK_GBS,
-               note="four passes of the segmented recurrence plus the rate-gradient reduction; float32 gradients")
+               note="float32 gradients")
     del t, dO, dW, ws, outs, deta, dW0, flush, flush_rd
     torch.cuda.empty_cache()
     return rec
@@ -346,12 +346,20 @@ def main():
                 others[name] = run_workload(name, max(10, a.steps // 2), 3, a.flush_mb, a.other_order)
             except Exception as e:  # a mode not built yet is reported, not fatal
                 others[name] = {"error": str(e)[:200]}
-    backward = None
-    if not a.no_backward and method_of(head["mode"]) == "per_token_linear" and head["dtype"] == "bf16":
-        try:
-            backward = run_backward(a.workload, max(10, a.steps // 2), 3, a.flush_mb, head["mode"])
-        except Exception as e:  # reported, not fatal
-            backward = {"error": str(e)[:200]}
+    # backward records: the headline workload, and (with the other workloads) every workload whose mode
+    # has a backward (bf16 per-token and large-chunk linear)
+    backward = {}
+    if not a.no_backward:
+        names = [a.workload] + ([] if a.no_others else [n for n in workloads.WORKLOADS if n != a.workload])
+        for name in names:
+            sw = workloads.spec(name)
+            mode = OTHER_ORDER[sw["mode"]] if a.other_order else sw["mode"]
+            if sw["dtype"] != "bf16" or method_of(mode) not in ("per_token_linear", "large_chunk_linear"):
+                continue
+            try:
+                backward[name] = run_backward(name, max(10, a.steps // 2), 3, a.flush_mb, mode)
+            except Exception as e:  # reported, not fatal
+                backward[name] = {"error": str(e)[:200]}
     s = workloads.spec(a.workload, mode=head["mode"])
     k = head["kernel"]
     peak = HBM_PEAK_GBS if k["bound"] == "hbm" else BF16_PEAK_TFLOPS
