@@ -225,8 +225,9 @@ int ttt_la_event_destroy(void* event);
  *                  bytes of device scratch (contents on entry do not matter)
  *   stream         hipStream_t (NULL = the default stream)
  *
- * Supported set: bf16; per-token d_k = d_v in {64, 128}, chunk in
- * {16, 32, 64, 128}; large-chunk linear d_k = d_v in {64, 128}, any chunk.
+ * Supported set: per-token as ttt_la_forward (bf16 or fp32, d_k = d_v in
+ * {64, 128}); large-chunk linear bf16, d_k = d_v in {64, 128}, any chunk.
+ * dO has io_dtype.
  * Every pointer is required (ERR_NULL), except that the per-token arrays
  * may be NULL when T = 0 (then dW0 = dW_out); no output may overlap an input,
  * another output or the workspace (ERR_ALIAS).  Checks, ownership and

@@ -236,7 +236,7 @@ def backward(Q, K, V, eta, W0, dO, dW_out, chunk: int, mode="per_token_linear", 
     """Gradients of the per-token forward: given the inputs of ``forward``,
     ``dO`` (gradient of O, like V) and ``dW_out`` (gradient of the final
     memory, float32 like W0), return ``(dQ, dK, dV, deta, dW0)``, all
-    float32.  bfloat16 inputs only; argument checks as in ``forward``."""
+    float32.  Argument checks as in ``forward``."""
     import torch
 
     m = _mode(mode)
@@ -249,8 +249,9 @@ def backward(Q, K, V, eta, W0, dO, dW_out, chunk: int, mode="per_token_linear", 
             raise ValueError(f"{name} must be on the same CUDA device as Q")
         if not t.is_contiguous():
             raise ValueError(f"{name} must be contiguous")
-    if Q.dtype != torch.bfloat16 or K.dtype != Q.dtype or V.dtype != Q.dtype or dO.dtype != Q.dtype:
-        raise ValueError("Q, K, V, dO must be bfloat16")
+    if Q.dtype not in (torch.bfloat16, torch.float32) or K.dtype != Q.dtype or V.dtype != Q.dtype or \
+            dO.dtype != Q.dtype:
+        raise ValueError("Q, K, V, dO must share dtype bfloat16 or float32")
     if eta.dtype != torch.float32 or W0.dtype != torch.float32 or dW_out.dtype != torch.float32:
         raise ValueError("eta, W0 and dW_out must be float32")
     if Q.dim() != 4 or K.shape != Q.shape or V.dim() != 4 or V.shape[:3] != Q.shape[:3] or dO.shape != V.shape:
@@ -259,7 +260,7 @@ def backward(Q, K, V, eta, W0, dO, dW_out, chunk: int, mode="per_token_linear", 
     dv = V.shape[3]
     if tuple(eta.shape) != (B, H, T) or tuple(W0.shape) != (B, H, dk, dv) or dW_out.shape != W0.shape:
         raise ValueError("eta must be [B,H,T], W0 and dW_out [B,H,d_k,d_v]")
-    desc = make_desc(B, H, T, dk, dv, 0, BF16)
+    desc = make_desc(B, H, T, dk, dv, 0, BF16 if Q.dtype == torch.bfloat16 else FP32)
     f32 = dict(dtype=torch.float32, device=dev)
     dQ, dK, dV = torch.empty(Q.shape, **f32), torch.empty(K.shape, **f32), torch.empty(V.shape, **f32)
     deta, dW0 = torch.empty_like(eta), torch.empty_like(W0)

@@ -184,10 +184,10 @@ int ttt_la_forward(const void* Q, const void* K, const void* V, const float* eta
 }
 
 static bool backward_ok(const ttt_la_desc& d, int64_t chunk, int32_t mode) {
-  if (!supported(d, chunk, mode) || d.io_dtype != TTT_LA_BF16) return false;
+  if (!supported(d, chunk, mode)) return false;
   switch (method_of(mode)) {
     case TTT_LA_PER_TOKEN_LINEAR: return ttt::per_token_backward_supported(d.d_k, d.d_v, chunk, d.io_dtype);
-    case TTT_LA_LARGE_CHUNK_LINEAR: return true;
+    case TTT_LA_LARGE_CHUNK_LINEAR: return d.io_dtype == TTT_LA_BF16;
   }
   return false;
 }
@@ -215,7 +215,7 @@ int ttt_la_backward(const void* Q, const void* K, const void* V, const float* et
   const size_t need = backward_workspace(d, chunk, mode);
   if (workspace_bytes < need) return TTT_LA_ERR_WORKSPACE;
 
-  const size_t es = 2;
+  const size_t es = d.io_dtype == TTT_LA_BF16 ? 2 : 4;
   const size_t ntok = (size_t)(d.B * d.H * d.T);
   const size_t st_bytes = (size_t)state_elems(d, TTT_LA_PER_TOKEN_LINEAR) * 4;
   const Range ins[7] = {range(Q, ntok * d.d_k * es), range(K, ntok * d.d_k * es), range(V, ntok * d.d_v * es),

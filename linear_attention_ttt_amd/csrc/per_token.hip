@@ -736,7 +736,10 @@ struct Fp32Cfg {
   static_assert(C % 16 == 0 && DK % 32 == 0, "tile shape");
 };
 
-template <int DK, int C, bool EXCL>
+// REV and EM as for the bf16 output pass: REV walks the head's sequence in
+// reverse (chunk row r of chunk c is original token T - 1 - (cC + r)); EM
+// places the rates on the keys (0), on the outputs (1) or nowhere (2).
+template <int DK, int C, bool EXCL, bool REV = false, int EM = 0>
 __global__ __launch_bounds__(256) void per_token_fp32_kernel(
     const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
     const float* __restrict__ eta, const float* __restrict__ W0, float* __restrict__ O,
@@ -767,6 +770,8 @@ __global__ __launch_bounds__(256) void per_token_fp32_kernel(
   const int bi = tid / 16, bj = tid % 16;
   const int cg = tid % 8, r8 = tid / 8;
   const int nchunks = (T + C - 1) / C;
+  // original token of position t of the walk
+  auto tok = [&](int t) -> size_t { return REV ? (size_t)(T - 1 - t) : (size_t)t; };
   for (int c = 0; c < nchunks; ++c) {
     const int t0 = c * C;
     __syncthreads();
@@ -774,15 +779,15 @@ __global__ __launch_bounds__(256) void per_token_fp32_kernel(
       const int r = i / (DK / 4), a4 = i % (DK / 4);
       const bool ok = t0 + r < T;
       const floatx4 z = {0.f, 0.f, 0.f, 0.f};
-      *(floatx4*)(q + r * QP + 4 * a4) = ok ? *(const floatx4*)(Qh + (size_t)(t0 + r) * DK + 4 * a4) : z;
-      *(floatx4*)(k + r * QP + 4 * a4) = ok ? *(const floatx4*)(Kh + (size_t)(t0 + r) * DK + 4 * a4) : z;
+      *(floatx4*)(q + r * QP + 4 * a4) = ok ? *(const floatx4*)(Qh + tok(t0 + r) * DK + 4 * a4) : z;
+      *(floatx4*)(k + r * QP + 4 * a4) = ok ? *(const floatx4*)(Kh + tok(t0 + r) * DK + 4 * a4) : z;
     }
     for (int i = tid; i < C * TV / 4; i += 256) {
       const int r = i / (TV / 4), n4 = i % (TV / 4);
       const floatx4 z = {0.f, 0.f, 0.f, 0.f};
-      *(floatx4*)(v + r * TV + 4 * n4) = (t0 + r < T) ? *(const floatx4*)(Vh + (size_t)(t0 + r) * DV + tv0 + 4 * n4) : z;
+      *(floatx4*)(v + r * TV + 4 * n4) = (t0 + r < T) ? *(const floatx4*)(Vh + tok(t0 + r) * DV + tv0 + 4 * n4) : z;
     }
-    for (int i = tid; i < C; i += 256) e[i] = (t0 + i < T) ? Eh[t0 + i] : 0.f;
+    for (int i = tid; i < C; i += 256) e[i] = (t0 + i < T) ? Eh[tok(t0 + i)] : 0.f;
     __syncthreads();
     // scores with the causal mask (diagonal included) and eta of the key token: SB x SB block per thread
     if (bj <= bi) {
@@ -810,7 +815,7 @@ __global__ __launch_bounds__(256) void per_token_fp32_kernel(
 #pragma unroll
         for (int cc = 0; cc < SB; ++cc) {
           const int i = SB * bi + r, j = SB * bj + cc;
-          p[i * PP + j] = (EXCL ? j < i : j <= i) ? acc[r][cc] * e[j] : 0.f;
+          p[i * PP + j] = (EXCL ? j < i : j <= i) ? (EM == 0 ? acc[r][cc] * e[j] : acc[r][cc]) : 0.f;
         }
     } else {
 #pragma unroll
@@ -832,7 +837,8 @@ __global__ __launch_bounds__(256) void per_token_fp32_kernel(
 #pragma unroll
         for (int x = 0; x < 4; ++x) acc2 += qa[x] * *(const floatx4*)(s + (a + x) * TV + 4 * cg);
       }
-      if (t0 + i < T) *(floatx4*)(Oh + (size_t)(t0 + i) * DV + tv0 + 4 * cg) = acc + acc2;
+      if (t0 + i < T)
+        *(floatx4*)(Oh + tok(t0 + i) * DV + tv0 + 4 * cg) = EM == 1 ? e[i] * (acc + acc2) : acc + acc2;
     }
     __syncthreads();
     // state: rows r8 + 32m of s, columns 4cg..4cg+3, over the chunk's keys
@@ -843,7 +849,7 @@ __global__ __launch_bounds__(256) void per_token_fp32_kernel(
       for (int m = 0; m < RS; ++m) acc[m] = *(const floatx4*)(s + (r8 + 32 * m) * TV + 4 * cg);
 #pragma unroll 4
       for (int j = 0; j < C; ++j) {
-        const floatx4 ev = e[j] * *(const floatx4*)(v + j * TV + 4 * cg);
+        const floatx4 ev = (EM == 0 ? e[j] : 1.f) * *(const floatx4*)(v + j * TV + 4 * cg);
 #pragma unroll
         for (int m = 0; m < RS; ++m) acc[m] += k[j * QP + r8 + 32 * m] * ev;
       }
@@ -1021,11 +1027,20 @@ __global__ __launch_bounds__(256) void pt_transpose2_kernel(const float* __restr
   for (int y = y0; y < 64; y += 4) dst[(size_t)(64 * tc + y) * D + 64 * tr + x] = tile[x][y];
 }
 
-// In place: u -> dV = eta u, and deta = <u, v> per token (u fp32, V bf16).
-// A token's row is covered by D/8 consecutive lanes, 8 values each; the
-// products are summed over those lanes.
-template <int D>
-__global__ __launch_bounds__(256) void pt_bwd_rate_grad_kernel(float* __restrict__ u, const bf16* __restrict__ V,
+// In place: u -> dV = eta u, and deta = <u, v> per token (u fp32, V bf16 or
+// fp32).  A token's row is covered by D/8 consecutive lanes, 8 values each;
+// the products are summed over those lanes.
+__device__ __forceinline__ void v8_of(const bf16* p, floatx4& a, floatx4& b) {
+  const u32x4 vv = *(const u32x4*)p;
+  a = floatx4{bf16lo_f(vv[0]), bf16hi_f(vv[0]), bf16lo_f(vv[1]), bf16hi_f(vv[1])};
+  b = floatx4{bf16lo_f(vv[2]), bf16hi_f(vv[2]), bf16lo_f(vv[3]), bf16hi_f(vv[3])};
+}
+__device__ __forceinline__ void v8_of(const float* p, floatx4& a, floatx4& b) {
+  a = *(const floatx4*)p;
+  b = *(const floatx4*)(p + 4);
+}
+template <int D, typename VT>
+__global__ __launch_bounds__(256) void pt_bwd_rate_grad_kernel(float* __restrict__ u, const VT* __restrict__ V,
                                                                const float* __restrict__ eta, float* __restrict__ deta,
                                                                long long ntok) {
   constexpr int LPT = D / 8;          // lanes per token
@@ -1034,21 +1049,16 @@ __global__ __launch_bounds__(256) void pt_bwd_rate_grad_kernel(float* __restrict
   for (long long t = (long long)blockIdx.x * TPB + threadIdx.x / LPT; t < ntok; t += (long long)gridDim.x * TPB) {
     const size_t o = (size_t)t * D + sub * 8;
     const floatx4 u0 = *(const floatx4*)(u + o), u1 = *(const floatx4*)(u + o + 4);
-    const u32x4 vv = *(const u32x4*)(V + o);
+    floatx4 v0, v1;
+    v8_of(V + o, v0, v1);
     const float e = eta[t];
     *(floatx4*)(u + o) = e * u0;
     *(floatx4*)(u + o + 4) = e * u1;
     float dot = 0.f;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      dot = fmaf(u0[2 * j], bf16lo_f(vv[j]), dot);
-      dot = fmaf(u0[2 * j + 1], bf16hi_f(vv[j]), dot);
-    }
+    for (int j = 0; j < 4; ++j) dot = fmaf(u0[j], v0[j], dot);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      dot = fmaf(u1[2 * j], bf16lo_f(vv[2 + j]), dot);
-      dot = fmaf(u1[2 * j + 1], bf16hi_f(vv[2 + j]), dot);
-    }
+    for (int j = 0; j < 4; ++j) dot = fmaf(u1[j], v1[j], dot);
 #pragma unroll
     for (int m = LPT / 2; m >= 1; m >>= 1) dot += __shfl_xor(dot, m);   // within the token's lanes
     if (sub == 0) deta[t] = dot;
@@ -1084,18 +1094,70 @@ static hipError_t launch_bwd(const BackwardArgs& a, hipStream_t stream) {
   if (ntok > 0) {
     constexpr int TPB = 256 / (D / 8);
     const unsigned grid = (unsigned)std::min<long long>((ntok + TPB - 1) / TPB, 8192);
-    hipLaunchKernelGGL(pt_bwd_rate_grad_kernel<D>, dim3(grid), dim3(256), 0, stream, (float*)a.dV, V, a.eta, a.deta,
-                       ntok);
+    hipLaunchKernelGGL((pt_bwd_rate_grad_kernel<D, bf16>), dim3(grid), dim3(256), 0, stream, (float*)a.dV, V, a.eta,
+                       a.deta, ntok);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+// float32 inputs: the same three passes with the float32 kernel (tiles of `chunk` tokens, one
+// workgroup per head and 32 columns, sequential over the head's tiles)
+template <int DK, int C>
+static hipError_t launch_bwd_fp32(const BackwardArgs& a, hipStream_t stream) {
+  const int BH = (int)(a.B * a.H), T = (int)a.T, DV = (int)a.DV;
+  const long long ntok = (long long)BH * a.T;
+  const BwdLayout L = bwd_layout(a.B, a.H, a.T, DK);
+  char* ws = (char*)a.ws;
+  float* w0t = (float*)(ws + L.w0t);
+  float* dwt = (float*)(ws + L.dwt);
+  float* junk = (float*)(ws + L.junk);
+  const float *Q = (const float*)a.Q, *K = (const float*)a.K, *V = (const float*)a.V, *dO = (const float*)a.dO;
+  const bool excl = a.other_order != 0;
+  hipError_t e;
+  hipLaunchKernelGGL(pt_transpose2_kernel<DK>, dim3(BH * 2 * (DK / 64) * (DK / 64)), dim3(256), 0, stream, a.W0, a.dW,
+                     w0t, dwt);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const size_t lds = fp32_lds_bytes<DK, C>();
+  auto pass = [&](auto kern, const float* q, const float* k, const float* v, const float* w0, float* o,
+                  float* wout) -> hipError_t {
+    hipError_t err = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL(kern, dim3(BH * (DV / 32)), dim3(256), lds, stream, q, k, v, a.eta, w0, o, wout, T, DV);
+    return hipGetLastError();
+  };
+  if ((e = pass(excl ? per_token_fp32_kernel<DK, C, true, false, 0> : per_token_fp32_kernel<DK, C, false, false, 0>,
+                dO, V, K, w0t, (float*)a.dQ, junk)) != hipSuccess)
+    return e;
+  if ((e = pass(excl ? per_token_fp32_kernel<DK, C, true, true, 2> : per_token_fp32_kernel<DK, C, false, true, 2>, K,
+                Q, dO, a.dW, (float*)a.dV, a.dW0)) != hipSuccess)
+    return e;
+  if ((e = pass(excl ? per_token_fp32_kernel<DK, C, true, true, 1> : per_token_fp32_kernel<DK, C, false, true, 1>, V,
+                dO, Q, dwt, (float*)a.dK, junk)) != hipSuccess)
+    return e;
+  if (ntok > 0) {
+    constexpr int TPB = 256 / (DK / 8);
+    const unsigned grid = (unsigned)std::min<long long>((ntok + TPB - 1) / TPB, 8192);
+    hipLaunchKernelGGL((pt_bwd_rate_grad_kernel<DK, float>), dim3(grid), dim3(256), 0, stream, (float*)a.dV, V, a.eta,
+                       a.deta, ntok);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   return hipSuccess;
 }
 
 bool per_token_backward_supported(int64_t dk, int64_t dv, int64_t chunk, int dtype) {
-  return dtype == 1 && per_token_supported(dk, dv, chunk, dtype);
+  return per_token_supported(dk, dv, chunk, dtype);
 }
 
 hipError_t launch_per_token_backward(const BackwardArgs& a, hipStream_t stream) {
+  if (a.dtype == 0) {
+    const int c = a.chunk <= 16 ? 16 : a.chunk <= 32 ? 32 : 64;
+    if (a.DK == 64)
+      return c == 16 ? launch_bwd_fp32<64, 16>(a, stream) : c == 32 ? launch_bwd_fp32<64, 32>(a, stream)
+                                                             : launch_bwd_fp32<64, 64>(a, stream);
+    return c == 16 ? launch_bwd_fp32<128, 16>(a, stream) : c == 32 ? launch_bwd_fp32<128, 32>(a, stream)
+                                                          : launch_bwd_fp32<128, 64>(a, stream);
+  }
   return a.DK == 128 ? launch_bwd<128>(a, stream) : launch_bwd<64>(a, stream);
 }
 

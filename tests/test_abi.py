@@ -195,7 +195,6 @@ def bcall(desc=None, mode=0, chunk=64, ws_bytes=1 << 34, **kw):
     (dict(mode=2, desc=la.make_desc(1, 2, 128, 128, 128, 256, la.BF16)), 6),    # no SwiGLU backward
     (dict(mode=5, desc=la.make_desc(1, 2, 128, 128, 128, 256, la.BF16)), 6),
     (dict(mode=1, desc=la.make_desc(1, 2, 128, 64, 64, 0, la.FP32)), 6),
-    (dict(desc=la.make_desc(1, 2, 128, 64, 64, 0, la.FP32)), 6),       # bf16 only
     (dict(desc=la.make_desc(1, 2, 128, 96, 96, 0, la.BF16)), 6),
     (dict(chunk=256), 6),
     (dict(ws_bytes=0), 8),
@@ -223,7 +222,8 @@ def test_backward_workspace():
         12 * nc * m * (2 * nsplit + 2) + 12 * 196608 * 4 + 12 * m
     assert la.backward_workspace_bytes(dl, 4096, "large_chunk_linear_update_first") == \
         la.backward_workspace_bytes(dl, 4096, "large_chunk_linear")
-    assert la.backward_workspace_bytes(la.make_desc(1, 1, 64, 64, 64, 0, la.FP32), 64, 0) == 0
+    # float32 per-token: the transposed states and the discarded memory (one segment, no slots)
+    assert la.backward_workspace_bytes(la.make_desc(1, 1, 64, 64, 64, 0, la.FP32), 64, 0) == 3 * 64 * 64 * 4
     assert bcall(desc=d, ws_bytes=n - 1) == 8
     # a backward segment holds at most 2^21 tokens (float32 rows addressed below 2^31 bytes)
     d1 = la.make_desc(256, 1, 1 << 22, 128, 128, 0, la.BF16)

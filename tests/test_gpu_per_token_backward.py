@@ -16,8 +16,8 @@ def run_backward(t, g, s):
     return out
 
 
-def grads_to_device(gr, dev="cuda"):
-    return dict(dO=torch.from_numpy(gr["dO"]).to(dev).to(torch.bfloat16), dW=torch.from_numpy(gr["dW"]).to(dev))
+def grads_to_device(gr, dev="cuda", dtype=torch.bfloat16):
+    return dict(dO=torch.from_numpy(gr["dO"]).to(dev).to(dtype), dW=torch.from_numpy(gr["dW"]).to(dev))
 
 
 def check_backward(s, x, gr, out, heads=None, label=""):
@@ -28,10 +28,11 @@ def check_backward(s, x, gr, out, heads=None, label=""):
         return a.reshape((B * H,) + a.shape[2:])[heads][None]
     ref = oracle.backward(sel(x["Q"]), sel(x["K"]), sel(x["V"]), sel(x["eta"]), sel(x["W0"]), sel(gr["dO"]),
                           sel(gr["dW"]), s["chunk"], s["mode"])
-    errs = {n: err(gpu_heads(o, heads), r, "bf16") for n, o, r in zip(NAMES, out, ref)}
-    print(f"[{s['mode']} backward {label}] " + " ".join(f"{n}={e:.3e}" for n, e in errs.items()), flush=True)
+    dt = s["dtype"]
+    errs = {n: err(gpu_heads(o, heads), r, dt) for n, o, r in zip(NAMES, out, ref)}
+    print(f"[{s['mode']} backward {label} {dt}] " + " ".join(f"{n}={e:.3e}" for n, e in errs.items()), flush=True)
     for n, e in errs.items():
-        assert e <= tol("bf16"), f"{n} error {e} > {tol('bf16')}"
+        assert e <= tol(dt), f"{n} error {e} > {tol(dt)}"
 
 
 @pytest.mark.parametrize("mode", ["per_token_linear", "per_token_linear_exclusive"])
@@ -89,3 +90,26 @@ def test_per_token_backward_workload_B4H16T4096_sampled_heads():
     gr = workloads.generate_grads(s, seed=0)
     out = run_backward(to_device(x, s), grads_to_device(gr), s)
     check_backward(s, x, gr, out, heads=[0, 21, 63], label="B4H16T4096 heads 0,21,63")
+
+
+@pytest.mark.parametrize("mode", ["per_token_linear", "per_token_linear_exclusive"])
+@pytest.mark.parametrize("B,H,T,d,chunk", [
+    (1, 1, 256, 64, 64),
+    (2, 2, 203, 128, 32),      # ragged tail
+    (1, 2, 90, 64, 16),
+    (1, 1, 1, 64, 64),         # single token
+])
+def test_per_token_backward_fp32(mode, B, H, T, d, chunk):
+    s = workloads.make_spec(mode, B, H, T, d, chunk=chunk, dtype="fp32", eta="sigmoid")
+    x = workloads.generate(s, seed=14)
+    gr = workloads.generate_grads(s, seed=14)
+    out = run_backward(to_device(x, s), grads_to_device(gr, dtype=torch.float32), s)
+    check_backward(s, x, gr, out, label=f"{B},{H},{T},{d},c{chunk}")
+
+
+def test_per_token_backward_workload_fp32_full():
+    s = workloads.spec("per_token_fp32_B1H1T256_d64_c64")
+    x = workloads.generate(s, seed=0)
+    gr = workloads.generate_grads(s, seed=0)
+    out = run_backward(to_device(x, s), grads_to_device(gr, dtype=torch.float32), s)
+    check_backward(s, x, gr, out, label="fp32 B1H1T256")
