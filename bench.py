@@ -58,12 +58,14 @@ def algorithmic(s: dict) -> tuple[int, float]:
     es = 2 if s["dtype"] == "bf16" else 4
     n = B * H * T
     m = method_of(s["mode"])
-    state = B * H * (3 * dk * dh if m == "large_chunk_swiglu" else dk * dv) * 4
+    state = B * H * (3 * dk * dh if m.startswith("large_chunk_swiglu") else dk * dv) * 4
     nbytes = n * (2 * dk + 2 * dv) * es + n * 4 + 2 * state
     if m == "per_token_linear":
         flops = n * (4 * dk * dv + (C + 1) * (dk + dv))
     elif m == "large_chunk_linear":
         flops = n * 4 * dk * dv + B * H * (-(-T // C)) * 3 * dk * dv
+    elif m == "large_chunk_swiglu_last_layer":
+        flops = n * 12 * dk * dh       # Q read 6, K features 4, W2 gradient 2
     else:
         flops = n * 18 * dk * dh
     return nbytes, float(flops)
@@ -88,16 +90,20 @@ def dominant_kernel(s: dict) -> tuple[str, float, str]:
                 float(algorithmic(s)[0]), "hbm")
     if m == "large_chunk_linear":
         return "lact_delta_kernel (chunk update)", float(n * ((dk + dv) * es + 4)), "hbm"
+    if m == "large_chunk_swiglu_last_layer":
+        return "swiglu_recur_kernel (recurrence)", float(n * 6 * dk * dh), "mfma"
     return "swiglu_recur_kernel (recurrence)", float(n * 12 * dk * dh), "mfma"
 
 
-def run_workload(name: str, steps: int, warmup: int, flush_mb: int, other_order: bool = False):
+def run_workload(name: str, steps: int, warmup: int, flush_mb: int, other_order: bool = False, mode=None):
     import torch
     import linear_attention_ttt_amd as la
 
     s = workloads.spec(name)
     if other_order:
         s["mode"] = OTHER_ORDER[s["mode"]]
+    if mode:
+        s["mode"] = mode
     x = workloads.generate(s, seed=0)
     dev = torch.device("cuda:0")
     dt = torch.bfloat16 if s["dtype"] == "bf16" else torch.float32
@@ -313,7 +319,10 @@ def main():
     ap.add_argument("--no-others", action="store_true", help="skip the other workloads' sub-records")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--flush-mb", type=int, default=512)
-    ap.add_argument("--no-backward", action="store_true", help="skip the per-token backward sub-record")
+    ap.add_argument("--no-backward", action="store_true", help="skip the backward sub-records")
+    ap.add_argument("--mode", default=None,
+                    help="run the workload in this mode instead of its own (same shapes; e.g. "
+                         "large_chunk_swiglu_last_layer on the SwiGLU workload); implies --no-others")
     ap.add_argument("--other-order", action="store_true",
                     help="run every workload in its method's other read order (exclusive per-token read, "
                          "update-then-read chunks)")
@@ -336,7 +345,9 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    head = run_workload(a.workload, a.steps, a.warmup, a.flush_mb, a.other_order)
+    if a.mode:
+        a.no_others = True
+    head = run_workload(a.workload, a.steps, a.warmup, a.flush_mb, a.other_order, a.mode)
     others = {}
     if not a.no_others:
         for name in workloads.WORKLOADS:
@@ -353,7 +364,7 @@ def main():
         names = [a.workload] + ([] if a.no_others else [n for n in workloads.WORKLOADS if n != a.workload])
         for name in names:
             sw = workloads.spec(name)
-            mode = OTHER_ORDER[sw["mode"]] if a.other_order else sw["mode"]
+            mode = a.mode or (OTHER_ORDER[sw["mode"]] if a.other_order else sw["mode"])
             if sw["dtype"] != "bf16" or method_of(mode) not in ("per_token_linear", "large_chunk_linear"):
                 continue
             try:
@@ -364,7 +375,7 @@ def main():
     k = head["kernel"]
     peak = HBM_PEAK_GBS if k["bound"] == "hbm" else BF16_PEAK_TFLOPS
     roof = {"bound": k["bound"], "achieved": k["achieved"], "peak": peak, "unit": k["unit"],
-            "frac": k["achieved"] / peak, "traffic": None if a.other_order else traffic_per_launch(k["name"]),
+            "frac": k["achieved"] / peak, "traffic": None if (a.other_order or a.mode) else traffic_per_launch(k["name"]),
             "kernel": k["name"], "kernel_ms": k["ms_mean"], "units_per_launch": k["units_per_launch"],
             "step_frac": head["hbm_frac"] if k["bound"] == "hbm" else head["bf16_mfma_frac"]}
     line = {

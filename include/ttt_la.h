@@ -39,6 +39,15 @@
  *     read order of the LaCT review's read-order section, applied chunk by
  *     chunk).  W_out is the same as in the read-first mode.
  *
+ *   TTT_LA_LARGE_CHUNK_SWIGLU_LAST_LAYER: the SwiGLU memory with only its
+ *     last layer trained and no normalisation (the paper summary's ablation
+ *     ladder, technical section 4: update only the last layer, then drop the
+ *     weight normalisation).  W1 and W3 stay as given, so with
+ *     phi(x) = silu(x W1) * (x W3) this is block-causal linear attention in
+ *     that feature space: O_c = phi(Q_c) W2; W2 <- W2 + phi(K_c)^T diag(eta_c) V_c.
+ *     Same shapes, support and workspace as TTT_LA_LARGE_CHUNK_SWIGLU;
+ *     W_out holds W1 and W3 unchanged and the final W2.
+ *
  * Conventions: row vectors, W stored [d_in, d_out] row-major; every tensor
  * contiguous with the last dimension fastest.
  *
@@ -80,7 +89,8 @@ enum {
     TTT_LA_LARGE_CHUNK_SWIGLU = 2,
     TTT_LA_PER_TOKEN_LINEAR_EXCLUSIVE = 3,
     TTT_LA_LARGE_CHUNK_LINEAR_UPDATE_FIRST = 4,
-    TTT_LA_LARGE_CHUNK_SWIGLU_UPDATE_FIRST = 5
+    TTT_LA_LARGE_CHUNK_SWIGLU_UPDATE_FIRST = 5,
+    TTT_LA_LARGE_CHUNK_SWIGLU_LAST_LAYER = 6
 };
 
 /* Element type of Q, K, V and O.  eta and the fast-weight state are always
@@ -111,7 +121,7 @@ typedef struct ttt_la_desc {
  *   chunk  tokens per chunk (>= 1)
  *   mode   TTT_LA_PER_TOKEN_LINEAR | TTT_LA_LARGE_CHUNK_LINEAR | TTT_LA_LARGE_CHUNK_SWIGLU,
  *          or an ordering variant (3 | 4 | 5: same shapes, support and workspace as
- *          modes 0 | 1 | 2)
+ *          modes 0 | 1 | 2), or TTT_LA_LARGE_CHUNK_SWIGLU_LAST_LAYER (6, as mode 2)
  *   desc   sizes and io_dtype (host pointer)
  *   O      [B,H,T,d_v]  io_dtype, device (written)
  *   W_out  same layout as W0, float32, device (written); W_out == W0 (in
@@ -254,7 +264,7 @@ const char* ttt_la_status_string(int status);
 /* ABI version of this header (incremented on incompatible change). */
 int ttt_la_abi_version(void);
 
-#define TTT_LA_ABI_VERSION 3
+#define TTT_LA_ABI_VERSION 4
 
 #ifdef __cplusplus
 }

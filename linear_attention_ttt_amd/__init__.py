@@ -19,7 +19,7 @@ import os
 
 __all__ = ["forward", "backward", "backward_raw", "backward_workspace_bytes", "forward_timed_raw", "TimingEvent", "workspace_bytes", "TTTLAError", "MODES", "Desc", "lib", "library_path",
            "PER_TOKEN_LINEAR", "LARGE_CHUNK_LINEAR", "LARGE_CHUNK_SWIGLU", "PER_TOKEN_LINEAR_EXCLUSIVE",
-           "LARGE_CHUNK_LINEAR_UPDATE_FIRST", "LARGE_CHUNK_SWIGLU_UPDATE_FIRST"]
+           "LARGE_CHUNK_LINEAR_UPDATE_FIRST", "LARGE_CHUNK_SWIGLU_UPDATE_FIRST", "LARGE_CHUNK_SWIGLU_LAST_LAYER"]
 
 PER_TOKEN_LINEAR = 0
 LARGE_CHUNK_LINEAR = 1
@@ -27,10 +27,12 @@ LARGE_CHUNK_SWIGLU = 2
 PER_TOKEN_LINEAR_EXCLUSIVE = 3
 LARGE_CHUNK_LINEAR_UPDATE_FIRST = 4
 LARGE_CHUNK_SWIGLU_UPDATE_FIRST = 5
+LARGE_CHUNK_SWIGLU_LAST_LAYER = 6
 MODES = {"per_token_linear": PER_TOKEN_LINEAR, "large_chunk_linear": LARGE_CHUNK_LINEAR,
          "large_chunk_swiglu": LARGE_CHUNK_SWIGLU, "per_token_linear_exclusive": PER_TOKEN_LINEAR_EXCLUSIVE,
          "large_chunk_linear_update_first": LARGE_CHUNK_LINEAR_UPDATE_FIRST,
-         "large_chunk_swiglu_update_first": LARGE_CHUNK_SWIGLU_UPDATE_FIRST}
+         "large_chunk_swiglu_update_first": LARGE_CHUNK_SWIGLU_UPDATE_FIRST,
+         "large_chunk_swiglu_last_layer": LARGE_CHUNK_SWIGLU_LAST_LAYER}
 FP32, BF16 = 0, 1
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -196,7 +198,7 @@ def forward(Q, K, V, eta, W0, chunk: int, mode, *, out=None, W_out=None, workspa
     if tuple(eta.shape) != (B, H, T):
         raise ValueError("eta must be [B,H,T]")
     dh = 0
-    if m in (LARGE_CHUNK_SWIGLU, LARGE_CHUNK_SWIGLU_UPDATE_FIRST):
+    if m in (LARGE_CHUNK_SWIGLU, LARGE_CHUNK_SWIGLU_UPDATE_FIRST, LARGE_CHUNK_SWIGLU_LAST_LAYER):
         if W0.dim() != 3 or tuple(W0.shape[:2]) != (B, H) or W0.shape[2] % (3 * dk) != 0:
             raise ValueError("SwiGLU W0 must be [B,H,3*d*d_h]")
         dh = W0.shape[2] // (3 * dk)

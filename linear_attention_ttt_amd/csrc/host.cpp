@@ -39,7 +39,8 @@ int32_t method_of(int32_t mode) {
     case TTT_LA_LARGE_CHUNK_LINEAR:
     case TTT_LA_LARGE_CHUNK_LINEAR_UPDATE_FIRST: return TTT_LA_LARGE_CHUNK_LINEAR;
     case TTT_LA_LARGE_CHUNK_SWIGLU:
-    case TTT_LA_LARGE_CHUNK_SWIGLU_UPDATE_FIRST: return TTT_LA_LARGE_CHUNK_SWIGLU;
+    case TTT_LA_LARGE_CHUNK_SWIGLU_UPDATE_FIRST:
+    case TTT_LA_LARGE_CHUNK_SWIGLU_LAST_LAYER: return TTT_LA_LARGE_CHUNK_SWIGLU;
   }
   return -1;
 }
@@ -169,7 +170,7 @@ int ttt_la_forward_timed(const void* Q, const void* K, const void* V, const floa
     e = ttt::launch_per_token(a, s, tm);
   } else {
     ttt::LargeChunkArgs a{Q, K, V, eta, W0, O, W_out, workspace, d.B, d.H, d.T, d.d_k, d.d_v, d.d_h, chunk, d.io_dtype,
-                          other};
+                          other, mode == TTT_LA_LARGE_CHUNK_SWIGLU_LAST_LAYER ? 1 : 0};
     e = method == TTT_LA_LARGE_CHUNK_LINEAR ? ttt::launch_large_chunk_linear(a, s, tm)
                                             : ttt::launch_large_chunk_swiglu(a, s, tm);
   }

@@ -74,6 +74,7 @@ struct LargeChunkArgs {
   int64_t B, H, T, DK, DV, DH, chunk;
   int dtype;
   int update_first;  // 1: a chunk takes its step, then its queries read the result
+  int last_layer_only = 0;  // SwiGLU: only W2 is updated, and nothing is normalised
 };
 
 bool large_chunk_linear_supported(int64_t dk, int64_t dv, int64_t chunk, int dtype);

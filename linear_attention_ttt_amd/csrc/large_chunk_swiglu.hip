@@ -101,7 +101,7 @@ __global__ __launch_bounds__(SW_WAVES * 64, 1) void swiglu_recur_kernel(
     const bf16* __restrict__ K, const bf16* __restrict__ V, const float* __restrict__ eta,
     const float* __restrict__ W0, float* __restrict__ Wout, bf16* __restrict__ states, float* __restrict__ ss2,
     unsigned* __restrict__ counters, unsigned* __restrict__ errflag, int T, int chunk, int nchunks, int head0,
-    int update_first) {
+    int update_first, int last_only) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
   RecurLds& S = *reinterpret_cast<RecurLds*>(smem_raw);
   constexpr int NT = SW_WAVES * 64;
@@ -303,8 +303,10 @@ __global__ __launch_bounds__(SW_WAVES * 64, 1) void swiglu_recur_kernel(
       for (int m = 0; m < 8; ++m) {
         const bf16x8 kt = join(ktr[m][0], ktr[m][1]);
         const bf16x8 vt = join(vtr[m][0], vtr[m][1]);
-        dW1[m] = mfma16(kt, daop, dW1[m]);
-        dW3[m] = mfma16(kt, dbop, dW3[m]);
+        if (!last_only) {
+          dW1[m] = mfma16(kt, daop, dW1[m]);
+          dW3[m] = mfma16(kt, dbop, dW3[m]);
+        }
         dW2[m] = mfma16(ehop, vt, dW2[m]);
       }
     }
@@ -330,15 +332,20 @@ __global__ __launch_bounds__(SW_WAVES * 64, 1) void swiglu_recur_kernel(
 #pragma unroll
         for (int mm = 0; mm < 2; ++mm) {
           const int f = (((2 * q + mm) * 4 + g) * 16 + li) * 4;
-          *(floatx4*)(S.w1 + f) = o1[mm] + dW1[2 * q + mm];
-          *(floatx4*)(S.w3 + f) = o3[mm] + dW3[2 * q + mm];
+          if (!last_only) {
+            *(floatx4*)(S.w1 + f) = o1[mm] + dW1[2 * q + mm];
+            *(floatx4*)(S.w3 + f) = o3[mm] + dW3[2 * q + mm];
+          }
           *(floatx4*)(S.w2 + f) = o2[mm] + dW2[2 * q + mm];
         }
       }
       __syncthreads();
     }
-    // W1, W3: unit columns over d, local (waves 0 and 1)
-    if (w < 2) {
+    // W1, W3: unit columns over d, local (waves 0 and 1).  With only the last layer updated there is
+    // no normalisation (every slice of a head takes the same branch, so none waits on the exchange).
+    if (last_only) {
+      // nothing: W1 and W3 stay as they are, W2 is not normalised
+    } else if (w < 2) {
       float* Wm = w == 0 ? S.w1 : S.w3;
       const int u = l & 15, r0 = (l >> 4) * 32;
       // rows r0 .. r0+31 of unit u as 8 groups of 4 consecutive rows (16 bytes each in this layout)
@@ -374,7 +381,7 @@ __global__ __launch_bounds__(SW_WAVES * 64, 1) void swiglu_recur_kernel(
       wait_vm<0>();
     }
     __syncthreads();
-    if (tid == 0) {
+    if (tid == 0 && !last_only) {
       __hip_atomic_fetch_add(&counters[bh], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       const unsigned target = (unsigned)SW_NSL * (unsigned)(c + 1);
       int spins = 0;
@@ -387,7 +394,7 @@ __global__ __launch_bounds__(SW_WAVES * 64, 1) void swiglu_recur_kernel(
       }
     }
     __syncthreads();
-    if (w >= 2 && w < 4) {
+    if (!last_only && w >= 2 && w < 4) {
       const int d = (w - 2) * 64 + l;
       float ss = 0.f;
       for (int s = 0; s < SW_NSL; ++s)
@@ -648,9 +655,10 @@ hipError_t launch_large_chunk_swiglu(const LargeChunkArgs& a, hipStream_t stream
   if ((e = mark(tm.start, stream)) != hipSuccess) return e;   // the recurrence: the sequential part
   for (int h0 = 0; h0 < BH; h0 += heads_per_launch) {
     const int nh = std::min(heads_per_launch, BH - h0);
-    int Ti = T, ci = chunk, nci = nchunks, hi = h0, uf = a.update_first ? 1 : 0;
+    int Ti = T, ci = chunk, nci = nchunks, hi = h0, uf = a.update_first ? 1 : 0, lo = a.last_layer_only ? 1 : 0;
     void* args[] = {(void*)&Kp, (void*)&Vp, (void*)&Ep, (void*)&W0p, (void*)&Wo, (void*)&states, (void*)&ss2,
-                    (void*)&counters, (void*)&err, (void*)&Ti, (void*)&ci, (void*)&nci, (void*)&hi, (void*)&uf};
+                    (void*)&counters, (void*)&err, (void*)&Ti, (void*)&ci, (void*)&nci, (void*)&hi, (void*)&uf,
+                    (void*)&lo};
     e = hipLaunchCooperativeKernel((const void*)swiglu_recur_kernel, dim3(nh * SW_NSL), dim3(SW_WAVES * 64), args,
                                    (unsigned)lds_r, stream);
     if (e != hipSuccess) return e;

@@ -308,8 +308,10 @@ def large_chunk_swiglu(Q, K, V, eta, W1, W3, W2, chunk, normalize=True,
     LaCT review, non-linear memory and read-order sections.
     ``read_first=False``: the chunk's queries read the weights after its
     update (the gradient is still taken at the weights before it).
-    ``normalize=False`` and ``update_w1w3=False`` are oracle-only switches
-    used by the pins.  Returns (O, (W1, W3, W2))."""
+    ``normalize=False`` with ``update_w1w3=False`` is the last-layer-only
+    variant of the paper summary's ablation ladder (technical section 4:
+    train only the last layer, then drop the weight normalisation).
+    Returns (O, (W1, W3, W2))."""
     Q, K, V, eta, W1, W3, W2 = map(_f64, (Q, K, V, eta, W1, W3, W2))
     W1, W3, W2 = W1.copy(), W3.copy(), W2.copy()
     T = Q.shape[2]
@@ -361,7 +363,8 @@ def forward(Q, K, V, eta, W0, chunk, mode, d_h=None):
     "large_chunk_swiglu", and the ordering variants
     "per_token_linear_exclusive" (a query reads before its token's update),
     "large_chunk_linear_update_first" and "large_chunk_swiglu_update_first"
-    (a chunk updates, then reads).  For per-token mode ``chunk`` does not
+    (a chunk updates, then reads), and "large_chunk_swiglu_last_layer"
+    (only W2 trained, no normalisation).  For per-token mode ``chunk`` does not
     change the result and is ignored.  For SwiGLU, W0 is the packed state and
     ``d_h`` is required.  Returns (O, W_final) with W_final in W0's layout."""
     if mode in ("per_token_linear", "per_token_linear_exclusive"):
@@ -373,5 +376,10 @@ def forward(Q, K, V, eta, W0, chunk, mode, d_h=None):
         W1, W3, W2 = swiglu_unpack(_f64(W0), d, d_h)
         O, (W1, W3, W2) = large_chunk_swiglu(Q, K, V, eta, W1, W3, W2, chunk,
                                              read_first=(mode == "large_chunk_swiglu"))
+        return O, swiglu_pack(W1, W3, W2)
+    if mode == "large_chunk_swiglu_last_layer":
+        d = Q.shape[-1]
+        W1, W3, W2 = swiglu_unpack(_f64(W0), d, d_h)
+        O, (W1, W3, W2) = large_chunk_swiglu(Q, K, V, eta, W1, W3, W2, chunk, normalize=False, update_w1w3=False)
         return O, swiglu_pack(W1, W3, W2)
     raise ValueError(f"unknown mode {mode!r}")

@@ -46,7 +46,7 @@ def test_exports_every_declared_symbol():
 
 @needs_lib
 def test_version_and_status_strings():
-    assert la.lib().ttt_la_abi_version() == 3
+    assert la.lib().ttt_la_abi_version() == 4
     for s in range(10):
         assert la.status_string(s) and la.status_string(s) != "unknown status"
     assert la.status_string(99) == "unknown status"
@@ -57,7 +57,7 @@ def test_version_and_status_strings():
     (dict(Q=None), 1), (dict(K=None), 1), (dict(V=None), 1), (dict(eta=None), 1), (dict(O=None), 1),
     (dict(W0=None), 1), (dict(W_out=None), 1),
     (dict(chunk=0), 3), (dict(chunk=-5), 3),
-    (dict(mode=6), 5), (dict(mode=-1), 5),
+    (dict(mode=7), 5), (dict(mode=-1), 5),
 ])
 def test_invalid_arguments(kw, code):
     assert call(**kw) == code
@@ -142,6 +142,10 @@ def test_ordering_variants_share_support_and_workspace():
     assert la.MODES["per_token_linear_exclusive"] == 3
     assert la.MODES["large_chunk_linear_update_first"] == 4
     assert la.MODES["large_chunk_swiglu_update_first"] == 5
+    assert la.MODES["large_chunk_swiglu_last_layer"] == 6
+    d6 = la.make_desc(2, 8, 32768, 128, 128, 256, la.BF16)
+    assert la.workspace_bytes(d6, 2048, 6) == la.workspace_bytes(d6, 2048, 2)
+    assert call(desc=la.make_desc(1, 1, 8, 128, 128, 0), mode=6) == 2      # needs d_h
     assert call(desc=la.make_desc(1, 1, 8, 96, 96), mode=3) == 6
 
 
@@ -191,7 +195,7 @@ def bcall(desc=None, mode=0, chunk=64, ws_bytes=1 << 34, **kw):
 @pytest.mark.parametrize("kw,code", [
     (dict(Q=None), 1), (dict(dO=None), 1), (dict(dW=None), 1), (dict(dQ=None), 1), (dict(deta=None), 1),
     (dict(dW0=None), 1), (dict(ws=None), 1), (dict(W0=None), 1),
-    (dict(mode=2), 2), (dict(mode=6), 5), (dict(chunk=0), 3),
+    (dict(mode=2), 2), (dict(mode=7), 5), (dict(chunk=0), 3),
     (dict(mode=2, desc=la.make_desc(1, 2, 128, 128, 128, 256, la.BF16)), 6),    # no SwiGLU backward
     (dict(mode=5, desc=la.make_desc(1, 2, 128, 128, 128, 256, la.BF16)), 6),
     (dict(mode=1, desc=la.make_desc(1, 2, 128, 64, 64, 0, la.FP32)), 6),

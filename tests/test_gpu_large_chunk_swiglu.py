@@ -85,3 +85,27 @@ def test_large_chunk_swiglu_update_first_workload_sampled_heads():
     x = workloads.generate(s, seed=0)
     O, W = run(to_device(x, s), s)
     check(s, x, O, W, heads=[4, 15], label="B2H8T32768 heads 4,15")
+
+
+@pytest.mark.parametrize("B,H,T,chunk", [
+    (1, 1, 300, 128),      # ragged last chunk
+    (2, 1, 700, 2048),     # a single chunk
+    (1, 1, 200, 37),
+    (1, 2, 1024, 256),
+    (1, 1, 40, 1),         # one token per chunk
+])
+def test_large_chunk_swiglu_last_layer_small(B, H, T, chunk):
+    s = workloads.make_spec("large_chunk_swiglu_last_layer", B, H, T, 128, d_h=256, chunk=chunk, dtype="bf16",
+                            eta_scale=0.02)
+    x = workloads.generate(s, seed=10)
+    O, W = run(to_device(x, s), s)
+    check(s, x, O, W, label=f"{B},{H},{T},c{chunk}")
+    n13 = 2 * 128 * 256                 # W1 and W3 are not trained: bit for bit the initial ones
+    assert torch.equal(W[..., :n13].cpu(), torch.from_numpy(x["W0"][..., :n13]))
+
+
+def test_large_chunk_swiglu_last_layer_workload_sampled_heads():
+    s = workloads.spec("large_chunk_swiglu_bf16_B2H8T32768_d128_dh256_c2048", mode="large_chunk_swiglu_last_layer")
+    x = workloads.generate(s, seed=0)
+    O, W = run(to_device(x, s), s)
+    check(s, x, O, W, heads=[1, 14], label="B2H8T32768 heads 1,14")

@@ -562,3 +562,14 @@ def test_mutants_swiglu_grad_are_caught(mutant):
 
 def test_mutant_linear_grad_is_caught():
     assert not check_linear_grad(grad_fn=_linear_grad_missing_eta)
+
+
+def test_last_layer_mode_dispatch_is_the_feature_space_form():
+    # the product mode's name dispatches to the pinned last-layer-only, unnormalised function
+    Q, K, V, eta, W1, W3, W2 = rand_swiglu(seed=19)
+    d, dh = W1.shape[-2], W1.shape[-1]
+    O, Wp = TO.forward(Q, K, V, eta, TO.swiglu_pack(W1, W3, W2), 3, "large_chunk_swiglu_last_layer", d_h=dh)
+    O2, (W1b, W3b, W2b) = TO.large_chunk_swiglu(Q, K, V, eta, W1, W3, W2, 3, normalize=False, update_w1w3=False)
+    assert np.array_equal(O, O2)
+    assert np.array_equal(Wp, TO.swiglu_pack(W1, W3, W2b))
+    assert np.array_equal(W1b, W1) and np.array_equal(W3b, W3)

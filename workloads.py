@@ -24,7 +24,9 @@ import numpy as np
 
 MODES = ("per_token_linear", "large_chunk_linear", "large_chunk_swiglu",
          # the other read orders: a query before its token's step; a chunk's step before its reads
-         "per_token_linear_exclusive", "large_chunk_linear_update_first", "large_chunk_swiglu_update_first")
+         "per_token_linear_exclusive", "large_chunk_linear_update_first", "large_chunk_swiglu_update_first",
+         # SwiGLU with only W2 trained and no normalisation
+         "large_chunk_swiglu_last_layer")
 
 # Named workloads.  Shapes follow the configurations the method is measured
 # on; T is the sequence length, d the head width, d_h the SwiGLU hidden width.
