@@ -109,3 +109,19 @@ def test_large_chunk_swiglu_last_layer_workload_sampled_heads():
     x = workloads.generate(s, seed=0)
     O, W = run(to_device(x, s), s)
     check(s, x, O, W, heads=[1, 14], label="B2H8T32768 heads 1,14")
+
+
+def test_large_chunk_swiglu_last_layer_both_paths_agree():
+    # one head (the parallel form: too few heads to fill the chip) against the same head inside a
+    # 16-head batch (the recurrence): both against the oracle, and their final W2 to fp32 rounding
+    s = workloads.make_spec("large_chunk_swiglu_last_layer", 1, 16, 1000, 128, d_h=256, chunk=128, dtype="bf16",
+                            eta_scale=0.02)
+    x = workloads.generate(s, seed=11)
+    t = to_device(x, s)
+    O16, W16 = run(t, s)
+    one = {k: v[:, 5:6].contiguous() for k, v in t.items()}
+    O1, W1 = run(one, dict(s, H=1))
+    check(dict(s, H=1), {k: v[:, 5:6] for k, v in x.items() if k in ("Q", "K", "V", "eta", "W0")}, O1, W1,
+          label="one head, parallel form")
+    check(s, x, O16, W16, heads=[5], label="head 5 of 16, recurrence")
+    assert err(W1.cpu().numpy(), W16[:, 5:6].cpu().numpy(), "bf16") <= 1e-5
