@@ -198,6 +198,7 @@ struct SegArgs {
   bf16* O;
   float* Wout;
   int T, nseg, seg_len;             // segment s covers tokens [s*seg_len, (s+1)*seg_len), whole tiles of both passes
+  int start_transposed = 0;         // 1: segment s > 0 starts from the transpose of the state in slot s
 };
 
 // The program of wave W (wave-uniform).  One program for all waves keeps the
@@ -343,7 +344,19 @@ __device__ __forceinline__ void seg_wave(const SegArgs& A, unsigned char* smem, 
   floatx4 S[MT];
   const floatx4* pp = A.part + ((size_t)bh * nseg * NW + W) * MT * 64 + l;   // slot 0 of this head
   constexpr int SLOT = NW * MT * 64;                                         // floatx4 per slot
-  if (s > 0) {
+  if (s > 0 && A.start_transposed) {
+    // the transpose of the slot's state: element (row x, column y) of the slot sits in wave y/16,
+    // lane 16g + y%16 and row tile m, register r of seg_srow(m, g, r) = x
+    const float* ps = (const float*)(A.part + ((size_t)bh * nseg + s) * SLOT);
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int y = seg_srow(m, g, r), x = 16 * W + li;
+        const int mx = 2 * (x >> 5) + ((x >> 2) & 1), gx = (x >> 3) & 3, rx = x & 3;
+        S[m][r] = ps[((size_t)((y >> 4) * MT + mx) * 64 + 16 * gx + (y & 15)) * 4 + rx];
+      }
+  } else if (s > 0) {
     // start state of this segment, prepared by pt_seg_scan_kernel in the same fragment layout
 #pragma unroll
     for (int m = 0; m < MT; ++m) S[m] = pp[(size_t)s * SLOT + m * 64];
@@ -918,13 +931,14 @@ size_t per_token_workspace(int64_t B, int64_t H, int64_t T, int64_t dk, int64_t 
 // The three kernels of one bf16 pass over every head (forward order, or reversed with REV).
 template <int D, bool REV, int EM, bool OF32 = false>
 static hipError_t launch_seg_pass(const SegArgs& A, int BH, bool excl, hipStream_t stream, const Timing& tm) {
+  // (start_transposed: the slots already hold the transposed start states; no increments, no scan)
   using CfgD = IncrCfg<D>;
   using CfgF = SegCfg<D, seg_tile<D>()>;
   // The scan kernel turns the increments into start states, so each output workgroup loads one
   // slot (measured: cheaper than summing the earlier slots in every workgroup's prologue, the
   // increments are still in the last-level cache when the scan reads them).
   hipError_t e;
-  if (A.nseg > 1) {
+  if (A.nseg > 1 && !A.start_transposed) {
     auto kd = pt_incr_kernel<D, REV, EM != 0>;
     if ((e = hipFuncSetAttribute((const void*)kd, hipFuncAttributeMaxDynamicSharedMemorySize, CfgD::LDS_BYTES)) !=
         hipSuccess)
@@ -1089,7 +1103,8 @@ static hipError_t launch_bwd(const BackwardArgs& a, hipStream_t stream) {
   if ((e = launch_seg_pass<D, false, 0, true>(Aq, BH, excl, stream, none)) != hipSuccess) return e;
   const SegArgs Au{K, Q, dO, a.eta, a.dW, slots, (bf16*)a.dV, a.dW0, T, sp.nseg, sp.seg_len};
   if ((e = launch_seg_pass<D, true, 2, true>(Au, BH, excl, stream, none)) != hipSuccess) return e;
-  const SegArgs Ak{V, dO, Q, a.eta, dwt, slots, (bf16*)a.dK, junk, T, sp.nseg, sp.seg_len};
+  // G^T's recurrence has the transposed increments and start states: it reuses the u pass's slots
+  const SegArgs Ak{V, dO, Q, a.eta, dwt, slots, (bf16*)a.dK, junk, T, sp.nseg, sp.seg_len, 1};
   if ((e = launch_seg_pass<D, true, 1, true>(Ak, BH, excl, stream, none)) != hipSuccess) return e;
   if (ntok > 0) {
     constexpr int TPB = 256 / (D / 8);
