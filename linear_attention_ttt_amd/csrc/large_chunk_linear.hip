@@ -562,19 +562,32 @@ __global__ __launch_bounds__(256) void lact_bwd_prod_kernel(const bf16* __restri
   const __amdgpu_buffer_rsrc_t rv32 = make_rsrc(dV + base * D, ntok * D * 4);
   const __amdgpu_buffer_rsrc_t rde = make_rsrc(deta + base, ntok * 4);
   const int nblk = (int)((ntok + 15) / 16);
-  for (int b = w; b < nblk; b += 4) {
-    const unsigned trow = (unsigned)(16 * b + li);         // this lane's token (B operand column, output row)
+  // several 16-token blocks per wave and step: the loads of all are issued before any is computed
+  struct Ops {
     bf16x8 xd[KP], xk[KP], xv[KP];
+    uint2v vc[MT];
+    float e;
+  };
+  auto load = [&](int b, Ops& x) {
+    const unsigned trow = (unsigned)(16 * b + li);
 #pragma unroll
     for (int p = 0; p < KP; ++p) {
       const unsigned o = trow * (D * 2) + (unsigned)(32 * p + 8 * g) * 2;
-      if constexpr (DQ) xd[p] = __builtin_bit_cast(bf16x8, buf_load16(rdo, o));
+      if constexpr (DQ) x.xd[p] = __builtin_bit_cast(bf16x8, buf_load16(rdo, o));
       if constexpr (UW) {
-        xk[p] = __builtin_bit_cast(bf16x8, buf_load16(rk, o));
-        xv[p] = __builtin_bit_cast(bf16x8, buf_load16(rv, o));
+        x.xk[p] = __builtin_bit_cast(bf16x8, buf_load16(rk, o));
+        x.xv[p] = __builtin_bit_cast(bf16x8, buf_load16(rv, o));
       }
     }
-    const float e = UW ? __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(re, trow * 4, 0, 0)) : 0.f;
+    if constexpr (UW) {
+      x.e = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(re, trow * 4, 0, 0));
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+        x.vc[mt] = __builtin_amdgcn_raw_buffer_load_b64(rv, trow * (D * 2) + (unsigned)(16 * mt + 4 * g) * 2, 0, 0);
+    }
+  };
+  auto compute = [&](int b, const Ops& x) {
+    const unsigned trow = (unsigned)(16 * b + li);
     float dot = 0.f;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
@@ -584,11 +597,11 @@ __global__ __launch_bounds__(256) void lact_bwd_prod_kernel(const bf16* __restri
         const int ao = (16 * mt + li) * Cfg::ROWB + (32 * p + 8 * g) * 2;
 #pragma unroll
         for (int pl = 0; pl < Cfg::NPL; ++pl) {
-          if constexpr (DQ) aq = mfma16(*(const bf16x8*)(smem + pl * Cfg::PLANE + ao), xd[p], aq);
+          if constexpr (DQ) aq = mfma16(*(const bf16x8*)(smem + pl * Cfg::PLANE + ao), x.xd[p], aq);
           if constexpr (UW) {
             const unsigned char* b0 = smem + Cfg::OFF_U + pl * Cfg::PLANE + ao;
-            au = mfma16(*(const bf16x8*)(b0), xk[p], au);
-            aw = mfma16(*(const bf16x8*)(b0 + Cfg::MAT), xv[p], aw);
+            au = mfma16(*(const bf16x8*)(b0), x.xk[p], au);
+            aw = mfma16(*(const bf16x8*)(b0 + Cfg::MAT), x.xv[p], aw);
           }
         }
       }
@@ -597,9 +610,9 @@ __global__ __launch_bounds__(256) void lact_bwd_prod_kernel(const bf16* __restri
       const unsigned o32 = trow * (D * 4) + col * 4;
       if constexpr (DQ) buf_store16(rq32, o32, __builtin_bit_cast(u32x4, aq));
       if constexpr (UW) {
-        buf_store16(rv32, o32, __builtin_bit_cast(u32x4, e * au));
-        buf_store16(rk32, o32, __builtin_bit_cast(u32x4, e * aw));
-        const uint2v vv = __builtin_amdgcn_raw_buffer_load_b64(rv, trow * (D * 2) + col * 2, 0, 0);
+        buf_store16(rv32, o32, __builtin_bit_cast(u32x4, x.e * au));
+        buf_store16(rk32, o32, __builtin_bit_cast(u32x4, x.e * aw));
+        const uint2v vv = x.vc[mt];
         dot = fmaf(au[0], bf16lo_f(vv[0]), dot);
         dot = fmaf(au[1], bf16hi_f(vv[0]), dot);
         dot = fmaf(au[2], bf16lo_f(vv[1]), dot);
@@ -611,6 +624,16 @@ __global__ __launch_bounds__(256) void lact_bwd_prod_kernel(const bf16* __restri
       dot += __shfl_xor(dot, 32);
       if (g == 0) __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, dot), rde, trow * 4, 0, 0);
     }
+  };
+  constexpr int NBW = 2;            // blocks per wave and step (4 measured no faster)
+  for (int b = w; b < nblk; b += 4 * NBW) {
+    Ops x[NBW];
+#pragma unroll
+    for (int k = 0; k < NBW; ++k)
+      if (b + 4 * k < nblk) load(b + 4 * k, x[k]);   // wave-uniform
+#pragma unroll
+    for (int k = 0; k < NBW; ++k)
+      if (b + 4 * k < nblk) compute(b + 4 * k, x[k]);
   }
 }
 
