@@ -268,7 +268,7 @@ def backward(Q, K, V, eta, W0, dO, dW_T, chunk, mode):
     raise ValueError(f"no backward for mode {mode!r}")
 
 
-def large_chunk_linear(Q, K, V, eta, W0, chunk, normalize=True, read_first=True):
+def large_chunk_linear(Q, K, V, eta, W0, chunk, normalize=True, read_first=True, momentum=None, M0=None):
     """LaCT with a linear fast weight.  For each chunk (the last may be
     shorter): every query of the chunk reads W (the state left by earlier
     chunks); then W takes one step on the chunk's summed, eta-weighted
@@ -279,9 +279,14 @@ def large_chunk_linear(Q, K, V, eta, W0, chunk, normalize=True, read_first=True)
     normalisation after the update), read-order section (a chunk reads
     the memory of earlier chunks and only then updates it).
     ``read_first=False``: the chunk's queries read W after its update.
-    ``normalize=False`` is an oracle-only switch used by the pins."""
+    ``normalize=False`` is an oracle-only switch used by the pins.
+    ``momentum=beta`` (LaCT review, non-linear-memory section, which
+    compares momentum in the inner loop): the step applied is a momentum
+    buffer ``M_c = beta M_{c-1} - grad_c`` (``M`` starts at ``M0``, zeros
+    by default), then the normalisation; returns (O, W, M) instead."""
     Q, K, V, eta, W = map(_f64, (Q, K, V, eta, W0))
     W = W.copy()
+    M = np.zeros_like(W) if M0 is None else _f64(M0).copy()
     T = Q.shape[2]
     O = np.zeros(Q.shape[:-1] + (V.shape[-1],))
     for s in range(0, T, chunk):
@@ -289,11 +294,17 @@ def large_chunk_linear(Q, K, V, eta, W0, chunk, normalize=True, read_first=True)
         if read_first:
             O[:, :, s:e, :] = np.matmul(Q[:, :, s:e, :], W)
         g = linear_binding_grad(K[:, :, s:e, :], V[:, :, s:e, :], eta[:, :, s:e])
-        W = W - g
+        if momentum is None:
+            W = W - g
+        else:
+            M = momentum * M - g
+            W = W + M
         if normalize:
             W = normalize_columns(W)
         if not read_first:
             O[:, :, s:e, :] = np.matmul(Q[:, :, s:e, :], W)
+    if momentum is not None:
+        return O, W, M
     return O, W
 
 

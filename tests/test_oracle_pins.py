@@ -573,3 +573,52 @@ def test_last_layer_mode_dispatch_is_the_feature_space_form():
     assert np.array_equal(O, O2)
     assert np.array_equal(Wp, TO.swiglu_pack(W1, W3, W2b))
     assert np.array_equal(W1b, W1) and np.array_equal(W3b, W3)
+
+
+
+# ---------------------------------------------------------------------------
+# Large-chunk linear with momentum (LaCT review, non-linear-memory section)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("read_first", [True, False])
+def test_momentum_zero_is_the_plain_method(read_first):
+    Q, K, V, eta, W0 = rand_case(seed=31)
+    O, W = TO.large_chunk_linear(Q, K, V, eta, W0, 4, read_first=read_first)
+    Om, Wm, M = TO.large_chunk_linear(Q, K, V, eta, W0, 4, read_first=read_first, momentum=0.0)
+    assert np.array_equal(O, Om) and np.array_equal(W, Wm)
+    last = slice(12, 13)                                   # T = 13: the last chunk holds one token
+    assert np.allclose(M, np.swapaxes(K[:, :, last], -1, -2) @ (eta[:, :, last, None] * V[:, :, last]))
+
+
+def test_momentum_two_chunks_by_hand():
+    Q, K, V, eta, W0 = rand_case(T=8, seed=32)
+    beta = 0.7
+    D0 = np.swapaxes(K[:, :, :4], -1, -2) @ (eta[:, :, :4, None] * V[:, :, :4])
+    D1 = np.swapaxes(K[:, :, 4:], -1, -2) @ (eta[:, :, 4:, None] * V[:, :, 4:])
+    n = lambda X: X / np.linalg.norm(X, axis=-2, keepdims=True)  # noqa: E731
+    W1 = n(W0 + D0)
+    W2 = n(W1 + beta * D0 + D1)
+    O, W, M = TO.large_chunk_linear(Q, K, V, eta, W0, 4, momentum=beta)
+    assert np.allclose(O[:, :, :4], Q[:, :, :4] @ W0) and np.allclose(O[:, :, 4:], Q[:, :, 4:] @ W1)
+    assert np.allclose(W, W2) and np.allclose(M, beta * D0 + D1)
+
+
+@pytest.mark.parametrize("beta", [0.5, 0.9])
+def test_momentum_unnormalised_is_a_discounted_sum(beta):
+    # without the normalisation W_T = W0 + sum_c M_c with M_c = sum_{c' <= c} beta^(c - c') D_c'
+    Q, K, V, eta, W0 = rand_case(T=13, seed=33)
+    Ds = [np.swapaxes(K[:, :, s:s + 3], -1, -2) @ (eta[:, :, s:s + 3, None] * V[:, :, s:s + 3]) for s in range(0, 13, 3)]
+    Ms = [sum(beta ** (c - k) * Ds[k] for k in range(c + 1)) for c in range(len(Ds))]
+    _, W, M = TO.large_chunk_linear(Q, K, V, eta, W0, 3, normalize=False, momentum=beta)
+    assert np.allclose(W, W0 + sum(Ms)) and np.allclose(M, Ms[-1])
+
+
+@pytest.mark.parametrize("read_first", [True, False])
+def test_momentum_resume_with_the_buffer(read_first):
+    Q, K, V, eta, W0 = rand_case(T=13, seed=34)
+    O, W, M = TO.large_chunk_linear(Q, K, V, eta, W0, 3, read_first=read_first, momentum=0.8)
+    Oa, Wa, Ma = TO.large_chunk_linear(Q[:, :, :6], K[:, :, :6], V[:, :, :6], eta[:, :, :6], W0, 3,
+                                       read_first=read_first, momentum=0.8)
+    Ob, Wb, Mb = TO.large_chunk_linear(Q[:, :, 6:], K[:, :, 6:], V[:, :, 6:], eta[:, :, 6:], Wa, 3,
+                                       read_first=read_first, momentum=0.8, M0=Ma)
+    assert np.allclose(np.concatenate([Oa, Ob], axis=2), O) and np.allclose(Wb, W) and np.allclose(Mb, M)
