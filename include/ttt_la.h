@@ -174,6 +174,27 @@ int ttt_la_forward_timed(const void* Q, const void* K, const void* V, const floa
                          void* O, float* W_out, void* workspace, size_t workspace_bytes,
                          void* stream, void* ev_start, void* ev_stop);
 
+/*
+ * ttt_la_forward_momentum: the large-chunk linear modes (TTT_LA_LARGE_CHUNK_LINEAR and its
+ * update-first variant) with momentum in the inner loop, which the LaCT review's
+ * non-linear-memory section names among the update rules it compares.  Each chunk's step
+ * K_c^T diag(eta_c) V_c goes into a buffer M_c = momentum * M_{c-1} + K_c^T diag(eta_c) V_c,
+ * and W takes M_c instead, then the column normalisation:
+ *     W_c = colnorm(W_{c-1} + M_c).
+ * momentum = 0 with M0 = NULL is ttt_la_forward bit for bit.
+ *   M0         [B,H,d_k,d_v] float32, device: the buffer before the first chunk (NULL = zeros),
+ *              e.g. the M_out of a call on the preceding tokens
+ *   momentum   the coefficient (finite; ERR_SHAPE otherwise)
+ *   M_out      [B,H,d_k,d_v] float32, device: the buffer after the last chunk (NULL = not
+ *              written); M_out == M0 in place is allowed, any other overlap is ERR_ALIAS
+ * Other arguments, workspace, checks and status codes as ttt_la_forward; ERR_UNSUPPORTED
+ * for the other modes.  ttt_la_backward has no momentum form.
+ */
+int ttt_la_forward_momentum(const void* Q, const void* K, const void* V, const float* eta,
+                            const float* W0, const float* M0, float momentum, int64_t chunk,
+                            int32_t mode, const ttt_la_desc* desc, void* O, float* W_out,
+                            float* M_out, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Timing events for ttt_la_forward_timed and for timing calls on a stream.
  * ttt_la_event_create makes a hipEvent_t (returned through *event) that
  * records a timestamp without the system-scope memory fence an ordinary
@@ -264,7 +285,7 @@ const char* ttt_la_status_string(int status);
 /* ABI version of this header (incremented on incompatible change). */
 int ttt_la_abi_version(void);
 
-#define TTT_LA_ABI_VERSION 4
+#define TTT_LA_ABI_VERSION 5
 
 #ifdef __cplusplus
 }

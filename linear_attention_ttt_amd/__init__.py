@@ -17,7 +17,7 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["forward", "backward", "backward_raw", "backward_workspace_bytes", "forward_timed_raw", "TimingEvent", "workspace_bytes", "TTTLAError", "MODES", "Desc", "lib", "library_path",
+__all__ = ["forward", "forward_momentum", "forward_momentum_raw", "backward", "backward_raw", "backward_workspace_bytes", "forward_timed_raw", "TimingEvent", "workspace_bytes", "TTTLAError", "MODES", "Desc", "lib", "library_path",
            "PER_TOKEN_LINEAR", "LARGE_CHUNK_LINEAR", "LARGE_CHUNK_SWIGLU", "PER_TOKEN_LINEAR_EXCLUSIVE",
            "LARGE_CHUNK_LINEAR_UPDATE_FIRST", "LARGE_CHUNK_SWIGLU_UPDATE_FIRST", "LARGE_CHUNK_SWIGLU_LAST_LAYER"]
 
@@ -69,6 +69,9 @@ def lib() -> ctypes.CDLL:
         L.ttt_la_forward_timed.argtypes = [vp, vp, vp, vp, vp, i64, i32, ctypes.POINTER(Desc), vp, vp, vp,
                                            ctypes.c_size_t, vp, vp, vp]
         L.ttt_la_forward_timed.restype = ctypes.c_int
+        L.ttt_la_forward_momentum.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_float, i64, i32, ctypes.POINTER(Desc),
+                                              vp, vp, vp, vp, ctypes.c_size_t, vp]
+        L.ttt_la_forward_momentum.restype = ctypes.c_int
         L.ttt_la_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i32, ctypes.POINTER(Desc), vp, vp, vp, vp,
                                       vp, vp, ctypes.c_size_t, vp]
         L.ttt_la_backward.restype = ctypes.c_int
@@ -113,6 +116,13 @@ def backward_raw(Q, K, V, eta, W0, dO, dW_out, chunk, mode, desc: Desc, dQ, dK, 
     """ttt_la_backward on raw device addresses (ints or None); returns the status code."""
     return lib().ttt_la_backward(Q, K, V, eta, W0, dO, dW_out, int(chunk), _mode(mode), ctypes.byref(desc), dQ, dK,
                                  dV, deta, dW0, workspace, workspace_bytes_, stream)
+
+
+def forward_momentum_raw(Q, K, V, eta, W0, M0, momentum, chunk, mode, desc: Desc, O, W_out, M_out, workspace,
+                         workspace_bytes_, stream) -> int:
+    """ttt_la_forward_momentum on raw device addresses (ints or None); returns the status code."""
+    return lib().ttt_la_forward_momentum(Q, K, V, eta, W0, M0, float(momentum), int(chunk), _mode(mode),
+                                         ctypes.byref(desc), O, W_out, M_out, workspace, workspace_bytes_, stream)
 
 
 def status_string(status: int) -> str:
@@ -280,3 +290,43 @@ def backward(Q, K, V, eta, W0, dO, dW_out, chunk: int, mode="per_token_linear", 
     if status != 0:
         raise TTTLAError(status, status_string(status))
     return dQ, dK, dV, deta, dW0
+
+
+def forward_momentum(Q, K, V, eta, W0, chunk: int, momentum: float, M0=None, mode="large_chunk_linear", *,
+                     workspace=None, stream=None):
+    """Large-chunk linear forward with a momentum buffer (``ttt_la_forward_momentum``):
+    returns ``(O, W_out, M_out)``.  ``M0`` (float32 like W0) is the buffer before the first
+    chunk, zeros when None.  Same tensor checks as ``forward``."""
+    import torch
+
+    m = _mode(mode)
+    if m not in (LARGE_CHUNK_LINEAR, LARGE_CHUNK_LINEAR_UPDATE_FIRST):
+        raise ValueError("momentum is defined for the large-chunk linear modes")
+    for name, t in dict(Q=Q, K=K, V=V, eta=eta, W0=W0).items():
+        if not isinstance(t, torch.Tensor) or t.device != Q.device or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous tensor on Q's device")
+    if M0 is not None and (M0.shape != W0.shape or M0.dtype != torch.float32 or not M0.is_contiguous()):
+        raise ValueError("M0 must be a contiguous float32 tensor shaped like W0")
+    if Q.dtype != torch.bfloat16 or K.dtype != Q.dtype or V.dtype != Q.dtype:
+        raise ValueError("Q, K, V must be bfloat16")
+    B, H, T, dk = Q.shape
+    dv = V.shape[3]
+    desc = make_desc(B, H, T, dk, dv, 0, BF16)
+    O = torch.empty((B, H, T, dv), dtype=Q.dtype, device=Q.device)
+    Wo, Mo = torch.empty_like(W0), torch.empty_like(W0)
+    nbytes = workspace_bytes(desc, chunk, m)
+    ws = workspace
+    if nbytes > 0 and (ws is None or ws.numel() * ws.element_size() < nbytes):
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=Q.device)
+    ws_ptr = ws.data_ptr() if (ws is not None and nbytes > 0) else None
+    ws_len = ws.numel() * ws.element_size() if ws_ptr else 0
+    st = stream if stream is not None else torch.cuda.current_stream(Q.device).cuda_stream
+
+    def p(t):
+        return t.data_ptr() if t is not None and t.numel() > 0 else None
+
+    status = forward_momentum_raw(p(Q), p(K), p(V), p(eta), W0.data_ptr(), p(M0), momentum, chunk, m, desc, p(O),
+                                  Wo.data_ptr(), Mo.data_ptr(), ws_ptr, ws_len, st)
+    if status != 0:
+        raise TTTLAError(status, status_string(status))
+    return O, Wo, Mo

@@ -127,9 +127,10 @@ size_t ttt_la_workspace_bytes(const ttt_la_desc* desc, int64_t chunk, int32_t mo
   return workspace_for(*desc, chunk, mode);
 }
 
-int ttt_la_forward_timed(const void* Q, const void* K, const void* V, const float* eta, const float* W0,
-                         int64_t chunk, int32_t mode, const ttt_la_desc* desc, void* O, float* W_out,
-                         void* workspace, size_t workspace_bytes, void* stream, void* ev_start, void* ev_stop) {
+static int forward_impl(const void* Q, const void* K, const void* V, const float* eta, const float* W0,
+                        int64_t chunk, int32_t mode, const ttt_la_desc* desc, void* O, float* W_out,
+                        void* workspace, size_t workspace_bytes, void* stream, void* ev_start, void* ev_stop,
+                        const float* M0, float* M_out, float momentum) {
   int st = check_problem(desc, chunk, mode);
   if (st != TTT_LA_OK) return st;
   const ttt_la_desc d = *desc;
@@ -157,6 +158,14 @@ int ttt_la_forward_timed(const void* Q, const void* K, const void* V, const floa
     if (overlap(rWo, ins[i])) return TTT_LA_ERR_ALIAS;
   if (overlap(rWo, rW0) && W_out != W0) return TTT_LA_ERR_ALIAS;
   if (overlap(rO, rWo) || overlap(rO, rWs) || overlap(rWo, rWs)) return TTT_LA_ERR_ALIAS;
+  // momentum buffers (large-chunk linear only): M0 is an input, M_out an output; M_out == M0 in place
+  const Range rM0 = range(M0, (size_t)state_elems(d, method) * 4);
+  const Range rMo = range(M_out, (size_t)state_elems(d, method) * 4);
+  for (const Range& in : ins)
+    if (overlap(rMo, in)) return TTT_LA_ERR_ALIAS;
+  if (overlap(rO, rM0) || overlap(rWo, rM0) || overlap(rWs, rM0)) return TTT_LA_ERR_ALIAS;
+  if (overlap(rMo, rM0) && M_out != M0) return TTT_LA_ERR_ALIAS;
+  if (overlap(rMo, rO) || overlap(rMo, rWo) || overlap(rMo, rWs)) return TTT_LA_ERR_ALIAS;
 
   hipStream_t s = (hipStream_t)stream;
   ttt::Timing tm;
@@ -170,11 +179,30 @@ int ttt_la_forward_timed(const void* Q, const void* K, const void* V, const floa
     e = ttt::launch_per_token(a, s, tm);
   } else {
     ttt::LargeChunkArgs a{Q, K, V, eta, W0, O, W_out, workspace, d.B, d.H, d.T, d.d_k, d.d_v, d.d_h, chunk, d.io_dtype,
-                          other, mode == TTT_LA_LARGE_CHUNK_SWIGLU_LAST_LAYER ? 1 : 0};
+                          other, mode == TTT_LA_LARGE_CHUNK_SWIGLU_LAST_LAYER ? 1 : 0, M0, M_out, momentum};
     e = method == TTT_LA_LARGE_CHUNK_LINEAR ? ttt::launch_large_chunk_linear(a, s, tm)
                                             : ttt::launch_large_chunk_swiglu(a, s, tm);
   }
   return e == hipSuccess ? TTT_LA_OK : TTT_LA_ERR_HIP;
+}
+
+int ttt_la_forward_timed(const void* Q, const void* K, const void* V, const float* eta, const float* W0,
+                         int64_t chunk, int32_t mode, const ttt_la_desc* desc, void* O, float* W_out,
+                         void* workspace, size_t workspace_bytes, void* stream, void* ev_start, void* ev_stop) {
+  return forward_impl(Q, K, V, eta, W0, chunk, mode, desc, O, W_out, workspace, workspace_bytes, stream, ev_start,
+                      ev_stop, nullptr, nullptr, 0.f);
+}
+
+int ttt_la_forward_momentum(const void* Q, const void* K, const void* V, const float* eta, const float* W0,
+                            const float* M0, float momentum, int64_t chunk, int32_t mode, const ttt_la_desc* desc,
+                            void* O, float* W_out, float* M_out, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+  const int st = check_problem(desc, chunk, mode);
+  if (st != TTT_LA_OK) return st;
+  if (method_of(mode) != TTT_LA_LARGE_CHUNK_LINEAR) return TTT_LA_ERR_UNSUPPORTED;
+  if (!(momentum == momentum) || momentum < -1e30f || momentum > 1e30f) return TTT_LA_ERR_SHAPE;   // NaN or inf
+  return forward_impl(Q, K, V, eta, W0, chunk, mode, desc, O, W_out, workspace, workspace_bytes, stream, nullptr,
+                      nullptr, M0, M_out, momentum);
 }
 
 int ttt_la_forward(const void* Q, const void* K, const void* V, const float* eta, const float* W0,

@@ -75,6 +75,11 @@ struct LargeChunkArgs {
   int dtype;
   int update_first;  // 1: a chunk takes its step, then its queries read the result
   int last_layer_only = 0;  // SwiGLU: only W2 is updated, and nothing is normalised
+  // large-chunk linear: momentum buffer M_c = momentum M_{c-1} + dW_c (from M0, zeros when null;
+  // the final buffer into M_out when not null)
+  const float* M0 = nullptr;
+  float* M_out = nullptr;
+  float momentum = 0.f;
 };
 
 bool large_chunk_linear_supported(int64_t dk, int64_t dv, int64_t chunk, int dtype);

@@ -179,19 +179,26 @@ __global__ __launch_bounds__(256, 4) void lact_delta_kernel(const bf16* __restri
 //    the next window of chunks are loaded while the current window is
 //    scanned (two register buffers); the column norm is a DPP wave sum.
 // ---------------------------------------------------------------------------
+// With momentum beta the step applied is the buffer M_c = beta M_{c-1} + dW_c (M from M0, or
+// zeros when M0 is null; written to Mout when it is not null).  beta = 0 without M0 gives the
+// plain step bit for bit (0 * 0 + dW = dW).
 template <int D, bool UF>
 __global__ __launch_bounds__(256) void lact_scan_kernel(const float* __restrict__ W0, const float* __restrict__ part,
                                                         float* __restrict__ wprev_t, float* __restrict__ Wout,
-                                                        int nchunks, int nsplit) {
+                                                        int nchunks, int nsplit, const float* M0, float* Mout,
+                                                        float beta) {
   constexpr int RPL = D / 64;
   constexpr int WIN = D == 64 ? 12 : 6;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
   const int j = (blockIdx.x % (D / 4)) * 4 + w;
   const int bh = blockIdx.x / (D / 4);
-  float Wc[RPL];
+  float Wc[RPL], Mc[RPL];
   const float* W0h = W0 + (size_t)bh * D * D;
 #pragma unroll
-  for (int r = 0; r < RPL; ++r) Wc[r] = W0h[(size_t)(l + 64 * r) * D + j];
+  for (int r = 0; r < RPL; ++r) {
+    Wc[r] = W0h[(size_t)(l + 64 * r) * D + j];
+    Mc[r] = M0 ? M0[(size_t)bh * D * D + (size_t)(l + 64 * r) * D + j] : 0.f;
+  }
   // slice updates of chunks c0 .. c0+WIN-1, loaded unconditionally (indices clamped) so that every window
   // issues the same loads and the waits for one window never cover the next one's
   auto issue = [&](int c0, float (&raw)[LC_MAXSPLIT][WIN][RPL]) {
@@ -221,7 +228,8 @@ __global__ __launch_bounds__(256) void lact_scan_kernel(const float* __restrict_
 #pragma unroll
         for (int s = 1; s < LC_MAXSPLIT; ++s) d += s < nsplit ? raw[s][i][r] : 0.f;
         if (!UF) Wt[l + 64 * r] = Wc[r];
-        Wc[r] += d;
+        Mc[r] = fmaf(beta, Mc[r], d);
+        Wc[r] += Mc[r];
         ss = fmaf(Wc[r], Wc[r], ss);
       }
       const float inv = 1.0f / fmaxf(sqrtf(wave_sum(ss)), 1e-12f);
@@ -250,6 +258,10 @@ __global__ __launch_bounds__(256) void lact_scan_kernel(const float* __restrict_
   float* Wo = Wout + (size_t)bh * D * D;
 #pragma unroll
   for (int r = 0; r < RPL; ++r) Wo[(size_t)(l + 64 * r) * D + j] = Wc[r];
+  if (Mout) {
+#pragma unroll
+    for (int r = 0; r < RPL; ++r) Mout[(size_t)bh * D * D + (size_t)(l + 64 * r) * D + j] = Mc[r];
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -394,7 +406,8 @@ hipError_t launch_lact(const LargeChunkArgs& a, hipStream_t stream, const Timing
     if ((e = mark(tm.stop, stream)) != hipSuccess) return e;
   }
   auto kscan = a.update_first ? lact_scan_kernel<D, true> : lact_scan_kernel<D, false>;
-  hipLaunchKernelGGL(kscan, dim3(BH * D / 4), dim3(256), 0, stream, a.W0, part, wprev, a.W_out, nchunks, nsplit);
+  hipLaunchKernelGGL(kscan, dim3(BH * D / 4), dim3(256), 0, stream, a.W0, part, wprev, a.W_out, nchunks, nsplit, a.M0,
+                     a.M_out, a.momentum);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || nchunks == 0) return e;
   using Cfg = LactReadCfg<D>;
@@ -685,7 +698,8 @@ hipError_t launch_lact_bwd(const BackwardArgs& a, hipStream_t stream) {
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   auto kscan = uf ? lact_scan_kernel<D, true> : lact_scan_kernel<D, false>;
-  hipLaunchKernelGGL(kscan, dim3(BH * D / 4), dim3(256), 0, stream, a.W0, partA, wprev, junk, nchunks, nsplit);
+  hipLaunchKernelGGL(kscan, dim3(BH * D / 4), dim3(256), 0, stream, a.W0, partA, wprev, junk, nchunks, nsplit,
+                     (const float*)nullptr, (float*)nullptr, 0.0f);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   auto kb = uf ? lact_bwd_scan_kernel<D, true> : lact_bwd_scan_kernel<D, false>;
   hipLaunchKernelGGL(kb, dim3(BH * D / 4), dim3(256), 0, stream, a.W0, a.dW, partA, partB, wprev, dpt, a.dW0, nchunks,

@@ -39,14 +39,15 @@ def test_exports_every_declared_symbol():
     names = declared_functions()
     assert {"ttt_la_forward", "ttt_la_workspace_bytes", "ttt_la_status_string", "ttt_la_abi_version",
             "ttt_la_event_create", "ttt_la_event_record", "ttt_la_event_elapsed_ms",
-            "ttt_la_event_destroy", "ttt_la_backward", "ttt_la_backward_workspace_bytes"} <= set(names)
+            "ttt_la_event_destroy", "ttt_la_backward", "ttt_la_backward_workspace_bytes",
+            "ttt_la_forward_momentum"} <= set(names)
     for n in names:
         assert hasattr(L, n), f"{n} not exported"
 
 
 @needs_lib
 def test_version_and_status_strings():
-    assert la.lib().ttt_la_abi_version() == 4
+    assert la.lib().ttt_la_abi_version() == 5
     for s in range(10):
         assert la.status_string(s) and la.status_string(s) != "unknown status"
     assert la.status_string(99) == "unknown status"
@@ -233,3 +234,26 @@ def test_backward_workspace():
     d1 = la.make_desc(256, 1, 1 << 22, 128, 128, 0, la.BF16)
     st1 = 256 * 128 * 128 * 4
     assert la.backward_workspace_bytes(d1, 64, 0) == 2 * st1 + 3 * st1
+
+
+def mcall(mode=1, momentum=0.9, M0=ptr(8), M_out=ptr(9), desc=None, **kw):
+    if desc is None:
+        desc = la.make_desc(1, 2, 128, 64, 64, 0, la.BF16)
+    p = dict(Q=ptr(0), K=ptr(1), V=ptr(2), eta=ptr(3), W0=ptr(4), O=ptr(5), W_out=ptr(6), ws=ptr(7))
+    p.update(kw)
+    return la.forward_momentum_raw(p["Q"], p["K"], p["V"], p["eta"], p["W0"], M0, momentum, 64, mode, desc, p["O"],
+                                   p["W_out"], M_out, p["ws"], 1 << 33, None)
+
+
+@needs_lib
+@pytest.mark.parametrize("kw,code", [
+    (dict(mode=0), 6), (dict(mode=2, desc=la.make_desc(1, 2, 128, 128, 128, 256, la.BF16)), 6), (dict(mode=3), 6),
+    (dict(mode=7), 5), (dict(momentum=float("nan")), 2), (dict(momentum=float("inf")), 2),
+    (dict(W0=None), 1),
+    (dict(M_out=ptr(0)), 7),                  # M_out over Q
+    (dict(M_out=ptr(6)), 7),                  # M_out over W_out
+    (dict(M_out=ptr(8) + 4), 7),              # partly over M0
+    (dict(M0=ptr(5)), 7),                     # M0 over O
+])
+def test_momentum_invalid_arguments(kw, code):
+    assert mcall(**kw) == code

@@ -86,3 +86,58 @@ def test_large_chunk_linear_update_first_workload_sampled_heads():
     x = workloads.generate(s, seed=0)
     O, W = run(to_device(x, s), s)
     check(s, x, O, W, heads=[3, 11], label="B1H12T196608 heads 3,11")
+
+
+def momentum_check(s, x, O, W, M, beta, M0=None, label=""):
+    import oracle
+    Or, Wr, Mr = oracle.large_chunk_linear(x["Q"], x["K"], x["V"], x["eta"], x["W0"], s["chunk"],
+                                           read_first=s["mode"] == "large_chunk_linear", momentum=beta, M0=M0)
+    eo, ew, em = (err(O.float().cpu().numpy(), Or, "bf16"), err(W.cpu().numpy(), Wr, "bf16"),
+                  err(M.cpu().numpy(), Mr, "bf16"))
+    print(f"[{s['mode']} momentum {beta} {label}] err_O={eo:.3e} err_W={ew:.3e} err_M={em:.3e}", flush=True)
+    assert max(eo, ew, em) <= tol("bf16")
+
+
+@pytest.mark.parametrize("mode", ["large_chunk_linear", "large_chunk_linear_update_first"])
+@pytest.mark.parametrize("B,H,T,d,chunk,beta", [
+    (1, 2, 300, 64, 128, 0.9),
+    (1, 3, 1000, 128, 300, 0.5),
+    (1, 2, 97, 64, 1, 0.9),        # one token per chunk: many momentum steps
+    (1, 1, 2500, 64, 2048, -0.3),
+])
+def test_large_chunk_linear_momentum(mode, B, H, T, d, chunk, beta):
+    s = workloads.make_spec(mode, B, H, T, d, chunk=chunk, dtype="bf16", eta_scale=0.05)
+    x = workloads.generate(s, seed=23)
+    t = to_device(x, s)
+    O, W, M = la.forward_momentum(t["Q"], t["K"], t["V"], t["eta"], t["W0"], chunk, beta, mode=mode)
+    torch.cuda.synchronize()
+    momentum_check(s, x, O, W, M, beta, label=f"{B},{H},{T},{d},c{chunk}")
+
+
+def test_large_chunk_linear_momentum_zero_is_forward_and_resume():
+    s = workloads.make_spec("large_chunk_linear", 1, 3, 700, 64, chunk=128, dtype="bf16", eta_scale=0.05)
+    x = workloads.generate(s, seed=24)
+    t = to_device(x, s)
+    O0, W0_ = run(t, s)
+    Om, Wm, _ = la.forward_momentum(t["Q"], t["K"], t["V"], t["eta"], t["W0"], 128, 0.0)
+    torch.cuda.synchronize()
+    assert torch.equal(O0, Om) and torch.equal(W0_, Wm)          # momentum 0 is the plain method, bit for bit
+    O, W, M = la.forward_momentum(t["Q"], t["K"], t["V"], t["eta"], t["W0"], 128, 0.8)
+    a = {k: (v[:, :, :256].contiguous() if k != "W0" else v) for k, v in t.items()}
+    b = {k: (v[:, :, 256:].contiguous() if k != "W0" else v) for k, v in t.items()}
+    Oa, Wa, Ma = la.forward_momentum(a["Q"], a["K"], a["V"], a["eta"], a["W0"], 128, 0.8)
+    Ob, Wb, Mb = la.forward_momentum(b["Q"], b["K"], b["V"], b["eta"], Wa, 128, 0.8, M0=Ma)
+    torch.cuda.synchronize()
+    assert err(torch.cat([Oa, Ob], 2).float().cpu().numpy(), O.float().cpu().numpy(), "bf16") <= tol("bf16")
+    assert err(Wb.cpu().numpy(), W.cpu().numpy(), "bf16") <= 1e-5 and err(Mb.cpu().numpy(), M.cpu().numpy(), "bf16") <= 1e-5
+
+
+def test_large_chunk_linear_momentum_workload_sampled_heads():
+    s = workloads.spec("large_chunk_linear_bf16_B1H12T196608_d64_c4096")
+    x = workloads.generate(s, seed=0)
+    t = to_device(x, s)
+    O, W, M = la.forward_momentum(t["Q"], t["K"], t["V"], t["eta"], t["W0"], s["chunk"], 0.9)
+    torch.cuda.synchronize()
+    sel = lambda a: a[:, [4, 9]]  # noqa: E731
+    xs = {k: sel(v) for k, v in x.items() if k in ("Q", "K", "V", "eta", "W0")}
+    momentum_check(dict(s), xs, sel(O), sel(W), sel(M), 0.9, label="B1H12T196608 heads 4,9")
