@@ -95,7 +95,8 @@ def dominant_kernel(s: dict) -> tuple[str, float, str]:
     return "swiglu_recur_kernel (recurrence)", float(n * 12 * dk * dh), "mfma"
 
 
-def run_workload(name: str, steps: int, warmup: int, flush_mb: int, other_order: bool = False, mode=None):
+def run_workload(name: str, steps: int, warmup: int, flush_mb: int, other_order: bool = False, mode=None,
+                 momentum=None):
     import torch
     import linear_attention_ttt_amd as la
 
@@ -133,8 +134,17 @@ def run_workload(name: str, steps: int, warmup: int, flush_mb: int, other_order:
     ptrs = [t[k].data_ptr() for k in ("Q", "K", "V", "eta", "W0")]
     sptr = stream.cuda_stream
 
+    Mbuf = torch.zeros_like(Wout) if momentum is not None else None
+
     def step(timing=None):
-        if timing is None:
+        if momentum is not None:   # ttt_la_forward_momentum has no timed form: events around the whole call
+            if timing is not None:
+                timing[0].record(sptr)
+            st = la.forward_momentum_raw(*ptrs, Mbuf.data_ptr(), momentum, s["chunk"], s["mode"], desc, O.data_ptr(),
+                                         Wout.data_ptr(), Mbuf.data_ptr(), ws.data_ptr(), ws.numel(), sptr)
+            if timing is not None:
+                timing[1].record(sptr)
+        elif timing is None:
             st = la.forward_raw(*ptrs, s["chunk"], s["mode"], desc, O.data_ptr(), Wout.data_ptr(), ws.data_ptr(),
                                 ws.numel(), sptr)
         else:
@@ -320,6 +330,9 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--flush-mb", type=int, default=512)
     ap.add_argument("--no-backward", action="store_true", help="skip the backward sub-records")
+    ap.add_argument("--momentum", type=float, default=None,
+                    help="large-chunk linear workloads: run ttt_la_forward_momentum with this coefficient (the "
+                         "kernel-timing loop then times whole calls); implies --no-others --no-backward")
     ap.add_argument("--mode", default=None,
                     help="run the workload in this mode instead of its own (same shapes; e.g. "
                          "large_chunk_swiglu_last_layer on the SwiGLU workload); implies --no-others")
@@ -347,7 +360,9 @@ def main():
         del src, dst
     if a.mode:
         a.no_others = True
-    head = run_workload(a.workload, a.steps, a.warmup, a.flush_mb, a.other_order, a.mode)
+    if a.momentum is not None:
+        a.no_others = a.no_backward = True
+    head = run_workload(a.workload, a.steps, a.warmup, a.flush_mb, a.other_order, a.mode, a.momentum)
     others = {}
     if not a.no_others:
         for name in workloads.WORKLOADS:
@@ -375,7 +390,7 @@ def main():
     k = head["kernel"]
     peak = HBM_PEAK_GBS if k["bound"] == "hbm" else BF16_PEAK_TFLOPS
     roof = {"bound": k["bound"], "achieved": k["achieved"], "peak": peak, "unit": k["unit"],
-            "frac": k["achieved"] / peak, "traffic": None if (a.other_order or a.mode) else traffic_per_launch(k["name"]),
+            "frac": k["achieved"] / peak, "traffic": None if (a.other_order or a.mode or a.momentum is not None) else traffic_per_launch(k["name"]),
             "kernel": k["name"], "kernel_ms": k["ms_mean"], "units_per_launch": k["units_per_launch"],
             "step_frac": head["hbm_frac"] if k["bound"] == "hbm" else head["bf16_mfma_frac"]}
     line = {

@@ -1,6 +1,7 @@
 // C-ABI entry points of libttt_la: argument validation, workspace sizing
 // and dispatch to the gfx950 kernels.  Every check runs before the first
 // HIP call, so an invalid call enqueues nothing and writes nothing.
+#include <cmath>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -200,7 +201,7 @@ int ttt_la_forward_momentum(const void* Q, const void* K, const void* V, const f
   const int st = check_problem(desc, chunk, mode);
   if (st != TTT_LA_OK) return st;
   if (method_of(mode) != TTT_LA_LARGE_CHUNK_LINEAR) return TTT_LA_ERR_UNSUPPORTED;
-  if (!(momentum == momentum) || momentum < -1e30f || momentum > 1e30f) return TTT_LA_ERR_SHAPE;   // NaN or inf
+  if (!std::isfinite(momentum)) return TTT_LA_ERR_SHAPE;
   return forward_impl(Q, K, V, eta, W0, chunk, mode, desc, O, W_out, workspace, workspace_bytes, stream, nullptr,
                       nullptr, M0, M_out, momentum);
 }
