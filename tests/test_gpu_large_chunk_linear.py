@@ -141,3 +141,30 @@ def test_large_chunk_linear_momentum_workload_sampled_heads():
     sel = lambda a: a[:, [4, 9]]  # noqa: E731
     xs = {k: sel(v) for k, v in x.items() if k in ("Q", "K", "V", "eta", "W0")}
     momentum_check(dict(s), xs, sel(O), sel(W), sel(M), 0.9, label="B1H12T196608 heads 4,9")
+
+
+
+def test_large_chunk_linear_momentum_in_place_buffer():
+    # M_out == M0: the buffer is updated in place, as two calls on the halves of the sequence show
+    s = workloads.make_spec("large_chunk_linear", 1, 2, 512, 64, chunk=128, dtype="bf16", eta_scale=0.05)
+    x = workloads.generate(s, seed=25)
+    t = to_device(x, s)
+    O, W, M = la.forward_momentum(t["Q"], t["K"], t["V"], t["eta"], t["W0"], 128, 0.7)
+    desc = la.make_desc(1, 2, 256, 64, 64, 0, la.BF16)
+    ws = torch.empty(max(la.workspace_bytes(desc, 128, 1), 1), dtype=torch.uint8, device="cuda")
+    Mbuf = torch.zeros_like(t["W0"])
+    Wcur = t["W0"].clone()
+    outs = []
+    for h in (slice(0, 256), slice(256, 512)):
+        part = {k: t[k][:, :, h].contiguous() for k in ("Q", "K", "V", "eta")}
+        Oh = torch.empty((1, 2, 256, 64), dtype=torch.bfloat16, device="cuda")
+        st = la.forward_momentum_raw(part["Q"].data_ptr(), part["K"].data_ptr(), part["V"].data_ptr(),
+                                     part["eta"].data_ptr(), Wcur.data_ptr(), Mbuf.data_ptr(), 0.7, 128, 1, desc,
+                                     Oh.data_ptr(), Wcur.data_ptr(), Mbuf.data_ptr(), ws.data_ptr(), ws.numel(),
+                                     torch.cuda.current_stream().cuda_stream)
+        assert st == 0
+        outs.append(Oh)
+    torch.cuda.synchronize()
+    assert err(torch.cat(outs, 2).float().cpu().numpy(), O.float().cpu().numpy(), "bf16") <= tol("bf16")
+    assert err(Wcur.cpu().numpy(), W.cpu().numpy(), "bf16") <= 1e-5
+    assert err(Mbuf.cpu().numpy(), M.cpu().numpy(), "bf16") <= 1e-5

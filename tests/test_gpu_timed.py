@@ -11,6 +11,10 @@ CASES = [
     workloads.make_spec("per_token_linear", 1, 2, 300, 64, chunk=32, dtype="fp32"),
     workloads.make_spec("large_chunk_linear", 1, 2, 1000, 64, chunk=256, dtype="bf16"),
     workloads.make_spec("large_chunk_swiglu", 1, 1, 300, 128, d_h=256, chunk=128, dtype="bf16"),
+    workloads.make_spec("per_token_linear_exclusive", 1, 2, 300, 128, chunk=64, dtype="bf16"),
+    workloads.make_spec("large_chunk_linear_update_first", 1, 2, 1000, 64, chunk=256, dtype="bf16"),
+    workloads.make_spec("large_chunk_swiglu_last_layer", 1, 1, 300, 128, d_h=256, chunk=128, dtype="bf16"),
+    workloads.make_spec("large_chunk_swiglu_last_layer", 1, 16, 300, 128, d_h=256, chunk=128, dtype="bf16"),
 ]
 
 
