@@ -1,22 +1,36 @@
 """Throughput of the TTT-layer forward pass (libttt_la) on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                    [--no-others] [--no-cpu] [--flush-mb 512] [--calibrate-copy-mb N]
+                    [--no-others] [--no-cpu] [--no-backward] [--flush-mb 512]
+                    [--calibrate-copy-mb N] [--mode M] [--other-order] [--momentum B]
 
 A step is one ttt_la_forward call over one batch of synthetic inputs that
-are already resident in HBM.  Before every step a 512 MB buffer is
-overwritten and another 512 MB buffer read, so the 256 MB last-level cache
-and the L2s hold none of the inputs and no dirty lines; each step is timed
-with HIP events on the stream the kernels run on, and the K steps are
-bracketed by device synchronisation.  Prints ONE
-JSON line (the headline workload, plus sub-records for the other
-workloads of the method under "workloads").
+are already resident in HBM.  Each workload is timed three ways:
+
+* flushed (the headline ``value`` and ``ms_per_step``): before every step a
+  512 MB buffer is overwritten and another 512 MB buffer read, so the 256 MB
+  last-level cache and the L2s hold none of the inputs and no dirty lines;
+  each step is bracketed by HIP events on the stream the kernels run on and
+  the K steps by device synchronisation;
+* steady state: K calls back to back, rotating over copies of the inputs
+  and outputs whose total exceeds the caches, timed as a whole, so the
+  write-back of one call's outputs falls inside the timed window of the
+  next (no eviction between calls);
+* dominant kernel: the library records fence-free events around it
+  (ttt_la_forward_timed), for the roofline.
+
+Prints ONE JSON line: the headline workload (the largest per-token one),
+with sub-records for the other workloads under "workloads" (each with its
+own roofline, counter traffic and CPU baseline) and backward records under
+"backward".
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -32,11 +46,14 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 FP32_VALU_PEAK_TFLOPS = 157.3  # MI355X fp32 vector
 
-
 # each method's other read order (exclusive per-token read, update-then-read chunks): same kernels and work
 OTHER_ORDER = {"per_token_linear": "per_token_linear_exclusive",
                "large_chunk_linear": "large_chunk_linear_update_first",
                "large_chunk_swiglu": "large_chunk_swiglu_update_first"}
+
+# kernel source each workload's dominant kernel is built from (counter summaries are keyed to its hash)
+KERNEL_SOURCE = {"per_token_linear": "per_token.hip", "large_chunk_linear": "large_chunk_linear.hip",
+                 "large_chunk_swiglu": "large_chunk_swiglu.hip", "large_chunk_swiglu_last_layer": "large_chunk_swiglu.hip"}
 
 
 def method_of(mode: str) -> str:
@@ -46,20 +63,25 @@ def method_of(mode: str) -> str:
     return mode
 
 
+def o_size(s: dict) -> int:
+    return 4 if s.get("o_dtype", s["dtype"]) == "fp32" else (2 if s["dtype"] == "bf16" else 4)
+
+
 def algorithmic(s: dict) -> tuple[int, float]:
     """Bytes the method must move and flops it must do for one forward pass.
 
-    Bytes: read Q, K, V, eta once, write O once, read W0 and write W_out.
-    Flops per token-head: per-token mode 4 d_k d_v (rank-1 update + read)
-    plus (C+1)(d_k+d_v) for the causal half of the intra-chunk products;
-    large-chunk linear 4 d^2 plus 3 d^2 per chunk for the normalisation;
-    SwiGLU 18 d d_h (Q read 6, K forward 4, four gradient products 8)."""
+    Bytes: read Q, K, V, eta once, write O once (in its element type), read
+    W0 and write W_out.  Flops per token-head: per-token mode 4 d_k d_v
+    (rank-1 update + read) plus (C+1)(d_k+d_v) for the causal half of the
+    intra-chunk products; large-chunk linear 4 d^2 plus 3 d^2 per chunk for
+    the normalisation; SwiGLU 18 d d_h (Q read 6, K forward 4, four
+    gradient products 8)."""
     B, H, T, dk, dv, dh, C = s["B"], s["H"], s["T"], s["d_k"], s["d_v"], s["d_h"], s["chunk"]
     es = 2 if s["dtype"] == "bf16" else 4
     n = B * H * T
     m = method_of(s["mode"])
     state = B * H * (3 * dk * dh if m.startswith("large_chunk_swiglu") else dk * dv) * 4
-    nbytes = n * (2 * dk + 2 * dv) * es + n * 4 + 2 * state
+    nbytes = n * (2 * dk + dv) * es + n * dv * o_size(s) + n * 4 + 2 * state
     if m == "per_token_linear":
         flops = n * (4 * dk * dv + (C + 1) * (dk + dv))
     elif m == "large_chunk_linear":
@@ -95,6 +117,30 @@ def dominant_kernel(s: dict) -> tuple[str, float, str]:
     return "swiglu_recur_kernel (recurrence)", float(n * 12 * dk * dh), "mfma"
 
 
+def traffic_per_launch(name: str, s: dict):
+    """HBM bytes per launch of the workload's dominant kernel from the
+    committed counter summary ``profiles/traffic_<workload>.md``
+    (FETCH_SIZE + WRITE_SIZE, calibrated against a copy of known size), or
+    None when there is none, it was taken in another mode or output dtype,
+    or the kernel source changed since."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{name}.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_sha = re.search(r"source_sha256:\s*([0-9a-f]{64})", text)
+    m_bytes = re.search(r"hbm_bytes_per_launch:\s*([0-9]+)", text)
+    m_mode = re.search(r"mode:\s*(\S+)", text)
+    m_odt = re.search(r"o_dtype:\s*(\S+)", text)
+    if not (m_sha and m_bytes and m_mode and m_odt):
+        return None
+    if m_mode.group(1) != s["mode"] or m_odt.group(1) != s.get("o_dtype", s["dtype"]):
+        return None
+    src = os.path.join(ROOT, "linear_attention_ttt_amd", "csrc", KERNEL_SOURCE[method_of(s["mode"])])
+    if hashlib.sha256(open(src, "rb").read()).hexdigest() != m_sha.group(1):
+        return None
+    return int(m_bytes.group(1))
+
+
 def run_workload(name: str, steps: int, warmup: int, flush_mb: int, other_order: bool = False, mode=None,
                  momentum=None):
     import torch
@@ -108,67 +154,72 @@ def run_workload(name: str, steps: int, warmup: int, flush_mb: int, other_order:
     x = workloads.generate(s, seed=0)
     dev = torch.device("cuda:0")
     dt = torch.bfloat16 if s["dtype"] == "bf16" else torch.float32
-    t = {k: torch.from_numpy(x[k]).to(dev) for k in ("Q", "K", "V", "eta", "W0")}
-    for k in ("Q", "K", "V"):
-        t[k] = t[k].to(dt)
-    del x
+    odt = torch.float32 if s["o_dtype"] == "fp32" else dt
     B, H, T, dv = s["B"], s["H"], s["T"], s["d_v"]
-    O = torch.empty((B, H, T, dv), dtype=dt, device=dev)
-    Wout = torch.empty_like(t["W0"])
-    desc = la.make_desc(B, H, T, s["d_k"], dv, s["d_h"], la.BF16 if dt == torch.bfloat16 else la.FP32)
+    desc = la.make_desc(B, H, T, s["d_k"], dv, s["d_h"], la.BF16 if dt == torch.bfloat16 else la.FP32,
+                        la.O_FP32 if odt != dt else la.O_AS_INPUT)
     nws = la.workspace_bytes(desc, s["chunk"], s["mode"])
+    nbytes, flops = algorithmic(s)
+    # copies of the inputs and outputs for the steady-state loop: enough that their total exceeds the
+    # caches (256 MB last-level cache) several times over
+    nsets = int(min(8, max(2, -(-(768 << 20) // max(nbytes, 1)))))
+    sets = []
+    for i in range(nsets):
+        t = {k: torch.from_numpy(np.ascontiguousarray(x[k])).to(dev) for k in ("Q", "K", "V", "eta", "W0")}
+        for k in ("Q", "K", "V"):
+            t[k] = t[k].to(dt)
+        t["O"] = torch.empty((B, H, T, dv), dtype=odt, device=dev)
+        t["Wout"] = torch.empty_like(t["W0"])
+        t["M"] = torch.zeros_like(t["W0"]) if momentum is not None else None
+        sets.append(t)
+    del x
     ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
-    # cache eviction before every step, outside the timed region: overwrite one buffer, then read
+    # cache eviction before every flushed step, outside the timed region: overwrite one buffer, then read
     # another, so that the last-level cache and the L2s hold neither the inputs nor dirty lines whose
     # write-back would otherwise land in the next timed step
     flush = torch.empty(flush_mb << 20, dtype=torch.uint8, device=dev)
-    flush_rd = torch.ones((flush_mb << 20) // 4, dtype=torch.float32, device=dev)   # fp32: summed without a converted copy
+    flush_rd = torch.ones((flush_mb << 20) // 4, dtype=torch.float32, device=dev)   # fp32: summed without a copy
 
     def evict(v):
         flush.fill_(v)
         flush_rd.sum()
 
     stream = torch.cuda.current_stream(dev)
-
-    # arguments prepared once: each step is one library call (no Python-side checks inside the timed region)
-    ptrs = [t[k].data_ptr() for k in ("Q", "K", "V", "eta", "W0")]
     sptr = stream.cuda_stream
 
-    Mbuf = torch.zeros_like(Wout) if momentum is not None else None
-
-    def step(timing=None):
+    # arguments prepared once: each step is one library call (no Python-side checks inside the timed region)
+    def step(i=0, timing=None):
+        t = sets[i % nsets]
+        ptrs = [t[k].data_ptr() for k in ("Q", "K", "V", "eta", "W0")]
         if momentum is not None:   # ttt_la_forward_momentum has no timed form: events around the whole call
             if timing is not None:
                 timing[0].record(sptr)
-            st = la.forward_momentum_raw(*ptrs, Mbuf.data_ptr(), momentum, s["chunk"], s["mode"], desc, O.data_ptr(),
-                                         Wout.data_ptr(), Mbuf.data_ptr(), ws.data_ptr(), ws.numel(), sptr)
+            st = la.forward_momentum_raw(*ptrs, t["M"].data_ptr(), momentum, s["chunk"], s["mode"], desc,
+                                         t["O"].data_ptr(), t["Wout"].data_ptr(), t["M"].data_ptr(), ws.data_ptr(),
+                                         ws.numel(), sptr)
             if timing is not None:
                 timing[1].record(sptr)
         elif timing is None:
-            st = la.forward_raw(*ptrs, s["chunk"], s["mode"], desc, O.data_ptr(), Wout.data_ptr(), ws.data_ptr(),
-                                ws.numel(), sptr)
+            st = la.forward_raw(*ptrs, s["chunk"], s["mode"], desc, t["O"].data_ptr(), t["Wout"].data_ptr(),
+                                ws.data_ptr(), ws.numel(), sptr)
         else:
-            st = la.forward_timed_raw(*ptrs, s["chunk"], s["mode"], desc, O.data_ptr(), Wout.data_ptr(),
+            st = la.forward_timed_raw(*ptrs, s["chunk"], s["mode"], desc, t["O"].data_ptr(), t["Wout"].data_ptr(),
                                       ws.data_ptr(), ws.numel(), sptr, timing[0].handle, timing[1].handle)
         if st != 0:
             raise RuntimeError(f"ttt_la_forward failed: {la.status_string(st)}")
 
     # reference call through the checked binding (also validates the raw arguments above)
-    la.forward(t["Q"], t["K"], t["V"], t["eta"], t["W0"], s["chunk"], s["mode"], out=O, W_out=Wout, workspace=ws)
+    t0 = sets[0]
+    la.forward(t0["Q"], t0["K"], t0["V"], t0["eta"], t0["W0"], s["chunk"], s["mode"], out=t0["O"],
+               W_out=t0["Wout"], workspace=ws, out_dtype=odt)
 
     for _ in range(warmup):
         evict(1)
         step()
     torch.cuda.synchronize()
-    # Two timed loops over the same steps.  The step time comes from events on the stream around whole
-    # calls with nothing recorded inside them; the dominant kernel is timed in a second loop by events
-    # the library records around it (fence-free events from ttt_la_event_create, so the timestamps do
-    # not write back and invalidate the caches between the kernels; even so, the two extra queue packets
-    # lengthen a step by a few microseconds, which is why the step time is not taken from this loop).
+    # 1. flushed steps, each between events on the stream with nothing recorded inside the call
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    kstarts = [la.TimingEvent() for _ in range(steps)]
-    kends = [la.TimingEvent() for _ in range(steps)]
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     for i in range(steps):
@@ -179,27 +230,51 @@ def run_workload(name: str, steps: int, warmup: int, flush_mb: int, other_order:
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms = np.array([a.elapsed_time(b) for a, b in zip(starts, ends)])
+    # 2. steady state: back-to-back calls over the rotating copies, one pair of events around them all
+    for i in range(nsets):
+        step(i)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record(stream)
+    for i in range(steps):
+        step(i)
+    b.record(stream)
+    torch.cuda.synchronize()
+    ss_ms = a.elapsed_time(b) / steps
+    # 3. the dominant kernel, between fence-free events the library records around it (the two extra queue
+    # packets lengthen a step by a few microseconds, so the step time is not taken from this loop)
+    kstarts = [la.TimingEvent() for _ in range(steps)]
+    kends = [la.TimingEvent() for _ in range(steps)]
     for i in range(steps):
         evict(i & 0xFF)
         step(timing=(kstarts[i], kends[i]))
     torch.cuda.synchronize()
-    kms = np.array([a.elapsed_ms(b) for a, b in zip(kstarts, kends)])
-    nbytes, flops = algorithmic(s)
+    kms = np.array([a_.elapsed_ms(b_) for a_, b_ in zip(kstarts, kends)])
     kname, kunits, kbound = dominant_kernel(s)
     kmean_s = float(kms.mean()) * 1e-3
     mean_s = float(ms.mean()) * 1e-3
+    peak = HBM_PEAK_GBS if kbound == "hbm" else BF16_PEAK_TFLOPS
+    achieved = kunits / kmean_s / (1e9 if kbound == "hbm" else 1e12)
+    plain = not (other_order or mode or momentum is not None)
+    roof = {"bound": kbound, "achieved": achieved, "peak": peak, "unit": "GB/s" if kbound == "hbm" else "TFLOP/s",
+            "frac": achieved / peak, "traffic": traffic_per_launch(name, s) if plain else None,
+            "kernel": kname, "kernel_ms": float(kms.mean()), "kernel_ms_min": float(kms.min()),
+            "units_per_launch": kunits,
+            "step_frac": (nbytes / mean_s / 1e9 / HBM_PEAK_GBS) if kbound == "hbm"
+            else (flops / mean_s / 1e12 / BF16_PEAK_TFLOPS),
+            "steady_state_step_frac": (nbytes / (ss_ms * 1e-3) / 1e9 / HBM_PEAK_GBS) if kbound == "hbm"
+            else (flops / (ss_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS)}
     rec = dict(workload=name, mode=s["mode"], B=B, H=H, T=T, d=s["d_k"], d_h=s["d_h"], chunk=s["chunk"],
-               dtype=s["dtype"], ms_per_step=float(ms.mean()), ms_min=float(ms.min()), ms_median=float(np.median(ms)),
-               tokens_per_s=B * T / mean_s, token_heads_per_s=B * H * T / mean_s,
+               dtype=s["dtype"], o_dtype=s["o_dtype"], ms_per_step=float(ms.mean()), ms_min=float(ms.min()),
+               ms_median=float(np.median(ms)), tokens_per_s=B * T / mean_s, token_heads_per_s=B * H * T / mean_s,
+               steady_state=dict(ms_per_step=ss_ms, tokens_per_s=B * T / (ss_ms * 1e-3), input_sets=nsets,
+                                 note="back-to-back calls over rotating copies of the inputs and outputs, "
+                                      "no eviction between calls"),
                algorithmic_bytes=nbytes, algorithmic_flops=flops,
                hbm_GBps=nbytes / mean_s / 1e9, hbm_frac=nbytes / mean_s / 1e9 / HBM_PEAK_GBS,
                bf16_mfma_TFLOPs=flops / mean_s / 1e12, bf16_mfma_frac=flops / mean_s / 1e12 / BF16_PEAK_TFLOPS,
-               wall_s_including_flush=wall,
-               kernel=dict(name=kname, ms_mean=float(kms.mean()), ms_min=float(kms.min()), bound=kbound,
-                           units_per_launch=kunits,
-                           achieved=kunits / kmean_s / (1e9 if kbound == "hbm" else 1e12),
-                           unit="GB/s" if kbound == "hbm" else "TFLOP/s"))
-    del t, O, Wout, ws, flush, flush_rd
+               wall_s_including_flush=wall, roofline=roof)
+    del sets, ws, flush, flush_rd
     torch.cuda.empty_cache()
     return rec
 
@@ -267,26 +342,6 @@ def run_backward(name: str, steps: int, warmup: int, flush_mb: int, mode: str):
     return rec
 
 
-def traffic_per_launch(kernel: str):
-    """HBM bytes per launch of the dominant kernel from the committed counter
-    summary (FETCH_SIZE + WRITE_SIZE, calibrated against a copy of known
-    size), or None when there is none or the kernel source changed since."""
-    import hashlib
-    import re
-    path = os.path.join(ROOT, "profiles", "traffic_per_token_output_pass_B4H16T4096_d128.md")
-    src = os.path.join(ROOT, "linear_attention_ttt_amd", "csrc", "per_token.hip")
-    if not kernel.startswith("pt_seg_kernel") or not os.path.exists(path):
-        return None
-    text = open(path).read()
-    m_sha = re.search(r"source_sha256:\s*([0-9a-f]{64})", text)
-    m_bytes = re.search(r"hbm_bytes_per_launch:\s*([0-9]+)", text)
-    if not m_sha or not m_bytes:
-        return None
-    if hashlib.sha256(open(src, "rb").read()).hexdigest() != m_sha.group(1):
-        return None
-    return int(m_bytes.group(1))
-
-
 def cpu_baseline(name: str, mode: str, target_s: float = 12.0):
     """Time the fp64 oracle on a bounded sample of the workload: whole
     sequences of a subset of the (independent) heads, scaled to the full
@@ -302,7 +357,7 @@ def cpu_baseline(name: str, mode: str, target_s: float = 12.0):
 
     # calibrate on one head, then size the sample to about target_s seconds
     h1 = heads([0])
-    c0, w0 = time.process_time(), time.perf_counter()
+    w0 = time.perf_counter()
     oracle.forward(h1["Q"], h1["K"], h1["V"], h1["eta"], h1["W0"], s["chunk"], s["mode"], d_h=s["d_h"])
     one = time.perf_counter() - w0
     nh = int(max(1, min(BH, target_s / max(one, 1e-3))))
@@ -327,7 +382,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=workloads.HEADLINE)
     ap.add_argument("--no-others", action="store_true", help="skip the other workloads' sub-records")
-    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baselines")
     ap.add_argument("--flush-mb", type=int, default=512)
     ap.add_argument("--no-backward", action="store_true", help="skip the backward sub-records")
     ap.add_argument("--momentum", type=float, default=None,
@@ -363,13 +418,20 @@ def main():
     if a.momentum is not None:
         a.no_others = a.no_backward = True
     head = run_workload(a.workload, a.steps, a.warmup, a.flush_mb, a.other_order, a.mode, a.momentum)
+    if not a.no_cpu:
+        head["cpu_baseline"] = cpu_baseline(a.workload, head["mode"], target_s=15.0)
+    print(f"# {a.workload}: {head['ms_per_step']:.4f} ms/step", file=sys.stderr, flush=True)
     others = {}
     if not a.no_others:
         for name in workloads.WORKLOADS:
             if name == a.workload:
                 continue
             try:
-                others[name] = run_workload(name, max(10, a.steps // 2), 3, a.flush_mb, a.other_order)
+                rec = run_workload(name, max(10, a.steps // 2), 3, a.flush_mb, a.other_order)
+                if not a.no_cpu:
+                    rec["cpu_baseline"] = cpu_baseline(name, rec["mode"], target_s=8.0)
+                others[name] = rec
+                print(f"# {name}: {rec['ms_per_step']:.4f} ms/step", file=sys.stderr, flush=True)
             except Exception as e:  # a mode not built yet is reported, not fatal
                 others[name] = {"error": str(e)[:200]}
     # backward records: the headline workload, and (with the other workloads) every workload whose mode
@@ -387,12 +449,7 @@ def main():
             except Exception as e:  # reported, not fatal
                 backward[name] = {"error": str(e)[:200]}
     s = workloads.spec(a.workload, mode=head["mode"])
-    k = head["kernel"]
-    peak = HBM_PEAK_GBS if k["bound"] == "hbm" else BF16_PEAK_TFLOPS
-    roof = {"bound": k["bound"], "achieved": k["achieved"], "peak": peak, "unit": k["unit"],
-            "frac": k["achieved"] / peak, "traffic": None if (a.other_order or a.mode or a.momentum is not None) else traffic_per_launch(k["name"]),
-            "kernel": k["name"], "kernel_ms": k["ms_mean"], "units_per_launch": k["units_per_launch"],
-            "step_frac": head["hbm_frac"] if k["bound"] == "hbm" else head["bf16_mfma_frac"]}
+    roof = head.pop("roofline")
     line = {
         "metric": METRIC,
         "value": head["tokens_per_s"],
@@ -407,11 +464,13 @@ def main():
         "dtype": s["dtype"],
         "data": "synthetic (seeded; shapes and distributions of the workload)",
         "config": {"workload": a.workload, "mode": s["mode"], "B": s["B"], "H": s["H"], "T": s["T"],
-                   "d_k": s["d_k"], "d_v": s["d_v"], "d_h": s["d_h"], "chunk": s["chunk"]},
+                   "d_k": s["d_k"], "d_v": s["d_v"], "d_h": s["d_h"], "chunk": s["chunk"],
+                   "o_dtype": s["o_dtype"]},
         "bf16_mfma_frac": head["bf16_mfma_frac"],
         "token_heads_per_s": head["token_heads_per_s"],
+        "steady_state": head["steady_state"],
         "roofline": roof,
-        "cpu_baseline": None if a.no_cpu else cpu_baseline(a.workload, head["mode"]),
+        "cpu_baseline": head.get("cpu_baseline"),
         "workloads": others,
         "backward": backward,
     }

@@ -74,7 +74,7 @@ enum {
     TTT_LA_ERR_SHAPE = 2,       /* negative or zero size where one is required,       */
                                 /* or d_k != d_v where the mode needs them equal      */
     TTT_LA_ERR_CHUNK = 3,       /* chunk < 1                                          */
-    TTT_LA_ERR_DTYPE = 4,       /* io_dtype is not one of ttt_la_dtype                */
+    TTT_LA_ERR_DTYPE = 4,       /* io_dtype or o_dtype is not one of its enum values  */
     TTT_LA_ERR_MODE = 5,        /* mode is not one of ttt_la_mode                     */
     TTT_LA_ERR_UNSUPPORTED = 6, /* valid arguments that no compiled kernel covers     */
     TTT_LA_ERR_ALIAS = 7,       /* an output overlaps an input or another output      */
@@ -93,19 +93,30 @@ enum {
     TTT_LA_LARGE_CHUNK_SWIGLU_LAST_LAYER = 6
 };
 
-/* Element type of Q, K, V and O.  eta and the fast-weight state are always
- * float32. */
+/* Element type of Q, K and V (and, by default, of O).  eta and the
+ * fast-weight state are always float32. */
 enum {
     TTT_LA_FP32 = 0,
     TTT_LA_BF16 = 1
 };
 
+/* Element type of O (ttt_la_desc.o_dtype). */
+enum {
+    TTT_LA_O_AS_INPUT = 0, /* O has io_dtype                                          */
+    TTT_LA_O_FP32 = 1      /* O is float32 whatever io_dtype is: the kernels keep      */
+                           /* float32 accumulators, so this only drops the final       */
+                           /* rounding of a bf16 output, which alone costs up to half  */
+                           /* a bf16 ulp of max|o| (over 2% of the output RMS when the */
+                           /* outputs are heavy-tailed, e.g. 32 heads of 32K tokens)   */
+};
+
 /* Problem description.  d_h is the SwiGLU hidden width (ignored by the
- * linear modes).  io_dtype is TTT_LA_FP32 or TTT_LA_BF16. */
+ * linear modes).  io_dtype is TTT_LA_FP32 or TTT_LA_BF16; o_dtype is
+ * TTT_LA_O_AS_INPUT or TTT_LA_O_FP32 (any other value is ERR_DTYPE). */
 typedef struct ttt_la_desc {
     int64_t B, H, T, d_k, d_v, d_h;
     int32_t io_dtype;
-    int32_t reserved; /* must be 0 */
+    int32_t o_dtype;
 } ttt_la_desc;
 
 /*
@@ -123,7 +134,7 @@ typedef struct ttt_la_desc {
  *          or an ordering variant (3 | 4 | 5: same shapes, support and workspace as
  *          modes 0 | 1 | 2), or TTT_LA_LARGE_CHUNK_SWIGLU_LAST_LAYER (6, as mode 2)
  *   desc   sizes and io_dtype (host pointer)
- *   O      [B,H,T,d_v]  io_dtype, device (written)
+ *   O      [B,H,T,d_v]  io_dtype (float32 with o_dtype TTT_LA_O_FP32), device (written)
  *   W_out  same layout as W0, float32, device (written); W_out == W0 (in
  *          place) is allowed, any other overlap between an output and an
  *          input, or between O, W_out and the workspace, is ERR_ALIAS
@@ -285,7 +296,7 @@ const char* ttt_la_status_string(int status);
 /* ABI version of this header (incremented on incompatible change). */
 int ttt_la_abi_version(void);
 
-#define TTT_LA_ABI_VERSION 5
+#define TTT_LA_ABI_VERSION 6
 
 #ifdef __cplusplus
 }

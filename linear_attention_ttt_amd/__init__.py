@@ -19,7 +19,8 @@ import os
 
 __all__ = ["forward", "forward_momentum", "forward_momentum_raw", "backward", "backward_raw", "backward_workspace_bytes", "forward_timed_raw", "TimingEvent", "workspace_bytes", "TTTLAError", "MODES", "Desc", "lib", "library_path",
            "PER_TOKEN_LINEAR", "LARGE_CHUNK_LINEAR", "LARGE_CHUNK_SWIGLU", "PER_TOKEN_LINEAR_EXCLUSIVE",
-           "LARGE_CHUNK_LINEAR_UPDATE_FIRST", "LARGE_CHUNK_SWIGLU_UPDATE_FIRST", "LARGE_CHUNK_SWIGLU_LAST_LAYER"]
+           "LARGE_CHUNK_LINEAR_UPDATE_FIRST", "LARGE_CHUNK_SWIGLU_UPDATE_FIRST", "LARGE_CHUNK_SWIGLU_LAST_LAYER",
+           "O_AS_INPUT", "O_FP32", "make_desc"]
 
 PER_TOKEN_LINEAR = 0
 LARGE_CHUNK_LINEAR = 1
@@ -34,6 +35,7 @@ MODES = {"per_token_linear": PER_TOKEN_LINEAR, "large_chunk_linear": LARGE_CHUNK
          "large_chunk_swiglu_update_first": LARGE_CHUNK_SWIGLU_UPDATE_FIRST,
          "large_chunk_swiglu_last_layer": LARGE_CHUNK_SWIGLU_LAST_LAYER}
 FP32, BF16 = 0, 1
+O_AS_INPUT, O_FP32 = 0, 1      # ttt_la_desc.o_dtype
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_HERE, "libttt_la.so")
@@ -48,7 +50,7 @@ class TTTLAError(RuntimeError):
 class Desc(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int64), ("H", ctypes.c_int64), ("T", ctypes.c_int64),
                 ("d_k", ctypes.c_int64), ("d_v", ctypes.c_int64), ("d_h", ctypes.c_int64),
-                ("io_dtype", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("io_dtype", ctypes.c_int32), ("o_dtype", ctypes.c_int32)]
 
 
 _LIB = None
@@ -99,8 +101,18 @@ def _mode(mode) -> int:
     return MODES[mode] if isinstance(mode, str) else int(mode)
 
 
-def make_desc(B, H, T, d_k, d_v, d_h=0, io_dtype=BF16) -> Desc:
-    return Desc(B, H, T, d_k, d_v, d_h, io_dtype, 0)
+def make_desc(B, H, T, d_k, d_v, d_h=0, io_dtype=BF16, o_dtype=O_AS_INPUT) -> Desc:
+    return Desc(B, H, T, d_k, d_v, d_h, io_dtype, o_dtype)
+
+
+def _o_dtype(out_dtype, in_dtype):
+    """(torch dtype of O, o_dtype code) for the requested output dtype (None: the input dtype)."""
+    import torch
+    if out_dtype is None or out_dtype == in_dtype:
+        return in_dtype, O_AS_INPUT
+    if out_dtype == torch.float32:
+        return torch.float32, O_FP32
+    raise ValueError("out_dtype must be None, the input dtype or torch.float32")
 
 
 def workspace_bytes(desc: Desc, chunk: int, mode) -> int:
@@ -172,7 +184,7 @@ class TimingEvent:
 
 
 def forward(Q, K, V, eta, W0, chunk: int, mode, *, out=None, W_out=None, workspace=None, stream=None,
-            timing=None):
+            timing=None, out_dtype=None):
     """Run the TTT forward pass.
 
     Q, K ``[B,H,T,d_k]`` and V ``[B,H,T,d_v]`` (bfloat16 or float32, same
@@ -184,7 +196,8 @@ def forward(Q, K, V, eta, W0, chunk: int, mode, *, out=None, W_out=None, workspa
     has the library record them around the call's dominant kernel;
     ``start.elapsed_ms(stop)`` (``elapsed_time`` for torch events) then gives
     that kernel's duration.  ``stream`` is a raw hipStream_t (default: torch's
-    current stream)."""
+    current stream).  ``out_dtype=torch.float32`` returns O in float32 for
+    bfloat16 inputs (``TTT_LA_O_FP32``: no final rounding of the outputs)."""
     import torch
 
     m = _mode(mode)
@@ -214,8 +227,12 @@ def forward(Q, K, V, eta, W0, chunk: int, mode, *, out=None, W_out=None, workspa
         dh = W0.shape[2] // (3 * dk)
     elif tuple(W0.shape) != (B, H, dk, dv):
         raise ValueError("W0 must be [B,H,d_k,d_v]")
-    desc = make_desc(B, H, T, dk, dv, dh, BF16 if Q.dtype == torch.bfloat16 else FP32)
-    O = out if out is not None else torch.empty((B, H, T, dv), dtype=Q.dtype, device=dev)
+    odt, ocode = _o_dtype(out_dtype, Q.dtype)
+    desc = make_desc(B, H, T, dk, dv, dh, BF16 if Q.dtype == torch.bfloat16 else FP32, ocode)
+    if out is not None and (out.dtype != odt or tuple(out.shape) != (B, H, T, dv) or not out.is_contiguous()
+                            or out.device != dev):
+        raise ValueError("out must be a contiguous [B,H,T,d_v] tensor of the output dtype on Q's device")
+    O = out if out is not None else torch.empty((B, H, T, dv), dtype=odt, device=dev)
     Wo = W_out if W_out is not None else torch.empty_like(W0)
     nbytes = workspace_bytes(desc, chunk, m)
     ws = workspace
@@ -245,7 +262,8 @@ def forward(Q, K, V, eta, W0, chunk: int, mode, *, out=None, W_out=None, workspa
 
 
 def backward(Q, K, V, eta, W0, dO, dW_out, chunk: int, mode="per_token_linear", *, workspace=None, stream=None):
-    """Gradients of the per-token forward: given the inputs of ``forward``,
+    """Gradients of the forward in the per-token and large-chunk linear modes (both read orders of
+    each): given the inputs of ``forward``,
     ``dO`` (gradient of O, like V) and ``dW_out`` (gradient of the final
     memory, float32 like W0), return ``(dQ, dK, dV, deta, dW0)``, all
     float32.  Argument checks as in ``forward``."""
@@ -293,7 +311,7 @@ def backward(Q, K, V, eta, W0, dO, dW_out, chunk: int, mode="per_token_linear", 
 
 
 def forward_momentum(Q, K, V, eta, W0, chunk: int, momentum: float, M0=None, mode="large_chunk_linear", *,
-                     workspace=None, stream=None):
+                     workspace=None, stream=None, out_dtype=None):
     """Large-chunk linear forward with a momentum buffer (``ttt_la_forward_momentum``):
     returns ``(O, W_out, M_out)``.  ``M0`` (float32 like W0) is the buffer before the first
     chunk, zeros when None.  Same tensor checks as ``forward``."""
@@ -311,8 +329,9 @@ def forward_momentum(Q, K, V, eta, W0, chunk: int, momentum: float, M0=None, mod
         raise ValueError("Q, K, V must be bfloat16")
     B, H, T, dk = Q.shape
     dv = V.shape[3]
-    desc = make_desc(B, H, T, dk, dv, 0, BF16)
-    O = torch.empty((B, H, T, dv), dtype=Q.dtype, device=Q.device)
+    odt, ocode = _o_dtype(out_dtype, Q.dtype)
+    desc = make_desc(B, H, T, dk, dv, 0, BF16, ocode)
+    O = torch.empty((B, H, T, dv), dtype=odt, device=Q.device)
     Wo, Mo = torch.empty_like(W0), torch.empty_like(W0)
     nbytes = workspace_bytes(desc, chunk, m)
     ws = workspace

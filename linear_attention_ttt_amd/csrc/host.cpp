@@ -50,6 +50,9 @@ bool other_order(int32_t mode) {
          mode == TTT_LA_LARGE_CHUNK_SWIGLU_UPDATE_FIRST;
 }
 
+// 1 when O is float32 (asked for, or the inputs are float32 already)
+int o_f32(const ttt_la_desc& d) { return d.o_dtype == TTT_LA_O_FP32 || d.io_dtype == TTT_LA_FP32 ? 1 : 0; }
+
 int64_t state_elems(const ttt_la_desc& d, int method) {
   if (method == TTT_LA_LARGE_CHUNK_SWIGLU) return d.B * d.H * 3 * d.d_k * d.d_h;
   return d.B * d.H * d.d_k * d.d_v;
@@ -61,7 +64,7 @@ int check_problem(const ttt_la_desc* d, int64_t chunk, int32_t mode) {
   const int32_t method = method_of(mode);
   if (method < 0) return TTT_LA_ERR_MODE;
   if (d->io_dtype != TTT_LA_FP32 && d->io_dtype != TTT_LA_BF16) return TTT_LA_ERR_DTYPE;
-  if (d->reserved != 0) return TTT_LA_ERR_SHAPE;
+  if (d->o_dtype != TTT_LA_O_AS_INPUT && d->o_dtype != TTT_LA_O_FP32) return TTT_LA_ERR_DTYPE;
   if (d->B < 1 || d->H < 1 || d->T < 0 || d->d_k < 1 || d->d_v < 1) return TTT_LA_ERR_SHAPE;
   if (method == TTT_LA_LARGE_CHUNK_SWIGLU && (d->d_h < 1 || d->d_k != d->d_v)) return TTT_LA_ERR_SHAPE;
   int64_t x;
@@ -91,7 +94,7 @@ bool supported(const ttt_la_desc& d, int64_t chunk, int32_t mode) {
 size_t workspace_for(const ttt_la_desc& d, int64_t chunk, int32_t mode) {
   switch (method_of(mode)) {
     case TTT_LA_PER_TOKEN_LINEAR:
-      return ttt::per_token_workspace(d.B, d.H, d.T, d.d_k, d.d_v, d.io_dtype);
+      return ttt::per_token_workspace(d.B, d.H, d.T, d.d_k, d.d_v, d.io_dtype, o_f32(d));
     case TTT_LA_LARGE_CHUNK_LINEAR:
       return ttt::large_chunk_linear_workspace(d.B, d.H, d.T, d.d_k, d.d_v, chunk);
     case TTT_LA_LARGE_CHUNK_SWIGLU:
@@ -112,7 +115,7 @@ const char* ttt_la_status_string(int s) {
     case TTT_LA_ERR_NULL: return "a required pointer is NULL";
     case TTT_LA_ERR_SHAPE: return "invalid shape";
     case TTT_LA_ERR_CHUNK: return "chunk must be >= 1";
-    case TTT_LA_ERR_DTYPE: return "io_dtype is not TTT_LA_FP32 or TTT_LA_BF16";
+    case TTT_LA_ERR_DTYPE: return "io_dtype is not TTT_LA_FP32 or TTT_LA_BF16, or o_dtype is not TTT_LA_O_AS_INPUT or TTT_LA_O_FP32";
     case TTT_LA_ERR_MODE: return "unknown mode";
     case TTT_LA_ERR_UNSUPPORTED: return "no compiled kernel supports this shape, dtype or chunk";
     case TTT_LA_ERR_ALIAS: return "an output overlaps an input or another output";
@@ -148,7 +151,7 @@ static int forward_impl(const void* Q, const void* K, const void* V, const float
   const Range rV = range(V, ntok * d.d_v * es), rE = range(eta, ntok * 4);
   const int32_t method = method_of(mode);
   const Range rW0 = range(W0, (size_t)state_elems(d, method) * 4);
-  const Range rO = range(O, ntok * d.d_v * es);
+  const Range rO = range(O, ntok * d.d_v * (o_f32(d) ? 4 : es));
   const Range rWo = range(W_out, (size_t)state_elems(d, method) * 4);
   const Range rWs = range(workspace, need);
   const Range ins[5] = {rQ, rK, rV, rE, rW0};
@@ -176,11 +179,12 @@ static int forward_impl(const void* Q, const void* K, const void* V, const float
   const int other = other_order(mode) ? 1 : 0;
   if (method == TTT_LA_PER_TOKEN_LINEAR) {
     ttt::PerTokenArgs a{Q, K, V, eta, W0, O, W_out, workspace, d.B, d.H, d.T, d.d_k, d.d_v, chunk, d.io_dtype,
-                        other};
+                        other, o_f32(d)};
     e = ttt::launch_per_token(a, s, tm);
   } else {
     ttt::LargeChunkArgs a{Q, K, V, eta, W0, O, W_out, workspace, d.B, d.H, d.T, d.d_k, d.d_v, d.d_h, chunk, d.io_dtype,
-                          other, mode == TTT_LA_LARGE_CHUNK_SWIGLU_LAST_LAYER ? 1 : 0, M0, M_out, momentum};
+                          other, mode == TTT_LA_LARGE_CHUNK_SWIGLU_LAST_LAYER ? 1 : 0, M0, M_out, momentum,
+                          o_f32(d)};
     e = method == TTT_LA_LARGE_CHUNK_LINEAR ? ttt::launch_large_chunk_linear(a, s, tm)
                                             : ttt::launch_large_chunk_swiglu(a, s, tm);
   }
@@ -215,6 +219,7 @@ int ttt_la_forward(const void* Q, const void* K, const void* V, const float* eta
 
 static bool backward_ok(const ttt_la_desc& d, int64_t chunk, int32_t mode) {
   if (!supported(d, chunk, mode)) return false;
+  if (d.o_dtype != TTT_LA_O_AS_INPUT) return false;   // dO has io_dtype
   switch (method_of(mode)) {
     case TTT_LA_PER_TOKEN_LINEAR: return ttt::per_token_backward_supported(d.d_k, d.d_v, chunk, d.io_dtype);
     case TTT_LA_LARGE_CHUNK_LINEAR: return d.io_dtype == TTT_LA_BF16;

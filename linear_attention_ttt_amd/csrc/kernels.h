@@ -26,6 +26,7 @@ struct PerTokenArgs {
   int64_t B, H, T, DK, DV, chunk;
   int dtype;      // 0 = fp32, 1 = bf16
   int exclusive;  // 1: a query reads before its own token's step
+  int o_f32;      // 1: O is float32 (bf16 inputs; float32 inputs always give float32 O)
 };
 
 // Sequence segments of the bf16 per-token path (segments per head, tokens per segment).
@@ -35,7 +36,7 @@ struct SegPlan {
 // a segment holds at most max_seg_tokens tokens (its views are addressed with 32-bit offsets)
 SegPlan per_token_seg_plan(int64_t BH, int64_t T, int64_t dk, int64_t max_seg_tokens = (int64_t)1 << 22);
 bool per_token_supported(int64_t dk, int64_t dv, int64_t chunk, int dtype);
-size_t per_token_workspace(int64_t B, int64_t H, int64_t T, int64_t dk, int64_t dv, int dtype);
+size_t per_token_workspace(int64_t B, int64_t H, int64_t T, int64_t dk, int64_t dv, int dtype, int o_f32);
 hipError_t launch_per_token(const PerTokenArgs& a, hipStream_t stream, const Timing& tm);
 
 // Backward (bf16 inputs): gradients of O and of the final memory in, float32 gradients of Q, K, V,
@@ -80,6 +81,7 @@ struct LargeChunkArgs {
   const float* M0 = nullptr;
   float* M_out = nullptr;
   float momentum = 0.f;
+  int o_f32 = 0;  // 1: O is float32
 };
 
 bool large_chunk_linear_supported(int64_t dk, int64_t dv, int64_t chunk, int dtype);

@@ -283,9 +283,10 @@ struct LactReadCfg {
   static constexpr int SWZ = D / 8 >= 16 ? 15 : D / 8 - 1;
 };
 
-template <int D>
+// OF32: float32 outputs, stored straight from the accumulators (16 bytes per lane: 4 columns of one token).
+template <int D, bool OF32>
 __global__ __launch_bounds__(256, 2) void lact_read_kernel(const bf16* __restrict__ Q, const float* __restrict__ wprev_t,
-                                                           bf16* __restrict__ O, int T, int chunk, int nchunks,
+                                                           void* __restrict__ O, int T, int chunk, int nchunks,
                                                            int parts, int part_len) {
   using Cfg = LactReadCfg<D>;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -314,11 +315,13 @@ __global__ __launch_bounds__(256, 2) void lact_read_kernel(const bf16* __restric
   }
   unsigned char* ring = smem + 2 * Cfg::W_BYTES + w * LR_STAGES * Cfg::QW_BYTES;
   const bf16* Qh = Q + (size_t)bh * T * D;
-  bf16* Oh = O + (size_t)bh * T * D;
+  const size_t oes = OF32 ? 4 : 2;
+  unsigned char* Oh = (unsigned char*)O + (size_t)bh * T * D * oes;
   const int ntiles = (t1 - t0 + 63) / 64;
   // one buffer view of this part's queries and outputs (rows past its end read 0 / are dropped)
   const __amdgpu_buffer_rsrc_t rq = make_rsrc(Qh + (size_t)t0 * D, (long long)(t1 - t0) * Cfg::ROWB);
-  const __amdgpu_buffer_rsrc_t ro = make_rsrc(Oh + (size_t)t0 * D, (long long)(t1 - t0) * Cfg::ROWB);
+  const __amdgpu_buffer_rsrc_t ro = make_rsrc(Oh + (size_t)t0 * D * oes, (long long)(t1 - t0) * D * oes);
+  constexpr int ST = OF32 ? Cfg::MT : Cfg::QI;    // output stores per wave per tile
   auto issue = [&](int i) {
     unsigned char* dst = ring + (i % LR_STAGES) * Cfg::QW_BYTES;
     const unsigned t = (unsigned)i * 64 * Cfg::ROWB;
@@ -354,11 +357,11 @@ __global__ __launch_bounds__(256, 2) void lact_read_kernel(const bf16* __restric
     if (i == 0)
       wait_vm<2 * Cfg::QI>();
     else if (i == 1)
-      wait_vm<3 * Cfg::QI>();
+      wait_vm<2 * Cfg::QI + ST>();
     else if (i == 2)
-      wait_vm<4 * Cfg::QI>();
+      wait_vm<2 * Cfg::QI + 2 * ST>();
     else
-      wait_vm<5 * Cfg::QI>();
+      wait_vm<2 * Cfg::QI + 3 * ST>();
     issue(i + LR_STAGES - 1);
     unsigned char* qs = ring + (i % LR_STAGES) * Cfg::QW_BYTES;   // this wave's 16 rows
     bf16x8 qop[Cfg::KT];
@@ -374,16 +377,22 @@ __global__ __launch_bounds__(256, 2) void lact_read_kernel(const bf16* __restric
         acc = mfma16(*(const bf16x8*)(wh + m * 16 * Cfg::ROWB + nat[ks]), qop[ks], acc);
         acc = mfma16(*(const bf16x8*)(wl + m * 16 * Cfg::ROWB + nat[ks]), qop[ks], acc);
       }
-      const int piece = 2 * m + (g >> 1);
-      *(bf16x4*)(qs + li * Cfg::ROWB + ((piece ^ (li & Cfg::SWZ)) << 4) + (g & 1) * 8) =
-          to_bf16x4(acc[0], acc[1], acc[2], acc[3]);
+      if constexpr (OF32) {
+        buf_store16(ro, (unsigned)(((i * 64 + 16 * w + li) * D + 16 * m + 4 * g) * 4), __builtin_bit_cast(u32x4, acc));
+      } else {
+        const int piece = 2 * m + (g >> 1);
+        *(bf16x4*)(qs + li * Cfg::ROWB + ((piece ^ (li & Cfg::SWZ)) << 4) + (g & 1) * 8) =
+            to_bf16x4(acc[0], acc[1], acc[2], acc[3]);
+      }
     }
-    const unsigned t = (unsigned)i * 64 * Cfg::ROWB;
-    u32x4 v[Cfg::QI];
+    if constexpr (!OF32) {
+      const unsigned t = (unsigned)i * 64 * Cfg::ROWB;
+      u32x4 v[Cfg::QI];
 #pragma unroll
-    for (int k = 0; k < Cfg::QI; ++k) v[k] = *(const u32x4*)(qs + k * 1024 + 16 * l);
+      for (int k = 0; k < Cfg::QI; ++k) v[k] = *(const u32x4*)(qs + k * 1024 + 16 * l);
 #pragma unroll
-    for (int k = 0; k < Cfg::QI; ++k) buf_store16(ro, t + qoff[k], v[k]);
+      for (int k = 0; k < Cfg::QI; ++k) buf_store16(ro, t + qoff[k], v[k]);
+    }
   }
   wait_vm<0>();
 }
@@ -411,7 +420,8 @@ hipError_t launch_lact(const LargeChunkArgs& a, hipStream_t stream, const Timing
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || nchunks == 0) return e;
   using Cfg = LactReadCfg<D>;
-  e = hipFuncSetAttribute((const void*)lact_read_kernel<D>, hipFuncAttributeMaxDynamicSharedMemorySize, Cfg::LDS);
+  auto kread = a.o_f32 ? lact_read_kernel<D, true> : lact_read_kernel<D, false>;
+  e = hipFuncSetAttribute((const void*)kread, hipFuncAttributeMaxDynamicSharedMemorySize, Cfg::LDS);
   if (e != hipSuccess) return e;
   // about a quarter chunk (at least 256 tokens) per workgroup
   int part_len = (chunk + 3) / 4;
@@ -419,8 +429,8 @@ hipError_t launch_lact(const LargeChunkArgs& a, hipStream_t stream, const Timing
   part_len = (part_len + 63) / 64 * 64;
   part_len = part_len > (1 << 20) ? (1 << 20) : part_len;   // 32-bit byte offsets within a part
   const int parts = (chunk + part_len - 1) / part_len;
-  hipLaunchKernelGGL(lact_read_kernel<D>, dim3(BH * nchunks * parts), dim3(256), Cfg::LDS, stream, (const bf16*)a.Q,
-                     wprev, (bf16*)a.O, T, chunk, nchunks, parts, part_len);
+  hipLaunchKernelGGL(kread, dim3(BH * nchunks * parts), dim3(256), Cfg::LDS, stream, (const bf16*)a.Q, wprev, a.O, T,
+                     chunk, nchunks, parts, part_len);
   return hipGetLastError();
 }
 

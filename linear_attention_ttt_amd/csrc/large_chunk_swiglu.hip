@@ -28,6 +28,7 @@
 //    through LDS; products use the bf16 hi + lo split of the weights and of
 //    H so the only visible rounding is that of the bf16 output.
 #include <algorithm>
+#include <cstdlib>
 
 #include "device_common.h"
 #include "kernels.h"
@@ -101,7 +102,7 @@ __global__ __launch_bounds__(SW_WAVES * 64, 1) void swiglu_recur_kernel(
     const bf16* __restrict__ K, const bf16* __restrict__ V, const float* __restrict__ eta,
     const float* __restrict__ W0, float* __restrict__ Wout, bf16* __restrict__ states, float* __restrict__ ss2,
     unsigned* __restrict__ counters, unsigned* __restrict__ errflag, int T_in, int chunk, int nchunks_in, int head0,
-    int update_first, int last_only, int par_nchunks) {
+    int update_first, int last_only, int par_nchunks, int spin_limit, unsigned target_extra) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
   RecurLds& S = *reinterpret_cast<RecurLds*>(smem_raw);
   constexpr int NT = SW_WAVES * 64;
@@ -392,11 +393,13 @@ __global__ __launch_bounds__(SW_WAVES * 64, 1) void swiglu_recur_kernel(
     __syncthreads();
     if (tid == 0 && !last_only) {
       __hip_atomic_fetch_add(&counters[bh], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      const unsigned target = (unsigned)SW_NSL * (unsigned)(c + 1);
+      // bounded wait: on giving up the call's error flag is raised (the read kernel then fills every
+      // output with NaN) and the workgroup carries on, so every kernel still ends
+      const unsigned target = (unsigned)SW_NSL * (unsigned)(c + 1) + target_extra;
       int spins = 0;
       while (__hip_atomic_load(&counters[bh], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
         __builtin_amdgcn_s_sleep(2);
-        if (++spins > SW_SPIN_LIMIT) {
+        if (++spins > spin_limit) {
           __hip_atomic_store(errflag, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           break;
         }
@@ -527,10 +530,16 @@ __device__ __forceinline__ int w2_swz(int row) { return (row >> 2) & 3; }
 // ~6 % slower, the lone wave waits on its own LDS reads).
 constexpr int SW_RW = 8;                  // waves per read workgroup
 constexpr int SW_RT = SW_TT / SW_RW;      // tokens per wave (2 tiles of 16)
+// OF32: float32 outputs (16 bytes per lane: 4 consecutive columns of one token).
+// errflag: raised by the recurrence when a cross-workgroup wait gave up; then every output of the call
+// and every head's final weights are filled with NaN instead.
+template <bool OF32>
 __global__ __launch_bounds__(SW_RW * 64, 1) void swiglu_read_kernel(const bf16* __restrict__ Q,
                                                                     const bf16* __restrict__ states,
-                                                                    bf16* __restrict__ O, int T, int chunk,
-                                                                    int nchunks, int tiles) {
+                                                                    void* __restrict__ O, int T, int chunk,
+                                                                    int nchunks, int tiles,
+                                                                    const unsigned* __restrict__ errflag,
+                                                                    float* __restrict__ Wout) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
   ReadLds& L = *reinterpret_cast<ReadLds*>(smem_raw);
   constexpr int D = SW_D, DH = SW_DH, NTH = SW_RW * 64, TT = SW_RT / 16;
@@ -542,9 +551,27 @@ __global__ __launch_bounds__(SW_RW * 64, 1) void swiglu_read_kernel(const bf16* 
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g = l >> 4, li = l & 15;
   const int cend = min((c + 1) * chunk, T);
   const int t0 = c * chunk + tile * SW_TT;
+  const size_t P = (size_t)D * DH;
+  if (__hip_atomic_load(errflag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u) {
+    // the recurrence could not complete: no output of this call is valid
+    constexpr int OES = OF32 ? 4 : 2;
+    const float nan = __builtin_nanf("");
+    if (t0 < cend) {
+      unsigned char* Ot = (unsigned char*)O + ((size_t)bh * T + t0) * D * OES;
+      const int n = (cend - t0 < SW_TT ? cend - t0 : SW_TT) * D;
+      for (int i = threadIdx.x; i < n; i += NTH) {
+        if constexpr (OF32)
+          ((float*)Ot)[i] = nan;
+        else
+          ((bf16*)Ot)[i] = (bf16)nan;
+      }
+    }
+    if (c == 0 && tile == 0)
+      for (int i = threadIdx.x; i < 3 * (int)P; i += NTH) Wout[(size_t)bh * 3 * P + i] = nan;
+    return;
+  }
   if (t0 >= cend) return;   // uniform over the workgroup, before any barrier
   const bf16* st = states + ((size_t)bh * nchunks + c) * SW_STATE;
-  const size_t P = (size_t)D * DH;
 
   // this wave's queries as B operands (col = token, k = 8 consecutive d)
   const bf16* Qh = Q + (size_t)bh * T * D;
@@ -653,15 +680,20 @@ __global__ __launch_bounds__(SW_RW * 64, 1) void swiglu_read_kernel(const bf16* 
       }
     }
   }
-  bf16* Oh = O + (size_t)bh * T * D;
-  const __amdgpu_buffer_rsrc_t ro = make_rsrc(Oh + (size_t)t0 * D, ((long long)cend - t0) * D * 2);
+  constexpr int OES = OF32 ? 4 : 2;
+  unsigned char* Oh = (unsigned char*)O + (size_t)bh * T * D * OES;
+  const __amdgpu_buffer_rsrc_t ro = make_rsrc(Oh + (size_t)t0 * D * OES, ((long long)cend - t0) * D * OES);
 #pragma unroll
   for (int tt = 0; tt < TT; ++tt)
 #pragma unroll
     for (int nt = 0; nt < 8; ++nt) {
-      const bf16x4 o = to_bf16x4(oacc[nt][tt][0], oacc[nt][tt][1], oacc[nt][tt][2], oacc[nt][tt][3]);
-      __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(uint2v, o), ro,
-                                            (unsigned)((SW_RT * w + 16 * tt + li) * D * 2 + (16 * nt + 4 * g) * 2), 0, 0);
+      const unsigned off = (unsigned)(((SW_RT * w + 16 * tt + li) * D + 16 * nt + 4 * g) * OES);
+      if constexpr (OF32) {
+        buf_store16(ro, off, __builtin_bit_cast(u32x4, oacc[nt][tt]));
+      } else {
+        const bf16x4 o = to_bf16x4(oacc[nt][tt][0], oacc[nt][tt][1], oacc[nt][tt][2], oacc[nt][tt][3]);
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(uint2v, o), ro, off, 0, 0);
+      }
     }
 }
 
@@ -696,6 +728,32 @@ size_t large_chunk_swiglu_workspace(int64_t B, int64_t H, int64_t T, int64_t d, 
   (void)d;
   (void)dh;
   return sw_layout(B * H, (T + chunk - 1) / chunk).total;
+}
+
+// O_c = f_{W_{c-1}}(Q_c) for every chunk, from the stored states
+static hipError_t launch_read(const LargeChunkArgs& a, const bf16* states, int nchunks, const unsigned* err,
+                              hipStream_t stream) {
+  const size_t lds_o = sizeof(ReadLds);
+  auto kread = a.o_f32 ? swiglu_read_kernel<true> : swiglu_read_kernel<false>;
+  hipError_t e = hipFuncSetAttribute((const void*)kread, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_o);
+  if (e != hipSuccess) return e;
+  const int chunk = (int)a.chunk, tiles = (chunk + SW_TT - 1) / SW_TT;
+  hipLaunchKernelGGL(kread, dim3((unsigned)(a.B * a.H) * nchunks * tiles), dim3(SW_RW * 64), lds_o, stream,
+                     (const bf16*)a.Q, states, a.O, (int)a.T, chunk, nchunks, tiles, err, a.W_out);
+  return hipGetLastError();
+}
+
+// Test hook: with TTT_LA_TEST_SPIN_GIVEUP set to a nonzero integer in the environment, every
+// cross-workgroup wait of the recurrence waits for a count that never arrives and gives up after that
+// many sleeps, so the error path (NaN outputs) can be checked while every kernel still ends.
+static void spin_params(int* limit, unsigned* extra) {
+  *limit = SW_SPIN_LIMIT;
+  *extra = 0u;
+  const char* v = getenv("TTT_LA_TEST_SPIN_GIVEUP");
+  if (v && atoi(v) > 0) {
+    *limit = atoi(v) < 4096 ? atoi(v) : 4096;
+    *extra = 1u << 30;
+  }
 }
 
 hipError_t launch_large_chunk_swiglu(const LargeChunkArgs& a, hipStream_t stream, const Timing& tm) {
@@ -734,7 +792,7 @@ hipError_t launch_large_chunk_swiglu(const LargeChunkArgs& a, hipStream_t stream
     if ((e = mark(tm.start, stream)) != hipSuccess) return e;
     hipLaunchKernelGGL(swiglu_recur_kernel, dim3(BH * nchunks * SW_NSL), dim3(SW_WAVES * 64), lds_r, stream,
                        (const bf16*)a.K, (const bf16*)a.V, a.eta, a.W0, (float*)states, states, ss2, counters, err, T,
-                       chunk, nchunks, 0, 0, 1, nchunks);
+                       chunk, nchunks, 0, 0, 1, nchunks, SW_SPIN_LIMIT, 0u);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if ((e = mark(tm.stop, stream)) != hipSuccess) return e;
     const long long np = (long long)BH * SW_D * (SW_DH / 8);
@@ -745,19 +803,16 @@ hipError_t launch_large_chunk_swiglu(const LargeChunkArgs& a, hipStream_t stream
     hipLaunchKernelGGL(swiglu_ll_fill_kernel, dim3((unsigned)((nf + 255) / 256)), dim3(256), 0, stream, a.W0, states,
                        a.W_out, BH, nchunks);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    const size_t lds_o = sizeof(ReadLds);
-    e = hipFuncSetAttribute((const void*)swiglu_read_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_o);
-    if (e != hipSuccess) return e;
-    const int tiles = (chunk + SW_TT - 1) / SW_TT;
-    hipLaunchKernelGGL(swiglu_read_kernel, dim3(BH * nchunks * tiles), dim3(SW_RW * 64), lds_o, stream,
-                       (const bf16*)a.Q, (const bf16*)states, (bf16*)a.O, T, chunk, nchunks, tiles);
-    return hipGetLastError();
+    return launch_read(a, states, nchunks, err, stream);
   }
   const bf16* Kp = (const bf16*)a.K;
   const bf16* Vp = (const bf16*)a.V;
   const float* Ep = a.eta;
   const float* W0p = a.W0;
   float* Wo = a.W_out;
+  int spin_limit;
+  unsigned spin_extra;
+  spin_params(&spin_limit, &spin_extra);
   if ((e = mark(tm.start, stream)) != hipSuccess) return e;   // the recurrence: the sequential part
   for (int h0 = 0; h0 < BH; h0 += heads_per_launch) {
     const int nh = std::min(heads_per_launch, BH - h0);
@@ -765,20 +820,14 @@ hipError_t launch_large_chunk_swiglu(const LargeChunkArgs& a, hipStream_t stream
     int pn = 0;
     void* args[] = {(void*)&Kp, (void*)&Vp, (void*)&Ep, (void*)&W0p, (void*)&Wo, (void*)&states, (void*)&ss2,
                     (void*)&counters, (void*)&err, (void*)&Ti, (void*)&ci, (void*)&nci, (void*)&hi, (void*)&uf,
-                    (void*)&lo, (void*)&pn};
+                    (void*)&lo, (void*)&pn, (void*)&spin_limit, (void*)&spin_extra};
     e = hipLaunchCooperativeKernel((const void*)swiglu_recur_kernel, dim3(nh * SW_NSL), dim3(SW_WAVES * 64), args,
                                    (unsigned)lds_r, stream);
     if (e != hipSuccess) return e;
   }
   if ((e = mark(tm.stop, stream)) != hipSuccess) return e;
   if (nchunks == 0) return hipSuccess;
-  const size_t lds_o = sizeof(ReadLds);
-  e = hipFuncSetAttribute((const void*)swiglu_read_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_o);
-  if (e != hipSuccess) return e;
-  const int tiles = (chunk + SW_TT - 1) / SW_TT;
-  hipLaunchKernelGGL(swiglu_read_kernel, dim3(BH * nchunks * tiles), dim3(SW_RW * 64), lds_o, stream, (const bf16*)a.Q,
-                     (const bf16*)states, (bf16*)a.O, T, chunk, nchunks, tiles);
-  return hipGetLastError();
+  return launch_read(a, states, nchunks, err, stream);
 }
 
 }  // namespace ttt

@@ -922,9 +922,12 @@ SegPlan per_token_seg_plan(int64_t BH, int64_t T, int64_t dk, int64_t max_seg_to
   return SegPlan{(int)nseg, (int)(tiles * 64)};
 }
 
-size_t per_token_workspace(int64_t B, int64_t H, int64_t T, int64_t dk, int64_t dv, int dtype) {
+// float32 output rows of a segment stay below 2^31 bytes: 2^21 tokens at d = 128
+constexpr int64_t F32_OUT_MAX_SEG_TOKENS = (int64_t)1 << 21;
+
+size_t per_token_workspace(int64_t B, int64_t H, int64_t T, int64_t dk, int64_t dv, int dtype, int o_f32) {
   if (dtype != 1) return 0;
-  const SegPlan sp = per_token_seg_plan(B * H, T, dk);
+  const SegPlan sp = per_token_seg_plan(B * H, T, dk, o_f32 ? F32_OUT_MAX_SEG_TOKENS : ((int64_t)1 << 22));
   return sp.nseg > 1 ? (size_t)sp.nseg * (size_t)(B * H) * (size_t)dk * (size_t)dv * sizeof(float) : 0;
 }
 
@@ -963,9 +966,11 @@ static hipError_t launch_seg_pass(const SegArgs& A, int BH, bool excl, hipStream
 template <int D>
 static hipError_t launch_seg(const PerTokenArgs& a, hipStream_t stream, const Timing& tm) {
   const int BH = (int)(a.B * a.H);
-  const SegPlan sp = per_token_seg_plan(BH, a.T, D);
+  const SegPlan sp = per_token_seg_plan(BH, a.T, D, a.o_f32 ? F32_OUT_MAX_SEG_TOKENS : ((int64_t)1 << 22));
+  // (SegArgs.O is typed bf16; with float32 outputs the kernel writes floats through it)
   const SegArgs A{(const bf16*)a.Q, (const bf16*)a.K, (const bf16*)a.V, a.eta, a.W0, (floatx4*)a.ws,
                   (bf16*)a.O, a.W_out, (int)a.T, sp.nseg, sp.seg_len};
+  if (a.o_f32) return launch_seg_pass<D, false, 0, true>(A, BH, a.exclusive != 0, stream, tm);
   return launch_seg_pass<D, false, 0>(A, BH, a.exclusive != 0, stream, tm);
 }
 

@@ -20,7 +20,13 @@ def to_device(x, s, dev="cuda"):
     return t
 
 
+def out_dtype(s):
+    """torch dtype of O for workload parameters ``s``."""
+    return torch.float32 if s.get("o_dtype", s["dtype"]) == "fp32" else torch.bfloat16
+
+
 def run(t, s, chunk=None, **kw):
+    kw.setdefault("out_dtype", out_dtype(s))
     O, W = la.forward(t["Q"], t["K"], t["V"], t["eta"], t["W0"], s["chunk"] if chunk is None else chunk,
                       s["mode"], **kw)
     torch.cuda.synchronize()

@@ -47,7 +47,7 @@ def test_exports_every_declared_symbol():
 
 @needs_lib
 def test_version_and_status_strings():
-    assert la.lib().ttt_la_abi_version() == 5
+    assert la.lib().ttt_la_abi_version() == 6
     for s in range(10):
         assert la.status_string(s) and la.status_string(s) != "unknown status"
     assert la.status_string(99) == "unknown status"
@@ -92,10 +92,45 @@ def test_invalid_shapes(desc, mode, code):
 
 
 @needs_lib
-def test_reserved_field_must_be_zero():
-    d = la.make_desc(1, 1, 8, 64, 64)
-    d.reserved = 1
-    assert call(desc=d) == 2
+@pytest.mark.parametrize("o_dtype", [2, -1, 7])
+def test_output_dtype_outside_enum(o_dtype):
+    assert call(desc=la.make_desc(1, 1, 8, 64, 64, 0, la.BF16, o_dtype)) == 4
+
+
+@needs_lib
+def test_float32_output_range_checked_for_aliasing():
+    # with float32 O the output spans twice the bytes of a bf16 one: it reaches into K placed just after
+    desc = la.make_desc(1, 2, 128, 64, 64, 0, la.BF16, la.O_FP32)
+    obytes16 = 1 * 2 * 128 * 64 * 2
+    assert call(O=ptr(1) - obytes16, desc=desc) == 7
+    # just clear of K it passes the alias check and stops at the (missing) workspace, before any HIP call
+    assert la.workspace_bytes(desc, 64, 0) > 0
+    assert call(O=ptr(1) - 2 * obytes16 - 256, desc=desc, ws=None, ws_bytes=0, chunk=64) == 8
+
+
+@needs_lib
+def test_backward_needs_output_in_input_dtype():
+    d = la.make_desc(1, 2, 256, 128, 128, 0, la.BF16, la.O_FP32)
+    assert la.backward_workspace_bytes(d, 64, "per_token_linear") == 0
+    r = la.backward_raw(ptr(0), ptr(1), ptr(2), ptr(3), ptr(4), ptr(5), ptr(6), 64, "per_token_linear", d, ptr(7),
+                        ptr(8), ptr(9), ptr(10), ptr(11), ptr(12), 1 << 33, None)
+    assert r == 6
+
+
+@needs_lib
+def test_float32_output_workspace():
+    # per-token: float32 rows cap a segment at 2^21 tokens, so a long sequence may take more segments
+    for o in (la.O_AS_INPUT, la.O_FP32):
+        d = la.make_desc(1, 32, 32768, 128, 128, 0, la.BF16, o)
+        assert la.workspace_bytes(d, 128, "per_token_linear") > 0
+    one = la.make_desc(1, 1, 1 << 22, 128, 128, 0, la.BF16, la.O_AS_INPUT)
+    one32 = la.make_desc(1, 1, 1 << 22, 128, 128, 0, la.BF16, la.O_FP32)
+    assert la.workspace_bytes(one32, 64, 0) >= la.workspace_bytes(one, 64, 0)
+    # the large-chunk modes' workspace does not depend on the output dtype
+    for mode, dd, chunk in ((1, la.make_desc(1, 12, 196608, 64, 64, 0, la.BF16), 4096),
+                            (2, la.make_desc(2, 8, 32768, 128, 128, 256, la.BF16), 2048)):
+        d32 = la.make_desc(dd.B, dd.H, dd.T, dd.d_k, dd.d_v, dd.d_h, la.BF16, la.O_FP32)
+        assert la.workspace_bytes(d32, chunk, mode) == la.workspace_bytes(dd, chunk, mode)
 
 
 @needs_lib

@@ -37,9 +37,10 @@ WORKLOADS = {
     "per_token_bf16_B4H16T4096_d128_c64": dict(
         mode="per_token_linear", B=4, H=16, T=4096, d_k=128, d_v=128, d_h=0, chunk=64,
         dtype="bf16", eta="sigmoid", eta_scale=0.1, w0="normal", w0_std=0.02),
+    # O in float32: rounding even the exact outputs of these 32 heads to bf16 would exceed 2% of their RMS
     "per_token_bf16_B1H32T32768_d128_c128": dict(
         mode="per_token_linear", B=1, H=32, T=32768, d_k=128, d_v=128, d_h=0, chunk=128,
-        dtype="bf16", eta="sigmoid", eta_scale=0.1, w0="normal", w0_std=0.02),
+        dtype="bf16", eta="sigmoid", eta_scale=0.1, w0="normal", w0_std=0.02, o_dtype="fp32"),
     "large_chunk_linear_bf16_B1H12T196608_d64_c4096": dict(
         mode="large_chunk_linear", B=1, H=12, T=196608, d_k=64, d_v=64, d_h=0, chunk=4096,
         dtype="bf16", eta="uniform", eta_scale=0.05, w0="normal", w0_std=0.02),
@@ -48,32 +49,36 @@ WORKLOADS = {
         dtype="bf16", eta="uniform", eta_scale=0.02, w0="normal", w0_std=0.02),
 }
 
-# The workload the headline throughput is quoted on.
-HEADLINE = "per_token_bf16_B4H16T4096_d128_c64"
+# The workload the headline throughput is quoted on: the largest of the per-token mode.
+HEADLINE = "per_token_bf16_B1H32T32768_d128_c128"
 
 
 def bf16_round(x: np.ndarray) -> np.ndarray:
     """Round float32 values to the nearest bfloat16 (ties to even) and
-    return them as float32 (finite inputs only)."""
-    b = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
-    r = ((b + 0x7FFF + ((b >> 16) & 1)) >> 16) << 16
-    return r.astype(np.uint32).view(np.float32)
+    return them as float32 (finite inputs only: for those the sum below
+    stays under 2^32)."""
+    b = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    r = (b + np.uint32(0x7FFF) + ((b >> np.uint32(16)) & np.uint32(1))) & np.uint32(0xFFFF0000)
+    return r.view(np.float32)
 
 
 def spec(name: str, **overrides) -> dict:
-    """A copy of a named workload's parameters with overrides applied."""
+    """A copy of a named workload's parameters with overrides applied.
+    ``o_dtype`` is the element type of the outputs O (the input dtype
+    unless the workload names another)."""
     s = dict(WORKLOADS[name])
+    s.setdefault("o_dtype", s["dtype"])
     s.update(overrides)
     return s
 
 
 def make_spec(mode, B, H, T, d_k, d_v=None, d_h=0, chunk=64, dtype="bf16",
-              eta="uniform", eta_scale=0.1, w0="normal", w0_std=0.02) -> dict:
+              eta="uniform", eta_scale=0.1, w0="normal", w0_std=0.02, o_dtype=None) -> dict:
     """Build a workload parameter dict for an arbitrary shape."""
     assert mode in MODES
     return dict(mode=mode, B=B, H=H, T=T, d_k=d_k, d_v=d_k if d_v is None else d_v,
                 d_h=d_h, chunk=chunk, dtype=dtype, eta=eta, eta_scale=eta_scale,
-                w0=w0, w0_std=w0_std)
+                w0=w0, w0_std=w0_std, o_dtype=dtype if o_dtype is None else o_dtype)
 
 
 def generate(s: dict, seed: int = 0) -> dict:
