@@ -6,6 +6,9 @@ benchmark's CPU-baseline leg, never by the library or its binding.
 """
 from .ttt_oracle import (  # noqa: F401
     NORM_EPS,
+    NS_COEFFS,
+    NS_EPS,
+    NS_STEPS,
     backward,
     forward,
     large_chunk_linear,
@@ -13,6 +16,7 @@ from .ttt_oracle import (  # noqa: F401
     large_chunk_swiglu,
     linear_binding_grad,
     linear_binding_loss,
+    newton_schulz5,
     normalize_columns,
     per_token_linear,
     per_token_linear_backward,

@@ -308,8 +308,41 @@ def large_chunk_linear(Q, K, V, eta, W0, chunk, normalize=True, read_first=True,
     return O, W
 
 
+# Coefficients of the quintic Newton-Schulz iteration of the Muon optimizer
+# (K. Jordan et al., "Muon: An optimizer for hidden layers in neural
+# networks", 2024): each step maps every singular value s of the normalised
+# matrix to a s + b s^3 + c s^5, which drives all of them towards a band
+# around 1 in five steps.
+NS_COEFFS = (3.4445, -4.7750, 2.0315)
+NS_STEPS = 5
+NS_EPS = 1e-7
+
+
+def newton_schulz5(G):
+    """Approximate orthogonalisation of a matrix step by the Muon iteration
+    (LaCT review, non-linear memory section: Muon transforms the matrix
+    gradients by Newton-Schulz iterations).  Over the last two axes:
+    ``X = G / (||G||_F + 1e-7)``, transposed when it has more rows than
+    columns; five times ``A = X X^T``, ``X = a X + (b A + c A A) X``; then
+    transposed back.  With ``G = U diag(s) V^T`` the result is
+    ``U diag(p(s / (||G||_F + 1e-7))) V^T``, ``p`` the scalar quintic
+    applied five times."""
+    a, b, c = NS_COEFFS
+    X = _f64(G)
+    X = X / (np.sqrt(np.sum(X * X, axis=(-2, -1), keepdims=True)) + NS_EPS)
+    tall = X.shape[-2] > X.shape[-1]
+    if tall:
+        X = np.swapaxes(X, -1, -2)
+    for _ in range(NS_STEPS):
+        A = np.matmul(X, np.swapaxes(X, -1, -2))
+        X = a * X + np.matmul(b * A + c * np.matmul(A, A), X)
+    if tall:
+        X = np.swapaxes(X, -1, -2)
+    return X
+
+
 def large_chunk_swiglu(Q, K, V, eta, W1, W3, W2, chunk, normalize=True,
-                       update_w1w3=True, read_first=True):
+                       update_w1w3=True, read_first=True, momentum=None, M0=None, muon_scale=None):
     """LaCT with a SwiGLU fast-weight MLP.  For each chunk: the chunk's
     queries read ``f_W``; the eta-weighted binding-loss gradient of the
     chunk is taken at those same weights; one descent step is applied to
@@ -322,9 +355,21 @@ def large_chunk_swiglu(Q, K, V, eta, W1, W3, W2, chunk, normalize=True,
     ``normalize=False`` with ``update_w1w3=False`` is the last-layer-only
     variant of the paper summary's ablation ladder (technical section 4:
     train only the last layer, then drop the weight normalisation).
-    Returns (O, (W1, W3, W2))."""
+
+    Update rules the LaCT review's non-linear-memory section compares with
+    plain descent: ``momentum=beta`` keeps one buffer per matrix,
+    ``M = beta M + step`` (``step`` = minus the chunk's gradient; ``M``
+    starts at ``M0 = (M1, M3, M2)``, zeros by default), and the weights take
+    ``M`` instead of the step; ``muon_scale=s`` replaces what the weights
+    take (the step, or ``M``) by ``s * newton_schulz5(.)`` of it, matrix by
+    matrix.  The normalisation follows either.  Returns (O, (W1, W3, W2)),
+    plus (M1, M3, M2) when ``momentum`` is given."""
     Q, K, V, eta, W1, W3, W2 = map(_f64, (Q, K, V, eta, W1, W3, W2))
     W1, W3, W2 = W1.copy(), W3.copy(), W2.copy()
+    if M0 is None:
+        M = [np.zeros_like(W1), np.zeros_like(W3), np.zeros_like(W2)]
+    else:
+        M = [_f64(m).copy() for m in M0]
     T = Q.shape[2]
     O = np.zeros(Q.shape[:-1] + (W2.shape[-1],))
     for s in range(0, T, chunk):
@@ -333,10 +378,16 @@ def large_chunk_swiglu(Q, K, V, eta, W1, W3, W2, chunk, normalize=True,
             O[:, :, s:e, :] = swiglu_forward(Q[:, :, s:e, :], W1, W3, W2)
         g1, g3, g2 = swiglu_binding_grad(K[:, :, s:e, :], V[:, :, s:e, :],
                                          eta[:, :, s:e], W1, W3, W2)
+        steps = [-g1, -g3, -g2]                # descent on the binding loss
+        if momentum is not None:
+            M = [momentum * m + st for m, st in zip(M, steps)]
+            steps = list(M)
+        if muon_scale is not None:
+            steps = [muon_scale * newton_schulz5(st) for st in steps]
         if update_w1w3:
-            W1 = W1 - g1
-            W3 = W3 - g3
-        W2 = W2 - g2
+            W1 = W1 + steps[0]
+            W3 = W3 + steps[1]
+        W2 = W2 + steps[2]
         if normalize:
             if update_w1w3:
                 W1 = normalize_columns(W1)
@@ -344,6 +395,8 @@ def large_chunk_swiglu(Q, K, V, eta, W1, W3, W2, chunk, normalize=True,
             W2 = normalize_columns(W2)
         if not read_first:
             O[:, :, s:e, :] = swiglu_forward(Q[:, :, s:e, :], W1, W3, W2)
+    if momentum is not None:
+        return O, (W1, W3, W2), tuple(M)
     return O, (W1, W3, W2)
 
 

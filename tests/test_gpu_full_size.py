@@ -10,6 +10,7 @@ the 32-head, 32K-token per-token workload (rounding even its exact outputs
 to bf16 would exceed the bound) and in the input dtype elsewhere.
 """
 import gc
+import os
 
 import numpy as np
 import pytest
@@ -107,8 +108,12 @@ def test_full_size_all_heads(name, mode, ngroups, g):
         else:
             scale = np.sqrt(sum(gr[nm]["sumsq"] for gr in groups) / sum(gr[nm]["n"] for gr in groups))
         errs[nm] = max_err / scale
-    print(f"[{s['mode']} {name} all {s['B'] * s['H']} heads, O {s['o_dtype']}] err_O={errs['O']:.3e} "
-          f"err_W={errs['W']:.3e} tol={tol(s['dtype'])}", flush=True)
+    line = (f"[{s['mode']} {name} all {s['B'] * s['H']} heads, O {s['o_dtype']}] err_O={errs['O']:.3e} "
+            f"err_W={errs['W']:.3e} tol={tol(s['dtype'])}")
+    print(line, flush=True)
+    if os.environ.get("TTT_ERRLOG"):
+        with open(os.environ["TTT_ERRLOG"], "a") as f:
+            f.write(line + "\n")
     del _runs[(name, mode)]
     assert errs["O"] <= tol(s["dtype"])
     assert errs["W"] <= tol(s["dtype"])

@@ -129,7 +129,9 @@ def test_large_chunk_swiglu_float32_output(B, H, T, chunk, mode):
     (2, 9, "large_chunk_swiglu_last_layer"),
 ])
 def test_large_chunk_swiglu_more_heads_than_one_launch(B, H, mode):
-    s = workloads.make_spec(mode, B, H, 300, 128, d_h=256, chunk=128, dtype="bf16", eta_scale=0.02)
+    # float32 O: what is checked is the state carried through the launches, not the output rounding (the
+    # bf16 rounding of these outputs alone comes within a hair of the bound for this seed)
+    s = workloads.make_spec(mode, B, H, 300, 128, d_h=256, chunk=128, dtype="bf16", eta_scale=0.02, o_dtype="fp32")
     x = workloads.generate(s, seed=16)
     O, W = run(to_device(x, s), s)
     check(s, x, O, W, label=f"{B}x{H} heads")
