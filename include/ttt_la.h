@@ -79,7 +79,9 @@ enum {
     TTT_LA_ERR_UNSUPPORTED = 6, /* valid arguments that no compiled kernel covers     */
     TTT_LA_ERR_ALIAS = 7,       /* an output overlaps an input or another output      */
     TTT_LA_ERR_WORKSPACE = 8,   /* workspace smaller than ttt_la_workspace_bytes()    */
-    TTT_LA_ERR_HIP = 9          /* a kernel launch failed (hipGetLastError)           */
+    TTT_LA_ERR_HIP = 9,         /* a kernel launch failed (hipGetLastError)           */
+    TTT_LA_ERR_SCRATCH = 10     /* ttt_la_forward_noalloc: the problem needs more     */
+                                /* workspace than the library's scratch holds         */
 };
 
 /* Modes. */
@@ -280,6 +282,29 @@ int ttt_la_backward(const void* Q, const void* K, const void* V, const float* et
                     int32_t mode, const ttt_la_desc* desc, void* dQ, void* dK, void* dV,
                     float* deta, float* dW0, void* workspace, size_t workspace_bytes,
                     void* stream);
+
+/*
+ * ttt_la_forward_noalloc: ttt_la_forward for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments, results, checks and
+ * status codes as ttt_la_forward, without the workspace: the call uses a
+ * device scratch array of TTT_LA_NOALLOC_SCRATCH_BYTES that the library
+ * holds itself (one per GPU, in the library's code object, from the first
+ * use on that GPU until the process ends; its address is looked up on the
+ * calling thread's current device, which must be the device of `stream`).
+ * The call allocates and frees nothing.
+ *   TTT_LA_ERR_SCRATCH  the problem needs more than TTT_LA_NOALLOC_SCRATCH_BYTES
+ *                       of workspace (ttt_la_workspace_bytes); nothing is enqueued
+ *   TTT_LA_ERR_HIP      the scratch address could not be obtained
+ * Every call on a GPU shares that GPU's scratch: calls that may overlap in
+ * time on one GPU (on different streams, or from several host threads)
+ * race on it and must be ordered by the caller.  Whatever the kernels need
+ * zeroed is cleared by the call itself, on `stream`.
+ */
+#define TTT_LA_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+int ttt_la_forward_noalloc(const void* Q, const void* K, const void* V, const float* eta,
+                           const float* W0, int64_t chunk, int32_t mode, const ttt_la_desc* desc,
+                           void* O, float* W_out, void* stream);
 
 /* Bytes of device workspace ttt_la_backward needs (0 for invalid or
  * unsupported arguments). */

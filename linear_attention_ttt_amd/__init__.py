@@ -17,7 +17,7 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["forward", "forward_momentum", "forward_momentum_raw", "backward", "backward_raw", "backward_workspace_bytes", "forward_timed_raw", "TimingEvent", "workspace_bytes", "TTTLAError", "MODES", "Desc", "lib", "library_path",
+__all__ = ["forward", "forward_noalloc_raw", "NOALLOC_SCRATCH_BYTES", "forward_momentum", "forward_momentum_raw", "backward", "backward_raw", "backward_workspace_bytes", "forward_timed_raw", "TimingEvent", "workspace_bytes", "TTTLAError", "MODES", "Desc", "lib", "library_path",
            "PER_TOKEN_LINEAR", "LARGE_CHUNK_LINEAR", "LARGE_CHUNK_SWIGLU", "PER_TOKEN_LINEAR_EXCLUSIVE",
            "LARGE_CHUNK_LINEAR_UPDATE_FIRST", "LARGE_CHUNK_SWIGLU_UPDATE_FIRST", "LARGE_CHUNK_SWIGLU_LAST_LAYER",
            "O_AS_INPUT", "O_FP32", "make_desc"]
@@ -74,6 +74,8 @@ def lib() -> ctypes.CDLL:
         L.ttt_la_forward_momentum.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_float, i64, i32, ctypes.POINTER(Desc),
                                               vp, vp, vp, vp, ctypes.c_size_t, vp]
         L.ttt_la_forward_momentum.restype = ctypes.c_int
+        L.ttt_la_forward_noalloc.argtypes = [vp, vp, vp, vp, vp, i64, i32, ctypes.POINTER(Desc), vp, vp, vp]
+        L.ttt_la_forward_noalloc.restype = ctypes.c_int
         L.ttt_la_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i32, ctypes.POINTER(Desc), vp, vp, vp, vp,
                                       vp, vp, ctypes.c_size_t, vp]
         L.ttt_la_backward.restype = ctypes.c_int
@@ -146,6 +148,16 @@ def forward_raw(Q, K, V, eta, W0, chunk, mode, desc: Desc, O, W_out, workspace, 
     """Call ttt_la_forward with raw integer device addresses; returns the status."""
     return int(lib().ttt_la_forward(Q, K, V, eta, W0, int(chunk), _mode(mode), ctypes.byref(desc), O, W_out,
                                     workspace, int(workspace_bytes_), stream))
+
+
+def forward_noalloc_raw(Q, K, V, eta, W0, chunk, mode, desc: Desc, O, W_out, stream) -> int:
+    """ttt_la_forward_noalloc (the library's own device scratch instead of a workspace) with raw
+    integer device addresses; returns the status."""
+    return int(lib().ttt_la_forward_noalloc(Q, K, V, eta, W0, int(chunk), _mode(mode), ctypes.byref(desc), O, W_out,
+                                            stream))
+
+
+NOALLOC_SCRATCH_BYTES = 128 << 20     # TTT_LA_NOALLOC_SCRATCH_BYTES
 
 
 def forward_timed_raw(Q, K, V, eta, W0, chunk, mode, desc: Desc, O, W_out, workspace, workspace_bytes_,

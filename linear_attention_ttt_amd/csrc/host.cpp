@@ -121,6 +121,7 @@ const char* ttt_la_status_string(int s) {
     case TTT_LA_ERR_ALIAS: return "an output overlaps an input or another output";
     case TTT_LA_ERR_WORKSPACE: return "workspace too small";
     case TTT_LA_ERR_HIP: return "HIP kernel launch failed";
+    case TTT_LA_ERR_SCRATCH: return "the problem needs more workspace than the allocation-free entry point's scratch";
   }
   return "unknown status";
 }
