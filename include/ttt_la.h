@@ -188,18 +188,20 @@ int ttt_la_forward_timed(const void* Q, const void* K, const void* V, const floa
                          void* stream, void* ev_start, void* ev_stop);
 
 /*
- * ttt_la_forward_momentum: the large-chunk linear modes (TTT_LA_LARGE_CHUNK_LINEAR and its
- * update-first variant) with momentum in the inner loop, which the LaCT review's
- * non-linear-memory section names among the update rules it compares.  Each chunk's step
- * K_c^T diag(eta_c) V_c goes into a buffer M_c = momentum * M_{c-1} + K_c^T diag(eta_c) V_c,
- * and W takes M_c instead, then the column normalisation:
- *     W_c = colnorm(W_{c-1} + M_c).
- * momentum = 0 with M0 = NULL is ttt_la_forward bit for bit.
- *   M0         [B,H,d_k,d_v] float32, device: the buffer before the first chunk (NULL = zeros),
+ * ttt_la_forward_momentum: the large-chunk modes (linear: TTT_LA_LARGE_CHUNK_LINEAR and its
+ * update-first variant; SwiGLU: TTT_LA_LARGE_CHUNK_SWIGLU and its update-first variant) with
+ * momentum in the inner loop, one of the update rules the LaCT review's non-linear-memory
+ * section compares.  Each chunk's step S_c (linear: K_c^T diag(eta_c) V_c; SwiGLU: minus the
+ * gradient of each of W1, W3, W2, at the weights that read the chunk) goes into a buffer
+ * M_c = momentum * M_{c-1} + S_c, and W takes M_c instead, then the column normalisation:
+ *     W_c = colnorm(W_{c-1} + M_c)   (per matrix for SwiGLU).
+ * momentum = 0 with M0 = NULL gives ttt_la_forward's O and W_out bit for bit.
+ *   M0         float32, device, the layout of W0: the buffer before the first chunk (NULL = zeros),
  *              e.g. the M_out of a call on the preceding tokens
  *   momentum   the coefficient (finite; ERR_SHAPE otherwise)
- *   M_out      [B,H,d_k,d_v] float32, device: the buffer after the last chunk (NULL = not
- *              written); M_out == M0 in place is allowed, any other overlap is ERR_ALIAS
+ *   M_out      float32, device, the layout of W0: the buffer after the last chunk; linear: NULL =
+ *              not written; SwiGLU: required (ERR_NULL), the buffers are kept there during the
+ *              call; M_out == M0 in place is allowed, any other overlap is ERR_ALIAS
  * Other arguments, workspace, checks and status codes as ttt_la_forward; ERR_UNSUPPORTED
  * for the other modes.  ttt_la_backward has no momentum form.
  */
@@ -207,6 +209,37 @@ int ttt_la_forward_momentum(const void* Q, const void* K, const void* V, const f
                             const float* W0, const float* M0, float momentum, int64_t chunk,
                             int32_t mode, const ttt_la_desc* desc, void* O, float* W_out,
                             float* M_out, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * ttt_la_forward_muon: the SwiGLU modes (TTT_LA_LARGE_CHUNK_SWIGLU and its update-first
+ * variant) with Muon as the update rule (LaCT review, non-linear-memory section: Muon
+ * transforms the matrix gradients by Newton-Schulz iterations; the L2 normalisation follows
+ * the update).  For each chunk and each of W1, W3, W2 the step S (minus the gradient at the
+ * weights that read the chunk; with momentum != 0 or M0 given, the buffer
+ * M_c = momentum * M_{c-1} + S) is replaced by
+ *     muon_scale * NS5(S),
+ * NS5 being the quintic Newton-Schulz iteration of the Muon optimizer (K. Jordan et al.,
+ * 2024): X = S / (||S||_F + 1e-7), taken transposed when it has more rows than columns (W2),
+ * then five times X <- 3.4445 X + (-4.7750 A + 2.0315 A A) X with A = X X^T, transposed back;
+ * then W <- colnorm(W + muon_scale * NS5(S)).  The orthogonalised step has singular values
+ * near 1 whatever the rates, so muon_scale is its size (the pages fix none).
+ *   M0, momentum, M_out  as ttt_la_forward_momentum; M_out may be NULL only when
+ *              momentum = 0 and M0 = NULL (no buffer; ERR_NULL otherwise)
+ *   muon_scale finite (ERR_SHAPE otherwise)
+ *   workspace  at least ttt_la_muon_workspace_bytes(desc, chunk, mode) bytes: ttt_la_forward's
+ *              plus 3.3 MB per head for the iteration's exchange between the workgroups of a head
+ * Other arguments, checks and status codes as ttt_la_forward; ERR_UNSUPPORTED for the other
+ * modes.
+ */
+int ttt_la_forward_muon(const void* Q, const void* K, const void* V, const float* eta,
+                        const float* W0, const float* M0, float momentum, float muon_scale,
+                        int64_t chunk, int32_t mode, const ttt_la_desc* desc, void* O,
+                        float* W_out, float* M_out, void* workspace, size_t workspace_bytes,
+                        void* stream);
+
+/* Bytes of device workspace ttt_la_forward_muon needs (0 for invalid or unsupported
+ * arguments). */
+size_t ttt_la_muon_workspace_bytes(const ttt_la_desc* desc, int64_t chunk, int32_t mode);
 
 /* Timing events for ttt_la_forward_timed and for timing calls on a stream.
  * ttt_la_event_create makes a hipEvent_t (returned through *event) that
@@ -321,7 +354,7 @@ const char* ttt_la_status_string(int status);
 /* ABI version of this header (incremented on incompatible change). */
 int ttt_la_abi_version(void);
 
-#define TTT_LA_ABI_VERSION 6
+#define TTT_LA_ABI_VERSION 7
 
 #ifdef __cplusplus
 }

@@ -17,7 +17,7 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["forward", "forward_noalloc_raw", "NOALLOC_SCRATCH_BYTES", "forward_momentum", "forward_momentum_raw", "backward", "backward_raw", "backward_workspace_bytes", "forward_timed_raw", "TimingEvent", "workspace_bytes", "TTTLAError", "MODES", "Desc", "lib", "library_path",
+__all__ = ["forward", "forward_muon", "forward_muon_raw", "muon_workspace_bytes", "forward_noalloc_raw", "NOALLOC_SCRATCH_BYTES", "forward_momentum", "forward_momentum_raw", "backward", "backward_raw", "backward_workspace_bytes", "forward_timed_raw", "TimingEvent", "workspace_bytes", "TTTLAError", "MODES", "Desc", "lib", "library_path",
            "PER_TOKEN_LINEAR", "LARGE_CHUNK_LINEAR", "LARGE_CHUNK_SWIGLU", "PER_TOKEN_LINEAR_EXCLUSIVE",
            "LARGE_CHUNK_LINEAR_UPDATE_FIRST", "LARGE_CHUNK_SWIGLU_UPDATE_FIRST", "LARGE_CHUNK_SWIGLU_LAST_LAYER",
            "O_AS_INPUT", "O_FP32", "make_desc"]
@@ -76,6 +76,11 @@ def lib() -> ctypes.CDLL:
         L.ttt_la_forward_momentum.restype = ctypes.c_int
         L.ttt_la_forward_noalloc.argtypes = [vp, vp, vp, vp, vp, i64, i32, ctypes.POINTER(Desc), vp, vp, vp]
         L.ttt_la_forward_noalloc.restype = ctypes.c_int
+        L.ttt_la_forward_muon.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_float, ctypes.c_float, i64, i32,
+                                          ctypes.POINTER(Desc), vp, vp, vp, vp, ctypes.c_size_t, vp]
+        L.ttt_la_forward_muon.restype = ctypes.c_int
+        L.ttt_la_muon_workspace_bytes.argtypes = [ctypes.POINTER(Desc), i64, i32]
+        L.ttt_la_muon_workspace_bytes.restype = ctypes.c_size_t
         L.ttt_la_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i32, ctypes.POINTER(Desc), vp, vp, vp, vp,
                                       vp, vp, ctypes.c_size_t, vp]
         L.ttt_la_backward.restype = ctypes.c_int
@@ -322,16 +327,72 @@ def backward(Q, K, V, eta, W0, dO, dW_out, chunk: int, mode="per_token_linear", 
     return dQ, dK, dV, deta, dW0
 
 
-def forward_momentum(Q, K, V, eta, W0, chunk: int, momentum: float, M0=None, mode="large_chunk_linear", *,
-                     workspace=None, stream=None, out_dtype=None):
-    """Large-chunk linear forward with a momentum buffer (``ttt_la_forward_momentum``):
-    returns ``(O, W_out, M_out)``.  ``M0`` (float32 like W0) is the buffer before the first
-    chunk, zeros when None.  Same tensor checks as ``forward``."""
+def muon_workspace_bytes(desc: Desc, chunk: int, mode) -> int:
+    return int(lib().ttt_la_muon_workspace_bytes(ctypes.byref(desc), int(chunk), _mode(mode)))
+
+
+def forward_muon_raw(Q, K, V, eta, W0, M0, momentum, muon_scale, chunk, mode, desc: Desc, O, W_out, M_out, workspace,
+                     workspace_bytes_, stream) -> int:
+    """ttt_la_forward_muon on raw device addresses (ints or None); returns the status code."""
+    return lib().ttt_la_forward_muon(Q, K, V, eta, W0, M0, float(momentum), float(muon_scale), int(chunk),
+                                     _mode(mode), ctypes.byref(desc), O, W_out, M_out, workspace, workspace_bytes_,
+                                     stream)
+
+
+def forward_muon(Q, K, V, eta, W0, chunk: int, muon_scale: float, momentum: float = 0.0, M0=None,
+                 mode="large_chunk_swiglu", *, workspace=None, stream=None, out_dtype=None):
+    """SwiGLU forward with Muon as the update rule (``ttt_la_forward_muon``): returns
+    ``(O, W_out, M_out)`` (``M_out`` None without momentum and ``M0``).  Same tensor checks as
+    ``forward``."""
     import torch
 
     m = _mode(mode)
-    if m not in (LARGE_CHUNK_LINEAR, LARGE_CHUNK_LINEAR_UPDATE_FIRST):
-        raise ValueError("momentum is defined for the large-chunk linear modes")
+    if m not in (LARGE_CHUNK_SWIGLU, LARGE_CHUNK_SWIGLU_UPDATE_FIRST):
+        raise ValueError("Muon is defined for the SwiGLU modes (read-first and update-first)")
+    for name, t in dict(Q=Q, K=K, V=V, eta=eta, W0=W0).items():
+        if not isinstance(t, torch.Tensor) or t.device != Q.device or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous tensor on Q's device")
+    if M0 is not None and (M0.shape != W0.shape or M0.dtype != torch.float32 or not M0.is_contiguous()):
+        raise ValueError("M0 must be a contiguous float32 tensor shaped like W0")
+    if Q.dtype != torch.bfloat16 or K.dtype != Q.dtype or V.dtype != Q.dtype:
+        raise ValueError("Q, K, V must be bfloat16")
+    B, H, T, dk = Q.shape
+    if W0.dim() != 3 or tuple(W0.shape[:2]) != (B, H) or W0.shape[2] % (3 * dk) != 0:
+        raise ValueError("SwiGLU W0 must be [B,H,3*d*d_h]")
+    dh = W0.shape[2] // (3 * dk)
+    odt, ocode = _o_dtype(out_dtype, Q.dtype)
+    desc = make_desc(B, H, T, dk, dk, dh, BF16, ocode)
+    O = torch.empty((B, H, T, dk), dtype=odt, device=Q.device)
+    Wo = torch.empty_like(W0)
+    Mo = torch.empty_like(W0) if (momentum != 0.0 or M0 is not None) else None
+    nbytes = muon_workspace_bytes(desc, chunk, m)
+    ws = workspace
+    if nbytes > 0 and (ws is None or ws.numel() * ws.element_size() < nbytes):
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=Q.device)
+    ws_len = ws.numel() * ws.element_size() if ws is not None else 0
+    st = stream if stream is not None else torch.cuda.current_stream(Q.device).cuda_stream
+
+    def p(t):
+        return t.data_ptr() if t is not None and t.numel() > 0 else None
+
+    status = forward_muon_raw(p(Q), p(K), p(V), p(eta), W0.data_ptr(), p(M0), momentum, muon_scale, chunk, m, desc,
+                              p(O), Wo.data_ptr(), p(Mo), p(ws), ws_len, st)
+    if status != 0:
+        raise TTTLAError(status, status_string(status))
+    return O, Wo, Mo
+
+
+def forward_momentum(Q, K, V, eta, W0, chunk: int, momentum: float, M0=None, mode="large_chunk_linear", *,
+                     workspace=None, stream=None, out_dtype=None):
+    """Large-chunk forward (linear or SwiGLU memory) with a momentum buffer
+    (``ttt_la_forward_momentum``): returns ``(O, W_out, M_out)``.  ``M0`` (float32 like W0) is
+    the buffer before the first chunk, zeros when None.  Same tensor checks as ``forward``."""
+    import torch
+
+    m = _mode(mode)
+    if m not in (LARGE_CHUNK_LINEAR, LARGE_CHUNK_LINEAR_UPDATE_FIRST, LARGE_CHUNK_SWIGLU,
+                 LARGE_CHUNK_SWIGLU_UPDATE_FIRST):
+        raise ValueError("momentum is defined for the large-chunk linear and SwiGLU modes (not last-layer)")
     for name, t in dict(Q=Q, K=K, V=V, eta=eta, W0=W0).items():
         if not isinstance(t, torch.Tensor) or t.device != Q.device or not t.is_contiguous():
             raise ValueError(f"{name} must be a contiguous tensor on Q's device")
@@ -341,8 +402,14 @@ def forward_momentum(Q, K, V, eta, W0, chunk: int, momentum: float, M0=None, mod
         raise ValueError("Q, K, V must be bfloat16")
     B, H, T, dk = Q.shape
     dv = V.shape[3]
+    if m in (LARGE_CHUNK_SWIGLU, LARGE_CHUNK_SWIGLU_UPDATE_FIRST):
+        if W0.dim() != 3 or tuple(W0.shape[:2]) != (B, H) or W0.shape[2] % (3 * dk) != 0 or dv != dk:
+            raise ValueError("SwiGLU W0 must be [B,H,3*d*d_h] with d = d_k = d_v")
+    elif tuple(W0.shape) != (B, H, dk, dv):
+        raise ValueError("W0 must be [B,H,d_k,d_v]")
+    dh = W0.shape[2] // (3 * dk) if m in (LARGE_CHUNK_SWIGLU, LARGE_CHUNK_SWIGLU_UPDATE_FIRST) else 0
     odt, ocode = _o_dtype(out_dtype, Q.dtype)
-    desc = make_desc(B, H, T, dk, dv, 0, BF16, ocode)
+    desc = make_desc(B, H, T, dk, dv, dh, BF16, ocode)
     O = torch.empty((B, H, T, dv), dtype=odt, device=Q.device)
     Wo, Mo = torch.empty_like(W0), torch.empty_like(W0)
     nbytes = workspace_bytes(desc, chunk, m)

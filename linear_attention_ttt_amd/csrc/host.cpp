@@ -103,6 +103,14 @@ size_t workspace_for(const ttt_la_desc& d, int64_t chunk, int32_t mode) {
   return 0;
 }
 
+size_t muon_workspace_for(const ttt_la_desc& d, int64_t chunk) {
+  return ttt::large_chunk_swiglu_workspace(d.B, d.H, d.T, d.d_k, d.d_h, chunk, 1);
+}
+
+bool swiglu_rule_mode(int32_t mode) {
+  return mode == TTT_LA_LARGE_CHUNK_SWIGLU || mode == TTT_LA_LARGE_CHUNK_SWIGLU_UPDATE_FIRST;
+}
+
 }  // namespace
 
 extern "C" {
@@ -135,7 +143,7 @@ size_t ttt_la_workspace_bytes(const ttt_la_desc* desc, int64_t chunk, int32_t mo
 static int forward_impl(const void* Q, const void* K, const void* V, const float* eta, const float* W0,
                         int64_t chunk, int32_t mode, const ttt_la_desc* desc, void* O, float* W_out,
                         void* workspace, size_t workspace_bytes, void* stream, void* ev_start, void* ev_stop,
-                        const float* M0, float* M_out, float momentum) {
+                        const float* M0, float* M_out, float momentum, int muon = 0, float muon_scale = 0.f) {
   int st = check_problem(desc, chunk, mode);
   if (st != TTT_LA_OK) return st;
   const ttt_la_desc d = *desc;
@@ -143,7 +151,7 @@ static int forward_impl(const void* Q, const void* K, const void* V, const float
   if (!W0 || !W_out) return TTT_LA_ERR_NULL;
   if (have_tokens && (!Q || !K || !V || !eta || !O)) return TTT_LA_ERR_NULL;
   if (!supported(d, chunk, mode)) return TTT_LA_ERR_UNSUPPORTED;
-  const size_t need = workspace_for(d, chunk, mode);
+  const size_t need = muon ? muon_workspace_for(d, chunk) : workspace_for(d, chunk, mode);
   if (need > 0 && (!workspace || workspace_bytes < need)) return TTT_LA_ERR_WORKSPACE;
 
   const size_t es = d.io_dtype == TTT_LA_BF16 ? 2 : 4;
@@ -185,7 +193,7 @@ static int forward_impl(const void* Q, const void* K, const void* V, const float
   } else {
     ttt::LargeChunkArgs a{Q, K, V, eta, W0, O, W_out, workspace, d.B, d.H, d.T, d.d_k, d.d_v, d.d_h, chunk, d.io_dtype,
                           other, mode == TTT_LA_LARGE_CHUNK_SWIGLU_LAST_LAYER ? 1 : 0, M0, M_out, momentum,
-                          o_f32(d)};
+                          o_f32(d), muon, muon_scale};
     e = method == TTT_LA_LARGE_CHUNK_LINEAR ? ttt::launch_large_chunk_linear(a, s, tm)
                                             : ttt::launch_large_chunk_swiglu(a, s, tm);
   }
@@ -205,10 +213,30 @@ int ttt_la_forward_momentum(const void* Q, const void* K, const void* V, const f
                             void* stream) {
   const int st = check_problem(desc, chunk, mode);
   if (st != TTT_LA_OK) return st;
-  if (method_of(mode) != TTT_LA_LARGE_CHUNK_LINEAR) return TTT_LA_ERR_UNSUPPORTED;
+  if (method_of(mode) != TTT_LA_LARGE_CHUNK_LINEAR && !swiglu_rule_mode(mode)) return TTT_LA_ERR_UNSUPPORTED;
   if (!std::isfinite(momentum)) return TTT_LA_ERR_SHAPE;
+  if (swiglu_rule_mode(mode) && !M_out) return TTT_LA_ERR_NULL;   // the SwiGLU buffers live in M_out
   return forward_impl(Q, K, V, eta, W0, chunk, mode, desc, O, W_out, workspace, workspace_bytes, stream, nullptr,
                       nullptr, M0, M_out, momentum);
+}
+
+size_t ttt_la_muon_workspace_bytes(const ttt_la_desc* desc, int64_t chunk, int32_t mode) {
+  if (check_problem(desc, chunk, mode) != TTT_LA_OK || !swiglu_rule_mode(mode) || !supported(*desc, chunk, mode))
+    return 0;
+  return muon_workspace_for(*desc, chunk);
+}
+
+int ttt_la_forward_muon(const void* Q, const void* K, const void* V, const float* eta, const float* W0,
+                        const float* M0, float momentum, float muon_scale, int64_t chunk, int32_t mode,
+                        const ttt_la_desc* desc, void* O, float* W_out, float* M_out, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  const int st = check_problem(desc, chunk, mode);
+  if (st != TTT_LA_OK) return st;
+  if (!swiglu_rule_mode(mode)) return TTT_LA_ERR_UNSUPPORTED;
+  if (!std::isfinite(momentum) || !std::isfinite(muon_scale)) return TTT_LA_ERR_SHAPE;
+  if ((momentum != 0.f || M0) && !M_out) return TTT_LA_ERR_NULL;   // the buffers live in M_out
+  return forward_impl(Q, K, V, eta, W0, chunk, mode, desc, O, W_out, workspace, workspace_bytes, stream, nullptr,
+                      nullptr, M0, M_out, momentum, 1, muon_scale);
 }
 
 int ttt_la_forward(const void* Q, const void* K, const void* V, const float* eta, const float* W0,

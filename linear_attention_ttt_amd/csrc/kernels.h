@@ -82,6 +82,9 @@ struct LargeChunkArgs {
   float* M_out = nullptr;
   float momentum = 0.f;
   int o_f32 = 0;  // 1: O is float32
+  // SwiGLU: Muon (the step of each matrix replaced by muon_scale * NS5(step)); momentum needs M_out
+  int muon = 0;
+  float muon_scale = 0.f;
 };
 
 bool large_chunk_linear_supported(int64_t dk, int64_t dv, int64_t chunk, int dtype);
@@ -91,7 +94,8 @@ size_t large_chunk_linear_backward_workspace(int64_t B, int64_t H, int64_t T, in
 hipError_t launch_large_chunk_linear_backward(const BackwardArgs& a, hipStream_t stream);
 
 bool large_chunk_swiglu_supported(int64_t d, int64_t dh, int64_t chunk, int dtype);
-size_t large_chunk_swiglu_workspace(int64_t B, int64_t H, int64_t T, int64_t d, int64_t dh, int64_t chunk);
+size_t large_chunk_swiglu_workspace(int64_t B, int64_t H, int64_t T, int64_t d, int64_t dh, int64_t chunk,
+                                    int muon = 0);
 hipError_t launch_large_chunk_swiglu(const LargeChunkArgs& a, hipStream_t stream, const Timing& tm);
 
 }  // namespace ttt

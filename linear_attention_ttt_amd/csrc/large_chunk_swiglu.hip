@@ -12,7 +12,8 @@
 // d_h) are then divided by max(norm, 1e-12).
 //
 // Two kernels:
-//  * swiglu_recur_kernel (cooperative, sequential over chunks): a head's
+//  * swiglu_recur_kernel (sequential over chunks; every workgroup of a
+//    launch resident at once, see launch_large_chunk_swiglu): a head's
 //    hidden units are split into NSL slices of NS units, one workgroup per
 //    slice.  With that split dW1[:, s], dW3[:, s], dW2[s, :] and the W1/W3
 //    normalisation are local to the slice; only the W2 column norms need a
@@ -98,11 +99,225 @@ __global__ void zero_u32_kernel(unsigned* p, int n) {
   if (i < n) p[i] = 0u;
 }
 
+// Update rules of the recurrence (compile-time RULE of swiglu_recur_kernel):
+//   0  plain descent: W <- W + dW (dW = minus the chunk's eta-weighted gradient);
+//   1  momentum: M <- beta M + dW, W <- W + M;
+//   2  Muon: the step (dW, or M <- beta M + dW with momentum) is replaced by
+//      muon_scale * NS5(step) for each matrix, NS5 the quintic Newton-Schulz
+//      iteration of the Muon optimizer (five steps X <- a X + (b A + c A^2) X,
+//      A = X X^T, from X = step / (||step||_F + 1e-7); W2's step is taken
+//      transposed, so all three are d x d_h).
+// The column normalisation follows in every rule.
+constexpr float NS_A = 3.4445f, NS_B = -4.7750f, NS_C = 2.0315f, NS_EPS = 1e-7f;
+constexpr int NS_STEPS = 5;
+struct SwRule {
+  const float* M0;   // momentum buffers before the first chunk, state layout (null: zeros)
+  float* Mout;       // momentum buffers, updated at every chunk end (null: no momentum)
+  float beta;        // momentum coefficient
+  float muon_scale;  // scale of the orthogonalised step (RULE 2)
+  float* ns;         // RULE 2: per head [NSL][3][d][d] partial Gram matrices, then [3][d][d] their sums
+};
+constexpr size_t NS_HEAD_FLOATS = (size_t)(SW_NSL + 1) * 3 * SW_D * SW_D;
+
+// Barrier of the NSL workgroups of head bh (their counter; the k-th barrier waits for NSL * k arrivals).
+// Bounded: on giving up the call's error flag is raised (the read kernel then fills every output with
+// NaN) and the workgroup carries on, so every kernel still ends.  Stores that the other workgroups read
+// after it must be complete (wait_vm<0>) before it.
+__device__ __forceinline__ void head_barrier_wait(unsigned* counters, unsigned* errflag, int bh, unsigned& nbar,
+                                                  int spin_limit, unsigned target_extra) {
+  __syncthreads();
+  ++nbar;
+  if (threadIdx.x == 0) {
+    __hip_atomic_fetch_add(&counters[bh], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const unsigned target = (unsigned)SW_NSL * nbar + target_extra;
+    int spins = 0;
+    while (__hip_atomic_load(&counters[bh], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+      __builtin_amdgcn_s_sleep(2);
+      if (++spins > spin_limit) {
+        __hip_atomic_store(errflag, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        break;
+      }
+    }
+  }
+  __syncthreads();
+}
+
+// RULE 2 at the end of chunk c: replace the step of the three matrices by muon_scale * NS5(step).  On
+// entry S.w* hold W + dW and the LDS of the K/V stages (every copy into it has landed) holds, after
+// 3 d NS floats, the weights before the update in the layout of S.w*.  The steps (with momentum:
+// M <- beta M + dW, kept in R.Mout) are the columns of three d x d_h matrices X (W2's transposed), split
+// by hidden unit over the head's NSL workgroups; the iteration needs A = X X^T = the sum over workgroups
+// of X_s X_s^T.  Per step each workgroup writes its three partial Gram matrices, sums 8 rows of each over
+// the NSL partials, and after a second barrier reads the full sums back; wave w then updates rows
+// 32w .. 32w + 31 of its workgroup's columns, X_s <- a X_s + b A X_s + c A (A X_s) (bf16 hi + lo
+// products, float32 accumulation).  The Frobenius normalisation comes from trace(X X^T) of the first
+// step.  LDS of the stages: X [3][d][NS] float32, Y [3][d][NS] (A X), then wave w's rows of A as bf16
+// [hi, lo][32][d].  Kept out of line: its registers are not the recurrence's.
+__device__ __attribute__((noinline)) void swiglu_muon_steps(RecurLds& S, const SwRule& R, int bh, int sl, int u0,
+                                                           int c, unsigned* counters, unsigned* errflag,
+                                                           unsigned& nbar, int spin_limit, unsigned target_extra) {
+  constexpr int D = SW_D, DH = SW_DH, NS = SW_NS, G = D * D, NT = SW_WAVES * 64;
+  const int tid = threadIdx.x, l = tid & 63, g = l >> 4, li = l & 15;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  auto head_barrier = [&]() { head_barrier_wait(counters, errflag, bh, nbar, spin_limit, target_extra); };
+  float* X = (float*)&S.kv[0][0][0][0];
+  float* Y = X + 3 * D * NS;
+  unsigned char* Aw = (unsigned char*)(Y + 3 * D * NS) + w * (2 * 32 * D * 2);
+  const bool mom = R.Mout != nullptr;
+  const float* Msrc = c == 0 ? R.M0 : R.Mout;
+  const float* Mi = mom && Msrc ? Msrc + (size_t)bh * 3 * D * DH : nullptr;
+  float* Mh = mom ? R.Mout + (size_t)bh * 3 * D * DH : nullptr;
+  for (int k = 0; k < 8; ++k) {
+    const int i = tid + NT * k, d = i >> 4, u = i & 15, u2 = i >> 7, d2 = i & 127;
+    const int li3[3] = {w13i(d, u), w13i(d, u), w2i(u2, d2)};
+    float* e[3] = {S.w1 + li3[0], S.w3 + li3[1], S.w2 + li3[2]};
+    const size_t go[3] = {(size_t)d * DH + u0 + u, (size_t)D * DH + (size_t)d * DH + u0 + u,
+                          2 * (size_t)D * DH + (size_t)(u0 + u2) * D + d2};
+    const int xi[3] = {d * NS + u, D * NS + d * NS + u, 2 * D * NS + d2 * NS + u2};
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+      const float before = Y[j * D * NS + li3[j]];
+      const float m = Mi ? __hip_atomic_load(Mi + go[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0.f;
+      const float st = (*e[j] - before) + (mom ? R.beta * m : 0.f);
+      if (mom) __hip_atomic_store(Mh + go[j], st, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      *e[j] = before;
+      X[xi[j]] = st;
+    }
+  }
+  if (mom) wait_vm<0>();
+  __syncthreads();
+  float* nsh = R.ns + (size_t)bh * NS_HEAD_FLOATS;   // [NSL][3][d][d] partials, then [3][d][d] sums
+  const __amdgpu_buffer_rsrc_t rn = make_rsrc(nsh, (long long)NS_HEAD_FLOATS * 4);
+  constexpr unsigned SUMS = (unsigned)SW_NSL * 3 * G;   // float offset of the sums
+  float f[3] = {1.f, 1.f, 1.f};
+  for (int it = 0; it < NS_STEPS; ++it) {
+    // this workgroup's partial Gram matrices G = X_s X_s^T; wave w: row tiles 2w, 2w+1 (stored
+    // transposed: G is symmetric up to rounding)
+#pragma unroll
+    for (int m = 0; m < 3; ++m) {
+      const float* Xm = X + m * D * NS;
+      bf16x4 ah[2], al[2];
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        const floatx4 x = *(const floatx4*)(Xm + (16 * (2 * w + tt) + li) * NS + 4 * g);
+        const uint2 s0 = split2(x[0], x[1]), s1 = split2(x[2], x[3]);
+        ah[tt] = __builtin_bit_cast(bf16x4, uint2{s0.x, s1.x});
+        al[tt] = __builtin_bit_cast(bf16x4, uint2{s0.y, s1.y});
+      }
+#pragma unroll
+      for (int tj = 0; tj < 8; ++tj) {
+        const floatx4 x = *(const floatx4*)(Xm + (16 * tj + li) * NS + 4 * g);
+        const uint2 s0 = split2(x[0], x[1]), s1 = split2(x[2], x[3]);
+        const bf16x4 bh = __builtin_bit_cast(bf16x4, uint2{s0.x, s1.x});
+        const bf16x4 bl = __builtin_bit_cast(bf16x4, uint2{s0.y, s1.y});
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+          floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+          acc = mfma16k16(ah[tt], bh, acc);
+          acc = mfma16k16(ah[tt], bl, acc);
+          acc = mfma16k16(al[tt], bh, acc);
+          const unsigned off = ((((unsigned)sl * 3 + m) * D + 16 * tj + li) * D + 16 * (2 * w + tt) + 4 * g) * 4;
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc), rn, off, 0, 16);
+        }
+      }
+    }
+    wait_vm<0>();
+    head_barrier();
+    // rows 8 sl .. 8 sl + 7 of the three sums, over the NSL partials in a fixed order
+    for (int q = tid; q < 3 * 8 * (D / 4); q += NT) {
+      const int m = q / (8 * (D / 4)), row = 8 * sl + (q / (D / 4)) % 8, c4 = q % (D / 4);
+      floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+      for (int s2 = 0; s2 < SW_NSL; ++s2)
+        acc += __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(
+                                               rn, ((((unsigned)s2 * 3 + m) * D + row) * D + 4 * c4) * 4, 0, 16));
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc), rn,
+                                             (SUMS + ((unsigned)m * D + row) * D + 4 * c4) * 4, 0, 16);
+    }
+    wait_vm<0>();
+    head_barrier();
+#pragma unroll 1
+    for (int m = 0; m < 3; ++m) {
+      float* Xm = X + m * D * NS;
+      float* Ym = Y + m * D * NS;
+      const unsigned abase = SUMS + (unsigned)m * G;
+      if (it == 0) {   // 1 / (||X||_F + eps), with ||X||_F^2 = trace(X X^T)
+        const float t = __hip_atomic_load(nsh + abase + l * (D + 1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) +
+                        __hip_atomic_load(nsh + abase + (l + 64) * (D + 1), __ATOMIC_RELAXED,
+                                          __HIP_MEMORY_SCOPE_AGENT);
+        f[m] = 1.0f / (sqrtf(wave_sum(t)) + NS_EPS);
+      }
+      const float fx = it == 0 ? f[m] : 1.f, f2 = fx * fx;   // A of the normalised X is f^2 A
+      // this wave's rows 32w .. 32w + 31 of f^2 A as bf16 hi + lo, 16-byte pieces swizzled by row
+      for (int q = l; q < 32 * (D / 4); q += 64) {
+        const int row = q / (D / 4), c4 = q % (D / 4);
+        const floatx4 a = f2 * __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                                rn, (abase + (32u * w + row) * D + 4 * c4) * 4, 0, 16));
+        const uint2 s0 = split2(a[0], a[1]), s1 = split2(a[2], a[3]);
+        const int off = row * (2 * D) + (((c4 >> 1) ^ (row & 15)) << 4) + (c4 & 1) * 8;
+        *(uint2*)(Aw + off) = uint2{s0.x, s1.x};
+        *(uint2*)(Aw + 32 * D * 2 + off) = uint2{s0.y, s1.y};
+      }
+      // P = A' B for B = X or Y (d x NS in LDS): rows 32w + 16tt + 4g + r, column li of the lane
+      auto prod = [&](const float* Bm, floatx4 (&acc)[2]) {
+        acc[0] = acc[1] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < D / 32; ++ks) {
+          floatx4 b0, b1;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            b0[j] = Bm[(32 * ks + 8 * g + j) * NS + li];
+            b1[j] = Bm[(32 * ks + 8 * g + 4 + j) * NS + li];
+          }
+          bf16x8 bh, bl;
+          split8(b0, b1, bh, bl);
+#pragma unroll
+          for (int tt = 0; tt < 2; ++tt) {
+            const int row = 16 * tt + li, off = row * (2 * D) + (((4 * ks + g) ^ (row & 15)) << 4);
+            const bf16x8 ah = *(const bf16x8*)(Aw + off), al = *(const bf16x8*)(Aw + 32 * D * 2 + off);
+            acc[tt] = mfma16(ah, bh, acc[tt]);
+            acc[tt] = mfma16(ah, bl, acc[tt]);
+            acc[tt] = mfma16(al, bh, acc[tt]);
+          }
+        }
+      };
+      floatx4 y[2], z[2];
+      prod(Xm, y);                    // A' X; A' (f X) = f A' X
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          y[tt][r] *= fx;
+          Ym[(32 * w + 16 * tt + 4 * g + r) * NS + li] = y[tt][r];
+        }
+      __syncthreads();                // every row of A' X is in LDS; every wave is done reading X
+      prod(Ym, z);                    // A' (A' X)
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float* xp = Xm + (32 * w + 16 * tt + 4 * g + r) * NS + li;
+          *xp = NS_A * fx * *xp + NS_B * y[tt][r] + NS_C * z[tt][r];
+        }
+    }
+    __syncthreads();                  // every row of the new X before its next use
+  }
+  // W <- W + muon_scale * NS5(step) (W was put back to its value before the update above)
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const int i = tid + NT * k, d = i >> 4, u = i & 15, u2 = i >> 7, d2 = i & 127;
+    S.w1[w13i(d, u)] += R.muon_scale * X[d * NS + u];
+    S.w3[w13i(d, u)] += R.muon_scale * X[D * NS + d * NS + u];
+    S.w2[w2i(u2, d2)] += R.muon_scale * X[2 * D * NS + d2 * NS + u2];
+  }
+  __syncthreads();
+}
+
+template <int RULE>
 __global__ __launch_bounds__(SW_WAVES * 64, 1) void swiglu_recur_kernel(
     const bf16* __restrict__ K, const bf16* __restrict__ V, const float* __restrict__ eta,
     const float* __restrict__ W0, float* __restrict__ Wout, bf16* __restrict__ states, float* __restrict__ ss2,
     unsigned* __restrict__ counters, unsigned* __restrict__ errflag, int T_in, int chunk, int nchunks_in, int head0,
-    int update_first, int last_only, int par_nchunks, int spin_limit, unsigned target_extra) {
+    int update_first, int last_only, int par_nchunks, int spin_limit, unsigned target_extra, SwRule R) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
   RecurLds& S = *reinterpret_cast<RecurLds*>(smem_raw);
   constexpr int NT = SW_WAVES * 64;
@@ -208,7 +423,11 @@ __global__ __launch_bounds__(SW_WAVES * 64, 1) void swiglu_recur_kernel(
   for (int m = 0; m < 8; ++m)
     tr_off[m] = (unsigned)(trow * SW_KROW + (((2 * m + ((li >> 1) & 1)) ^ sw_swz(trow)) << 4) + (li & 1) * 8);
 
+  int last_c = -1, last_gi = 0, last_slot = 0;   // the latest stage issued (RULE 2 re-issues it)
   auto issue = [&](int c, int gi, int slot) {
+    last_c = c;
+    last_gi = gi;
+    last_slot = slot;
     const int t0 = c * chunk + gi * SW_GT;
     const int n = min(c * chunk + chunk, T) - t0;   // valid tokens; rows beyond read as 0
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kh + (size_t)t0 * D, (long long)n * SW_KROW);
@@ -219,6 +438,20 @@ __global__ __launch_bounds__(SW_WAVES * 64, 1) void swiglu_recur_kernel(
 #pragma unroll
     for (int j = 0; j < SW_STAGE / 1024; ++j) dma16<true>(rv, dma_off[j], S.kv[w][slot][1] + j * 1024);
     if (l < SW_GT) dma4<true>(re, (unsigned)(l * 4), S.eta[w][slot]);
+  };
+
+  // Barrier of the head's NSL workgroups (through their counter; the k-th barrier waits for NSL * k
+  // arrivals).  Bounded: on giving up the call's error flag is raised (the read kernel then fills every
+  // output with NaN) and the workgroup carries on, so every kernel still ends.  Stores that other
+  // workgroups read after it must be complete (wait_vm<0>) before it.
+  unsigned nbar = 0;   // head barriers passed
+  auto head_barrier = [&]() { head_barrier_wait(counters, errflag, bh, nbar, spin_limit, target_extra); };
+
+  // RULE 2 at a chunk end (see swiglu_muon_steps); the stage whose copy was in flight when the iteration
+  // took the LDS of the stages is copied again afterwards
+  auto muon_phase = [&](int c) {
+    swiglu_muon_steps(S, R, bh, sl, u0, c, counters, errflag, nbar, spin_limit, target_extra);
+    if (last_c > c) issue(last_c, last_gi, last_slot);
   };
 
   bf16x8 w1op[4], w3op[4], w2op[4];
@@ -321,7 +554,46 @@ __global__ __launch_bounds__(SW_WAVES * 64, 1) void swiglu_recur_kernel(
       }
     }
 
-    // ---- end of chunk: the waves add their partial gradients in a fixed order, then normalise ----
+    // ---- end of chunk ----
+    // Momentum and Muon: each thread keeps 8 weights of each matrix (W1, W3 element (d, u) = (i/16,
+    // i%16), W2 element (u, d) = (i/128, i%128), i = tid + 256 k): their values before the update and
+    // their momentum buffers (read at device scope: other chunks' values were written by this thread
+    // through the L2)
+    if constexpr (RULE == 1) {
+      // momentum: W + beta M goes into LDS before the partial gradients are added, so the adds leave
+      // W + beta M + dW; W itself is parked in M_out, and M <- beta M + dW is their difference after the
+      // adds.  The buffers are read at device scope (this thread wrote them through the L2).
+      const float* Msrc = c == 0 ? R.M0 : R.Mout;
+      const float* Mi = Msrc ? Msrc + (size_t)bh * 3 * D * DH : nullptr;
+      float* Mh = R.Mout + (size_t)bh * 3 * D * DH;
+      auto pre = [&](float* e, size_t go) {
+        const float m = Mi ? __hip_atomic_load(Mi + go, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0.f;
+        const float wo = *e;
+        __hip_atomic_store(Mh + go, wo, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        *e = wo + R.beta * m;
+      };
+#pragma unroll 1
+      for (int k = 0; k < 8; ++k) {
+        const int i = tid + NT * k, d = i >> 4, u = i & 15, u2 = i >> 7, d2 = i & 127;
+        pre(S.w1 + w13i(d, u), (size_t)d * DH + u0 + u);
+        pre(S.w3 + w13i(d, u), (size_t)D * DH + (size_t)d * DH + u0 + u);
+        pre(S.w2 + w2i(u2, d2), 2 * (size_t)D * DH + (size_t)(u0 + u2) * D + d2);
+      }
+      wait_vm<0>();
+      __syncthreads();   // every value moved before any wave adds its partial gradient
+    } else if constexpr (RULE == 2) {
+      // the weights before the update, copied into the LDS of the K/V stages (the stage in flight is
+      // copied again after the Newton-Schulz iteration, which uses that LDS too)
+      wait_vm<0>();
+      __syncthreads();
+      float* Wb = (float*)&S.kv[0][0][0][0] + 3 * D * NS;
+      for (int i = tid; i < 3 * D * NS / 4; i += NT)
+        ((floatx4*)Wb)[i] = i < D * NS / 4 ? ((const floatx4*)S.w1)[i]
+                            : i < 2 * D * NS / 4 ? ((const floatx4*)S.w3)[i - D * NS / 4]
+                                                 : ((const floatx4*)S.w2)[i - 2 * D * NS / 4];
+      __syncthreads();
+    }
+    // The waves add their partial gradients in a fixed order, then normalise.
     // dW1 lane layout: [d = 16m + 4g + r][u = li]; dW2: [u = 4g + r][d = 16m + li].  Every weight is
     // updated as (((W + P0) + P1) + P2) + P3 (P_k: wave k's partial), pipelined over quarters of the
     // weights: in pass p wave k adds its partial to quarter p - k (row tiles 2q, 2q+1 of the three
@@ -350,6 +622,24 @@ __global__ __launch_bounds__(SW_WAVES * 64, 1) void swiglu_recur_kernel(
         }
       }
       __syncthreads();
+    }
+    if constexpr (RULE == 1) {
+      float* Mh = R.Mout + (size_t)bh * 3 * D * DH;
+      auto post = [&](const float* e, size_t go) {
+        const float wo = __hip_atomic_load(Mh + go, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(Mh + go, *e - wo, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      };
+#pragma unroll 1
+      for (int k = 0; k < 8; ++k) {
+        const int i = tid + NT * k, d = i >> 4, u = i & 15, u2 = i >> 7, d2 = i & 127;
+        post(S.w1 + w13i(d, u), (size_t)d * DH + u0 + u);
+        post(S.w3 + w13i(d, u), (size_t)D * DH + (size_t)d * DH + u0 + u);
+        post(S.w2 + w2i(u2, d2), 2 * (size_t)D * DH + (size_t)(u0 + u2) * D + d2);
+      }
+      wait_vm<0>();
+      __syncthreads();   // every updated weight read before the normalisation rewrites it
+    } else if constexpr (RULE == 2) {
+      muon_phase(c);
     }
     // W1, W3: unit columns over d, local (waves 0 and 1).  With only the last layer updated there is
     // no normalisation (every slice of a head takes the same branch, so none waits on the exchange).
@@ -390,22 +680,10 @@ __global__ __launch_bounds__(SW_WAVES * 64, 1) void swiglu_recur_kernel(
       // invalidate the whole L2 at every chunk end (measured: ~9% of the recurrence).
       wait_vm<0>();
     }
-    __syncthreads();
-    if (tid == 0 && !last_only) {
-      __hip_atomic_fetch_add(&counters[bh], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      // bounded wait: on giving up the call's error flag is raised (the read kernel then fills every
-      // output with NaN) and the workgroup carries on, so every kernel still ends
-      const unsigned target = (unsigned)SW_NSL * (unsigned)(c + 1) + target_extra;
-      int spins = 0;
-      while (__hip_atomic_load(&counters[bh], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
-        __builtin_amdgcn_s_sleep(2);
-        if (++spins > spin_limit) {
-          __hip_atomic_store(errflag, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          break;
-        }
-      }
-    }
-    __syncthreads();
+    if (last_only)
+      __syncthreads();
+    else
+      head_barrier();   // every slice's partial W2 column norms are out
     if (!last_only && w >= 2 && w < 4) {
       const int d = (w - 2) * 64 + l;
       float ss = 0.f;
@@ -423,6 +701,20 @@ __global__ __launch_bounds__(SW_WAVES * 64, 1) void swiglu_recur_kernel(
       store_state(c + 1);
   }
   wait_vm<0>();
+  if constexpr (RULE >= 1) {
+    if (nchunks == 0 && R.Mout) {   // no chunk: the buffers pass through (zeros without M0)
+      const size_t hb = (size_t)bh * 3 * D * DH;
+      for (int i = tid; i < D * NS; i += NT) {
+        const int d = i / NS, u = i % NS;
+        for (int j = 0; j < 2; ++j) {
+          const size_t o = hb + (size_t)j * D * DH + (size_t)d * DH + u0 + u;
+          R.Mout[o] = R.M0 ? R.M0[o] : 0.f;
+        }
+        const size_t o2 = hb + 2 * (size_t)D * DH + (size_t)(u0 + i / D) * D + i % D;
+        R.Mout[o2] = R.M0 ? R.M0[o2] : 0.f;
+      }
+    }
+  }
 
   if (par) {   // this chunk's W2 update, [d][u] fp32, into Wout (the caller's per-chunk buffer)
     float* inc = Wout + ((size_t)bh * par_nchunks + cpar) * SW_STATE / 2;
@@ -698,10 +990,11 @@ __global__ __launch_bounds__(SW_RW * 64, 1) void swiglu_read_kernel(const bf16* 
 }
 
 struct SwLayout {
-  size_t states, ss2, counters, err, total;
+  size_t states, ss2, counters, err, ns, total;
 };
 
-SwLayout sw_layout(int64_t BH, int64_t nchunks) {
+// muon: room for the Newton-Schulz exchange (partial Gram matrices and their sums, per head)
+SwLayout sw_layout(int64_t BH, int64_t nchunks, int muon) {
   SwLayout L;
   L.states = 0;
   size_t off = (size_t)BH * nchunks * SW_STATE * 2;
@@ -713,6 +1006,9 @@ SwLayout sw_layout(int64_t BH, int64_t nchunks) {
   off += (size_t)BH * 4;
   L.err = off;
   off += 4;
+  off = (off + 255) & ~(size_t)255;
+  L.ns = off;
+  if (muon) off += (size_t)BH * NS_HEAD_FLOATS * 4;
   L.total = (off + 255) & ~(size_t)255;
   return L;
 }
@@ -724,10 +1020,10 @@ bool large_chunk_swiglu_supported(int64_t d, int64_t dh, int64_t chunk, int dtyp
   return dtype == 1 && d == SW_D && dh == SW_DH;
 }
 
-size_t large_chunk_swiglu_workspace(int64_t B, int64_t H, int64_t T, int64_t d, int64_t dh, int64_t chunk) {
+size_t large_chunk_swiglu_workspace(int64_t B, int64_t H, int64_t T, int64_t d, int64_t dh, int64_t chunk, int muon) {
   (void)d;
   (void)dh;
-  return sw_layout(B * H, (T + chunk - 1) / chunk).total;
+  return sw_layout(B * H, (T + chunk - 1) / chunk, muon).total;
 }
 
 // O_c = f_{W_{c-1}}(Q_c) for every chunk, from the stored states
@@ -760,7 +1056,7 @@ hipError_t launch_large_chunk_swiglu(const LargeChunkArgs& a, hipStream_t stream
   const int BH = (int)(a.B * a.H);
   const int T = (int)a.T, chunk = (int)a.chunk;
   const int nchunks = (int)((a.T + a.chunk - 1) / a.chunk);
-  const SwLayout lay = sw_layout(BH, nchunks);
+  const SwLayout lay = sw_layout(BH, nchunks, a.muon);
   unsigned char* ws = (unsigned char*)a.ws;
   bf16* states = (bf16*)(ws + lay.states);
   float* ss2 = (float*)(ws + lay.ss2);
@@ -772,27 +1068,30 @@ hipError_t launch_large_chunk_swiglu(const LargeChunkArgs& a, hipStream_t stream
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
 
+  // the update rule: plain descent, momentum (M_out given), Muon (with or without momentum)
+  const int rule = a.muon ? 2 : (a.M_out ? 1 : 0);
+  auto krec = rule == 2 ? swiglu_recur_kernel<2> : rule == 1 ? swiglu_recur_kernel<1> : swiglu_recur_kernel<0>;
+  const SwRule R{a.M0, a.M_out, a.momentum, a.muon_scale, (float*)(ws + lay.ns)};
   // the recurrence needs every workgroup of a head resident at once
   const size_t lds_r = sizeof(RecurLds);
-  e = hipFuncSetAttribute((const void*)swiglu_recur_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_r);
+  e = hipFuncSetAttribute((const void*)krec, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_r);
   if (e != hipSuccess) return e;
   int dev = 0, ncu = 0, per_cu = 0;
   if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
   if ((e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
-  if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)swiglu_recur_kernel, SW_WAVES * 64, lds_r)) !=
-      hipSuccess)
+  if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)krec, SW_WAVES * 64, lds_r)) != hipSuccess)
     return e;
   const int heads_per_launch = (per_cu * ncu) / SW_NSL;
-  if (heads_per_launch < 1) return hipErrorCooperativeLaunchTooLarge;
-  if (a.last_layer_only && !a.update_first && nchunks > 1 && BH * SW_NSL < ncu) {
+  if (heads_per_launch < 1) return hipErrorLaunchOutOfResources;
+  if (rule == 0 && a.last_layer_only && !a.update_first && nchunks > 1 && BH * SW_NSL < ncu) {
     // The fully parallel form: every (head, chunk) W2 update at once, a prefix over chunks, the reads.
     // Taken only when the heads alone leave compute units idle: the total work is the same as the
     // recurrence's, and at one workgroup per CU or more the recurrence measured faster (B2 H8 T32768:
     // 0.67 against 0.72 ms per call; it has no prefix pass and no state copies).
     if ((e = mark(tm.start, stream)) != hipSuccess) return e;
-    hipLaunchKernelGGL(swiglu_recur_kernel, dim3(BH * nchunks * SW_NSL), dim3(SW_WAVES * 64), lds_r, stream,
+    hipLaunchKernelGGL(swiglu_recur_kernel<0>, dim3(BH * nchunks * SW_NSL), dim3(SW_WAVES * 64), lds_r, stream,
                        (const bf16*)a.K, (const bf16*)a.V, a.eta, a.W0, (float*)states, states, ss2, counters, err, T,
-                       chunk, nchunks, 0, 0, 1, nchunks, SW_SPIN_LIMIT, 0u);
+                       chunk, nchunks, 0, 0, 1, nchunks, SW_SPIN_LIMIT, 0u, R);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if ((e = mark(tm.stop, stream)) != hipSuccess) return e;
     const long long np = (long long)BH * SW_D * (SW_DH / 8);
@@ -814,16 +1113,18 @@ hipError_t launch_large_chunk_swiglu(const LargeChunkArgs& a, hipStream_t stream
   unsigned spin_extra;
   spin_params(&spin_limit, &spin_extra);
   if ((e = mark(tm.start, stream)) != hipSuccess) return e;   // the recurrence: the sequential part
+  // The slices of a head wait for each other at every chunk end, so all workgroups of a launch must be
+  // resident together: a launch holds at most as many workgroups as the compute units hold at once (the
+  // occupancy query above; one workgroup per CU with this LDS size), which every workgroup of an ordinary
+  // launch on an otherwise idle device then is.  If other work held compute units for longer than the
+  // bounded wait, the wait gives up and the call's outputs become NaN (see swiglu_read_kernel) instead
+  // of hanging.  (An ordinary launch, unlike a cooperative one, can also be captured in a HIP graph.)
   for (int h0 = 0; h0 < BH; h0 += heads_per_launch) {
     const int nh = std::min(heads_per_launch, BH - h0);
-    int Ti = T, ci = chunk, nci = nchunks, hi = h0, uf = a.update_first ? 1 : 0, lo = a.last_layer_only ? 1 : 0;
-    int pn = 0;
-    void* args[] = {(void*)&Kp, (void*)&Vp, (void*)&Ep, (void*)&W0p, (void*)&Wo, (void*)&states, (void*)&ss2,
-                    (void*)&counters, (void*)&err, (void*)&Ti, (void*)&ci, (void*)&nci, (void*)&hi, (void*)&uf,
-                    (void*)&lo, (void*)&pn, (void*)&spin_limit, (void*)&spin_extra};
-    e = hipLaunchCooperativeKernel((const void*)swiglu_recur_kernel, dim3(nh * SW_NSL), dim3(SW_WAVES * 64), args,
-                                   (unsigned)lds_r, stream);
-    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(krec, dim3(nh * SW_NSL), dim3(SW_WAVES * 64), lds_r, stream, Kp, Vp, Ep, W0p, Wo, states, ss2,
+                       counters, err, T, chunk, nchunks, h0, a.update_first ? 1 : 0, a.last_layer_only ? 1 : 0, 0,
+                       spin_limit, spin_extra, R);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if ((e = mark(tm.stop, stream)) != hipSuccess) return e;
   if (nchunks == 0) return hipSuccess;

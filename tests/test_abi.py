@@ -47,7 +47,7 @@ def test_exports_every_declared_symbol():
 
 @needs_lib
 def test_version_and_status_strings():
-    assert la.lib().ttt_la_abi_version() == 6
+    assert la.lib().ttt_la_abi_version() == 7
     for s in range(10):
         assert la.status_string(s) and la.status_string(s) != "unknown status"
     assert la.status_string(99) == "unknown status"
@@ -282,7 +282,8 @@ def mcall(mode=1, momentum=0.9, M0=ptr(8), M_out=ptr(9), desc=None, **kw):
 
 @needs_lib
 @pytest.mark.parametrize("kw,code", [
-    (dict(mode=0), 6), (dict(mode=2, desc=la.make_desc(1, 2, 128, 128, 128, 256, la.BF16)), 6), (dict(mode=3), 6),
+    (dict(mode=0), 6), (dict(mode=6, desc=la.make_desc(1, 2, 128, 128, 128, 256, la.BF16)), 6), (dict(mode=3), 6),
+    (dict(mode=2, desc=la.make_desc(1, 2, 128, 128, 128, 256, la.BF16), M_out=None), 1),   # SwiGLU needs M_out
     (dict(mode=7), 5), (dict(momentum=float("nan")), 2), (dict(momentum=float("inf")), 2),
     (dict(W0=None), 1),
     (dict(M_out=ptr(0)), 7),                  # M_out over Q
@@ -292,3 +293,40 @@ def mcall(mode=1, momentum=0.9, M0=ptr(8), M_out=ptr(9), desc=None, **kw):
 ])
 def test_momentum_invalid_arguments(kw, code):
     assert mcall(**kw) == code
+
+
+def muoncall(mode=2, momentum=0.9, scale=0.1, M0=ptr(8), M_out=ptr(9), desc=None, ws_bytes=1 << 33, **kw):
+    if desc is None:
+        desc = la.make_desc(1, 2, 128, 128, 128, 256, la.BF16)
+    p = dict(Q=ptr(0), K=ptr(1), V=ptr(2), eta=ptr(3), W0=ptr(4), O=ptr(5), W_out=ptr(6), ws=ptr(7))
+    p.update(kw)
+    return la.forward_muon_raw(p["Q"], p["K"], p["V"], p["eta"], p["W0"], M0, momentum, scale, 64, mode, desc,
+                               p["O"], p["W_out"], M_out, p["ws"], ws_bytes, None)
+
+
+@needs_lib
+@pytest.mark.parametrize("kw,code", [
+    (dict(mode=0, desc=la.make_desc(1, 2, 128, 64, 64, 0, la.BF16)), 6),
+    (dict(mode=1, desc=la.make_desc(1, 2, 128, 64, 64, 0, la.BF16)), 6),
+    (dict(mode=6), 6), (dict(mode=9), 5),
+    (dict(scale=float("nan")), 2), (dict(momentum=float("inf")), 2),
+    (dict(M_out=None), 1),                            # momentum without a buffer
+    (dict(M_out=None, momentum=0.0), 1),              # M0 given without a buffer
+    (dict(W0=None), 1), (dict(O=None), 1),
+    (dict(M_out=ptr(4) + 4), 7),                      # buffer over W0
+    (dict(ws_bytes=1024), 8),                         # workspace too small
+])
+def test_muon_invalid_arguments(kw, code):
+    assert muoncall(**kw) == code
+
+
+@needs_lib
+def test_muon_workspace_holds_the_exchange():
+    d = la.make_desc(2, 8, 32768, 128, 128, 256, la.BF16)
+    plain = la.workspace_bytes(d, 2048, "large_chunk_swiglu")
+    muon = la.muon_workspace_bytes(d, 2048, "large_chunk_swiglu")
+    per_head = (16 + 1) * 3 * 128 * 128 * 4            # partial Gram matrices and their sums
+    assert plain > 0 and muon >= plain + 16 * per_head
+    assert la.muon_workspace_bytes(d, 2048, "large_chunk_swiglu_update_first") == muon
+    assert la.muon_workspace_bytes(d, 2048, "large_chunk_swiglu_last_layer") == 0
+    assert la.muon_workspace_bytes(la.make_desc(1, 2, 128, 64, 64, 0, la.BF16), 64, "large_chunk_linear") == 0
