@@ -142,7 +142,7 @@ def traffic_per_launch(name: str, s: dict):
 
 
 def run_workload(name: str, steps: int, warmup: int, flush_mb: int, other_order: bool = False, mode=None,
-                 momentum=None):
+                 momentum=None, muon=None):
     import torch
     import linear_attention_ttt_amd as la
 
@@ -158,7 +158,8 @@ def run_workload(name: str, steps: int, warmup: int, flush_mb: int, other_order:
     B, H, T, dv = s["B"], s["H"], s["T"], s["d_v"]
     desc = la.make_desc(B, H, T, s["d_k"], dv, s["d_h"], la.BF16 if dt == torch.bfloat16 else la.FP32,
                         la.O_FP32 if odt != dt else la.O_AS_INPUT)
-    nws = la.workspace_bytes(desc, s["chunk"], s["mode"])
+    nws = la.muon_workspace_bytes(desc, s["chunk"], s["mode"]) if muon is not None else \
+        la.workspace_bytes(desc, s["chunk"], s["mode"])
     nbytes, flops = algorithmic(s)
     # copies of the inputs and outputs for the steady-state loop: enough that their total exceeds the
     # caches (256 MB last-level cache) several times over
@@ -170,7 +171,7 @@ def run_workload(name: str, steps: int, warmup: int, flush_mb: int, other_order:
             t[k] = t[k].to(dt)
         t["O"] = torch.empty((B, H, T, dv), dtype=odt, device=dev)
         t["Wout"] = torch.empty_like(t["W0"])
-        t["M"] = torch.zeros_like(t["W0"]) if momentum is not None else None
+        t["M"] = torch.zeros_like(t["W0"]) if momentum is not None else None   # (Muon with momentum too)
         sets.append(t)
     del x
     ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
@@ -191,7 +192,15 @@ def run_workload(name: str, steps: int, warmup: int, flush_mb: int, other_order:
     def step(i=0, timing=None):
         t = sets[i % nsets]
         ptrs = [t[k].data_ptr() for k in ("Q", "K", "V", "eta", "W0")]
-        if momentum is not None:   # ttt_la_forward_momentum has no timed form: events around the whole call
+        if muon is not None:       # no timed form either
+            if timing is not None:
+                timing[0].record(sptr)
+            mp = t["M"].data_ptr() if t["M"] is not None else None
+            st = la.forward_muon_raw(*ptrs, mp, momentum or 0.0, muon, s["chunk"], s["mode"], desc, t["O"].data_ptr(),
+                                     t["Wout"].data_ptr(), mp, ws.data_ptr(), ws.numel(), sptr)
+            if timing is not None:
+                timing[1].record(sptr)
+        elif momentum is not None:   # ttt_la_forward_momentum has no timed form: events around the whole call
             if timing is not None:
                 timing[0].record(sptr)
             st = la.forward_momentum_raw(*ptrs, t["M"].data_ptr(), momentum, s["chunk"], s["mode"], desc,
@@ -210,8 +219,9 @@ def run_workload(name: str, steps: int, warmup: int, flush_mb: int, other_order:
 
     # reference call through the checked binding (also validates the raw arguments above)
     t0 = sets[0]
-    la.forward(t0["Q"], t0["K"], t0["V"], t0["eta"], t0["W0"], s["chunk"], s["mode"], out=t0["O"],
-               W_out=t0["Wout"], workspace=ws, out_dtype=odt)
+    if muon is None and momentum is None:
+        la.forward(t0["Q"], t0["K"], t0["V"], t0["eta"], t0["W0"], s["chunk"], s["mode"], out=t0["O"],
+                   W_out=t0["Wout"], workspace=ws, out_dtype=odt)
 
     for _ in range(warmup):
         evict(1)
@@ -255,7 +265,7 @@ def run_workload(name: str, steps: int, warmup: int, flush_mb: int, other_order:
     mean_s = float(ms.mean()) * 1e-3
     peak = HBM_PEAK_GBS if kbound == "hbm" else BF16_PEAK_TFLOPS
     achieved = kunits / kmean_s / (1e9 if kbound == "hbm" else 1e12)
-    plain = not (other_order or mode or momentum is not None)
+    plain = not (other_order or mode or momentum is not None or muon is not None)
     roof = {"bound": kbound, "achieved": achieved, "peak": peak, "unit": "GB/s" if kbound == "hbm" else "TFLOP/s",
             "frac": achieved / peak, "traffic": traffic_per_launch(name, s) if plain else None,
             "kernel": kname, "kernel_ms": float(kms.mean()), "kernel_ms_min": float(kms.min()),
@@ -264,7 +274,12 @@ def run_workload(name: str, steps: int, warmup: int, flush_mb: int, other_order:
             else (flops / mean_s / 1e12 / BF16_PEAK_TFLOPS),
             "steady_state_step_frac": (nbytes / (ss_ms * 1e-3) / 1e9 / HBM_PEAK_GBS) if kbound == "hbm"
             else (flops / (ss_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS)}
+    if not plain:
+        roof["kernel"] += " (whole call: the update-rule entries have no timed form)" if (
+            momentum is not None or muon is not None) else ""
     rec = dict(workload=name, mode=s["mode"], B=B, H=H, T=T, d=s["d_k"], d_h=s["d_h"], chunk=s["chunk"],
+               update_rule=("muon %g" % muon if muon is not None else "") +
+               (" momentum %g" % momentum if momentum is not None else "") or "descent",
                dtype=s["dtype"], o_dtype=s["o_dtype"], ms_per_step=float(ms.mean()), ms_min=float(ms.min()),
                ms_median=float(np.median(ms)), tokens_per_s=B * T / mean_s, token_heads_per_s=B * H * T / mean_s,
                steady_state=dict(ms_per_step=ss_ms, tokens_per_s=B * T / (ss_ms * 1e-3), input_sets=nsets,
@@ -388,6 +403,11 @@ def main():
     ap.add_argument("--momentum", type=float, default=None,
                     help="large-chunk linear workloads: run ttt_la_forward_momentum with this coefficient (the "
                          "kernel-timing loop then times whole calls); implies --no-others --no-backward")
+    ap.add_argument("--muon", type=float, default=None,
+                    help="SwiGLU workloads: run ttt_la_forward_muon with this scale (with --momentum too if given); "
+                         "implies --no-others --no-backward")
+    ap.add_argument("--no-variants", action="store_true",
+                    help="skip the update-rule records (momentum, Muon) of the large-chunk workloads")
     ap.add_argument("--mode", default=None,
                     help="run the workload in this mode instead of its own (same shapes; e.g. "
                          "large_chunk_swiglu_last_layer on the SwiGLU workload); implies --no-others")
@@ -415,9 +435,11 @@ def main():
         del src, dst
     if a.mode:
         a.no_others = True
-    if a.momentum is not None:
-        a.no_others = a.no_backward = True
-    head = run_workload(a.workload, a.steps, a.warmup, a.flush_mb, a.other_order, a.mode, a.momentum)
+    if a.momentum is not None or a.muon is not None:
+        a.no_others = a.no_backward = a.no_variants = True
+    if a.mode or a.other_order:
+        a.no_variants = True
+    head = run_workload(a.workload, a.steps, a.warmup, a.flush_mb, a.other_order, a.mode, a.momentum, a.muon)
     if not a.no_cpu:
         head["cpu_baseline"] = cpu_baseline(a.workload, head["mode"], target_s=15.0)
     print(f"# {a.workload}: {head['ms_per_step']:.4f} ms/step", file=sys.stderr, flush=True)
@@ -434,6 +456,21 @@ def main():
                 print(f"# {name}: {rec['ms_per_step']:.4f} ms/step", file=sys.stderr, flush=True)
             except Exception as e:  # a mode not built yet is reported, not fatal
                 others[name] = {"error": str(e)[:200]}
+    # the other update rules the LaCT review compares (momentum, Muon) on the large-chunk workloads
+    variants = {}
+    if not a.no_variants:
+        for key, name, mom, mu in (
+                ("linear momentum 0.9", "large_chunk_linear_bf16_B1H12T196608_d64_c4096", 0.9, None),
+                ("swiglu momentum 0.9", "large_chunk_swiglu_bf16_B2H8T32768_d128_dh256_c2048", 0.9, None),
+                ("swiglu muon 0.05", "large_chunk_swiglu_bf16_B2H8T32768_d128_dh256_c2048", None, 0.05),
+                ("swiglu muon 0.05 momentum 0.9", "large_chunk_swiglu_bf16_B2H8T32768_d128_dh256_c2048", 0.9, 0.05)):
+            try:
+                rec = run_workload(name, max(10, a.steps // 2), 3, a.flush_mb, momentum=mom, muon=mu)
+                variants[key] = {k: rec[k] for k in ("workload", "mode", "update_rule", "ms_per_step", "ms_min",
+                                                     "tokens_per_s", "steady_state", "hbm_frac", "bf16_mfma_frac")}
+                print(f"# {key}: {rec['ms_per_step']:.4f} ms/step", file=sys.stderr, flush=True)
+            except Exception as e:  # reported, not fatal
+                variants[key] = {"error": str(e)[:200]}
     # backward records: the headline workload, and (with the other workloads) every workload whose mode
     # has a backward (bf16 per-token and large-chunk linear)
     backward = {}
@@ -472,6 +509,7 @@ def main():
         "roofline": roof,
         "cpu_baseline": head.get("cpu_baseline"),
         "workloads": others,
+        "update_rules": variants,
         "backward": backward,
     }
     print(json.dumps(line), flush=True)
