@@ -14,6 +14,7 @@ from .ttt_oracle import (  # noqa: F401
     large_chunk_linear,
     large_chunk_linear_backward,
     large_chunk_swiglu,
+    large_chunk_swiglu_backward,
     linear_binding_grad,
     linear_binding_loss,
     newton_schulz5,
@@ -22,6 +23,9 @@ from .ttt_oracle import (  # noqa: F401
     per_token_linear_backward,
     silu,
     silu_prime,
+    silu_second,
+    swiglu_read_backward,
+    swiglu_step_vjp,
     swiglu_binding_grad,
     swiglu_binding_loss,
     swiglu_forward,

@@ -256,15 +256,146 @@ def large_chunk_linear_backward(Q, K, V, eta, W0, dO, dW_T, chunk, read_first=Tr
     return dQ, dK, dV, deta, G
 
 
-def backward(Q, K, V, eta, W0, dO, dW_T, chunk, mode):
+def silu_second(a):
+    """Second derivative of SiLU: ``s (1 - s) (2 + a (1 - 2 s))`` with ``s = sigmoid(a)``."""
+    s = 1.0 / (1.0 + np.exp(-a))
+    return s * (1.0 - s) * (2.0 + a * (1.0 - 2.0 * s))
+
+
+def swiglu_read_backward(X, W1, W3, W2, dY):
+    """Reverse-mode gradients of ``Y = f_W(X)`` (the SwiGLU MLP) given ``dY``:
+    ``(dX, (dW1, dW3, dW2))``.  With ``a = X W1``, ``b = X W3``,
+    ``h = silu(a) b``: ``dh = dY W2^T``, ``dW2 = h^T dY``,
+    ``da = dh b silu'(a)``, ``db = dh silu(a)``, ``dW1 = X^T da``,
+    ``dW3 = X^T db``, ``dX = da W1^T + db W3^T``."""
+    X, W1, W3, W2, dY = map(_f64, (X, W1, W3, W2, dY))
+    tr = lambda M: np.swapaxes(M, -1, -2)  # noqa: E731
+    a, b = X @ W1, X @ W3
+    h = silu(a) * b
+    dh = dY @ tr(W2)
+    da = dh * b * silu_prime(a)
+    db = dh * silu(a)
+    return da @ tr(W1) + db @ tr(W3), (tr(X) @ da, tr(X) @ db, tr(h) @ dY)
+
+
+def swiglu_step_vjp(K, V, eta, W1, W3, W2, D1, D3, D2):
+    """Vector-Jacobian product of the chunk step ``S(W, K, V, eta) = sum_i
+    eta_i grad_W <f_W(k_i), v_i>`` with the cotangent ``(D1, D3, D2)``.
+
+    ``<(D1, D3, D2), S> = sum_i eta_i <ydot_i, v_i> =: phi`` where ``ydot_i``
+    is the directional derivative of ``f_W(k_i)`` along the cotangent: with
+    ``a = k W1``, ``b = k W3``, ``s = silu(a)``, ``h = s b``,
+    ``adot = k D1``, ``bdot = k D3``, ``hdot = silu'(a) adot b + s bdot``,
+    ``ydot = hdot W2 + h D2``.  Writing ``g = v W2^T`` and ``r = v D2^T``,
+    ``phi_i / eta_i = sum_u hdot_u g_u + h_u r_u``, whose partial
+    derivatives (derived by hand) give
+      ``d/dv = eta ydot``, ``d/deta = <ydot, v>``,
+      ``Pa = silu''(a) adot b g + silu'(a) (bdot g + b r)`` (w.r.t. ``a``),
+      ``Pb = silu'(a) adot g + s r`` (``b``), ``Padot = silu'(a) b g``,
+      ``Pbdot = s g``, ``Pg = hdot`` (w.r.t. ``g``);
+      ``d/dk = eta (Pa W1^T + Pb W3^T + Padot D1^T + Pbdot D3^T)``,
+      ``d/dW1 = K^T (eta Pa)``, ``d/dW3 = K^T (eta Pb)``,
+      ``d/dW2 = (eta Pg)^T V``.
+    Returns ``(dK, dV, deta, (dW1, dW3, dW2))``."""
+    K, V, eta, W1, W3, W2, D1, D3, D2 = map(_f64, (K, V, eta, W1, W3, W2, D1, D3, D2))
+    tr = lambda M: np.swapaxes(M, -1, -2)  # noqa: E731
+    e = eta[..., None]
+    a, b = K @ W1, K @ W3
+    s, s1, s2 = silu(a), silu_prime(a), silu_second(a)
+    h = s * b
+    ad, bd = K @ D1, K @ D3
+    hd = s1 * ad * b + s * bd
+    g, r = V @ tr(W2), V @ tr(D2)
+    yd = hd @ W2 + h @ D2
+    Pa = s2 * ad * b * g + s1 * (bd * g + b * r)
+    Pb = s1 * ad * g + s * r
+    Pad = s1 * b * g
+    Pbd = s * g
+    dK = e * (Pa @ tr(W1) + Pb @ tr(W3) + Pad @ tr(D1) + Pbd @ tr(D3))
+    dV = e * yd
+    deta = np.sum(yd * V, axis=-1)
+    return dK, dV, deta, (tr(K) @ (e * Pa), tr(K) @ (e * Pb), tr(e * hd) @ V)
+
+
+def _normalize_backward(U, G):
+    """Gradient through ``W = U / max(||U column||, 1e-12)`` per column, given
+    the gradient ``G`` of ``W``: ``(G - w (w . G)) / n`` (``G / 1e-12`` at the
+    floor, where the map is linear)."""
+    n = np.sqrt(np.sum(U * U, axis=-2, keepdims=True))
+    w = U / np.maximum(n, NORM_EPS)
+    return np.where(n > NORM_EPS, (G - w * np.sum(w * G, axis=-2, keepdims=True)) / np.maximum(n, NORM_EPS),
+                    G / NORM_EPS)
+
+
+def large_chunk_swiglu_backward(Q, K, V, eta, W1, W3, W2, dO, dW_T, chunk, read_first=True, normalize=True,
+                                update_w1w3=True):
+    """Reverse-mode gradients of :func:`large_chunk_swiglu` (plain descent):
+    given ``dO`` and ``dW_T = (dW1, dW3, dW2)`` of the final weights, return
+    ``(dQ, dK, dV, deta, (dW1_0, dW3_0, dW2_0))``.
+
+    Derived by hand from the chunk loop, walked backwards.  Chunk c forms
+    ``U_c = W_{c-1} + S(W_{c-1})`` (``S`` the eta-weighted descent step, see
+    :func:`swiglu_step_vjp`) and ``W_c`` = its column normalisation; its
+    queries read ``R_c = W_{c-1}`` (``W_c`` when not ``read_first``).  With
+    ``G`` the gradient of the newest weights (``dW_T`` at the end), for each
+    chunk from the last: update-first read: ``dQ_c`` and ``G +=`` the read's
+    weight gradient at ``W_c`` (:func:`swiglu_read_backward`);
+    normalisation: ``dU = (G - w (w . G)) / n`` per column; step: the
+    weights before it get ``dU`` plus the step's vector-Jacobian product with
+    ``dU``, and ``dK_c``, ``dV_c``, ``deta_c`` come from the same product;
+    read-first read: ``dQ_c`` and the read's weight gradient at ``W_{c-1}``.
+    A matrix the loop does not update (``update_w1w3=False``) passes ``G`` on
+    unchanged and gets only the step's product (through the hidden features).
+    ``dW0`` is ``G`` after the first chunk."""
+    Q, K, V, eta, dO = map(_f64, (Q, K, V, eta, dO))
+    Ws = [tuple(_f64(w).copy() for w in (W1, W3, W2))]
+    Us = []
+    T = Q.shape[2]
+    starts = list(range(0, T, chunk))
+    upd = (update_w1w3, update_w1w3, True)
+    for s0 in starts:
+        e = min(s0 + chunk, T)
+        g = swiglu_binding_grad(K[:, :, s0:e], V[:, :, s0:e], eta[:, :, s0:e], *Ws[-1])
+        U = tuple(w - gg if u else w for w, gg, u in zip(Ws[-1], g, upd))
+        Us.append(U)
+        Ws.append(tuple(normalize_columns(x) if (normalize and u) else x for x, u in zip(U, upd)))
+    dQ, dK, dV = np.zeros_like(Q), np.zeros_like(K), np.zeros_like(V)
+    deta = np.zeros_like(eta)
+    G = [_f64(x).copy() for x in dW_T]
+    for c in range(len(starts) - 1, -1, -1):
+        s0, e = starts[c], min(starts[c] + chunk, T)
+        if not read_first:
+            dq, gr = swiglu_read_backward(Q[:, :, s0:e], *Ws[c + 1], dO[:, :, s0:e])
+            dQ[:, :, s0:e] = dq
+            G = [x + y for x, y in zip(G, gr)]
+        dU = [(_normalize_backward(u, x) if normalize else x) if up else np.zeros_like(x)
+              for u, x, up in zip(Us[c], G, upd)]
+        dk, dv, de, gs = swiglu_step_vjp(K[:, :, s0:e], V[:, :, s0:e], eta[:, :, s0:e], *Ws[c], *dU)
+        dK[:, :, s0:e], dV[:, :, s0:e], deta[:, :, s0:e] = dk, dv, de
+        G = [(d if up else x) + y for d, x, y, up in zip(dU, G, gs, upd)]
+        if read_first:
+            dq, gr = swiglu_read_backward(Q[:, :, s0:e], *Ws[c], dO[:, :, s0:e])
+            dQ[:, :, s0:e] = dq
+            G = [x + y for x, y in zip(G, gr)]
+    return dQ, dK, dV, deta, tuple(G)
+
+
+def backward(Q, K, V, eta, W0, dO, dW_T, chunk, mode, d_h=None):
     """Gradients ``(dQ, dK, dV, deta, dW0)`` by mode name, with the
-    library's argument order.  The per-token and large-chunk linear modes
-    have a backward."""
+    library's argument order.  For the SwiGLU modes ``W0`` and ``dW_T`` are
+    packed states and ``d_h`` is required; ``dW0`` is returned packed."""
     if mode in ("per_token_linear", "per_token_linear_exclusive"):
         return per_token_linear_backward(Q, K, V, eta, W0, dO, dW_T, inclusive=(mode == "per_token_linear"))
     if mode in ("large_chunk_linear", "large_chunk_linear_update_first"):
         return large_chunk_linear_backward(Q, K, V, eta, W0, dO, dW_T, chunk,
                                            read_first=(mode == "large_chunk_linear"))
+    if mode in ("large_chunk_swiglu", "large_chunk_swiglu_update_first", "large_chunk_swiglu_last_layer"):
+        d = Q.shape[-1]
+        last = mode == "large_chunk_swiglu_last_layer"
+        dq, dk, dv, de, G = large_chunk_swiglu_backward(
+            Q, K, V, eta, *swiglu_unpack(_f64(W0), d, d_h), dO, swiglu_unpack(_f64(dW_T), d, d_h), chunk,
+            read_first=(mode != "large_chunk_swiglu_update_first"), normalize=not last, update_w1w3=not last)
+        return dq, dk, dv, de, swiglu_pack(*G)
     raise ValueError(f"no backward for mode {mode!r}")
 
 
