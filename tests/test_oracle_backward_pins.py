@@ -126,7 +126,20 @@ def test_backward_dispatch():
         b = TO.large_chunk_linear_backward(Q, K, V, eta, W0, dO, dW, 4, read_first=rf)
         assert all(np.array_equal(x, y) for x, y in zip(a, b))
     with pytest.raises(ValueError):
-        TO.backward(Q, K, V, eta, W0, dO, dW, 64, "large_chunk_swiglu")
+        TO.backward(Q, K, V, eta, W0, dO, dW, 64, "no_such_mode")
+    # SwiGLU: packed states in and out, the three modes' flags
+    rng = np.random.default_rng(6)
+    B, H, T, d, dh = 1, 2, 7, 4, 6
+    Qs, Ks, Vs, dOs = (rng.standard_normal((B, H, T, d)) for _ in range(4))
+    es = 0.3 * rng.standard_normal((B, H, T))
+    Ws = [0.5 * rng.standard_normal(shp) for shp in ((B, H, d, dh), (B, H, d, dh), (B, H, dh, d))]
+    dWs = [rng.standard_normal(w.shape) for w in Ws]
+    for mode, kw in (("large_chunk_swiglu", {}), ("large_chunk_swiglu_update_first", dict(read_first=False)),
+                     ("large_chunk_swiglu_last_layer", dict(normalize=False, update_w1w3=False))):
+        a = TO.backward(Qs, Ks, Vs, es, TO.swiglu_pack(*Ws), dOs, TO.swiglu_pack(*dWs), 3, mode, d_h=dh)
+        b = TO.large_chunk_swiglu_backward(Qs, Ks, Vs, es, *Ws, dOs, dWs, 3, **kw)
+        assert all(np.array_equal(x, y) for x, y in zip(a[:4], b[:4]))
+        assert np.array_equal(a[4], TO.swiglu_pack(*b[4]))
 
 
 # ---------------------------------------------------------------------------
