@@ -279,8 +279,9 @@ def forward(Q, K, V, eta, W0, chunk: int, mode, *, out=None, W_out=None, workspa
 
 
 def backward(Q, K, V, eta, W0, dO, dW_out, chunk: int, mode="per_token_linear", *, workspace=None, stream=None):
-    """Gradients of the forward in the per-token and large-chunk linear modes (both read orders of
-    each): given the inputs of ``forward``,
+    """Gradients of the forward (with O in the input dtype) in every mode: per-token and large-chunk
+    linear (both read orders) and the three SwiGLU modes (``W0`` and ``dW_out`` packed like the
+    forward's state): given the inputs of ``forward``,
     ``dO`` (gradient of O, like V) and ``dW_out`` (gradient of the final
     memory, float32 like W0), return ``(dQ, dK, dV, deta, dW0)``, all
     float32.  Argument checks as in ``forward``."""
@@ -305,9 +306,16 @@ def backward(Q, K, V, eta, W0, dO, dW_out, chunk: int, mode="per_token_linear", 
         raise ValueError("Q, K must be [B,H,T,d_k], V and dO [B,H,T,d_v]")
     B, H, T, dk = Q.shape
     dv = V.shape[3]
-    if tuple(eta.shape) != (B, H, T) or tuple(W0.shape) != (B, H, dk, dv) or dW_out.shape != W0.shape:
+    dh = 0
+    if m in (LARGE_CHUNK_SWIGLU, LARGE_CHUNK_SWIGLU_UPDATE_FIRST, LARGE_CHUNK_SWIGLU_LAST_LAYER):
+        if W0.dim() != 3 or tuple(W0.shape[:2]) != (B, H) or W0.shape[2] % (3 * dk) != 0 or dv != dk:
+            raise ValueError("SwiGLU W0 must be [B,H,3*d*d_h] with d = d_k = d_v")
+        dh = W0.shape[2] // (3 * dk)
+        if tuple(eta.shape) != (B, H, T) or dW_out.shape != W0.shape:
+            raise ValueError("eta must be [B,H,T] and dW_out shaped like W0")
+    elif tuple(eta.shape) != (B, H, T) or tuple(W0.shape) != (B, H, dk, dv) or dW_out.shape != W0.shape:
         raise ValueError("eta must be [B,H,T], W0 and dW_out [B,H,d_k,d_v]")
-    desc = make_desc(B, H, T, dk, dv, 0, BF16 if Q.dtype == torch.bfloat16 else FP32)
+    desc = make_desc(B, H, T, dk, dv, dh, BF16 if Q.dtype == torch.bfloat16 else FP32)
     f32 = dict(dtype=torch.float32, device=dev)
     dQ, dK, dV = torch.empty(Q.shape, **f32), torch.empty(K.shape, **f32), torch.empty(V.shape, **f32)
     deta, dW0 = torch.empty_like(eta), torch.empty_like(W0)

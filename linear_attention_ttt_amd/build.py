@@ -16,7 +16,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libttt_la.so")
-SOURCES = ["host.cpp", "per_token.hip", "large_chunk_linear.hip", "large_chunk_swiglu.hip", "noalloc.hip"]
+SOURCES = ["host.cpp", "per_token.hip", "large_chunk_linear.hip", "large_chunk_swiglu.hip",
+           "large_chunk_swiglu_backward.hip", "noalloc.hip"]
 ARCH = "gfx950"
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
          # packed fp32 vector ops stay off: only scalar and MFMA fp32 paths

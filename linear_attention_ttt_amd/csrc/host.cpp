@@ -252,13 +252,17 @@ static bool backward_ok(const ttt_la_desc& d, int64_t chunk, int32_t mode) {
   switch (method_of(mode)) {
     case TTT_LA_PER_TOKEN_LINEAR: return ttt::per_token_backward_supported(d.d_k, d.d_v, chunk, d.io_dtype);
     case TTT_LA_LARGE_CHUNK_LINEAR: return d.io_dtype == TTT_LA_BF16;
+    case TTT_LA_LARGE_CHUNK_SWIGLU: return d.io_dtype == TTT_LA_BF16;   // (supported: d = 128, d_h = 256)
   }
   return false;
 }
 
 static size_t backward_workspace(const ttt_la_desc& d, int64_t chunk, int32_t mode) {
-  if (method_of(mode) == TTT_LA_PER_TOKEN_LINEAR) return ttt::per_token_backward_workspace(d.B, d.H, d.T, d.d_k);
-  return ttt::large_chunk_linear_backward_workspace(d.B, d.H, d.T, d.d_k, chunk);
+  switch (method_of(mode)) {
+    case TTT_LA_PER_TOKEN_LINEAR: return ttt::per_token_backward_workspace(d.B, d.H, d.T, d.d_k);
+    case TTT_LA_LARGE_CHUNK_LINEAR: return ttt::large_chunk_linear_backward_workspace(d.B, d.H, d.T, d.d_k, chunk);
+  }
+  return ttt::large_chunk_swiglu_backward_workspace(d.B, d.H, d.T, chunk);
 }
 
 size_t ttt_la_backward_workspace_bytes(const ttt_la_desc* desc, int64_t chunk, int32_t mode) {
@@ -281,7 +285,7 @@ int ttt_la_backward(const void* Q, const void* K, const void* V, const float* et
 
   const size_t es = d.io_dtype == TTT_LA_BF16 ? 2 : 4;
   const size_t ntok = (size_t)(d.B * d.H * d.T);
-  const size_t st_bytes = (size_t)state_elems(d, TTT_LA_PER_TOKEN_LINEAR) * 4;
+  const size_t st_bytes = (size_t)state_elems(d, method_of(mode)) * 4;
   const Range ins[7] = {range(Q, ntok * d.d_k * es), range(K, ntok * d.d_k * es), range(V, ntok * d.d_v * es),
                         range(eta, ntok * 4), range(W0, st_bytes), range(dO, ntok * d.d_v * es),
                         range(dW_out, st_bytes)};
@@ -296,9 +300,14 @@ int ttt_la_backward(const void* Q, const void* K, const void* V, const float* et
 
   ttt::BackwardArgs a{Q,  K,  V,    eta, W0,        dO,  dW_out, dQ,  dK,  dV,          deta,
                          dW0, workspace, d.B, d.H, d.T, d.d_k, d.d_v, chunk, d.io_dtype, other_order(mode) ? 1 : 0};
-  const hipError_t e = method_of(mode) == TTT_LA_PER_TOKEN_LINEAR
-                           ? ttt::launch_per_token_backward(a, (hipStream_t)stream)
-                           : ttt::launch_large_chunk_linear_backward(a, (hipStream_t)stream);
+  hipError_t e;
+  switch (method_of(mode)) {
+    case TTT_LA_PER_TOKEN_LINEAR: e = ttt::launch_per_token_backward(a, (hipStream_t)stream); break;
+    case TTT_LA_LARGE_CHUNK_LINEAR: e = ttt::launch_large_chunk_linear_backward(a, (hipStream_t)stream); break;
+    default:
+      e = ttt::launch_large_chunk_swiglu_backward(a, mode == TTT_LA_LARGE_CHUNK_SWIGLU_LAST_LAYER ? 1 : 0,
+                                                  (hipStream_t)stream);
+  }
   return e == hipSuccess ? TTT_LA_OK : TTT_LA_ERR_HIP;
 }
 

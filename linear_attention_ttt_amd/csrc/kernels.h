@@ -97,5 +97,13 @@ bool large_chunk_swiglu_supported(int64_t d, int64_t dh, int64_t chunk, int dtyp
 size_t large_chunk_swiglu_workspace(int64_t B, int64_t H, int64_t T, int64_t d, int64_t dh, int64_t chunk,
                                     int muon = 0);
 hipError_t launch_large_chunk_swiglu(const LargeChunkArgs& a, hipStream_t stream, const Timing& tm);
+// the recurrence again with every chunk's float32 weights into dump [BH][nchunks][3 d d_h] and the column
+// norms before each normalisation into dnorm [BH][nchunks][640]; a.ws is a forward workspace of
+// swiglu_forward_workspace_plain(BH, nchunks) bytes; a.W_out receives the final weights
+hipError_t launch_swiglu_recur_dump(const LargeChunkArgs& a, float* dump, float* dnorm, hipStream_t stream);
+size_t swiglu_forward_workspace_plain(int64_t BH, int64_t nchunks);
+// backward of the SwiGLU modes (2, 5, 6): recomputation, then the reverse chunk loop
+size_t large_chunk_swiglu_backward_workspace(int64_t B, int64_t H, int64_t T, int64_t chunk);
+hipError_t launch_large_chunk_swiglu_backward(const BackwardArgs& a, int last_layer_only, hipStream_t stream);
 
 }  // namespace ttt

@@ -116,6 +116,10 @@ struct SwRule {
   float beta;        // momentum coefficient
   float muon_scale;  // scale of the orthogonalised step (RULE 2)
   float* ns;         // RULE 2: per head [NSL][3][d][d] partial Gram matrices, then [3][d][d] their sums
+  // DUMP (the backward's recomputation): after chunk c, the float32 weights (packed W1 | W3 | W2) into
+  // dump[head][c], and the column norms before the normalisation into dnorm[head][c][W1 256 | W3 256 | W2 128]
+  float* dump;
+  float* dnorm;
 };
 constexpr size_t NS_HEAD_FLOATS = (size_t)(SW_NSL + 1) * 3 * SW_D * SW_D;
 
@@ -312,7 +316,7 @@ __device__ __attribute__((noinline)) void swiglu_muon_steps(RecurLds& S, const S
   __syncthreads();
 }
 
-template <int RULE>
+template <int RULE, bool DUMP = false>
 __global__ __launch_bounds__(SW_WAVES * 64, 1) void swiglu_recur_kernel(
     const bf16* __restrict__ K, const bf16* __restrict__ V, const float* __restrict__ eta,
     const float* __restrict__ W0, float* __restrict__ Wout, bf16* __restrict__ states, float* __restrict__ ss2,
@@ -660,6 +664,9 @@ __global__ __launch_bounds__(SW_WAVES * 64, 1) void swiglu_recur_kernel(
       ss += __shfl_xor(ss, 16);
       ss += __shfl_xor(ss, 32);
       const float inv = 1.0f / fmaxf(sqrtf(ss), 1e-12f);
+      if constexpr (DUMP) {
+        if (l < 16) R.dnorm[((size_t)bh * nchunks + c) * 640 + w * DH + u0 + u] = sqrtf(ss);
+      }
 #pragma unroll
       for (int k = 0; k < 8; ++k) *(floatx4*)(Wm + w13i(r0 + 4 * k, u)) = x[k] * inv;
     } else if (w < 4) {
@@ -691,10 +698,25 @@ __global__ __launch_bounds__(SW_WAVES * 64, 1) void swiglu_recur_kernel(
         ss += __hip_atomic_load(&ss2[(((size_t)bh * 2 + (c & 1)) * SW_NSL + s) * D + d], __ATOMIC_RELAXED,
                                 __HIP_MEMORY_SCOPE_AGENT);
       const float inv = 1.0f / fmaxf(sqrtf(ss), 1e-12f);
+      if constexpr (DUMP) {
+        if (sl == 0) R.dnorm[((size_t)bh * nchunks + c) * 640 + 2 * DH + d] = sqrtf(ss);
+      }
 #pragma unroll
       for (int k = 0; k < NS / 4; ++k) *(floatx4*)(S.w2 + w2i(4 * k, d)) *= inv;
     }
     __syncthreads();
+    if constexpr (DUMP) {   // the weights after this chunk's update
+      float* Wd = R.dump + ((size_t)bh * nchunks + c) * 3 * D * DH;
+      for (int i = tid; i < D * NS; i += NT) {
+        const int d = i / NS, u = i % NS;
+        Wd[(size_t)d * DH + u0 + u] = S.w1[w13i(d, u)];
+        Wd[(size_t)D * DH + (size_t)d * DH + u0 + u] = S.w3[w13i(d, u)];
+      }
+      for (int i = tid; i < NS * D; i += NT) {
+        const int u = i / D, d = i % D;
+        Wd[2 * (size_t)D * DH + (size_t)(u0 + u) * D + d] = S.w2[w2i(u, d)];
+      }
+    }
     if (update_first)
       store_state(c);
     else if (c + 1 < nchunks)
@@ -1026,6 +1048,52 @@ size_t large_chunk_swiglu_workspace(int64_t B, int64_t H, int64_t T, int64_t d, 
   return sw_layout(B * H, (T + chunk - 1) / chunk, muon).total;
 }
 
+// The backward's recomputation of the recurrence (plain descent): the weights after every chunk and the
+// column norms before each normalisation, into dump / dnorm (see SwRule); no outputs are read.  The
+// forward workspace (states, counters) is that of ttt_la_forward for the same problem.
+static void spin_params(int* limit, unsigned* extra);
+hipError_t launch_swiglu_recur_dump(const LargeChunkArgs& a, float* dump, float* dnorm, hipStream_t stream) {
+  const int BH = (int)(a.B * a.H);
+  const int T = (int)a.T, chunk = (int)a.chunk;
+  const int nchunks = (int)((a.T + a.chunk - 1) / a.chunk);
+  const SwLayout lay = sw_layout(BH, nchunks, 0);
+  unsigned char* ws = (unsigned char*)a.ws;
+  bf16* states = (bf16*)(ws + lay.states);
+  float* ss2 = (float*)(ws + lay.ss2);
+  unsigned* counters = (unsigned*)(ws + lay.counters);
+  unsigned* err = (unsigned*)(ws + lay.err);
+  const int nz = BH + 1;
+  hipLaunchKernelGGL(zero_u32_kernel, dim3((nz + 255) / 256), dim3(256), 0, stream, counters, nz);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  auto krec = swiglu_recur_kernel<0, true>;
+  const size_t lds_r = sizeof(RecurLds);
+  if ((e = hipFuncSetAttribute((const void*)krec, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_r)) !=
+      hipSuccess)
+    return e;
+  int dev = 0, ncu = 0, per_cu = 0;
+  if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
+  if ((e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
+  if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)krec, SW_WAVES * 64, lds_r)) != hipSuccess)
+    return e;
+  const int heads_per_launch = (per_cu * ncu) / SW_NSL;
+  if (heads_per_launch < 1) return hipErrorLaunchOutOfResources;
+  int spin_limit;
+  unsigned spin_extra;
+  spin_params(&spin_limit, &spin_extra);
+  const SwRule R{nullptr, nullptr, 0.f, 0.f, nullptr, dump, dnorm};
+  for (int h0 = 0; h0 < BH; h0 += heads_per_launch) {
+    const int nh = std::min(heads_per_launch, BH - h0);
+    hipLaunchKernelGGL(krec, dim3(nh * SW_NSL), dim3(SW_WAVES * 64), lds_r, stream, (const bf16*)a.K,
+                       (const bf16*)a.V, a.eta, a.W0, a.W_out, states, ss2, counters, err, T, chunk, nchunks, h0,
+                       0, a.last_layer_only ? 1 : 0, 0, spin_limit, spin_extra, R);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+size_t swiglu_forward_workspace_plain(int64_t BH, int64_t nchunks) { return sw_layout(BH, nchunks, 0).total; }
+
 // O_c = f_{W_{c-1}}(Q_c) for every chunk, from the stored states
 static hipError_t launch_read(const LargeChunkArgs& a, const bf16* states, int nchunks, const unsigned* err,
                               hipStream_t stream) {
@@ -1071,7 +1139,7 @@ hipError_t launch_large_chunk_swiglu(const LargeChunkArgs& a, hipStream_t stream
   // the update rule: plain descent, momentum (M_out given), Muon (with or without momentum)
   const int rule = a.muon ? 2 : (a.M_out ? 1 : 0);
   auto krec = rule == 2 ? swiglu_recur_kernel<2> : rule == 1 ? swiglu_recur_kernel<1> : swiglu_recur_kernel<0>;
-  const SwRule R{a.M0, a.M_out, a.momentum, a.muon_scale, (float*)(ws + lay.ns)};
+  const SwRule R{a.M0, a.M_out, a.momentum, a.muon_scale, (float*)(ws + lay.ns), nullptr, nullptr};
   // the recurrence needs every workgroup of a head resident at once
   const size_t lds_r = sizeof(RecurLds);
   e = hipFuncSetAttribute((const void*)krec, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_r);

@@ -232,8 +232,10 @@ def bcall(desc=None, mode=0, chunk=64, ws_bytes=1 << 34, **kw):
     (dict(Q=None), 1), (dict(dO=None), 1), (dict(dW=None), 1), (dict(dQ=None), 1), (dict(deta=None), 1),
     (dict(dW0=None), 1), (dict(ws=None), 1), (dict(W0=None), 1),
     (dict(mode=2), 2), (dict(mode=7), 5), (dict(chunk=0), 3),
-    (dict(mode=2, desc=la.make_desc(1, 2, 128, 128, 128, 256, la.BF16)), 6),    # no SwiGLU backward
-    (dict(mode=5, desc=la.make_desc(1, 2, 128, 128, 128, 256, la.BF16)), 6),
+    (dict(mode=2, desc=la.make_desc(1, 2, 128, 128, 128, 256, la.FP32)), 6),    # SwiGLU backward: bf16 only
+    (dict(mode=2, desc=la.make_desc(1, 2, 128, 128, 128, 256, la.BF16), ws_bytes=1024), 8),   # its workspace
+    (dict(mode=5, desc=la.make_desc(1, 2, 128, 128, 128, 256, la.BF16, la.O_FP32)), 6),   # dO has io_dtype
+    (dict(mode=6, desc=la.make_desc(1, 2, 128, 128, 128, 128, la.BF16)), 6),     # d_h = 128 not compiled
     (dict(mode=1, desc=la.make_desc(1, 2, 128, 64, 64, 0, la.FP32)), 6),
     (dict(desc=la.make_desc(1, 2, 128, 96, 96, 0, la.BF16)), 6),
     (dict(chunk=256), 6),
@@ -330,3 +332,14 @@ def test_muon_workspace_holds_the_exchange():
     assert la.muon_workspace_bytes(d, 2048, "large_chunk_swiglu_update_first") == muon
     assert la.muon_workspace_bytes(d, 2048, "large_chunk_swiglu_last_layer") == 0
     assert la.muon_workspace_bytes(la.make_desc(1, 2, 128, 64, 64, 0, la.BF16), 64, "large_chunk_linear") == 0
+
+
+@needs_lib
+def test_swiglu_backward_workspace():
+    d = la.make_desc(2, 8, 32768, 128, 128, 256, la.BF16)
+    n = la.backward_workspace_bytes(d, 2048, "large_chunk_swiglu")
+    # at least: the recomputation's float32 weights of every chunk (16 heads x 16 chunks x 384 KB)
+    assert n > 16 * 16 * 3 * 128 * 256 * 4
+    assert la.backward_workspace_bytes(d, 2048, "large_chunk_swiglu_update_first") == n
+    assert la.backward_workspace_bytes(d, 2048, "large_chunk_swiglu_last_layer") == n
+    assert la.backward_workspace_bytes(la.make_desc(2, 8, 32768, 128, 128, 256, la.BF16, la.O_FP32), 2048, 2) == 0
