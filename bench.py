@@ -313,7 +313,7 @@ def run_backward(name: str, steps: int, warmup: int, flush_mb: int, mode: str):
     dW = torch.from_numpy(gr["dW"]).to(dev)
     del x, gr
     B, H, T, d = s["B"], s["H"], s["T"], s["d_k"]
-    desc = la.make_desc(B, H, T, d, d, 0, la.BF16)
+    desc = la.make_desc(B, H, T, d, d, s["d_h"], la.BF16)
     ws = torch.empty(la.backward_workspace_bytes(desc, s["chunk"], s["mode"]), dtype=torch.uint8, device=dev)
     outs = [torch.empty((B, H, T, d), dtype=torch.float32, device=dev) for _ in range(3)]
     deta = torch.empty((B, H, T), dtype=torch.float32, device=dev)
@@ -346,12 +346,19 @@ def run_backward(name: str, steps: int, warmup: int, flush_mb: int, mode: str):
     torch.cuda.synchronize()
     ms = np.array([a.elapsed_time(b) for a, b in zip(starts, ends)])
     n = B * H * T
-    nbytes = n * (4 * d * 2 + 4) + n * (3 * d * 4 + 4) + 3 * B * H * d * d * 4
+    state = int(np.prod(workloads.state_shape(s))) * 4
+    nbytes = n * (4 * d * 2 + 4) + n * (3 * d * 4 + 4) + 3 * state
     mean_s = float(ms.mean()) * 1e-3
     rec = dict(workload=name, mode=s["mode"], ms_per_step=float(ms.mean()), ms_min=float(ms.min()),
                tokens_per_s=B * T / mean_s, algorithmic_bytes=nbytes, hbm_GBps=nbytes / mean_s / 1e9,
                hbm_frac=nbytes / mean_s / 1e9 / HBM_PEAK_GBS,
                note="float32 gradients")
+    if method_of(s["mode"]).startswith("large_chunk_swiglu"):
+        # per token-head: the step's vector-Jacobian product 30 d d_h, the read's gradients 16 d d_h, the
+        # recomputed recurrence 12 d d_h (all as bf16 MFMA products; the hi + lo splits not counted)
+        flops = n * 58 * d * s["d_h"]
+        rec.update(algorithmic_flops=flops, bf16_mfma_TFLOPs=flops / mean_s / 1e12,
+                   bf16_mfma_frac=flops / mean_s / 1e12 / BF16_PEAK_TFLOPS)
     del t, dO, dW, ws, outs, deta, dW0, flush, flush_rd
     torch.cuda.empty_cache()
     return rec
@@ -471,15 +478,14 @@ def main():
                 print(f"# {key}: {rec['ms_per_step']:.4f} ms/step", file=sys.stderr, flush=True)
             except Exception as e:  # reported, not fatal
                 variants[key] = {"error": str(e)[:200]}
-    # backward records: the headline workload, and (with the other workloads) every workload whose mode
-    # has a backward (bf16 per-token and large-chunk linear)
+    # backward records: the headline workload, and (with the other workloads) every bf16 workload
     backward = {}
     if not a.no_backward:
         names = [a.workload] + ([] if a.no_others else [n for n in workloads.WORKLOADS if n != a.workload])
         for name in names:
             sw = workloads.spec(name)
             mode = a.mode or (OTHER_ORDER[sw["mode"]] if a.other_order else sw["mode"])
-            if sw["dtype"] != "bf16" or method_of(mode) not in ("per_token_linear", "large_chunk_linear"):
+            if sw["dtype"] != "bf16":
                 continue
             try:
                 backward[name] = run_backward(name, max(10, a.steps // 2), 3, a.flush_mb, mode)
