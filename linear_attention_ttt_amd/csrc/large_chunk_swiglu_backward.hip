@@ -49,12 +49,22 @@ __device__ __forceinline__ float to_f(float x) { return x; }
 __device__ __forceinline__ float to_f(bf16 x) { return (float)x; }
 
 // ---------------------------------------------------------------------------
-// C[b] = alpha * A[b] B[b] + beta * C[b] over a batch (blockIdx.z): A is M x K,
-// B is K x N, addressed by element strides (one of each operand's strides is
-// 1: the tile loads run along it), C row-major with row stride sCm.  64 x 64
-// tiles, 32-deep steps staged in LDS as float32 [m][k] and [n][k]; wave
-// (wm, wn) computes the 32 x 32 quarter (wm, wn) with 16x16x32 MFMAs on the
-// bf16 hi + lo split of its operands.  Bounds-checked on M, N and K.
+// C = A B (+ beta C) over a batch, with the contraction optionally split:
+// blockIdx.z = batch * nsplit + split, split s covering k in [s kper,
+// min(K, (s + 1) kper)) and writing its partial product to C + s bCs.  A is
+// M x K, B is K x N, addressed by element strides; one stride of each operand
+// is 1.  An operand whose contraction index is contiguous (A: sAk = 1, B:
+// sBk = 1) is staged in LDS as [row][k] and read as 16-byte MFMA fragments;
+// otherwise (ATR / BTR) it is staged as [k][row] in its own order and read
+// with the transposed LDS read.  Float32 operands are split into bf16 hi +
+// lo planes on the way into LDS (three products per pair, float32
+// accumulation); bf16 operands are exact and have no lo plane.
+// 128 x 128 tiles, 32-deep steps, 4 waves of 64 x 64 (4 x 4 16x16x32 MFMA
+// tiles each); the next step's tiles are loaded into registers while the
+// current one is multiplied.  Requirements (checked by the host): the
+// contiguous extent of every operand is a whole number of tiles (M, N
+// multiples of 128 where they are contiguous, K a multiple of 32 where it
+// is); the strided extent may be ragged (rows past it read as zero).
 // ---------------------------------------------------------------------------
 struct GemmArgs {
   const void* A;
@@ -63,77 +73,178 @@ struct GemmArgs {
   int M, N, K;
   long long sAm, sAk, sBk, sBn, sCm;
   long long bA, bB, bC;
-  float alpha, beta;
+  float beta;
+  int nsplit, kper;
+  long long bCs;
 };
-constexpr int GBM = 64, GBN = 64, GBK = 32, GLD = GBK + 4;
+constexpr int GT = 128, GK = 32;
+constexpr int PLANE_ROW = GK * 2 + 16;          // [row][k] plane: 64 bytes of k + 16 bytes of padding
+constexpr int PLANE_TR_ROW = GT * 2 + 32;       // [k][row] plane: 256 bytes of rows + 32 bytes of padding
+constexpr int PLANE_BYTES = GT * PLANE_ROW;     // 10240 >= GK * PLANE_TR_ROW = 9216
 
-template <typename TA, typename TB>
-__global__ __launch_bounds__(256) void sw_gemm_kernel(GemmArgs g) {
-  __shared__ __attribute__((aligned(16))) float As[GBM * GLD];
-  __shared__ __attribute__((aligned(16))) float Bs[GBN * GLD];
-  const long long bz = blockIdx.z;
+template <typename T>
+struct GemmOperand {
+  static constexpr bool F32 = sizeof(T) == 4;
+  static constexpr int LOADS = F32 ? 4 : 2;     // 16-byte loads per thread per tile
+};
+
+// One operand tile (rows r0.., k in [k0, kend)) into registers: 16-byte pieces, zeros past the ragged extent.
+template <typename T, bool TR>
+__device__ __forceinline__ void gemm_load(u32x4 (&v)[GemmOperand<T>::LOADS], const T* P, long long s_row,
+                                          long long s_k, int r0, int rend, int k0, int kend) {
+  constexpr bool F32 = GemmOperand<T>::F32;
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int q = 0; q < GemmOperand<T>::LOADS; ++q) {
+    const int idx = tid + 256 * q;
+    bool ok;
+    const T* src;
+    if (!TR) {      // [row][k]: F32 8 pieces of 4 per row, bf16 4 pieces of 8
+      const int row = F32 ? idx >> 3 : idx >> 2, pc = F32 ? idx & 7 : idx & 3;
+      ok = r0 + row < rend;
+      src = P + (long long)(r0 + row) * s_row + (k0 + pc * (F32 ? 4 : 8));
+    } else {        // [k][row]: F32 32 pieces of 4 per k, bf16 16 pieces of 8
+      const int kr = F32 ? idx >> 5 : idx >> 4, pc = F32 ? idx & 31 : idx & 15;
+      ok = k0 + kr < kend;
+      src = P + (long long)(k0 + kr) * s_k + (r0 + pc * (F32 ? 4 : 8));
+    }
+    v[q] = ok ? *(const u32x4*)src : u32x4{0u, 0u, 0u, 0u};
+  }
+}
+
+// The registers of gemm_load into the hi (and lo) planes.
+template <typename T, bool TR>
+__device__ __forceinline__ void gemm_store(const u32x4 (&v)[GemmOperand<T>::LOADS], unsigned char* hi,
+                                           unsigned char* lo) {
+  constexpr bool F32 = GemmOperand<T>::F32;
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int q = 0; q < GemmOperand<T>::LOADS; ++q) {
+    const int idx = tid + 256 * q;
+    int off;
+    if (!TR) {
+      const int row = F32 ? idx >> 3 : idx >> 2, pc = F32 ? idx & 7 : idx & 3;
+      off = row * PLANE_ROW + pc * (F32 ? 8 : 16);
+    } else {
+      const int kr = F32 ? idx >> 5 : idx >> 4, pc = F32 ? idx & 31 : idx & 15;
+      off = kr * PLANE_TR_ROW + pc * (F32 ? 8 : 16);
+    }
+    if (F32) {
+      const floatx4 f = __builtin_bit_cast(floatx4, v[q]);
+      const uint2 s0 = split2(f[0], f[1]), s1 = split2(f[2], f[3]);
+      *(uint2*)(hi + off) = uint2{s0.x, s1.x};
+      *(uint2*)(lo + off) = uint2{s0.y, s1.y};
+    } else {
+      *(u32x4*)(hi + off) = v[q];
+    }
+  }
+}
+
+// MFMA fragment of rows rb .. rb + 15 (lane: row rb + l % 16, k = 8 (l / 16) .. + 7) from a plane.
+template <bool TR>
+__device__ __forceinline__ bf16x8 gemm_frag(const unsigned char* plane, int rb) {
+  const int l = threadIdx.x & 63, g = l >> 4, i = l & 15;
+  if (!TR) return *(const bf16x8*)(plane + (rb + i) * PLANE_ROW + g * 16);
+  const unsigned char* p = plane + (8 * g + (i >> 2)) * PLANE_TR_ROW + (rb + 4 * (i & 3)) * 2;
+  const bf16x4 a = lds_read_tr16(p), b = lds_read_tr16(p + 4 * PLANE_TR_ROW);
+  return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+
+template <typename TA, typename TB, bool ATR, bool BTR>
+__global__ __launch_bounds__(256, 2) void sw_gemm_kernel(GemmArgs g) {
+  constexpr bool AF = GemmOperand<TA>::F32, BF = GemmOperand<TB>::F32;
+  __shared__ __attribute__((aligned(16))) unsigned char lds[4 * PLANE_BYTES];
+  unsigned char* ahi = lds;
+  unsigned char* alo = lds + PLANE_BYTES;
+  unsigned char* bhi = lds + 2 * PLANE_BYTES;
+  unsigned char* blo = lds + 3 * PLANE_BYTES;
+  const int nsplit = g.nsplit;
+  const long long bz = blockIdx.z / nsplit;
+  const int split = blockIdx.z % nsplit;
   const TA* A = (const TA*)g.A + bz * g.bA;
   const TB* B = (const TB*)g.B + bz * g.bB;
-  float* C = g.C + bz * g.bC;
-  const int m0 = blockIdx.y * GBM, n0 = blockIdx.x * GBN;
+  float* C = g.C + bz * g.bC + split * g.bCs;
+  const int m0 = blockIdx.y * GT, n0 = blockIdx.x * GT;
+  const int kbeg = split * g.kper, kend = min(g.K, kbeg + g.kper);
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, gq = l >> 4, li = l & 15;
   const int wm = w >> 1, wn = w & 1;
-  floatx4 acc[2][2];
+  // operand A rows are m (row stride sAm, k stride sAk); operand B rows are n (sBn, sBk)
+  const long long a_row = g.sAm, a_k = g.sAk, b_row = g.sBn, b_k = g.sBk;
+  floatx4 acc[4][4];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
-  const bool a_kfast = g.sAk == 1, b_kfast = g.sBk == 1;
-  for (int k0 = 0; k0 < g.K; k0 += GBK) {
-    for (int i = tid; i < GBM * GBK; i += 256) {
-      const int mm = a_kfast ? i / GBK : i % GBM, kk = a_kfast ? i % GBK : i / GBM;
-      const int m = m0 + mm, k = k0 + kk;
-      As[mm * GLD + kk] = (m < g.M && k < g.K) ? to_f(A[m * g.sAm + k * g.sAk]) : 0.f;
-    }
-    for (int i = tid; i < GBN * GBK; i += 256) {
-      const int nn = b_kfast ? i / GBK : i % GBN, kk = b_kfast ? i % GBK : i / GBN;
-      const int n = n0 + nn, k = k0 + kk;
-      Bs[nn * GLD + kk] = (n < g.N && k < g.K) ? to_f(B[k * g.sBk + n * g.sBn]) : 0.f;
-    }
+    for (int j = 0; j < 4; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+  u32x4 va[GemmOperand<TA>::LOADS], vb[GemmOperand<TB>::LOADS];
+  if (kbeg < kend) {
+    gemm_load<TA, ATR>(va, A, a_row, a_k, m0, g.M, kbeg, kend);
+    gemm_load<TB, BTR>(vb, B, b_row, b_k, n0, g.N, kbeg, kend);
+  }
+  for (int k0 = kbeg; k0 < kend; k0 += GK) {
+    gemm_store<TA, ATR>(va, ahi, alo);
+    gemm_store<TB, BTR>(vb, bhi, blo);
     __syncthreads();
-    bf16x8 ah[2], al[2], bh[2], bl[2];
+    if (k0 + GK < kend) {
+      gemm_load<TA, ATR>(va, A, a_row, a_k, m0, g.M, k0 + GK, kend);
+      gemm_load<TB, BTR>(vb, B, b_row, b_k, n0, g.N, k0 + GK, kend);
+    }
+    bf16x8 bh[4], bl[4];
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const float* pa = As + (32 * wm + 16 * t + li) * GLD + 8 * gq;
-      split8(*(const floatx4*)pa, *(const floatx4*)(pa + 4), ah[t], al[t]);
-      const float* pb = Bs + (32 * wn + 16 * t + li) * GLD + 8 * gq;
-      split8(*(const floatx4*)pb, *(const floatx4*)(pb + 4), bh[t], bl[t]);
+    for (int j = 0; j < 4; ++j) {
+      bh[j] = gemm_frag<BTR>(bhi, 64 * wn + 16 * j);
+      if (BF) bl[j] = gemm_frag<BTR>(blo, 64 * wn + 16 * j);
     }
 #pragma unroll
-    for (int tm = 0; tm < 2; ++tm)
+    for (int i = 0; i < 4; ++i) {
+      const bf16x8 ah = gemm_frag<ATR>(ahi, 64 * wm + 16 * i);
+      bf16x8 al;
+      if (AF) al = gemm_frag<ATR>(alo, 64 * wm + 16 * i);
 #pragma unroll
-      for (int tn = 0; tn < 2; ++tn) {
-        acc[tm][tn] = mfma16(ah[tm], bh[tn], acc[tm][tn]);
-        acc[tm][tn] = mfma16(ah[tm], bl[tn], acc[tm][tn]);
-        acc[tm][tn] = mfma16(al[tm], bh[tn], acc[tm][tn]);
+      for (int j = 0; j < 4; ++j) {
+        acc[i][j] = mfma16(ah, bh[j], acc[i][j]);
+        if (BF) acc[i][j] = mfma16(ah, bl[j], acc[i][j]);
+        if (AF) acc[i][j] = mfma16(al, bh[j], acc[i][j]);
       }
+    }
     __syncthreads();
   }
 #pragma unroll
-  for (int tm = 0; tm < 2; ++tm)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int tn = 0; tn < 2; ++tn)
+    for (int r = 0; r < 4; ++r) {
+      const int m = m0 + 64 * wm + 16 * i + 4 * gq + r;
+      if (m >= g.M) continue;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int m = m0 + 32 * wm + 16 * tm + 4 * gq + r, n = n0 + 32 * wn + 16 * tn + li;
-        if (m < g.M && n < g.N) {
-          float* p = C + (long long)m * g.sCm + n;
-          const float v = g.alpha * acc[tm][tn][r];
-          *p = g.beta != 0.f ? v + g.beta * *p : v;
-        }
+      for (int j = 0; j < 4; ++j) {
+        const int n = n0 + 64 * wn + 16 * j + li;
+        float* p = C + (long long)m * g.sCm + n;
+        *p = g.beta != 0.f ? acc[i][j][r] + g.beta * *p : acc[i][j][r];
       }
+    }
 }
 
+// Launch with the operand orientations taken from the strides; nsplit > 1 splits the contraction into
+// pieces of kper (a multiple of GK) whose partial products go to C + s bCs.
 template <typename TA, typename TB>
-hipError_t gemm(const GemmArgs& g, int batch, hipStream_t stream) {
+hipError_t gemm(GemmArgs g, int batch, hipStream_t stream, int nsplit = 1, long long bCs = 0) {
   if (g.M <= 0 || g.N <= 0) return hipSuccess;
-  hipLaunchKernelGGL((sw_gemm_kernel<TA, TB>), dim3((g.N + GBN - 1) / GBN, (g.M + GBM - 1) / GBM, batch), dim3(256), 0,
-                     stream, g);
+  const bool atr = g.sAk != 1, btr = g.sBk != 1;
+  // the contiguous extent of each operand must be whole tiles (or whole k steps)
+  if ((atr ? (g.sAm != 1 || g.M % GT) : (g.K % GK)) || (btr ? (g.sBn != 1 || g.N % GT) : (g.K % GK)) || g.N % GT)
+    return hipErrorInvalidValue;
+  if (nsplit < 1) nsplit = 1;
+  g.kper = (((g.K + nsplit - 1) / nsplit) + GK - 1) / GK * GK;
+  g.nsplit = nsplit;
+  g.bCs = bCs;
+  const dim3 grid((unsigned)(g.N / GT), (unsigned)((g.M + GT - 1) / GT), (unsigned)(batch * nsplit));
+  if (atr && btr)
+    hipLaunchKernelGGL((sw_gemm_kernel<TA, TB, true, true>), grid, dim3(256), 0, stream, g);
+  else if (atr)
+    hipLaunchKernelGGL((sw_gemm_kernel<TA, TB, true, false>), grid, dim3(256), 0, stream, g);
+  else if (btr)
+    hipLaunchKernelGGL((sw_gemm_kernel<TA, TB, false, true>), grid, dim3(256), 0, stream, g);
+  else
+    hipLaunchKernelGGL((sw_gemm_kernel<TA, TB, false, false>), grid, dim3(256), 0, stream, g);
   return hipGetLastError();
 }
 
@@ -247,38 +358,45 @@ __global__ __launch_bounds__(256) void sw_bwd_prep(const float* __restrict__ G, 
   }
 }
 
-// G (packed W1 | W3 | W2 per head) from the chunk's terms:
+// G (packed W1 | W3 | W2 per head) from the chunk's terms, each the sum of its split partials in a fixed order
+// (J13, A13: s13 partials of [BH][d][2 d_h]; J2, A2: s2 partials of [BH][d_h][d]):
 //   add_read_only: G += A (the read's weight gradient: A13 [d][W1 | W3 parts], A2 [d_h][d]);
 //   otherwise: G = base + J (+ A when with_read), base = dU (from Wcat / W2cat) for an updated matrix, G
 //   itself for a matrix the loop does not update (W1, W3 in the last-layer mode).
 __global__ __launch_bounds__(256) void sw_bwd_gupdate(float* __restrict__ G, const float* __restrict__ Wcat,
                                                       const float* __restrict__ W2cat, const float* __restrict__ J13,
                                                       const float* __restrict__ J2, const float* __restrict__ A13,
-                                                      const float* __restrict__ A2, int add_read_only, int with_read,
-                                                      int last_only) {
-  const long long h = blockIdx.y;
+                                                      const float* __restrict__ A2, int s13, int s2,
+                                                      int add_read_only, int with_read, int last_only) {
+  const long long h = blockIdx.y, BH = gridDim.y;
   const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
   if (i >= 3 * BP) return;
   float* g = G + h * 3 * BP + i;
+  auto psum = [](const float* P, int n, long long stride, long long off) {
+    float x = 0.f;
+    for (int s = 0; s < n; ++s) x += P[s * stride + off];
+    return x;
+  };
   float a, j, base;
   if (i < 2 * BP) {
     const int m = (int)(i / BP);
     const long long k = i % BP, d = k / BDH, u = k % BDH;
-    a = A13 ? A13[h * BD * 2 * BDH + d * 2 * BDH + m * BDH + u] : 0.f;
+    const long long off = h * BD * 2 * BDH + d * 2 * BDH + m * BDH + u, stride = BH * BD * 2 * BDH;
+    a = A13 ? psum(A13, s13, stride, off) : 0.f;
     if (add_read_only) {
       *g += a;
       return;
     }
-    j = J13[h * BD * 2 * BDH + d * 2 * BDH + m * BDH + u];
+    j = psum(J13, s13, stride, off);
     base = last_only ? *g : Wcat[h * BD * 4 * BDH + d * 4 * BDH + (2 + m) * BDH + u];
   } else {
     const long long k = i - 2 * BP;
-    a = A2 ? A2[h * BP + k] : 0.f;
+    a = A2 ? psum(A2, s2, BH * BP, h * BP + k) : 0.f;
     if (add_read_only) {
       *g += a;
       return;
     }
-    j = J2[h * BP + k];
+    j = psum(J2, s2, BH * BP, h * BP + k);
     base = W2cat[h * 2 * BP + BP + k];
   }
   *g = base + j + (with_read ? a : 0.f);
@@ -311,9 +429,20 @@ struct BwdSwLayout {
   size_t fws, wfin, dump, dnorm, wcat, w2cat, z1, e1, z2, e2, e3, j13, j2, a13, a2, total;
 };
 size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
+// Split of the products that contract over a chunk's tokens: enough workgroups (about 512) for the chip, at
+// least 128 tokens per split, at most 16 splits.
+int token_split(int tiles_per_head, int64_t BH, int64_t Cc) {
+  const int64_t want = 512 / std::max<int64_t>(1, tiles_per_head * BH);
+  const int64_t most = std::max<int64_t>(1, Cc / 128);
+  return (int)std::max<int64_t>(1, std::min<int64_t>(std::min<int64_t>(want, most), 16));
+}
+constexpr int TILES13 = (BD / GT) * (2 * BDH / GT);   // a [d][2 d_h] product
+constexpr int TILES2 = (BDH / GT) * (BD / GT);        // a [d_h][d] product
+
 BwdSwLayout bwd_sw_layout(int64_t BH, int64_t T, int64_t chunk) {
   BwdSwLayout L;
   const int64_t nch = (T + chunk - 1) / chunk, Cc = std::min<int64_t>(chunk, T);
+  const int64_t s13 = token_split(TILES13, BH, Cc), s2 = token_split(TILES2, BH, Cc);
   size_t o = 0;
   L.fws = o; o += al256(swiglu_forward_workspace_plain(BH, nch));
   L.wfin = o; o += al256((size_t)BH * 3 * BP * 4);
@@ -326,10 +455,10 @@ BwdSwLayout bwd_sw_layout(int64_t BH, int64_t T, int64_t chunk) {
   L.z2 = o; o += al256((size_t)BH * Cc * 2 * BDH * 4);
   L.e2 = o; o += al256((size_t)BH * Cc * 2 * BDH * 4);
   L.e3 = o; o += al256((size_t)BH * Cc * BDH * 4);
-  L.j13 = o; o += al256((size_t)BH * BD * 2 * BDH * 4);
-  L.j2 = o; o += al256((size_t)BH * BP * 4);
-  L.a13 = o; o += al256((size_t)BH * BD * 2 * BDH * 4);
-  L.a2 = o; o += al256((size_t)BH * BP * 4);
+  L.j13 = o; o += al256((size_t)s13 * BH * BD * 2 * BDH * 4);
+  L.j2 = o; o += al256((size_t)s2 * BH * BP * 4);
+  L.a13 = o; o += al256((size_t)s13 * BH * BD * 2 * BDH * 4);
+  L.a2 = o; o += al256((size_t)s2 * BH * BP * 4);
   L.total = o;
   return L;
 }
@@ -341,7 +470,8 @@ GemmArgs gargs(const void* A, long long sAm, long long sAk, long long bA, const 
   g.M = M; g.N = N; g.K = K;
   g.sAm = sAm; g.sAk = sAk; g.sBk = sBk; g.sBn = sBn; g.sCm = sCm;
   g.bA = bA; g.bB = bB; g.bC = bC;
-  g.alpha = 1.f; g.beta = beta;
+  g.beta = beta;
+  g.nsplit = 1; g.kper = K; g.bCs = 0;
   return g;
 }
 
@@ -381,6 +511,8 @@ hipError_t launch_large_chunk_swiglu_backward(const BackwardArgs& a, int last_on
   float* dV = (float*)a.dV;
   const long long SP = 3 * BP;      // elements of a packed state
   const long long cap = std::min<long long>(C, T);   // leading dimension (tokens) of the chunk buffers
+  const int s13 = token_split(TILES13, BH, cap), s2 = token_split(TILES2, BH, cap);
+  const long long p13 = (long long)BH * BD * 2 * BDH, p2 = (long long)BH * BP;   // partial strides
   hipError_t e;
   const long long ncopy = (long long)BH * SP;
   hipLaunchKernelGGL(sw_bwd_copy, dim3((unsigned)((ncopy + 255) / 256)), dim3(256), 0, stream, G, a.dW, ncopy);
@@ -420,9 +552,10 @@ hipError_t launch_large_chunk_swiglu_backward(const BackwardArgs& a, int last_on
         return e2;
     // (Q^T da | Q^T db), (silu(a) b)^T dO
     if ((e2 = gemm<bf16, float>(gargs(Qc, 1, BD, T * BD, Eq, 2 * BDH, 1, cap * 2 * BDH, A13, 2 * BDH, BD * 2 * BDH,
-                                      BD, 2 * BDH, Cc), BH, stream)) != hipSuccess)
+                                      BD, 2 * BDH, Cc), BH, stream, s13, p13)) != hipSuccess)
       return e2;
-    return gemm<float, bf16>(gargs(Hq, 1, BDH, cap * BDH, dOc, BD, 1, T * BD, A2, BD, BP, BDH, BD, Cc), BH, stream);
+    return gemm<float, bf16>(gargs(Hq, 1, BDH, cap * BDH, dOc, BD, 1, T * BD, A2, BD, BP, BDH, BD, Cc), BH, stream, s2,
+                             p2);
   };
 
   for (int c = nch - 1; c >= 0; --c) {
@@ -435,7 +568,7 @@ hipError_t launch_large_chunk_swiglu_backward(const BackwardArgs& a, int last_on
     if (!read_first) {   // the chunk's queries read W_c: their gradient reaches G before the normalisation
       if ((e = read_phase(Wc, wc_stride, c0, Cc)) != hipSuccess) return e;
       hipLaunchKernelGGL(sw_bwd_gupdate, dim3((unsigned)((3 * BP + 255) / 256), BH), dim3(256), 0, stream, G, Wcat,
-                         W2cat, J13, J2, A13, A2, 1, 0, last_only);
+                         W2cat, J13, J2, A13, A2, s13, s2, 1, 0, last_only);
       if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     hipLaunchKernelGGL(sw_bwd_prep, dim3(640 / 4, BH), dim3(256), 0, stream, G, Wc, wc_stride, dnorm + (long long)c * 640,
@@ -466,14 +599,14 @@ hipError_t launch_large_chunk_swiglu_backward(const BackwardArgs& a, int last_on
     if ((e = hipGetLastError()) != hipSuccess) return e;
     // J13 = K^T (eta Pa | eta Pb), J2 = (eta hdot)^T V
     if ((e = gemm<bf16, float>(gargs(Kc, 1, BD, T * BD, E1, 4 * BDH, 1, cap * 4 * BDH, J13, 2 * BDH, BD * 2 * BDH, BD,
-                                     2 * BDH, Cc), BH, stream)) != hipSuccess)
+                                     2 * BDH, Cc), BH, stream, s13, p13)) != hipSuccess)
       return e;
-    if ((e = gemm<float, bf16>(gargs(E3, 1, BDH, cap * BDH, Vc, BD, 1, T * BD, J2, BD, BP, BDH, BD, Cc), BH, stream)) !=
-        hipSuccess)
+    if ((e = gemm<float, bf16>(gargs(E3, 1, BDH, cap * BDH, Vc, BD, 1, T * BD, J2, BD, BP, BDH, BD, Cc), BH, stream, s2,
+                               p2)) != hipSuccess)
       return e;
     if (read_first && (e = read_phase(Wp, wp_stride, c0, Cc)) != hipSuccess) return e;
     hipLaunchKernelGGL(sw_bwd_gupdate, dim3((unsigned)((3 * BP + 255) / 256), BH), dim3(256), 0, stream, G, Wcat, W2cat,
-                       J13, J2, A13, A2, 0, read_first ? 1 : 0, last_only);
+                       J13, J2, A13, A2, s13, s2, 0, read_first ? 1 : 0, last_only);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   return hipSuccess;
