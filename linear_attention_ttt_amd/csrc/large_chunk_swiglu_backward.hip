@@ -27,10 +27,12 @@
 // (Q^T da, Q^T db, (silu(a) b)^T dO).
 //
 // Every chunk's weights and column norms come from running the recurrence
-// again with a float32 dump (launch_swiglu_recur_dump).  Each step above is a
-// batched product over the heads on bf16 MFMA with float32 operands split
-// into bf16 hi + lo (three products: hi hi, hi lo, lo hi) and float32
-// accumulation, or an elementwise kernel; the host walks the chunks.
+// again with a float32 dump (launch_swiglu_recur_dump).  The products are
+// batched over the heads on bf16 MFMA with float32 operands split into bf16
+// hi + lo (three products: hi hi, hi lo, lo hi; two when the other operand is
+// bf16 input) and float32 accumulation; the products of the tokens with the
+// weights run fused with the elementwise factors they feed
+// (sw_bwd_pair_kernel); the host walks the chunks.
 #include <algorithm>
 
 #include "device_common.h"
@@ -250,117 +252,246 @@ hipError_t gemm(GemmArgs g, int batch, hipStream_t stream, int nsplit = 1, long 
 
 __device__ __forceinline__ float sigm(float a) { return 1.0f / (1.0f + expf(-a)); }
 
-// The step's elementwise part for chunk tokens t < Cc, units u < d_h (one thread each; grid.y = head):
-// Z1 [t][a | b | adot | bdot], Z2 [t][g | r] -> E1 [t][eta Pa | eta Pb | eta Padot | eta Pbdot],
-// E2 [t][hdot | h], E3 [t][eta hdot].
-__global__ __launch_bounds__(256) void sw_bwd_step_elem(const float* __restrict__ Z1, const float* __restrict__ Z2,
-                                                        const float* __restrict__ eta, float* __restrict__ E1,
-                                                        float* __restrict__ E2, float* __restrict__ E3, int Cc,
-                                                        long long ldz, int T, int c0) {
-  const long long h = blockIdx.y;
-  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
-  if (i >= (long long)Cc * BDH) return;
-  const long long t = i / BDH;
-  const int u = (int)(i % BDH);
-  const float* z1 = Z1 + h * ldz * 4 * BDH + t * 4 * BDH;
-  const float* z2 = Z2 + h * ldz * 2 * BDH + t * 2 * BDH;
-  const float a = z1[u], b = z1[BDH + u], ad = z1[2 * BDH + u], bd = z1[3 * BDH + u];
-  const float gg = z2[u], r = z2[BDH + u];
-  const float e = eta[h * T + c0 + t];
-  const float sg = sigm(a), s = a * sg, s1 = sg * (1.0f + a * (1.0f - sg));
-  const float s2 = sg * (1.0f - sg) * (2.0f + a * (1.0f - 2.0f * sg));
-  const float hh = s * b, hd = s1 * ad * b + s * bd;
-  float* e1 = E1 + h * ldz * 4 * BDH + t * 4 * BDH;
-  e1[u] = e * (s2 * ad * b * gg + s1 * (bd * gg + b * r));
-  e1[BDH + u] = e * (s1 * ad * gg + s * r);
-  e1[2 * BDH + u] = e * (s1 * b * gg);
-  e1[3 * BDH + u] = e * (s * gg);
-  float* e2 = E2 + h * ldz * 2 * BDH + t * 2 * BDH;
-  e2[u] = hd;
-  e2[BDH + u] = hh;
-  E3[h * ldz * BDH + t * BDH + u] = e * hd;
+// Column of the concatenated step operand Wcat ([d][1024] per head) holding part p (0: the weights W1 | W3,
+// 1: their tangents dU1 | dU3) of matrix m (0: W1, 1: W3) at hidden unit u: 32-unit slices, the slice's
+// W1 and W3 (or dU1 and dU3) columns side by side, so a 32-unit slice of all four is two 64-column pieces.
+// E1 uses the same column order, and J13 (= K^T E1's first 512 columns) the part-0 order.
+__device__ __forceinline__ int wcat_col(int p, int m, int u) { return p * 512 + (u >> 5) * 64 + m * 32 + (u & 31); }
+
+// ---------------------------------------------------------------------------
+// The two products of a 128-token tile that feed an elementwise step, with the
+// elementwise step as their epilogue (nothing but its results goes to memory):
+//   Z1 = X1 B1, X1 the tile's bf16 rows [t][d], B1 a 128-column fp32 block
+//        made of two 64-column pieces of a [d][ld1] matrix;
+//   Z2 = X2 B2^T, X2 bf16 [t][d], B2 a 64-row fp32 block of a [rows][d] matrix
+//        made of two 32-row pieces.
+// Wave w takes token rows 32 w .. 32 w + 31 of both, so that the values of one
+// (token, unit) in every column piece sit in one lane.  MODE 0 (the step's
+// vector-Jacobian factors, grid.x = 8 slices of 32 units): Z1 = k [W1 | W3 |
+// dU1 | dU3] (a, b, adot, bdot), Z2 = v [W2 ; dU2]^T (g, r) -> E1 [t][1024]
+// (wcat_col order: eta Pa, eta Pb | eta Padot, eta Pbdot), E2 [t][hdot | h],
+// E3 [t][eta hdot].  MODE 1 (the read's, grid.x = 4 slices of 64 units):
+// Z1 = q [R1 | R3] (a, b), Z2 = dO R2^T (dh) -> Eq [t][da | db], Hq [t][silu(a) b].
+// K = d = 128 in 32-deep steps, operands staged as in sw_gemm_kernel (B1 as a
+// [k][n] plane read transposed, B2 as [n][k]), the next step loaded while the
+// current one is multiplied.
+// ---------------------------------------------------------------------------
+struct PairArgs {
+  const bf16* X1;       // [BH][T][d], already offset to the chunk
+  const bf16* X2;
+  const float* B1;      // per head + bh * sB1
+  long long sB1;
+  int ld1, piece1, slice1;      // column c -> (c / 64) piece1 + s slice1 + c % 64
+  const float* B2;      // rows of d floats, per head + bh * sB2
+  long long sB2;
+  int piece2, slice2;           // row c -> (c / 32) piece2 + s slice2 + c % 32
+  const float* eta;     // [BH][T]
+  float* O1;            // MODE 0: E1, MODE 1: Eq   ([BH][cap][...])
+  float* O2;            // MODE 0: E2, MODE 1: Hq
+  float* O3;            // MODE 0: E3
+  int T, c0, Cc;
+  long long cap;
+};
+
+template <int MODE>
+__global__ __launch_bounds__(256, 2) void sw_bwd_pair_kernel(PairArgs a) {
+  constexpr int X_PLANE = GT * PLANE_ROW;            // [t][k] bf16: 10240
+  constexpr int B1_PLANE = GK * PLANE_TR_ROW;        // [k][n] bf16: 9216
+  constexpr int B2_PLANE = 64 * PLANE_ROW;           // [n][k] bf16: 5120
+  __shared__ __attribute__((aligned(16))) unsigned char lds[2 * X_PLANE + 2 * B1_PLANE + 2 * B2_PLANE];
+  unsigned char* x1p = lds;
+  unsigned char* x2p = lds + X_PLANE;
+  unsigned char* b1h = lds + 2 * X_PLANE;
+  unsigned char* b1l = b1h + B1_PLANE;
+  unsigned char* b2h = b1l + B1_PLANE;
+  unsigned char* b2l = b2h + B2_PLANE;
+  const int sl = blockIdx.x, t0 = blockIdx.y * GT;
+  const long long bh = blockIdx.z;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, gq = l >> 4, li = l & 15;
+  const long long xoff = bh * (long long)a.T * BD;
+  const bf16* X1 = a.X1 + xoff;
+  const bf16* X2 = a.X2 + xoff;
+  const float* B1 = a.B1 + bh * a.sB1;
+  const float* B2 = a.B2 + bh * a.sB2;
+  const int Cc = a.Cc;
+  // loads of one 32-deep step: X1, X2 (2 pieces of 8 bf16 each per thread), B1 (4 pieces of 4 floats: 32 k
+  // rows x 32 pieces), B2 (2 pieces of 4 floats: 64 rows x 8 pieces)
+  u32x4 v1[2], v2[2], vb1[4], vb2[2];
+  auto load = [&](int k0) {
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int idx = tid + 256 * q, row = idx >> 2, pc = idx & 3;
+      const bool ok = t0 + row < Cc;
+      const long long o = (long long)(t0 + row) * BD + k0 + 8 * pc;
+      v1[q] = ok ? *(const u32x4*)(X1 + o) : u32x4{0u, 0u, 0u, 0u};
+      v2[q] = ok ? *(const u32x4*)(X2 + o) : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int idx = tid + 256 * q, kr = idx >> 5, c = (idx & 31) * 4;
+      vb1[q] = *(const u32x4*)(B1 + (long long)(k0 + kr) * a.ld1 + (c >> 6) * a.piece1 + sl * a.slice1 + (c & 63));
+    }
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int idx = tid + 256 * q, row = idx >> 3, pc = idx & 7;
+      const int r = (row >> 5) * a.piece2 + sl * a.slice2 + (row & 31);
+      vb2[q] = *(const u32x4*)(B2 + (long long)r * BD + k0 + 4 * pc);
+    }
+  };
+  auto store = [&]() {
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int idx = tid + 256 * q, row = idx >> 2, pc = idx & 3;
+      *(u32x4*)(x1p + row * PLANE_ROW + pc * 16) = v1[q];
+      *(u32x4*)(x2p + row * PLANE_ROW + pc * 16) = v2[q];
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int idx = tid + 256 * q, kr = idx >> 5, pc = idx & 31;
+      const floatx4 f = __builtin_bit_cast(floatx4, vb1[q]);
+      const uint2 s0 = split2(f[0], f[1]), s1 = split2(f[2], f[3]);
+      *(uint2*)(b1h + kr * PLANE_TR_ROW + pc * 8) = uint2{s0.x, s1.x};
+      *(uint2*)(b1l + kr * PLANE_TR_ROW + pc * 8) = uint2{s0.y, s1.y};
+    }
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int idx = tid + 256 * q, row = idx >> 3, pc = idx & 7;
+      const floatx4 f = __builtin_bit_cast(floatx4, vb2[q]);
+      const uint2 s0 = split2(f[0], f[1]), s1 = split2(f[2], f[3]);
+      *(uint2*)(b2h + row * PLANE_ROW + pc * 8) = uint2{s0.x, s1.x};
+      *(uint2*)(b2l + row * PLANE_ROW + pc * 8) = uint2{s0.y, s1.y};
+    }
+  };
+  floatx4 z1[2][8], z2[2][4];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) z1[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) z2[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+  }
+  load(0);
+  for (int k0 = 0; k0 < BD; k0 += GK) {
+    store();
+    __syncthreads();
+    if (k0 + GK < BD) load(k0 + GK);
+    bf16x8 x1[2], x2[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      x1[i] = gemm_frag<false>(x1p, 32 * w + 16 * i);
+      x2[i] = gemm_frag<false>(x2p, 32 * w + 16 * i);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const bf16x8 bh = gemm_frag<true>(b1h, 16 * j), bl = gemm_frag<true>(b1l, 16 * j);
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        z1[i][j] = mfma16(x1[i], bh, z1[i][j]);
+        z1[i][j] = mfma16(x1[i], bl, z1[i][j]);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const bf16x8 bh = gemm_frag<false>(b2h, 16 * j), bl = gemm_frag<false>(b2l, 16 * j);
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        z2[i][j] = mfma16(x2[i], bh, z2[i][j]);
+        z2[i][j] = mfma16(x2[i], bl, z2[i][j]);
+      }
+    }
+    __syncthreads();
+  }
+  // epilogue: lane (gq, li) holds rows 32 w + 16 i + 4 gq + r, columns 16 j + li of every piece
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = t0 + 32 * w + 16 * i + 4 * gq + r;
+      if (t >= Cc) continue;
+      const long long orow = bh * a.cap + t;
+      if (MODE == 0) {
+        const float e = a.eta[bh * a.T + a.c0 + t];
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+          const float av = z1[i][jj][r], bv = z1[i][2 + jj][r], ad = z1[i][4 + jj][r], bd = z1[i][6 + jj][r];
+          const float gg = z2[i][jj][r], rr = z2[i][2 + jj][r];
+          const float sg = sigm(av), sv = av * sg, s1 = sg * (1.0f + av * (1.0f - sg));
+          const float s2 = sg * (1.0f - sg) * (2.0f + av * (1.0f - 2.0f * sg));
+          const float hh = sv * bv, hd = s1 * ad * bv + sv * bd;
+          const int u = 32 * sl + 16 * jj + li;
+          float* e1 = a.O1 + orow * 4 * BDH;
+          e1[wcat_col(0, 0, u)] = e * (s2 * ad * bv * gg + s1 * (bd * gg + bv * rr));
+          e1[wcat_col(0, 1, u)] = e * (s1 * ad * gg + sv * rr);
+          e1[wcat_col(1, 0, u)] = e * (s1 * bv * gg);
+          e1[wcat_col(1, 1, u)] = e * (sv * gg);
+          float* e2 = a.O2 + orow * 2 * BDH;
+          e2[u] = hd;
+          e2[BDH + u] = hh;
+          a.O3[orow * BDH + u] = e * hd;
+        }
+      } else {
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const float av = z1[i][jj][r], bv = z1[i][4 + jj][r], dh = z2[i][jj][r];
+          const float sg = sigm(av), sv = av * sg, s1 = sg * (1.0f + av * (1.0f - sg));
+          const int u = 64 * sl + 16 * jj + li;
+          float* eq = a.O1 + orow * 2 * BDH;
+          eq[u] = dh * bv * s1;
+          eq[BDH + u] = dh * sv;
+          a.O2[orow * BDH + u] = sv * bv;
+        }
+      }
+    }
 }
 
-// The read's elementwise part: Zq [t][a | b], Dh [t][dh] -> Eq [t][da | db], Hq [t][silu(a) b].
-__global__ __launch_bounds__(256) void sw_bwd_read_elem(const float* __restrict__ Zq, const float* __restrict__ Dh,
-                                                        float* __restrict__ Eq, float* __restrict__ Hq, int Cc,
-                                                        long long ldz) {
-  const long long h = blockIdx.y;
-  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
-  if (i >= (long long)Cc * BDH) return;
-  const long long t = i / BDH;
-  const int u = (int)(i % BDH);
-  const float* zq = Zq + h * ldz * 2 * BDH + t * 2 * BDH;
-  const float a = zq[u], b = zq[BDH + u];
-  const float dh = Dh[h * ldz * BDH + t * BDH + u];
-  const float sg = sigm(a), s = a * sg, s1 = sg * (1.0f + a * (1.0f - sg));
-  float* eq = Eq + h * ldz * 2 * BDH + t * 2 * BDH;
-  eq[u] = dh * b * s1;
-  eq[BDH + u] = dh * s;
-  Hq[h * ldz * BDH + t * BDH + u] = s * b;
-}
-
-// Per head, one wave per column: the normalisation's backward dU of G (packed W1 | W3 | W2) at the chunk's
-// normalised weights Wc and norms nrm, and the operand blocks of the step at the weights before it (Wp):
-// Wcat [d][W1 | W3 | dU1 | dU3] (d x 4 d_h), W2cat [W2 ; dU2] (2 d_h x d).  Columns 0..255: W1, 256..511:
-// W3, 512..639: W2.  last_only: dU1 = dU3 = 0, dU2 = G2.
+// Per head: the normalisation's backward dU of G (packed W1 | W3 | W2) at the chunk's normalised weights Wc and
+// norms nrm, and the step's operands at the weights before it (Wp): Wcat [d][1024] in wcat_col order (part 0:
+// W1, W3; part 1: dU1, dU3), W2cat [W2 ; dU2] (2 d_h x d).  Block (matrix m, group of 64 columns): 4 row groups
+// x 64 columns, each thread summing w . G over its rows, the 4 partials added in a fixed order through LDS.
+// Norm columns: 0..255 W1, 256..511 W3, 512..639 W2.  last_only: dU1 = dU3 = 0, dU2 = G2.
 __global__ __launch_bounds__(256) void sw_bwd_prep(const float* __restrict__ G, const float* __restrict__ Wc,
                                                    long long wc_stride, const float* __restrict__ nrm,
                                                    long long nrm_stride, const float* __restrict__ Wp,
                                                    long long wp_stride, float* __restrict__ Wcat,
                                                    float* __restrict__ W2cat, int last_only) {
+  __shared__ float part[4][64];
   const long long h = blockIdx.y;
-  const int col = blockIdx.x * 4 + (threadIdx.x >> 6), l = threadIdx.x & 63;
-  const float* g = G + h * 3 * BP;
-  const float* wc = Wc + h * wc_stride;
-  const float* wp = Wp + h * wp_stride;
+  const int grp = blockIdx.x, m = grp < 4 ? 0 : grp < 8 ? 1 : 2;
+  const int col = (m < 2 ? (grp & 3) : grp - 8) * 64 + (threadIdx.x & 63), rg = threadIdx.x >> 6;
+  const int ld = m < 2 ? BDH : BD, rows = m < 2 ? BD : BDH;
+  const long long base = (long long)m * BP;
+  const float* g = G + h * 3 * BP + base;
+  const float* wc = Wc + h * wc_stride + base;
+  const float* wp = Wp + h * wp_stride + base;
+  float dot = 0.f;
+  for (int r = rg; r < rows; r += 4) dot += g[(long long)r * ld + col] * wc[(long long)r * ld + col];
+  part[rg][threadIdx.x & 63] = dot;
+  __syncthreads();
+  const int cl = threadIdx.x & 63;
+  dot = ((part[0][cl] + part[1][cl]) + part[2][cl]) + part[3][cl];
+  const float n = nrm[h * nrm_stride + (m < 2 ? m * BDH + col : 2 * BDH + col)];
   float* wcat = Wcat + h * BD * 4 * BDH;
-  float* w2cat = W2cat + h * 2 * BDH * BD;
-  if (col < 2 * BDH) {              // a column of W1 or W3: d = l, l + 64
-    const int m = col / BDH, u = col % BDH;
-    const long long base = m * BP;
-    float gv[2], wv[2], dot = 0.f;
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int d = l + 64 * j;
-      gv[j] = g[base + (long long)d * BDH + u];
-      wv[j] = wc[base + (long long)d * BDH + u];
-      dot += gv[j] * wv[j];
-      wcat[(long long)d * 4 * BDH + m * BDH + u] = wp[base + (long long)d * BDH + u];
-    }
-    dot = wave_sum(dot);
-    const float n = nrm[h * nrm_stride + col];
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int d = l + 64 * j;
-      const float du = last_only ? 0.f : (n > BNORM_EPS ? (gv[j] - wv[j] * dot) / n : gv[j] / BNORM_EPS);
-      wcat[(long long)d * 4 * BDH + (2 + m) * BDH + u] = du;
-    }
-  } else {                          // a column of W2: units u = l, l + 64, l + 128, l + 192
-    const int dcol = col - 2 * BDH;
-    float gv[4], wv[4], dot = 0.f;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int u = l + 64 * j;
-      gv[j] = g[2 * BP + (long long)u * BD + dcol];
-      wv[j] = wc[2 * BP + (long long)u * BD + dcol];
-      dot += gv[j] * wv[j];
-      w2cat[(long long)u * BD + dcol] = wp[2 * BP + (long long)u * BD + dcol];
-    }
-    dot = wave_sum(dot);
-    const float n = last_only ? 0.f : nrm[h * nrm_stride + col];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int u = l + 64 * j;
-      const float du = last_only ? gv[j] : (n > BNORM_EPS ? (gv[j] - wv[j] * dot) / n : gv[j] / BNORM_EPS);
-      w2cat[(long long)(BDH + u) * BD + dcol] = du;
+  float* w2cat = W2cat + h * 2 * BP;
+  for (int r = rg; r < rows; r += 4) {
+    const long long o = (long long)r * ld + col;
+    const float gv = g[o];
+    float du = n > BNORM_EPS ? (gv - wc[o] * dot) / n : gv / BNORM_EPS;
+    if (m < 2) {
+      if (last_only) du = 0.f;
+      wcat[(long long)r * 4 * BDH + wcat_col(0, m, col)] = wp[o];
+      wcat[(long long)r * 4 * BDH + wcat_col(1, m, col)] = du;
+    } else {
+      if (last_only) du = gv;
+      w2cat[o] = wp[o];
+      w2cat[BP + o] = du;
     }
   }
 }
 
 // G (packed W1 | W3 | W2 per head) from the chunk's terms, each the sum of its split partials in a fixed order
-// (J13, A13: s13 partials of [BH][d][2 d_h]; J2, A2: s2 partials of [BH][d_h][d]):
-//   add_read_only: G += A (the read's weight gradient: A13 [d][W1 | W3 parts], A2 [d_h][d]);
+// (J13: s13 partials of [BH][d][2 d_h] in wcat_col part-0 order; A13: s13 partials of [BH][d][W1 part | W3
+// part]; J2, A2: s2 partials of [BH][d_h][d]); four consecutive elements per thread:
+//   add_read_only: G += A (the read's weight gradient);
 //   otherwise: G = base + J (+ A when with_read), base = dU (from Wcat / W2cat) for an updated matrix, G
 //   itself for a matrix the loop does not update (W1, W3 in the last-layer mode).
 __global__ __launch_bounds__(256) void sw_bwd_gupdate(float* __restrict__ G, const float* __restrict__ Wcat,
@@ -369,37 +500,38 @@ __global__ __launch_bounds__(256) void sw_bwd_gupdate(float* __restrict__ G, con
                                                       const float* __restrict__ A2, int s13, int s2,
                                                       int add_read_only, int with_read, int last_only) {
   const long long h = blockIdx.y, BH = gridDim.y;
-  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  const long long i = ((long long)blockIdx.x * 256 + threadIdx.x) * 4;
   if (i >= 3 * BP) return;
-  float* g = G + h * 3 * BP + i;
+  floatx4* g = (floatx4*)(G + h * 3 * BP + i);
   auto psum = [](const float* P, int n, long long stride, long long off) {
-    float x = 0.f;
-    for (int s = 0; s < n; ++s) x += P[s * stride + off];
+    floatx4 x = {0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < n; ++s) x += *(const floatx4*)(P + s * stride + off);
     return x;
   };
-  float a, j, base;
+  floatx4 av = {0.f, 0.f, 0.f, 0.f}, jv, base;
   if (i < 2 * BP) {
     const int m = (int)(i / BP);
-    const long long k = i % BP, d = k / BDH, u = k % BDH;
-    const long long off = h * BD * 2 * BDH + d * 2 * BDH + m * BDH + u, stride = BH * BD * 2 * BDH;
-    a = A13 ? psum(A13, s13, stride, off) : 0.f;
+    const long long k = i % BP, d = k / BDH;
+    const int u = (int)(k % BDH);
+    const long long stride = BH * BD * 2 * BDH, hoff = h * BD * 2 * BDH + d * 2 * BDH;
+    if (A13) av = psum(A13, s13, stride, hoff + m * BDH + u);
     if (add_read_only) {
-      *g += a;
+      *g += av;
       return;
     }
-    j = psum(J13, s13, stride, off);
-    base = last_only ? *g : Wcat[h * BD * 4 * BDH + d * 4 * BDH + (2 + m) * BDH + u];
+    jv = psum(J13, s13, stride, hoff + wcat_col(0, m, u));
+    base = last_only ? *g : *(const floatx4*)(Wcat + h * BD * 4 * BDH + d * 4 * BDH + wcat_col(1, m, u));
   } else {
     const long long k = i - 2 * BP;
-    a = A2 ? psum(A2, s2, BH * BP, h * BP + k) : 0.f;
+    if (A2) av = psum(A2, s2, BH * BP, h * BP + k);
     if (add_read_only) {
-      *g += a;
+      *g += av;
       return;
     }
-    j = psum(J2, s2, BH * BP, h * BP + k);
-    base = W2cat[h * 2 * BP + BP + k];
+    jv = psum(J2, s2, BH * BP, h * BP + k);
+    base = *(const floatx4*)(W2cat + h * 2 * BP + BP + k);
   }
-  *g = base + j + (with_read ? a : 0.f);
+  *g = base + jv + (with_read ? av : floatx4{0.f, 0.f, 0.f, 0.f});
 }
 
 // dV = eta ydot (ydot computed into dV), deta = <ydot, v>: one wave per token.
@@ -426,13 +558,13 @@ __global__ __launch_bounds__(256) void sw_bwd_copy(float* __restrict__ dst, cons
 }
 
 struct BwdSwLayout {
-  size_t fws, wfin, dump, dnorm, wcat, w2cat, z1, e1, z2, e2, e3, j13, j2, a13, a2, total;
+  size_t fws, wfin, dump, dnorm, wcat, w2cat, e1, e2, e3, j13, j2, a13, a2, total;
 };
 size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
-// Split of the products that contract over a chunk's tokens: enough workgroups (about 512) for the chip, at
+// Split of the products that contract over a chunk's tokens: enough workgroups (about 256) for the chip, at
 // least 128 tokens per split, at most 16 splits.
 int token_split(int tiles_per_head, int64_t BH, int64_t Cc) {
-  const int64_t want = 512 / std::max<int64_t>(1, tiles_per_head * BH);
+  const int64_t want = 256 / std::max<int64_t>(1, tiles_per_head * BH);
   const int64_t most = std::max<int64_t>(1, Cc / 128);
   return (int)std::max<int64_t>(1, std::min<int64_t>(std::min<int64_t>(want, most), 16));
 }
@@ -450,9 +582,7 @@ BwdSwLayout bwd_sw_layout(int64_t BH, int64_t T, int64_t chunk) {
   L.dnorm = o; o += al256((size_t)BH * nch * 640 * 4);
   L.wcat = o; o += al256((size_t)BH * BD * 4 * BDH * 4);
   L.w2cat = o; o += al256((size_t)BH * 2 * BDH * BD * 4);
-  L.z1 = o; o += al256((size_t)BH * Cc * 4 * BDH * 4);
   L.e1 = o; o += al256((size_t)BH * Cc * 4 * BDH * 4);
-  L.z2 = o; o += al256((size_t)BH * Cc * 2 * BDH * 4);
   L.e2 = o; o += al256((size_t)BH * Cc * 2 * BDH * 4);
   L.e3 = o; o += al256((size_t)BH * Cc * BDH * 4);
   L.j13 = o; o += al256((size_t)s13 * BH * BD * 2 * BDH * 4);
@@ -492,9 +622,7 @@ hipError_t launch_large_chunk_swiglu_backward(const BackwardArgs& a, int last_on
   float* dnorm = (float*)(ws + L.dnorm);
   float* Wcat = (float*)(ws + L.wcat);
   float* W2cat = (float*)(ws + L.w2cat);
-  float* Z1 = (float*)(ws + L.z1);
   float* E1 = (float*)(ws + L.e1);
-  float* Z2 = (float*)(ws + L.z2);
   float* E2 = (float*)(ws + L.e2);
   float* E3 = (float*)(ws + L.e3);
   float* J13 = (float*)(ws + L.j13);
@@ -528,21 +656,13 @@ hipError_t launch_large_chunk_swiglu_backward(const BackwardArgs& a, int last_on
     hipError_t e2;
     const bf16* Qc = Q + c0 * BD;
     const bf16* dOc = dO + c0 * BD;
-    float* Zq = Z1;    // [Cc][a | b]        (Z1's room)
-    float* Dh = Z2;    // [Cc][dh]           (Z2's room)
-    float* Eq = E1;    // [Cc][da | db]      (E1's room)
-    float* Hq = E2;    // [Cc][silu(a) b]    (E2's room)
-    // a = Q R1, b = Q R3
-    for (int m = 0; m < 2; ++m)
-      if ((e2 = gemm<bf16, float>(gargs(Qc, BD, 1, T * BD, R + m * BP, BDH, 1, rstride, Zq + m * BDH, 2 * BDH,
-                                        cap * 2 * BDH, Cc, BDH, BD), BH, stream)) != hipSuccess)
-        return e2;
-    // dh = dO R2^T
-    if ((e2 = gemm<bf16, float>(gargs(dOc, BD, 1, T * BD, R + 2 * BP, 1, BD, rstride, Dh, BDH, cap * BDH, Cc, BDH, BD),
-                                BH, stream)) != hipSuccess)
-      return e2;
-    hipLaunchKernelGGL(sw_bwd_read_elem, dim3((unsigned)(((long long)Cc * BDH + 255) / 256), BH), dim3(256), 0, stream,
-                       Zq, Dh, Eq, Hq, Cc, cap);
+    float* Eq = E1;    // [Cc][da | db]        (E1's room)
+    float* Hq = E2;    // [Cc][silu(a) b]      (E2's room)
+    // a = Q R1, b = Q R3, dh = dO R2^T and their elementwise step
+    const PairArgs pa{Qc, dOc, R, rstride, BDH, (int)BP, 64, R + 2 * BP, rstride, 32, 64, nullptr, Eq, Hq, nullptr,
+                      (int)T, (int)c0, Cc, cap};
+    hipLaunchKernelGGL(sw_bwd_pair_kernel<1>, dim3(BDH / 64, (unsigned)((Cc + GT - 1) / GT), BH), dim3(256), 0, stream,
+                       pa);
     if ((e2 = hipGetLastError()) != hipSuccess) return e2;
     // dQ = da R1^T + db R3^T
     for (int m = 0; m < 2; ++m)
@@ -567,24 +687,20 @@ hipError_t launch_large_chunk_swiglu_backward(const BackwardArgs& a, int last_on
     const long long wc_stride = (long long)nch * SP;
     if (!read_first) {   // the chunk's queries read W_c: their gradient reaches G before the normalisation
       if ((e = read_phase(Wc, wc_stride, c0, Cc)) != hipSuccess) return e;
-      hipLaunchKernelGGL(sw_bwd_gupdate, dim3((unsigned)((3 * BP + 255) / 256), BH), dim3(256), 0, stream, G, Wcat,
+      hipLaunchKernelGGL(sw_bwd_gupdate, dim3((unsigned)((3 * BP / 4 + 255) / 256), BH), dim3(256), 0, stream, G, Wcat,
                          W2cat, J13, J2, A13, A2, s13, s2, 1, 0, last_only);
       if ((e = hipGetLastError()) != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(sw_bwd_prep, dim3(640 / 4, BH), dim3(256), 0, stream, G, Wc, wc_stride, dnorm + (long long)c * 640,
+    hipLaunchKernelGGL(sw_bwd_prep, dim3(10, BH), dim3(256), 0, stream, G, Wc, wc_stride, dnorm + (long long)c * 640,
                        (long long)nch * 640, Wp, wp_stride, Wcat, W2cat, last_only);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const bf16* Kc = K + c0 * BD;
     const bf16* Vc = V + c0 * BD;
-    // Z1 = K [W1 | W3 | dU1 | dU3], Z2 = V [W2 ; dU2]^T
-    if ((e = gemm<bf16, float>(gargs(Kc, BD, 1, T * BD, Wcat, 4 * BDH, 1, BD * 4 * BDH, Z1, 4 * BDH, cap * 4 * BDH, Cc,
-                                     4 * BDH, BD), BH, stream)) != hipSuccess)
-      return e;
-    if ((e = gemm<bf16, float>(gargs(Vc, BD, 1, T * BD, W2cat, 1, BD, 2 * BP, Z2, 2 * BDH, cap * 2 * BDH, Cc, 2 * BDH,
-                                     BD), BH, stream)) != hipSuccess)
-      return e;
-    hipLaunchKernelGGL(sw_bwd_step_elem, dim3((unsigned)(((long long)Cc * BDH + 255) / 256), BH), dim3(256), 0, stream,
-                       Z1, Z2, a.eta, E1, E2, E3, Cc, cap, (int)T, (int)c0);
+    // k [W1 | W3 | dU1 | dU3], v [W2 ; dU2]^T and the step's elementwise factors
+    const PairArgs ps{Kc, Vc, Wcat, BD * 4 * BDH, 4 * BDH, 512, 64, W2cat, 2 * BP, BDH, 32, a.eta, E1, E2, E3, (int)T,
+                      (int)c0, Cc, cap};
+    hipLaunchKernelGGL(sw_bwd_pair_kernel<0>, dim3(BDH / 32, (unsigned)((Cc + GT - 1) / GT), BH), dim3(256), 0, stream,
+                       ps);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     // dK = E1 [W1 | W3 | dU1 | dU3]^T
     if ((e = gemm<float, float>(gargs(E1, 4 * BDH, 1, cap * 4 * BDH, Wcat, 1, 4 * BDH, BD * 4 * BDH, dK + c0 * BD, BD,
@@ -605,7 +721,7 @@ hipError_t launch_large_chunk_swiglu_backward(const BackwardArgs& a, int last_on
                                p2)) != hipSuccess)
       return e;
     if (read_first && (e = read_phase(Wp, wp_stride, c0, Cc)) != hipSuccess) return e;
-    hipLaunchKernelGGL(sw_bwd_gupdate, dim3((unsigned)((3 * BP + 255) / 256), BH), dim3(256), 0, stream, G, Wcat, W2cat,
+    hipLaunchKernelGGL(sw_bwd_gupdate, dim3((unsigned)((3 * BP / 4 + 255) / 256), BH), dim3(256), 0, stream, G, Wcat, W2cat,
                        J13, J2, A13, A2, s13, s2, 0, read_first ? 1 : 0, last_only);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
