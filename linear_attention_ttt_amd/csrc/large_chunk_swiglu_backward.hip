@@ -61,12 +61,14 @@ __device__ __forceinline__ float to_f(bf16 x) { return (float)x; }
 // with the transposed LDS read.  Float32 operands are split into bf16 hi +
 // lo planes on the way into LDS (three products per pair, float32
 // accumulation); bf16 operands are exact and have no lo plane.
-// 128 x 128 tiles, 32-deep steps, 4 waves of 64 x 64 (4 x 4 16x16x32 MFMA
-// tiles each); the next step's tiles are loaded into registers while the
-// current one is multiplied.  Requirements (checked by the host): the
-// contiguous extent of every operand is a whole number of tiles (M, N
-// multiples of 128 where they are contiguous, K a multiple of 32 where it
-// is); the strided extent may be ragged (rows past it read as zero).
+// BM x 128 tiles (BM = 128 or 64), 32-deep steps, 4 waves of BM/2 x 64
+// (BM/32 x 4 16x16x32 MFMA tiles each); the next step's tiles are loaded into
+// registers while the current one is multiplied.  B may come in two pieces
+// along k (B2 for k >= kseg, at k - kseg; only where k is contiguous).
+// Requirements (checked by the host): the contiguous extent of every operand
+// is a whole number of tiles (M a multiple of BM and N of 128 where they are
+// contiguous, K and kseg multiples of 32 where k is); the strided extent may
+// be ragged (rows past it read as zero).
 // ---------------------------------------------------------------------------
 struct GemmArgs {
   const void* A;
@@ -78,60 +80,67 @@ struct GemmArgs {
   float beta;
   int nsplit, kper;
   long long bCs;
+  const void* B2;
+  int kseg;
 };
 constexpr int GT = 128, GK = 32;
 constexpr int PLANE_ROW = GK * 2 + 16;          // [row][k] plane: 64 bytes of k + 16 bytes of padding
-constexpr int PLANE_TR_ROW = GT * 2 + 32;       // [k][row] plane: 256 bytes of rows + 32 bytes of padding
+constexpr int PLANE_TR_ROW = GT * 2 + 32;       // [k][row] plane (128 rows): 256 bytes + 32 bytes of padding
 constexpr int PLANE_BYTES = GT * PLANE_ROW;     // 10240 >= GK * PLANE_TR_ROW = 9216
 
-template <typename T>
+template <typename T, int ROWS = GT>
 struct GemmOperand {
   static constexpr bool F32 = sizeof(T) == 4;
-  static constexpr int LOADS = F32 ? 4 : 2;     // 16-byte loads per thread per tile
+  static constexpr int PER = F32 ? 4 : 8;                     // elements per 16-byte piece
+  static constexpr int LOADS = ROWS * GK / PER / 256;         // 16-byte loads per thread per tile
+  static constexpr int KPC = GK / PER;                        // [row][k]: pieces per row
+  static constexpr int RPC = ROWS / PER;                      // [k][row]: pieces per k
+  static constexpr int TR_ROW = ROWS * 2 + 32;                // [k][row] plane row stride
 };
 
-// One operand tile (rows r0.., k in [k0, kend)) into registers: 16-byte pieces, zeros past the ragged extent.
-template <typename T, bool TR>
-__device__ __forceinline__ void gemm_load(u32x4 (&v)[GemmOperand<T>::LOADS], const T* P, long long s_row,
-                                          long long s_k, int r0, int rend, int k0, int kend) {
-  constexpr bool F32 = GemmOperand<T>::F32;
+// One operand tile (ROWS rows from r0, k in [k0, kend)) into registers: 16-byte pieces, zeros past the
+// ragged extent; with kseg, steps at k0 >= kseg read P2 at k0 - kseg.
+template <typename T, bool TR, int ROWS>
+__device__ __forceinline__ void gemm_load(u32x4 (&v)[(GemmOperand<T, ROWS>::LOADS)], const T* P, long long s_row,
+                                          long long s_k, int r0, int rend, int k0, int kend,
+                                          const T* P2 = nullptr, int kseg = 0x7fffffff) {
+  using O = GemmOperand<T, ROWS>;
   const int tid = threadIdx.x;
+  if (k0 >= kseg) {
+    P = P2;
+    k0 -= kseg;
+    kend -= kseg;
+  }
 #pragma unroll
-  for (int q = 0; q < GemmOperand<T>::LOADS; ++q) {
+  for (int q = 0; q < O::LOADS; ++q) {
     const int idx = tid + 256 * q;
     bool ok;
     const T* src;
-    if (!TR) {      // [row][k]: F32 8 pieces of 4 per row, bf16 4 pieces of 8
-      const int row = F32 ? idx >> 3 : idx >> 2, pc = F32 ? idx & 7 : idx & 3;
+    if (!TR) {
+      const int row = idx / O::KPC, pc = idx % O::KPC;
       ok = r0 + row < rend;
-      src = P + (long long)(r0 + row) * s_row + (k0 + pc * (F32 ? 4 : 8));
-    } else {        // [k][row]: F32 32 pieces of 4 per k, bf16 16 pieces of 8
-      const int kr = F32 ? idx >> 5 : idx >> 4, pc = F32 ? idx & 31 : idx & 15;
+      src = P + (long long)(r0 + row) * s_row + (k0 + pc * O::PER);
+    } else {
+      const int kr = idx / O::RPC, pc = idx % O::RPC;
       ok = k0 + kr < kend;
-      src = P + (long long)(k0 + kr) * s_k + (r0 + pc * (F32 ? 4 : 8));
+      src = P + (long long)(k0 + kr) * s_k + (r0 + pc * O::PER);
     }
     v[q] = ok ? *(const u32x4*)src : u32x4{0u, 0u, 0u, 0u};
   }
 }
 
 // The registers of gemm_load into the hi (and lo) planes.
-template <typename T, bool TR>
-__device__ __forceinline__ void gemm_store(const u32x4 (&v)[GemmOperand<T>::LOADS], unsigned char* hi,
+template <typename T, bool TR, int ROWS>
+__device__ __forceinline__ void gemm_store(const u32x4 (&v)[(GemmOperand<T, ROWS>::LOADS)], unsigned char* hi,
                                            unsigned char* lo) {
-  constexpr bool F32 = GemmOperand<T>::F32;
+  using O = GemmOperand<T, ROWS>;
   const int tid = threadIdx.x;
 #pragma unroll
-  for (int q = 0; q < GemmOperand<T>::LOADS; ++q) {
+  for (int q = 0; q < O::LOADS; ++q) {
     const int idx = tid + 256 * q;
-    int off;
-    if (!TR) {
-      const int row = F32 ? idx >> 3 : idx >> 2, pc = F32 ? idx & 7 : idx & 3;
-      off = row * PLANE_ROW + pc * (F32 ? 8 : 16);
-    } else {
-      const int kr = F32 ? idx >> 5 : idx >> 4, pc = F32 ? idx & 31 : idx & 15;
-      off = kr * PLANE_TR_ROW + pc * (F32 ? 8 : 16);
-    }
-    if (F32) {
+    const int off = !TR ? (idx / O::KPC) * PLANE_ROW + (idx % O::KPC) * 16 / (O::F32 ? 2 : 1)
+                        : (idx / O::RPC) * O::TR_ROW + (idx % O::RPC) * 16 / (O::F32 ? 2 : 1);
+    if (O::F32) {
       const floatx4 f = __builtin_bit_cast(floatx4, v[q]);
       const uint2 s0 = split2(f[0], f[1]), s1 = split2(f[2], f[3]);
       *(uint2*)(hi + off) = uint2{s0.x, s1.x};
@@ -142,19 +151,23 @@ __device__ __forceinline__ void gemm_store(const u32x4 (&v)[GemmOperand<T>::LOAD
   }
 }
 
-// MFMA fragment of rows rb .. rb + 15 (lane: row rb + l % 16, k = 8 (l / 16) .. + 7) from a plane.
+// MFMA fragment of rows rb .. rb + 15 (lane: row rb + l % 16, k = 8 (l / 16) .. + 7) from a plane whose
+// transposed form has row stride tr_row.
 template <bool TR>
-__device__ __forceinline__ bf16x8 gemm_frag(const unsigned char* plane, int rb) {
+__device__ __forceinline__ bf16x8 gemm_frag(const unsigned char* plane, int rb, int tr_row = PLANE_TR_ROW) {
   const int l = threadIdx.x & 63, g = l >> 4, i = l & 15;
   if (!TR) return *(const bf16x8*)(plane + (rb + i) * PLANE_ROW + g * 16);
-  const unsigned char* p = plane + (8 * g + (i >> 2)) * PLANE_TR_ROW + (rb + 4 * (i & 3)) * 2;
-  const bf16x4 a = lds_read_tr16(p), b = lds_read_tr16(p + 4 * PLANE_TR_ROW);
+  const unsigned char* p = plane + (8 * g + (i >> 2)) * tr_row + (rb + 4 * (i & 3)) * 2;
+  const bf16x4 a = lds_read_tr16(p), b = lds_read_tr16(p + 4 * tr_row);
   return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 }
 
-template <typename TA, typename TB, bool ATR, bool BTR>
+template <typename TA, typename TB, bool ATR, bool BTR, int BM>
 __global__ __launch_bounds__(256, 2) void sw_gemm_kernel(GemmArgs g) {
-  constexpr bool AF = GemmOperand<TA>::F32, BF = GemmOperand<TB>::F32;
+  using OA = GemmOperand<TA, BM>;
+  using OB = GemmOperand<TB, GT>;
+  constexpr bool AF = OA::F32, BF = OB::F32;
+  constexpr int MI = BM / 32;             // row tiles per wave
   __shared__ __attribute__((aligned(16))) unsigned char lds[4 * PLANE_BYTES];
   unsigned char* ahi = lds;
   unsigned char* alo = lds + PLANE_BYTES;
@@ -165,42 +178,43 @@ __global__ __launch_bounds__(256, 2) void sw_gemm_kernel(GemmArgs g) {
   const int split = blockIdx.z % nsplit;
   const TA* A = (const TA*)g.A + bz * g.bA;
   const TB* B = (const TB*)g.B + bz * g.bB;
+  const TB* B2 = g.B2 ? (const TB*)g.B2 + bz * g.bB : nullptr;
   float* C = g.C + bz * g.bC + split * g.bCs;
-  const int m0 = blockIdx.y * GT, n0 = blockIdx.x * GT;
+  const int m0 = blockIdx.y * BM, n0 = blockIdx.x * GT;
   const int kbeg = split * g.kper, kend = min(g.K, kbeg + g.kper);
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, gq = l >> 4, li = l & 15;
   const int wm = w >> 1, wn = w & 1;
   // operand A rows are m (row stride sAm, k stride sAk); operand B rows are n (sBn, sBk)
   const long long a_row = g.sAm, a_k = g.sAk, b_row = g.sBn, b_k = g.sBk;
-  floatx4 acc[4][4];
+  floatx4 acc[MI][4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < MI; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
-  u32x4 va[GemmOperand<TA>::LOADS], vb[GemmOperand<TB>::LOADS];
+  u32x4 va[OA::LOADS], vb[OB::LOADS];
   if (kbeg < kend) {
-    gemm_load<TA, ATR>(va, A, a_row, a_k, m0, g.M, kbeg, kend);
-    gemm_load<TB, BTR>(vb, B, b_row, b_k, n0, g.N, kbeg, kend);
+    gemm_load<TA, ATR, BM>(va, A, a_row, a_k, m0, g.M, kbeg, kend);
+    gemm_load<TB, BTR, GT>(vb, B, b_row, b_k, n0, g.N, kbeg, kend, B2, g.kseg);
   }
   for (int k0 = kbeg; k0 < kend; k0 += GK) {
-    gemm_store<TA, ATR>(va, ahi, alo);
-    gemm_store<TB, BTR>(vb, bhi, blo);
+    gemm_store<TA, ATR, BM>(va, ahi, alo);
+    gemm_store<TB, BTR, GT>(vb, bhi, blo);
     __syncthreads();
     if (k0 + GK < kend) {
-      gemm_load<TA, ATR>(va, A, a_row, a_k, m0, g.M, k0 + GK, kend);
-      gemm_load<TB, BTR>(vb, B, b_row, b_k, n0, g.N, k0 + GK, kend);
+      gemm_load<TA, ATR, BM>(va, A, a_row, a_k, m0, g.M, k0 + GK, kend);
+      gemm_load<TB, BTR, GT>(vb, B, b_row, b_k, n0, g.N, k0 + GK, kend, B2, g.kseg);
     }
     bf16x8 bh[4], bl[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      bh[j] = gemm_frag<BTR>(bhi, 64 * wn + 16 * j);
-      if (BF) bl[j] = gemm_frag<BTR>(blo, 64 * wn + 16 * j);
+      bh[j] = gemm_frag<BTR>(bhi, 64 * wn + 16 * j, OB::TR_ROW);
+      if (BF) bl[j] = gemm_frag<BTR>(blo, 64 * wn + 16 * j, OB::TR_ROW);
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const bf16x8 ah = gemm_frag<ATR>(ahi, 64 * wm + 16 * i);
+    for (int i = 0; i < MI; ++i) {
+      const bf16x8 ah = gemm_frag<ATR>(ahi, (BM / 2) * wm + 16 * i, OA::TR_ROW);
       bf16x8 al;
-      if (AF) al = gemm_frag<ATR>(alo, 64 * wm + 16 * i);
+      if (AF) al = gemm_frag<ATR>(alo, (BM / 2) * wm + 16 * i, OA::TR_ROW);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         acc[i][j] = mfma16(ah, bh[j], acc[i][j]);
@@ -211,10 +225,10 @@ __global__ __launch_bounds__(256, 2) void sw_gemm_kernel(GemmArgs g) {
     __syncthreads();
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < MI; ++i)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int m = m0 + 64 * wm + 16 * i + 4 * gq + r;
+      const int m = m0 + (BM / 2) * wm + 16 * i + 4 * gq + r;
       if (m >= g.M) continue;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -225,28 +239,40 @@ __global__ __launch_bounds__(256, 2) void sw_gemm_kernel(GemmArgs g) {
     }
 }
 
+template <typename TA, typename TB, int BM>
+void gemm_launch(const GemmArgs& g, dim3 grid, bool atr, bool btr, hipStream_t stream) {
+  if (atr && btr)
+    hipLaunchKernelGGL((sw_gemm_kernel<TA, TB, true, true, BM>), grid, dim3(256), 0, stream, g);
+  else if (atr)
+    hipLaunchKernelGGL((sw_gemm_kernel<TA, TB, true, false, BM>), grid, dim3(256), 0, stream, g);
+  else if (btr)
+    hipLaunchKernelGGL((sw_gemm_kernel<TA, TB, false, true, BM>), grid, dim3(256), 0, stream, g);
+  else
+    hipLaunchKernelGGL((sw_gemm_kernel<TA, TB, false, false, BM>), grid, dim3(256), 0, stream, g);
+}
+
 // Launch with the operand orientations taken from the strides; nsplit > 1 splits the contraction into
-// pieces of kper (a multiple of GK) whose partial products go to C + s bCs.
+// pieces of kper (a multiple of GK) whose partial products go to C + s bCs.  Products with few column tiles
+// use 64-row tiles, so that the grid still has several workgroups per CU.
 template <typename TA, typename TB>
 hipError_t gemm(GemmArgs g, int batch, hipStream_t stream, int nsplit = 1, long long bCs = 0) {
   if (g.M <= 0 || g.N <= 0) return hipSuccess;
   const bool atr = g.sAk != 1, btr = g.sBk != 1;
+  const int bm = (!atr && g.N <= GT) ? 64 : GT;
   // the contiguous extent of each operand must be whole tiles (or whole k steps)
-  if ((atr ? (g.sAm != 1 || g.M % GT) : (g.K % GK)) || (btr ? (g.sBn != 1 || g.N % GT) : (g.K % GK)) || g.N % GT)
+  if ((atr ? (g.sAm != 1 || g.M % bm) : (g.K % GK)) || (btr ? (g.sBn != 1 || g.N % GT) : (g.K % GK)) || g.N % GT)
     return hipErrorInvalidValue;
+  if (g.B2 && (btr || g.kseg % GK || g.kseg <= 0)) return hipErrorInvalidValue;
+  if (!g.B2) g.kseg = 0x7fffffff;
   if (nsplit < 1) nsplit = 1;
   g.kper = (((g.K + nsplit - 1) / nsplit) + GK - 1) / GK * GK;
   g.nsplit = nsplit;
   g.bCs = bCs;
-  const dim3 grid((unsigned)(g.N / GT), (unsigned)((g.M + GT - 1) / GT), (unsigned)(batch * nsplit));
-  if (atr && btr)
-    hipLaunchKernelGGL((sw_gemm_kernel<TA, TB, true, true>), grid, dim3(256), 0, stream, g);
-  else if (atr)
-    hipLaunchKernelGGL((sw_gemm_kernel<TA, TB, true, false>), grid, dim3(256), 0, stream, g);
-  else if (btr)
-    hipLaunchKernelGGL((sw_gemm_kernel<TA, TB, false, true>), grid, dim3(256), 0, stream, g);
+  const dim3 grid((unsigned)(g.N / GT), (unsigned)((g.M + bm - 1) / bm), (unsigned)(batch * nsplit));
+  if (bm == 64)
+    gemm_launch<TA, TB, 64>(g, grid, atr, btr, stream);
   else
-    hipLaunchKernelGGL((sw_gemm_kernel<TA, TB, false, false>), grid, dim3(256), 0, stream, g);
+    gemm_launch<TA, TB, GT>(g, grid, atr, btr, stream);
   return hipGetLastError();
 }
 
@@ -446,46 +472,57 @@ __global__ __launch_bounds__(256, 2) void sw_bwd_pair_kernel(PairArgs a) {
 
 // Per head: the normalisation's backward dU of G (packed W1 | W3 | W2) at the chunk's normalised weights Wc and
 // norms nrm, and the step's operands at the weights before it (Wp): Wcat [d][1024] in wcat_col order (part 0:
-// W1, W3; part 1: dU1, dU3), W2cat [W2 ; dU2] (2 d_h x d).  Block (matrix m, group of 64 columns): 4 row groups
-// x 64 columns, each thread summing w . G over its rows, the 4 partials added in a fixed order through LDS.
-// Norm columns: 0..255 W1, 256..511 W3, 512..639 W2.  last_only: dU1 = dU3 = 0, dU2 = G2.
+// W1, W3; part 1: dU1, dU3), W2cat [W2 ; dU2] (2 d_h x d).  Block (matrix m, group of 16 columns): 16 row
+// groups x 16 columns, each thread summing w . G over its rows (8 of W1 / W3, 16 of W2), the 16 partials
+// added in a fixed order through LDS.  Norm columns: 0..255 W1, 256..511 W3, 512..639 W2.
+// last_only: dU1 = dU3 = 0, dU2 = G2.
 __global__ __launch_bounds__(256) void sw_bwd_prep(const float* __restrict__ G, const float* __restrict__ Wc,
                                                    long long wc_stride, const float* __restrict__ nrm,
                                                    long long nrm_stride, const float* __restrict__ Wp,
                                                    long long wp_stride, float* __restrict__ Wcat,
                                                    float* __restrict__ W2cat, int last_only) {
-  __shared__ float part[4][64];
+  __shared__ float part[16][17];
   const long long h = blockIdx.y;
-  const int grp = blockIdx.x, m = grp < 4 ? 0 : grp < 8 ? 1 : 2;
-  const int col = (m < 2 ? (grp & 3) : grp - 8) * 64 + (threadIdx.x & 63), rg = threadIdx.x >> 6;
-  const int ld = m < 2 ? BDH : BD, rows = m < 2 ? BD : BDH;
+  const int grp = blockIdx.x, m = grp < 16 ? 0 : grp < 32 ? 1 : 2;
+  const int cl = threadIdx.x & 15, rg = threadIdx.x >> 4;
+  const int col = (m < 2 ? (grp & 15) : grp - 32) * 16 + cl;
+  const int ld = m < 2 ? BDH : BD, rows = m < 2 ? BD : BDH, per = rows / 16;
   const long long base = (long long)m * BP;
   const float* g = G + h * 3 * BP + base;
   const float* wc = Wc + h * wc_stride + base;
   const float* wp = Wp + h * wp_stride + base;
-  float dot = 0.f;
-  for (int r = rg; r < rows; r += 4) dot += g[(long long)r * ld + col] * wc[(long long)r * ld + col];
-  part[rg][threadIdx.x & 63] = dot;
+  float gv[16], dot = 0.f;
+#pragma unroll
+  for (int k = 0; k < 16; ++k)
+    if (k < per) {
+      const long long o = (long long)(rg + 16 * k) * ld + col;
+      gv[k] = g[o];
+      dot += gv[k] * wc[o];
+    }
+  part[rg][cl] = dot;
   __syncthreads();
-  const int cl = threadIdx.x & 63;
-  dot = ((part[0][cl] + part[1][cl]) + part[2][cl]) + part[3][cl];
+  dot = 0.f;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) dot += part[r][cl];
   const float n = nrm[h * nrm_stride + (m < 2 ? m * BDH + col : 2 * BDH + col)];
   float* wcat = Wcat + h * BD * 4 * BDH;
   float* w2cat = W2cat + h * 2 * BP;
-  for (int r = rg; r < rows; r += 4) {
-    const long long o = (long long)r * ld + col;
-    const float gv = g[o];
-    float du = n > BNORM_EPS ? (gv - wc[o] * dot) / n : gv / BNORM_EPS;
-    if (m < 2) {
-      if (last_only) du = 0.f;
-      wcat[(long long)r * 4 * BDH + wcat_col(0, m, col)] = wp[o];
-      wcat[(long long)r * 4 * BDH + wcat_col(1, m, col)] = du;
-    } else {
-      if (last_only) du = gv;
-      w2cat[o] = wp[o];
-      w2cat[BP + o] = du;
+#pragma unroll
+  for (int k = 0; k < 16; ++k)
+    if (k < per) {
+      const int r = rg + 16 * k;
+      const long long o = (long long)r * ld + col;
+      float du = n > BNORM_EPS ? (gv[k] - wc[o] * dot) / n : gv[k] / BNORM_EPS;
+      if (m < 2) {
+        if (last_only) du = 0.f;
+        wcat[(long long)r * 4 * BDH + wcat_col(0, m, col)] = wp[o];
+        wcat[(long long)r * 4 * BDH + wcat_col(1, m, col)] = du;
+      } else {
+        if (last_only) du = gv[k];
+        w2cat[o] = wp[o];
+        w2cat[BP + o] = du;
+      }
     }
-  }
 }
 
 // G (packed W1 | W3 | W2 per head) from the chunk's terms, each the sum of its split partials in a fixed order
@@ -602,6 +639,7 @@ GemmArgs gargs(const void* A, long long sAm, long long sAk, long long bA, const 
   g.bA = bA; g.bB = bB; g.bC = bC;
   g.beta = beta;
   g.nsplit = 1; g.kper = K; g.bCs = 0;
+  g.B2 = nullptr; g.kseg = 0;
   return g;
 }
 
@@ -664,12 +702,11 @@ hipError_t launch_large_chunk_swiglu_backward(const BackwardArgs& a, int last_on
     hipLaunchKernelGGL(sw_bwd_pair_kernel<1>, dim3(BDH / 64, (unsigned)((Cc + GT - 1) / GT), BH), dim3(256), 0, stream,
                        pa);
     if ((e2 = hipGetLastError()) != hipSuccess) return e2;
-    // dQ = da R1^T + db R3^T
-    for (int m = 0; m < 2; ++m)
-      if ((e2 = gemm<float, float>(gargs(Eq + m * BDH, 2 * BDH, 1, cap * 2 * BDH, R + m * BP, 1, BDH, rstride,
-                                         dQ + c0 * BD, BD, T * BD, Cc, BD, BDH, m == 0 ? 0.f : 1.f), BH, stream)) !=
-          hipSuccess)
-        return e2;
+    // dQ = da R1^T + db R3^T: one product over k = (unit of R1 | unit of R3)
+    GemmArgs gq = gargs(Eq, 2 * BDH, 1, cap * 2 * BDH, R, 1, BDH, rstride, dQ + c0 * BD, BD, T * BD, Cc, BD, 2 * BDH);
+    gq.B2 = R + BP;
+    gq.kseg = BDH;
+    if ((e2 = gemm<float, float>(gq, BH, stream)) != hipSuccess) return e2;
     // (Q^T da | Q^T db), (silu(a) b)^T dO
     if ((e2 = gemm<bf16, float>(gargs(Qc, 1, BD, T * BD, Eq, 2 * BDH, 1, cap * 2 * BDH, A13, 2 * BDH, BD * 2 * BDH,
                                       BD, 2 * BDH, Cc), BH, stream, s13, p13)) != hipSuccess)
@@ -691,7 +728,7 @@ hipError_t launch_large_chunk_swiglu_backward(const BackwardArgs& a, int last_on
                          W2cat, J13, J2, A13, A2, s13, s2, 1, 0, last_only);
       if ((e = hipGetLastError()) != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(sw_bwd_prep, dim3(10, BH), dim3(256), 0, stream, G, Wc, wc_stride, dnorm + (long long)c * 640,
+    hipLaunchKernelGGL(sw_bwd_prep, dim3(40, BH), dim3(256), 0, stream, G, Wc, wc_stride, dnorm + (long long)c * 640,
                        (long long)nch * 640, Wp, wp_stride, Wcat, W2cat, last_only);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const bf16* Kc = K + c0 * BD;
