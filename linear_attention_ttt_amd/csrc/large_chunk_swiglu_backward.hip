@@ -31,8 +31,9 @@
 // batched over the heads on bf16 MFMA with float32 operands split into bf16
 // hi + lo (three products: hi hi, hi lo, lo hi; two when the other operand is
 // bf16 input) and float32 accumulation; the products of the tokens with the
-// weights run fused with the elementwise factors they feed
-// (sw_bwd_pair_kernel); the host walks the chunks.
+// weights run fused with the elementwise factors they feed and the products
+// of those factors with the weights (sw_bwd_step_kernel, sw_bwd_read_kernel);
+// the host walks the chunks.
 #include <algorithm>
 
 #include "device_common.h"
@@ -278,29 +279,22 @@ hipError_t gemm(GemmArgs g, int batch, hipStream_t stream, int nsplit = 1, long 
 
 __device__ __forceinline__ float sigm(float a) { return 1.0f / (1.0f + expf(-a)); }
 
-// Column of the concatenated step operand Wcat ([d][1024] per head) holding part p (0: the weights W1 | W3,
-// 1: their tangents dU1 | dU3) of matrix m (0: W1, 1: W3) at hidden unit u: 32-unit slices, the slice's
-// W1 and W3 (or dU1 and dU3) columns side by side, so a 32-unit slice of all four is two 64-column pieces.
-// E1 uses the same column order, and J13 (= K^T E1's first 512 columns) the part-0 order.
-__device__ __forceinline__ int wcat_col(int p, int m, int u) { return p * 512 + (u >> 5) * 64 + m * 32 + (u & 31); }
+// Column of the concatenated step operand Wcat ([d][1024] per head) holding part p (0: the weights, 1: their
+// tangents dU) of matrix m (0: W1, 1: W3) at hidden unit u: 16-unit slices of 64 columns (W1, W3, dU1, dU3).
+__device__ __forceinline__ int wcat_col(int p, int m, int u) { return (u >> 4) * 64 + (2 * p + m) * 16 + (u & 15); }
+// Column of E1a ([t][512]: eta Pa, eta Pb) and of J13 = K^T E1a ([d][512]) for matrix m at unit u.
+__device__ __forceinline__ int j13_col(int m, int u) { return (u >> 4) * 32 + m * 16 + (u & 15); }
 
 // ---------------------------------------------------------------------------
-// The two products of a 128-token tile that feed an elementwise step, with the
-// elementwise step as their epilogue (nothing but its results goes to memory):
-//   Z1 = X1 B1, X1 the tile's bf16 rows [t][d], B1 a 128-column fp32 block
-//        made of two 64-column pieces of a [d][ld1] matrix;
-//   Z2 = X2 B2^T, X2 bf16 [t][d], B2 a 64-row fp32 block of a [rows][d] matrix
-//        made of two 32-row pieces.
-// Wave w takes token rows 32 w .. 32 w + 31 of both, so that the values of one
-// (token, unit) in every column piece sit in one lane.  MODE 0 (the step's
-// vector-Jacobian factors, grid.x = 8 slices of 32 units): Z1 = k [W1 | W3 |
-// dU1 | dU3] (a, b, adot, bdot), Z2 = v [W2 ; dU2]^T (g, r) -> E1 [t][1024]
-// (wcat_col order: eta Pa, eta Pb | eta Padot, eta Pbdot), E2 [t][hdot | h],
-// E3 [t][eta hdot].  MODE 1 (the read's, grid.x = 4 slices of 64 units):
-// Z1 = q [R1 | R3] (a, b), Z2 = dO R2^T (dh) -> Eq [t][da | db], Hq [t][silu(a) b].
-// K = d = 128 in 32-deep steps, operands staged as in sw_gemm_kernel (B1 as a
-// [k][n] plane read transposed, B2 as [n][k]), the next step loaded while the
-// current one is multiplied.
+// The read's two products of a 128-token tile with their elementwise step as
+// the epilogue (grid.x = 4 slices of 64 units; nothing but the results goes to
+// memory): Z1 = q [R1 | R3] (a, b: 128 columns, two 64-column pieces of the
+// [d][d_h] matrices), Z2 = dO R2^T (dh: 64 rows of R2) -> Eq [t][da | db],
+// Hq [t][silu(a) b].  Wave w takes token rows 32 w .. 32 w + 31 of both, so
+// that a, b and dh of one (token, unit) sit in one lane.  K = d = 128 in
+// 32-deep steps, operands staged as in sw_gemm_kernel (B1 as a [k][n] plane
+// read transposed, B2 as [n][k]), the next step loaded while the current one
+// is multiplied.
 // ---------------------------------------------------------------------------
 struct PairArgs {
   const bf16* X1;       // [BH][T][d], already offset to the chunk
@@ -311,16 +305,13 @@ struct PairArgs {
   const float* B2;      // rows of d floats, per head + bh * sB2
   long long sB2;
   int piece2, slice2;           // row c -> (c / 32) piece2 + s slice2 + c % 32
-  const float* eta;     // [BH][T]
-  float* O1;            // MODE 0: E1, MODE 1: Eq   ([BH][cap][...])
-  float* O2;            // MODE 0: E2, MODE 1: Hq
-  float* O3;            // MODE 0: E3
+  float* Eq;            // [BH][cap][2 d_h]
+  float* Hq;            // [BH][cap][d_h]
   int T, c0, Cc;
   long long cap;
 };
 
-template <int MODE>
-__global__ __launch_bounds__(256, 2) void sw_bwd_pair_kernel(PairArgs a) {
+__global__ __launch_bounds__(256, 2) void sw_bwd_read_kernel(PairArgs a) {
   constexpr int X_PLANE = GT * PLANE_ROW;            // [t][k] bf16: 10240
   constexpr int B1_PLANE = GK * PLANE_TR_ROW;        // [k][n] bf16: 9216
   constexpr int B2_PLANE = 64 * PLANE_ROW;           // [n][k] bf16: 5120
@@ -435,39 +426,264 @@ __global__ __launch_bounds__(256, 2) void sw_bwd_pair_kernel(PairArgs a) {
       const int t = t0 + 32 * w + 16 * i + 4 * gq + r;
       if (t >= Cc) continue;
       const long long orow = bh * a.cap + t;
-      if (MODE == 0) {
-        const float e = a.eta[bh * a.T + a.c0 + t];
 #pragma unroll
-        for (int jj = 0; jj < 2; ++jj) {
-          const float av = z1[i][jj][r], bv = z1[i][2 + jj][r], ad = z1[i][4 + jj][r], bd = z1[i][6 + jj][r];
-          const float gg = z2[i][jj][r], rr = z2[i][2 + jj][r];
-          const float sg = sigm(av), sv = av * sg, s1 = sg * (1.0f + av * (1.0f - sg));
-          const float s2 = sg * (1.0f - sg) * (2.0f + av * (1.0f - 2.0f * sg));
-          const float hh = sv * bv, hd = s1 * ad * bv + sv * bd;
-          const int u = 32 * sl + 16 * jj + li;
-          float* e1 = a.O1 + orow * 4 * BDH;
-          e1[wcat_col(0, 0, u)] = e * (s2 * ad * bv * gg + s1 * (bd * gg + bv * rr));
-          e1[wcat_col(0, 1, u)] = e * (s1 * ad * gg + sv * rr);
-          e1[wcat_col(1, 0, u)] = e * (s1 * bv * gg);
-          e1[wcat_col(1, 1, u)] = e * (sv * gg);
-          float* e2 = a.O2 + orow * 2 * BDH;
-          e2[u] = hd;
-          e2[BDH + u] = hh;
-          a.O3[orow * BDH + u] = e * hd;
-        }
-      } else {
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          const float av = z1[i][jj][r], bv = z1[i][4 + jj][r], dh = z2[i][jj][r];
-          const float sg = sigm(av), sv = av * sg, s1 = sg * (1.0f + av * (1.0f - sg));
-          const int u = 64 * sl + 16 * jj + li;
-          float* eq = a.O1 + orow * 2 * BDH;
-          eq[u] = dh * bv * s1;
-          eq[BDH + u] = dh * sv;
-          a.O2[orow * BDH + u] = sv * bv;
-        }
+      for (int jj = 0; jj < 4; ++jj) {
+        const float av = z1[i][jj][r], bv = z1[i][4 + jj][r], dh = z2[i][jj][r];
+        const float sg = sigm(av), sv = av * sg, s1 = sg * (1.0f + av * (1.0f - sg));
+        const int u = 64 * sl + 16 * jj + li;
+        float* eq = a.Eq + orow * 2 * BDH;
+        eq[u] = dh * bv * s1;
+        eq[BDH + u] = dh * sv;
+        a.Hq[orow * BDH + u] = sv * bv;
       }
     }
+}
+
+// ---------------------------------------------------------------------------
+// The step's vector-Jacobian product for a 128-token tile of one head, all of
+// it but the two products that contract over the chunk's tokens (K^T E1a and
+// E3^T V): 8 waves of 16 tokens each; the 256 hidden units are visited in 16
+// slices of 16, and per slice
+//   Z1 = k [W1 | W3 | dU1 | dU3]_slice (a, b, adot, bdot: 64 columns),
+//   Z2 = v [W2 ; dU2]_slice^T (g, r: 32 columns),
+//   the elementwise factors eta Pa, eta Pb, eta Padot, eta Pbdot, hdot, h,
+//   E1a = (eta Pa, eta Pb) and E3 = eta hdot to memory (for the weight
+//   gradient), and
+//   dK += [eta Pa | eta Pb | eta Padot | eta Pbdot] [W1 | W3 | dU1 | dU3]_slice^T,
+//   ydot += [hdot | h] [W2 ; dU2]_slice,
+// then dK, dV = eta ydot and deta = <ydot, v> are written.  The k and v rows
+// of a wave's tokens stay in registers as MFMA operands for all slices; a
+// slice's weights (fp32) are staged once per workgroup as bf16 hi + lo planes
+// that serve both products they enter ([d][64 columns] read transposed for Z1
+// and directly for dK; [32 rows][d] read directly for Z2 and transposed for
+// ydot), the next slice's loaded into registers meanwhile; a wave's factors
+// pass through its own LDS planes ([column][token], read transposed as the A
+// operand), so the slice needs no barrier between its two halves.
+// ---------------------------------------------------------------------------
+struct StepArgs {
+  const bf16* K;        // [BH][T][d], offset to the chunk
+  const bf16* V;
+  const float* eta;     // [BH][T]
+  const float* Wcat;    // [BH][d][1024] (wcat_col order)
+  const float* W2cat;   // [BH][2 d_h][d]
+  float* E1a;           // [BH][cap][512] (j13_col order)
+  float* E3;            // [BH][cap][d_h]
+  float* dK;            // [BH][T][d], offset to the chunk
+  float* dV;
+  float* deta;          // [BH][T], offset to the chunk
+  int T, c0, Cc;
+  long long cap;
+};
+constexpr int ST_WAVES = 8, ST_TOK = 16 * ST_WAVES;
+constexpr int ST_WC_ROW = 64 * 2 + 32;         // [d][64 columns] bf16 plane row: 160 bytes
+constexpr int ST_W2_ROW = BD * 2 + 32;         // [32 rows][d] plane row: 288 bytes
+constexpr int ST_WC_PLANE = BD * ST_WC_ROW;    // 20480
+constexpr int ST_W2_PLANE = 32 * ST_W2_ROW;    // 9216
+constexpr int ST_E1_PLANE = 64 * 32;           // [64 columns][16 tokens] bf16
+constexpr int ST_E2_PLANE = 32 * 32;           // [32 rows][16 tokens]
+constexpr int ST_WAVE_BYTES = 2 * ST_E1_PLANE + 2 * ST_E2_PLANE;
+constexpr int ST_LDS = 2 * ST_WC_PLANE + 2 * ST_W2_PLANE + ST_WAVES * ST_WAVE_BYTES;   // 108544
+
+// Transposed fragment (rows m = rb + l % 16 of the MFMA operand, k = 8 (l / 16) .. + 7) of a [k][m] plane.
+__device__ __forceinline__ bf16x8 frag_tr(const unsigned char* plane, int row_bytes, int k0, int rb) {
+  const int l = threadIdx.x & 63, g = l >> 4, i = l & 15;
+  const unsigned char* p = plane + (k0 + 8 * g + (i >> 2)) * row_bytes + (rb + 4 * (i & 3)) * 2;
+  const bf16x4 x = lds_read_tr16(p), y = lds_read_tr16(p + 4 * row_bytes);
+  return bf16x8{x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
+}
+// Direct fragment (rows rb + l % 16, k = k0 + 8 (l / 16) .. + 7) of a [m][k] plane.
+__device__ __forceinline__ bf16x8 frag_dir(const unsigned char* plane, int row_bytes, int k0, int rb) {
+  const int l = threadIdx.x & 63, g = l >> 4, i = l & 15;
+  return *(const bf16x8*)(plane + (rb + i) * row_bytes + (k0 + 8 * g) * 2);
+}
+
+__global__ __launch_bounds__(ST_WAVES * 64, 1) void sw_bwd_step_kernel(StepArgs a) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char st_lds[];
+  unsigned char* wch = st_lds;
+  unsigned char* wcl = wch + ST_WC_PLANE;
+  unsigned char* w2h = wcl + ST_WC_PLANE;
+  unsigned char* w2l = w2h + ST_W2_PLANE;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, gq = l >> 4, li = l & 15;
+  unsigned char* e1h = w2l + ST_W2_PLANE + w * ST_WAVE_BYTES;
+  unsigned char* e1l = e1h + ST_E1_PLANE;
+  unsigned char* e2h = e1l + ST_E1_PLANE;
+  unsigned char* e2l = e2h + ST_E2_PLANE;
+  const long long bh = blockIdx.y;
+  const int t0 = blockIdx.x * ST_TOK + 16 * w;     // this wave's first token (chunk-relative)
+  const int Cc = a.Cc;
+  const float* Wc = a.Wcat + bh * BD * 4 * BDH;
+  const float* W2 = a.W2cat + bh * 2 * BP;
+  const long long trow = bh * (long long)a.T;      // row of token 0 of the chunk in [BH][T]
+  // k and v rows of the wave's tokens as MFMA A operands (row li, d = 32 ks + 8 gq ..)
+  bf16x8 kf[4], vf[4];
+  {
+    const int t = t0 + li;
+    const bool ok = t < Cc;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const long long o = (trow + t) * BD + 32 * ks + 8 * gq;
+      kf[ks] = ok ? *(const bf16x8*)(a.K + o) : bf16x8{};
+      vf[ks] = ok ? *(const bf16x8*)(a.V + o) : bf16x8{};
+    }
+  }
+  float er[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int t = t0 + 4 * gq + r;
+    er[r] = t < Cc ? a.eta[trow + a.c0 + t] : 0.f;
+  }
+  // a slice's weights: Wcat [d][64 columns] (4 pieces of 4 floats per thread), W2cat 32 rows (2 pieces)
+  u32x4 pw[4], p2[2];
+  auto load = [&](int s) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int idx = tid + 512 * q, d = idx >> 4, pc = idx & 15;
+      pw[q] = *(const u32x4*)(Wc + (long long)d * 4 * BDH + 64 * s + 4 * pc);
+    }
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int idx = tid + 512 * q, row = idx >> 5, pc = idx & 31;
+      const int srow = (row >> 4) * BDH + 16 * s + (row & 15);
+      p2[q] = *(const u32x4*)(W2 + (long long)srow * BD + 4 * pc);
+    }
+  };
+  auto store = [&]() {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int idx = tid + 512 * q, d = idx >> 4, pc = idx & 15;
+      const floatx4 f = __builtin_bit_cast(floatx4, pw[q]);
+      const uint2 s0 = split2(f[0], f[1]), s1 = split2(f[2], f[3]);
+      *(uint2*)(wch + d * ST_WC_ROW + pc * 8) = uint2{s0.x, s1.x};
+      *(uint2*)(wcl + d * ST_WC_ROW + pc * 8) = uint2{s0.y, s1.y};
+    }
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int idx = tid + 512 * q, row = idx >> 5, pc = idx & 31;
+      const floatx4 f = __builtin_bit_cast(floatx4, p2[q]);
+      const uint2 s0 = split2(f[0], f[1]), s1 = split2(f[2], f[3]);
+      *(uint2*)(w2h + row * ST_W2_ROW + pc * 8) = uint2{s0.x, s1.x};
+      *(uint2*)(w2l + row * ST_W2_ROW + pc * 8) = uint2{s0.y, s1.y};
+    }
+  };
+  floatx4 dk[8], yd[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) dk[j] = yd[j] = floatx4{0.f, 0.f, 0.f, 0.f};
+  constexpr int NSLICE = BDH / 16;
+  load(0);
+  store();
+  load(1);
+  __syncthreads();
+  for (int s = 0; s < NSLICE; ++s) {
+    // Z1 (a, b, adot, bdot) and Z2 (g, r) of the wave's 16 tokens and the slice's 16 units
+    floatx4 z1[4], z2[2];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) z1[j] = floatx4{0.f, 0.f, 0.f, 0.f};
+    z2[0] = z2[1] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        z1[j] = mfma16(kf[ks], frag_tr(wch, ST_WC_ROW, 32 * ks, 16 * j), z1[j]);
+        z1[j] = mfma16(kf[ks], frag_tr(wcl, ST_WC_ROW, 32 * ks, 16 * j), z1[j]);
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        z2[j] = mfma16(vf[ks], frag_dir(w2h, ST_W2_ROW, 32 * ks, 16 * j), z2[j]);
+        z2[j] = mfma16(vf[ks], frag_dir(w2l, ST_W2_ROW, 32 * ks, 16 * j), z2[j]);
+      }
+    }
+    // the elementwise factors: lane (gq, li) holds tokens t0 + 4 gq + r of unit 16 s + li
+    const int u = 16 * s + li;
+    float f1[4][4], f2[2][4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float av = z1[0][r], bv = z1[1][r], ad = z1[2][r], bd = z1[3][r], gg = z2[0][r], rr = z2[1][r];
+      const float e = er[r];
+      const float sg = sigm(av), sv = av * sg, s1 = sg * (1.0f + av * (1.0f - sg));
+      const float s2 = sg * (1.0f - sg) * (2.0f + av * (1.0f - 2.0f * sg));
+      const float hd = s1 * ad * bv + sv * bd;
+      f1[0][r] = e * (s2 * ad * bv * gg + s1 * (bd * gg + bv * rr));
+      f1[1][r] = e * (s1 * ad * gg + sv * rr);
+      f1[2][r] = e * (s1 * bv * gg);
+      f1[3][r] = e * (sv * gg);
+      f2[0][r] = hd;
+      f2[1][r] = sv * bv;
+      const int t = t0 + 4 * gq + r;
+      if (t < Cc) {
+        const long long orow = bh * a.cap + t;
+        a.E1a[orow * 2 * BDH + j13_col(0, u)] = f1[0][r];
+        a.E1a[orow * 2 * BDH + j13_col(1, u)] = f1[1][r];
+        a.E3[orow * BDH + u] = e * hd;
+      }
+    }
+    // the factors into the wave's [column][token] planes (4 consecutive tokens per lane and column)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint2 s0 = split2(f1[q][0], f1[q][1]), s1 = split2(f1[q][2], f1[q][3]);
+      const int off = (16 * q + li) * 32 + 8 * gq;
+      *(uint2*)(e1h + off) = uint2{s0.x, s1.x};
+      *(uint2*)(e1l + off) = uint2{s0.y, s1.y};
+    }
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const uint2 s0 = split2(f2[q][0], f2[q][1]), s1 = split2(f2[q][2], f2[q][3]);
+      const int off = (16 * q + li) * 32 + 8 * gq;
+      *(uint2*)(e2h + off) = uint2{s0.x, s1.x};
+      *(uint2*)(e2l + off) = uint2{s0.y, s1.y};
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_wave_barrier();
+    // dK += E1 Wcat_slice^T (k = the slice's 64 columns), ydot += E2 W2cat_slice (k = its 32 rows)
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const bf16x8 ah = frag_tr(e1h, 32, 32 * ks, 0), al = frag_tr(e1l, 32, 32 * ks, 0);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const bf16x8 bh = frag_dir(wch, ST_WC_ROW, 32 * ks, 16 * j), bl = frag_dir(wcl, ST_WC_ROW, 32 * ks, 16 * j);
+        dk[j] = mfma16(ah, bh, dk[j]);
+        dk[j] = mfma16(ah, bl, dk[j]);
+        dk[j] = mfma16(al, bh, dk[j]);
+      }
+    }
+    {
+      const bf16x8 ah = frag_tr(e2h, 32, 0, 0), al = frag_tr(e2l, 32, 0, 0);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const bf16x8 bh = frag_tr(w2h, ST_W2_ROW, 0, 16 * j), bl = frag_tr(w2l, ST_W2_ROW, 0, 16 * j);
+        yd[j] = mfma16(ah, bh, yd[j]);
+        yd[j] = mfma16(ah, bl, yd[j]);
+        yd[j] = mfma16(al, bh, yd[j]);
+      }
+    }
+    __syncthreads();                 // every wave is done with the slice's weight planes
+    if (s + 1 < NSLICE) {
+      store();
+      if (s + 2 < NSLICE) load(s + 2);
+      __syncthreads();
+    }
+  }
+  // dK, dV = eta ydot, deta = <ydot, v>: lane (gq, li) holds tokens t0 + 4 gq + r, d = 16 j + li
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int t = t0 + 4 * gq + r;
+    const bool ok = t < Cc;
+    float dot = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int d = 16 * j + li;
+      if (ok) {
+        const long long o = (trow + t) * BD + d;
+        a.dK[o] = dk[j][r];
+        a.dV[o] = er[r] * yd[j][r];
+        dot += yd[j][r] * (float)a.V[o];
+      }
+    }
+    dot += __shfl_xor(dot, 1);
+    dot += __shfl_xor(dot, 2);
+    dot += __shfl_xor(dot, 4);
+    dot += __shfl_xor(dot, 8);
+    if (ok && li == 0) a.deta[trow + t] = dot;
+  }
 }
 
 // Per head: the normalisation's backward dU of G (packed W1 | W3 | W2) at the chunk's normalised weights Wc and
@@ -526,7 +742,7 @@ __global__ __launch_bounds__(256) void sw_bwd_prep(const float* __restrict__ G, 
 }
 
 // G (packed W1 | W3 | W2 per head) from the chunk's terms, each the sum of its split partials in a fixed order
-// (J13: s13 partials of [BH][d][2 d_h] in wcat_col part-0 order; A13: s13 partials of [BH][d][W1 part | W3
+// (J13: s13 partials of [BH][d][2 d_h] in j13_col order; A13: s13 partials of [BH][d][W1 part | W3
 // part]; J2, A2: s2 partials of [BH][d_h][d]); four consecutive elements per thread:
 //   add_read_only: G += A (the read's weight gradient);
 //   otherwise: G = base + J (+ A when with_read), base = dU (from Wcat / W2cat) for an updated matrix, G
@@ -556,7 +772,7 @@ __global__ __launch_bounds__(256) void sw_bwd_gupdate(float* __restrict__ G, con
       *g += av;
       return;
     }
-    jv = psum(J13, s13, stride, hoff + wcat_col(0, m, u));
+    jv = psum(J13, s13, stride, hoff + j13_col(m, u));
     base = last_only ? *g : *(const floatx4*)(Wcat + h * BD * 4 * BDH + d * 4 * BDH + wcat_col(1, m, u));
   } else {
     const long long k = i - 2 * BP;
@@ -569,24 +785,6 @@ __global__ __launch_bounds__(256) void sw_bwd_gupdate(float* __restrict__ G, con
     base = *(const floatx4*)(W2cat + h * 2 * BP + BP + k);
   }
   *g = base + jv + (with_read ? av : floatx4{0.f, 0.f, 0.f, 0.f});
-}
-
-// dV = eta ydot (ydot computed into dV), deta = <ydot, v>: one wave per token.
-__global__ __launch_bounds__(256) void sw_bwd_finish_v(float* __restrict__ dV, float* __restrict__ deta,
-                                                       const bf16* __restrict__ V, const float* __restrict__ eta,
-                                                       int T, int c0, int Cc) {
-  const long long h = blockIdx.y;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6), l = threadIdx.x & 63;
-  if (t >= Cc) return;
-  const long long row = h * T + c0 + t;
-  float* y = dV + row * BD;
-  const bf16* v = V + row * BD;
-  const float e = eta[row];
-  const float y0 = y[l], y1 = y[l + 64];
-  const float dot = wave_sum(y0 * (float)v[l] + y1 * (float)v[l + 64]);
-  y[l] = e * y0;
-  y[l + 64] = e * y1;
-  if (l == 0) deta[row] = dot;
 }
 
 __global__ __launch_bounds__(256) void sw_bwd_copy(float* __restrict__ dst, const float* __restrict__ src, long long n) {
@@ -619,8 +817,8 @@ BwdSwLayout bwd_sw_layout(int64_t BH, int64_t T, int64_t chunk) {
   L.dnorm = o; o += al256((size_t)BH * nch * 640 * 4);
   L.wcat = o; o += al256((size_t)BH * BD * 4 * BDH * 4);
   L.w2cat = o; o += al256((size_t)BH * 2 * BDH * BD * 4);
-  L.e1 = o; o += al256((size_t)BH * Cc * 4 * BDH * 4);
-  L.e2 = o; o += al256((size_t)BH * Cc * 2 * BDH * 4);
+  L.e1 = o; o += al256((size_t)BH * Cc * 2 * BDH * 4);     // E1a, or the read's Eq
+  L.e2 = o; o += al256((size_t)BH * Cc * BDH * 4);         // the read's Hq
   L.e3 = o; o += al256((size_t)BH * Cc * BDH * 4);
   L.j13 = o; o += al256((size_t)s13 * BH * BD * 2 * BDH * 4);
   L.j2 = o; o += al256((size_t)s2 * BH * BP * 4);
@@ -689,6 +887,9 @@ hipError_t launch_large_chunk_swiglu_backward(const BackwardArgs& a, int last_on
   fa.last_layer_only = last_only;
   if ((e = launch_swiglu_recur_dump(fa, dump, dnorm, stream)) != hipSuccess) return e;
 
+  if ((e = hipFuncSetAttribute((const void*)sw_bwd_step_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, ST_LDS)) !=
+      hipSuccess)
+    return e;
   const bool read_first = !a.other_order;
   auto read_phase = [&](const float* R, long long rstride, long long c0, int Cc) -> hipError_t {
     hipError_t e2;
@@ -697,9 +898,9 @@ hipError_t launch_large_chunk_swiglu_backward(const BackwardArgs& a, int last_on
     float* Eq = E1;    // [Cc][da | db]        (E1's room)
     float* Hq = E2;    // [Cc][silu(a) b]      (E2's room)
     // a = Q R1, b = Q R3, dh = dO R2^T and their elementwise step
-    const PairArgs pa{Qc, dOc, R, rstride, BDH, (int)BP, 64, R + 2 * BP, rstride, 32, 64, nullptr, Eq, Hq, nullptr,
-                      (int)T, (int)c0, Cc, cap};
-    hipLaunchKernelGGL(sw_bwd_pair_kernel<1>, dim3(BDH / 64, (unsigned)((Cc + GT - 1) / GT), BH), dim3(256), 0, stream,
+    const PairArgs pa{Qc, dOc, R, rstride, BDH, (int)BP, 64, R + 2 * BP, rstride, 32, 64, Eq, Hq, (int)T, (int)c0, Cc,
+                      cap};
+    hipLaunchKernelGGL(sw_bwd_read_kernel, dim3(BDH / 64, (unsigned)((Cc + GT - 1) / GT), BH), dim3(256), 0, stream,
                        pa);
     if ((e2 = hipGetLastError()) != hipSuccess) return e2;
     // dQ = da R1^T + db R3^T: one product over k = (unit of R1 | unit of R3)
@@ -733,25 +934,14 @@ hipError_t launch_large_chunk_swiglu_backward(const BackwardArgs& a, int last_on
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const bf16* Kc = K + c0 * BD;
     const bf16* Vc = V + c0 * BD;
-    // k [W1 | W3 | dU1 | dU3], v [W2 ; dU2]^T and the step's elementwise factors
-    const PairArgs ps{Kc, Vc, Wcat, BD * 4 * BDH, 4 * BDH, 512, 64, W2cat, 2 * BP, BDH, 32, a.eta, E1, E2, E3, (int)T,
-                      (int)c0, Cc, cap};
-    hipLaunchKernelGGL(sw_bwd_pair_kernel<0>, dim3(BDH / 32, (unsigned)((Cc + GT - 1) / GT), BH), dim3(256), 0, stream,
-                       ps);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    // dK = E1 [W1 | W3 | dU1 | dU3]^T
-    if ((e = gemm<float, float>(gargs(E1, 4 * BDH, 1, cap * 4 * BDH, Wcat, 1, 4 * BDH, BD * 4 * BDH, dK + c0 * BD, BD,
-                                      T * BD, Cc, BD, 4 * BDH), BH, stream)) != hipSuccess)
-      return e;
-    // ydot = E2 [W2 ; dU2] (into dV), then dV = eta ydot and deta = <ydot, v>
-    if ((e = gemm<float, float>(gargs(E2, 2 * BDH, 1, cap * 2 * BDH, W2cat, BD, 1, 2 * BP, dV + c0 * BD, BD, T * BD, Cc,
-                                      BD, 2 * BDH), BH, stream)) != hipSuccess)
-      return e;
-    hipLaunchKernelGGL(sw_bwd_finish_v, dim3((unsigned)((Cc + 3) / 4), BH), dim3(256), 0, stream, dV, a.deta, V, a.eta,
-                       (int)T, (int)c0, Cc);
+    // the step's vector-Jacobian product except the weight terms: dK, dV, deta, and E1a, E3 for those
+    const StepArgs sa{Kc, Vc, a.eta, Wcat, W2cat, E1, E3, dK + c0 * BD, dV + c0 * BD, a.deta + c0, (int)T, (int)c0, Cc,
+                      cap};
+    hipLaunchKernelGGL(sw_bwd_step_kernel, dim3((unsigned)((Cc + ST_TOK - 1) / ST_TOK), BH), dim3(ST_WAVES * 64),
+                       ST_LDS, stream, sa);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     // J13 = K^T (eta Pa | eta Pb), J2 = (eta hdot)^T V
-    if ((e = gemm<bf16, float>(gargs(Kc, 1, BD, T * BD, E1, 4 * BDH, 1, cap * 4 * BDH, J13, 2 * BDH, BD * 2 * BDH, BD,
+    if ((e = gemm<bf16, float>(gargs(Kc, 1, BD, T * BD, E1, 2 * BDH, 1, cap * 2 * BDH, J13, 2 * BDH, BD * 2 * BDH, BD,
                                      2 * BDH, Cc), BH, stream, s13, p13)) != hipSuccess)
       return e;
     if ((e = gemm<float, bf16>(gargs(E3, 1, BDH, cap * BDH, Vc, BD, 1, T * BD, J2, BD, BP, BDH, BD, Cc), BH, stream, s2,
