@@ -227,15 +227,38 @@ __device__ __attribute__((noinline)) void swiglu_muon_steps(RecurLds& S, const S
     }
     wait_vm<0>();
     head_barrier();
-    // rows 8 sl .. 8 sl + 7 of the three sums, over the NSL partials in a fixed order
-    for (int q = tid; q < 3 * 8 * (D / 4); q += NT) {
-      const int m = q / (8 * (D / 4)), row = 8 * sl + (q / (D / 4)) % 8, c4 = q % (D / 4);
-      floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-      for (int s2 = 0; s2 < SW_NSL; ++s2)
-        acc += __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(
-                                               rn, ((((unsigned)s2 * 3 + m) * D + row) * D + 4 * c4) * 4, 0, 16));
-      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc), rn,
-                                             (SUMS + ((unsigned)m * D + row) * D + 4 * c4) * 4, 0, 16);
+    // rows 8 sl .. 8 sl + 7 of the three sums, over the NSL partials in a fixed order (three 16-byte pieces
+    // per thread; the partials' loads are issued in groups of 8 so that they are in flight together)
+    {
+      constexpr int RS = 3 * 8 * (D / 4) / NT;
+      static_assert(RS * NT == 3 * 8 * (D / 4), "reduce-scatter items per thread");
+      floatx4 acc[RS];
+      unsigned src[RS], dst[RS];
+#pragma unroll
+      for (int k = 0; k < RS; ++k) {
+        const int q = tid + NT * k;
+        const int m = q / (8 * (D / 4)), row = 8 * sl + (q / (D / 4)) % 8, c4 = q % (D / 4);
+        acc[k] = floatx4{0.f, 0.f, 0.f, 0.f};
+        src[k] = (((unsigned)m * D + row) * D + 4 * c4) * 4;
+        dst[k] = (SUMS + ((unsigned)m * D + row) * D + 4 * c4) * 4;
+      }
+#pragma unroll
+      for (int s0 = 0; s0 < SW_NSL; s0 += 8) {
+        floatx4 v[8][RS];
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+#pragma unroll
+          for (int k = 0; k < RS; ++k)
+            v[j][k] = __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                      rn, src[k] + (unsigned)(s0 + j) * 3 * G * 4, 0, 16));
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+#pragma unroll
+          for (int k = 0; k < RS; ++k) acc[k] += v[j][k];
+      }
+#pragma unroll
+      for (int k = 0; k < RS; ++k)
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[k]), rn, dst[k], 0, 16);
     }
     wait_vm<0>();
     head_barrier();
@@ -252,14 +275,24 @@ __device__ __attribute__((noinline)) void swiglu_muon_steps(RecurLds& S, const S
       }
       const float fx = it == 0 ? f[m] : 1.f, f2 = fx * fx;   // A of the normalised X is f^2 A
       // this wave's rows 32w .. 32w + 31 of f^2 A as bf16 hi + lo, 16-byte pieces swizzled by row
-      for (int q = l; q < 32 * (D / 4); q += 64) {
-        const int row = q / (D / 4), c4 = q % (D / 4);
-        const floatx4 a = f2 * __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                                rn, (abase + (32u * w + row) * D + 4 * c4) * 4, 0, 16));
-        const uint2 s0 = split2(a[0], a[1]), s1 = split2(a[2], a[3]);
-        const int off = row * (2 * D) + (((c4 >> 1) ^ (row & 15)) << 4) + (c4 & 1) * 8;
-        *(uint2*)(Aw + off) = uint2{s0.x, s1.x};
-        *(uint2*)(Aw + 32 * D * 2 + off) = uint2{s0.y, s1.y};
+      {
+        constexpr int AG = 32 * (D / 4) / 64;   // 16-byte pieces per lane, loaded together
+        floatx4 av[AG];
+#pragma unroll
+        for (int k = 0; k < AG; ++k) {
+          const int q = l + 64 * k, row = q / (D / 4), c4 = q % (D / 4);
+          av[k] = __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                  rn, (abase + (32u * w + row) * D + 4 * c4) * 4, 0, 16));
+        }
+#pragma unroll
+        for (int k = 0; k < AG; ++k) {
+          const int q = l + 64 * k, row = q / (D / 4), c4 = q % (D / 4);
+          const floatx4 a = f2 * av[k];
+          const uint2 s0 = split2(a[0], a[1]), s1 = split2(a[2], a[3]);
+          const int off = row * (2 * D) + (((c4 >> 1) ^ (row & 15)) << 4) + (c4 & 1) * 8;
+          *(uint2*)(Aw + off) = uint2{s0.x, s1.x};
+          *(uint2*)(Aw + 32 * D * 2 + off) = uint2{s0.y, s1.y};
+        }
       }
       // P = A' B for B = X or Y (d x NS in LDS): rows 32w + 16tt + 4g + r, column li of the lane
       auto prod = [&](const float* Bm, floatx4 (&acc)[2]) {
