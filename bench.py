@@ -295,7 +295,7 @@ def run_workload(name: str, steps: int, warmup: int, flush_mb: int, other_order:
 
 
 def run_backward(name: str, steps: int, warmup: int, flush_mb: int, mode: str):
-    """Time ttt_la_backward (per-token and large-chunk linear modes) on a workload's inputs and
+    """Time ttt_la_backward (the workload's mode: per-token, large-chunk linear or SwiGLU) on its inputs and
     seeded upstream gradients, each call bracketed by events with the caches
     flushed in between, as for the forward.  Algorithmic bytes: read Q, K,
     V, dO (bf16), eta, W0, dW; write dQ, dK, dV (fp32), deta, dW0."""
