@@ -44,6 +44,7 @@ import workloads  # noqa: E402
 METRIC = "tokens/s and % of bf16 MFMA peak for TTT-linear-attn fwd, 1 MI355X"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+CEILINGS = {}                  # practical ceilings measured on this GPU at the start of the run (practical_ceilings)
 FP32_VALU_PEAK_TFLOPS = 157.3  # MI355X fp32 vector
 
 # each method's other read order (exclusive per-token read, update-then-read chunks): same kernels and work
@@ -274,6 +275,10 @@ def run_workload(name: str, steps: int, warmup: int, flush_mb: int, other_order:
             else (flops / mean_s / 1e12 / BF16_PEAK_TFLOPS),
             "steady_state_step_frac": (nbytes / (ss_ms * 1e-3) / 1e9 / HBM_PEAK_GBS) if kbound == "hbm"
             else (flops / (ss_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS)}
+    if CEILINGS:
+        prac = CEILINGS["copy_GBps"] if kbound == "hbm" else CEILINGS["bf16_gemm_TFLOPs"]
+        roof["practical_peak"] = prac
+        roof["practical_frac"] = achieved / prac
     if not plain:
         roof["kernel"] += " (whole call: the update-rule entries have no timed form)" if (
             momentum is not None or muon is not None) else ""
@@ -364,6 +369,62 @@ def run_backward(name: str, steps: int, warmup: int, flush_mb: int, mode: str):
     return rec
 
 
+def practical_ceilings(reps: int = 5):
+    """Measured practical ceilings of this GPU, next to the published peaks: a 1 GiB device copy (bytes read +
+    written per second) and an 8192^3 bf16 matrix product (dense FLOP/s of the vendor library).  Best of
+    `reps` runs each, timed with events."""
+    import torch
+
+    def best(fn):
+        fn()
+        ts = []
+        for _ in range(reps):
+            a0, b0 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a0.record()
+            fn()
+            b0.record()
+            torch.cuda.synchronize()
+            ts.append(a0.elapsed_time(b0) * 1e-3)
+        return min(ts)
+
+    n = 1 << 28                                   # 2^28 floats = 1 GiB
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    t_copy = best(lambda: dst.copy_(src))
+    del src, dst
+    m = 8192
+    x = torch.randn((m, m), dtype=torch.bfloat16, device="cuda")
+    y = torch.randn((m, m), dtype=torch.bfloat16, device="cuda")
+    t_mm = best(lambda: torch.matmul(x, y))
+    del x, y
+    torch.cuda.empty_cache()
+    return {"copy_GBps": 2 * 4 * n / t_copy / 1e9, "bf16_gemm_TFLOPs": 2 * m ** 3 / t_mm / 1e12,
+            "how": "best of 5: 1 GiB fp32 device copy (read + write bytes), 8192^3 bf16 torch.matmul; "
+                   "roofline.practical_frac = achieved / (copy_GBps for HBM-bound kernels, bf16_gemm_TFLOPs for "
+                   "MFMA-bound ones)"}
+
+
+def host_info():
+    """The host the oracle baseline runs on: CPU model, core counts, BLAS threads."""
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas = None
+    try:
+        from threadpoolctl import threadpool_info
+        blas = [{"api": i.get("internal_api"), "threads": i.get("num_threads")} for i in threadpool_info()]
+    except Exception:  # threadpoolctl missing: reported as unknown
+        pass
+    return {"cpu_model": model, "os_cpu_count": os.cpu_count(), "affinity_cpus": len(os.sched_getaffinity(0)),
+            "blas": blas}
+
+
 def cpu_baseline(name: str, mode: str, target_s: float = 12.0):
     """Time the fp64 oracle on a bounded sample of the workload: whole
     sequences of a subset of the (independent) heads, scaled to the full
@@ -394,7 +455,7 @@ def cpu_baseline(name: str, mode: str, target_s: float = 12.0):
             "kind": "oracle",
             "sample": f"{nh} of {BH} heads of {name}, full T={s['T']}; {wall:.1f} s wall, {cpu:.1f} s CPU; "
                       f"scaled by {BH}/{nh} (heads are independent)",
-            "host_cpus_available": len(os.sched_getaffinity(0))}
+            "host_cpus_available": len(os.sched_getaffinity(0)), "host": host_info()}
 
 
 def main():
@@ -440,6 +501,7 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    CEILINGS.update(practical_ceilings())
     if a.mode:
         a.no_others = True
     if a.momentum is not None or a.muon is not None:
@@ -513,6 +575,7 @@ def main():
         "token_heads_per_s": head["token_heads_per_s"],
         "steady_state": head["steady_state"],
         "roofline": roof,
+        "practical_ceilings": CEILINGS,
         "cpu_baseline": head.get("cpu_baseline"),
         "workloads": others,
         "update_rules": variants,
