@@ -1,7 +1,7 @@
 /*
  * libttt_la - forward pass of a test-time-training (TTT) layer with
- * key-value binding, and the backward pass of its per-token and large-chunk
- * linear forms, for AMD Instinct MI355X (gfx950).
+ * key-value binding, its backward pass, and the large-chunk forms with the
+ * momentum and Muon update rules, for AMD Instinct MI355X (gfx950).
  *
  * The method (pages on "Test-Time Training with KV Binding Is Secretly
  * Linear Attention", paper summary technical sections 2B and 3, and the
@@ -265,10 +265,11 @@ int ttt_la_event_destroy(void* event);
 /*
  * ttt_la_backward(Q, K, V, eta, W0, dO, dW_out, chunk, mode) -> (dQ, dK, dV, deta, dW0)
  *
- * Gradients of a scalar loss through ttt_la_forward in the per-token and
- * large-chunk linear modes, for training the model around the layer (the
- * paper summary reports the parallel form's speed-up for training as well as
- * inference, technical section 4).
+ * Gradients of a scalar loss through ttt_la_forward in every mode that
+ * trains the memory, for training the model around the layer (the paper
+ * summary reports the parallel form's speed-up for training as well as
+ * inference, technical section 4; the LaCT review, language section, reports
+ * training throughput).
  *   Per-token: with G_t = dW_out + sum of q_j^T dO_j over the reads j at or
  *   after token t (strictly after it for TTT_LA_PER_TOKEN_LINEAR_EXCLUSIVE),
  *   and S_t the memory token t's query reads:
@@ -282,28 +283,41 @@ int ttt_la_event_destroy(void* event);
  *   the floor); G = dP_c; (read-first) G += A_c.  Then dQ_c = dO_c R_c^T,
  *   dK_c = diag(eta) V_c dP_c^T, dV_c = diag(eta) K_c dP_c,
  *   deta_t = k_t dP_c v_t^T, and dW0 = G.
+ *   SwiGLU (LaCT review, non-linear-memory and read-order sections): chunk c
+ *   forms U_c = W_{c-1} + S(W_{c-1}), S the eta-weighted descent step of the
+ *   binding loss, and W_c = U_c normalised per column (W1, W3 over d, W2 over
+ *   d_h); from the last chunk back the read's gradient enters G before
+ *   (update-first) or after (read-first) the chunk's step, the normalisation's
+ *   backward is (G - w (w . G)) / n per column, and the step's vector-Jacobian
+ *   product (through the gradient of the binding loss, so with silu's second
+ *   derivative) gives dK, dV, deta of the chunk and the weight term added to
+ *   the previous weights' gradient.  TTT_LA_LARGE_CHUNK_SWIGLU_LAST_LAYER has
+ *   no normalisation and no W1 / W3 step.  dW0 = G at the start.
  *
  *   Q, K, V, eta, W0, chunk, desc   as passed to ttt_la_forward (the forward
  *                  outputs are not needed: the memories are recomputed)
- *   mode           TTT_LA_PER_TOKEN_LINEAR, TTT_LA_PER_TOKEN_LINEAR_EXCLUSIVE,
- *                  TTT_LA_LARGE_CHUNK_LINEAR or TTT_LA_LARGE_CHUNK_LINEAR_UPDATE_FIRST
- *                  (ERR_UNSUPPORTED for the SwiGLU modes)
+ *   mode           any mode of ttt_la_forward: TTT_LA_PER_TOKEN_LINEAR,
+ *                  TTT_LA_PER_TOKEN_LINEAR_EXCLUSIVE, TTT_LA_LARGE_CHUNK_LINEAR,
+ *                  TTT_LA_LARGE_CHUNK_LINEAR_UPDATE_FIRST, TTT_LA_LARGE_CHUNK_SWIGLU,
+ *                  TTT_LA_LARGE_CHUNK_SWIGLU_UPDATE_FIRST, TTT_LA_LARGE_CHUNK_SWIGLU_LAST_LAYER
  *   dO             [B,H,T,d_v] io_dtype, device: gradient of O
- *   dW_out         [B,H,d_k,d_v] float32, device: gradient of W_out (pass
- *                  zeros if the final memory does not reach the loss)
+ *   dW_out         float32, device, W_out's shape ([B,H,d_k,d_v], or the packed
+ *                  W1 | W3 | W2 per head in the SwiGLU modes): gradient of W_out
+ *                  (pass zeros if the final memory does not reach the loss)
  *   dQ, dK         [B,H,T,d_k] float32, device (written)
  *   dV             [B,H,T,d_v] float32, device (written)
  *                  (float32 whatever io_dtype is: rounding these heavy-tailed
  *                  gradients to bf16 alone would use up the accuracy budget)
  *   deta           [B,H,T] float32, device (written)
- *   dW0            [B,H,d_k,d_v] float32, device (written)
+ *   dW0            float32, device, W0's shape (written)
  *   workspace, workspace_bytes
  *                  at least ttt_la_backward_workspace_bytes(desc, chunk, mode)
  *                  bytes of device scratch (contents on entry do not matter)
  *   stream         hipStream_t (NULL = the default stream)
  *
  * Supported set: per-token as ttt_la_forward (bf16 or fp32, d_k = d_v in
- * {64, 128}); large-chunk linear bf16, d_k = d_v in {64, 128}, any chunk.
+ * {64, 128}); large-chunk linear bf16, d_k = d_v in {64, 128}, any chunk;
+ * SwiGLU bf16, d = 128, d_h = 256, any chunk, o_dtype TTT_LA_O_AS_INPUT.
  * dO has io_dtype.
  * Every pointer is required (ERR_NULL), except that the per-token arrays
  * may be NULL when T = 0 (then dW0 = dW_out); no output may overlap an input,
