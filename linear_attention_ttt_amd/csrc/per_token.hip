@@ -36,6 +36,7 @@
 // one token; they are staged as whole rows in the tile's dead V region and
 // leave with 16-byte stores after the next barrier.
 #include <algorithm>
+#include <type_traits>
 
 #include "device_common.h"
 #include "kernels.h"
@@ -752,7 +753,13 @@ struct Fp32Cfg {
 // REV and EM as for the bf16 output pass: REV walks the head's sequence in
 // reverse (chunk row r of chunk c is original token T - 1 - (cC + r)); EM
 // places the rates on the keys (0), on the outputs (1) or nowhere (2).
-template <int DK, int C, bool EXCL, bool REV = false, int EM = 0>
+// PAR (short sequences, few heads): one workgroup per (head, column tile,
+// chunk) instead of per (head, column tile): the workgroup of chunk c runs
+// the state updates of chunks 0 .. c-1 itself (loading only their keys,
+// values and rates) and then chunk c's outputs, so the chunks' score and
+// output phases run in parallel; only the last chunk's workgroup takes its
+// own state update and writes W_out.
+template <int DK, int C, bool EXCL, bool REV = false, int EM = 0, bool PAR = false>
 __global__ __launch_bounds__(256) void per_token_fp32_kernel(
     const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
     const float* __restrict__ eta, const float* __restrict__ W0, float* __restrict__ O,
@@ -767,8 +774,11 @@ __global__ __launch_bounds__(256) void per_token_fp32_kernel(
   float* p = q + Cfg::OFF_P;            // [C][PP]: eta_j * (q_i . k_j) for j <= i, else 0
   float* s = q + Cfg::OFF_S;            // [DK][TV]
   const int NV = DV / TV;
-  const int bh = blockIdx.x / NV;
-  const int tv0 = (blockIdx.x % NV) * TV;
+  const int nchunks = (T + C - 1) / C;
+  const int wg = PAR ? (int)blockIdx.x / nchunks : (int)blockIdx.x;
+  const int c_own = PAR ? (int)blockIdx.x % nchunks : nchunks - 1;   // the last chunk this workgroup reaches
+  const int bh = wg / NV;
+  const int tv0 = (wg % NV) * TV;
   const int tid = threadIdx.x;
   const float* Qh = Q + (size_t)bh * T * DK;
   const float* Kh = K + (size_t)bh * T * DK;
@@ -782,17 +792,18 @@ __global__ __launch_bounds__(256) void per_token_fp32_kernel(
   // thread roles: score block (rows SB*bi.., cols SB*bj..); output / state column group cg (4 columns)
   const int bi = tid / 16, bj = tid % 16;
   const int cg = tid % 8, r8 = tid / 8;
-  const int nchunks = (T + C - 1) / C;
   // original token of position t of the walk
   auto tok = [&](int t) -> size_t { return REV ? (size_t)(T - 1 - t) : (size_t)t; };
-  for (int c = 0; c < nchunks; ++c) {
+  for (int c = 0; c <= c_own; ++c) {
     const int t0 = c * C;
+    const bool out = !PAR || c == c_own;                        // this chunk's outputs (workgroup-uniform)
+    const bool upd = !PAR || c < c_own || c_own == nchunks - 1;  // its state update is needed here
     __syncthreads();
     for (int i = tid; i < C * DK / 4; i += 256) {
       const int r = i / (DK / 4), a4 = i % (DK / 4);
       const bool ok = t0 + r < T;
       const floatx4 z = {0.f, 0.f, 0.f, 0.f};
-      *(floatx4*)(q + r * QP + 4 * a4) = ok ? *(const floatx4*)(Qh + tok(t0 + r) * DK + 4 * a4) : z;
+      if (out) *(floatx4*)(q + r * QP + 4 * a4) = ok ? *(const floatx4*)(Qh + tok(t0 + r) * DK + 4 * a4) : z;
       *(floatx4*)(k + r * QP + 4 * a4) = ok ? *(const floatx4*)(Kh + tok(t0 + r) * DK + 4 * a4) : z;
     }
     for (int i = tid; i < C * TV / 4; i += 256) {
@@ -802,60 +813,62 @@ __global__ __launch_bounds__(256) void per_token_fp32_kernel(
     }
     for (int i = tid; i < C; i += 256) e[i] = (t0 + i < T) ? Eh[tok(t0 + i)] : 0.f;
     __syncthreads();
-    // scores with the causal mask (diagonal included) and eta of the key token: SB x SB block per thread
-    if (bj <= bi) {
-      float acc[SB][SB];
-#pragma unroll
-      for (int r = 0; r < SB; ++r)
-#pragma unroll
-        for (int cc = 0; cc < SB; ++cc) acc[r][cc] = 0.f;
-#pragma unroll 2
-      for (int a = 0; a < DK; a += 4) {
-        floatx4 qa[SB], ka[SB];
-#pragma unroll
-        for (int r = 0; r < SB; ++r) qa[r] = *(const floatx4*)(q + (SB * bi + r) * QP + a);
-#pragma unroll
-        for (int cc = 0; cc < SB; ++cc) ka[cc] = *(const floatx4*)(k + (SB * bj + cc) * QP + a);
+    if (out) {
+      // scores with the causal mask (diagonal included) and eta of the key token: SB x SB block per thread
+      if (bj <= bi) {
+        float acc[SB][SB];
 #pragma unroll
         for (int r = 0; r < SB; ++r)
 #pragma unroll
-          for (int cc = 0; cc < SB; ++cc)
+          for (int cc = 0; cc < SB; ++cc) acc[r][cc] = 0.f;
+#pragma unroll 2
+        for (int a = 0; a < DK; a += 4) {
+          floatx4 qa[SB], ka[SB];
 #pragma unroll
-            for (int x = 0; x < 4; ++x) acc[r][cc] = fmaf(qa[r][x], ka[cc][x], acc[r][cc]);
-      }
+          for (int r = 0; r < SB; ++r) qa[r] = *(const floatx4*)(q + (SB * bi + r) * QP + a);
 #pragma unroll
-      for (int r = 0; r < SB; ++r)
+          for (int cc = 0; cc < SB; ++cc) ka[cc] = *(const floatx4*)(k + (SB * bj + cc) * QP + a);
 #pragma unroll
-        for (int cc = 0; cc < SB; ++cc) {
-          const int i = SB * bi + r, j = SB * bj + cc;
-          p[i * PP + j] = (EXCL ? j < i : j <= i) ? (EM == 0 ? acc[r][cc] * e[j] : acc[r][cc]) : 0.f;
+          for (int r = 0; r < SB; ++r)
+#pragma unroll
+            for (int cc = 0; cc < SB; ++cc)
+#pragma unroll
+              for (int x = 0; x < 4; ++x) acc[r][cc] = fmaf(qa[r][x], ka[cc][x], acc[r][cc]);
         }
-    } else {
 #pragma unroll
-      for (int r = 0; r < SB; ++r)
+        for (int r = 0; r < SB; ++r)
 #pragma unroll
-        for (int cc = 0; cc < SB; ++cc) p[(SB * bi + r) * PP + SB * bj + cc] = 0.f;
-    }
-    __syncthreads();
-    // outputs: rows r8 + 32m, columns 4cg..4cg+3
-#pragma unroll 1
-    for (int i = r8; i < C; i += 32) {
-      floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 8
-      for (int j = 0; j < C; ++j) acc += p[i * PP + j] * *(const floatx4*)(v + j * TV + 4 * cg);
-      floatx4 acc2 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-      for (int a = 0; a < DK; a += 4) {
-        const floatx4 qa = *(const floatx4*)(q + i * QP + a);
+          for (int cc = 0; cc < SB; ++cc) {
+            const int i = SB * bi + r, j = SB * bj + cc;
+            p[i * PP + j] = (EXCL ? j < i : j <= i) ? (EM == 0 ? acc[r][cc] * e[j] : acc[r][cc]) : 0.f;
+          }
+      } else {
 #pragma unroll
-        for (int x = 0; x < 4; ++x) acc2 += qa[x] * *(const floatx4*)(s + (a + x) * TV + 4 * cg);
+        for (int r = 0; r < SB; ++r)
+#pragma unroll
+          for (int cc = 0; cc < SB; ++cc) p[(SB * bi + r) * PP + SB * bj + cc] = 0.f;
       }
-      if (t0 + i < T)
-        *(floatx4*)(Oh + tok(t0 + i) * DV + tv0 + 4 * cg) = EM == 1 ? e[i] * (acc + acc2) : acc + acc2;
+      __syncthreads();
+      // outputs: rows r8 + 32m, columns 4cg..4cg+3
+#pragma unroll 1
+      for (int i = r8; i < C; i += 32) {
+        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
+        for (int j = 0; j < C; ++j) acc += p[i * PP + j] * *(const floatx4*)(v + j * TV + 4 * cg);
+        floatx4 acc2 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+        for (int a = 0; a < DK; a += 4) {
+          const floatx4 qa = *(const floatx4*)(q + i * QP + a);
+#pragma unroll
+          for (int x = 0; x < 4; ++x) acc2 += qa[x] * *(const floatx4*)(s + (a + x) * TV + 4 * cg);
+        }
+        if (t0 + i < T)
+          *(floatx4*)(Oh + tok(t0 + i) * DV + tv0 + 4 * cg) = EM == 1 ? e[i] * (acc + acc2) : acc + acc2;
+      }
+      __syncthreads();
     }
-    __syncthreads();
     // state: rows r8 + 32m of s, columns 4cg..4cg+3, over the chunk's keys
-    {
+    if (upd) {
       constexpr int RS = DK / 32;
       floatx4 acc[RS];
 #pragma unroll
@@ -871,11 +884,16 @@ __global__ __launch_bounds__(256) void per_token_fp32_kernel(
     }
   }
   __syncthreads();
+  if (PAR && c_own != nchunks - 1) return;   // workgroup-uniform
   for (int i = tid; i < DK * TV / 4; i += 256) {
     const int a = i / (TV / 4), n4 = i % (TV / 4);
     *(floatx4*)(Wout + (size_t)bh * DK * DV + (size_t)a * DV + tv0 + 4 * n4) = *(const floatx4*)(s + a * TV + 4 * n4);
   }
 }
+
+// The float32 kernel's PAR form repeats the earlier chunks' state updates in every chunk's workgroup
+// (quadratic in the chunk count): only for short sequences.
+constexpr long long FP32_PAR_MAX_CHUNKS = 16;
 
 template <int DK, int C>
 static size_t fp32_lds_bytes() {
@@ -887,11 +905,16 @@ static size_t fp32_lds_bytes() {
 // ---------------------------------------------------------------------------
 template <int DK, int C>
 static hipError_t launch_fp32(const PerTokenArgs& a, hipStream_t stream, const Timing& tm) {
-  auto kern = a.exclusive ? per_token_fp32_kernel<DK, C, true> : per_token_fp32_kernel<DK, C, false>;
+  // few (head, column tile) workgroups over a short sequence: one workgroup per chunk as well (PAR)
+  const long long wgs = a.B * a.H * (a.DV / 32), nchunks = (a.T + C - 1) / C;
+  const bool par = nchunks >= 2 && nchunks <= FP32_PAR_MAX_CHUNKS && wgs * nchunks <= 256;
+  auto kern = par ? (a.exclusive ? per_token_fp32_kernel<DK, C, true, false, 0, true>
+                                 : per_token_fp32_kernel<DK, C, false, false, 0, true>)
+                  : (a.exclusive ? per_token_fp32_kernel<DK, C, true> : per_token_fp32_kernel<DK, C, false>);
   const size_t lds = fp32_lds_bytes<DK, C>();
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  const int grid = (int)(a.B * a.H * (a.DV / 32));
+  const int grid = (int)(par ? wgs * nchunks : wgs);
   if ((e = mark(tm.start, stream)) != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3(grid), dim3(256), lds, stream, (const float*)a.Q, (const float*)a.K,
                      (const float*)a.V, a.eta, a.W0, (float*)a.O, a.W_out, (int)a.T, (int)a.DV);
@@ -1139,21 +1162,33 @@ static hipError_t launch_bwd_fp32(const BackwardArgs& a, hipStream_t stream) {
                      w0t, dwt);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const size_t lds = fp32_lds_bytes<DK, C>();
+  const long long wgs = (long long)BH * (DV / 32), nchunks = (a.T + C - 1) / C;
+  const bool par = nchunks >= 2 && nchunks <= FP32_PAR_MAX_CHUNKS && wgs * nchunks <= 256;
   auto pass = [&](auto kern, const float* q, const float* k, const float* v, const float* w0, float* o,
                   float* wout) -> hipError_t {
     hipError_t err = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(kern, dim3(BH * (DV / 32)), dim3(256), lds, stream, q, k, v, a.eta, w0, o, wout, T, DV);
+    hipLaunchKernelGGL(kern, dim3((unsigned)(par ? wgs * nchunks : wgs)), dim3(256), lds, stream, q, k, v, a.eta, w0,
+                       o, wout, T, DV);
     return hipGetLastError();
   };
-  if ((e = pass(excl ? per_token_fp32_kernel<DK, C, true, false, 0> : per_token_fp32_kernel<DK, C, false, false, 0>,
-                dO, V, K, w0t, (float*)a.dQ, junk)) != hipSuccess)
+  // the kernel of one pass: read order, walk direction, rate placement, and the PAR form for short sequences
+  auto pick = [&](auto excl_t, auto rev_t, auto em_t) {
+    constexpr bool X = decltype(excl_t)::value, R = decltype(rev_t)::value;
+    constexpr int M = decltype(em_t)::value;
+    return par ? per_token_fp32_kernel<DK, C, X, R, M, true> : per_token_fp32_kernel<DK, C, X, R, M, false>;
+  };
+  using F = std::false_type;
+  using Tr = std::true_type;
+  using E0 = std::integral_constant<int, 0>;
+  using E1 = std::integral_constant<int, 1>;
+  using E2 = std::integral_constant<int, 2>;
+  if ((e = pass(excl ? pick(Tr{}, F{}, E0{}) : pick(F{}, F{}, E0{}), dO, V, K, w0t, (float*)a.dQ, junk)) != hipSuccess)
     return e;
-  if ((e = pass(excl ? per_token_fp32_kernel<DK, C, true, true, 2> : per_token_fp32_kernel<DK, C, false, true, 2>, K,
-                Q, dO, a.dW, (float*)a.dV, a.dW0)) != hipSuccess)
+  if ((e = pass(excl ? pick(Tr{}, Tr{}, E2{}) : pick(F{}, Tr{}, E2{}), K, Q, dO, a.dW, (float*)a.dV, a.dW0)) !=
+      hipSuccess)
     return e;
-  if ((e = pass(excl ? per_token_fp32_kernel<DK, C, true, true, 1> : per_token_fp32_kernel<DK, C, false, true, 1>, V,
-                dO, Q, dwt, (float*)a.dK, junk)) != hipSuccess)
+  if ((e = pass(excl ? pick(Tr{}, Tr{}, E1{}) : pick(F{}, Tr{}, E1{}), V, dO, Q, dwt, (float*)a.dK, junk)) != hipSuccess)
     return e;
   if (ntok > 0) {
     constexpr int TPB = 256 / (DK / 8);

@@ -98,6 +98,7 @@ def test_per_token_backward_workload_B4H16T4096_sampled_heads():
     (2, 2, 203, 128, 32),      # ragged tail
     (1, 2, 90, 64, 16),
     (1, 1, 1, 64, 64),         # single token
+    (1, 1, 1100, 64, 64),      # 18 chunks: the sequential form of the float32 kernel
 ])
 def test_per_token_backward_fp32(mode, B, H, T, d, chunk):
     s = workloads.make_spec(mode, B, H, T, d, chunk=chunk, dtype="fp32", eta="sigmoid")
