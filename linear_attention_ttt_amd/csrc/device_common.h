@@ -179,6 +179,7 @@ __device__ __forceinline__ void g2lds4(const void* gsrc, void* lds_wave_base) {
 // accesses at or beyond nbytes read 0 and drop writes, which is how the
 // kernels treat the ragged end of a sequence.
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned uint2v __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, long long nbytes) {
   const int n = nbytes <= 0 ? 0 : (nbytes > 0x7fffffffLL ? 0x7fffffff : (int)nbytes);

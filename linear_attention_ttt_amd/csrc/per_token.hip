@@ -200,6 +200,8 @@ struct SegArgs {
   float* Wout;
   int T, nseg, seg_len;             // segment s covers tokens [s*seg_len, (s+1)*seg_len), whole tiles of both passes
   int start_transposed = 0;         // 1: segment s > 0 starts from the transpose of the state in slot s
+  const bf16* aux = nullptr;        // DOT: the rows each output row is dotted with ([B,H,T,D], original order)
+  float* dpart = nullptr;           // DOT: per-wave partial dots, [B,H,T][D / 16] (original order)
 };
 
 // The program of wave W (wave-uniform).  One program for all waves keeps the
@@ -217,8 +219,13 @@ struct SegArgs {
 // OF32: the outputs are float32 (A.O points to floats) and leave straight
 // from the accumulators, 16 bytes per lane (4 columns of one token), instead
 // of as bf16 rows staged in LDS.
-template <int D, int CT, bool EXCL, bool REV, int EM, bool OF32>
+// DOT (with OF32): each output row o_t (before the rate of EM 1 scales it)
+// is also dotted with row t of A.aux over the wave's 16 columns, and the
+// partial goes to A.dpart[t][W] (the backward's rate gradient <u_t, v_t>
+// without a pass of its own over u).
+template <int D, int CT, bool EXCL, bool REV, int EM, bool OF32, bool DOT = false>
 __device__ __forceinline__ void seg_wave(const SegArgs& A, unsigned char* smem, int bh, int s, int W, int l) {
+  static_assert(!DOT || OF32, "the partial dots are taken from the float32 output path");
   using Cfg = SegCfg<D, CT>;
   constexpr int NB = Cfg::NB;
   constexpr int C = Cfg::C, ROWB = Cfg::ROWB, MT = Cfg::MT, KP = Cfg::KP, NW = Cfg::NW;
@@ -274,6 +281,11 @@ __device__ __forceinline__ void seg_wave(const SegArgs& A, unsigned char* smem, 
   const __amdgpu_buffer_rsrc_t ro = make_rsrc(Oh + first * D, seg_toks * ROWB);
   const __amdgpu_buffer_rsrc_t ro32 =
       make_rsrc((float*)(void*)A.O + ((size_t)bh * T + first) * D, OF32 ? seg_toks * D * 4 : 0);
+  // DOT: the aux rows (bf16) and the partial dots of the segment, addressed like the outputs
+  const __amdgpu_buffer_rsrc_t raux =
+      make_rsrc(DOT ? (const void*)(A.aux + ((size_t)bh * T + first) * D) : nullptr, DOT ? seg_toks * ROWB : 0);
+  const __amdgpu_buffer_rsrc_t rdp =
+      make_rsrc(DOT ? (const void*)(A.dpart + ((size_t)bh * T + first) * NW) : nullptr, DOT ? seg_toks * NW * 4 : 0);
   const int erow = W * Cfg::EPW + l;   // the tile row whose eta lane l moves
   constexpr unsigned OOB = 0x80000000u;
   // byte offset in the segment's views of load k of tile i (of its eta value)
@@ -295,6 +307,22 @@ __device__ __forceinline__ void seg_wave(const SegArgs& A, unsigned char* smem, 
     } else {
       return (unsigned)(((long long)i * C + row) * D * 4) + col;
     }
+  };
+  // DOT: segment row of output row 16ib + li of tile i (OOB before the segment in reverse order)
+  auto seg_row = [&](int i, int ib) -> long long {
+    const int row = 16 * ib + li;
+    if constexpr (REV)
+      return seg_toks - 1 - (long long)i * C - row;
+    else
+      return (long long)i * C + row;
+  };
+  auto aux_ofs = [&](int i, int ib) -> unsigned {
+    const long long r = seg_row(i, ib);
+    return r >= 0 ? (unsigned)(r * ROWB) + (unsigned)((16 * W + 4 * g) * 2) : OOB;
+  };
+  auto dpart_ofs = [&](int i, int ib) -> unsigned {
+    const long long r = seg_row(i, ib);
+    return r >= 0 ? (unsigned)(r * NW + W) * 4u : OOB;
   };
   auto eta_ofs = [&](int i) -> unsigned {
     if constexpr (REV) {
@@ -386,13 +414,16 @@ __device__ __forceinline__ void seg_wave(const SegArgs& A, unsigned char* smem, 
     // wave the order is stores(i-2), Q(i+1) [tile i-1 start], K/V/eta(i+1) [tile i-1 middle].
     // With OF32 a tile's NB stores follow its K/V/eta issue: after tile i's loads come
     // stores(i-2), Q(i+1), K/V/eta(i+1), stores(i-1).
+    // DOT: its NB aux loads come right after Q(i+2) and are complete before the tile's stores (the wait
+    // before them), and each tile stores NB partial dots after its outputs.
+    constexpr int NBS = DOT ? 2 * NB : NB;   // stores per tile
     if constexpr (OF32) {
       if (i == 0)
         wait_vm_barrier<LOADS>();
       else if (i == 1)
-        wait_vm_barrier<LOADS + NB>();
+        wait_vm_barrier<LOADS + NBS>();
       else
-        wait_vm_barrier<LOADS + 2 * NB>();
+        wait_vm_barrier<LOADS + 2 * NBS>();
     } else if (i < 2) {
       wait_vm_barrier<LOADS>();
     } else {
@@ -403,6 +434,12 @@ __device__ __forceinline__ void seg_wave(const SegArgs& A, unsigned char* smem, 
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     }
     issue_q(i + Cfg::STAGES - 1);   // into the slot read during tile i-1
+    u32x2 vd[NB];                   // DOT: aux row 16ib + li, columns 16W + 4g .. + 3 (bf16)
+    if constexpr (DOT) {
+#pragma unroll
+      for (int ib = 0; ib < NB; ++ib)
+        vd[ib] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(raux, aux_ofs(i, ib), 0, 0));
+    }
     const unsigned char* st = smem + Cfg::OFF_RING + (i % Cfg::STAGES) * Cfg::STAGE;
     const unsigned char* ks = st + Cfg::OFF_K;
     const unsigned char* vs = st + Cfg::OFF_V;
@@ -515,6 +552,9 @@ __device__ __forceinline__ void seg_wave(const SegArgs& A, unsigned char* smem, 
     }
     // outputs into the V region of this slot (written out after the next barrier), or straight out
     unsigned char* ob = smem + Cfg::OFF_RING + (i % Cfg::STAGES) * Cfg::STAGE + Cfg::OFF_V;
+    // DOT: the aux loads have landed once only K/V/eta(i+2) may be outstanding (in both issue orders
+    // that copy comes after them)
+    if constexpr (DOT) wait_vm<2 * Cfg::MAT_LOADS + 1>();
 #pragma unroll
     for (int ib = 0; ib < NB; ++ib) {
       const float eq = EM == 1 ? es[16 * ib + li] : 1.f;   // rate of the output row's own token
@@ -523,6 +563,18 @@ __device__ __forceinline__ void seg_wave(const SegArgs& A, unsigned char* smem, 
       else
         *(bf16x4*)(ob + ib * 16 * ROWB + ofr) = to_bf16x4(eq * acc[ib][0], eq * acc[ib][1], eq * acc[ib][2],
                                                           eq * acc[ib][3]);
+    }
+    if constexpr (DOT) {
+#pragma unroll
+      for (int ib = 0; ib < NB; ++ib) {
+        float dot = acc[ib][0] * bf16lo_f(vd[ib].x) + acc[ib][1] * bf16hi_f(vd[ib].x) +
+                    acc[ib][2] * bf16lo_f(vd[ib].y) + acc[ib][3] * bf16hi_f(vd[ib].y);
+        dot += __shfl_xor(dot, 16);     // the four column groups of the row: lanes li + 16 g
+        dot += __shfl_xor(dot, 32);
+        // one store per block (lanes g = 0 carry it), so every wave issues the same count
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, dot), rdp,
+                                              g == 0 ? dpart_ofs(i, ib) : OOB, 0, 0);
+      }
     }
     if constexpr (Cfg::KC == 2) {
       bf16x8 ka1[MT];
@@ -554,13 +606,13 @@ __device__ __forceinline__ void seg_wave(const SegArgs& A, unsigned char* smem, 
 
 // Outputs of segment s of head bh (grid BH x nseg), starting from W0 plus
 // the increments of the earlier segments of the head.
-template <int D, int CT, bool EXCL, bool REV, int EM, bool OF32>
+template <int D, int CT, bool EXCL, bool REV, int EM, bool OF32, bool DOT = false>
 __global__ __attribute__((amdgpu_flat_work_group_size(1, D / 16 * WAVE),
                           amdgpu_waves_per_eu(SegCfg<D, CT>::WAVES_PER_SIMD))) void pt_seg_kernel(SegArgs A) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int bh = blockIdx.x / A.nseg, s = blockIdx.x % A.nseg;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  seg_wave<D, CT, EXCL, REV, EM, OF32>(A, smem, bh, s, w, threadIdx.x & 63);
+  seg_wave<D, CT, EXCL, REV, EM, OF32, DOT>(A, smem, bh, s, w, threadIdx.x & 63);
 }
 
 // Segment increments dS_s = K_s^T diag(eta_s) V_s for every segment but the
@@ -955,7 +1007,7 @@ size_t per_token_workspace(int64_t B, int64_t H, int64_t T, int64_t dk, int64_t 
 }
 
 // The three kernels of one bf16 pass over every head (forward order, or reversed with REV).
-template <int D, bool REV, int EM, bool OF32 = false>
+template <int D, bool REV, int EM, bool OF32 = false, bool DOT = false>
 static hipError_t launch_seg_pass(const SegArgs& A, int BH, bool excl, hipStream_t stream, const Timing& tm) {
   // (start_transposed: the slots already hold the transposed start states; no increments, no scan)
   using CfgD = IncrCfg<D>;
@@ -975,8 +1027,8 @@ static hipError_t launch_seg_pass(const SegArgs& A, int BH, bool excl, hipStream
                        A.nseg);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  auto kf = excl ? pt_seg_kernel<D, seg_tile<D>(), true, REV, EM, OF32>
-                 : pt_seg_kernel<D, seg_tile<D>(), false, REV, EM, OF32>;
+  auto kf = excl ? pt_seg_kernel<D, seg_tile<D>(), true, REV, EM, OF32, DOT>
+                 : pt_seg_kernel<D, seg_tile<D>(), false, REV, EM, OF32, DOT>;
   if ((e = hipFuncSetAttribute((const void*)kf, hipFuncAttributeMaxDynamicSharedMemorySize, CfgF::LDS_BYTES)) !=
       hipSuccess)
     return e;
@@ -1029,7 +1081,7 @@ hipError_t launch_per_token(const PerTokenArgs& a, hipStream_t stream, const Tim
 // float32 rows of a segment must stay below 2^31 bytes: 2^21 tokens at d = 128
 constexpr int64_t BWD_MAX_SEG_TOKENS = (int64_t)1 << 21;
 struct BwdLayout {
-  size_t slots, w0t, dwt, junk, total;
+  size_t slots, w0t, dwt, junk, dpart, total;
 };
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 static BwdLayout bwd_layout(int64_t B, int64_t H, int64_t T, int64_t D) {
@@ -1041,6 +1093,7 @@ static BwdLayout bwd_layout(int64_t B, int64_t H, int64_t T, int64_t D) {
   L.w0t = o; o += align256(st);
   L.dwt = o; o += align256(st);
   L.junk = o; o += align256(st);
+  L.dpart = o; o += align256((size_t)B * H * T * (D / 16) * 4);   // bf16 path: the u pass's partial dots
   L.total = o;
   return L;
 }
@@ -1107,6 +1160,18 @@ __global__ __launch_bounds__(256) void pt_bwd_rate_grad_kernel(float* __restrict
   }
 }
 
+// deta_t = <u_t, v_t> from the u pass's per-wave partials (NW of them per token, summed in wave order).
+template <int NW>
+__global__ __launch_bounds__(256) void pt_bwd_dot_sum_kernel(const float* __restrict__ dpart, float* __restrict__ deta,
+                                                             long long ntok) {
+  for (long long t = (long long)blockIdx.x * 256 + threadIdx.x; t < ntok; t += (long long)gridDim.x * 256) {
+    float x = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) x += dpart[t * NW + w];
+    deta[t] = x;
+  }
+}
+
 template <int D>
 static hipError_t launch_bwd(const BackwardArgs& a, hipStream_t stream) {
   const int BH = (int)(a.B * a.H);
@@ -1129,16 +1194,18 @@ static hipError_t launch_bwd(const BackwardArgs& a, hipStream_t stream) {
   // (SegArgs.O is typed bf16; the OF32 passes write floats through it)
   const SegArgs Aq{dO, V, K, a.eta, w0t, slots, (bf16*)a.dQ, junk, T, sp.nseg, sp.seg_len};
   if ((e = launch_seg_pass<D, false, 0, true>(Aq, BH, excl, stream, none)) != hipSuccess) return e;
-  const SegArgs Au{K, Q, dO, a.eta, a.dW, slots, (bf16*)a.dV, a.dW0, T, sp.nseg, sp.seg_len};
-  if ((e = launch_seg_pass<D, true, 2, true>(Au, BH, excl, stream, none)) != hipSuccess) return e;
+  // u_t = k_t G_t: written as dV = eta u (rates on the outputs), with the partials of deta = <u, v>
+  float* dpart = (float*)(ws + L.dpart);
+  SegArgs Au{K, Q, dO, a.eta, a.dW, slots, (bf16*)a.dV, a.dW0, T, sp.nseg, sp.seg_len};
+  Au.aux = V;
+  Au.dpart = dpart;
+  if ((e = launch_seg_pass<D, true, 1, true, true>(Au, BH, excl, stream, none)) != hipSuccess) return e;
   // G^T's recurrence has the transposed increments and start states: it reuses the u pass's slots
   const SegArgs Ak{V, dO, Q, a.eta, dwt, slots, (bf16*)a.dK, junk, T, sp.nseg, sp.seg_len, 1};
   if ((e = launch_seg_pass<D, true, 1, true>(Ak, BH, excl, stream, none)) != hipSuccess) return e;
   if (ntok > 0) {
-    constexpr int TPB = 256 / (D / 8);
-    const unsigned grid = (unsigned)std::min<long long>((ntok + TPB - 1) / TPB, 8192);
-    hipLaunchKernelGGL((pt_bwd_rate_grad_kernel<D, bf16>), dim3(grid), dim3(256), 0, stream, (float*)a.dV, V, a.eta,
-                       a.deta, ntok);
+    const unsigned grid = (unsigned)std::min<long long>((ntok + 255) / 256, 8192);
+    hipLaunchKernelGGL((pt_bwd_dot_sum_kernel<D / 16>), dim3(grid), dim3(256), 0, stream, dpart, a.deta, ntok);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   return hipSuccess;
