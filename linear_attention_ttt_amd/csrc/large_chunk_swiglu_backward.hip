@@ -32,7 +32,7 @@
 // hi + lo (three products: hi hi, hi lo, lo hi; two when the other operand is
 // bf16 input) and float32 accumulation; the products of the tokens with the
 // weights run fused with the elementwise factors they feed and the products
-// of those factors with the weights (sw_bwd_step_kernel, sw_bwd_read_kernel);
+// of those factors with the weights (sw_bwd_step_kernel, sw_bwd_read_step_kernel);
 // the host walks the chunks.
 #include <algorithm>
 
@@ -286,160 +286,6 @@ __device__ __forceinline__ int wcat_col(int p, int m, int u) { return (u >> 4) *
 __device__ __forceinline__ int j13_col(int m, int u) { return (u >> 4) * 32 + m * 16 + (u & 15); }
 
 // ---------------------------------------------------------------------------
-// The read's two products of a 128-token tile with their elementwise step as
-// the epilogue (grid.x = 4 slices of 64 units; nothing but the results goes to
-// memory): Z1 = q [R1 | R3] (a, b: 128 columns, two 64-column pieces of the
-// [d][d_h] matrices), Z2 = dO R2^T (dh: 64 rows of R2) -> Eq [t][da | db],
-// Hq [t][silu(a) b].  Wave w takes token rows 32 w .. 32 w + 31 of both, so
-// that a, b and dh of one (token, unit) sit in one lane.  K = d = 128 in
-// 32-deep steps, operands staged as in sw_gemm_kernel (B1 as a [k][n] plane
-// read transposed, B2 as [n][k]), the next step loaded while the current one
-// is multiplied.
-// ---------------------------------------------------------------------------
-struct PairArgs {
-  const bf16* X1;       // [BH][T][d], already offset to the chunk
-  const bf16* X2;
-  const float* B1;      // per head + bh * sB1
-  long long sB1;
-  int ld1, piece1, slice1;      // column c -> (c / 64) piece1 + s slice1 + c % 64
-  const float* B2;      // rows of d floats, per head + bh * sB2
-  long long sB2;
-  int piece2, slice2;           // row c -> (c / 32) piece2 + s slice2 + c % 32
-  float* Eq;            // [BH][cap][2 d_h]
-  float* Hq;            // [BH][cap][d_h]
-  int T, c0, Cc;
-  long long cap;
-};
-
-__global__ __launch_bounds__(256, 2) void sw_bwd_read_kernel(PairArgs a) {
-  constexpr int X_PLANE = GT * PLANE_ROW;            // [t][k] bf16: 10240
-  constexpr int B1_PLANE = GK * PLANE_TR_ROW;        // [k][n] bf16: 9216
-  constexpr int B2_PLANE = 64 * PLANE_ROW;           // [n][k] bf16: 5120
-  __shared__ __attribute__((aligned(16))) unsigned char lds[2 * X_PLANE + 2 * B1_PLANE + 2 * B2_PLANE];
-  unsigned char* x1p = lds;
-  unsigned char* x2p = lds + X_PLANE;
-  unsigned char* b1h = lds + 2 * X_PLANE;
-  unsigned char* b1l = b1h + B1_PLANE;
-  unsigned char* b2h = b1l + B1_PLANE;
-  unsigned char* b2l = b2h + B2_PLANE;
-  const int sl = blockIdx.x, t0 = blockIdx.y * GT;
-  const long long bh = blockIdx.z;
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, gq = l >> 4, li = l & 15;
-  const long long xoff = bh * (long long)a.T * BD;
-  const bf16* X1 = a.X1 + xoff;
-  const bf16* X2 = a.X2 + xoff;
-  const float* B1 = a.B1 + bh * a.sB1;
-  const float* B2 = a.B2 + bh * a.sB2;
-  const int Cc = a.Cc;
-  // loads of one 32-deep step: X1, X2 (2 pieces of 8 bf16 each per thread), B1 (4 pieces of 4 floats: 32 k
-  // rows x 32 pieces), B2 (2 pieces of 4 floats: 64 rows x 8 pieces)
-  u32x4 v1[2], v2[2], vb1[4], vb2[2];
-  auto load = [&](int k0) {
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int idx = tid + 256 * q, row = idx >> 2, pc = idx & 3;
-      const bool ok = t0 + row < Cc;
-      const long long o = (long long)(t0 + row) * BD + k0 + 8 * pc;
-      v1[q] = ok ? *(const u32x4*)(X1 + o) : u32x4{0u, 0u, 0u, 0u};
-      v2[q] = ok ? *(const u32x4*)(X2 + o) : u32x4{0u, 0u, 0u, 0u};
-    }
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int idx = tid + 256 * q, kr = idx >> 5, c = (idx & 31) * 4;
-      vb1[q] = *(const u32x4*)(B1 + (long long)(k0 + kr) * a.ld1 + (c >> 6) * a.piece1 + sl * a.slice1 + (c & 63));
-    }
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int idx = tid + 256 * q, row = idx >> 3, pc = idx & 7;
-      const int r = (row >> 5) * a.piece2 + sl * a.slice2 + (row & 31);
-      vb2[q] = *(const u32x4*)(B2 + (long long)r * BD + k0 + 4 * pc);
-    }
-  };
-  auto store = [&]() {
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int idx = tid + 256 * q, row = idx >> 2, pc = idx & 3;
-      *(u32x4*)(x1p + row * PLANE_ROW + pc * 16) = v1[q];
-      *(u32x4*)(x2p + row * PLANE_ROW + pc * 16) = v2[q];
-    }
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int idx = tid + 256 * q, kr = idx >> 5, pc = idx & 31;
-      const floatx4 f = __builtin_bit_cast(floatx4, vb1[q]);
-      const uint2 s0 = split2(f[0], f[1]), s1 = split2(f[2], f[3]);
-      *(uint2*)(b1h + kr * PLANE_TR_ROW + pc * 8) = uint2{s0.x, s1.x};
-      *(uint2*)(b1l + kr * PLANE_TR_ROW + pc * 8) = uint2{s0.y, s1.y};
-    }
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int idx = tid + 256 * q, row = idx >> 3, pc = idx & 7;
-      const floatx4 f = __builtin_bit_cast(floatx4, vb2[q]);
-      const uint2 s0 = split2(f[0], f[1]), s1 = split2(f[2], f[3]);
-      *(uint2*)(b2h + row * PLANE_ROW + pc * 8) = uint2{s0.x, s1.x};
-      *(uint2*)(b2l + row * PLANE_ROW + pc * 8) = uint2{s0.y, s1.y};
-    }
-  };
-  floatx4 z1[2][8], z2[2][4];
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) z1[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int j = 0; j < 4; ++j) z2[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
-  }
-  load(0);
-  for (int k0 = 0; k0 < BD; k0 += GK) {
-    store();
-    __syncthreads();
-    if (k0 + GK < BD) load(k0 + GK);
-    bf16x8 x1[2], x2[2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      x1[i] = gemm_frag<false>(x1p, 32 * w + 16 * i);
-      x2[i] = gemm_frag<false>(x2p, 32 * w + 16 * i);
-    }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const bf16x8 bh = gemm_frag<true>(b1h, 16 * j), bl = gemm_frag<true>(b1l, 16 * j);
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        z1[i][j] = mfma16(x1[i], bh, z1[i][j]);
-        z1[i][j] = mfma16(x1[i], bl, z1[i][j]);
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const bf16x8 bh = gemm_frag<false>(b2h, 16 * j), bl = gemm_frag<false>(b2l, 16 * j);
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        z2[i][j] = mfma16(x2[i], bh, z2[i][j]);
-        z2[i][j] = mfma16(x2[i], bl, z2[i][j]);
-      }
-    }
-    __syncthreads();
-  }
-  // epilogue: lane (gq, li) holds rows 32 w + 16 i + 4 gq + r, columns 16 j + li of every piece
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int t = t0 + 32 * w + 16 * i + 4 * gq + r;
-      if (t >= Cc) continue;
-      const long long orow = bh * a.cap + t;
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const float av = z1[i][jj][r], bv = z1[i][4 + jj][r], dh = z2[i][jj][r];
-        const float sg = sigm(av), sv = av * sg, s1 = sg * (1.0f + av * (1.0f - sg));
-        const int u = 64 * sl + 16 * jj + li;
-        float* eq = a.Eq + orow * 2 * BDH;
-        eq[u] = dh * bv * s1;
-        eq[BDH + u] = dh * sv;
-        a.Hq[orow * BDH + u] = sv * bv;
-      }
-    }
-}
-
-// ---------------------------------------------------------------------------
 // The step's vector-Jacobian product for a 128-token tile of one head, all of
 // it but the two products that contract over the chunk's tokens (K^T E1a and
 // E3^T V): 8 waves of 16 tokens each; the 256 hidden units are visited in 16
@@ -474,7 +320,7 @@ struct StepArgs {
   int T, c0, Cc;
   long long cap;
 };
-constexpr int ST_WAVES = 8, ST_TOK = 16 * ST_WAVES;
+constexpr int ST_WAVES = 8, ST_TOK = 16 * ST_WAVES, ST_NT = 64 * ST_WAVES;
 constexpr int ST_WC_ROW = 64 * 2 + 32;         // [d][64 columns] bf16 plane row: 160 bytes
 constexpr int ST_W2_ROW = BD * 2 + 32;         // [32 rows][d] plane row: 288 bytes
 constexpr int ST_WC_PLANE = BD * ST_WC_ROW;    // 20480
@@ -686,57 +532,241 @@ __global__ __launch_bounds__(ST_WAVES * 64, 1) void sw_bwd_step_kernel(StepArgs 
   }
 }
 
+// ---------------------------------------------------------------------------
+// The read's gradients for a 128-token tile of one head at read weights R
+// (packed W1 | W3 | W2): 8 waves of 16 tokens, the 256 hidden units in 16
+// slices of 16, and per slice
+//   a = q R1_slice, b = q R3_slice (32 columns), dh = dO R2_slice^T (16),
+//   da = dh b silu'(a), db = dh silu(a), h = silu(a) b,
+//   Eq = (da, db) and Hq = h to memory (the operands of the weight terms
+//   Q^T Eq and Hq^T dO), and dQ += [da | db] [R1 | R3]_slice^T,
+// then dQ is written.  Structure as sw_bwd_step_kernel: q and dO rows in
+// registers, the slice's weights staged once per workgroup as bf16 hi + lo
+// planes ([d][32 columns]: read transposed for a, b and directly for dQ;
+// [16 rows][d] read directly for dh), each wave's factors through its own
+// [column][token] planes.
+// ---------------------------------------------------------------------------
+struct ReadStepArgs {
+  const bf16* Q;        // [BH][T][d], offset to the chunk
+  const bf16* dO;
+  const float* R;       // read weights, per head + bh * sR
+  long long sR;
+  float* Eq;            // [BH][cap][2 d_h]
+  float* Hq;            // [BH][cap][d_h]
+  float* dQ;            // [BH][T][d], offset to the chunk
+  int T, Cc;
+  long long cap;
+};
+constexpr int RS_W13_ROW = 32 * 2 + 32;         // [d][32 columns] bf16 plane row: 96 bytes
+constexpr int RS_W13_PLANE = BD * RS_W13_ROW;   // 12288
+constexpr int RS_W2_PLANE = 16 * ST_W2_ROW;     // [16 rows][d]: 4608
+constexpr int RS_E_PLANE = 32 * 32;             // [32 columns][16 tokens] bf16
+constexpr int RS_WAVE_BYTES = 2 * RS_E_PLANE;
+constexpr int RS_LDS = 2 * RS_W13_PLANE + 2 * RS_W2_PLANE + ST_WAVES * RS_WAVE_BYTES;   // 50176
+constexpr int RS_PW = BD * 32 / 4 / ST_NT, RS_P2 = 16 * BD / 4 / ST_NT;               // 16-byte pieces per thread
+
+__global__ __launch_bounds__(ST_NT, 1) void sw_bwd_read_step_kernel(ReadStepArgs a) {
+  __shared__ __attribute__((aligned(16))) unsigned char lds[RS_LDS];
+  unsigned char* wh = lds;
+  unsigned char* wl = wh + RS_W13_PLANE;
+  unsigned char* w2h = wl + RS_W13_PLANE;
+  unsigned char* w2l = w2h + RS_W2_PLANE;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, gq = l >> 4, li = l & 15;
+  unsigned char* eh = w2l + RS_W2_PLANE + w * RS_WAVE_BYTES;
+  unsigned char* el = eh + RS_E_PLANE;
+  const long long bh = blockIdx.y;
+  const int t0 = blockIdx.x * ST_TOK + 16 * w;
+  const int Cc = a.Cc;
+  const float* R = a.R + bh * a.sR;
+  const long long trow = bh * (long long)a.T;
+  bf16x8 qf[4], of[4];
+  {
+    const int t = t0 + li;
+    const bool ok = t < Cc;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const long long o = (trow + t) * BD + 32 * ks + 8 * gq;
+      qf[ks] = ok ? *(const bf16x8*)(a.Q + o) : bf16x8{};
+      of[ks] = ok ? *(const bf16x8*)(a.dO + o) : bf16x8{};
+    }
+  }
+  // a slice's weights: R1, R3 columns 16 s .. 16 s + 15 ([d][32 columns]: 8 pieces of 4 floats per d), R2 rows
+  // 16 s .. 16 s + 15 (32 pieces each)
+  u32x4 pw[RS_PW], p2[RS_P2];
+  auto load = [&](int s) {
+#pragma unroll
+    for (int q = 0; q < RS_PW; ++q) {
+      const int idx = tid + ST_NT * q, d = idx >> 3, pc = idx & 7;
+      pw[q] = *(const u32x4*)(R + (long long)(pc >> 2) * BP + (long long)d * BDH + 16 * s + 4 * (pc & 3));
+    }
+#pragma unroll
+    for (int q = 0; q < RS_P2; ++q) {
+      const int idx = tid + ST_NT * q, row = idx >> 5, pc = idx & 31;
+      p2[q] = *(const u32x4*)(R + 2 * BP + (long long)(16 * s + row) * BD + 4 * pc);
+    }
+  };
+  auto store = [&]() {
+#pragma unroll
+    for (int q = 0; q < RS_PW; ++q) {
+      const int idx = tid + ST_NT * q, d = idx >> 3, pc = idx & 7;
+      const floatx4 f = __builtin_bit_cast(floatx4, pw[q]);
+      const uint2 s0 = split2(f[0], f[1]), s1 = split2(f[2], f[3]);
+      *(uint2*)(wh + d * RS_W13_ROW + pc * 8) = uint2{s0.x, s1.x};
+      *(uint2*)(wl + d * RS_W13_ROW + pc * 8) = uint2{s0.y, s1.y};
+    }
+#pragma unroll
+    for (int q = 0; q < RS_P2; ++q) {
+      const int idx = tid + ST_NT * q, row = idx >> 5, pc = idx & 31;
+      const floatx4 f = __builtin_bit_cast(floatx4, p2[q]);
+      const uint2 s0 = split2(f[0], f[1]), s1 = split2(f[2], f[3]);
+      *(uint2*)(w2h + row * ST_W2_ROW + pc * 8) = uint2{s0.x, s1.x};
+      *(uint2*)(w2l + row * ST_W2_ROW + pc * 8) = uint2{s0.y, s1.y};
+    }
+  };
+  floatx4 dq[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) dq[j] = floatx4{0.f, 0.f, 0.f, 0.f};
+  constexpr int NSLICE = BDH / 16;
+  load(0);
+  store();
+  load(1);
+  __syncthreads();
+  for (int s = 0; s < NSLICE; ++s) {
+    floatx4 z1[2], z2 = {0.f, 0.f, 0.f, 0.f};
+    z1[0] = z1[1] = z2;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        z1[j] = mfma16(qf[ks], frag_tr(wh, RS_W13_ROW, 32 * ks, 16 * j), z1[j]);
+        z1[j] = mfma16(qf[ks], frag_tr(wl, RS_W13_ROW, 32 * ks, 16 * j), z1[j]);
+      }
+      z2 = mfma16(of[ks], frag_dir(w2h, ST_W2_ROW, 32 * ks, 0), z2);
+      z2 = mfma16(of[ks], frag_dir(w2l, ST_W2_ROW, 32 * ks, 0), z2);
+    }
+    // the elementwise step: lane (gq, li) holds tokens t0 + 4 gq + r of unit 16 s + li
+    const int u = 16 * s + li;
+    float f1[2][4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float av = z1[0][r], bv = z1[1][r], dh = z2[r];
+      const float sg = sigm(av), sv = av * sg, s1 = sg * (1.0f + av * (1.0f - sg));
+      f1[0][r] = dh * bv * s1;
+      f1[1][r] = dh * sv;
+      const int t = t0 + 4 * gq + r;
+      if (t < Cc) {
+        const long long orow = bh * a.cap + t;
+        a.Eq[orow * 2 * BDH + u] = f1[0][r];
+        a.Eq[orow * 2 * BDH + BDH + u] = f1[1][r];
+        a.Hq[orow * BDH + u] = sv * bv;
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const uint2 s0 = split2(f1[q][0], f1[q][1]), s1 = split2(f1[q][2], f1[q][3]);
+      const int off = (16 * q + li) * 32 + 8 * gq;
+      *(uint2*)(eh + off) = uint2{s0.x, s1.x};
+      *(uint2*)(el + off) = uint2{s0.y, s1.y};
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_wave_barrier();
+    // dQ += [da | db] [R1 | R3]_slice^T (k = the slice's 32 columns)
+    {
+      const bf16x8 ah = frag_tr(eh, 32, 0, 0), al = frag_tr(el, 32, 0, 0);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const bf16x8 bh = frag_dir(wh, RS_W13_ROW, 0, 16 * j), bl = frag_dir(wl, RS_W13_ROW, 0, 16 * j);
+        dq[j] = mfma16(ah, bh, dq[j]);
+        dq[j] = mfma16(ah, bl, dq[j]);
+        dq[j] = mfma16(al, bh, dq[j]);
+      }
+    }
+    __syncthreads();                 // every wave is done with the slice's weight planes
+    if (s + 1 < NSLICE) {
+      store();
+      if (s + 2 < NSLICE) load(s + 2);
+      __syncthreads();
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int t = t0 + 4 * gq + r;
+    if (t < Cc) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) a.dQ[(trow + t) * BD + 16 * j + li] = dq[j][r];
+    }
+  }
+}
+
 // Per head: the normalisation's backward dU of G (packed W1 | W3 | W2) at the chunk's normalised weights Wc and
 // norms nrm, and the step's operands at the weights before it (Wp): Wcat [d][1024] in wcat_col order (part 0:
-// W1, W3; part 1: dU1, dU3), W2cat [W2 ; dU2] (2 d_h x d).  Block (matrix m, group of 16 columns): 16 row
-// groups x 16 columns, each thread summing w . G over its rows (8 of W1 / W3, 16 of W2), the 16 partials
-// added in a fixed order through LDS.  Norm columns: 0..255 W1, 256..511 W3, 512..639 W2.
-// last_only: dU1 = dU3 = 0, dU2 = G2.
+// W1, W3; part 1: dU1, dU3), W2cat [W2 ; dU2] (2 d_h x d).  Block (matrix m, group of 16 columns): 64 row
+// groups x 4 column quads, each thread holding 4 columns (16-byte accesses) of 2 rows of W1 / W3 or 4 rows of
+// W2 and summing w . G over them; the 64 partials of a column are added in a fixed order through LDS.
+// Norm columns: 0..255 W1, 256..511 W3, 512..639 W2.  last_only: dU1 = dU3 = 0, dU2 = G2.
 __global__ __launch_bounds__(256) void sw_bwd_prep(const float* __restrict__ G, const float* __restrict__ Wc,
                                                    long long wc_stride, const float* __restrict__ nrm,
                                                    long long nrm_stride, const float* __restrict__ Wp,
                                                    long long wp_stride, float* __restrict__ Wcat,
                                                    float* __restrict__ W2cat, int last_only) {
-  __shared__ float part[16][17];
+  __shared__ float part[64][17];
+  __shared__ float dots[16];
   const long long h = blockIdx.y;
   const int grp = blockIdx.x, m = grp < 16 ? 0 : grp < 32 ? 1 : 2;
-  const int cl = threadIdx.x & 15, rg = threadIdx.x >> 4;
-  const int col = (m < 2 ? (grp & 15) : grp - 32) * 16 + cl;
-  const int ld = m < 2 ? BDH : BD, rows = m < 2 ? BD : BDH, per = rows / 16;
+  const int cq = threadIdx.x & 3, rg = threadIdx.x >> 2;      // column quad, row group
+  const int col0 = (m < 2 ? (grp & 15) : grp - 32) * 16, col = col0 + 4 * cq;
+  const int ld = m < 2 ? BDH : BD;
+  constexpr int PER_MAX = 4;
+  const int per = m < 2 ? BD / 64 : BDH / 64;                 // rows per thread: 2 or 4
   const long long base = (long long)m * BP;
   const float* g = G + h * 3 * BP + base;
   const float* wc = Wc + h * wc_stride + base;
   const float* wp = Wp + h * wp_stride + base;
-  float gv[16], dot = 0.f;
+  floatx4 gv[PER_MAX], wv[PER_MAX];
+  floatx4 dot = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int k = 0; k < 16; ++k)
+  for (int k = 0; k < PER_MAX; ++k)
     if (k < per) {
-      const long long o = (long long)(rg + 16 * k) * ld + col;
-      gv[k] = g[o];
-      dot += gv[k] * wc[o];
+      const long long o = (long long)(rg + 64 * k) * ld + col;
+      gv[k] = *(const floatx4*)(g + o);
+      wv[k] = *(const floatx4*)(wc + o);
+      dot += gv[k] * wv[k];
     }
-  part[rg][cl] = dot;
-  __syncthreads();
-  dot = 0.f;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) dot += part[r][cl];
-  const float n = nrm[h * nrm_stride + (m < 2 ? m * BDH + col : 2 * BDH + col)];
+  for (int j = 0; j < 4; ++j) part[rg][4 * cq + j] = dot[j];
+  __syncthreads();
+  if (threadIdx.x < 16) {
+    float x = 0.f;
+    for (int r = 0; r < 64; ++r) x += part[r][threadIdx.x];
+    dots[threadIdx.x] = x;
+  }
+  __syncthreads();
+  floatx4 dt, n;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    dt[j] = dots[4 * cq + j];
+    n[j] = nrm[h * nrm_stride + (m < 2 ? m * BDH : 2 * BDH) + col + j];
+  }
   float* wcat = Wcat + h * BD * 4 * BDH;
   float* w2cat = W2cat + h * 2 * BP;
 #pragma unroll
-  for (int k = 0; k < 16; ++k)
+  for (int k = 0; k < PER_MAX; ++k)
     if (k < per) {
-      const int r = rg + 16 * k;
+      const int r = rg + 64 * k;
       const long long o = (long long)r * ld + col;
-      float du = n > BNORM_EPS ? (gv[k] - wc[o] * dot) / n : gv[k] / BNORM_EPS;
+      floatx4 du;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        du[j] = n[j] > BNORM_EPS ? (gv[k][j] - wv[k][j] * dt[j]) / n[j] : gv[k][j] / BNORM_EPS;
+      const floatx4 w0 = *(const floatx4*)(wp + o);
       if (m < 2) {
-        if (last_only) du = 0.f;
-        wcat[(long long)r * 4 * BDH + wcat_col(0, m, col)] = wp[o];
-        wcat[(long long)r * 4 * BDH + wcat_col(1, m, col)] = du;
+        if (last_only) du = floatx4{0.f, 0.f, 0.f, 0.f};
+        *(floatx4*)(wcat + (long long)r * 4 * BDH + wcat_col(0, m, col)) = w0;
+        *(floatx4*)(wcat + (long long)r * 4 * BDH + wcat_col(1, m, col)) = du;
       } else {
         if (last_only) du = gv[k];
-        w2cat[o] = wp[o];
-        w2cat[BP + o] = du;
+        *(floatx4*)(w2cat + o) = w0;
+        *(floatx4*)(w2cat + BP + o) = du;
       }
     }
 }
@@ -897,17 +927,11 @@ hipError_t launch_large_chunk_swiglu_backward(const BackwardArgs& a, int last_on
     const bf16* dOc = dO + c0 * BD;
     float* Eq = E1;    // [Cc][da | db]        (E1's room)
     float* Hq = E2;    // [Cc][silu(a) b]      (E2's room)
-    // a = Q R1, b = Q R3, dh = dO R2^T and their elementwise step
-    const PairArgs pa{Qc, dOc, R, rstride, BDH, (int)BP, 64, R + 2 * BP, rstride, 32, 64, Eq, Hq, (int)T, (int)c0, Cc,
-                      cap};
-    hipLaunchKernelGGL(sw_bwd_read_kernel, dim3(BDH / 64, (unsigned)((Cc + GT - 1) / GT), BH), dim3(256), 0, stream,
-                       pa);
+    // the read's factors and dQ
+    const ReadStepArgs ra{Qc, dOc, R, rstride, Eq, Hq, dQ + c0 * BD, (int)T, Cc, cap};
+    hipLaunchKernelGGL(sw_bwd_read_step_kernel, dim3((unsigned)((Cc + ST_TOK - 1) / ST_TOK), BH), dim3(ST_NT), 0,
+                       stream, ra);
     if ((e2 = hipGetLastError()) != hipSuccess) return e2;
-    // dQ = da R1^T + db R3^T: one product over k = (unit of R1 | unit of R3)
-    GemmArgs gq = gargs(Eq, 2 * BDH, 1, cap * 2 * BDH, R, 1, BDH, rstride, dQ + c0 * BD, BD, T * BD, Cc, BD, 2 * BDH);
-    gq.B2 = R + BP;
-    gq.kseg = BDH;
-    if ((e2 = gemm<float, float>(gq, BH, stream)) != hipSuccess) return e2;
     // (Q^T da | Q^T db), (silu(a) b)^T dO
     if ((e2 = gemm<bf16, float>(gargs(Qc, 1, BD, T * BD, Eq, 2 * BDH, 1, cap * 2 * BDH, A13, 2 * BDH, BD * 2 * BDH,
                                       BD, 2 * BDH, Cc), BH, stream, s13, p13)) != hipSuccess)
