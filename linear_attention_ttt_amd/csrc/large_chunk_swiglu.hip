@@ -81,6 +81,30 @@ __device__ __forceinline__ int w2i(int u, int d) { return (((d >> 4) * 4 + (u >>
 // logistic function with the hardware reciprocal (about 1 ulp): its value
 // only feeds bf16 operands or a bf16 hi + lo pair, so a correctly rounded
 // division buys nothing here
+// One matrix of a recurrence stage: 8 direct-to-LDS loads of 16 bytes per lane (non-temporal), load j into
+// LDS lds + 1024 j + 16 lane.  The instruction offset (1024 (j % 4)) is added to both the global and the LDS
+// address, so four loads share one M0 and off[j] is the global offset less it.  Written as one asm statement
+// (M0 set twice instead of per load); the compiler does not see these loads, so the caller counts them in
+// its vmcnt waits, as with dma16.
+__device__ __forceinline__ void stage_dma(__amdgpu_buffer_rsrc_t r, const unsigned (&off)[8], const void* lds) {
+  unsigned saved;
+  const unsigned base = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)lds);
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\t"
+      "buffer_load_dwordx4 %4, %1, 0 offen nt lds\n\t"
+      "buffer_load_dwordx4 %5, %1, 0 offen offset:1024 nt lds\n\t"
+      "buffer_load_dwordx4 %6, %1, 0 offen offset:2048 nt lds\n\t"
+      "buffer_load_dwordx4 %7, %1, 0 offen offset:3072 nt lds\n\t"
+      "s_mov_b32 m0, %3\n\ts_nop 0\n\t"
+      "buffer_load_dwordx4 %8, %1, 0 offen nt lds\n\t"
+      "buffer_load_dwordx4 %9, %1, 0 offen offset:1024 nt lds\n\t"
+      "buffer_load_dwordx4 %10, %1, 0 offen offset:2048 nt lds\n\t"
+      "buffer_load_dwordx4 %11, %1, 0 offen offset:3072 nt lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(r), "s"(base), "s"(base + 4096u), "v"(off[0]), "v"(off[1]), "v"(off[2]), "v"(off[3]), "v"(off[4]),
+        "v"(off[5]), "v"(off[6]), "v"(off[7]));
+}
 __device__ __forceinline__ float sigmoid_fast(float a) { return __builtin_amdgcn_rcpf(1.0f + __expf(-a)); }
 
 __device__ __forceinline__ void split_store8(bf16* hi, bf16* lo, const float* f) {
@@ -433,11 +457,13 @@ __global__ __launch_bounds__(SW_WAVES * 64, 1) void swiglu_recur_kernel(
     const int ng = (min(c * chunk + chunk, T) - c * chunk + SW_GT - 1) / SW_GT;
     return ng > w ? (ng - w + SW_WAVES - 1) / SW_WAVES : 0;
   };
-  auto advance = [&](int& c, int& k) {       // next step of this wave (c == nchunks: none left)
+  // next step of this wave (c == nchunks: none left); kn caches count(c)
+  auto advance = [&](int& c, int& k, int& kn) {
     ++k;
-    while (c < nchunks && k >= count(c)) {
+    while (c < nchunks && k >= kn) {
       ++c;
       k = 0;
+      kn = c < nchunks ? count(c) : 0;
     }
   };
   auto group_of = [&](int c, int k) {
@@ -446,11 +472,13 @@ __global__ __launch_bounds__(SW_WAVES * 64, 1) void swiglu_recur_kernel(
   };
   // per-lane byte offsets: direct-to-LDS rows (4 per load), row-wise operand reads (row 16tt + li,
   // piece 4ks + g) and transposed reads (rows 16tt + 4g .. + 3, columns 16m + li)
+  // (load j of a stage: LDS bytes 1024 j + 16 lane; the instruction offset 1024 (j % 4) applies to both the
+  // global and the LDS address, so four loads share one LDS base and dma_off[j] is the global offset less it)
   unsigned dma_off[SW_STAGE / 1024];
 #pragma unroll
   for (int j = 0; j < SW_STAGE / 1024; ++j) {
     const int row = 4 * j + (l >> 4);
-    dma_off[j] = (unsigned)(row * SW_KROW + (((l & 15) ^ sw_swz(row)) << 4));
+    dma_off[j] = (unsigned)(row * SW_KROW + (((l & 15) ^ sw_swz(row)) << 4) - 1024 * (j & 3));
   }
   unsigned fwd_off[4], tr_off[8];
 #pragma unroll
@@ -470,10 +498,8 @@ __global__ __launch_bounds__(SW_WAVES * 64, 1) void swiglu_recur_kernel(
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kh + (size_t)t0 * D, (long long)n * SW_KROW);
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vh + (size_t)t0 * D, (long long)n * SW_KROW);
     const __amdgpu_buffer_rsrc_t re = make_rsrc(Eh + t0, (long long)n * 4);
-#pragma unroll
-    for (int j = 0; j < SW_STAGE / 1024; ++j) dma16<true>(rk, dma_off[j], S.kv[w][slot][0] + j * 1024);
-#pragma unroll
-    for (int j = 0; j < SW_STAGE / 1024; ++j) dma16<true>(rv, dma_off[j], S.kv[w][slot][1] + j * 1024);
+    stage_dma(rk, dma_off, S.kv[w][slot][0]);
+    stage_dma(rv, dma_off, S.kv[w][slot][1]);
     if (l < SW_GT) dma4<true>(re, (unsigned)(l * 4), S.eta[w][slot]);
   };
 
@@ -493,13 +519,13 @@ __global__ __launch_bounds__(SW_WAVES * 64, 1) void swiglu_recur_kernel(
 
   bf16x8 w1op[4], w3op[4], w2op[4];
   floatx4 dW1[8], dW3[8], dW2[8];
-  int ic = 0, ik = -1;                       // issue cursor: chunk, step within the chunk
-  advance(ic, ik);
-  int cc = ic, ck = ik;                      // compute cursor
+  int ic = 0, ik = -1, ikn = nchunks > 0 ? count(0) : 0;   // issue cursor: chunk, step within it, count
+  advance(ic, ik, ikn);
+  int cc = ic, ck = ik, ckn = ikn;           // compute cursor
   int step = 0;
   if (ic < nchunks) {
     issue(ic, group_of(ic, ik), 0);
-    advance(ic, ik);
+    advance(ic, ik, ikn);
   }
 
   for (int c = 0; c < nchunks; ++c) {
@@ -516,14 +542,14 @@ __global__ __launch_bounds__(SW_WAVES * 64, 1) void swiglu_recur_kernel(
 #pragma unroll
     for (int m = 0; m < 8; ++m) dW1[m] = dW3[m] = dW2[m] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-    for (; cc == c; advance(cc, ck), ++step) {
+    for (; cc == c; advance(cc, ck, ckn), ++step) {
       const int slot = step & 1;
       // the next stage goes into the one read during the previous step; this step's stage has
       // landed once only the next stage's loads are outstanding
       if (ic < nchunks) {
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         issue(ic, group_of(ic, ik), slot ^ 1);
-        advance(ic, ik);
+        advance(ic, ik, ikn);
         wait_vm<SW_LOADS>();
       } else {
         wait_vm<0>();
@@ -579,15 +605,18 @@ __global__ __launch_bounds__(SW_WAVES * 64, 1) void swiglu_recur_kernel(
       }
       // ---- partial chunk gradients over the 32 tokens ----
       // dW1[d][u] += K^T da, dW3[d][u] += K^T db, dW2[u][d] += eh^T V
+      if (!last_only) {
 #pragma unroll
-      for (int m = 0; m < 8; ++m) {
-        const bf16x8 kt = join(ktr[m][0], ktr[m][1]);
-        const bf16x8 vt = join(vtr[m][0], vtr[m][1]);
-        if (!last_only) {
+        for (int m = 0; m < 8; ++m) {
+          const bf16x8 kt = join(ktr[m][0], ktr[m][1]);
+          const bf16x8 vt = join(vtr[m][0], vtr[m][1]);
           dW1[m] = mfma16(kt, daop, dW1[m]);
           dW3[m] = mfma16(kt, dbop, dW3[m]);
+          dW2[m] = mfma16(ehop, vt, dW2[m]);
         }
-        dW2[m] = mfma16(ehop, vt, dW2[m]);
+      } else {
+#pragma unroll
+        for (int m = 0; m < 8; ++m) dW2[m] = mfma16(ehop, join(vtr[m][0], vtr[m][1]), dW2[m]);
       }
     }
 
