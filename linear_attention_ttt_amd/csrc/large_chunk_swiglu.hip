@@ -58,7 +58,7 @@ constexpr int SW_LOADS = 2 * SW_STAGE / 1024 + 1;   // direct-to-LDS loads per w
 
 struct RecurLds {
   unsigned char kv[SW_WAVES][2][2][SW_STAGE];   // [wave][stage][K, V]
-  float eta[SW_WAVES][2][SW_GT];
+  float eta[SW_WAVES][2][64];               // one value per lane copied; the first SW_GT are the stage's
   float w1[SW_D * SW_NS];   // W1[d][u] at w13i(d, u)
   float w3[SW_D * SW_NS];   // W3[d][u] at w13i(d, u)
   float w2[SW_NS * SW_D];   // W2[u][d] at w2i(u, d)
@@ -495,12 +495,15 @@ __global__ __launch_bounds__(SW_WAVES * 64, 1) void swiglu_recur_kernel(
     last_slot = slot;
     const int t0 = c * chunk + gi * SW_GT;
     const int n = min(c * chunk + chunk, T) - t0;   // valid tokens; rows beyond read as 0
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kh + (size_t)t0 * D, (long long)n * SW_KROW);
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vh + (size_t)t0 * D, (long long)n * SW_KROW);
-    const __amdgpu_buffer_rsrc_t re = make_rsrc(Eh + t0, (long long)n * 4);
+    // (1 <= n <= SW_GT: the sizes need no clamping)
+    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)(Kh + (size_t)t0 * D), (short)0,
+                                                                        n * SW_KROW, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)(Vh + (size_t)t0 * D), (short)0,
+                                                                        n * SW_KROW, 0x00020000);
+    const __amdgpu_buffer_rsrc_t re = __builtin_amdgcn_make_buffer_rsrc((void*)(Eh + t0), (short)0, n * 4, 0x00020000);
     stage_dma(rk, dma_off, S.kv[w][slot][0]);
     stage_dma(rv, dma_off, S.kv[w][slot][1]);
-    if (l < SW_GT) dma4<true>(re, (unsigned)(l * 4), S.eta[w][slot]);
+    dma4<true>(re, (unsigned)(l * 4), S.eta[w][slot]);    // lanes past the group read 0
   };
 
   // Barrier of the head's NSL workgroups (through their counter; the k-th barrier waits for NSL * k
@@ -554,8 +557,9 @@ __global__ __launch_bounds__(SW_WAVES * 64, 1) void swiglu_recur_kernel(
       } else {
         wait_vm<0>();
       }
+      // K of the stage at kb, V at kb + SW_STAGE; each lane's offset is added first so that the
+      // constant parts (V, token tile) become instruction offsets
       const unsigned char* kb = S.kv[w][slot][0];
-      const unsigned char* vb = S.kv[w][slot][1];
 
       // ---- forward of the 32 tokens: A = K W1, B = K W3, Dh = V W2^T (rows: tokens 16tt + 4g + r) ----
       floatx4 A[2], Bv[2], Dh[2];
@@ -566,8 +570,8 @@ __global__ __launch_bounds__(SW_WAVES * 64, 1) void swiglu_recur_kernel(
       for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
-          kop[ks][tt] = *(const bf16x8*)(kb + tt * 16 * SW_KROW + fwd_off[ks]);
-          vop[ks][tt] = *(const bf16x8*)(vb + tt * 16 * SW_KROW + fwd_off[ks]);
+          kop[ks][tt] = *(const bf16x8*)(kb + fwd_off[ks] + tt * 16 * SW_KROW);
+          vop[ks][tt] = *(const bf16x8*)(kb + fwd_off[ks] + SW_STAGE + tt * 16 * SW_KROW);
         }
       // transposed operands of the gradient products (k slot (g, j) = token 16(j/4) + 4g + j%4),
       // read while the forward products run
@@ -576,8 +580,8 @@ __global__ __launch_bounds__(SW_WAVES * 64, 1) void swiglu_recur_kernel(
       for (int m = 0; m < 8; ++m)
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
-          ktr[m][tt] = lds_read_tr16(kb + tt * 16 * SW_KROW + tr_off[m]);
-          vtr[m][tt] = lds_read_tr16(vb + tt * 16 * SW_KROW + tr_off[m]);
+          ktr[m][tt] = lds_read_tr16(kb + tr_off[m] + tt * 16 * SW_KROW);
+          vtr[m][tt] = lds_read_tr16(kb + tr_off[m] + SW_STAGE + tt * 16 * SW_KROW);
         }
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks)
