@@ -249,10 +249,11 @@ def test_backward_invalid_arguments(kw, code):
 
 @needs_lib
 def test_backward_workspace():
-    # segment slots (4 segments per head here, as in the forward), W0^T, dW^T and a discarded memory
+    # segment slots (4 segments per head here, as in the forward), W0^T, dW^T, a discarded memory and the
+    # u pass's partial dots (B H T d/16 floats)
     d = la.make_desc(4, 16, 4096, 128, 128, 0, la.BF16)
     st = 64 * 128 * 128 * 4
-    n = la.workspace_bytes(d, 64, "per_token_linear") + 3 * st
+    n = la.workspace_bytes(d, 64, "per_token_linear") + 3 * st + 4 * 16 * 4096 * 8 * 4
     assert la.backward_workspace_bytes(d, 64, "per_token_linear") == n
     assert la.backward_workspace_bytes(d, 64, "per_token_linear_exclusive") == n
     # large-chunk linear: two sets of chunk updates (K^T diag(eta) V and Q^T dO), the memories and the
@@ -264,13 +265,15 @@ def test_backward_workspace():
         12 * nc * m * (2 * nsplit + 2) + 12 * 196608 * 4 + 12 * m
     assert la.backward_workspace_bytes(dl, 4096, "large_chunk_linear_update_first") == \
         la.backward_workspace_bytes(dl, 4096, "large_chunk_linear")
-    # float32 per-token: the transposed states and the discarded memory (one segment, no slots)
-    assert la.backward_workspace_bytes(la.make_desc(1, 1, 64, 64, 64, 0, la.FP32), 64, 0) == 3 * 64 * 64 * 4
+    # float32 per-token: the transposed states and the discarded memory (one segment, no slots); the
+    # partial-dot rows are laid out in every case
+    assert la.backward_workspace_bytes(la.make_desc(1, 1, 64, 64, 64, 0, la.FP32), 64, 0) == \
+        3 * 64 * 64 * 4 + 64 * 4 * 4
     assert bcall(desc=d, ws_bytes=n - 1) == 8
     # a backward segment holds at most 2^21 tokens (float32 rows addressed below 2^31 bytes)
     d1 = la.make_desc(256, 1, 1 << 22, 128, 128, 0, la.BF16)
     st1 = 256 * 128 * 128 * 4
-    assert la.backward_workspace_bytes(d1, 64, 0) == 2 * st1 + 3 * st1
+    assert la.backward_workspace_bytes(d1, 64, 0) == 2 * st1 + 3 * st1 + 256 * (1 << 22) * 8 * 4
 
 
 def mcall(mode=1, momentum=0.9, M0=ptr(8), M_out=ptr(9), desc=None, **kw):
