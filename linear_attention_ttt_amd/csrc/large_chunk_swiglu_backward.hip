@@ -28,12 +28,15 @@
 //
 // Every chunk's weights and column norms come from running the recurrence
 // again with a float32 dump (launch_swiglu_recur_dump).  The products are
-// batched over the heads on bf16 MFMA with float32 operands split into bf16
-// hi + lo (three products: hi hi, hi lo, lo hi; two when the other operand is
-// bf16 input) and float32 accumulation; the products of the tokens with the
-// weights run fused with the elementwise factors they feed and the products
-// of those factors with the weights (sw_bwd_step_kernel, sw_bwd_read_step_kernel);
-// the host walks the chunks.
+// batched over the heads on bf16 MFMA with float32 accumulation; a float32
+// weight operand is split into bf16 hi + lo (three products: hi hi, hi lo,
+// lo hi; two when the other operand is bf16 input).  The products of the
+// tokens with the weights run fused with the elementwise factors they feed and
+// the products of those factors with the weights (sw_bwd_step_kernel,
+// sw_bwd_read_step_kernel); the factors that the weight gradients contract
+// over the chunk's tokens (E1a, E3, Eq, Hq) go to memory rounded to bf16, like
+// the token inputs they meet there, and those products take one bf16 product
+// each.  The host walks the chunks.
 #include <algorithm>
 
 #include "device_common.h"
@@ -312,8 +315,8 @@ struct StepArgs {
   const float* eta;     // [BH][T]
   const float* Wcat;    // [BH][d][1024] (wcat_col order)
   const float* W2cat;   // [BH][2 d_h][d]
-  float* E1a;           // [BH][cap][512] (j13_col order)
-  float* E3;            // [BH][cap][d_h]
+  bf16* E1a;            // [BH][cap][512] (j13_col order)
+  bf16* E3;             // [BH][cap][d_h]
   float* dK;            // [BH][T][d], offset to the chunk
   float* dV;
   float* deta;          // [BH][T], offset to the chunk
@@ -457,9 +460,9 @@ __global__ __launch_bounds__(ST_WAVES * 64, 1) void sw_bwd_step_kernel(StepArgs 
       const int t = t0 + 4 * gq + r;
       if (t < Cc) {
         const long long orow = bh * a.cap + t;
-        a.E1a[orow * 2 * BDH + j13_col(0, u)] = f1[0][r];
-        a.E1a[orow * 2 * BDH + j13_col(1, u)] = f1[1][r];
-        a.E3[orow * BDH + u] = e * hd;
+        a.E1a[orow * 2 * BDH + j13_col(0, u)] = (bf16)f1[0][r];
+        a.E1a[orow * 2 * BDH + j13_col(1, u)] = (bf16)f1[1][r];
+        a.E3[orow * BDH + u] = (bf16)(e * hd);
       }
     }
     // the factors into the wave's [column][token] planes (4 consecutive tokens per lane and column)
@@ -551,8 +554,8 @@ struct ReadStepArgs {
   const bf16* dO;
   const float* R;       // read weights, per head + bh * sR
   long long sR;
-  float* Eq;            // [BH][cap][2 d_h]
-  float* Hq;            // [BH][cap][d_h]
+  bf16* Eq;             // [BH][cap][2 d_h]
+  bf16* Hq;             // [BH][cap][d_h]
   float* dQ;            // [BH][T][d], offset to the chunk
   int T, Cc;
   long long cap;
@@ -656,9 +659,9 @@ __global__ __launch_bounds__(ST_NT, 1) void sw_bwd_read_step_kernel(ReadStepArgs
       const int t = t0 + 4 * gq + r;
       if (t < Cc) {
         const long long orow = bh * a.cap + t;
-        a.Eq[orow * 2 * BDH + u] = f1[0][r];
-        a.Eq[orow * 2 * BDH + BDH + u] = f1[1][r];
-        a.Hq[orow * BDH + u] = sv * bv;
+        a.Eq[orow * 2 * BDH + u] = (bf16)f1[0][r];
+        a.Eq[orow * 2 * BDH + BDH + u] = (bf16)f1[1][r];
+        a.Hq[orow * BDH + u] = (bf16)(sv * bv);
       }
     }
 #pragma unroll
@@ -847,9 +850,9 @@ BwdSwLayout bwd_sw_layout(int64_t BH, int64_t T, int64_t chunk) {
   L.dnorm = o; o += al256((size_t)BH * nch * 640 * 4);
   L.wcat = o; o += al256((size_t)BH * BD * 4 * BDH * 4);
   L.w2cat = o; o += al256((size_t)BH * 2 * BDH * BD * 4);
-  L.e1 = o; o += al256((size_t)BH * Cc * 2 * BDH * 4);     // E1a, or the read's Eq
-  L.e2 = o; o += al256((size_t)BH * Cc * BDH * 4);         // the read's Hq
-  L.e3 = o; o += al256((size_t)BH * Cc * BDH * 4);
+  L.e1 = o; o += al256((size_t)BH * Cc * 2 * BDH * 2);     // E1a, or the read's Eq (bf16)
+  L.e2 = o; o += al256((size_t)BH * Cc * BDH * 2);         // the read's Hq (bf16)
+  L.e3 = o; o += al256((size_t)BH * Cc * BDH * 2);         // E3 (bf16)
   L.j13 = o; o += al256((size_t)s13 * BH * BD * 2 * BDH * 4);
   L.j2 = o; o += al256((size_t)s2 * BH * BP * 4);
   L.a13 = o; o += al256((size_t)s13 * BH * BD * 2 * BDH * 4);
@@ -888,9 +891,9 @@ hipError_t launch_large_chunk_swiglu_backward(const BackwardArgs& a, int last_on
   float* dnorm = (float*)(ws + L.dnorm);
   float* Wcat = (float*)(ws + L.wcat);
   float* W2cat = (float*)(ws + L.w2cat);
-  float* E1 = (float*)(ws + L.e1);
-  float* E2 = (float*)(ws + L.e2);
-  float* E3 = (float*)(ws + L.e3);
+  bf16* E1 = (bf16*)(ws + L.e1);
+  bf16* E2 = (bf16*)(ws + L.e2);
+  bf16* E3 = (bf16*)(ws + L.e3);
   float* J13 = (float*)(ws + L.j13);
   float* J2 = (float*)(ws + L.j2);
   float* A13 = (float*)(ws + L.a13);
@@ -925,18 +928,18 @@ hipError_t launch_large_chunk_swiglu_backward(const BackwardArgs& a, int last_on
     hipError_t e2;
     const bf16* Qc = Q + c0 * BD;
     const bf16* dOc = dO + c0 * BD;
-    float* Eq = E1;    // [Cc][da | db]        (E1's room)
-    float* Hq = E2;    // [Cc][silu(a) b]      (E2's room)
+    bf16* Eq = E1;     // [Cc][da | db]        (E1's room)
+    bf16* Hq = E2;     // [Cc][silu(a) b]      (E2's room)
     // the read's factors and dQ
     const ReadStepArgs ra{Qc, dOc, R, rstride, Eq, Hq, dQ + c0 * BD, (int)T, Cc, cap};
     hipLaunchKernelGGL(sw_bwd_read_step_kernel, dim3((unsigned)((Cc + ST_TOK - 1) / ST_TOK), BH), dim3(ST_NT), 0,
                        stream, ra);
     if ((e2 = hipGetLastError()) != hipSuccess) return e2;
     // (Q^T da | Q^T db), (silu(a) b)^T dO
-    if ((e2 = gemm<bf16, float>(gargs(Qc, 1, BD, T * BD, Eq, 2 * BDH, 1, cap * 2 * BDH, A13, 2 * BDH, BD * 2 * BDH,
+    if ((e2 = gemm<bf16, bf16>(gargs(Qc, 1, BD, T * BD, Eq, 2 * BDH, 1, cap * 2 * BDH, A13, 2 * BDH, BD * 2 * BDH,
                                       BD, 2 * BDH, Cc), BH, stream, s13, p13)) != hipSuccess)
       return e2;
-    return gemm<float, bf16>(gargs(Hq, 1, BDH, cap * BDH, dOc, BD, 1, T * BD, A2, BD, BP, BDH, BD, Cc), BH, stream, s2,
+    return gemm<bf16, bf16>(gargs(Hq, 1, BDH, cap * BDH, dOc, BD, 1, T * BD, A2, BD, BP, BDH, BD, Cc), BH, stream, s2,
                              p2);
   };
 
@@ -965,10 +968,10 @@ hipError_t launch_large_chunk_swiglu_backward(const BackwardArgs& a, int last_on
                        ST_LDS, stream, sa);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     // J13 = K^T (eta Pa | eta Pb), J2 = (eta hdot)^T V
-    if ((e = gemm<bf16, float>(gargs(Kc, 1, BD, T * BD, E1, 2 * BDH, 1, cap * 2 * BDH, J13, 2 * BDH, BD * 2 * BDH, BD,
+    if ((e = gemm<bf16, bf16>(gargs(Kc, 1, BD, T * BD, E1, 2 * BDH, 1, cap * 2 * BDH, J13, 2 * BDH, BD * 2 * BDH, BD,
                                      2 * BDH, Cc), BH, stream, s13, p13)) != hipSuccess)
       return e;
-    if ((e = gemm<float, bf16>(gargs(E3, 1, BDH, cap * BDH, Vc, BD, 1, T * BD, J2, BD, BP, BDH, BD, Cc), BH, stream, s2,
+    if ((e = gemm<bf16, bf16>(gargs(E3, 1, BDH, cap * BDH, Vc, BD, 1, T * BD, J2, BD, BP, BDH, BD, Cc), BH, stream, s2,
                                p2)) != hipSuccess)
       return e;
     if (read_first && (e = read_phase(Wp, wp_stride, c0, Cc)) != hipSuccess) return e;
