@@ -103,7 +103,9 @@ struct GemmOperand {
 };
 
 // One operand tile (ROWS rows from r0, k in [k0, kend)) into registers: 16-byte pieces, zeros past the
-// ragged extent; with kseg, steps at k0 >= kseg read P2 at k0 - kseg.
+// ragged extent; with kseg, steps at k0 >= kseg read P2 at k0 - kseg.  Buffer loads over the valid region
+// (rows below rend, or k below kend for a transposed operand; byte offsets below 2^31): a piece past it
+// reads 0 without a branch, so the compiler can count the loads in flight.
 template <typename T, bool TR, int ROWS>
 __device__ __forceinline__ void gemm_load(u32x4 (&v)[(GemmOperand<T, ROWS>::LOADS)], const T* P, long long s_row,
                                           long long s_k, int r0, int rend, int k0, int kend,
@@ -115,21 +117,20 @@ __device__ __forceinline__ void gemm_load(u32x4 (&v)[(GemmOperand<T, ROWS>::LOAD
     k0 -= kseg;
     kend -= kseg;
   }
+  const long long nvalid = TR ? (long long)kend * s_k : (long long)rend * s_row;
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(P, nvalid * (long long)sizeof(T));
 #pragma unroll
   for (int q = 0; q < O::LOADS; ++q) {
     const int idx = tid + 256 * q;
-    bool ok;
-    const T* src;
+    long long off;
     if (!TR) {
       const int row = idx / O::KPC, pc = idx % O::KPC;
-      ok = r0 + row < rend;
-      src = P + (long long)(r0 + row) * s_row + (k0 + pc * O::PER);
+      off = (long long)(r0 + row) * s_row + (k0 + pc * O::PER);
     } else {
       const int kr = idx / O::RPC, pc = idx % O::RPC;
-      ok = k0 + kr < kend;
-      src = P + (long long)(k0 + kr) * s_k + (r0 + pc * O::PER);
+      off = (long long)(k0 + kr) * s_k + (r0 + pc * O::PER);
     }
-    v[q] = ok ? *(const u32x4*)src : u32x4{0u, 0u, 0u, 0u};
+    v[q] = buf_load16(rs, (unsigned)(off * (long long)sizeof(T)));
   }
 }
 
@@ -195,19 +196,20 @@ __global__ __launch_bounds__(256, 2) void sw_gemm_kernel(GemmArgs g) {
   for (int i = 0; i < MI; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
-  u32x4 va[OA::LOADS], vb[OB::LOADS];
-  if (kbeg < kend) {
-    gemm_load<TA, ATR, BM>(va, A, a_row, a_k, m0, g.M, kbeg, kend);
-    gemm_load<TB, BTR, GT>(vb, B, b_row, b_k, n0, g.N, kbeg, kend, B2, g.kseg);
-  }
-  for (int k0 = kbeg; k0 < kend; k0 += GK) {
+  // two steps' tiles in flight in registers, in two sets used alternately (no copies between them, so
+  // each set's loads have two steps to arrive): set 0 holds the even steps from kbeg, set 1 the odd
+  u32x4 va0[OA::LOADS], vb0[OB::LOADS], va1[OA::LOADS], vb1[OB::LOADS];
+  auto load = [&](u32x4 (&va)[OA::LOADS], u32x4 (&vb)[OB::LOADS], int k) {
+    gemm_load<TA, ATR, BM>(va, A, a_row, a_k, m0, g.M, k, kend);
+    gemm_load<TB, BTR, GT>(vb, B, b_row, b_k, n0, g.N, k, kend, B2, g.kseg);
+  };
+  // one step: the set's tiles into LDS, the set reloaded with the step two ahead, the products
+  auto step = [&](u32x4 (&va)[OA::LOADS], u32x4 (&vb)[OB::LOADS], int k0) {
     gemm_store<TA, ATR, BM>(va, ahi, alo);
     gemm_store<TB, BTR, GT>(vb, bhi, blo);
     __syncthreads();
-    if (k0 + GK < kend) {
-      gemm_load<TA, ATR, BM>(va, A, a_row, a_k, m0, g.M, k0 + GK, kend);
-      gemm_load<TB, BTR, GT>(vb, B, b_row, b_k, n0, g.N, k0 + GK, kend, B2, g.kseg);
-    }
+    load(va, vb, k0 + 2 * GK);   // unconditional (past the end it reads zeros or unused values), so that
+                                 // the loads in flight are the same on every path
     bf16x8 bh[4], bl[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -227,6 +229,15 @@ __global__ __launch_bounds__(256, 2) void sw_gemm_kernel(GemmArgs g) {
       }
     }
     __syncthreads();
+  };
+  load(va0, vb0, kbeg);
+  asm volatile("" ::: "memory");   // set 0's loads stay the older ones, as in every later step
+  load(va1, vb1, kbeg + GK);
+  // (the loop only comes back after a step of set 1, so on every path set 1's loads are the newer)
+  for (int k0 = kbeg; k0 < kend; k0 += 2 * GK) {
+    step(va0, vb0, k0);
+    if (k0 + GK >= kend) break;
+    step(va1, vb1, k0 + GK);
   }
 #pragma unroll
   for (int i = 0; i < MI; ++i)
