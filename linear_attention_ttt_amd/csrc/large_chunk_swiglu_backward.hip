@@ -233,12 +233,15 @@ __global__ __launch_bounds__(256, 2) void sw_gemm_kernel(GemmArgs g) {
   load(va0, vb0, kbeg);
   asm volatile("" ::: "memory");   // set 0's loads stay the older ones, as in every later step
   load(va1, vb1, kbeg + GK);
-  // (the loop only comes back after a step of set 1, so on every path set 1's loads are the newer)
-  for (int k0 = kbeg; k0 < kend; k0 += 2 * GK) {
+  // pairs of steps, then an odd last step: the loop has no exit between its two steps, so on every path
+  // into a step of set 0 the loads of set 1 are the newer ones
+  const int nsteps = kend > kbeg ? (kend - kbeg + GK - 1) / GK : 0;
+  int k0 = kbeg;
+  for (int p = 0; p < nsteps / 2; ++p, k0 += 2 * GK) {
     step(va0, vb0, k0);
-    if (k0 + GK >= kend) break;
     step(va1, vb1, k0 + GK);
   }
+  if (nsteps & 1) step(va0, vb0, k0);
 #pragma unroll
   for (int i = 0; i < MI; ++i)
 #pragma unroll
