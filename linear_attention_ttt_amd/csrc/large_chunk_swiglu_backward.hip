@@ -299,6 +299,12 @@ __device__ __forceinline__ float sigm(float a) { return 1.0f / (1.0f + expf(-a))
 // Column of the concatenated step operand Wcat ([d][1024] per head) holding part p (0: the weights, 1: their
 // tangents dU) of matrix m (0: W1, 1: W3) at hidden unit u: 16-unit slices of 64 columns (W1, W3, dU1, dU3).
 __device__ __forceinline__ int wcat_col(int p, int m, int u) { return (u >> 4) * 64 + (2 * p + m) * 16 + (u & 15); }
+// A bf16 store into a buffer: a store past the buffer's end is dropped, so the factor stores of a tile's
+// ragged last rows need no branch (branches around stores keep the compiler from counting them, and it
+// would then wait for every store before each load of the next weight slice).
+__device__ __forceinline__ void st_bf16(__amdgpu_buffer_rsrc_t r, unsigned off, float x) {
+  __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, (bf16)x), r, off, 0, 0);
+}
 // Column of E1a ([t][512]: eta Pa, eta Pb) and of J13 = K^T E1a ([d][512]) for matrix m at unit u.
 __device__ __forceinline__ int j13_col(int m, int u) { return (u >> 4) * 32 + m * 16 + (u & 15); }
 
@@ -521,7 +527,9 @@ __global__ __launch_bounds__(ST_WAVES * 64, 1) void sw_bwd_step_kernel(StepArgs 
     __syncthreads();                 // every wave is done with the slice's weight planes
     if (s + 1 < NSLICE) {
       store();
-      if (s + 2 < NSLICE) load(s + 2);
+      // unconditional (the last slice again at the end, unused), so that the loads in flight are the
+      // same on every path and the wait for them does not also wait for the factor stores
+      load(s + 2 < NSLICE ? s + 2 : NSLICE - 1);
       __syncthreads();
     }
   }
@@ -596,6 +604,8 @@ __global__ __launch_bounds__(ST_NT, 1) void sw_bwd_read_step_kernel(ReadStepArgs
   const int Cc = a.Cc;
   const float* R = a.R + bh * a.sR;
   const long long trow = bh * (long long)a.T;
+  const __amdgpu_buffer_rsrc_t req = make_rsrc(a.Eq + bh * a.cap * 2 * BDH, (long long)Cc * 2 * BDH * 2);
+  const __amdgpu_buffer_rsrc_t rhq = make_rsrc(a.Hq + bh * a.cap * BDH, (long long)Cc * BDH * 2);
   bf16x8 qf[4], of[4];
   {
     const int t = t0 + li;
@@ -670,13 +680,10 @@ __global__ __launch_bounds__(ST_NT, 1) void sw_bwd_read_step_kernel(ReadStepArgs
       const float sg = sigm(av), sv = av * sg, s1 = sg * (1.0f + av * (1.0f - sg));
       f1[0][r] = dh * bv * s1;
       f1[1][r] = dh * sv;
-      const int t = t0 + 4 * gq + r;
-      if (t < Cc) {
-        const long long orow = bh * a.cap + t;
-        a.Eq[orow * 2 * BDH + u] = (bf16)f1[0][r];
-        a.Eq[orow * 2 * BDH + BDH + u] = (bf16)f1[1][r];
-        a.Hq[orow * BDH + u] = (bf16)(sv * bv);
-      }
+      const int t = t0 + 4 * gq + r;   // rows past Cc fall outside the buffers: their stores are dropped
+      st_bf16(req, (unsigned)((t * 2 * BDH + u) * 2), f1[0][r]);
+      st_bf16(req, (unsigned)((t * 2 * BDH + BDH + u) * 2), f1[1][r]);
+      st_bf16(rhq, (unsigned)((t * BDH + u) * 2), sv * bv);
     }
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
@@ -701,7 +708,9 @@ __global__ __launch_bounds__(ST_NT, 1) void sw_bwd_read_step_kernel(ReadStepArgs
     __syncthreads();                 // every wave is done with the slice's weight planes
     if (s + 1 < NSLICE) {
       store();
-      if (s + 2 < NSLICE) load(s + 2);
+      // unconditional (the last slice again at the end, unused), so that the loads in flight are the
+      // same on every path and the wait for them does not also wait for the factor stores
+      load(s + 2 < NSLICE ? s + 2 : NSLICE - 1);
       __syncthreads();
     }
   }
