@@ -51,28 +51,23 @@ constexpr int BDH = 256;           // d_h
 constexpr long long BP = (long long)BD * BDH;   // elements of one d x d_h matrix
 constexpr float BNORM_EPS = 1e-12f;
 
-__device__ __forceinline__ float to_f(float x) { return x; }
-__device__ __forceinline__ float to_f(bf16 x) { return (float)x; }
 
 // ---------------------------------------------------------------------------
-// C = A B (+ beta C) over a batch, with the contraction optionally split:
+// C = A B over a batch, with the contraction optionally split:
 // blockIdx.z = batch * nsplit + split, split s covering k in [s kper,
 // min(K, (s + 1) kper)) and writing its partial product to C + s bCs.  A is
 // M x K, B is K x N, addressed by element strides; one stride of each operand
 // is 1.  An operand whose contraction index is contiguous (A: sAk = 1, B:
 // sBk = 1) is staged in LDS as [row][k] and read as 16-byte MFMA fragments;
 // otherwise (ATR / BTR) it is staged as [k][row] in its own order and read
-// with the transposed LDS read.  Float32 operands are split into bf16 hi +
-// lo planes on the way into LDS (three products per pair, float32
-// accumulation); bf16 operands are exact and have no lo plane.
-// BM x 128 tiles (BM = 128 or 64), 32-deep steps, 4 waves of BM/2 x 64
-// (BM/32 x 4 16x16x32 MFMA tiles each); the next step's tiles are loaded into
-// registers while the current one is multiplied.  B may come in two pieces
-// along k (B2 for k >= kseg, at k - kseg; only where k is contiguous).
+// with the transposed LDS read.  Both operands are bf16 (float32
+// accumulation).  BM x 128 tiles (BM = 128 or 64), 32-deep steps, 4 waves of
+// BM/2 x 64 (BM/32 x 4 16x16x32 MFMA tiles each); the tiles of the next two
+// steps are in flight in registers while the current one is multiplied.
 // Requirements (checked by the host): the contiguous extent of every operand
 // is a whole number of tiles (M a multiple of BM and N of 128 where they are
-// contiguous, K and kseg multiples of 32 where k is); the strided extent may
-// be ragged (rows past it read as zero).
+// contiguous, K a multiple of 32 where k is); the strided extent may be
+// ragged (rows past it read as zero).
 // ---------------------------------------------------------------------------
 struct GemmArgs {
   const void* A;
@@ -81,11 +76,8 @@ struct GemmArgs {
   int M, N, K;
   long long sAm, sAk, sBk, sBn, sCm;
   long long bA, bB, bC;
-  float beta;
   int nsplit, kper;
   long long bCs;
-  const void* B2;
-  int kseg;
 };
 constexpr int GT = 128, GK = 32;
 constexpr int PLANE_ROW = GK * 2 + 16;          // [row][k] plane: 64 bytes of k + 16 bytes of padding
@@ -94,8 +86,8 @@ constexpr int PLANE_BYTES = GT * PLANE_ROW;     // 10240 >= GK * PLANE_TR_ROW = 
 
 template <typename T, int ROWS = GT>
 struct GemmOperand {
-  static constexpr bool F32 = sizeof(T) == 4;
-  static constexpr int PER = F32 ? 4 : 8;                     // elements per 16-byte piece
+  static_assert(sizeof(T) == 2, "bf16 operands");
+  static constexpr int PER = 8;                               // elements per 16-byte piece
   static constexpr int LOADS = ROWS * GK / PER / 256;         // 16-byte loads per thread per tile
   static constexpr int KPC = GK / PER;                        // [row][k]: pieces per row
   static constexpr int RPC = ROWS / PER;                      // [k][row]: pieces per k
@@ -103,20 +95,14 @@ struct GemmOperand {
 };
 
 // One operand tile (ROWS rows from r0, k in [k0, kend)) into registers: 16-byte pieces, zeros past the
-// ragged extent; with kseg, steps at k0 >= kseg read P2 at k0 - kseg.  Buffer loads over the valid region
+// ragged extent.  Buffer loads over the valid region
 // (rows below rend, or k below kend for a transposed operand; byte offsets below 2^31): a piece past it
 // reads 0 without a branch, so the compiler can count the loads in flight.
 template <typename T, bool TR, int ROWS>
 __device__ __forceinline__ void gemm_load(u32x4 (&v)[(GemmOperand<T, ROWS>::LOADS)], const T* P, long long s_row,
-                                          long long s_k, int r0, int rend, int k0, int kend,
-                                          const T* P2 = nullptr, int kseg = 0x7fffffff) {
+                                          long long s_k, int r0, int rend, int k0, int kend) {
   using O = GemmOperand<T, ROWS>;
   const int tid = threadIdx.x;
-  if (k0 >= kseg) {
-    P = P2;
-    k0 -= kseg;
-    kend -= kseg;
-  }
   const long long nvalid = TR ? (long long)kend * s_k : (long long)rend * s_row;
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(P, nvalid * (long long)sizeof(T));
 #pragma unroll
@@ -134,25 +120,16 @@ __device__ __forceinline__ void gemm_load(u32x4 (&v)[(GemmOperand<T, ROWS>::LOAD
   }
 }
 
-// The registers of gemm_load into the hi (and lo) planes.
+// The registers of gemm_load into the LDS plane.
 template <typename T, bool TR, int ROWS>
-__device__ __forceinline__ void gemm_store(const u32x4 (&v)[(GemmOperand<T, ROWS>::LOADS)], unsigned char* hi,
-                                           unsigned char* lo) {
+__device__ __forceinline__ void gemm_store(const u32x4 (&v)[(GemmOperand<T, ROWS>::LOADS)], unsigned char* plane) {
   using O = GemmOperand<T, ROWS>;
   const int tid = threadIdx.x;
 #pragma unroll
   for (int q = 0; q < O::LOADS; ++q) {
     const int idx = tid + 256 * q;
-    const int off = !TR ? (idx / O::KPC) * PLANE_ROW + (idx % O::KPC) * 16 / (O::F32 ? 2 : 1)
-                        : (idx / O::RPC) * O::TR_ROW + (idx % O::RPC) * 16 / (O::F32 ? 2 : 1);
-    if (O::F32) {
-      const floatx4 f = __builtin_bit_cast(floatx4, v[q]);
-      const uint2 s0 = split2(f[0], f[1]), s1 = split2(f[2], f[3]);
-      *(uint2*)(hi + off) = uint2{s0.x, s1.x};
-      *(uint2*)(lo + off) = uint2{s0.y, s1.y};
-    } else {
-      *(u32x4*)(hi + off) = v[q];
-    }
+    const int off = !TR ? (idx / O::KPC) * PLANE_ROW + (idx % O::KPC) * 16 : (idx / O::RPC) * O::TR_ROW + (idx % O::RPC) * 16;
+    *(u32x4*)(plane + off) = v[q];
   }
 }
 
@@ -171,19 +148,15 @@ template <typename TA, typename TB, bool ATR, bool BTR, int BM>
 __global__ __launch_bounds__(256, 2) void sw_gemm_kernel(GemmArgs g) {
   using OA = GemmOperand<TA, BM>;
   using OB = GemmOperand<TB, GT>;
-  constexpr bool AF = OA::F32, BF = OB::F32;
   constexpr int MI = BM / 32;             // row tiles per wave
-  __shared__ __attribute__((aligned(16))) unsigned char lds[4 * PLANE_BYTES];
-  unsigned char* ahi = lds;
-  unsigned char* alo = lds + PLANE_BYTES;
-  unsigned char* bhi = lds + 2 * PLANE_BYTES;
-  unsigned char* blo = lds + 3 * PLANE_BYTES;
+  __shared__ __attribute__((aligned(16))) unsigned char lds[2 * PLANE_BYTES];
+  unsigned char* ap = lds;
+  unsigned char* bp = lds + PLANE_BYTES;
   const int nsplit = g.nsplit;
   const long long bz = blockIdx.z / nsplit;
   const int split = blockIdx.z % nsplit;
   const TA* A = (const TA*)g.A + bz * g.bA;
   const TB* B = (const TB*)g.B + bz * g.bB;
-  const TB* B2 = g.B2 ? (const TB*)g.B2 + bz * g.bB : nullptr;
   float* C = g.C + bz * g.bC + split * g.bCs;
   const int m0 = blockIdx.y * BM, n0 = blockIdx.x * GT;
   const int kbeg = split * g.kper, kend = min(g.K, kbeg + g.kper);
@@ -201,32 +174,23 @@ __global__ __launch_bounds__(256, 2) void sw_gemm_kernel(GemmArgs g) {
   u32x4 va0[OA::LOADS], vb0[OB::LOADS], va1[OA::LOADS], vb1[OB::LOADS];
   auto load = [&](u32x4 (&va)[OA::LOADS], u32x4 (&vb)[OB::LOADS], int k) {
     gemm_load<TA, ATR, BM>(va, A, a_row, a_k, m0, g.M, k, kend);
-    gemm_load<TB, BTR, GT>(vb, B, b_row, b_k, n0, g.N, k, kend, B2, g.kseg);
+    gemm_load<TB, BTR, GT>(vb, B, b_row, b_k, n0, g.N, k, kend);
   };
   // one step: the set's tiles into LDS, the set reloaded with the step two ahead, the products
   auto step = [&](u32x4 (&va)[OA::LOADS], u32x4 (&vb)[OB::LOADS], int k0) {
-    gemm_store<TA, ATR, BM>(va, ahi, alo);
-    gemm_store<TB, BTR, GT>(vb, bhi, blo);
+    gemm_store<TA, ATR, BM>(va, ap);
+    gemm_store<TB, BTR, GT>(vb, bp);
     __syncthreads();
     load(va, vb, k0 + 2 * GK);   // unconditional (past the end it reads zeros or unused values), so that
                                  // the loads in flight are the same on every path
-    bf16x8 bh[4], bl[4];
+    bf16x8 bf[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      bh[j] = gemm_frag<BTR>(bhi, 64 * wn + 16 * j, OB::TR_ROW);
-      if (BF) bl[j] = gemm_frag<BTR>(blo, 64 * wn + 16 * j, OB::TR_ROW);
-    }
+    for (int j = 0; j < 4; ++j) bf[j] = gemm_frag<BTR>(bp, 64 * wn + 16 * j, OB::TR_ROW);
 #pragma unroll
     for (int i = 0; i < MI; ++i) {
-      const bf16x8 ah = gemm_frag<ATR>(ahi, (BM / 2) * wm + 16 * i, OA::TR_ROW);
-      bf16x8 al;
-      if (AF) al = gemm_frag<ATR>(alo, (BM / 2) * wm + 16 * i, OA::TR_ROW);
+      const bf16x8 af = gemm_frag<ATR>(ap, (BM / 2) * wm + 16 * i, OA::TR_ROW);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        acc[i][j] = mfma16(ah, bh[j], acc[i][j]);
-        if (BF) acc[i][j] = mfma16(ah, bl[j], acc[i][j]);
-        if (AF) acc[i][j] = mfma16(al, bh[j], acc[i][j]);
-      }
+      for (int j = 0; j < 4; ++j) acc[i][j] = mfma16(af, bf[j], acc[i][j]);
     }
     __syncthreads();
   };
@@ -252,7 +216,7 @@ __global__ __launch_bounds__(256, 2) void sw_gemm_kernel(GemmArgs g) {
       for (int j = 0; j < 4; ++j) {
         const int n = n0 + 64 * wn + 16 * j + li;
         float* p = C + (long long)m * g.sCm + n;
-        *p = g.beta != 0.f ? acc[i][j][r] + g.beta * *p : acc[i][j][r];
+        *p = acc[i][j][r];
       }
     }
 }
@@ -280,8 +244,6 @@ hipError_t gemm(GemmArgs g, int batch, hipStream_t stream, int nsplit = 1, long 
   // the contiguous extent of each operand must be whole tiles (or whole k steps)
   if ((atr ? (g.sAm != 1 || g.M % bm) : (g.K % GK)) || (btr ? (g.sBn != 1 || g.N % GT) : (g.K % GK)) || g.N % GT)
     return hipErrorInvalidValue;
-  if (g.B2 && (btr || g.kseg % GK || g.kseg <= 0)) return hipErrorInvalidValue;
-  if (!g.B2) g.kseg = 0x7fffffff;
   if (nsplit < 1) nsplit = 1;
   g.kper = (((g.K + nsplit - 1) / nsplit) + GK - 1) / GK * GK;
   g.nsplit = nsplit;
@@ -885,15 +847,13 @@ BwdSwLayout bwd_sw_layout(int64_t BH, int64_t T, int64_t chunk) {
 }
 
 GemmArgs gargs(const void* A, long long sAm, long long sAk, long long bA, const void* B, long long sBk, long long sBn,
-               long long bB, float* C, long long sCm, long long bC, int M, int N, int K, float beta = 0.f) {
+               long long bB, float* C, long long sCm, long long bC, int M, int N, int K) {
   GemmArgs g;
   g.A = A; g.B = B; g.C = C;
   g.M = M; g.N = N; g.K = K;
   g.sAm = sAm; g.sAk = sAk; g.sBk = sBk; g.sBn = sBn; g.sCm = sCm;
   g.bA = bA; g.bB = bB; g.bC = bC;
-  g.beta = beta;
   g.nsplit = 1; g.kper = K; g.bCs = 0;
-  g.B2 = nullptr; g.kseg = 0;
   return g;
 }
 
