@@ -78,9 +78,6 @@ __device__ __forceinline__ int sw_swz(int row) { return (int)((0x159DAE2673FBC84
 __device__ __forceinline__ int w13i(int d, int u) { return ((d >> 2) * 16 + u) * 4 + (d & 3); }
 __device__ __forceinline__ int w2i(int u, int d) { return (((d >> 4) * 4 + (u >> 2)) * 16 + (d & 15)) * 4 + (u & 3); }
 
-// logistic function with the hardware reciprocal (about 1 ulp): its value
-// only feeds bf16 operands or a bf16 hi + lo pair, so a correctly rounded
-// division buys nothing here
 // One matrix of a recurrence stage: 8 direct-to-LDS loads of 16 bytes per lane (non-temporal), load j into
 // LDS lds + 1024 j + 16 lane.  The instruction offset (1024 (j % 4)) is added to both the global and the LDS
 // address, so four loads share one M0 and off[j] is the global offset less it.  Written as one asm statement
@@ -105,6 +102,9 @@ __device__ __forceinline__ void stage_dma(__amdgpu_buffer_rsrc_t r, const unsign
       : "s"(r), "s"(base), "s"(base + 4096u), "v"(off[0]), "v"(off[1]), "v"(off[2]), "v"(off[3]), "v"(off[4]),
         "v"(off[5]), "v"(off[6]), "v"(off[7]));
 }
+// logistic function with the hardware reciprocal (about 1 ulp): its value
+// only feeds bf16 operands or a bf16 hi + lo pair, so a correctly rounded
+// division buys nothing here
 __device__ __forceinline__ float sigmoid_fast(float a) { return __builtin_amdgcn_rcpf(1.0f + __expf(-a)); }
 
 __device__ __forceinline__ void split_store8(bf16* hi, bf16* lo, const float* f) {
