@@ -160,3 +160,31 @@ def test_per_token_segmentation_invariance(d):
     for nh in (16, 1):
         assert err(outs[nh][0], outs[256][0], "bf16") <= 1e-4
         assert err(outs[nh][1], outs[256][1], "bf16") <= 1e-4
+
+
+@pytest.mark.parametrize("B,H,T,mode", [
+    (4, 16, 333, "per_token_linear"),              # 64 heads, ragged tail
+    (4, 16, 64, "per_token_linear_exclusive"),     # one whole tile
+    (4, 16, 1, "per_token_linear"),                # single token
+    (2, 40, 130, "per_token_linear_exclusive"),    # 80 heads, 3 segments of one tile
+    (3, 25, 200, "per_token_linear"),              # 75 heads, 2 segments
+])
+def test_per_token_many_heads(B, H, T, mode):
+    # 64 to 255 heads of d = 128 with bf16 outputs: one to three segments per head (head counts that
+    # are not powers of two in the last cases); the same heads in a batch of 8 are cut into one segment
+    # per 64-token tile
+    s = workloads.make_spec(mode, B, H, T, 128, chunk=64, dtype="bf16", eta="sigmoid")
+    x = workloads.generate(s, seed=21)
+    t = to_device(x, s)
+    O, W = run(t, s)
+    check(s, x, O, W, label=f"{B},{H},{T} {mode}")
+    if mode == "per_token_linear_exclusive":
+        _, Wi = run(t, dict(s, mode="per_token_linear"))
+        assert torch.equal(W, Wi)
+    # the first 8 heads alone reach the same final state to float32 rounding (their bf16
+    # outputs may differ by an ulp, which for the largest entries is about 2% of the RMS)
+    part = {k: v.reshape((B * H,) + tuple(v.shape[2:]))[:8].reshape((1, 8) + tuple(v.shape[2:])).contiguous()
+            for k, v in t.items()}
+    _, Ws = run(part, dict(s, B=1, H=8))
+    Wc = W.reshape((B * H,) + tuple(W.shape[2:]))[:8].cpu().numpy()
+    assert err(Ws[0].cpu().numpy(), Wc, "bf16") <= 1e-4
