@@ -1001,6 +1001,10 @@ __global__ __launch_bounds__(SW_RW * 64, 1) void swiglu_read_kernel(const bf16* 
 
   constexpr int NSLICE = DH / SW_US;
   load_slice(0, 0);
+  // the query loads and the first slice complete, by a wait the compiler sees (vmcnt(0)): otherwise its
+  // own waits for the query registers (it cannot see the copies) fall inside the loop, where they would
+  // also wait for the next slice's copy issued just before
+  __builtin_amdgcn_s_waitcnt(0x0F70);
   for (int s = 0; s < NSLICE; ++s) {
     const int buf = s & 1;
     // slice s has landed and every wave is done with slice s-1, whose buffer the next copy reuses
