@@ -806,11 +806,13 @@ struct Fp32Cfg {
 // reverse (chunk row r of chunk c is original token T - 1 - (cC + r)); EM
 // places the rates on the keys (0), on the outputs (1) or nowhere (2).
 // PAR (short sequences, few heads): one workgroup per (head, column tile,
-// chunk) instead of per (head, column tile): the workgroup of chunk c runs
-// the state updates of chunks 0 .. c-1 itself (loading only their keys,
-// values and rates) and then chunk c's outputs, so the chunks' score and
-// output phases run in parallel; only the last chunk's workgroup takes its
-// own state update and writes W_out.
+// chunk) instead of per (head, column tile): the workgroup of chunk c adds
+// the state updates of the tokens before the chunk itself (each thread its
+// own state entries, token by token in order as the chunk loop does, reading
+// keys, values and rates straight from memory with no barrier in between)
+// and then computes chunk c's outputs, so the chunks' score and output
+// phases run in parallel; only the last chunk's workgroup takes its own
+// state update and writes W_out.
 template <int DK, int C, bool EXCL, bool REV = false, int EM = 0, bool PAR = false>
 __global__ __launch_bounds__(256) void per_token_fp32_kernel(
     const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
@@ -837,16 +839,36 @@ __global__ __launch_bounds__(256) void per_token_fp32_kernel(
   const float* Vh = V + (size_t)bh * T * DV;
   const float* Eh = eta + (size_t)bh * T;
   float* Oh = O + (size_t)bh * T * DV;
-  for (int i = tid; i < DK * TV / 4; i += 256) {
-    const int a = i / (TV / 4), n4 = i % (TV / 4);
-    *(floatx4*)(s + a * TV + 4 * n4) = *(const floatx4*)(W0 + (size_t)bh * DK * DV + (size_t)a * DV + tv0 + 4 * n4);
-  }
   // thread roles: score block (rows SB*bi.., cols SB*bj..); output / state column group cg (4 columns)
   const int bi = tid / 16, bj = tid % 16;
   const int cg = tid % 8, r8 = tid / 8;
   // original token of position t of the walk
   auto tok = [&](int t) -> size_t { return REV ? (size_t)(T - 1 - t) : (size_t)t; };
-  for (int c = 0; c <= c_own; ++c) {
+  constexpr int RS = DK / 32;           // state rows r8 + 32m of each thread
+  static_assert(TV == 32, "8 column groups of 4 x 32 row groups cover the state tile");
+  if constexpr (PAR) {
+    // the state before chunk c_own: W0 plus every earlier token's update, in token order
+    floatx4 acc[RS];
+#pragma unroll
+    for (int m = 0; m < RS; ++m)
+      acc[m] = *(const floatx4*)(W0 + (size_t)bh * DK * DV + (size_t)(r8 + 32 * m) * DV + tv0 + 4 * cg);
+    const int tend = c_own * C;   // < T
+#pragma unroll 8
+    for (int t = 0; t < tend; ++t) {
+      const size_t o = tok(t);
+      const floatx4 ev = (EM == 0 ? Eh[o] : 1.f) * *(const floatx4*)(Vh + o * DV + tv0 + 4 * cg);
+#pragma unroll
+      for (int m = 0; m < RS; ++m) acc[m] += Kh[o * DK + r8 + 32 * m] * ev;
+    }
+#pragma unroll
+    for (int m = 0; m < RS; ++m) *(floatx4*)(s + (r8 + 32 * m) * TV + 4 * cg) = acc[m];
+  } else {
+    for (int i = tid; i < DK * TV / 4; i += 256) {
+      const int a = i / (TV / 4), n4 = i % (TV / 4);
+      *(floatx4*)(s + a * TV + 4 * n4) = *(const floatx4*)(W0 + (size_t)bh * DK * DV + (size_t)a * DV + tv0 + 4 * n4);
+    }
+  }
+  for (int c = PAR ? c_own : 0; c <= c_own; ++c) {
     const int t0 = c * C;
     const bool out = !PAR || c == c_own;                        // this chunk's outputs (workgroup-uniform)
     const bool upd = !PAR || c < c_own || c_own == nchunks - 1;  // its state update is needed here
@@ -921,7 +943,6 @@ __global__ __launch_bounds__(256) void per_token_fp32_kernel(
     }
     // state: rows r8 + 32m of s, columns 4cg..4cg+3, over the chunk's keys
     if (upd) {
-      constexpr int RS = DK / 32;
       floatx4 acc[RS];
 #pragma unroll
       for (int m = 0; m < RS; ++m) acc[m] = *(const floatx4*)(s + (r8 + 32 * m) * TV + 4 * cg);
