@@ -78,8 +78,10 @@ __device__ __forceinline__ int sw_swz(int row) { return (int)((0x159DAE2673FBC84
 __device__ __forceinline__ int w13i(int d, int u) { return ((d >> 2) * 16 + u) * 4 + (d & 3); }
 __device__ __forceinline__ int w2i(int u, int d) { return (((d >> 4) * 4 + (u >> 2)) * 16 + (d & 15)) * 4 + (u & 3); }
 
-// One matrix of a recurrence stage: 8 direct-to-LDS loads of 16 bytes per lane (non-temporal), load j into
-// LDS lds + 1024 j + 16 lane.  The instruction offset (1024 (j % 4)) is added to both the global and the LDS
+// One matrix of a recurrence stage: 8 direct-to-LDS loads of 16 bytes per lane, load j into LDS
+// lds + 1024 j + 16 lane.  The loads keep the ordinary cache policy: every slice workgroup of a head reads
+// the same K and V rows, so the lines should stay in L2 for the others (measured: ~1.5 % faster than
+// non-temporal loads).  The instruction offset (1024 (j % 4)) is added to both the global and the LDS
 // address, so four loads share one M0 and off[j] is the global offset less it.  Written as one asm statement
 // (M0 set twice instead of per load); the compiler does not see these loads, so the caller counts them in
 // its vmcnt waits, as with dma16.
@@ -88,15 +90,15 @@ __device__ __forceinline__ void stage_dma(__amdgpu_buffer_rsrc_t r, const unsign
   const unsigned base = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)lds);
   asm volatile(
       "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\t"
-      "buffer_load_dwordx4 %4, %1, 0 offen nt lds\n\t"
-      "buffer_load_dwordx4 %5, %1, 0 offen offset:1024 nt lds\n\t"
-      "buffer_load_dwordx4 %6, %1, 0 offen offset:2048 nt lds\n\t"
-      "buffer_load_dwordx4 %7, %1, 0 offen offset:3072 nt lds\n\t"
+      "buffer_load_dwordx4 %4, %1, 0 offen lds\n\t"
+      "buffer_load_dwordx4 %5, %1, 0 offen offset:1024 lds\n\t"
+      "buffer_load_dwordx4 %6, %1, 0 offen offset:2048 lds\n\t"
+      "buffer_load_dwordx4 %7, %1, 0 offen offset:3072 lds\n\t"
       "s_mov_b32 m0, %3\n\ts_nop 0\n\t"
-      "buffer_load_dwordx4 %8, %1, 0 offen nt lds\n\t"
-      "buffer_load_dwordx4 %9, %1, 0 offen offset:1024 nt lds\n\t"
-      "buffer_load_dwordx4 %10, %1, 0 offen offset:2048 nt lds\n\t"
-      "buffer_load_dwordx4 %11, %1, 0 offen offset:3072 nt lds\n\t"
+      "buffer_load_dwordx4 %8, %1, 0 offen lds\n\t"
+      "buffer_load_dwordx4 %9, %1, 0 offen offset:1024 lds\n\t"
+      "buffer_load_dwordx4 %10, %1, 0 offen offset:2048 lds\n\t"
+      "buffer_load_dwordx4 %11, %1, 0 offen offset:3072 lds\n\t"
       "s_mov_b32 m0, %0"
       : "=&s"(saved)
       : "s"(r), "s"(base), "s"(base + 4096u), "v"(off[0]), "v"(off[1]), "v"(off[2]), "v"(off[3]), "v"(off[4]),
