@@ -71,8 +71,9 @@ int check_problem(const ttt_la_desc* d, int64_t chunk, int32_t mode) {
   const int64_t dmax = d->d_k > d->d_v ? d->d_k : d->d_v;
   if (!mul_ok(d->B, d->H, &x) || !mul_ok(x, d->T, &x) || !mul_ok(x, dmax, &x) || !mul_ok(x, 4, &x))
     return TTT_LA_ERR_SHAPE;
+  int64_t y;
   if (method == TTT_LA_LARGE_CHUNK_SWIGLU &&
-      (!mul_ok(d->B * d->H, 3 * d->d_k, &x) || !mul_ok(x, d->d_h, &x) || !mul_ok(x, 4, &x)))
+      (!mul_ok(3, d->d_k, &y) || !mul_ok(d->B * d->H, y, &x) || !mul_ok(x, d->d_h, &x) || !mul_ok(x, 4, &x)))
     return TTT_LA_ERR_SHAPE;
   if (chunk < 1) return TTT_LA_ERR_CHUNK;
   return TTT_LA_OK;
@@ -171,7 +172,7 @@ static int forward_impl(const void* Q, const void* K, const void* V, const float
     if (overlap(rWo, ins[i])) return TTT_LA_ERR_ALIAS;
   if (overlap(rWo, rW0) && W_out != W0) return TTT_LA_ERR_ALIAS;
   if (overlap(rO, rWo) || overlap(rO, rWs) || overlap(rWo, rWs)) return TTT_LA_ERR_ALIAS;
-  // momentum buffers (large-chunk linear only): M0 is an input, M_out an output; M_out == M0 in place
+  // momentum buffers (large-chunk modes): M0 is an input, M_out an output; M_out == M0 in place
   const Range rM0 = range(M0, (size_t)state_elems(d, method) * 4);
   const Range rMo = range(M_out, (size_t)state_elems(d, method) * 4);
   for (const Range& in : ins)

@@ -86,6 +86,8 @@ def test_null_desc():
     (la.make_desc(1, 1, 8, 64, 64, 0, 7), 0, 4),       # bad dtype
     (la.make_desc(1, 1, 8, 96, 96), 0, 6),             # d not compiled
     (la.make_desc(1, 1, 8, 64, 128), 0, 6),            # d_k != d_v not compiled
+    (la.make_desc(1, 1, 0, 2**62, 2**62, 256), 2, 2),  # sizes that overflow 64 bits (no tokens)
+    (la.make_desc(1, 1, 0, 128, 128, 2**62), 2, 2),
 ])
 def test_invalid_shapes(desc, mode, code):
     assert call(desc=desc, mode=mode) == code
