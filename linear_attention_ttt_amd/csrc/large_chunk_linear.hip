@@ -55,7 +55,7 @@ inline int64_t slice_of(int64_t BH, int64_t nchunks, int64_t chunk) {
 // 1. partial dW = sum_{t in slice} k_t^T (eta_t v_t), one slice per workgroup
 // ---------------------------------------------------------------------------
 template <int D>
-__global__ __launch_bounds__(256, 4) void lact_delta_kernel(const bf16* __restrict__ K, const bf16* __restrict__ V,
+__global__ __launch_bounds__(256, D == 64 ? 4 : 2) void lact_delta_kernel(const bf16* __restrict__ K, const bf16* __restrict__ V,
                                                             const float* __restrict__ eta, float* __restrict__ part,
                                                             int T, int chunk, int nchunks, int nsplit, int slice) {
   constexpr int ROW = D * 2 + 32;              // padded LDS row (bytes)

@@ -1137,10 +1137,16 @@ __global__ __launch_bounds__(256) void pt_transpose2_kernel(const float* __restr
   float* dst = (which ? bt : at) + (size_t)bh * D * D;
   const int x = threadIdx.x & 63, y0 = threadIdx.x >> 6;
 #pragma unroll
-  for (int y = y0; y < 64; y += 4) tile[y][x] = src[(size_t)(64 * tr + y) * D + 64 * tc + x];
+  for (int k = 0; k < 16; ++k) {
+    const int y = y0 + 4 * k;
+    tile[y][x] = src[(size_t)(64 * tr + y) * D + 64 * tc + x];
+  }
   __syncthreads();
 #pragma unroll
-  for (int y = y0; y < 64; y += 4) dst[(size_t)(64 * tc + y) * D + 64 * tr + x] = tile[x][y];
+  for (int k = 0; k < 16; ++k) {
+    const int y = y0 + 4 * k;
+    dst[(size_t)(64 * tc + y) * D + 64 * tr + x] = tile[x][y];
+  }
 }
 
 // In place: u -> dV = eta u, and deta = <u, v> per token (u fp32, V bf16 or
