@@ -902,7 +902,9 @@ __global__ __launch_bounds__(256) void swiglu_ll_fill_kernel(const float* __rest
 struct ReadLds {
   unsigned char w13[2][4][SW_US * SW_D * 2];   // W1T hi, W1T lo, W3T hi, W3T lo: [32 units][128 d]
   unsigned char w2[2][2][SW_D * SW_US * 2];    // W2T hi, lo: [n][32 units]
+  unsigned char q[SW_TT * SW_D * 2];           // the queries of a tile: [token][d], pieces at c ^ sw_swz(token)
 };
+static_assert(sizeof(ReadLds) <= 160 * 1024, "read kernel LDS");
 constexpr int RW13_ROW = SW_D * 2;
 constexpr int RW2_ROW = SW_US * 2;
 __device__ __forceinline__ int w2_swz(int row) { return (row >> 2) & 3; }
@@ -912,6 +914,14 @@ __device__ __forceinline__ int w2_swz(int row) { return (row >> 2) & 3; }
 // ~6 % slower, the lone wave waits on its own LDS reads).
 constexpr int SW_RW = 8;                  // waves per read workgroup
 constexpr int SW_RT = SW_TT / SW_RW;      // tokens per wave (2 tiles of 16)
+constexpr int SW_RSTORES = SW_RT / 16 * 8;   // output stores per wave per tile
+// Persistent over tiles: the tiles (head, chunk, 256-token tile) in the order in which the tiles of a
+// chunk are adjacent are dealt to the XCDs in 8 contiguous shares, and workgroup r of an XCD takes tiles
+// r, r + step, ... of its share (step = workgroups per XCD), so the tiles of a chunk run at about the same
+// time on one XCD and its weights are fetched into one L2.  While a tile is computed, the next tile's
+// queries are copied into LDS and its first weight slice follows the current tile's last; the current
+// tile's output stores drain while the next one starts.  With a grid of one workgroup per tile this is
+// the plain one-tile-per-workgroup form.
 // OF32: float32 outputs (16 bytes per lane: 4 consecutive columns of one token).
 // errflag: raised by the recurrence when a cross-workgroup wait gave up; then every output of the call
 // and every head's final weights are filled with NaN instead.
@@ -919,57 +929,85 @@ template <bool OF32>
 __global__ __launch_bounds__(SW_RW * 64, 1) void swiglu_read_kernel(const bf16* __restrict__ Q,
                                                                     const bf16* __restrict__ states,
                                                                     void* __restrict__ O, int T, int chunk,
-                                                                    int nchunks, int tiles,
+                                                                    int nchunks, int tiles, int ntiles,
                                                                     const unsigned* __restrict__ errflag,
                                                                     float* __restrict__ Wout) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
   ReadLds& L = *reinterpret_cast<ReadLds*>(smem_raw);
   constexpr int D = SW_D, DH = SW_DH, NTH = SW_RW * 64, TT = SW_RT / 16;
-  // the token tiles of one chunk run on one XCD, so its weights are fetched into one L2
-  const int lb = (gridDim.x & 7) == 0 ? xcd_logical_block(blockIdx.x, gridDim.x) : blockIdx.x;
-  const int tile = lb % tiles;
-  const int c = (lb / tiles) % nchunks;
-  const int bh = lb / (tiles * nchunks);
+  constexpr int OES = OF32 ? 4 : 2;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g = l >> 4, li = l & 15;
-  const int cend = min((c + 1) * chunk, T);
-  const int t0 = c * chunk + tile * SW_TT;
   const size_t P = (size_t)D * DH;
+  // this workgroup's k-th tile (logical index, tiles of a chunk adjacent), or -1 past its last
+  const bool by_xcd = (ntiles & 7) == 0 && (gridDim.x & 7) == 0;
+  const int per = by_xcd ? ntiles >> 3 : ntiles;
+  const int xcd = by_xcd ? (int)(blockIdx.x & 7) : 0;
+  const int r0 = by_xcd ? (int)(blockIdx.x >> 3) : (int)blockIdx.x;
+  const int step = by_xcd ? (int)(gridDim.x >> 3) : (int)gridDim.x;
+  auto tile_at = [&](int k) -> int {
+    const int i = r0 + step * k;
+    return i < per ? xcd * per + i : -1;
+  };
+  struct Tile {
+    int bh, c, tile, t0, cend;
+  };
+  auto decode = [&](int lb) {
+    Tile t;
+    t.tile = lb % tiles;
+    t.c = (lb / tiles) % nchunks;
+    t.bh = lb / (tiles * nchunks);
+    t.cend = min((t.c + 1) * chunk, T);
+    t.t0 = t.c * chunk + t.tile * SW_TT;
+    return t;
+  };
   if (__hip_atomic_load(errflag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u) {
     // the recurrence could not complete: no output of this call is valid
-    constexpr int OES = OF32 ? 4 : 2;
     const float nan = __builtin_nanf("");
-    if (t0 < cend) {
-      unsigned char* Ot = (unsigned char*)O + ((size_t)bh * T + t0) * D * OES;
-      const int n = (cend - t0 < SW_TT ? cend - t0 : SW_TT) * D;
-      for (int i = threadIdx.x; i < n; i += NTH) {
-        if constexpr (OF32)
-          ((float*)Ot)[i] = nan;
-        else
-          ((bf16*)Ot)[i] = (bf16)nan;
+    for (int k = 0; tile_at(k) >= 0; ++k) {
+      const Tile t = decode(tile_at(k));
+      if (t.t0 < t.cend) {
+        unsigned char* Ot = (unsigned char*)O + ((size_t)t.bh * T + t.t0) * D * OES;
+        const int n = (t.cend - t.t0 < SW_TT ? t.cend - t.t0 : SW_TT) * D;
+        for (int i = threadIdx.x; i < n; i += NTH) {
+          if constexpr (OF32)
+            ((float*)Ot)[i] = nan;
+          else
+            ((bf16*)Ot)[i] = (bf16)nan;
+        }
       }
+      if (t.c == 0 && t.tile == 0)
+        for (int i = threadIdx.x; i < 3 * (int)P; i += NTH) Wout[(size_t)t.bh * 3 * P + i] = nan;
     }
-    if (c == 0 && tile == 0)
-      for (int i = threadIdx.x; i < 3 * (int)P; i += NTH) Wout[(size_t)bh * 3 * P + i] = nan;
     return;
   }
-  if (t0 >= cend) return;   // uniform over the workgroup, before any barrier
-  const bf16* st = states + ((size_t)bh * nchunks + c) * SW_STATE;
+  // the next tile at or after k with tokens (tiles past a short last chunk's end have none), or -1
+  auto next_tile = [&](int k) -> int {
+    for (;; ++k) {
+      const int lb = tile_at(k);
+      if (lb < 0) return -1;
+      const Tile t = decode(lb);
+      if (t.t0 < t.cend) return k;
+    }
+  };
 
-  // this wave's queries as B operands (col = token, k = 8 consecutive d)
-  const bf16* Qh = Q + (size_t)bh * T * D;
-  bf16x8 qop[TT][4];
+  // a tile's queries -> L.q by direct-to-LDS copies: each wave copies 8 KB (rows 32 w .. 32 w + 31);
+  // rows past the chunk's end read 0
+  constexpr int JQ = SW_TT * D * 2 / 1024 / SW_RW;
+  unsigned offq[JQ];
 #pragma unroll
-  for (int tt = 0; tt < TT; ++tt) {
-    const int t = min(t0 + SW_RT * w + 16 * tt + li, cend - 1);
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-      qop[tt][ks] = __builtin_bit_cast(bf16x8, __builtin_nontemporal_load((const u32x4*)(Qh + (size_t)t * D + 32 * ks + 8 * g)));
+  for (int j = 0; j < JQ; ++j) {
+    const int b = (w * JQ + j) * 1024 + 16 * l, row = b >> 8, q = (b & 255) >> 4;
+    offq[j] = (unsigned)(row * D * 2 + ((q ^ sw_swz(row)) << 4));
   }
-
-  // weight slice s -> LDS buffer buf by direct-to-LDS copies: each wave copies 4 KB of the W1T/W3T
-  // planes (4 x 1 KB) and 2 KB of the W2T planes (2 x 1 KB)
+  auto load_q = [&](const Tile& t) {
+    const __amdgpu_buffer_rsrc_t rq =
+        make_rsrc(Q + ((size_t)t.bh * T + t.t0) * D, ((long long)t.cend - t.t0) * D * 2);
+#pragma unroll
+    for (int j = 0; j < JQ; ++j) dma16<true>(rq, offq[j], L.q + (w * JQ + j) * 1024);
+  };
+  // weight slice sl of a tile's chunk -> LDS buffer buf: each wave copies 4 KB of the W1T/W3T planes
+  // (4 x 1 KB) and 2 KB of the W2T planes (2 x 1 KB)
   constexpr int J13 = 4 * SW_US * SW_D * 2 / 1024 / SW_RW, J2 = 2 * SW_D * SW_US * 2 / 1024 / SW_RW;
-  const __amdgpu_buffer_rsrc_t rs = make_rsrc(st, (long long)SW_STATE * 2);
   unsigned off13[J13], off2[J2];
 #pragma unroll
   for (int j = 0; j < J13; ++j) {
@@ -981,7 +1019,9 @@ __global__ __launch_bounds__(SW_RW * 64, 1) void swiglu_read_kernel(const bf16* 
     const int k2 = w * J2 + j, plane = k2 >> 3, b = (k2 & 7) * 1024 + 16 * l, n = b >> 6, q = (b & 63) >> 4;
     off2[j] = (unsigned)(((size_t)(4 + plane) * P + (size_t)n * DH + ((q ^ w2_swz(n)) << 3)) * 2);
   }
-  auto load_slice = [&](int sl, int buf) {
+  auto load_slice = [&](const Tile& t, int sl, int buf) {
+    const __amdgpu_buffer_rsrc_t rs =
+        make_rsrc(states + ((size_t)t.bh * nchunks + t.c) * SW_STATE, (long long)SW_STATE * 2);
     const unsigned u13 = (unsigned)(SW_US * sl * D * 2), u2 = (unsigned)(SW_US * sl * 2);
 #pragma unroll
     for (int j = 0; j < J13; ++j) {
@@ -995,92 +1035,121 @@ __global__ __launch_bounds__(SW_RW * 64, 1) void swiglu_read_kernel(const bf16* 
     }
   };
 
-  floatx4 oacc[8][TT];
-#pragma unroll
-  for (int nt = 0; nt < 8; ++nt)
-#pragma unroll
-    for (int tt = 0; tt < TT; ++tt) oacc[nt][tt] = floatx4{0.f, 0.f, 0.f, 0.f};
-
   constexpr int NSLICE = DH / SW_US;
-  load_slice(0, 0);
-  // the query loads and the first slice complete, by a wait the compiler sees (vmcnt(0)): otherwise its
-  // own waits for the query registers (it cannot see the copies) fall inside the loop, where they would
-  // also wait for the next slice's copy issued just before
-  __builtin_amdgcn_s_waitcnt(0x0F70);
-  for (int s = 0; s < NSLICE; ++s) {
-    const int buf = s & 1;
-    // slice s has landed and every wave is done with slice s-1, whose buffer the next copy reuses
-    // (the query loads issued before the first copy are complete too)
-    wait_vm_barrier<0>();
-    if (s + 1 < NSLICE) load_slice(s + 1, buf ^ 1);
-    // H^T = silu(A^T) * B^T as bf16 hi + lo, k-slot order of the 32 units: 4g..4g+3 of unit tile 0,
-    // then of unit tile 1
-    bf16x8 hh[TT], hl[TT];
+  static_assert(NSLICE % 2 == 0, "a tile's first slice goes into buffer 0");
+  int k = next_tile(0);
+  if (k < 0) return;   // uniform over the workgroup, before any barrier
+  Tile cur = decode(tile_at(k));
+  load_q(cur);
+  load_slice(cur, 0, 0);
+  for (bool first = true;; first = false) {
+    // this tile's queries and first slice have landed, every wave is done with the previous tile (only
+    // its output stores, issued after the first slice's copy, may be outstanding)
+    if (first)
+      wait_vm_barrier<0>();
+    else
+      wait_vm_barrier<SW_RSTORES>();
+    // this wave's queries as B operands (col = token, k = 8 consecutive d)
+    bf16x8 qop[TT][4];
 #pragma unroll
-    for (int ut = 0; ut < 2; ++ut) {
-      // A^T, B^T [unit][token] for one 16-unit tile x the wave's 4 token tiles
-      floatx4 at[TT], bt[TT];
+    for (int tt = 0; tt < TT; ++tt) {
+      const int row = SW_RT * w + 16 * tt + li;
 #pragma unroll
-      for (int tt = 0; tt < TT; ++tt) at[tt] = bt[tt] = floatx4{0.f, 0.f, 0.f, 0.f};
+      for (int ks = 0; ks < 4; ++ks)
+        qop[tt][ks] = *(const bf16x8*)(L.q + row * D * 2 + (((4 * ks + g) ^ sw_swz(row)) << 4));
+    }
+    const int kn = next_tile(k + 1);
+    const Tile nxt = decode(kn >= 0 ? tile_at(kn) : 0);
+    barrier();   // every wave holds its queries: the buffer takes the next tile's
+    if (kn >= 0) load_q(nxt);
+
+    floatx4 oacc[8][TT];
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const int off = (16 * ut + li) * RW13_ROW + (((4 * ks + g) ^ sw_swz(16 * ut + li)) << 4);
-        const bf16x8 w1h = *(const bf16x8*)(L.w13[buf][0] + off);
-        const bf16x8 w1l = *(const bf16x8*)(L.w13[buf][1] + off);
-        const bf16x8 w3h = *(const bf16x8*)(L.w13[buf][2] + off);
-        const bf16x8 w3l = *(const bf16x8*)(L.w13[buf][3] + off);
+    for (int nt = 0; nt < 8; ++nt)
+#pragma unroll
+      for (int tt = 0; tt < TT; ++tt) oacc[nt][tt] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+    for (int s = 0; s < NSLICE; ++s) {
+      const int buf = s & 1;
+      // slice s has landed and every wave is done with slice s - 1, whose buffer the next copy reuses
+      // (at s = 1 this also completes the next tile's query copy and the previous tile's stores)
+      if (s > 0) wait_vm_barrier<0>();
+      if (s + 1 < NSLICE)
+        load_slice(cur, s + 1, buf ^ 1);
+      else if (kn >= 0)
+        load_slice(nxt, 0, buf ^ 1);
+      // H^T = silu(A^T) * B^T as bf16 hi + lo, k-slot order of the 32 units: 4g..4g+3 of unit tile 0,
+      // then of unit tile 1
+      bf16x8 hh[TT], hl[TT];
+#pragma unroll
+      for (int ut = 0; ut < 2; ++ut) {
+        // A^T, B^T [unit][token] for one 16-unit tile x the wave's token tiles
+        floatx4 at[TT], bt[TT];
+#pragma unroll
+        for (int tt = 0; tt < TT; ++tt) at[tt] = bt[tt] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          const int off = (16 * ut + li) * RW13_ROW + (((4 * ks + g) ^ sw_swz(16 * ut + li)) << 4);
+          const bf16x8 w1h = *(const bf16x8*)(L.w13[buf][0] + off);
+          const bf16x8 w1l = *(const bf16x8*)(L.w13[buf][1] + off);
+          const bf16x8 w3h = *(const bf16x8*)(L.w13[buf][2] + off);
+          const bf16x8 w3l = *(const bf16x8*)(L.w13[buf][3] + off);
+#pragma unroll
+          for (int tt = 0; tt < TT; ++tt) {
+            at[tt] = mfma16(w1h, qop[tt][ks], at[tt]);
+            at[tt] = mfma16(w1l, qop[tt][ks], at[tt]);
+            bt[tt] = mfma16(w3h, qop[tt][ks], bt[tt]);
+            bt[tt] = mfma16(w3l, qop[tt][ks], bt[tt]);
+          }
+        }
+#pragma unroll
+        for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float a = at[tt][r];
+            const float h = a * sigmoid_fast(a) * bt[tt][r];
+            const bf16 hb = (bf16)h;
+            hh[tt][4 * ut + r] = hb;
+            hl[tt][4 * ut + r] = (bf16)(h - (float)hb);
+          }
+      }
+      // O^T[n][t] += W2^T[n][units] H^T[units][t]
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt) {
+        const unsigned char* rowh = L.w2[buf][0] + (16 * nt + li) * RW2_ROW;
+        const unsigned char* rowl = L.w2[buf][1] + (16 * nt + li) * RW2_ROW;
+        // units 4g..4g+3 and 16+4g..16+4g+3: halves of the 16-byte pieces g/2 and 2+g/2
+        const int p0 = (((g >> 1) ^ w2_swz(16 * nt + li)) << 4) + (g & 1) * 8;
+        const int p1 = (((2 + (g >> 1)) ^ w2_swz(16 * nt + li)) << 4) + (g & 1) * 8;
+        const bf16x8 w2h = join(*(const bf16x4*)(rowh + p0), *(const bf16x4*)(rowh + p1));
+        const bf16x8 w2l = join(*(const bf16x4*)(rowl + p0), *(const bf16x4*)(rowl + p1));
 #pragma unroll
         for (int tt = 0; tt < TT; ++tt) {
-          at[tt] = mfma16(w1h, qop[tt][ks], at[tt]);
-          at[tt] = mfma16(w1l, qop[tt][ks], at[tt]);
-          bt[tt] = mfma16(w3h, qop[tt][ks], bt[tt]);
-          bt[tt] = mfma16(w3l, qop[tt][ks], bt[tt]);
+          oacc[nt][tt] = mfma16(w2h, hh[tt], oacc[nt][tt]);
+          oacc[nt][tt] = mfma16(w2h, hl[tt], oacc[nt][tt]);
+          oacc[nt][tt] = mfma16(w2l, hh[tt], oacc[nt][tt]);
         }
       }
+    }
+    unsigned char* Oh = (unsigned char*)O + (size_t)cur.bh * T * D * OES;
+    const __amdgpu_buffer_rsrc_t ro =
+        make_rsrc(Oh + (size_t)cur.t0 * D * OES, ((long long)cur.cend - cur.t0) * D * OES);
 #pragma unroll
-      for (int tt = 0; tt < TT; ++tt)
+    for (int tt = 0; tt < TT; ++tt)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float a = at[tt][r];
-          const float h = a * sigmoid_fast(a) * bt[tt][r];
-          const bf16 hb = (bf16)h;
-          hh[tt][4 * ut + r] = hb;
-          hl[tt][4 * ut + r] = (bf16)(h - (float)hb);
+      for (int nt = 0; nt < 8; ++nt) {
+        const unsigned off = (unsigned)(((SW_RT * w + 16 * tt + li) * D + 16 * nt + 4 * g) * OES);
+        if constexpr (OF32) {
+          buf_store16(ro, off, __builtin_bit_cast(u32x4, oacc[nt][tt]));
+        } else {
+          const bf16x4 o = to_bf16x4(oacc[nt][tt][0], oacc[nt][tt][1], oacc[nt][tt][2], oacc[nt][tt][3]);
+          __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(uint2v, o), ro, off, 0, 0);
         }
-    }
-    // O^T[n][t] += W2^T[n][units] H^T[units][t]
-#pragma unroll
-    for (int nt = 0; nt < 8; ++nt) {
-      const unsigned char* rowh = L.w2[buf][0] + (16 * nt + li) * RW2_ROW;
-      const unsigned char* rowl = L.w2[buf][1] + (16 * nt + li) * RW2_ROW;
-      // units 4g..4g+3 and 16+4g..16+4g+3: halves of the 16-byte pieces g/2 and 2+g/2
-      const int p0 = (((g >> 1) ^ w2_swz(16 * nt + li)) << 4) + (g & 1) * 8;
-      const int p1 = (((2 + (g >> 1)) ^ w2_swz(16 * nt + li)) << 4) + (g & 1) * 8;
-      const bf16x8 w2h = join(*(const bf16x4*)(rowh + p0), *(const bf16x4*)(rowh + p1));
-      const bf16x8 w2l = join(*(const bf16x4*)(rowl + p0), *(const bf16x4*)(rowl + p1));
-#pragma unroll
-      for (int tt = 0; tt < TT; ++tt) {
-        oacc[nt][tt] = mfma16(w2h, hh[tt], oacc[nt][tt]);
-        oacc[nt][tt] = mfma16(w2h, hl[tt], oacc[nt][tt]);
-        oacc[nt][tt] = mfma16(w2l, hh[tt], oacc[nt][tt]);
       }
-    }
+    if (kn < 0) break;
+    k = kn;
+    cur = nxt;
   }
-  constexpr int OES = OF32 ? 4 : 2;
-  unsigned char* Oh = (unsigned char*)O + (size_t)bh * T * D * OES;
-  const __amdgpu_buffer_rsrc_t ro = make_rsrc(Oh + (size_t)t0 * D * OES, ((long long)cend - t0) * D * OES);
-#pragma unroll
-  for (int tt = 0; tt < TT; ++tt)
-#pragma unroll
-    for (int nt = 0; nt < 8; ++nt) {
-      const unsigned off = (unsigned)(((SW_RT * w + 16 * tt + li) * D + 16 * nt + 4 * g) * OES);
-      if constexpr (OF32) {
-        buf_store16(ro, off, __builtin_bit_cast(u32x4, oacc[nt][tt]));
-      } else {
-        const bf16x4 o = to_bf16x4(oacc[nt][tt][0], oacc[nt][tt][1], oacc[nt][tt][2], oacc[nt][tt][3]);
-        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(uint2v, o), ro, off, 0, 0);
-      }
-    }
 }
 
 struct SwLayout {
@@ -1173,9 +1242,17 @@ static hipError_t launch_read(const LargeChunkArgs& a, const bf16* states, int n
   auto kread = a.o_f32 ? swiglu_read_kernel<true> : swiglu_read_kernel<false>;
   hipError_t e = hipFuncSetAttribute((const void*)kread, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_o);
   if (e != hipSuccess) return e;
+  int dev = 0, ncu = 0;
+  if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
+  if ((e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
   const int chunk = (int)a.chunk, tiles = (chunk + SW_TT - 1) / SW_TT;
-  hipLaunchKernelGGL(kread, dim3((unsigned)(a.B * a.H) * nchunks * tiles), dim3(SW_RW * 64), lds_o, stream,
-                     (const bf16*)a.Q, states, a.O, (int)a.T, chunk, nchunks, tiles, err, a.W_out);
+  const long long ntiles = (long long)(a.B * a.H) * nchunks * tiles;
+  if (ntiles > INT32_MAX) return hipErrorInvalidValue;
+  // one workgroup per CU (a multiple of 8, so the tiles of a chunk stay on one XCD) walking the tiles, or
+  // one per tile when there are fewer tiles or they do not split evenly over the XCDs
+  const long long grid = ntiles > ncu && ntiles % 8 == 0 && ncu >= 8 ? ncu / 8 * 8 : ntiles;
+  hipLaunchKernelGGL(kread, dim3((unsigned)grid), dim3(SW_RW * 64), lds_o, stream, (const bf16*)a.Q, states, a.O,
+                     (int)a.T, chunk, nchunks, tiles, (int)ntiles, err, a.W_out);
   return hipGetLastError();
 }
 
