@@ -144,21 +144,21 @@ __device__ __forceinline__ bf16x8 gemm_frag(const unsigned char* plane, int rb, 
   return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 }
 
+// One output tile (column tile bx, row tile by, batch entry and contraction split bz) of a product.
 template <typename TA, typename TB, bool ATR, bool BTR, int BM>
-__global__ __launch_bounds__(256, 2) void sw_gemm_kernel(GemmArgs g) {
+__device__ __forceinline__ void gemm_tile(const GemmArgs& g, int bx, int by, int bzs, unsigned char* lds) {
   using OA = GemmOperand<TA, BM>;
   using OB = GemmOperand<TB, GT>;
   constexpr int MI = BM / 32;             // row tiles per wave
-  __shared__ __attribute__((aligned(16))) unsigned char lds[2 * PLANE_BYTES];
   unsigned char* ap = lds;
   unsigned char* bp = lds + PLANE_BYTES;
   const int nsplit = g.nsplit;
-  const long long bz = blockIdx.z / nsplit;
-  const int split = blockIdx.z % nsplit;
+  const long long bz = bzs / nsplit;
+  const int split = bzs % nsplit;
   const TA* A = (const TA*)g.A + bz * g.bA;
   const TB* B = (const TB*)g.B + bz * g.bB;
   float* C = g.C + bz * g.bC + split * g.bCs;
-  const int m0 = blockIdx.y * BM, n0 = blockIdx.x * GT;
+  const int m0 = by * BM, n0 = bx * GT;
   const int kbeg = split * g.kper, kend = min(g.K, kbeg + g.kper);
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, gq = l >> 4, li = l & 15;
   const int wm = w >> 1, wn = w & 1;
@@ -221,6 +221,26 @@ __global__ __launch_bounds__(256, 2) void sw_gemm_kernel(GemmArgs g) {
     }
 }
 
+template <typename TA, typename TB, bool ATR, bool BTR, int BM>
+__global__ __launch_bounds__(256, 2) void sw_gemm_kernel(GemmArgs g) {
+  __shared__ __attribute__((aligned(16))) unsigned char lds[2 * PLANE_BYTES];
+  gemm_tile<TA, TB, ATR, BTR, BM>(g, blockIdx.x, blockIdx.y, blockIdx.z, lds);
+}
+
+// Two independent products of the same orientation and tile height in one launch: the first nb0
+// workgroups compute g0 (grid gx0 x gy0 x batch splits), the rest g1, so that neither product's tail
+// leaves compute units idle and the pair costs one launch.
+template <typename TA, typename TB, bool ATR, bool BTR, int BM>
+__global__ __launch_bounds__(256, 2) void sw_gemm2_kernel(GemmArgs g0, GemmArgs g1, int nb0, int gx0, int gy0, int gx1,
+                                                          int gy1) {
+  __shared__ __attribute__((aligned(16))) unsigned char lds[2 * PLANE_BYTES];
+  const int b = blockIdx.x;
+  if (b < nb0)   // uniform over the workgroup
+    gemm_tile<TA, TB, ATR, BTR, BM>(g0, b % gx0, (b / gx0) % gy0, b / (gx0 * gy0), lds);
+  else
+    gemm_tile<TA, TB, ATR, BTR, BM>(g1, (b - nb0) % gx1, ((b - nb0) / gx1) % gy1, (b - nb0) / (gx1 * gy1), lds);
+}
+
 template <typename TA, typename TB, int BM>
 void gemm_launch(const GemmArgs& g, dim3 grid, bool atr, bool btr, hipStream_t stream) {
   if (atr && btr)
@@ -236,23 +256,63 @@ void gemm_launch(const GemmArgs& g, dim3 grid, bool atr, bool btr, hipStream_t s
 // Launch with the operand orientations taken from the strides; nsplit > 1 splits the contraction into
 // pieces of kper (a multiple of GK) whose partial products go to C + s bCs.  Products with few column tiles
 // use 64-row tiles, so that the grid still has several workgroups per CU.
-template <typename TA, typename TB>
-hipError_t gemm(GemmArgs g, int batch, hipStream_t stream, int nsplit = 1, long long bCs = 0) {
-  if (g.M <= 0 || g.N <= 0) return hipSuccess;
-  const bool atr = g.sAk != 1, btr = g.sBk != 1;
-  const int bm = (!atr && g.N <= GT) ? 64 : GT;
+// Orientation, tile height and grid of a product (nsplit and bCs folded into g); false if its shape does not
+// fit the kernel.
+struct GemmPlan {
+  bool atr, btr;
+  int bm;
+  dim3 grid;
+};
+static bool gemm_plan(GemmArgs& g, int batch, int nsplit, long long bCs, GemmPlan& pl) {
+  pl.atr = g.sAk != 1;
+  pl.btr = g.sBk != 1;
+  pl.bm = (!pl.atr && g.N <= GT) ? 64 : GT;
   // the contiguous extent of each operand must be whole tiles (or whole k steps)
-  if ((atr ? (g.sAm != 1 || g.M % bm) : (g.K % GK)) || (btr ? (g.sBn != 1 || g.N % GT) : (g.K % GK)) || g.N % GT)
-    return hipErrorInvalidValue;
+  if ((pl.atr ? (g.sAm != 1 || g.M % pl.bm) : (g.K % GK)) || (pl.btr ? (g.sBn != 1 || g.N % GT) : (g.K % GK)) ||
+      g.N % GT)
+    return false;
   if (nsplit < 1) nsplit = 1;
   g.kper = (((g.K + nsplit - 1) / nsplit) + GK - 1) / GK * GK;
   g.nsplit = nsplit;
   g.bCs = bCs;
-  const dim3 grid((unsigned)(g.N / GT), (unsigned)((g.M + bm - 1) / bm), (unsigned)(batch * nsplit));
+  pl.grid = dim3((unsigned)(g.N / GT), (unsigned)((g.M + pl.bm - 1) / pl.bm), (unsigned)(batch * nsplit));
+  return true;
+}
+
+template <typename TA, typename TB>
+hipError_t gemm(GemmArgs g, int batch, hipStream_t stream, int nsplit = 1, long long bCs = 0) {
+  if (g.M <= 0 || g.N <= 0) return hipSuccess;
+  GemmPlan pl;
+  if (!gemm_plan(g, batch, nsplit, bCs, pl)) return hipErrorInvalidValue;
+  const bool atr = pl.atr, btr = pl.btr;
+  const int bm = pl.bm;
+  const dim3 grid = pl.grid;
   if (bm == 64)
     gemm_launch<TA, TB, 64>(g, grid, atr, btr, stream);
   else
     gemm_launch<TA, TB, GT>(g, grid, atr, btr, stream);
+  return hipGetLastError();
+}
+
+// Two independent products in one launch when they share orientation and tile height (else two launches).
+template <typename TA, typename TB>
+hipError_t gemm2(GemmArgs g0, int batch0, int nsplit0, long long bCs0, GemmArgs g1, int batch1, int nsplit1,
+                 long long bCs1, hipStream_t stream) {
+  if (g0.M <= 0 || g0.N <= 0) return gemm<TA, TB>(g1, batch1, stream, nsplit1, bCs1);
+  if (g1.M <= 0 || g1.N <= 0) return gemm<TA, TB>(g0, batch0, stream, nsplit0, bCs0);
+  GemmPlan p0, p1;
+  GemmArgs h0 = g0, h1 = g1;
+  if (!gemm_plan(h0, batch0, nsplit0, bCs0, p0) || !gemm_plan(h1, batch1, nsplit1, bCs1, p1))
+    return hipErrorInvalidValue;
+  if (p0.atr != p1.atr || p0.btr != p1.btr || p0.bm != p1.bm || !p0.atr || !p0.btr || p0.bm != GT) {
+    hipError_t e = gemm<TA, TB>(g0, batch0, stream, nsplit0, bCs0);
+    return e != hipSuccess ? e : gemm<TA, TB>(g1, batch1, stream, nsplit1, bCs1);
+  }
+  const long long nb0 = (long long)p0.grid.x * p0.grid.y * p0.grid.z;
+  const long long nb1 = (long long)p1.grid.x * p1.grid.y * p1.grid.z;
+  if (nb0 + nb1 > INT32_MAX) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((sw_gemm2_kernel<TA, TB, true, true, GT>), dim3((unsigned)(nb0 + nb1)), dim3(256), 0, stream, h0,
+                     h1, (int)nb0, (int)p0.grid.x, (int)p0.grid.y, (int)p1.grid.x, (int)p1.grid.y);
   return hipGetLastError();
 }
 
@@ -919,11 +979,10 @@ hipError_t launch_large_chunk_swiglu_backward(const BackwardArgs& a, int last_on
                        stream, ra);
     if ((e2 = hipGetLastError()) != hipSuccess) return e2;
     // (Q^T da | Q^T db), (silu(a) b)^T dO
-    if ((e2 = gemm<bf16, bf16>(gargs(Qc, 1, BD, T * BD, Eq, 2 * BDH, 1, cap * 2 * BDH, A13, 2 * BDH, BD * 2 * BDH,
-                                      BD, 2 * BDH, Cc), BH, stream, s13, p13)) != hipSuccess)
-      return e2;
-    return gemm<bf16, bf16>(gargs(Hq, 1, BDH, cap * BDH, dOc, BD, 1, T * BD, A2, BD, BP, BDH, BD, Cc), BH, stream, s2,
-                             p2);
+    return gemm2<bf16, bf16>(gargs(Qc, 1, BD, T * BD, Eq, 2 * BDH, 1, cap * 2 * BDH, A13, 2 * BDH, BD * 2 * BDH, BD,
+                                   2 * BDH, Cc), BH, s13, p13,
+                             gargs(Hq, 1, BDH, cap * BDH, dOc, BD, 1, T * BD, A2, BD, BP, BDH, BD, Cc), BH, s2, p2,
+                             stream);
   };
 
   for (int c = nch - 1; c >= 0; --c) {
@@ -951,11 +1010,10 @@ hipError_t launch_large_chunk_swiglu_backward(const BackwardArgs& a, int last_on
                        ST_LDS, stream, sa);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     // J13 = K^T (eta Pa | eta Pb), J2 = (eta hdot)^T V
-    if ((e = gemm<bf16, bf16>(gargs(Kc, 1, BD, T * BD, E1, 2 * BDH, 1, cap * 2 * BDH, J13, 2 * BDH, BD * 2 * BDH, BD,
-                                     2 * BDH, Cc), BH, stream, s13, p13)) != hipSuccess)
-      return e;
-    if ((e = gemm<bf16, bf16>(gargs(E3, 1, BDH, cap * BDH, Vc, BD, 1, T * BD, J2, BD, BP, BDH, BD, Cc), BH, stream, s2,
-                               p2)) != hipSuccess)
+    if ((e = gemm2<bf16, bf16>(gargs(Kc, 1, BD, T * BD, E1, 2 * BDH, 1, cap * 2 * BDH, J13, 2 * BDH, BD * 2 * BDH, BD,
+                                     2 * BDH, Cc), BH, s13, p13,
+                               gargs(E3, 1, BDH, cap * BDH, Vc, BD, 1, T * BD, J2, BD, BP, BDH, BD, Cc), BH, s2, p2,
+                               stream)) != hipSuccess)
       return e;
     if (read_first && (e = read_phase(Wp, wp_stride, c0, Cc)) != hipSuccess) return e;
     hipLaunchKernelGGL(sw_bwd_gupdate, dim3((unsigned)((3 * BP / 4 + 255) / 256), BH), dim3(256), 0, stream, G, Wcat, W2cat,
