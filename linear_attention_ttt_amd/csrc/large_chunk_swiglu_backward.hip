@@ -227,18 +227,27 @@ __global__ __launch_bounds__(256, 2) void sw_gemm_kernel(GemmArgs g) {
   gemm_tile<TA, TB, ATR, BTR, BM>(g, blockIdx.x, blockIdx.y, blockIdx.z, lds);
 }
 
-// Two independent products of the same orientation and tile height in one launch: the first nb0
-// workgroups compute g0 (grid gx0 x gy0 x batch splits), the rest g1, so that neither product's tail
-// leaves compute units idle and the pair costs one launch.
+// Up to four independent products of the same orientation and tile height in one launch: workgroups
+// [first[i], first[i + 1]) compute product i (grid gx[i] x gy[i] x batch splits), so that no product's
+// tail leaves compute units idle and the group costs one launch.
+constexpr int GEMM_GROUP = 4;
+struct GemmGroup {
+  GemmArgs g[GEMM_GROUP];
+  int first[GEMM_GROUP + 1];
+  int gx[GEMM_GROUP], gy[GEMM_GROUP];
+};
 template <typename TA, typename TB, bool ATR, bool BTR, int BM>
-__global__ __launch_bounds__(256, 2) void sw_gemm2_kernel(GemmArgs g0, GemmArgs g1, int nb0, int gx0, int gy0, int gx1,
-                                                          int gy1) {
+__global__ __launch_bounds__(256, 2) void sw_gemmg_kernel(GemmGroup G) {
   __shared__ __attribute__((aligned(16))) unsigned char lds[2 * PLANE_BYTES];
   const int b = blockIdx.x;
-  if (b < nb0)   // uniform over the workgroup
-    gemm_tile<TA, TB, ATR, BTR, BM>(g0, b % gx0, (b / gx0) % gy0, b / (gx0 * gy0), lds);
-  else
-    gemm_tile<TA, TB, ATR, BTR, BM>(g1, (b - nb0) % gx1, ((b - nb0) / gx1) % gy1, (b - nb0) / (gx1 * gy1), lds);
+#pragma unroll
+  for (int i = 0; i < GEMM_GROUP; ++i) {
+    if (b >= G.first[i] && b < G.first[i + 1]) {   // uniform over the workgroup
+      const int lb = b - G.first[i];
+      gemm_tile<TA, TB, ATR, BTR, BM>(G.g[i], lb % G.gx[i], (lb / G.gx[i]) % G.gy[i], lb / (G.gx[i] * G.gy[i]), lds);
+      return;
+    }
+  }
 }
 
 template <typename TA, typename TB, int BM>
@@ -294,25 +303,49 @@ hipError_t gemm(GemmArgs g, int batch, hipStream_t stream, int nsplit = 1, long 
   return hipGetLastError();
 }
 
-// Two independent products in one launch when they share orientation and tile height (else two launches).
+// Independent products (at most GEMM_GROUP) in one launch when they all have both operands transposed and
+// 128-row tiles, else one launch each.
+struct GemmJob {
+  GemmArgs g;
+  int batch, nsplit;
+  long long bCs;
+};
 template <typename TA, typename TB>
-hipError_t gemm2(GemmArgs g0, int batch0, int nsplit0, long long bCs0, GemmArgs g1, int batch1, int nsplit1,
-                 long long bCs1, hipStream_t stream) {
-  if (g0.M <= 0 || g0.N <= 0) return gemm<TA, TB>(g1, batch1, stream, nsplit1, bCs1);
-  if (g1.M <= 0 || g1.N <= 0) return gemm<TA, TB>(g0, batch0, stream, nsplit0, bCs0);
-  GemmPlan p0, p1;
-  GemmArgs h0 = g0, h1 = g1;
-  if (!gemm_plan(h0, batch0, nsplit0, bCs0, p0) || !gemm_plan(h1, batch1, nsplit1, bCs1, p1))
-    return hipErrorInvalidValue;
-  if (p0.atr != p1.atr || p0.btr != p1.btr || p0.bm != p1.bm || !p0.atr || !p0.btr || p0.bm != GT) {
-    hipError_t e = gemm<TA, TB>(g0, batch0, stream, nsplit0, bCs0);
-    return e != hipSuccess ? e : gemm<TA, TB>(g1, batch1, stream, nsplit1, bCs1);
+hipError_t gemm_group(const GemmJob* jobs, int n, hipStream_t stream) {
+  GemmGroup G;
+  int m = 0;
+  long long total = 0;
+  bool one_launch = n <= GEMM_GROUP;
+  for (int i = 0; i < n && one_launch; ++i) {
+    GemmArgs h = jobs[i].g;
+    if (h.M <= 0 || h.N <= 0) continue;
+    GemmPlan pl;
+    if (!gemm_plan(h, jobs[i].batch, jobs[i].nsplit, jobs[i].bCs, pl)) return hipErrorInvalidValue;
+    if (!pl.atr || !pl.btr || pl.bm != GT) {
+      one_launch = false;
+      break;
+    }
+    G.g[m] = h;
+    G.first[m] = (int)total;
+    G.gx[m] = (int)pl.grid.x;
+    G.gy[m] = (int)pl.grid.y;
+    total += (long long)pl.grid.x * pl.grid.y * pl.grid.z;
+    ++m;
   }
-  const long long nb0 = (long long)p0.grid.x * p0.grid.y * p0.grid.z;
-  const long long nb1 = (long long)p1.grid.x * p1.grid.y * p1.grid.z;
-  if (nb0 + nb1 > INT32_MAX) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((sw_gemm2_kernel<TA, TB, true, true, GT>), dim3((unsigned)(nb0 + nb1)), dim3(256), 0, stream, h0,
-                     h1, (int)nb0, (int)p0.grid.x, (int)p0.grid.y, (int)p1.grid.x, (int)p1.grid.y);
+  if (!one_launch || total > INT32_MAX) {
+    for (int i = 0; i < n; ++i) {
+      const hipError_t e = gemm<TA, TB>(jobs[i].g, jobs[i].batch, stream, jobs[i].nsplit, jobs[i].bCs);
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+  }
+  if (m == 0) return hipSuccess;
+  for (int i = m; i <= GEMM_GROUP; ++i) G.first[i] = (int)total;   // empty ranges
+  for (int i = m; i < GEMM_GROUP; ++i) {
+    G.g[i] = G.g[0];
+    G.gx[i] = G.gy[i] = 1;
+  }
+  hipLaunchKernelGGL((sw_gemmg_kernel<TA, TB, true, true, GT>), dim3((unsigned)total), dim3(256), 0, stream, G);
   return hipGetLastError();
 }
 
@@ -871,7 +904,7 @@ __global__ __launch_bounds__(256) void sw_bwd_copy(float* __restrict__ dst, cons
 }
 
 struct BwdSwLayout {
-  size_t fws, wfin, dump, dnorm, wcat, w2cat, e1, e2, e3, j13, j2, a13, a2, total;
+  size_t fws, wfin, dump, dnorm, wcat, w2cat, e1, eq, e2, e3, j13, j2, a13, a2, total;
 };
 size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
 // Split of the products that contract over a chunk's tokens: enough workgroups (about 256) for the chip, at
@@ -895,7 +928,8 @@ BwdSwLayout bwd_sw_layout(int64_t BH, int64_t T, int64_t chunk) {
   L.dnorm = o; o += al256((size_t)BH * nch * 640 * 4);
   L.wcat = o; o += al256((size_t)BH * BD * 4 * BDH * 4);
   L.w2cat = o; o += al256((size_t)BH * 2 * BDH * BD * 4);
-  L.e1 = o; o += al256((size_t)BH * Cc * 2 * BDH * 2);     // E1a, or the read's Eq (bf16)
+  L.e1 = o; o += al256((size_t)BH * Cc * 2 * BDH * 2);     // E1a (bf16)
+  L.eq = o; o += al256((size_t)BH * Cc * 2 * BDH * 2);     // the read's Eq (bf16)
   L.e2 = o; o += al256((size_t)BH * Cc * BDH * 2);         // the read's Hq (bf16)
   L.e3 = o; o += al256((size_t)BH * Cc * BDH * 2);         // E3 (bf16)
   L.j13 = o; o += al256((size_t)s13 * BH * BD * 2 * BDH * 4);
@@ -935,6 +969,7 @@ hipError_t launch_large_chunk_swiglu_backward(const BackwardArgs& a, int last_on
   float* Wcat = (float*)(ws + L.wcat);
   float* W2cat = (float*)(ws + L.w2cat);
   bf16* E1 = (bf16*)(ws + L.e1);
+  bf16* EQ = (bf16*)(ws + L.eq);
   bf16* E2 = (bf16*)(ws + L.e2);
   bf16* E3 = (bf16*)(ws + L.e3);
   float* J13 = (float*)(ws + L.j13);
@@ -967,22 +1002,29 @@ hipError_t launch_large_chunk_swiglu_backward(const BackwardArgs& a, int last_on
       hipSuccess)
     return e;
   const bool read_first = !a.other_order;
-  auto read_phase = [&](const float* R, long long rstride, long long c0, int Cc) -> hipError_t {
+  // the read's two token-contraction products of a chunk: (Q^T da | Q^T db) and (silu(a) b)^T dO
+  auto read_job13 = [&](long long c0, int Cc) {
+    return GemmJob{gargs(Q + c0 * BD, 1, BD, T * BD, EQ, 2 * BDH, 1, cap * 2 * BDH, A13, 2 * BDH, BD * 2 * BDH, BD,
+                         2 * BDH, Cc), BH, s13, p13};
+  };
+  auto read_job2 = [&](long long c0, int Cc) {
+    return GemmJob{gargs(E2, 1, BDH, cap * BDH, dO + c0 * BD, BD, 1, T * BD, A2, BD, BP, BDH, BD, Cc), BH, s2, p2};
+  };
+  auto read_phase = [&](const float* R, long long rstride, long long c0, int Cc, bool with_products) -> hipError_t {
     hipError_t e2;
     const bf16* Qc = Q + c0 * BD;
     const bf16* dOc = dO + c0 * BD;
-    bf16* Eq = E1;     // [Cc][da | db]        (E1's room)
+    bf16* Eq = EQ;     // [Cc][da | db]
     bf16* Hq = E2;     // [Cc][silu(a) b]      (E2's room)
     // the read's factors and dQ
     const ReadStepArgs ra{Qc, dOc, R, rstride, Eq, Hq, dQ + c0 * BD, (int)T, Cc, cap};
     hipLaunchKernelGGL(sw_bwd_read_step_kernel, dim3((unsigned)((Cc + ST_TOK - 1) / ST_TOK), BH), dim3(ST_NT), 0,
                        stream, ra);
     if ((e2 = hipGetLastError()) != hipSuccess) return e2;
+    if (!with_products) return hipSuccess;
     // (Q^T da | Q^T db), (silu(a) b)^T dO
-    return gemm2<bf16, bf16>(gargs(Qc, 1, BD, T * BD, Eq, 2 * BDH, 1, cap * 2 * BDH, A13, 2 * BDH, BD * 2 * BDH, BD,
-                                   2 * BDH, Cc), BH, s13, p13,
-                             gargs(Hq, 1, BDH, cap * BDH, dOc, BD, 1, T * BD, A2, BD, BP, BDH, BD, Cc), BH, s2, p2,
-                             stream);
+    const GemmJob jobs[2] = {read_job13(c0, Cc), read_job2(c0, Cc)};
+    return gemm_group<bf16, bf16>(jobs, 2, stream);
   };
 
   for (int c = nch - 1; c >= 0; --c) {
@@ -993,7 +1035,7 @@ hipError_t launch_large_chunk_swiglu_backward(const BackwardArgs& a, int last_on
     const float* Wc = dump + (long long)c * SP;                       // after it
     const long long wc_stride = (long long)nch * SP;
     if (!read_first) {   // the chunk's queries read W_c: their gradient reaches G before the normalisation
-      if ((e = read_phase(Wc, wc_stride, c0, Cc)) != hipSuccess) return e;
+      if ((e = read_phase(Wc, wc_stride, c0, Cc, true)) != hipSuccess) return e;
       hipLaunchKernelGGL(sw_bwd_gupdate, dim3((unsigned)((3 * BP / 4 + 255) / 256), BH), dim3(256), 0, stream, G, Wcat,
                          W2cat, J13, J2, A13, A2, s13, s2, 1, 0, last_only);
       if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -1009,13 +1051,15 @@ hipError_t launch_large_chunk_swiglu_backward(const BackwardArgs& a, int last_on
     hipLaunchKernelGGL(sw_bwd_step_kernel, dim3((unsigned)((Cc + ST_TOK - 1) / ST_TOK), BH), dim3(ST_WAVES * 64),
                        ST_LDS, stream, sa);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    // J13 = K^T (eta Pa | eta Pb), J2 = (eta hdot)^T V
-    if ((e = gemm2<bf16, bf16>(gargs(Kc, 1, BD, T * BD, E1, 2 * BDH, 1, cap * 2 * BDH, J13, 2 * BDH, BD * 2 * BDH, BD,
-                                     2 * BDH, Cc), BH, s13, p13,
-                               gargs(E3, 1, BDH, cap * BDH, Vc, BD, 1, T * BD, J2, BD, BP, BDH, BD, Cc), BH, s2, p2,
-                               stream)) != hipSuccess)
-      return e;
-    if (read_first && (e = read_phase(Wp, wp_stride, c0, Cc)) != hipSuccess) return e;
+    // J13 = K^T (eta Pa | eta Pb), J2 = (eta hdot)^T V; with the read first, the read's factors are formed
+    // before them and its two products join the same launch
+    if (read_first && (e = read_phase(Wp, wp_stride, c0, Cc, false)) != hipSuccess) return e;
+    const GemmJob jobs[4] = {
+        {gargs(Kc, 1, BD, T * BD, E1, 2 * BDH, 1, cap * 2 * BDH, J13, 2 * BDH, BD * 2 * BDH, BD, 2 * BDH, Cc), BH, s13,
+         p13},
+        {gargs(E3, 1, BDH, cap * BDH, Vc, BD, 1, T * BD, J2, BD, BP, BDH, BD, Cc), BH, s2, p2},
+        read_job13(c0, Cc), read_job2(c0, Cc)};
+    if ((e = gemm_group<bf16, bf16>(jobs, read_first ? 4 : 2, stream)) != hipSuccess) return e;
     hipLaunchKernelGGL(sw_bwd_gupdate, dim3((unsigned)((3 * BP / 4 + 255) / 256), BH), dim3(256), 0, stream, G, Wcat, W2cat,
                        J13, J2, A13, A2, s13, s2, 0, read_first ? 1 : 0, last_only);
     if ((e = hipGetLastError()) != hipSuccess) return e;
