@@ -378,7 +378,8 @@ __device__ __attribute__((noinline)) void swiglu_muon_steps(RecurLds& S, const S
 template <int RULE, bool DUMP = false>
 __global__ __launch_bounds__(SW_WAVES * 64, 1) void swiglu_recur_kernel(
     const bf16* __restrict__ K, const bf16* __restrict__ V, const float* __restrict__ eta,
-    const float* __restrict__ W0, float* __restrict__ Wout, bf16* __restrict__ states, float* __restrict__ ss2,
+    const float* __restrict__ W0, float* __restrict__ Wout, bf16* __restrict__ states,
+    unsigned long long* __restrict__ ss2,
     unsigned* __restrict__ counters, unsigned* __restrict__ errflag, int T_in, int chunk, int nchunks_in, int head0,
     int update_first, int last_only, int par_nchunks, int spin_limit, unsigned target_extra, SwRule R) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
@@ -747,24 +748,34 @@ __global__ __launch_bounds__(SW_WAVES * 64, 1) void swiglu_recur_kernel(
 #pragma unroll
         for (int j = 0; j < 4; ++j) ss = fmaf(x[j], x[j], ss);
       }
-      __hip_atomic_store(&ss2[(((size_t)bh * 2 + (c & 1)) * SW_NSL + sl) * D + d], ss, __ATOMIC_RELAXED,
-                         __HIP_MEMORY_SCOPE_AGENT);
-      // The partial norms are the only data exchanged, and every access to them is a device-scope
-      // atomic (coherent on its own).  Waiting for the stores to complete before the count goes up
-      // orders them before it; release/acquire on the count would in addition write back and
-      // invalidate the whole L2 at every chunk end (measured: ~9% of the recurrence).
-      wait_vm<0>();
-    }
-    if (last_only)
-      __syncthreads();
-    else
-      head_barrier();   // every slice's partial W2 column norms are out
-    if (!last_only && w >= 2 && w < 4) {
-      const int d = (w - 2) * 64 + l;
-      float ss = 0.f;
-      for (int s = 0; s < SW_NSL; ++s)
-        ss += __hip_atomic_load(&ss2[(((size_t)bh * 2 + (c & 1)) * SW_NSL + s) * D + d], __ATOMIC_RELAXED,
-                                __HIP_MEMORY_SCOPE_AGENT);
+      // The partial norms are the only data exchanged.  Each goes out with its chunk number in one
+      // 64-bit device-scope atomic (single-copy atomic, so the number vouches for the value it travels
+      // with), and the readers poll the slots themselves: a store and a load per exchange, instead of
+      // waiting for the store, raising a counter, polling it and then loading the values.  The slots
+      // of chunk c are reused at chunk c + 2, by which time every slice has read them (it wrote its
+      // chunk c + 1 partial after using chunk c's); the call clears them before the launch.
+      unsigned long long* slots = ss2 + ((size_t)bh * 2 + (c & 1)) * SW_NSL * D + d;
+      const unsigned want = (unsigned)(c + 1);
+      __hip_atomic_store(slots + (size_t)sl * D, ((unsigned long long)want << 32) | __float_as_uint(ss),
+                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      // every slice's partial of this chunk (bounded: on giving up the error flag is raised)
+      unsigned long long v[SW_NSL];
+      for (int spins = 0;; ++spins) {
+#pragma unroll
+        for (int s2 = 0; s2 < SW_NSL; ++s2)
+          v[s2] = __hip_atomic_load(slots + (size_t)s2 * D, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        bool all = true;
+#pragma unroll
+        for (int s2 = 0; s2 < SW_NSL; ++s2) all = all && (unsigned)(v[s2] >> 32) == want + target_extra;
+        if (all) break;
+        if (spins >= spin_limit) {
+          __hip_atomic_store(errflag, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+      }
+      ss = 0.f;
+      for (int s2 = 0; s2 < SW_NSL; ++s2) ss += __uint_as_float((unsigned)v[s2]);
       const float inv = 1.0f / fmaxf(sqrtf(ss), 1e-12f);
       if constexpr (DUMP) {
         if (sl == 0) R.dnorm[((size_t)bh * nchunks + c) * 640 + 2 * DH + d] = sqrtf(ss);
@@ -1163,7 +1174,7 @@ SwLayout sw_layout(int64_t BH, int64_t nchunks, int muon) {
   size_t off = (size_t)BH * nchunks * SW_STATE * 2;
   off = (off + 255) & ~(size_t)255;
   L.ss2 = off;
-  off += (size_t)BH * 2 * SW_NSL * SW_D * 4;
+  off += (size_t)BH * 2 * SW_NSL * SW_D * 8;   // 64-bit slots: chunk number | partial norm
   off = (off + 255) & ~(size_t)255;
   L.counters = off;
   off += (size_t)BH * 4;
@@ -1200,11 +1211,12 @@ hipError_t launch_swiglu_recur_dump(const LargeChunkArgs& a, float* dump, float*
   const SwLayout lay = sw_layout(BH, nchunks, 0);
   unsigned char* ws = (unsigned char*)a.ws;
   bf16* states = (bf16*)(ws + lay.states);
-  float* ss2 = (float*)(ws + lay.ss2);
+  auto* ss2 = (unsigned long long*)(ws + lay.ss2);
   unsigned* counters = (unsigned*)(ws + lay.counters);
   unsigned* err = (unsigned*)(ws + lay.err);
-  const int nz = BH + 1;
-  hipLaunchKernelGGL(zero_u32_kernel, dim3((nz + 255) / 256), dim3(256), 0, stream, counters, nz);
+  // the norm-exchange slots, the counters and the error flag start at zero (they are contiguous)
+  const int nz = (int)((lay.err + 4 - lay.ss2) / 4);
+  hipLaunchKernelGGL(zero_u32_kernel, dim3((nz + 255) / 256), dim3(256), 0, stream, (unsigned*)ss2, nz);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   auto krec = swiglu_recur_kernel<0, true>;
@@ -1276,12 +1288,13 @@ hipError_t launch_large_chunk_swiglu(const LargeChunkArgs& a, hipStream_t stream
   const SwLayout lay = sw_layout(BH, nchunks, a.muon);
   unsigned char* ws = (unsigned char*)a.ws;
   bf16* states = (bf16*)(ws + lay.states);
-  float* ss2 = (float*)(ws + lay.ss2);
+  auto* ss2 = (unsigned long long*)(ws + lay.ss2);
   unsigned* counters = (unsigned*)(ws + lay.counters);
   unsigned* err = (unsigned*)(ws + lay.err);
 
-  const int nz = BH + 1;
-  hipLaunchKernelGGL(zero_u32_kernel, dim3((nz + 255) / 256), dim3(256), 0, stream, counters, nz);
+  // the norm-exchange slots, the counters and the error flag start at zero (they are contiguous)
+  const int nz = (int)((lay.err + 4 - lay.ss2) / 4);
+  hipLaunchKernelGGL(zero_u32_kernel, dim3((nz + 255) / 256), dim3(256), 0, stream, (unsigned*)ss2, nz);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
 

@@ -140,7 +140,7 @@ def test_large_chunk_swiglu_float32_output(B, H, T, chunk, mode):
 
 
 @pytest.mark.parametrize("B,H,mode", [
-    (1, 20, "large_chunk_swiglu"),               # 16 heads in one cooperative launch, then 4
+    (1, 20, "large_chunk_swiglu"),               # 16 heads in one launch, then 4
     (1, 17, "large_chunk_swiglu_update_first"),  # then 1
     (2, 9, "large_chunk_swiglu_last_layer"),
 ])
