@@ -523,6 +523,18 @@ __global__ __launch_bounds__(SW_WAVES * 64, 1) void swiglu_recur_kernel(
     if (last_c > c) issue(last_c, last_gi, last_slot);
   };
 
+  // Momentum (RULE 1): weight k (0..7) of matrix j (W1, W3, W2) kept by this thread (the mapping is given
+  // at the chunk end): its place in the LDS copy and its float offset in the head's buffer [W1 | W3 | W2]
+  auto mom_elem = [&](int k, int j) -> float* {
+    const int i = tid + NT * k;
+    return j == 0 ? S.w1 + w13i(i >> 4, i & 15) : j == 1 ? S.w3 + w13i(i >> 4, i & 15) : S.w2 + w2i(i >> 7, i & 127);
+  };
+  auto mom_off = [&](int k, int j) -> size_t {
+    const int i = tid + NT * k;
+    return j < 2 ? (size_t)j * D * DH + (size_t)(i >> 4) * DH + u0 + (i & 15)
+                 : 2 * (size_t)D * DH + (size_t)(u0 + (i >> 7)) * D + (i & 127);
+  };
+
   bf16x8 w1op[4], w3op[4], w2op[4];
   floatx4 dW1[8], dW3[8], dW2[8];
   int ic = 0, ik = -1, ikn = nchunks > 0 ? count(0) : 0;   // issue cursor: chunk, step within it, count
@@ -639,18 +651,26 @@ __global__ __launch_bounds__(SW_WAVES * 64, 1) void swiglu_recur_kernel(
       const float* Msrc = c == 0 ? R.M0 : R.Mout;
       const float* Mi = Msrc ? Msrc + (size_t)bh * 3 * D * DH : nullptr;
       float* Mh = R.Mout + (size_t)bh * 3 * D * DH;
-      auto pre = [&](float* e, size_t go) {
-        const float m = Mi ? __hip_atomic_load(Mi + go, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0.f;
-        const float wo = *e;
-        __hip_atomic_store(Mh + go, wo, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        *e = wo + R.beta * m;
-      };
+      // (the thread's 24 buffer values are loaded 12 at a time: two memory round trips instead of 24;
+      // all 24 at once would push the wave past its registers)
 #pragma unroll 1
-      for (int k = 0; k < 8; ++k) {
-        const int i = tid + NT * k, d = i >> 4, u = i & 15, u2 = i >> 7, d2 = i & 127;
-        pre(S.w1 + w13i(d, u), (size_t)d * DH + u0 + u);
-        pre(S.w3 + w13i(d, u), (size_t)D * DH + (size_t)d * DH + u0 + u);
-        pre(S.w2 + w2i(u2, d2), 2 * (size_t)D * DH + (size_t)(u0 + u2) * D + d2);
+      for (int k0 = 0; k0 < 8; k0 += 4) {
+        float mv[4][3];
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+#pragma unroll
+          for (int j = 0; j < 3; ++j)
+            mv[k][j] = Mi ? __hip_atomic_load(Mi + mom_off(k0 + k, j), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                          : 0.f;
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+#pragma unroll
+          for (int j = 0; j < 3; ++j) {
+            float* e = mom_elem(k0 + k, j);
+            const float wo = *e;
+            __hip_atomic_store(Mh + mom_off(k0 + k, j), wo, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            *e = wo + R.beta * mv[k][j];
+          }
       }
       wait_vm<0>();
       __syncthreads();   // every value moved before any wave adds its partial gradient
@@ -698,16 +718,21 @@ __global__ __launch_bounds__(SW_WAVES * 64, 1) void swiglu_recur_kernel(
     }
     if constexpr (RULE == 1) {
       float* Mh = R.Mout + (size_t)bh * 3 * D * DH;
-      auto post = [&](const float* e, size_t go) {
-        const float wo = __hip_atomic_load(Mh + go, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(Mh + go, *e - wo, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      };
+      // M <- (W + beta M + dW) - W: the parked values loaded 12 at a time, then the differences stored
 #pragma unroll 1
-      for (int k = 0; k < 8; ++k) {
-        const int i = tid + NT * k, d = i >> 4, u = i & 15, u2 = i >> 7, d2 = i & 127;
-        post(S.w1 + w13i(d, u), (size_t)d * DH + u0 + u);
-        post(S.w3 + w13i(d, u), (size_t)D * DH + (size_t)d * DH + u0 + u);
-        post(S.w2 + w2i(u2, d2), 2 * (size_t)D * DH + (size_t)(u0 + u2) * D + d2);
+      for (int k0 = 0; k0 < 8; k0 += 4) {
+        float wv[4][3];
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+#pragma unroll
+          for (int j = 0; j < 3; ++j)
+            wv[k][j] = __hip_atomic_load(Mh + mom_off(k0 + k, j), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+#pragma unroll
+          for (int j = 0; j < 3; ++j)
+            __hip_atomic_store(Mh + mom_off(k0 + k, j), *mom_elem(k0 + k, j) - wv[k][j], __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
       }
       wait_vm<0>();
       __syncthreads();   // every updated weight read before the normalisation rewrites it
