@@ -1,4 +1,4 @@
-"""Plain fp64 CPU oracle for the TTT-with-KV-binding forward pass (and the per-token backward).
+"""Plain fp64 CPU oracle for the TTT-with-KV-binding forward pass, its update rules and its backward.
 
 TEST INFRASTRUCTURE ONLY. Nothing on the product path imports, calls or
 links this module: only the tests, the smoke check and the CPU-baseline leg
