@@ -509,12 +509,7 @@ __global__ __launch_bounds__(SW_WAVES * 64, 1) void swiglu_recur_kernel(
     dma4<true>(re, (unsigned)(l * 4), S.eta[w][slot]);    // lanes past the group read 0
   };
 
-  // Barrier of the head's NSL workgroups (through their counter; the k-th barrier waits for NSL * k
-  // arrivals).  Bounded: on giving up the call's error flag is raised (the read kernel then fills every
-  // output with NaN) and the workgroup carries on, so every kernel still ends.  Stores that other
-  // workgroups read after it must be complete (wait_vm<0>) before it.
-  unsigned nbar = 0;   // head barriers passed
-  auto head_barrier = [&]() { head_barrier_wait(counters, errflag, bh, nbar, spin_limit, target_extra); };
+  unsigned nbar = 0;   // head barriers passed (the Newton-Schulz exchange's, RULE 2; see head_barrier_wait)
 
   // RULE 2 at a chunk end (see swiglu_muon_steps); the stage whose copy was in flight when the iteration
   // took the LDS of the stages is copied again afterwards
